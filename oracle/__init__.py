@@ -1,0 +1,326 @@
+"""CPU oracle for one token-choice MoE layer -- TEST INFRASTRUCTURE ONLY.
+
+Only tests/, the smoke check in __graft_entry__ and the CPU-baseline leg of bench.py may
+import this package. The product library never imports it, and nothing here imports the
+product package.
+
+The arithmetic lives in moe_oracle.c (plain loops, double precision); this module compiles
+it with gcc when no up-to-date build exists and wraps each entry point with numpy arrays.
+Which part of the pages each function follows is stated in the C source.
+
+Parity status: every function here is pinned by tests under tests/ (marked "not gpu")
+against library routines, closed forms, brute force on tiny inputs or the OCP e4m3
+specification, except absolute output values for the full-size workloads, which no page
+prints ("parity unpinned" for those values; they rest on the pinned pieces).
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+_LIB = os.path.join(_HERE, "libmoe_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+F32, BF16, E4M3 = 0, 1, 2
+SOFTMAX_TOPK, SIGMOID_GROUP_TOPK = 0, 1
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle (gcc, -O2, OpenMP, no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-std=c11",
+                               "-shared", "-fPIC", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+P = C.c_void_p
+I32 = C.c_int
+I64 = C.c_int64
+
+
+def lib():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build()
+            L = C.CDLL(_LIB)
+            L.orc_e4m3_value.restype = C.c_double
+            L.orc_e4m3_value.argtypes = [C.c_uint8]
+            L.orc_e4m3_encode.restype = C.c_uint8
+            L.orc_e4m3_encode.argtypes = [C.c_float]
+            L.orc_quant_rows.argtypes = [P, I32, I64, I32, P, P]
+            L.orc_quant_weight.argtypes = [P, I32, I64, I32, I32, P, P]
+            L.orc_router_logits.argtypes = [P, P, I32, I32, I32, I32, P]
+            L.orc_route.argtypes = [P, P, P, I32, I32, I32, I32, I32, I32, C.c_double, P, P, P]
+            L.orc_permute.argtypes = [P, P, I32, I32, I32, P, P, P, P, P]
+            L.orc_expert_rows.argtypes = [I32, I32, I32, P, I32, P, P, P, P, P, I32, P, P,
+                                          I32, P, I64, P, P, P]
+            L.orc_layer_tokens.argtypes = [I32, I32, I32, I32, I32, I32, P, I32, I32, P, P,
+                                           P, P, I32, P, P, P, P, P, P, I32, P, I64, P]
+            L.orc_expert_bwd_rows.argtypes = [I32, I32, I32, P, P, I32, P, P, P, P, P, I64,
+                                              P, P]
+            L.orc_expert_wgrad_entries.argtypes = [I32, I32, P, P, P, P, I32, P, I32, P, P,
+                                                   P, P, I64, P, P, P, I64, P]
+            for f in ("orc_quant_rows", "orc_quant_weight", "orc_router_logits", "orc_route",
+                      "orc_permute", "orc_expert_rows", "orc_layer_tokens",
+                      "orc_expert_bwd_rows", "orc_expert_wgrad_entries"):
+                getattr(L, f).restype = None
+            _lib = L
+    return _lib
+
+
+# ------------------------------------------------------------------------------------
+# array helpers: the oracle takes numpy arrays (bf16 as uint16 bit patterns, e4m3 as uint8)
+# ------------------------------------------------------------------------------------
+
+def as_np(t):
+    """torch CPU tensor or numpy array -> (contiguous numpy array, dtype code)."""
+    try:
+        import torch
+        if isinstance(t, torch.Tensor):
+            t = t.detach().contiguous()
+            if t.dtype == torch.bfloat16:
+                return t.view(torch.int16).numpy().view(np.uint16), BF16
+            if t.dtype == torch.float32:
+                return t.numpy(), F32
+            if t.dtype == torch.uint8:
+                return t.numpy(), E4M3
+            raise TypeError(f"unsupported dtype {t.dtype}")
+    except ImportError:
+        pass
+    a = np.ascontiguousarray(t)
+    if a.dtype == np.uint16:
+        return a, BF16
+    if a.dtype == np.float32:
+        return a, F32
+    if a.dtype == np.uint8:
+        return a, E4M3
+    raise TypeError(f"unsupported dtype {a.dtype}")
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+def _f32(a):
+    return None if a is None else np.ascontiguousarray(np.asarray(a, dtype=np.float32))
+
+
+def _i32(a):
+    return None if a is None else np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def _i64(a):
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int64))
+
+
+# ------------------------------------------------------------------------------------
+# number formats
+# ------------------------------------------------------------------------------------
+
+def e4m3_value(code: int) -> float:
+    return lib().orc_e4m3_value(int(code))
+
+
+def e4m3_encode(v: float) -> int:
+    return lib().orc_e4m3_encode(float(v))
+
+
+def e4m3_decode_array(q: np.ndarray) -> np.ndarray:
+    table = np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
+    return table[q]
+
+
+def quant_rows(v, block: int = 128):
+    """1 x 128 block quantisation of [rows, cols] -> (codes uint8 [rows, cols], scales f32)."""
+    a, dt = as_np(v)
+    rows, cols = a.shape
+    assert cols % block == 0 and block == 128
+    q = np.empty((rows, cols), np.uint8)
+    s = np.empty((rows, cols // 128), np.float32)
+    lib().orc_quant_rows(_p(a), dt, rows, cols, _p(q), _p(s))
+    return q, s
+
+
+def quant_weight(w):
+    """128 x 128 block quantisation of [n, rows, cols] (or [rows, cols])."""
+    a, dt = as_np(w)
+    squeeze = a.ndim == 2
+    if squeeze:
+        a = a[None]
+    n, rows, cols = a.shape
+    assert rows % 128 == 0 and cols % 128 == 0
+    q = np.empty((n, rows, cols), np.uint8)
+    s = np.empty((n, rows // 128, cols // 128), np.float32)
+    lib().orc_quant_weight(_p(a), dt, n, rows, cols, _p(q), _p(s))
+    if squeeze:
+        return q[0], s[0]
+    return q, s
+
+
+# ------------------------------------------------------------------------------------
+# routing
+# ------------------------------------------------------------------------------------
+
+def router_logits(x, w_router) -> np.ndarray:
+    xa, dt = as_np(x)
+    wa, dt2 = as_np(w_router)
+    assert dt == dt2
+    T, H = xa.shape
+    E = wa.shape[0]
+    out = np.empty((T, E), np.float32)
+    lib().orc_router_logits(_p(xa), _p(wa), dt, T, H, E, _p(out))
+    return out
+
+
+def route(logits, k, router=SOFTMAX_TOPK, logit_bias=None, sel_bias=None, n_groups=1,
+          topk_groups=1, route_scale=1.0, return_scores=False):
+    lg = _f32(logits)
+    T, E = lg.shape
+    assert E <= 4096 and k <= E
+    idx = np.empty((T, k), np.int32)
+    gate = np.empty((T, k), np.float32)
+    sc = np.empty((T, E), np.float32) if return_scores else None
+    lib().orc_route(_p(lg), _p(_f32(logit_bias)), _p(_f32(sel_bias)), T, E, k, router,
+                    n_groups, topk_groups, float(route_scale), _p(idx), _p(gate), _p(sc))
+    if return_scores:
+        return idx, gate, sc
+    return idx, gate
+
+
+def route_cfg(cfg, logits, logit_bias=None, sel_bias=None, return_scores=False):
+    return route(logits, cfg.k, cfg.router, logit_bias, sel_bias, cfg.n_groups,
+                 cfg.topk_groups, cfg.route_scale, return_scores)
+
+
+def permute(topk_idx, topk_gate, E):
+    idx = _i32(topk_idx)
+    T, k = idx.shape
+    g = _f32(topk_gate)
+    counts = np.empty(E, np.int32)
+    offsets = np.empty(E + 1, np.int32)
+    pos = np.empty((T, k), np.int32)
+    src = np.empty(T * k, np.int32)
+    gp = np.empty(T * k, np.float32)
+    lib().orc_permute(_p(idx), _p(g), T, k, E, _p(counts), _p(offsets), _p(pos), _p(src),
+                      _p(gp))
+    return dict(counts=counts, offsets=offsets, pos=pos, src=src, gate_perm=gp)
+
+
+def gather_rows(x, pos):
+    """x_perm[pos[t, j]] = x[t]: the permuted copy (pure data movement)."""
+    a = np.asarray(x)
+    pos = np.asarray(pos)
+    T, k = pos.shape
+    out = np.empty((T * k,) + a.shape[1:], a.dtype)
+    for j in range(k):
+        out[pos[:, j]] = a
+    return out
+
+
+# ------------------------------------------------------------------------------------
+# expert math
+# ------------------------------------------------------------------------------------
+
+def expert_rows(x_perm, offsets, gate_perm, w13, w2, rows, x_scales=None, w13_scales=None,
+                w2_scales=None, quant_act=False, want_z=False):
+    """Expert math for selected rows of the expert-grouped buffer.
+    Returns (z or None, act, y_perm) as float64 arrays [n, 2F], [n, F], [n, H]."""
+    xa, xdt = as_np(x_perm)
+    w13a, wdt = as_np(w13)
+    w2a, wdt2 = as_np(w2)
+    assert wdt == wdt2
+    if w13a.ndim == 2:
+        w13a, w2a = w13a[None], w2a[None]
+    E, F2, H = w13a.shape
+    F = F2 // 2
+    rows = _i64(rows)
+    n = rows.shape[0]
+    z = np.empty((n, 2 * F)) if want_z else None
+    act = np.empty((n, F))
+    y = np.empty((n, H))
+    lib().orc_expert_rows(H, F, E, _p(xa), xdt, _p(_f32(x_scales)), _p(_i32(offsets)),
+                          _p(_f32(gate_perm)), _p(w13a), _p(w2a), wdt,
+                          _p(_f32(w13_scales)), _p(_f32(w2_scales)), int(quant_act),
+                          _p(rows), n, _p(z), _p(act), _p(y))
+    return z, act, y
+
+
+def layer_tokens(x, topk_idx, topk_gate, w13, w2, tokens, ws13=None, ws2=None, fp8=False,
+                 w13_scales=None, w2_scales=None, ws13_scales=None, ws2_scales=None,
+                 fold=True):
+    """The per-token loop for selected tokens -> y [n, H] float64."""
+    xa, xdt = as_np(x)
+    T, H = xa.shape
+    idx = _i32(topk_idx)
+    k = idx.shape[1]
+    w13a, wdt = as_np(w13)
+    w2a, _ = as_np(w2)
+    E, F2, _ = w13a.shape
+    F = F2 // 2
+    sF = 0
+    s13a = s2a = None
+    if ws13 is not None:
+        s13a, _ = as_np(ws13)
+        s2a, _ = as_np(ws2)
+        sF = s13a.shape[0] // 2
+    tokens = _i64(tokens)
+    n = tokens.shape[0]
+    y = np.empty((n, H))
+    lib().orc_layer_tokens(T, H, E, k, F, sF, _p(xa), xdt, int(fp8), _p(idx),
+                           _p(_f32(topk_gate)), _p(w13a), _p(w2a), wdt, _p(_f32(w13_scales)),
+                           _p(_f32(w2_scales)), _p(s13a), _p(s2a), _p(_f32(ws13_scales)),
+                           _p(_f32(ws2_scales)), int(fold), _p(tokens), n, _p(y))
+    return y
+
+
+def expert_bwd_rows(dy_perm, z, offsets, gate_perm, w13, w2, rows):
+    """Data gradients of selected rows -> (dx [n, H], dg [n])."""
+    dya, dt = as_np(dy_perm)
+    za, dt2 = as_np(z)
+    w13a, dt3 = as_np(w13)
+    w2a, dt4 = as_np(w2)
+    assert dt == dt2 == dt3 == dt4
+    if w13a.ndim == 2:
+        w13a, w2a = w13a[None], w2a[None]
+    E, F2, H = w13a.shape
+    F = F2 // 2
+    rows = _i64(rows)
+    n = rows.shape[0]
+    dx = np.empty((n, H))
+    dg = np.empty(n)
+    lib().orc_expert_bwd_rows(H, F, E, _p(dya), _p(za), dt, _p(_i32(offsets)),
+                              _p(_f32(gate_perm)), _p(w13a), _p(w2a), _p(rows), n, _p(dx),
+                              _p(dg))
+    return dx, dg
+
+
+def expert_wgrad_entries(dy_perm, z, act, x_perm, offsets, e, gate_perm, w2, w13_rc, w2_rc):
+    """Selected entries of dW13_e and dW2_e -> (dw13 [n13], dw2 [n2])."""
+    dya, dt = as_np(dy_perm)
+    za, _ = as_np(z)
+    aa, _ = as_np(act)
+    xa, _ = as_np(x_perm)
+    w2a, _ = as_np(w2)
+    if w2a.ndim == 2:
+        w2a = w2a[None]
+    _, H, F = w2a.shape
+    r13, c13 = (_i32(v) for v in w13_rc)
+    r2, c2 = (_i32(v) for v in w2_rc)
+    dw13 = np.empty(r13.shape[0])
+    dw2 = np.empty(r2.shape[0])
+    offs = _i32(offsets)
+    lib().orc_expert_wgrad_entries(H, F, _p(dya), _p(za), _p(aa), _p(xa), dt, _p(offs), e,
+                                   _p(_f32(gate_perm)), _p(w2a), _p(r13), _p(c13),
+                                   r13.shape[0], _p(dw13), _p(r2), _p(c2), r2.shape[0],
+                                   _p(dw2))
+    return dw13, dw2
