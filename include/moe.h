@@ -1,0 +1,211 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) forward pass of one token-choice
+ * Mixture-of-Experts layer on one GPU's share of tokens:
+ *
+ *   router scores -> top-k experts and gates -> permute (group the token copies by
+ *   expert) -> SwiGLU experts as one grouped GEMM (gate folded into the activation)
+ *   -> unpermute / combine back to token order,   y = sum_e g_e * Expert_e(x).
+ *
+ * The steps follow the per-token loop in the study notes "Megatron-Core MoE --
+ * 大规模稀疏专家并行实践" (实践案例, 案例 1) and the optimisations named in the
+ * technical summary "使用 Megatron Core 大规模训练混合专家模型（MoE）" (section 2.2
+ * memory-efficient permutation; section 2.4 grouped GEMM, fused routing/permutation and
+ * sync-free kernels).
+ *
+ * Conventions (every entry point):
+ *  - Pointers are DEVICE pointers owned by the caller, except `cfg` and `bytes`, which are
+ *    host pointers read (written) during the call only. The library never allocates or
+ *    frees device memory; scratch comes from the caller's workspace `ws` of `ws_bytes`
+ *    bytes, sized by moe_workspace_size().
+ *  - Work is enqueued on `stream` and the call returns at once. The library never
+ *    synchronises a stream or the device and never copies device -> host: expert counts
+ *    and offsets stay on the device.
+ *  - Arguments are validated on the host before anything is enqueued; on an invalid
+ *    argument nothing is launched and MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED or
+ *    MOE_ERR_WORKSPACE is returned. A failed launch returns MOE_ERR_HIP. Expert indices
+ *    are not validated on the device: topk_idx must come from moe_route or lie in [0, E).
+ *  - Every output is overwritten, never accumulated into. Results are deterministic:
+ *    bit-identical across runs (no floating-point atomics, no split-K).
+ *  - Layouts are row-major and contiguous. Both GEMM operands keep K contiguous, so each
+ *    expert GEMM is C = A B^T. fp8 scale tensors are fp32, row-major over blocks.
+ *  - Calls on different streams may overlap if their outputs and workspaces are disjoint.
+ */
+#ifndef MOE_AMD_H
+#define MOE_AMD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1,   /* null pointer, non-positive size, k > E, ... */
+    MOE_ERR_UNSUPPORTED = 2,   /* valid but not implemented (dtype mix, H % 128 != 0 ...) */
+    MOE_ERR_WORKSPACE = 3,     /* ws_bytes smaller than moe_workspace_size() */
+    MOE_ERR_HIP = 4            /* a HIP launch failed */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_E4M3 = 2 } moe_dtype;
+
+typedef enum {
+    /* select on the logits (ties to the lower expert index); gates = softmax over the k
+     * selected logits (the full softmax renormalised over the selected set) */
+    MOE_ROUTER_SOFTMAX_TOPK = 0,
+    /* s = sigmoid(logit) (evaluated in double, rounded once to fp32); key = s + sel_bias;
+     * group score = sum of the two largest keys of each of n_groups contiguous expert
+     * groups; keep topk_groups groups; top-k experts by key inside them;
+     * gates = route_scale * s / sum(s over the selected) (the bias selects only) */
+    MOE_ROUTER_SIGMOID_GROUP_TOPK = 1
+} moe_router;
+
+typedef enum {
+    MOE_OP_PERMUTE = 0,
+    MOE_OP_GROUPED_GEMM = 1,
+    MOE_OP_LAYER_FORWARD = 2,
+    MOE_OP_GROUPED_GEMM_BWD = 3
+} moe_op;
+
+/* Layer shape and numerics. Host memory, read only during a call. */
+typedef struct {
+    int32_t T;            /* tokens on this GPU */
+    int32_t H;            /* hidden size */
+    int32_t E;            /* routed experts (1 .. 1024) */
+    int32_t k;            /* experts per token (1 .. min(E, 32)) */
+    int32_t F;            /* SwiGLU width of one routed expert */
+    int32_t n_groups;     /* expert groups for the group-limited router (1 = none) */
+    int32_t topk_groups;  /* groups kept per token */
+    int32_t router;       /* moe_router */
+    float route_scale;    /* gate multiplier (1 for softmax, 2.5 DeepSeek-V3 style) */
+    int32_t act_dtype;    /* MOE_F32 or MOE_BF16: x, router weight, y_perm, y */
+    int32_t w_dtype;      /* expert GEMM operands: MOE_F32 (with act F32), MOE_BF16 or
+                             MOE_E4M3 (with act BF16: 1x128 activation scales, 128x128
+                             weight scales, fp32 accumulation) */
+    int32_t shared_F;     /* width of the always-on shared expert, 0 = none */
+} moe_config;
+
+/* Name of a status code (static string; never NULL). */
+const char* moe_status_string(int status);
+
+/* Workspace bytes needed by entry point `op` for `cfg`. Host only, no HIP call. */
+int moe_workspace_size(const moe_config* cfg, int op, size_t* bytes);
+
+/* Router scores ("scores = Router(x)" in the per-token loop): a linear router without bias,
+ *   logits[t, e] = sum_h x[t, h] * w_router[e, h],  fp32 accumulation and output.
+ * x [T, H] and w_router [E, H] are in cfg->act_dtype; logits [T, E] fp32. */
+int moe_router_logits(const moe_config* cfg, const void* x, const void* w_router,
+                      float* logits, hipStream_t stream);
+
+/* Top-k expert selection and gates ("experts = TopK(scores, k)"), one wavefront per token.
+ *   l[e] = fp32(logits[t, e] + logit_bias[e])    (logit_bias [E] fp32, may be NULL)
+ * then cfg->router (see moe_router). sel_bias [E] fp32 is used by the sigmoid router and
+ * may be NULL there (zero bias). Slots are in rank order: key descending, ties to the
+ * lower expert index (-0.0 ties +0.0).
+ * Outputs: topk_idx [T, k] int32, topk_gate [T, k] fp32. */
+int moe_route(const moe_config* cfg, const float* logits, const float* logit_bias,
+              const float* sel_bias, int32_t* topk_idx, float* topk_gate,
+              hipStream_t stream);
+
+/* Permute (the routing metadata -- indices, counts, offsets -- and the grouped copy of x),
+ * computed on the device without any host synchronisation. Dropless: exactly A = T*k rows.
+ *   counts[e]   = number of (t, j) with topk_idx[t, j] == e              [E]    int32
+ *   offsets     = exclusive prefix sum of counts (offsets[E] = A)          [E+1]  int32
+ *   pos[t*k+j]  = row of assignment (t, j); rows of one expert are in ascending token
+ *                 order (a stable counting sort)                           [A]    int32
+ *   src[row]    = token of a row                                           [A]    int32
+ *   gate_perm[row] = topk_gate of the assignment                           [A]    fp32
+ *   x_perm[pos[t*k+j], :] = x[t, :]                                        [A, H]
+ * With cfg->w_dtype == MOE_E4M3, x (bf16) is quantised per 1 x 128 block
+ * (s = fp32(amax / 448), q = e4m3_rne_saturate(fp32(x / s))): x_perm holds the e4m3
+ * codes and x_perm_scales [A, H/128] the scales; x_q [T, H] / x_q_scales [T, H/128]
+ * optionally (may be NULL) receive the quantised x in token order (for a shared expert).
+ * Otherwise x_perm has cfg->act_dtype and the scale pointers must be NULL. */
+int moe_permute(const moe_config* cfg, const void* x, const int32_t* topk_idx,
+                const float* topk_gate, int32_t* counts, int32_t* offsets, int32_t* pos,
+                int32_t* src, float* gate_perm, void* x_perm, float* x_perm_scales,
+                void* x_q, float* x_q_scales, void* ws, size_t ws_bytes,
+                hipStream_t stream);
+
+/* SwiGLU experts as one grouped GEMM over the expert-grouped rows (ragged per-expert M).
+ * For expert e and its rows R_e = [offsets[e], offsets[e+1]):
+ *   Z   = x_perm[R_e] W13_e^T                     [M_e, 2F]  (fp32 accumulation)
+ *   act = gate_perm[r] * silu(Z[:, :F]) * Z[:, F:] [M_e, F]   (gate folded in: the
+ *         memory-efficient permutation of the technical summary, section 2.2)
+ *   y_perm[R_e] = act W2_e^T                       [M_e, H]
+ * w13 [E, 2F, H] (rows 0..F-1 gate, F..2F-1 up), w2 [E, H, F]. With MOE_E4M3 weights,
+ * w13_scales [E, 2F/128, H/128] and w2_scales [E, H/128, F/128] are the 128 x 128 block
+ * scales, x_perm is e4m3 with x_perm_scales [A, H/128], and act is stored as e4m3 with
+ * act_scales [A, F/128] (quantised per 1 x 128 after the fold); otherwise all scale
+ * pointers must be NULL and act has cfg->act_dtype. y_perm has cfg->act_dtype.
+ * Shared expert (cfg->shared_F > 0): the same SwiGLU with weight 1 applied to every token
+ * of x_shared [T, H] (e4m3 + x_shared_scales in fp8 mode), weights ws13 [2*shared_F, H],
+ * ws2 [H, shared_F] (+ scales), output shared_y [T, H] in cfg->act_dtype. Pass NULL for
+ * all shared arguments when shared_F == 0.
+ * z_out [A, 2F] (optional, NULL = not saved): Z rounded to cfg->act_dtype, for a backward. */
+int moe_grouped_gemm_swiglu(const moe_config* cfg, const void* x_perm,
+                            const float* x_perm_scales, const int32_t* offsets,
+                            const float* gate_perm, const void* w13, const float* w13_scales,
+                            const void* w2, const float* w2_scales, const void* x_shared,
+                            const float* x_shared_scales, const void* ws13,
+                            const float* ws13_scales, const void* ws2,
+                            const float* ws2_scales, void* act, float* act_scales,
+                            void* y_perm, void* shared_y, void* z_out, void* ws,
+                            size_t ws_bytes, hipStream_t stream);
+
+/* Unpermute / combine: y[t, :] = sum_{j<k} y_perm[pos[t*k+j], :] (+ shared_y[t, :]),
+ * summed in fp32 in slot order and rounded once to cfg->act_dtype. The gates were folded
+ * in before the down projection, so no weight is applied here. A gather: no atomics.
+ * shared_y may be NULL. */
+int moe_unpermute_combine(const moe_config* cfg, const void* y_perm, const int32_t* pos,
+                          const void* shared_y, void* y, hipStream_t stream);
+
+/* The whole layer: router GEMM (skipped when logits_in != NULL), route, permute, grouped
+ * GEMM with the shared expert, combine. x [T, H] and w_router [E, H] in act_dtype; weights
+ * as in moe_grouped_gemm_swiglu; y [T, H] in act_dtype. Optional outputs (NULL = skip):
+ * logits_out [T, E], topk_idx_out [T, k], topk_gate_out [T, k], counts_out [E]. */
+int moe_layer_forward(const moe_config* cfg, const void* x, const void* w_router,
+                      const float* logit_bias, const float* sel_bias, const float* logits_in,
+                      const void* w13, const float* w13_scales, const void* w2,
+                      const float* w2_scales, const void* ws13, const float* ws13_scales,
+                      const void* ws2, const float* ws2_scales, void* y, float* logits_out,
+                      int32_t* topk_idx_out, float* topk_gate_out, int32_t* counts_out,
+                      void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Backward of the grouped expert MLP with the gate fold (bf16 operands, fp32
+ * accumulation), data and weight gradients as separate grouped GEMMs (the W/D split of
+ * the technical summary, section 2.3). Per expert rows R_e, with h = silu(Z_g) * Z_u and
+ * act = g * h recomputed from the saved z:
+ *   dA     = dy_perm W2_e                      dg[r] = sum_f dA[r, f] h[r, f]
+ *   dZ_g   = g dA Z_u silu'(Z_g)               dZ_u  = g dA silu(Z_g)
+ *   dx_perm = dZ W13_e                          [M_e, H]
+ *   dW2_e  = dy_perm[R_e]^T act[R_e]            [H, F]
+ *   dW13_e = dZ[R_e]^T x_perm[R_e]              [2F, H]
+ * dy_perm [A, H], x_perm [A, H], z [A, 2F], w13, w2 in bf16 (cfg->act_dtype == MOE_BF16);
+ * outputs dx_perm [A, H], dw13 [E, 2F, H], dw2 [E, H, F] bf16 and dgate_perm [A] fp32.
+ * Experts with no rows get zero weight gradients. */
+int moe_grouped_gemm_swiglu_bwd(const moe_config* cfg, const void* dy_perm,
+                                const void* x_perm, const void* z, const float* gate_perm,
+                                const int32_t* offsets, const void* w13, const void* w2,
+                                void* dx_perm, void* dw13, void* dw2, float* dgate_perm,
+                                void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* e4m3 block quantisation of n_mat matrices [rows, cols] (bf16 or fp32 input):
+ * one fp32 scale per block_rows x block_cols block, s = fp32(amax / 448) (1 for an
+ * all-zero block), q = e4m3_rne_saturate(fp32(v / s)) in the OCP E4M3 format.
+ * block_rows is 1 (activations) or 128 (weights); block_cols is 128; rows and cols must be
+ * multiples of the block. q [n_mat, rows, cols] uint8, scales
+ * [n_mat, rows/block_rows, cols/128] fp32. (FP8 E4M3 for expert GEMMs: "万亿参数MoE模型
+ * 训练的技术挑战", section 2.1.) */
+int moe_quantize_e4m3(const void* in, int32_t in_dtype, int64_t n_mat, int32_t rows,
+                      int32_t cols, int32_t block_rows, int32_t block_cols, uint8_t* q,
+                      float* scales, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_AMD_H */

@@ -70,9 +70,10 @@ def lib():
                                               P, P]
             L.orc_expert_wgrad_entries.argtypes = [I32, I32, P, P, P, P, I32, P, I32, P, P,
                                                    P, P, I64, P, P, P, I64, P]
+            L.orc_combine.argtypes = [P, P, I32, P, I32, I32, I32, P]
             for f in ("orc_quant_rows", "orc_quant_weight", "orc_router_logits", "orc_route",
                       "orc_permute", "orc_expert_rows", "orc_layer_tokens",
-                      "orc_expert_bwd_rows", "orc_expert_wgrad_entries"):
+                      "orc_expert_bwd_rows", "orc_expert_wgrad_entries", "orc_combine"):
                 getattr(L, f).restype = None
             _lib = L
     return _lib
@@ -225,6 +226,21 @@ def gather_rows(x, pos):
     for j in range(k):
         out[pos[:, j]] = a
     return out
+
+
+def combine(y_perm, pos, shared_y=None):
+    """y[t] = sum_j y_perm[pos[t, j]] (+ shared_y[t]) -> float64 [T, H]."""
+    ya, dt = as_np(y_perm)
+    sa = None
+    if shared_y is not None:
+        sa, dt2 = as_np(shared_y)
+        assert dt2 == dt
+    pos = _i32(pos)
+    T, k = pos.shape
+    H = ya.shape[1]
+    y = np.empty((T, H))
+    lib().orc_combine(_p(ya), _p(sa), dt, _p(pos), T, k, H, _p(y))
+    return y
 
 
 # ------------------------------------------------------------------------------------

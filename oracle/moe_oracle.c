@@ -591,3 +591,24 @@ void orc_expert_wgrad_entries(int H, int F, const void* dy_perm, const void* z,
     }
     free(dz);
 }
+
+/* ------------------------------------------------------------------------------------ */
+/* Unpermute / combine                                                                  */
+/* ------------------------------------------------------------------------------------ */
+
+/* y[t] = sum_j y_perm[pos[t*k+j]] (+ shared_y[t]): the token's expert outputs brought back
+ * to token order and added; the gates are already inside y_perm (folded before the down
+ * projection). Inputs fp32 or bf16 (shared_y may be NULL), output double. */
+void orc_combine(const void* y_perm, const void* shared_y, int dtype, const int32_t* pos,
+                 int T, int k, int H, double* y) {
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; ++t) {
+        for (int h = 0; h < H; ++h) {
+            double acc = 0.0;
+            for (int j = 0; j < k; ++j)
+                acc += load(y_perm, dtype, (int64_t)pos[(int64_t)t * k + j] * H + h);
+            if (shared_y) acc += load(shared_y, dtype, (int64_t)t * H + h);
+            y[(int64_t)t * H + h] = acc;
+        }
+    }
+}

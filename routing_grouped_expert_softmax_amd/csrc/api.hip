@@ -1,0 +1,375 @@
+// C ABI of the MoE-layer forward: host-side validation, workspace carving, launches.
+// Every entry point validates before it enqueues anything, never allocates device memory,
+// never synchronises and never copies device -> host.
+#include <string.h>
+
+#include "../../include/moe.h"
+#include "kernels.h"
+
+namespace {
+
+using moe::Segment;
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+size_t elem_bytes(int dtype) { return dtype == MOE_F32 ? 4 : dtype == MOE_BF16 ? 2 : 1; }
+
+// Validation of the configuration itself (shapes and numerics).
+int check_cfg(const moe_config* c) {
+    if (!c) return MOE_ERR_INVALID_ARG;
+    if (c->T < 1 || c->H < 1 || c->E < 1 || c->k < 1 || c->F < 1 || c->shared_F < 0)
+        return MOE_ERR_INVALID_ARG;
+    if (c->k > c->E) return MOE_ERR_INVALID_ARG;
+    if (c->E > 1024 || c->k > 32) return MOE_ERR_UNSUPPORTED;
+    if ((int64_t)c->T * c->k > (int64_t)1 << 30) return MOE_ERR_UNSUPPORTED;
+    if (c->router == MOE_ROUTER_SOFTMAX_TOPK) {
+        if (c->n_groups != 1 || c->topk_groups != 1) return MOE_ERR_INVALID_ARG;
+    } else if (c->router == MOE_ROUTER_SIGMOID_GROUP_TOPK) {
+        if (c->n_groups < 1 || c->topk_groups < 1 || c->topk_groups > c->n_groups)
+            return MOE_ERR_INVALID_ARG;
+        if (c->E % c->n_groups != 0) return MOE_ERR_INVALID_ARG;
+        int per = c->E / c->n_groups;
+        if (per < 2 || per * c->topk_groups < c->k) return MOE_ERR_INVALID_ARG;
+        if (c->n_groups > 64) return MOE_ERR_UNSUPPORTED;
+    } else {
+        return MOE_ERR_INVALID_ARG;
+    }
+    if (!(c->route_scale > 0.0f) || c->route_scale != c->route_scale) return MOE_ERR_INVALID_ARG;
+    if (c->act_dtype == MOE_F32) {
+        if (c->w_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
+        if (c->H % 64 || c->F % 32 || (c->shared_F && c->shared_F % 32)) return MOE_ERR_UNSUPPORTED;
+    } else if (c->act_dtype == MOE_BF16) {
+        if (c->w_dtype != MOE_BF16 && c->w_dtype != MOE_E4M3) return MOE_ERR_UNSUPPORTED;
+        if (c->H % 256 || c->F % 128 || (c->shared_F && c->shared_F % 128))
+            return MOE_ERR_UNSUPPORTED;
+    } else {
+        return MOE_ERR_INVALID_ARG;
+    }
+    return MOE_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// ---- workspace layouts -------------------------------------------------------------------
+struct Carve {
+    char* base;
+    size_t off = 0;
+    explicit Carve(void* p) : base((char*)p) {}
+    void* take(size_t bytes) {
+        void* p = base ? base + off : nullptr;
+        off += align_up(bytes);
+        return p;
+    }
+};
+
+size_t gemm_ws_bytes(const moe_config* c) {
+    const int dt = c->w_dtype;
+    const int A = c->T * c->k;
+    const int seg_groups = c->E + (c->shared_F ? 1 : 0);
+    const int rows = A + (c->shared_F ? c->T : 0);
+    size_t s1 = moe::grouped_gemm_plan(0, dt, rows, seg_groups, 2 * c->F, c->H).ws_bytes;
+    size_t s2 = moe::grouped_gemm_plan(1, dt, rows, seg_groups, c->H, c->F).ws_bytes;
+    size_t sched = align_up(s1 > s2 ? s1 : s2);
+    size_t shared = 0;
+    if (c->shared_F) {
+        const size_t eb = c->w_dtype == MOE_E4M3 ? 1 : elem_bytes(c->act_dtype);
+        shared += align_up((size_t)c->T * c->shared_F * eb);                // shared act
+        if (c->w_dtype == MOE_E4M3)
+            shared += align_up((size_t)c->T * (c->shared_F / 128) * 4);      // its scales
+    }
+    return sched + shared;
+}
+
+struct LayerWs {
+    float* logits;
+    int32_t* idx;
+    float* gate;
+    int32_t* counts;
+    int32_t* offsets;
+    int32_t* pos;
+    int32_t* src;
+    float* gate_perm;
+    void* x_perm;
+    float* x_perm_scales;
+    void* x_q;
+    float* x_q_scales;
+    void* act;
+    float* act_scales;
+    void* y_perm;
+    void* shared_y;
+    void* scratch;       // permute / grouped-GEMM scratch (used one after the other)
+    size_t total;
+};
+
+LayerWs carve_layer(const moe_config* c, void* ws) {
+    LayerWs L = {};
+    Carve cv(ws);
+    const size_t T = c->T, H = c->H, E = c->E, k = c->k, F = c->F, A = T * k;
+    const bool fp8 = c->w_dtype == MOE_E4M3;
+    const size_t ab = elem_bytes(c->act_dtype);
+    const size_t gb = fp8 ? 1 : ab;       // GEMM operand bytes
+    L.logits = (float*)cv.take(T * E * 4);
+    L.idx = (int32_t*)cv.take(A * 4);
+    L.gate = (float*)cv.take(A * 4);
+    L.counts = (int32_t*)cv.take(E * 4);
+    L.offsets = (int32_t*)cv.take((E + 1) * 4);
+    L.pos = (int32_t*)cv.take(A * 4);
+    L.src = (int32_t*)cv.take(A * 4);
+    L.gate_perm = (float*)cv.take(A * 4);
+    L.x_perm = cv.take(A * H * gb);
+    L.x_perm_scales = fp8 ? (float*)cv.take(A * (H / 128) * 4) : nullptr;
+    L.x_q = (fp8 && c->shared_F) ? cv.take(T * H) : nullptr;
+    L.x_q_scales = (fp8 && c->shared_F) ? (float*)cv.take(T * (H / 128) * 4) : nullptr;
+    L.act = cv.take(A * F * gb);
+    L.act_scales = fp8 ? (float*)cv.take(A * (F / 128) * 4) : nullptr;
+    L.y_perm = cv.take(A * H * ab);
+    L.shared_y = c->shared_F ? cv.take(T * H * ab) : nullptr;
+    size_t p = moe::permute_ws_bytes(c->T, c->k, c->E);
+    size_t g = gemm_ws_bytes(c);
+    L.scratch = cv.take(p > g ? p : g);
+    L.total = cv.off;
+    return L;
+}
+
+// The grouped GEMMs of the experts (routed, then the shared expert as a second segment).
+int run_experts(const moe_config* c, const void* x_perm, const float* x_perm_scales,
+                const int32_t* offsets, const float* gate_perm, const void* w13,
+                const float* w13_scales, const void* w2, const float* w2_scales,
+                const void* x_shared, const float* x_shared_scales, const void* ws13,
+                const float* ws13_scales, const void* ws2, const float* ws2_scales, void* act,
+                float* act_scales, void* y_perm, void* shared_y, void* z_out, void* ws,
+                hipStream_t stream) {
+    const int dt = c->w_dtype;
+    const int A = c->T * c->k;
+    // scratch: tile schedule, then the shared expert's activation (+ scales)
+    const int seg_groups = c->E + (c->shared_F ? 1 : 0);
+    const int rows = A + (c->shared_F ? c->T : 0);
+    size_t s1 = moe::grouped_gemm_plan(0, dt, rows, seg_groups, 2 * c->F, c->H).ws_bytes;
+    size_t s2 = moe::grouped_gemm_plan(1, dt, rows, seg_groups, c->H, c->F).ws_bytes;
+    Carve cv(ws);
+    void* sched = cv.take(s1 > s2 ? s1 : s2);
+    void* sh_act = nullptr;
+    float* sh_act_scales = nullptr;
+    if (c->shared_F) {
+        const size_t eb = dt == MOE_E4M3 ? 1 : elem_bytes(c->act_dtype);
+        sh_act = cv.take((size_t)c->T * c->shared_F * eb);
+        if (dt == MOE_E4M3) sh_act_scales = (float*)cv.take((size_t)c->T * (c->shared_F / 128) * 4);
+    }
+    Segment r1 = {x_perm, x_perm_scales, offsets, c->E, 0, gate_perm, w13, w13_scales,
+                  act, act_scales, z_out};
+    Segment r2 = {act, act_scales, offsets, c->E, 0, nullptr, w2, w2_scales, y_perm, nullptr,
+                  nullptr};
+    const bool fused_shared = c->shared_F == c->F;
+    if (!c->shared_F || fused_shared) {
+        Segment g1[2] = {r1, {}}, g2[2] = {r2, {}};
+        int nseg = 1;
+        if (c->shared_F) {
+            g1[1] = Segment{x_shared, x_shared_scales, nullptr, 1, c->T, nullptr, ws13,
+                            ws13_scales, sh_act, sh_act_scales, nullptr};
+            g2[1] = Segment{sh_act, sh_act_scales, nullptr, 1, c->T, nullptr, ws2, ws2_scales,
+                            shared_y, nullptr, nullptr};
+            nseg = 2;
+        }
+        hipError_t e = moe::launch_grouped_gemm(0, dt, g1, nseg, rows, 2 * c->F, c->H, sched, stream);
+        if (e == hipSuccess)
+            e = moe::launch_grouped_gemm(1, dt, g2, nseg, rows, c->H, c->F, sched, stream);
+        return hip_status(e);
+    }
+    // shared expert of another width: its own launches
+    hipError_t e = moe::launch_grouped_gemm(0, dt, &r1, 1, A, 2 * c->F, c->H, sched, stream);
+    if (e == hipSuccess) e = moe::launch_grouped_gemm(1, dt, &r2, 1, A, c->H, c->F, sched, stream);
+    Segment s1g = {x_shared, x_shared_scales, nullptr, 1, c->T, nullptr, ws13, ws13_scales,
+                   sh_act, sh_act_scales, nullptr};
+    Segment s2g = {sh_act, sh_act_scales, nullptr, 1, c->T, nullptr, ws2, ws2_scales, shared_y,
+                   nullptr, nullptr};
+    if (e == hipSuccess)
+        e = moe::launch_grouped_gemm(0, dt, &s1g, 1, c->T, 2 * c->shared_F, c->H, sched, stream);
+    if (e == hipSuccess)
+        e = moe::launch_grouped_gemm(1, dt, &s2g, 1, c->T, c->H, c->shared_F, sched, stream);
+    return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+    switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: unsupported shape or dtype";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace too small";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: a HIP launch failed";
+    default: return "unknown moe status";
+    }
+}
+
+int moe_workspace_size(const moe_config* cfg, int op, size_t* bytes) {
+    if (!bytes) return MOE_ERR_INVALID_ARG;
+    int st = check_cfg(cfg);
+    if (st) return st;
+    switch (op) {
+    case MOE_OP_PERMUTE: *bytes = moe::permute_ws_bytes(cfg->T, cfg->k, cfg->E); break;
+    case MOE_OP_GROUPED_GEMM: *bytes = gemm_ws_bytes(cfg); break;
+    case MOE_OP_LAYER_FORWARD: *bytes = carve_layer(cfg, nullptr).total; break;
+    case MOE_OP_GROUPED_GEMM_BWD: return MOE_ERR_UNSUPPORTED;
+    default: return MOE_ERR_INVALID_ARG;
+    }
+    return MOE_OK;
+}
+
+int moe_router_logits(const moe_config* cfg, const void* x, const void* w_router,
+                      float* logits, hipStream_t stream) {
+    int st = check_cfg(cfg);
+    if (st) return st;
+    if (!x || !w_router || !logits) return MOE_ERR_INVALID_ARG;
+    return hip_status(moe::launch_router_logits(cfg->act_dtype, x, w_router, cfg->T, cfg->H,
+                                                cfg->E, logits, stream));
+}
+
+int moe_route(const moe_config* cfg, const float* logits, const float* logit_bias,
+              const float* sel_bias, int32_t* topk_idx, float* topk_gate, hipStream_t stream) {
+    int st = check_cfg(cfg);
+    if (st) return st;
+    if (!logits || !topk_idx || !topk_gate) return MOE_ERR_INVALID_ARG;
+    return hip_status(moe::launch_route(cfg->router, logits, logit_bias, sel_bias, cfg->T,
+                                        cfg->E, cfg->k, cfg->n_groups, cfg->topk_groups,
+                                        cfg->route_scale, topk_idx, topk_gate, stream));
+}
+
+int moe_permute(const moe_config* cfg, const void* x, const int32_t* topk_idx,
+                const float* topk_gate, int32_t* counts, int32_t* offsets, int32_t* pos,
+                int32_t* src, float* gate_perm, void* x_perm, float* x_perm_scales, void* x_q,
+                float* x_q_scales, void* ws, size_t ws_bytes, hipStream_t stream) {
+    int st = check_cfg(cfg);
+    if (st) return st;
+    if (!x || !topk_idx || !topk_gate || !counts || !offsets || !pos || !src || !gate_perm ||
+        !x_perm || !ws)
+        return MOE_ERR_INVALID_ARG;
+    const bool fp8 = cfg->w_dtype == MOE_E4M3;
+    if (fp8 != (x_perm_scales != nullptr)) return MOE_ERR_INVALID_ARG;
+    if (!fp8 && (x_q || x_q_scales)) return MOE_ERR_INVALID_ARG;
+    if ((x_q == nullptr) != (x_q_scales == nullptr)) return MOE_ERR_INVALID_ARG;
+    if (ws_bytes < moe::permute_ws_bytes(cfg->T, cfg->k, cfg->E)) return MOE_ERR_WORKSPACE;
+    const int mode = fp8 ? 2 : (cfg->act_dtype == MOE_F32 ? 0 : 1);
+    return hip_status(moe::launch_permute(mode, x, topk_idx, topk_gate, cfg->T, cfg->H, cfg->E,
+                                          cfg->k, counts, offsets, pos, src, gate_perm, x_perm,
+                                          x_perm_scales, x_q, x_q_scales, ws, stream));
+}
+
+int moe_grouped_gemm_swiglu(const moe_config* cfg, const void* x_perm,
+                            const float* x_perm_scales, const int32_t* offsets,
+                            const float* gate_perm, const void* w13, const float* w13_scales,
+                            const void* w2, const float* w2_scales, const void* x_shared,
+                            const float* x_shared_scales, const void* ws13,
+                            const float* ws13_scales, const void* ws2,
+                            const float* ws2_scales, void* act, float* act_scales,
+                            void* y_perm, void* shared_y, void* z_out, void* ws,
+                            size_t ws_bytes, hipStream_t stream) {
+    int st = check_cfg(cfg);
+    if (st) return st;
+    if (!x_perm || !offsets || !gate_perm || !w13 || !w2 || !act || !y_perm || !ws)
+        return MOE_ERR_INVALID_ARG;
+    const bool fp8 = cfg->w_dtype == MOE_E4M3;
+    if (fp8) {
+        if (!x_perm_scales || !w13_scales || !w2_scales || !act_scales) return MOE_ERR_INVALID_ARG;
+        return MOE_ERR_UNSUPPORTED;          // e4m3 expert GEMMs: see moe_config.w_dtype
+    }
+    if (x_perm_scales || w13_scales || w2_scales || act_scales || x_shared_scales ||
+        ws13_scales || ws2_scales)
+        return MOE_ERR_INVALID_ARG;
+    if (cfg->shared_F) {
+        if (!x_shared || !ws13 || !ws2 || !shared_y) return MOE_ERR_INVALID_ARG;
+    } else if (x_shared || ws13 || ws2 || shared_y) {
+        return MOE_ERR_INVALID_ARG;
+    }
+    if (ws_bytes < gemm_ws_bytes(cfg)) return MOE_ERR_WORKSPACE;
+    return run_experts(cfg, x_perm, x_perm_scales, offsets, gate_perm, w13, w13_scales, w2,
+                       w2_scales, x_shared, x_shared_scales, ws13, ws13_scales, ws2,
+                       ws2_scales, act, act_scales, y_perm, shared_y, z_out, ws, stream);
+}
+
+int moe_unpermute_combine(const moe_config* cfg, const void* y_perm, const int32_t* pos,
+                          const void* shared_y, void* y, hipStream_t stream) {
+    int st = check_cfg(cfg);
+    if (st) return st;
+    if (!y_perm || !pos || !y) return MOE_ERR_INVALID_ARG;
+    return hip_status(moe::launch_combine(cfg->act_dtype, y_perm, pos, shared_y, cfg->T,
+                                          cfg->H, cfg->k, y, stream));
+}
+
+int moe_layer_forward(const moe_config* cfg, const void* x, const void* w_router,
+                      const float* logit_bias, const float* sel_bias, const float* logits_in,
+                      const void* w13, const float* w13_scales, const void* w2,
+                      const float* w2_scales, const void* ws13, const float* ws13_scales,
+                      const void* ws2, const float* ws2_scales, void* y, float* logits_out,
+                      int32_t* topk_idx_out, float* topk_gate_out, int32_t* counts_out,
+                      void* ws, size_t ws_bytes, hipStream_t stream) {
+    int st = check_cfg(cfg);
+    if (st) return st;
+    if (!x || !w13 || !w2 || !y || !ws) return MOE_ERR_INVALID_ARG;
+    if (!logits_in && !w_router) return MOE_ERR_INVALID_ARG;
+    const bool fp8 = cfg->w_dtype == MOE_E4M3;
+    if (fp8 && (!w13_scales || !w2_scales)) return MOE_ERR_INVALID_ARG;
+    if (fp8) return MOE_ERR_UNSUPPORTED;
+    if (cfg->shared_F && (!ws13 || !ws2)) return MOE_ERR_INVALID_ARG;
+    LayerWs L = carve_layer(cfg, nullptr);
+    if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    L = carve_layer(cfg, ws);
+    float* logits = logits_out ? logits_out : L.logits;
+    int32_t* idx = topk_idx_out ? topk_idx_out : L.idx;
+    float* gate = topk_gate_out ? topk_gate_out : L.gate;
+    int32_t* counts = counts_out ? counts_out : L.counts;
+    hipError_t e = hipSuccess;
+    const float* lg = logits_in;
+    if (!lg) {
+        e = moe::launch_router_logits(cfg->act_dtype, x, w_router, cfg->T, cfg->H, cfg->E,
+                                      logits, stream);
+        lg = logits;
+    }
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    e = moe::launch_route(cfg->router, lg, logit_bias, sel_bias, cfg->T, cfg->E, cfg->k,
+                          cfg->n_groups, cfg->topk_groups, cfg->route_scale, idx, gate, stream);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    const int mode = fp8 ? 2 : (cfg->act_dtype == MOE_F32 ? 0 : 1);
+    e = moe::launch_permute(mode, x, idx, gate, cfg->T, cfg->H, cfg->E, cfg->k, counts,
+                            L.offsets, L.pos, L.src, L.gate_perm, L.x_perm, L.x_perm_scales,
+                            L.x_q, L.x_q_scales, L.scratch, stream);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    const void* xs = fp8 ? L.x_q : x;
+    st = run_experts(cfg, L.x_perm, L.x_perm_scales, L.offsets, L.gate_perm, w13, w13_scales,
+                     w2, w2_scales, cfg->shared_F ? xs : nullptr, fp8 ? L.x_q_scales : nullptr,
+                     ws13, ws13_scales, ws2, ws2_scales, L.act, L.act_scales, L.y_perm,
+                     L.shared_y, nullptr, L.scratch, stream);
+    if (st) return st;
+    return hip_status(moe::launch_combine(cfg->act_dtype, L.y_perm, L.pos, L.shared_y, cfg->T,
+                                          cfg->H, cfg->k, y, stream));
+}
+
+int moe_grouped_gemm_swiglu_bwd(const moe_config* cfg, const void* dy_perm, const void* x_perm,
+                                const void* z, const float* gate_perm, const int32_t* offsets,
+                                const void* w13, const void* w2, void* dx_perm, void* dw13,
+                                void* dw2, float* dgate_perm, void* ws, size_t ws_bytes,
+                                hipStream_t stream) {
+    (void)dy_perm; (void)x_perm; (void)z; (void)gate_perm; (void)offsets; (void)w13; (void)w2;
+    (void)dx_perm; (void)dw13; (void)dw2; (void)dgate_perm; (void)ws; (void)ws_bytes;
+    (void)stream;
+    int st = check_cfg(cfg);
+    if (st) return st;
+    return MOE_ERR_UNSUPPORTED;
+}
+
+int moe_quantize_e4m3(const void* in, int32_t in_dtype, int64_t n_mat, int32_t rows,
+                      int32_t cols, int32_t block_rows, int32_t block_cols, uint8_t* q,
+                      float* scales, hipStream_t stream) {
+    if (!in || !q || !scales) return MOE_ERR_INVALID_ARG;
+    if (in_dtype != MOE_F32 && in_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+    if (n_mat < 1 || rows < 1 || cols < 1) return MOE_ERR_INVALID_ARG;
+    if (block_cols != 128 || (block_rows != 1 && block_rows != 128)) return MOE_ERR_UNSUPPORTED;
+    if (cols % 128 || rows % block_rows) return MOE_ERR_INVALID_ARG;
+    return hip_status(moe::launch_quantize(in, in_dtype, n_mat, rows, cols, block_rows, q,
+                                           scales, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,190 @@
+// Unpermute / combine: y[t] = sum_j y_perm[pos[t, j]] (+ shared_y[t]), fp32 sum in slot
+// order, one rounding to the output dtype. The gates were folded into the activations
+// before the down projection (memory-efficient permutation, technical summary section
+// 2.2), so this is a pure gather-sum: no weights, no atomics, deterministic.
+//
+// e4m3 block quantisation (the FP8 E4M3 format of "万亿参数MoE模型训练的技术挑战",
+// section 2.1) of weights (128 x 128 blocks) and activations (1 x 128 blocks) lives here
+// too: both are HBM-streaming kernels.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+// bf16: one wavefront per token, 8 values (16 bytes) per lane per step.
+__global__ __launch_bounds__(256) void combine_bf16_kernel(const uint4* __restrict__ y_perm,
+                                                           const int32_t* __restrict__ pos,
+                                                           const uint4* __restrict__ shared_y,
+                                                           int T, int row_chunks, int k,
+                                                           uint4* __restrict__ y) {
+    const int lane = threadIdx.x % kWave;
+    const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+    if (t >= T) return;
+    int my_pos = lane < k ? pos[(size_t)t * k + lane] : 0;
+    for (int c0 = 0; c0 < row_chunks; c0 += kWave) {
+        const int c = c0 + lane;
+        const bool ok = c < row_chunks;
+        float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        for (int j = 0; j < k; ++j) {
+            int r = __shfl(my_pos, j);
+            if (ok) {
+                uint4 v = y_perm[(size_t)r * row_chunks + c];
+                uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    acc[2 * i] += bf16_to_f32((uint16_t)(w[i] & 0xFFFFu));
+                    acc[2 * i + 1] += bf16_to_f32((uint16_t)(w[i] >> 16));
+                }
+            }
+        }
+        if (!ok) continue;
+        if (shared_y) {
+            uint4 v = shared_y[(size_t)t * row_chunks + c];
+            uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc[2 * i] += bf16_to_f32((uint16_t)(w[i] & 0xFFFFu));
+                acc[2 * i + 1] += bf16_to_f32((uint16_t)(w[i] >> 16));
+            }
+        }
+        uint4 o;
+        o.x = pack_bf16x2(acc[0], acc[1]);
+        o.y = pack_bf16x2(acc[2], acc[3]);
+        o.z = pack_bf16x2(acc[4], acc[5]);
+        o.w = pack_bf16x2(acc[6], acc[7]);
+        y[(size_t)t * row_chunks + c] = o;
+    }
+}
+
+// fp32: 4 values (16 bytes) per lane per step.
+__global__ __launch_bounds__(256) void combine_f32_kernel(const float4* __restrict__ y_perm,
+                                                          const int32_t* __restrict__ pos,
+                                                          const float4* __restrict__ shared_y,
+                                                          int T, int row_chunks, int k,
+                                                          float4* __restrict__ y) {
+    const int lane = threadIdx.x % kWave;
+    const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+    if (t >= T) return;
+    int my_pos = lane < k ? pos[(size_t)t * k + lane] : 0;
+    for (int c0 = 0; c0 < row_chunks; c0 += kWave) {
+        const int c = c0 + lane;
+        const bool ok = c < row_chunks;
+        float4 acc = make_float4(0, 0, 0, 0);
+        for (int j = 0; j < k; ++j) {
+            int r = __shfl(my_pos, j);
+            if (ok) {
+                float4 v = y_perm[(size_t)r * row_chunks + c];
+                acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+            }
+        }
+        if (!ok) continue;
+        if (shared_y) {
+            float4 v = shared_y[(size_t)t * row_chunks + c];
+            acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+        }
+        y[(size_t)t * row_chunks + c] = acc;
+    }
+}
+
+MOE_DEVICE float load_as_f32(const void* p, int dtype, size_t i) {
+    return dtype == 0 ? ((const float*)p)[i] : bf16_to_f32(((const uint16_t*)p)[i]);
+}
+
+// Activation quantiser, 1 x 128 blocks: one wavefront per 128-column block... per row:
+// each 16-lane group handles one block, 8 values per lane.
+__global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict__ in,
+                                                         int in_dtype, int64_t rows, int cols,
+                                                         uint8_t* __restrict__ q,
+                                                         float* __restrict__ scales) {
+    const int64_t nblk_row = cols / 128;
+    const int64_t gblk = (int64_t)blockIdx.x * 16 + threadIdx.x / 16;   // global block id
+    const int sub = threadIdx.x % 16;
+    const bool ok = gblk < rows * nblk_row;
+    const int64_t r = ok ? gblk / nblk_row : 0;
+    const int64_t b = ok ? gblk % nblk_row : 0;
+    const size_t base = (size_t)r * cols + (size_t)b * 128 + sub * 8;
+    float f[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = ok ? load_as_f32(in, in_dtype, base + i) : 0.0f;
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    float sc = e4m3_scale(amax);
+    if (!ok) return;
+    uint32_t c[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = e4m3_rne_sat(f[i] / sc);
+    uint2 packed;
+    packed.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+    packed.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+    *(uint2*)(q + base) = packed;
+    if (sub == 0) scales[gblk] = sc;
+}
+
+// Weight quantiser, 128 x 128 blocks: one 256-thread block per quantisation block; each
+// thread handles half a row (64 values) of the block.
+__global__ __launch_bounds__(256) void quant_weight_kernel(const void* __restrict__ in,
+                                                           int in_dtype, int rows, int cols,
+                                                           uint8_t* __restrict__ q,
+                                                           float* __restrict__ scales) {
+    __shared__ float red[4];
+    const int nbr = rows / 128, nbc = cols / 128;
+    const int64_t blk = blockIdx.x;                       // [mat, br, bc]
+    const int64_t mat = blk / ((int64_t)nbr * nbc);
+    const int br = (int)((blk / nbc) % nbr);
+    const int bc = (int)(blk % nbc);
+    const int r = br * 128 + threadIdx.x / 2;
+    const int c0 = bc * 128 + (threadIdx.x % 2) * 64;
+    const size_t base = ((size_t)mat * rows + r) * (size_t)cols + c0;
+    float amax = 0.0f;
+    for (int i = 0; i < 64; ++i) amax = fmaxf(amax, fabsf(load_as_f32(in, in_dtype, base + i)));
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float sc = e4m3_scale(amax);
+    for (int i = 0; i < 64; i += 4) {
+        uint32_t c0v = e4m3_rne_sat(load_as_f32(in, in_dtype, base + i) / sc);
+        uint32_t c1v = e4m3_rne_sat(load_as_f32(in, in_dtype, base + i + 1) / sc);
+        uint32_t c2v = e4m3_rne_sat(load_as_f32(in, in_dtype, base + i + 2) / sc);
+        uint32_t c3v = e4m3_rne_sat(load_as_f32(in, in_dtype, base + i + 3) / sc);
+        *(uint32_t*)(q + base + i) = c0v | (c1v << 8) | (c2v << 16) | (c3v << 24);
+    }
+    if (threadIdx.x == 0) scales[blk] = sc;
+}
+
+}  // namespace
+
+hipError_t launch_combine(int act_dtype, const void* y_perm, const int32_t* pos,
+                          const void* shared_y, int T, int H, int k, void* y, hipStream_t s) {
+    const int blocks = (T + 3) / 4;
+    if (act_dtype == 0)
+        combine_f32_kernel<<<blocks, 256, 0, s>>>((const float4*)y_perm, pos,
+                                                  (const float4*)shared_y, T, H / 4, k,
+                                                  (float4*)y);
+    else
+        combine_bf16_kernel<<<blocks, 256, 0, s>>>((const uint4*)y_perm, pos,
+                                                   (const uint4*)shared_y, T, H / 8, k,
+                                                   (uint4*)y);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize(const void* in, int in_dtype, int64_t n_mat, int rows, int cols,
+                           int block_rows, uint8_t* q, float* scales, hipStream_t s) {
+    if (block_rows == 1) {
+        int64_t nblocks = n_mat * rows * (int64_t)(cols / 128);
+        quant_rows_kernel<<<(unsigned)((nblocks + 15) / 16), 256, 0, s>>>(
+            in, in_dtype, n_mat * rows, cols, q, scales);
+    } else {
+        int64_t nblocks = n_mat * (int64_t)(rows / 128) * (cols / 128);
+        quant_weight_kernel<<<(unsigned)nblocks, 256, 0, s>>>(in, in_dtype, rows, cols, q,
+                                                              scales);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,94 @@
+// Device helpers shared by the MoE kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define MOE_DEVICE __device__ __forceinline__
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------------------
+// bf16 <-> fp32
+// ---------------------------------------------------------------------------------------
+MOE_DEVICE float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// fp32 -> bf16, round to nearest even (inputs are finite).
+MOE_DEVICE uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+MOE_DEVICE uint32_t pack_bf16x2(float lo, float hi) {
+    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// ---------------------------------------------------------------------------------------
+// OCP E4M3 (e4m3fn): bias 7, largest finite 448, subnormal step 2^-9, no infinities.
+// Round to nearest, ties to even, saturating at +-448; the sign of -0.0 is kept.
+// ---------------------------------------------------------------------------------------
+MOE_DEVICE uint32_t e4m3_rne_sat(float v) {
+    uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+    float a = fabsf(v);
+    if (!(a < 448.0f)) return sign | 0x7Eu;
+    if (a < 0.015625f) {                       // below 2^-6: multiples of 2^-9
+        float m = a * 512.0f;                  // exact
+        return sign | (uint32_t)rintf(m);      // 0..8; 8 is the smallest normal 0x08
+    }
+    uint32_t ua = __float_as_uint(a);
+    int ex = (int)(ua >> 23) - 127;            // -6 .. 8
+    uint32_t keep = (ua >> 20) & 7u;
+    uint32_t rest = ua & 0xFFFFFu;
+    if (rest > 0x80000u || (rest == 0x80000u && (keep & 1u))) keep += 1;
+    if (keep == 8u) { keep = 0; ex += 1; }
+    return sign | ((uint32_t)(ex + 7) << 3) | keep;
+}
+
+// e4m3 block scale: fp32(amax / 448), 1 for an all-zero block.
+MOE_DEVICE float e4m3_scale(float amax) { return amax == 0.0f ? 1.0f : amax / 448.0f; }
+
+// ---------------------------------------------------------------------------------------
+// Wavefront reductions (deterministic butterflies)
+// ---------------------------------------------------------------------------------------
+MOE_DEVICE uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        uint64_t o = __shfl_xor(v, off);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+MOE_DEVICE float wave_sum_f32(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    return v;
+}
+
+// Order-preserving map of a finite float to uint32 (-0.0 is mapped like +0.0).
+MOE_DEVICE uint32_t float_order_key(float f) {
+    f = (f == 0.0f) ? 0.0f : f;
+    uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+MOE_DEVICE float float_from_order_key(uint32_t o) {
+    uint32_t u = (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o;
+    return __uint_as_float(u);
+}
+
+// 64-bit rank key: a larger key wins, and on equal keys the lower index wins.
+MOE_DEVICE uint64_t rank_key(float key, int index) {
+    return ((uint64_t)float_order_key(key) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)index);
+}
+MOE_DEVICE int rank_key_index(uint64_t rk) { return (int)(0xFFFFFFFFu - (uint32_t)rk); }
+MOE_DEVICE float rank_key_value(uint64_t rk) { return float_from_order_key((uint32_t)(rk >> 32)); }
+
+MOE_DEVICE float silu_f32(float u) { return u / (1.0f + expf(-u)); }

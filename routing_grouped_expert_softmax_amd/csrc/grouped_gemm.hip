@@ -1,0 +1,487 @@
+// SwiGLU experts as one grouped GEMM over ragged, expert-grouped rows.
+//
+// The technical summary "使用 Megatron Core 大规模训练混合专家模型（MoE）" (section 2.4) runs
+// the many small expert GEMMs as one grouped GEMM; this is the gfx950 version:
+//
+//  * a schedule kernel turns the device-resident expert offsets into a list of M tiles
+//    (segment, expert, first row, rows), so no host synchronisation is needed;
+//  * one launch covers every (M tile, N tile) of every expert (and of the shared expert);
+//    workgroups past the live tile count exit at once;
+//  * workgroups are remapped so that each XCD (the hardware deals workgroups round-robin
+//    over 8 XCDs) works through one contiguous run of tiles, N fastest: the N tiles of one
+//    M tile share its activation rows in that XCD's L2;
+//  * bf16 tiles go global -> registers -> LDS (double buffered, padded rows) and into
+//    v_mfma_f32_32x32x16_bf16 with fp32 accumulation;
+//  * GEMM1 loads the gate rows [n0, n0+BN/2) and the matching up rows [F+n0, ...) of W13
+//    into one B tile, so a lane holds Z_gate and Z_up of the same (row, column) and the
+//    epilogue writes act = g * silu(Z_gate) * Z_up directly: the gate is folded into the
+//    activation before the down projection (memory-efficient permutation, section 2.2),
+//    and Z itself is never stored unless a backward asks for it.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+// ---------------------------------------------------------------------------------------
+// tile schedule
+// ---------------------------------------------------------------------------------------
+struct SegDev {
+    const void* a;
+    const float* a_scales;
+    const float* gate;
+    const void* w;
+    const float* w_scales;
+    void* out;
+    float* out_scales;
+    void* z_out;
+};
+
+struct SchedArgs {
+    const int32_t* offsets[2];
+    int groups[2];
+    int rows[2];
+    int nseg;
+};
+
+// tiles[i] = {seg << 20 | group, first row within the group, rows of the group,
+//             global row of the group's first row}; *total = number of M tiles.
+// One block of 1024 threads; each thread owns two consecutive group slots.
+__global__ __launch_bounds__(1024) void schedule_kernel(SchedArgs sa, int bm,
+                                                        int4* __restrict__ tiles,
+                                                        int* __restrict__ total) {
+    __shared__ int wsum[16];
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    int nslot = 0;
+    for (int s = 0; s < sa.nseg; ++s) nslot += sa.groups[s];
+    int seg_of[2], grp_of[2], m_of[2], base_of[2], nt_of[2];
+    int mine = 0;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        int slot = 2 * tid + q;
+        seg_of[q] = -1;
+        nt_of[q] = 0;
+        if (slot < nslot) {
+            int s = 0, g = slot;
+            if (g >= sa.groups[0]) { s = 1; g -= sa.groups[0]; }
+            int base, m;
+            if (sa.offsets[s]) {
+                base = sa.offsets[s][g];
+                m = sa.offsets[s][g + 1] - base;
+            } else {
+                base = 0;
+                m = sa.rows[s];
+            }
+            seg_of[q] = s; grp_of[q] = g; m_of[q] = m; base_of[q] = base;
+            nt_of[q] = (m + bm - 1) / bm;
+        }
+        mine += nt_of[q];
+    }
+    int v = mine;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        int o = __shfl_up(v, off);
+        if (lane >= off) v += o;
+    }
+    if (lane == kWave - 1) wsum[wave] = v;
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += wsum[w];
+    int start = before + v - mine;
+    if (tid == blockDim.x - 1) *total = before + v;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        for (int i = 0; i < nt_of[q]; ++i)
+            tiles[start + i] = make_int4((seg_of[q] << 20) | grp_of[q], i * bm, m_of[q],
+                                         base_of[q]);
+        start += nt_of[q];
+    }
+}
+
+struct GemmArgs {
+    SegDev seg[2];
+    const int4* tiles;
+    const int* total;
+    int N, K;          // GEMM N (before SwiGLU pairing) and K
+    int ntn;           // N tiles
+    int per_xcd_max;   // launched blocks / 8
+};
+
+// Map this workgroup to a live tile (XCD-aware); false when there is none.
+MOE_DEVICE bool pick_tile(const GemmArgs& ga, int& mt, int& nt) {
+    const int b = blockIdx.x;
+    const int xcd = b % 8, i = b / 8;
+    const int total = *ga.total * ga.ntn;
+    const int per = (total + 7) / 8;
+    if (i >= per) return false;
+    const int L = xcd * per + i;
+    if (L >= total) return false;
+    mt = L / ga.ntn;
+    nt = L % ga.ntn;
+    return true;
+}
+
+// ---------------------------------------------------------------------------------------
+// bf16 MFMA kernel
+//
+// LDS holds STAGES stages of [BM A rows | BN B rows] x 128 bytes (64 bf16 of K). Tiles are
+// filled by direct global -> LDS loads (global_load_lds_dwordx4: no staging registers),
+// each wave instruction filling 8 rows = 1 KB. Within a row the 16-byte chunks are
+// XOR-swizzled (physical chunk = logical chunk ^ (row & 7)) so that the 32 rows one MFMA
+// operand read touches spread over the LDS banks. Prefetch distance is STAGES - 1 K steps.
+// ---------------------------------------------------------------------------------------
+#define MOE_LDS __attribute__((address_space(3)))
+
+// s_waitcnt with vmcnt <= N, lgkmcnt == 0 (gfx9 encoding; expcnt not waited for).
+template <int N>
+MOE_DEVICE void wait_vm_lgkm0() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
+// Workgroup barrier without a memory fence: the pipeline orders its LDS traffic itself with
+// explicit waits; the empty asm statements keep the compiler from moving memory accesses
+// across the barrier.
+MOE_DEVICE void block_sync() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <int KIND, int BM, int BN, int WM, int WN, int STAGES>
+struct BfCfg {
+    static constexpr int kThreads = WM * WN * kWave;
+    static constexpr int kWaves = WM * WN;
+    static constexpr int kBK = 64;                          // bf16 per row per stage
+    static constexpr int kRowBytes = 128;
+    static constexpr int kRows = BM + BN;
+    static constexpr int kStageBytes = kRows * kRowBytes;
+    static constexpr int kDma = kRows / 8 / kWaves;         // DMA instructions per wave/stage
+    static constexpr int kTM = BM / WM / 32;                // 32x32 tiles per wave (M)
+    static constexpr int kTN = BN / WN / 32;                // 32x32 tiles per wave (N)
+    static constexpr size_t kLds = (size_t)STAGES * kStageBytes;
+    static_assert(kRows % (8 * kWaves) == 0, "DMA split");
+    static_assert(BM % (8 * kWaves) == 0 || true, "");
+    static_assert(KIND == 1 || kTN % 2 == 0, "GEMM1 needs gate/up tile pairs");
+    static_assert(kLds <= 160 * 1024, "LDS");
+    static_assert((STAGES - 2) * kDma < 64, "vmcnt");
+};
+
+template <int KIND, int BM, int BN, int WM, int WN, int STAGES>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs ga) {
+    using C = BfCfg<KIND, BM, BN, WM, WN, STAGES>;
+    extern __shared__ __align__(16) uint8_t lds[];
+    int mt, nt;
+    if (!pick_tile(ga, mt, nt)) return;
+    const int4 ti = ga.tiles[mt];
+    const int seg = ti.x >> 20, g = ti.x & 0xFFFFF;
+    const int m0 = ti.y, Mg = ti.z, rbase = ti.w;
+    const SegDev S = seg == 0 ? ga.seg[0] : ga.seg[1];
+    const int N = ga.N, K = ga.K;
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int wm = wave / WN, wn = wave % WN;
+
+    // ---- DMA sources: instruction q of this wave fills tile rows 8*(wave + q*kWaves) .. +7
+    const uint8_t* src[C::kDma];
+#pragma unroll
+    for (int q = 0; q < C::kDma; ++q) {
+        const int r = 8 * (wave + q * C::kWaves) + lane / 8;      // tile row
+        const int c = (lane % 8) ^ (r & 7);                        // logical 16-byte chunk
+        const uint8_t* rowp;
+        if (r < BM) {
+            const int rr = m0 + r < Mg ? m0 + r : Mg - 1;          // clamp the ragged tail
+            rowp = (const uint8_t*)S.a + ((size_t)(rbase + rr) * K) * 2;
+        } else {
+            const int rb = r - BM;
+            int wrow;
+            if (KIND == 0)
+                wrow = rb < BN / 2 ? nt * (BN / 2) + rb : N / 2 + nt * (BN / 2) + (rb - BN / 2);
+            else
+                wrow = nt * BN + rb;
+            rowp = (const uint8_t*)S.w + ((size_t)g * N + wrow) * (size_t)K * 2;
+        }
+        src[q] = rowp + c * 16;
+    }
+    auto issue = [&](int kstep, int stage) {
+        MOE_LDS uint8_t* base = (MOE_LDS uint8_t*)lds + stage * C::kStageBytes;
+#pragma unroll
+        for (int q = 0; q < C::kDma; ++q)
+            __builtin_amdgcn_global_load_lds(
+                (const void*)(src[q] + (size_t)kstep * C::kRowBytes),
+                (MOE_LDS void*)(base + (wave + q * C::kWaves) * 1024), 16, 0, 0);
+    };
+
+    // ---- MFMA operand addresses (bytes within a stage)
+    int a_off[C::kTM], b_off[C::kTN];
+#pragma unroll
+    for (int i = 0; i < C::kTM; ++i) a_off[i] = (wm * (BM / WM) + i * 32 + lane % 32) * C::kRowBytes;
+#pragma unroll
+    for (int j = 0; j < C::kTN; ++j) {
+        int row;
+        if (KIND == 0) {
+            constexpr int half = C::kTN / 2;
+            const int col = wn * (BN / 2 / WN) + (j % half) * 32 + lane % 32;
+            row = BM + (j < half ? col : BN / 2 + col);
+        } else {
+            row = BM + wn * (BN / WN) + j * 32 + lane % 32;
+        }
+        b_off[j] = row * C::kRowBytes;
+    }
+    // physical chunk of logical chunk (kk/8 + lane/32) of a row whose (row & 7) == lane & 7
+    int chunk_off[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) chunk_off[s] = (((2 * s + lane / 32) ^ (lane & 7)) * 16);
+
+    f32x16_t acc[C::kTM][C::kTN];
+#pragma unroll
+    for (int i = 0; i < C::kTM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::kTN; ++j) acc[i][j] = f32x16_t{};
+
+    const int nk = K / C::kBK;
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s)
+        if (s < nk) issue(s, s);
+    int stage = 0;
+    for (int kt = 0; kt < nk; ++kt) {
+        if (kt + STAGES - 2 < nk) wait_vm_lgkm0<(STAGES - 2) * C::kDma>();
+        else wait_vm_lgkm0<0>();
+        block_sync();
+        {
+            const int kn = kt + STAGES - 1;
+            int sn = stage + STAGES - 1;
+            if (sn >= STAGES) sn -= STAGES;
+            if (kn < nk) issue(kn, sn);
+        }
+        const uint8_t* base = lds + stage * C::kStageBytes;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            bf16x8_t av[C::kTM], bv[C::kTN];
+#pragma unroll
+            for (int i = 0; i < C::kTM; ++i)
+                av[i] = *(const bf16x8_t*)(base + a_off[i] + chunk_off[s]);
+#pragma unroll
+            for (int j = 0; j < C::kTN; ++j)
+                bv[j] = *(const bf16x8_t*)(base + b_off[j] + chunk_off[s]);
+#pragma unroll
+            for (int i = 0; i < C::kTM; ++i)
+#pragma unroll
+                for (int j = 0; j < C::kTN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j],
+                                                                        acc[i][j], 0, 0, 0);
+        }
+        if (++stage == STAGES) stage = 0;
+    }
+
+    // epilogue. 32x32 accumulator layout: element r of lane l is
+    // row (r/4)*8 + (l/32)*4 + r%4, column l%32.
+    if (KIND == 0) {
+        constexpr int half = C::kTN / 2;
+        const int F = N / 2;
+        uint16_t* out = (uint16_t*)S.out;
+        uint16_t* zo = (uint16_t*)S.z_out;
+#pragma unroll
+        for (int i = 0; i < C::kTM; ++i) {
+#pragma unroll
+            for (int jj = 0; jj < half; ++jj) {
+                const int col = nt * (BN / 2) + wn * (BN / 2 / WN) + jj * 32 + lane % 32;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = wm * (BM / WM) + i * 32 + (r / 4) * 8 + (lane / 32) * 4 + r % 4;
+                    if (m0 + row >= Mg) continue;
+                    const size_t grow = (size_t)rbase + m0 + row;
+                    const float zg = acc[i][jj][r], zu = acc[i][half + jj][r];
+                    const float gt = S.gate ? S.gate[grow] : 1.0f;
+                    out[grow * F + col] = f32_to_bf16(gt * (silu_f32(zg) * zu));
+                    if (zo) {
+                        zo[grow * N + col] = f32_to_bf16(zg);
+                        zo[grow * N + F + col] = f32_to_bf16(zu);
+                    }
+                }
+            }
+        }
+    } else {
+        uint16_t* out = (uint16_t*)S.out;
+#pragma unroll
+        for (int i = 0; i < C::kTM; ++i) {
+#pragma unroll
+            for (int j = 0; j < C::kTN; ++j) {
+                const int col = nt * BN + wn * (BN / WN) + j * 32 + lane % 32;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = wm * (BM / WM) + i * 32 + (r / 4) * 8 + (lane / 32) * 4 + r % 4;
+                    if (m0 + row >= Mg) continue;
+                    const size_t grow = (size_t)rbase + m0 + row;
+                    out[grow * N + col] = f32_to_bf16(acc[i][j][r]);
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// fp32 kernel (FMA): 64 rows x 64 columns per 256-thread block, K in steps of 16.
+// GEMM1: the 64 columns are 32 gate + the 32 matching up columns; thread (ty, tx) computes
+// rows 4ty..4ty+3 and act columns 2tx, 2tx+1 (gate and up each).
+// GEMM2: thread computes rows 4ty..4ty+3 and columns 4tx..4tx+3.
+// ---------------------------------------------------------------------------------------
+constexpr int kF32BM = 64;
+template <int KIND>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs ga) {
+    constexpr int BM = 64, BN = 64, BK = 16;
+    __shared__ float As[BK][BM + 4];
+    __shared__ float Bs[BK][BN + 4];
+    int mt, nt;
+    if (!pick_tile(ga, mt, nt)) return;
+    const int4 ti = ga.tiles[mt];
+    const int seg = ti.x >> 20, g = ti.x & 0xFFFFF;
+    const int m0 = ti.y, Mg = ti.z, rbase = ti.w;
+    const SegDev S = seg == 0 ? ga.seg[0] : ga.seg[1];
+    const int N = ga.N, K = ga.K;
+    const int tid = threadIdx.x, tx = tid % 16, ty = tid / 16;
+    const float* A = (const float*)S.a;
+    const float* W = (const float*)S.w + (size_t)g * N * K;
+    // loader: each thread loads 4 A values and 4 B values per K step
+    const int lr = tid / 4, lk = (tid % 4) * 4;          // row 0..63, k 0,4,8,12
+    int ar = m0 + lr < Mg ? m0 + lr : Mg - 1;
+    const float* a_src = A + (size_t)(rbase + ar) * K + lk;
+    int wrow;
+    if (KIND == 0)
+        wrow = lr < 32 ? nt * 32 + lr : N / 2 + nt * 32 + (lr - 32);
+    else
+        wrow = nt * BN + lr;
+    const float* b_src = W + (size_t)wrow * K + lk;
+    float acc[4][4] = {};
+    for (int k0 = 0; k0 < K; k0 += BK) {
+        float4 av = *(const float4*)(a_src + k0);
+        float4 bv = *(const float4*)(b_src + k0);
+        As[lk + 0][lr] = av.x; As[lk + 1][lr] = av.y; As[lk + 2][lr] = av.z; As[lk + 3][lr] = av.w;
+        Bs[lk + 0][lr] = bv.x; Bs[lk + 1][lr] = bv.y; Bs[lk + 2][lr] = bv.z; Bs[lk + 3][lr] = bv.w;
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < BK; ++kk) {
+            float a[4], b[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
+            if (KIND == 0) {
+                b[0] = Bs[kk][2 * tx];
+                b[1] = Bs[kk][2 * tx + 1];
+                b[2] = Bs[kk][32 + 2 * tx];
+                b[3] = Bs[kk][32 + 2 * tx + 1];
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx * 4 + j];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+        }
+        __syncthreads();
+    }
+    float* out = (float*)S.out;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = ty * 4 + i;
+        if (m0 + row >= Mg) continue;
+        const size_t grow = (size_t)rbase + m0 + row;
+        if (KIND == 0) {
+            const int F = N / 2;
+            const float gt = S.gate ? S.gate[grow] : 1.0f;
+            float* zo = (float*)S.z_out;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int col = nt * 32 + 2 * tx + j;
+                const float zg = acc[i][j], zu = acc[i][2 + j];
+                out[grow * F + col] = gt * (silu_f32(zg) * zu);
+                if (zo) {
+                    zo[grow * N + col] = zg;
+                    zo[grow * N + F + col] = zu;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) out[grow * N + nt * BN + tx * 4 + j] = acc[i][j];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// configurations
+// ---------------------------------------------------------------------------------------
+// bf16: BM=256, BN=256 (GEMM1: 128 act columns), 8 waves as 2 (M) x 4 (N), 2 stages.
+#define MOE_BF_CFG(KIND) KIND, 256, 256, 2, 4, 2
+
+template <int KIND, int BM, int BN, int WM, int WN, int STAGES>
+hipError_t run_bf16(const GemmArgs& ga, int nblocks, hipStream_t s) {
+    using C = BfCfg<KIND, BM, BN, WM, WN, STAGES>;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(
+            (const void*)gemm_bf16_kernel<KIND, BM, BN, WM, WN, STAGES>,
+            hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::kLds);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    gemm_bf16_kernel<KIND, BM, BN, WM, WN, STAGES><<<nblocks, C::kThreads, C::kLds, s>>>(ga);
+    return hipGetLastError();
+}
+
+int bm_for(int dtype) { return dtype == 0 ? kF32BM : 256; }
+int bn_for(int kind, int dtype) { (void)kind; return dtype == 0 ? 64 : 256; }
+
+size_t max_mtiles(int max_rows_total, int groups_total, int bm) {
+    return (size_t)(max_rows_total + bm - 1) / bm + (size_t)groups_total;
+}
+
+}  // namespace
+
+GemmPlan grouped_gemm_plan(int kind, int dtype, int max_rows_total, int groups_total, int N,
+                           int K) {
+    (void)kind; (void)N; (void)K;
+    GemmPlan p;
+    p.bm = bm_for(dtype);
+    p.ws_bytes = 256 + max_mtiles(max_rows_total, groups_total, p.bm) * sizeof(int4);
+    return p;
+}
+
+hipError_t launch_grouped_gemm(int kind, int dtype, const Segment* segs, int nseg,
+                               int max_rows_total, int N, int K, void* ws, hipStream_t s) {
+    const int bm = bm_for(dtype), bn = bn_for(kind, dtype);
+    int groups_total = 0;
+    SchedArgs sa = {};
+    GemmArgs ga = {};
+    for (int i = 0; i < nseg; ++i) {
+        sa.offsets[i] = segs[i].offsets;
+        sa.groups[i] = segs[i].groups;
+        sa.rows[i] = segs[i].rows;
+        groups_total += segs[i].groups;
+        ga.seg[i] = SegDev{segs[i].a, segs[i].a_scales, segs[i].gate, segs[i].w,
+                           segs[i].w_scales, segs[i].out, segs[i].out_scales, segs[i].z_out};
+    }
+    sa.nseg = nseg;
+    int* total = (int*)ws;
+    int4* tiles = (int4*)((char*)ws + 256);
+    schedule_kernel<<<1, 1024, 0, s>>>(sa, bm, tiles, total);
+    ga.tiles = tiles;
+    ga.total = total;
+    ga.N = N;
+    ga.K = K;
+    ga.ntn = N / bn;
+    size_t mtiles = max_mtiles(max_rows_total, groups_total, bm);
+    size_t nblocks = mtiles * ga.ntn;
+    nblocks = (nblocks + 7) / 8 * 8;
+    ga.per_xcd_max = (int)(nblocks / 8);
+    if (dtype == 0) {
+        if (kind == 0) gemm_f32_kernel<0><<<(unsigned)nblocks, 256, 0, s>>>(ga);
+        else gemm_f32_kernel<1><<<(unsigned)nblocks, 256, 0, s>>>(ga);
+        return hipGetLastError();
+    }
+    if (dtype == 1) {
+        if (kind == 0) return run_bf16<MOE_BF_CFG(0)>(ga, (int)nblocks, s);
+        return run_bf16<MOE_BF_CFG(1)>(ga, (int)nblocks, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace moe

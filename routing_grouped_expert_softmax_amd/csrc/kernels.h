@@ -1,0 +1,68 @@
+// Internal launch interface between the C ABI (api.cpp) and the kernel files.
+// Every launcher enqueues on `stream`, performs no validation (the ABI has done it) and
+// returns hipGetLastError() of its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---- router ----------------------------------------------------------------------------
+hipError_t launch_router_logits(int act_dtype, const void* x, const void* w_router, int T,
+                                int H, int E, float* logits, hipStream_t s);
+
+hipError_t launch_route(int router, const float* logits, const float* logit_bias,
+                        const float* sel_bias, int T, int E, int k, int n_groups,
+                        int topk_groups, float route_scale, int32_t* topk_idx,
+                        float* topk_gate, hipStream_t s);
+
+// ---- permute ---------------------------------------------------------------------------
+constexpr int kPermChunk = 512;   // assignments per counting block
+size_t permute_ws_bytes(int T, int k, int E);
+hipError_t launch_permute(int mode /*0 f32, 1 bf16, 2 e4m3 from bf16*/, const void* x,
+                          const int32_t* topk_idx, const float* topk_gate, int T, int H,
+                          int E, int k, int32_t* counts, int32_t* offsets, int32_t* pos,
+                          int32_t* src, float* gate_perm, void* x_perm,
+                          float* x_perm_scales, void* x_q, float* x_q_scales, void* ws,
+                          hipStream_t s);
+
+// ---- combine ---------------------------------------------------------------------------
+hipError_t launch_combine(int act_dtype, const void* y_perm, const int32_t* pos,
+                          const void* shared_y, int T, int H, int k, void* y, hipStream_t s);
+
+// ---- quantise --------------------------------------------------------------------------
+hipError_t launch_quantize(const void* in, int in_dtype, int64_t n_mat, int rows, int cols,
+                           int block_rows, uint8_t* q, float* scales, hipStream_t s);
+
+// ---- grouped GEMM ----------------------------------------------------------------------
+// One expert segment of a grouped GEMM launch: `groups` groups whose rows are
+// [offsets[g], offsets[g+1]) of `a` (offsets == nullptr: one group of `rows` rows).
+struct Segment {
+    const void* a;             // [rows_total, K] activations (dtype of the launch)
+    const float* a_scales;     // e4m3: [rows_total, K/128]
+    const int32_t* offsets;    // [groups+1] device, or nullptr
+    int groups;
+    int rows;                  // rows when offsets == nullptr
+    const float* gate;         // per-row gate (GEMM1 fold), nullptr = 1
+    const void* w;             // [groups, N, K]
+    const float* w_scales;     // e4m3: [groups, N/128, K/128]
+    void* out;                 // GEMM1: act [rows, N/2]; GEMM2: y [rows, N]
+    float* out_scales;         // GEMM1 e4m3: act scales [rows, N/2/128]
+    void* z_out;               // GEMM1 optional: Z [rows, N] in the activation dtype
+};
+
+struct GemmPlan {
+    int bm;                    // M tile of the chosen kernel
+    size_t ws_bytes;           // tile-schedule workspace
+};
+
+// kind: 0 = GEMM1 (gate/up + SwiGLU * gate), 1 = GEMM2 (plain).  dtype: moe_dtype of the
+// operands (F32, BF16, E4M3). N = output columns of the GEMM before the SwiGLU pairing.
+GemmPlan grouped_gemm_plan(int kind, int dtype, int max_rows_total, int groups_total, int N,
+                           int K);
+hipError_t launch_grouped_gemm(int kind, int dtype, const Segment* segs, int nseg,
+                               int max_rows_total, int N, int K, void* ws, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,225 @@
+// Permute: group the T*k (token, slot) assignments by expert, on the device, with no host
+// synchronisation (the sync-free kernels of the technical summary "使用 Megatron Core 大规模
+// 训练混合专家模型（MoE）", section 2.4; the routing metadata -- indices and offsets -- of the
+// study notes' case 1).
+//
+//   1. count:  per chunk of kPermChunk assignments, an LDS histogram over experts.
+//   2. scan:   per expert, an exclusive scan over chunks (chunk bases) and the totals;
+//              offsets = exclusive scan of the totals; chunk bases += offsets.
+//   3. rank:   one wavefront per chunk walks its assignments in order, 64 at a time; lanes
+//              with the same expert are found with log2(E) ballots, so a row is
+//              chunk base + running count + rank among equal lanes: a stable, atomic-free
+//              counting sort (rows of an expert in ascending token order).
+//   4. copy:   one wavefront per token reads the x row once and writes it to its k rows
+//              (16-byte accesses); in e4m3 mode the row is quantised per 1 x 128 block in
+//              registers first and the codes and scales are written instead.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+__global__ __launch_bounds__(256) void perm_count_kernel(const int32_t* __restrict__ idx,
+                                                         int A, int E,
+                                                         int32_t* __restrict__ chunk_counts) {
+    extern __shared__ int32_t hist[];
+    for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
+    __syncthreads();
+    const int a0 = blockIdx.x * kPermChunk;
+    for (int a = a0 + threadIdx.x; a < a0 + kPermChunk && a < A; a += blockDim.x)
+        atomicAdd(&hist[idx[a]], 1);
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x)
+        chunk_counts[(size_t)blockIdx.x * E + e] = hist[e];
+}
+
+// Single block of 1024 threads (E <= 1024 is validated by the ABI).
+__global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t* __restrict__ chunk_counts,
+                                                         int nchunk, int E, int A,
+                                                         int32_t* __restrict__ counts,
+                                                         int32_t* __restrict__ offsets) {
+    __shared__ int32_t tot[1024];
+    __shared__ int32_t wsum[16];
+    const int e = threadIdx.x;
+    int run = 0;
+    if (e < E) {
+        for (int c = 0; c < nchunk; ++c) {
+            int v = chunk_counts[(size_t)c * E + e];
+            chunk_counts[(size_t)c * E + e] = run;
+            run += v;
+        }
+        counts[e] = run;
+    }
+    // exclusive scan of the totals over experts: wavefront inclusive scans, then wave sums
+    const int lane = e % kWave, wave = e / kWave;
+    int v = run;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        int o = __shfl_up(v, off);
+        if (lane >= off) v += o;
+    }
+    if (lane == kWave - 1) wsum[wave] = v;
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += wsum[w];
+    int excl = before + v - run;
+    tot[e] = excl;
+    if (e < E) offsets[e] = excl;
+    if (e == 0) offsets[E] = A;
+    __syncthreads();
+    if (e < E)
+        for (int c = 0; c < nchunk; ++c) chunk_counts[(size_t)c * E + e] += tot[e];
+}
+
+// One wavefront per chunk.
+__global__ __launch_bounds__(64) void perm_rank_kernel(const int32_t* __restrict__ idx,
+                                                       const float* __restrict__ gate, int A,
+                                                       int E, int k, int nbits,
+                                                       const int32_t* __restrict__ chunk_base,
+                                                       int32_t* __restrict__ pos,
+                                                       int32_t* __restrict__ src,
+                                                       float* __restrict__ gate_perm) {
+    extern __shared__ int32_t running[];
+    const int lane = threadIdx.x;
+    for (int e = lane; e < E; e += kWave) running[e] = chunk_base[(size_t)blockIdx.x * E + e];
+    __syncthreads();
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int a0 = blockIdx.x * kPermChunk;
+    for (int it = 0; it < kPermChunk; it += kWave) {
+        const int a = a0 + it + lane;
+        const bool active = a < A;
+        const int e = active ? idx[a] : 0;
+        uint64_t same = __ballot(active);
+        for (int b = 0; b < nbits; ++b) {
+            uint64_t ones = __ballot(active && ((e >> b) & 1));
+            same &= ((e >> b) & 1) ? ones : ~ones;
+        }
+        int rank = __popcll(same & lt_mask);
+        int base = active ? running[e] : 0;
+        __builtin_amdgcn_wave_barrier();
+        // the highest lane of each expert group advances that expert's running count
+        if (active && (same >> lane) == 1ull) running[e] = base + __popcll(same);
+        __builtin_amdgcn_wave_barrier();
+        if (active) {
+            int row = base + rank;
+            pos[a] = row;
+            src[row] = a / k;
+            gate_perm[row] = gate[a];
+        }
+        if (a0 + it + kWave >= A) break;
+    }
+}
+
+// Row copy: 4 tokens per 256-thread block, 16-byte chunks.
+__global__ __launch_bounds__(256) void perm_copy_kernel(const uint4* __restrict__ x,
+                                                        const int32_t* __restrict__ pos,
+                                                        int T, int row_chunks, int k,
+                                                        uint4* __restrict__ x_perm) {
+    const int lane = threadIdx.x % kWave;
+    const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+    if (t >= T) return;
+    int my_pos = lane < k ? pos[(size_t)t * k + lane] : 0;
+    const uint4* xr = x + (size_t)t * row_chunks;
+    // every lane runs every iteration so that the shuffles read active lanes only
+    for (int c0 = 0; c0 < row_chunks; c0 += kWave) {
+        const int c = c0 + lane;
+        const bool ok = c < row_chunks;
+        uint4 v = ok ? xr[c] : make_uint4(0, 0, 0, 0);
+        for (int j = 0; j < k; ++j) {
+            int r = __shfl(my_pos, j);
+            if (ok) x_perm[(size_t)r * row_chunks + c] = v;
+        }
+    }
+}
+
+// e4m3 row quantise + copy. A wavefront covers 512 columns per step: 16 lanes per
+// 128-column block, 8 bf16 values (16 bytes) per lane.
+__global__ __launch_bounds__(256) void perm_quant_copy_kernel(
+    const uint4* __restrict__ x, const int32_t* __restrict__ pos, int T, int H, int k,
+    uint2* __restrict__ x_perm, float* __restrict__ x_perm_scales, uint2* __restrict__ x_q,
+    float* __restrict__ x_q_scales) {
+    const int lane = threadIdx.x % kWave;
+    const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+    if (t >= T) return;
+    int my_pos = lane < k ? pos[(size_t)t * k + lane] : 0;
+    const int row_chunks = H / 8;
+    const int nblk = H / 128;
+    const uint4* xr = x + (size_t)t * row_chunks;
+    // every lane runs every iteration (shuffles read active lanes only); 16-lane groups
+    // stay aligned to 128-column blocks because H % 128 == 0
+    for (int c0 = 0; c0 < row_chunks; c0 += kWave) {
+        const int c = c0 + lane;
+        const bool ok = c < row_chunks;
+        uint4 v = ok ? xr[c] : make_uint4(0, 0, 0, 0);
+        float f[8];
+        uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[2 * i] = bf16_to_f32((uint16_t)(w[i] & 0xFFFFu));
+            f[2 * i + 1] = bf16_to_f32((uint16_t)(w[i] >> 16));
+        }
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+        float sc = e4m3_scale(amax);
+        uint32_t q[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = e4m3_rne_sat(f[i] / sc);
+        uint2 packed;
+        packed.x = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
+        packed.y = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
+        const int blk = c / 16;
+        const bool leader = (c % 16) == 0;
+        if (x_q && ok) {
+            x_q[(size_t)t * row_chunks + c] = packed;
+            if (leader) x_q_scales[(size_t)t * nblk + blk] = sc;
+        }
+        for (int j = 0; j < k; ++j) {
+            int r = __shfl(my_pos, j);
+            if (ok) {
+                x_perm[(size_t)r * row_chunks + c] = packed;
+                if (leader) x_perm_scales[(size_t)r * nblk + blk] = sc;
+            }
+        }
+    }
+}
+
+}  // namespace
+
+size_t permute_ws_bytes(int T, int k, int E) {
+    size_t A = (size_t)T * k;
+    size_t nchunk = (A + kPermChunk - 1) / kPermChunk;
+    return nchunk * (size_t)E * sizeof(int32_t);
+}
+
+hipError_t launch_permute(int mode, const void* x, const int32_t* topk_idx,
+                          const float* topk_gate, int T, int H, int E, int k,
+                          int32_t* counts, int32_t* offsets, int32_t* pos, int32_t* src,
+                          float* gate_perm, void* x_perm, float* x_perm_scales, void* x_q,
+                          float* x_q_scales, void* ws, hipStream_t s) {
+    const int A = T * k;
+    const int nchunk = (A + kPermChunk - 1) / kPermChunk;
+    int32_t* chunk_counts = (int32_t*)ws;
+    int nbits = 0;
+    while ((1 << nbits) < E) ++nbits;
+    perm_count_kernel<<<nchunk, 256, E * sizeof(int32_t), s>>>(topk_idx, A, E, chunk_counts);
+    perm_scan_kernel<<<1, 1024, 0, s>>>(chunk_counts, nchunk, E, A, counts, offsets);
+    perm_rank_kernel<<<nchunk, 64, E * sizeof(int32_t), s>>>(topk_idx, topk_gate, A, E, k,
+                                                             nbits, chunk_counts, pos, src,
+                                                             gate_perm);
+    const int blocks = (T + 3) / 4;
+    if (mode == 2) {
+        perm_quant_copy_kernel<<<blocks, 256, 0, s>>>((const uint4*)x, pos, T, H, k,
+                                                      (uint2*)x_perm, x_perm_scales,
+                                                      (uint2*)x_q, x_q_scales);
+    } else {
+        const int elem = mode == 0 ? 4 : 2;
+        perm_copy_kernel<<<blocks, 256, 0, s>>>((const uint4*)x, pos, T, H * elem / 16, k,
+                                                (uint4*)x_perm);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace moe

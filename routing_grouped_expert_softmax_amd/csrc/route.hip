@@ -1,0 +1,284 @@
+// Router: logits = x W_r^T, and the per-token top-k selection with gates.
+//
+// Selection follows "experts = TopK(scores, k)" of the per-token loop in the study notes
+// "Megatron-Core MoE -- 大规模稀疏专家并行实践" (案例 1). It runs one wavefront per token:
+// lane l holds the keys of experts l, l+64, l+128, ... and k rounds of a 64-bit wavefront
+// max over (order-preserving key, inverted expert index) pick the next expert, so equal keys
+// go to the lower index without any arithmetic on the keys. The router logits stay fp32 (the
+// study notes warn that low-precision router scores collapse experts, 踩过的坑).
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int kRouteWaves = 4;      // tokens per 256-thread block
+
+// ---------------------------------------------------------------------------------------
+// top-k over the keys a wavefront holds; returns, in lane j < k, the j-th expert
+// ---------------------------------------------------------------------------------------
+template <int VPL>
+MOE_DEVICE int wave_topk(uint64_t (&rk)[VPL], int k, int lane) {
+    int mine = -1;
+    for (int j = 0; j < k; ++j) {
+        uint64_t best = 0;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) best = rk[v] > best ? rk[v] : best;
+        best = wave_max_u64(best);
+        int e = rank_key_index(best);
+        if (lane == j) mine = e;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v)
+            if (v * kWave + lane == e) rk[v] = 0;   // taken
+    }
+    return mine;
+}
+
+// ---------------------------------------------------------------------------------------
+// softmax router: select on l = logit + bias; gates = softmax over the selected logits
+// ---------------------------------------------------------------------------------------
+template <int VPL>
+__global__ __launch_bounds__(256) void route_softmax_kernel(
+    const float* __restrict__ logits, const float* __restrict__ logit_bias, int T, int E,
+    int k, int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate) {
+    const int lane = threadIdx.x % kWave;
+    const int t = blockIdx.x * kRouteWaves + threadIdx.x / kWave;
+    if (t >= T) return;
+    const float* row = logits + (size_t)t * E;
+    uint64_t rk[VPL];
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+        int e = v * kWave + lane;
+        rk[v] = 0;
+        if (e < E) {
+            float l = row[e];
+            if (logit_bias) l = l + logit_bias[e];
+            rk[v] = rank_key(l, e);
+        }
+    }
+    int e = wave_topk<VPL>(rk, k, lane);
+    float l = 0.0f;
+    if (lane < k) {
+        l = row[e];
+        if (logit_bias) l = l + logit_bias[e];
+    }
+    float l0 = __shfl(l, 0);
+    float num = lane < k ? expf(l - l0) : 0.0f;
+    float den = wave_sum_f32(num);
+    if (lane < k) {
+        topk_idx[(size_t)t * k + lane] = e;
+        topk_gate[(size_t)t * k + lane] = num / den;
+    }
+}
+
+// s = fp32(1 / (1 + exp(-l))), evaluated in double and rounded once.
+MOE_DEVICE float sigmoid_rounded(float l) {
+    return (float)(1.0 / (1.0 + exp(-(double)l)));
+}
+
+// ---------------------------------------------------------------------------------------
+// sigmoid + group-limited router (DeepSeek-V3 style)
+// ---------------------------------------------------------------------------------------
+template <int VPL>
+__global__ __launch_bounds__(256) void route_sigmoid_group_kernel(
+    const float* __restrict__ logits, const float* __restrict__ logit_bias,
+    const float* __restrict__ sel_bias, int T, int E, int k, int n_groups, int topk_groups,
+    float route_scale, int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate) {
+    const int lane = threadIdx.x % kWave;
+    const int t = blockIdx.x * kRouteWaves + threadIdx.x / kWave;
+    if (t >= T) return;
+    const float* row = logits + (size_t)t * E;
+    const int per = E / n_groups;
+    float key[VPL];
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+        int e = v * kWave + lane;
+        key[v] = 0.0f;
+        if (e < E) {
+            float l = row[e];
+            if (logit_bias) l = l + logit_bias[e];
+            float s = sigmoid_rounded(l);
+            key[v] = sel_bias ? s + sel_bias[e] : s;
+        }
+    }
+    // group score = sum of the two largest keys of the group; lane g keeps group g's score
+    uint64_t my_group_rk = 0;
+    for (int g = 0; g < n_groups; ++g) {
+        uint64_t rk[VPL];
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) {
+            int e = v * kWave + lane;
+            rk[v] = (e < E && e / per == g) ? rank_key(key[v], e) : 0;
+        }
+        uint64_t b1 = 0;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) b1 = rk[v] > b1 ? rk[v] : b1;
+        b1 = wave_max_u64(b1);
+        uint64_t b2 = 0;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) {
+            uint64_t r = rk[v] == b1 ? 0 : rk[v];
+            b2 = r > b2 ? r : b2;
+        }
+        b2 = wave_max_u64(b2);
+        float score = rank_key_value(b1) + rank_key_value(b2);
+        if (lane == g) my_group_rk = rank_key(score, g);
+    }
+    // keep the topk_groups best groups; lane g learns whether group g is kept
+    int kept = 0;
+    for (int i = 0; i < topk_groups; ++i) {
+        uint64_t best = wave_max_u64(my_group_rk);
+        if (lane == rank_key_index(best)) {
+            kept = 1;
+            my_group_rk = 0;
+        }
+    }
+    uint64_t rk[VPL];
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+        int e = v * kWave + lane;
+        int g = (e < E ? e : 0) / per;
+        int keep = __shfl(kept, g);
+        rk[v] = (e < E && keep) ? rank_key(key[v], e) : 0;
+    }
+    int e = wave_topk<VPL>(rk, k, lane);
+    float s = 0.0f;
+    if (lane < k) {
+        float l = row[e];
+        if (logit_bias) l = l + logit_bias[e];
+        s = sigmoid_rounded(l);
+    }
+    float den = wave_sum_f32(s);
+    if (lane < k) {
+        topk_idx[(size_t)t * k + lane] = e;
+        topk_gate[(size_t)t * k + lane] = route_scale * s / den;
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// router GEMM, fp32 operands: logits[t, e] = sum_h x[t, h] w[e, h] (fp32 FMA)
+// One wavefront per token row; lanes stride over h, each lane keeps E partial sums in
+// chunks of 8 experts, reduced across the wavefront.
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void router_logits_f32_kernel(
+    const float* __restrict__ x, const float* __restrict__ w, int T, int H, int E,
+    float* __restrict__ logits) {
+    const int lane = threadIdx.x % kWave;
+    const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+    if (t >= T) return;
+    const float* xr = x + (size_t)t * H;
+    for (int e0 = 0; e0 < E; e0 += 8) {
+        float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        for (int h = lane; h < H; h += kWave) {
+            float xv = xr[h];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (e0 + i < E) acc[i] = fmaf(xv, w[(size_t)(e0 + i) * H + h], acc[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float v = wave_sum_f32(acc[i]);
+            if (lane == 0 && e0 + i < E) logits[(size_t)t * E + e0 + i] = v;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// router GEMM, bf16 operands on MFMA 16x16x32 (fp32 accumulate).
+// Block: 256 threads (4 waves) computes 64 tokens x 64 experts; wave w owns tokens
+// [16w, 16w+16) x all 64 experts (4 MFMA column tiles). Operands are read straight from
+// global memory (K contiguous, 16 B per lane); x is read once per 64-expert column block,
+// and w (E x H, at most a few MB) stays in L2.
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void router_logits_bf16_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int T, int H, int E,
+    float* __restrict__ logits) {
+    const int lane = threadIdx.x % kWave;
+    const int wave = threadIdx.x / kWave;
+    const int t0 = blockIdx.x * 64 + wave * 16;
+    const int e_base = blockIdx.y * 64;
+    // operand rows for this lane (clamped into range; clamped rows are not stored)
+    int tr = t0 + (lane % 16);
+    tr = tr < T ? tr : T - 1;
+    const uint16_t* xa = x + (size_t)tr * H + 8 * (lane / 16);
+    const uint16_t* wb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        int er = e_base + 16 * j + (lane % 16);
+        er = er < E ? er : E - 1;
+        wb[j] = w + (size_t)er * H + 8 * (lane / 16);
+    }
+    f32x4_t acc[4] = {};
+    for (int h = 0; h < H; h += 32) {
+        bf16x8_t a = *(const bf16x8_t*)(xa + h);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            bf16x8_t b = *(const bf16x8_t*)(wb[j] + h);
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
+        }
+    }
+    // 16x16 output: lane holds rows 4*(lane/16)+i, column lane%16
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        int e = e_base + 16 * j + (lane % 16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            int t = t0 + 4 * (lane / 16) + i;
+            if (t < T && e < E) logits[(size_t)t * E + e] = acc[j][i];
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_router_logits(int act_dtype, const void* x, const void* w_router, int T,
+                                int H, int E, float* logits, hipStream_t s) {
+    if (act_dtype == 0) {
+        router_logits_f32_kernel<<<(T + 3) / 4, 256, 0, s>>>((const float*)x,
+                                                             (const float*)w_router, T, H, E,
+                                                             logits);
+    } else {
+        dim3 grid((T + 63) / 64, (E + 63) / 64);
+        router_logits_bf16_kernel<<<grid, 256, 0, s>>>((const uint16_t*)x,
+                                                       (const uint16_t*)w_router, T, H, E,
+                                                       logits);
+    }
+    return hipGetLastError();
+}
+
+template <int VPL>
+static void route_launch(int router, const float* logits, const float* logit_bias,
+                         const float* sel_bias, int T, int E, int k, int n_groups,
+                         int topk_groups, float route_scale, int32_t* topk_idx,
+                         float* topk_gate, hipStream_t s) {
+    int blocks = (T + kRouteWaves - 1) / kRouteWaves;
+    if (router == 0)
+        route_softmax_kernel<VPL><<<blocks, 256, 0, s>>>(logits, logit_bias, T, E, k,
+                                                         topk_idx, topk_gate);
+    else
+        route_sigmoid_group_kernel<VPL><<<blocks, 256, 0, s>>>(
+            logits, logit_bias, sel_bias, T, E, k, n_groups, topk_groups, route_scale,
+            topk_idx, topk_gate);
+}
+
+hipError_t launch_route(int router, const float* logits, const float* logit_bias,
+                        const float* sel_bias, int T, int E, int k, int n_groups,
+                        int topk_groups, float route_scale, int32_t* topk_idx,
+                        float* topk_gate, hipStream_t s) {
+    int vpl = (E + kWave - 1) / kWave;
+#define MOE_ROUTE_CASE(V)                                                                   \
+    if (vpl <= V) {                                                                         \
+        route_launch<V>(router, logits, logit_bias, sel_bias, T, E, k, n_groups,            \
+                        topk_groups, route_scale, topk_idx, topk_gate, s);                  \
+        return hipGetLastError();                                                           \
+    }
+    MOE_ROUTE_CASE(1)
+    MOE_ROUTE_CASE(2)
+    MOE_ROUTE_CASE(4)
+    MOE_ROUTE_CASE(8)
+    MOE_ROUTE_CASE(16)
+#undef MOE_ROUTE_CASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace moe

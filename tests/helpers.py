@@ -1,0 +1,47 @@
+"""Shared test helpers: the error metric and the small parity workloads."""
+import numpy as np
+import torch
+
+import moe_inputs as mi
+
+TOL = {mi.F32: 1e-5, mi.BF16: 2e-2, mi.E4M3: 6e-2}
+
+
+def rel_err(got, ref) -> float:
+    """max_i |got_i - ref_i| / max_i |ref_i| over the whole checked tensor (fp64)."""
+    g = got.detach().cpu().double().numpy() if isinstance(got, torch.Tensor) else np.asarray(got, np.float64)
+    r = ref.detach().cpu().double().numpy() if isinstance(ref, torch.Tensor) else np.asarray(ref, np.float64)
+    assert g.shape == r.shape, (g.shape, r.shape)
+    den = np.max(np.abs(r))
+    return float(np.max(np.abs(g - r)) / (den if den > 0 else 1.0))
+
+
+def tol(cfg) -> float:
+    return TOL[cfg.w_dtype if cfg.w_dtype == mi.E4M3 else cfg.act_dtype]
+
+
+# Small copies of each workload: same router, dtypes and structure, sizes the oracle finishes
+# in seconds, several M and N tiles per GEMM and ragged per-expert tails.
+SMALL = {
+    "tiny_fp32": mi.CONFIGS["tiny_fp32"],
+    "mixtral_small": mi.scaled(mi.CONFIGS["mixtral_bf16"], T=1000, H=512, F=512),
+    "qwen3_small": mi.scaled(mi.CONFIGS["qwen3_bf16"], T=520, H=512, F=256),
+    "dsv3_small": mi.scaled(mi.CONFIGS["dsv3_bf16"], T=520, H=512, F=256, shared_F=256),
+    "dsv3_small_wide_shared": mi.scaled(mi.CONFIGS["dsv3_bf16"], T=300, H=256, F=128,
+                                        shared_F=384),
+}
+
+
+def to_dev(t):
+    return None if t is None else t.cuda()
+
+
+def sample_rows(offsets, extra_per_group=1, seed=0):
+    """First, last and a random row of every non-empty group."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    for e in range(len(offsets) - 1):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if b > a:
+            rows += [a, b - 1] + list(rng.integers(a, b, extra_per_group))
+    return np.unique(np.array(rows, np.int64))

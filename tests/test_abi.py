@@ -1,0 +1,137 @@
+"""The C-ABI library loads on a host without a GPU, exports every entry point include/moe.h
+declares, sizes workspaces on the host and rejects invalid arguments before launching
+anything (no call here reaches a kernel)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import moe_inputs as mi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def moe():
+    import routing_grouped_expert_softmax_amd as m
+    return m
+
+
+def test_exports_every_declared_symbol(moe):
+    names = header_functions()
+    assert "moe_layer_forward" in names and len(names) >= 10
+    for n in names:
+        assert hasattr(moe.lib(), n), n
+    assert sorted(moe.EXPORTED) == names
+
+
+def test_status_strings(moe):
+    for s in range(5):
+        assert moe.status_string(s).startswith("MOE_")
+    assert "unknown" in moe.status_string(99)
+
+
+def cfgc(moe, base="dsv3_bf16", **kw):
+    return moe.make_config(mi.CONFIGS[base].replace(**kw))
+
+
+def ws_size(moe, c, op):
+    n = C.c_size_t(0)
+    st = moe.lib().moe_workspace_size(C.byref(c), op, C.byref(n))
+    return st, n.value
+
+
+def test_workspace_sizes_on_host(moe):
+    for name, cfg in mi.CONFIGS.items():
+        if cfg.w_dtype == mi.E4M3:
+            continue
+        c = moe.make_config(cfg)
+        st, p = ws_size(moe, c, moe.OP_PERMUTE)
+        assert st == 0 and p > 0
+        st, g = ws_size(moe, c, moe.OP_GROUPED_GEMM)
+        assert st == 0 and g > 0
+        st, l = ws_size(moe, c, moe.OP_LAYER_FORWARD)
+        assert st == 0
+        # the layer workspace holds x_perm and y_perm (A x H each) at least
+        eb = 4 if cfg.act_dtype == mi.F32 else 2
+        assert l >= 2 * cfg.T * cfg.k * cfg.H * eb
+    c = cfgc(moe)
+    assert ws_size(moe, c, 17)[0] == 1
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=0), 1), (dict(k=300), 1), (dict(E=2048, k=8, n_groups=8), 2),
+    (dict(H=7000), 2), (dict(F=2000), 2), (dict(n_groups=7), 1), (dict(topk_groups=9), 1),
+    (dict(router=5), 1), (dict(route_scale=0.0), 1), (dict(act_dtype=mi.F32), 2),
+    (dict(act_dtype=7), 1), (dict(k=33, E=256), 2), (dict(n_groups=128, topk_groups=64), 2),
+])
+def test_invalid_configs_rejected(moe, kw, status):
+    c = cfgc(moe, **kw)
+    assert ws_size(moe, c, moe.OP_LAYER_FORWARD)[0] == status
+    # every entry point runs the same check first and launches nothing
+    L = moe.lib()
+    dummy = C.c_void_p(16)
+    assert L.moe_route(C.byref(c), dummy, None, None, dummy, dummy, None) == status
+    assert L.moe_unpermute_combine(C.byref(c), dummy, dummy, None, dummy, None) == status
+
+
+def test_softmax_router_rejects_groups(moe):
+    c = cfgc(moe, "qwen3_bf16", n_groups=2, topk_groups=1)
+    assert ws_size(moe, c, moe.OP_PERMUTE)[0] == 1
+
+
+def test_null_pointers_rejected(moe):
+    L = moe.lib()
+    c = cfgc(moe)
+    d = C.c_void_p(16)
+    assert L.moe_router_logits(C.byref(c), None, d, d, None) == 1
+    assert L.moe_route(C.byref(c), None, None, None, d, d, None) == 1
+    assert L.moe_permute(C.byref(c), d, d, d, d, d, d, d, d, None, None, None, None, d,
+                         1 << 40, None) == 1
+    assert L.moe_unpermute_combine(C.byref(c), None, d, None, d, None) == 1
+    assert L.moe_layer_forward(C.byref(c), d, None, None, None, None, d, None, d, None, d,
+                               None, d, None, d, None, None, None, None, d, 1 << 40, None) == 1
+    assert L.moe_workspace_size(C.byref(c), 0, None) == 1
+    assert L.moe_quantize_e4m3(None, 1, 1, 128, 128, 1, 128, d, d, None) == 1
+
+
+def test_workspace_too_small_rejected(moe):
+    L = moe.lib()
+    c = cfgc(moe)
+    d = C.c_void_p(16)
+    st, need = ws_size(moe, c, moe.OP_PERMUTE)
+    assert L.moe_permute(C.byref(c), d, d, d, d, d, d, d, d, d, None, None, None, d,
+                         need - 1, None) == 3
+    st, need = ws_size(moe, c, moe.OP_LAYER_FORWARD)
+    assert L.moe_layer_forward(C.byref(c), d, d, None, None, None, d, None, d, None, d, None,
+                               d, None, d, None, None, None, None, d, need - 1, None) == 3
+
+
+def test_scale_pointer_consistency(moe):
+    L = moe.lib()
+    d = C.c_void_p(16)
+    c = cfgc(moe)                                   # bf16: scales must be NULL
+    st, need = ws_size(moe, c, moe.OP_PERMUTE)
+    assert L.moe_permute(C.byref(c), d, d, d, d, d, d, d, d, d, d, None, None, d, need,
+                         None) == 1
+    c8 = cfgc(moe, w_dtype=mi.E4M3)                 # e4m3: x_perm scales required
+    st, need8 = ws_size(moe, c8, moe.OP_PERMUTE)
+    assert L.moe_permute(C.byref(c8), d, d, d, d, d, d, d, d, d, None, None, None, d, need8,
+                         None) == 1
+
+
+def test_quantize_argument_checks(moe):
+    L = moe.lib()
+    d = C.c_void_p(16)
+    assert L.moe_quantize_e4m3(d, 1, 1, 128, 100, 1, 128, d, d, None) == 1
+    assert L.moe_quantize_e4m3(d, 1, 1, 100, 128, 128, 128, d, d, None) == 1
+    assert L.moe_quantize_e4m3(d, 1, 1, 128, 128, 64, 128, d, d, None) == 2
+    assert L.moe_quantize_e4m3(d, 5, 1, 128, 128, 1, 128, d, d, None) == 1

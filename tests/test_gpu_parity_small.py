@@ -1,0 +1,174 @@
+"""GPU path vs the CPU oracle, element by element, on small copies of every workload
+(several tiles per GEMM, ragged per-expert tails). All calls go through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+import oracle
+from helpers import SMALL, rel_err, tol, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def moe():
+    import routing_grouped_expert_softmax_amd as m
+    return m
+
+
+_CACHE = {}
+
+
+def case(name):
+    """Inputs and the oracle's routing / permutation of one small workload."""
+    if name in _CACHE:
+        return _CACHE[name]
+    cfg = SMALL[name]
+    inp = mi.make_inputs(cfg)
+    logits = oracle.router_logits(inp.x, inp.w_router)
+    lb = None if inp.logit_bias is None else inp.logit_bias.numpy()
+    sb = None if inp.sel_bias is None else inp.sel_bias.numpy()
+    idx, gate = oracle.route_cfg(cfg, logits, lb, sb)
+    perm = oracle.permute(idx, gate, cfg.E)
+    c = dict(cfg=cfg, inp=inp, logits=logits, idx=idx, gate=gate, perm=perm)
+    _CACHE[name] = c
+    return c
+
+
+NAMES = list(SMALL)
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_router_logits(moe, name):
+    c = case(name)
+    cfg, inp = c["cfg"], c["inp"]
+    print(f"[router_logits] {name}", flush=True)
+    got = moe.router_logits(cfg, inp.x.cuda(), inp.w_router.cuda())
+    torch.cuda.synchronize()
+    assert rel_err(got, c["logits"]) <= 1e-5
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_route_bit_exact_on_oracle_logits(moe, name):
+    c = case(name)
+    cfg, inp = c["cfg"], c["inp"]
+    print(f"[route] {name}", flush=True)
+    idx, gate = moe.route(cfg, torch.from_numpy(c["logits"]).cuda(), to_dev(inp.logit_bias),
+                          to_dev(inp.sel_bias))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(idx.cpu().numpy(), c["idx"])
+    np.testing.assert_allclose(gate.cpu().numpy(), c["gate"], rtol=1e-6, atol=0)
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_permute_bit_exact(moe, name):
+    c = case(name)
+    cfg, inp, perm = c["cfg"], c["inp"], c["perm"]
+    print(f"[permute] {name}", flush=True)
+    out = moe.permute(cfg, inp.x.cuda(), torch.from_numpy(c["idx"]).cuda(),
+                      torch.from_numpy(c["gate"]).cuda())
+    torch.cuda.synchronize()
+    for key in ("counts", "offsets", "pos", "src"):
+        np.testing.assert_array_equal(out[key].cpu().numpy(), perm[key], err_msg=key)
+    np.testing.assert_array_equal(out["gate_perm"].cpu().numpy(), perm["gate_perm"])
+    x_ref = oracle.gather_rows(oracle.as_np(inp.x)[0], perm["pos"])
+    np.testing.assert_array_equal(oracle.as_np(out["x_perm"].cpu())[0], x_ref)
+
+
+def oracle_x_perm(c):
+    x_np = oracle.as_np(c["inp"].x)[0]
+    xp = oracle.gather_rows(x_np, c["perm"]["pos"])
+    return torch.from_numpy(xp.view(np.int16)).view(torch.bfloat16) if xp.dtype == np.uint16 \
+        else torch.from_numpy(xp)
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_grouped_gemm(moe, name):
+    c = case(name)
+    cfg, inp, perm = c["cfg"], c["inp"], c["perm"]
+    print(f"[grouped_gemm] {name}", flush=True)
+    xp = oracle_x_perm(c)
+    sh = dict(x_shared=inp.x.cuda(), ws13=inp.ws13.cuda(), ws2=inp.ws2.cuda()) if cfg.shared_F else {}
+    out = moe.grouped_gemm_swiglu(cfg, xp.cuda(), torch.from_numpy(perm["offsets"]).cuda(),
+                                  torch.from_numpy(perm["gate_perm"]).cuda(), inp.w13.cuda(),
+                                  inp.w2.cuda(), save_z=True, **sh)
+    torch.cuda.synchronize()
+    rows = np.arange(cfg.A)
+    z_ref, act_ref, y_ref = oracle.expert_rows(xp, perm["offsets"], perm["gate_perm"], inp.w13,
+                                               inp.w2, rows, want_z=True)
+    t = tol(cfg)
+    assert rel_err(out["act"], act_ref) <= t
+    assert rel_err(out["y_perm"], y_ref) <= t
+    assert rel_err(out["z"], z_ref) <= t
+    if cfg.shared_F:
+        _, _, ys = oracle.expert_rows(inp.x, None, None, inp.ws13, inp.ws2, np.arange(cfg.T))
+        assert rel_err(out["shared_y"], ys) <= t
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_combine(moe, name):
+    c = case(name)
+    cfg, perm = c["cfg"], c["perm"]
+    print(f"[combine] {name}", flush=True)
+    g = torch.Generator().manual_seed(5)
+    dt = moe.act_torch_dtype(cfg)
+    yp = torch.randn(cfg.A, cfg.H, generator=g).to(dt)
+    sh = torch.randn(cfg.T, cfg.H, generator=g).to(dt) if cfg.shared_F else None
+    y = moe.unpermute_combine(cfg, yp.cuda(), torch.from_numpy(perm["pos"]).cuda(), to_dev(sh))
+    torch.cuda.synchronize()
+    ref = oracle.combine(yp, perm["pos"], sh)
+    # one rounding of an fp32 sum to the output dtype
+    bound = 1e-6 if cfg.act_dtype == mi.F32 else 2.0 ** -8
+    assert rel_err(y, ref) <= bound
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_layer_forward_on_oracle_logits(moe, name):
+    c = case(name)
+    cfg, inp = c["cfg"], c["inp"]
+    print(f"[layer_forward logits_in] {name}", flush=True)
+    y, ex = moe.layer_forward(cfg, inp.x.cuda(), inp.w_router.cuda(), inp.w13.cuda(),
+                              inp.w2.cuda(), to_dev(inp.logit_bias), to_dev(inp.sel_bias),
+                              torch.from_numpy(c["logits"]).cuda(), ws13=to_dev(inp.ws13),
+                              ws2=to_dev(inp.ws2), want=("topk_idx", "counts"))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(ex["topk_idx"].cpu().numpy(), c["idx"])
+    np.testing.assert_array_equal(ex["counts"].cpu().numpy(), c["perm"]["counts"])
+    ref = oracle.layer_tokens(inp.x, c["idx"], c["gate"], inp.w13, inp.w2, np.arange(cfg.T),
+                              inp.ws13, inp.ws2)
+    assert rel_err(y, ref) <= tol(cfg)
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_layer_forward_full_gpu_path(moe, name):
+    """Router GEMM on the GPU too. Tokens whose expert set differs from the oracle's must
+    sit on a near-tie of the routing key; the rest must match the oracle."""
+    c = case(name)
+    cfg, inp = c["cfg"], c["inp"]
+    print(f"[layer_forward full] {name}", flush=True)
+    y, ex = moe.layer_forward(cfg, inp.x.cuda(), inp.w_router.cuda(), inp.w13.cuda(),
+                              inp.w2.cuda(), to_dev(inp.logit_bias), to_dev(inp.sel_bias),
+                              ws13=to_dev(inp.ws13), ws2=to_dev(inp.ws2),
+                              want=("topk_idx", "logits"))
+    torch.cuda.synchronize()
+    gi = ex["topk_idx"].cpu().numpy()
+    same = np.all(np.sort(gi, 1) == np.sort(c["idx"], 1), axis=1)
+    assert same.mean() > 0.99
+    toks = np.nonzero(same)[0]
+    ref = oracle.layer_tokens(inp.x, c["idx"], c["gate"], inp.w13, inp.w2, toks, inp.ws13,
+                              inp.ws2)
+    assert rel_err(y.cpu()[toks], ref) <= tol(cfg)
+
+
+@pytest.mark.parametrize("name", ["dsv3_small", "tiny_fp32"])
+def test_deterministic(moe, name):
+    c = case(name)
+    cfg, inp = c["cfg"], c["inp"]
+    args = (cfg, inp.x.cuda(), inp.w_router.cuda(), inp.w13.cuda(), inp.w2.cuda(),
+            to_dev(inp.logit_bias), to_dev(inp.sel_bias))
+    kw = dict(ws13=to_dev(inp.ws13), ws2=to_dev(inp.ws2))
+    y1, _ = moe.layer_forward(*args, **kw)
+    y2, _ = moe.layer_forward(*args, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)

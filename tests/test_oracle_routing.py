@@ -208,3 +208,24 @@ def test_routing_event_count_from_the_pages():
     perm = oracle.permute(idx, gate, 8)
     assert int(perm["counts"].sum()) == events
     assert int(perm["offsets"][-1]) == events
+
+
+def test_combine_inverts_the_permutation():
+    """Combining the permuted copy of x (every row an identical expert output) gives k x."""
+    rng = np.random.default_rng(12)
+    T, E, k, H = 50, 16, 3, 24
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    idx, gate = oracle.route(lg, k)
+    perm = oracle.permute(idx, gate, E)
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    xp = oracle.gather_rows(x, perm["pos"])
+    np.testing.assert_array_equal(oracle.combine(xp, perm["pos"]), k * x.astype(np.float64))
+    sh = rng.standard_normal((T, H)).astype(np.float32)
+    np.testing.assert_allclose(oracle.combine(xp, perm["pos"], sh), k * x.astype(np.float64) + sh,
+                               rtol=1e-15)
+    # rows of expert e are the tokens routed to e, in ascending token order
+    for e in range(E):
+        rows = np.arange(perm["offsets"][e], perm["offsets"][e + 1])
+        toks = perm["src"][rows]
+        assert np.all(np.diff(toks) > 0)
+        assert set(toks) == set(np.nonzero((idx == e).any(1))[0])
