@@ -156,6 +156,28 @@ int moe_grouped_gemm_swiglu(const moe_config* cfg, const void* x_perm,
                             void* y_perm, void* shared_y, void* z_out, void* ws,
                             size_t ws_bytes, hipStream_t stream);
 
+/* The two halves of moe_grouped_gemm_swiglu as separate calls (same arguments and
+ * layouts), for callers that schedule or time them apart -- e.g. the data- and
+ * weight-gradient split of a backward.
+ * moe_grouped_gemm_up:   act (and optionally z_out) from x_perm and w13; with a shared
+ *                        expert, shared_act [T, shared_F] (+ shared_act_scales
+ *                        [T, shared_F/128] in e4m3 mode) from x_shared and ws13.
+ * moe_grouped_gemm_down: y_perm from act and w2; with a shared expert, shared_y from
+ *                        shared_act and ws2.
+ * Both need a workspace of moe_workspace_size(cfg, MOE_OP_GROUPED_GEMM) bytes. */
+int moe_grouped_gemm_up(const moe_config* cfg, const void* x_perm, const float* x_perm_scales,
+                        const int32_t* offsets, const float* gate_perm, const void* w13,
+                        const float* w13_scales, const void* x_shared,
+                        const float* x_shared_scales, const void* ws13,
+                        const float* ws13_scales, void* act, float* act_scales,
+                        void* shared_act, float* shared_act_scales, void* z_out, void* ws,
+                        size_t ws_bytes, hipStream_t stream);
+int moe_grouped_gemm_down(const moe_config* cfg, const void* act, const float* act_scales,
+                          const int32_t* offsets, const void* w2, const float* w2_scales,
+                          const void* shared_act, const float* shared_act_scales,
+                          const void* ws2, const float* ws2_scales, void* y_perm,
+                          void* shared_y, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Unpermute / combine: y[t, :] = sum_{j<k} y_perm[pos[t*k+j], :] (+ shared_y[t, :]),
  * summed in fp32 in slot order and rounded once to cfg->act_dtype. The gates were folded
  * in before the down projection, so no weight is applied here. A gather: no atomics.

@@ -25,7 +25,7 @@ OP_PERMUTE, OP_GROUPED_GEMM, OP_LAYER_FORWARD, OP_GROUPED_GEMM_BWD = 0, 1, 2, 3
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is missing: build it with `python -m routing_grouped_expert_softmax_amd.build`"
+        f"{LIB_PATH} is missing: build it with `python routing_grouped_expert_softmax_amd/build.py`"
         " (there is no fallback path)")
 
 
@@ -58,6 +58,8 @@ _SIGS = {
     "moe_permute": [CFG, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
     "moe_grouped_gemm_swiglu": [CFG, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P,
                                 P, SZ, P],
+    "moe_grouped_gemm_up": [CFG, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
+    "moe_grouped_gemm_down": [CFG, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
     "moe_unpermute_combine": [CFG, P, P, P, P, P],
     "moe_layer_forward": [CFG, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
     "moe_grouped_gemm_swiglu_bwd": [CFG, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
@@ -236,6 +238,60 @@ def grouped_gemm_swiglu(cfg, x_perm, offsets, gate_perm, w13, w2, x_perm_scales=
         _ptr(out["act"]), _ptr(out["act_scales"]), _ptr(out["y_perm"]), _ptr(out["shared_y"]),
         _ptr(out["z"]), _ptr(ws), ws.numel(), _stream(stream)))
     return out
+
+
+def grouped_gemm_up(cfg, x_perm, offsets, gate_perm, w13, act, x_perm_scales=None,
+                    w13_scales=None, x_shared=None, x_shared_scales=None, ws13=None,
+                    ws13_scales=None, act_scales=None, shared_act=None,
+                    shared_act_scales=None, z=None, ws=None, stream=None):
+    """GEMM1 (gate/up + SwiGLU, gate folded in) into caller-provided outputs."""
+    T, H, E, k, F = cfg.T, cfg.H, cfg.E, cfg.k, cfg.F
+    A = T * k
+    gd, ad = gemm_torch_dtype(cfg), act_torch_dtype(cfg)
+    sF = cfg.shared_F
+    if ws is None:
+        ws = workspace(cfg, OP_GROUPED_GEMM, x_perm.device)
+    c = make_config(cfg)
+    _check("moe_grouped_gemm_up", _lib.moe_grouped_gemm_up(
+        C.byref(c), _ptr(x_perm, gd, (A, H), "x_perm"),
+        _ptr(x_perm_scales, torch.float32, (A, H // 128), "x_perm_scales"),
+        _ptr(offsets, torch.int32, (E + 1,), "offsets"),
+        _ptr(gate_perm, torch.float32, (A,), "gate_perm"),
+        _ptr(w13, gd, (E, 2 * F, H), "w13"),
+        _ptr(w13_scales, torch.float32, (E, 2 * F // 128, H // 128), "w13_scales"),
+        _ptr(x_shared, gd, (T, H), "x_shared"),
+        _ptr(x_shared_scales, torch.float32, (T, H // 128), "x_shared_scales"),
+        _ptr(ws13, gd, (2 * sF, H), "ws13"),
+        _ptr(ws13_scales, torch.float32, (2 * sF // 128, H // 128), "ws13_scales"),
+        _ptr(act, gd, (A, F), "act"), _ptr(act_scales, torch.float32, (A, F // 128), "act_scales"),
+        _ptr(shared_act, gd, (T, sF), "shared_act"),
+        _ptr(shared_act_scales, torch.float32, (T, sF // 128), "shared_act_scales"),
+        _ptr(z, ad, (A, 2 * F), "z"), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def grouped_gemm_down(cfg, act, offsets, w2, y_perm, act_scales=None, w2_scales=None,
+                      shared_act=None, shared_act_scales=None, ws2=None, ws2_scales=None,
+                      shared_y=None, ws=None, stream=None):
+    """GEMM2 (down projection) into caller-provided outputs."""
+    T, H, E, k, F = cfg.T, cfg.H, cfg.E, cfg.k, cfg.F
+    A = T * k
+    gd, ad = gemm_torch_dtype(cfg), act_torch_dtype(cfg)
+    sF = cfg.shared_F
+    if ws is None:
+        ws = workspace(cfg, OP_GROUPED_GEMM, act.device)
+    c = make_config(cfg)
+    _check("moe_grouped_gemm_down", _lib.moe_grouped_gemm_down(
+        C.byref(c), _ptr(act, gd, (A, F), "act"),
+        _ptr(act_scales, torch.float32, (A, F // 128), "act_scales"),
+        _ptr(offsets, torch.int32, (E + 1,), "offsets"),
+        _ptr(w2, gd, (E, H, F), "w2"),
+        _ptr(w2_scales, torch.float32, (E, H // 128, F // 128), "w2_scales"),
+        _ptr(shared_act, gd, (T, sF), "shared_act"),
+        _ptr(shared_act_scales, torch.float32, (T, sF // 128), "shared_act_scales"),
+        _ptr(ws2, gd, (H, sF), "ws2"),
+        _ptr(ws2_scales, torch.float32, (H // 128, sF // 128), "ws2_scales"),
+        _ptr(y_perm, ad, (A, H), "y_perm"), _ptr(shared_y, ad, (T, H), "shared_y"),
+        _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def unpermute_combine(cfg, y_perm, pos, shared_y=None, y=None, stream=None):

@@ -1,5 +1,6 @@
 """Build libmoe_amd.so from the HIP sources for gfx950 (hipcc, one object per source,
-compiled in parallel, then linked). Run as `python -m routing_grouped_expert_softmax_amd.build`.
+compiled in parallel, then linked). Run as `python routing_grouped_expert_softmax_amd/build.py`
+(by path: importing the package itself loads the built library).
 """
 from __future__ import annotations
 

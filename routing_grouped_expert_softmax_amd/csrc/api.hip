@@ -63,14 +63,9 @@ struct Carve {
     }
 };
 
+size_t sched_ws_bytes(const moe_config* c);
+
 size_t gemm_ws_bytes(const moe_config* c) {
-    const int dt = c->w_dtype;
-    const int A = c->T * c->k;
-    const int seg_groups = c->E + (c->shared_F ? 1 : 0);
-    const int rows = A + (c->shared_F ? c->T : 0);
-    size_t s1 = moe::grouped_gemm_plan(0, dt, rows, seg_groups, 2 * c->F, c->H).ws_bytes;
-    size_t s2 = moe::grouped_gemm_plan(1, dt, rows, seg_groups, c->H, c->F).ws_bytes;
-    size_t sched = align_up(s1 > s2 ? s1 : s2);
     size_t shared = 0;
     if (c->shared_F) {
         const size_t eb = c->w_dtype == MOE_E4M3 ? 1 : elem_bytes(c->act_dtype);
@@ -78,7 +73,7 @@ size_t gemm_ws_bytes(const moe_config* c) {
         if (c->w_dtype == MOE_E4M3)
             shared += align_up((size_t)c->T * (c->shared_F / 128) * 4);      // its scales
     }
-    return sched + shared;
+    return align_up(sched_ws_bytes(c)) + shared;
 }
 
 struct LayerWs {
@@ -132,7 +127,69 @@ LayerWs carve_layer(const moe_config* c, void* ws) {
     return L;
 }
 
-// The grouped GEMMs of the experts (routed, then the shared expert as a second segment).
+size_t sched_ws_bytes(const moe_config* c) {
+    const int dt = c->w_dtype;
+    const int seg_groups = c->E + (c->shared_F ? 1 : 0);
+    const int rows = c->T * c->k + (c->shared_F ? c->T : 0);
+    size_t s1 = moe::grouped_gemm_plan(0, dt, rows, seg_groups, 2 * c->F, c->H).ws_bytes;
+    size_t s2 = moe::grouped_gemm_plan(1, dt, rows, seg_groups, c->H, c->F).ws_bytes;
+    return s1 > s2 ? s1 : s2;
+}
+
+// GEMM1 of the experts (gate/up projection + SwiGLU with the gate folded in): routed
+// experts as segment 0 and, when shared_F == F, the shared expert as segment 1 of the same
+// launch; a shared expert of another width gets its own launch.
+int run_up(const moe_config* c, const void* x_perm, const float* x_perm_scales,
+           const int32_t* offsets, const float* gate_perm, const void* w13,
+           const float* w13_scales, const void* x_shared, const float* x_shared_scales,
+           const void* ws13, const float* ws13_scales, void* act, float* act_scales,
+           void* shared_act, float* shared_act_scales, void* z_out, void* sched,
+           hipStream_t stream) {
+    const int dt = c->w_dtype;
+    const int A = c->T * c->k;
+    Segment r1 = {x_perm, x_perm_scales, offsets, c->E, 0, gate_perm, w13, w13_scales,
+                  act, act_scales, z_out};
+    Segment s1 = {x_shared, x_shared_scales, nullptr, 1, c->T, nullptr, ws13, ws13_scales,
+                  shared_act, shared_act_scales, nullptr};
+    if (!c->shared_F)
+        return hip_status(moe::launch_grouped_gemm(0, dt, &r1, 1, A, 2 * c->F, c->H, sched, stream));
+    if (c->shared_F == c->F) {
+        Segment g[2] = {r1, s1};
+        return hip_status(moe::launch_grouped_gemm(0, dt, g, 2, A + c->T, 2 * c->F, c->H, sched,
+                                                   stream));
+    }
+    hipError_t e = moe::launch_grouped_gemm(0, dt, &r1, 1, A, 2 * c->F, c->H, sched, stream);
+    if (e == hipSuccess)
+        e = moe::launch_grouped_gemm(0, dt, &s1, 1, c->T, 2 * c->shared_F, c->H, sched, stream);
+    return hip_status(e);
+}
+
+// GEMM2 of the experts (down projection), same segment layout as run_up.
+int run_down(const moe_config* c, const void* act, const float* act_scales,
+             const int32_t* offsets, const void* w2, const float* w2_scales,
+             const void* shared_act, const float* shared_act_scales, const void* ws2,
+             const float* ws2_scales, void* y_perm, void* shared_y, void* sched,
+             hipStream_t stream) {
+    const int dt = c->w_dtype;
+    const int A = c->T * c->k;
+    Segment r2 = {act, act_scales, offsets, c->E, 0, nullptr, w2, w2_scales, y_perm, nullptr,
+                  nullptr};
+    Segment s2 = {shared_act, shared_act_scales, nullptr, 1, c->T, nullptr, ws2, ws2_scales,
+                  shared_y, nullptr, nullptr};
+    if (!c->shared_F)
+        return hip_status(moe::launch_grouped_gemm(1, dt, &r2, 1, A, c->H, c->F, sched, stream));
+    if (c->shared_F == c->F) {
+        Segment g[2] = {r2, s2};
+        return hip_status(moe::launch_grouped_gemm(1, dt, g, 2, A + c->T, c->H, c->F, sched,
+                                                   stream));
+    }
+    hipError_t e = moe::launch_grouped_gemm(1, dt, &r2, 1, A, c->H, c->F, sched, stream);
+    if (e == hipSuccess)
+        e = moe::launch_grouped_gemm(1, dt, &s2, 1, c->T, c->H, c->shared_F, sched, stream);
+    return hip_status(e);
+}
+
+// Both GEMMs; the shared expert's activation lives in the workspace after the schedule.
 int run_experts(const moe_config* c, const void* x_perm, const float* x_perm_scales,
                 const int32_t* offsets, const float* gate_perm, const void* w13,
                 const float* w13_scales, const void* w2, const float* w2_scales,
@@ -140,54 +197,21 @@ int run_experts(const moe_config* c, const void* x_perm, const float* x_perm_sca
                 const float* ws13_scales, const void* ws2, const float* ws2_scales, void* act,
                 float* act_scales, void* y_perm, void* shared_y, void* z_out, void* ws,
                 hipStream_t stream) {
-    const int dt = c->w_dtype;
-    const int A = c->T * c->k;
-    // scratch: tile schedule, then the shared expert's activation (+ scales)
-    const int seg_groups = c->E + (c->shared_F ? 1 : 0);
-    const int rows = A + (c->shared_F ? c->T : 0);
-    size_t s1 = moe::grouped_gemm_plan(0, dt, rows, seg_groups, 2 * c->F, c->H).ws_bytes;
-    size_t s2 = moe::grouped_gemm_plan(1, dt, rows, seg_groups, c->H, c->F).ws_bytes;
     Carve cv(ws);
-    void* sched = cv.take(s1 > s2 ? s1 : s2);
+    void* sched = cv.take(sched_ws_bytes(c));
     void* sh_act = nullptr;
     float* sh_act_scales = nullptr;
     if (c->shared_F) {
-        const size_t eb = dt == MOE_E4M3 ? 1 : elem_bytes(c->act_dtype);
-        sh_act = cv.take((size_t)c->T * c->shared_F * eb);
-        if (dt == MOE_E4M3) sh_act_scales = (float*)cv.take((size_t)c->T * (c->shared_F / 128) * 4);
+        const bool fp8 = c->w_dtype == MOE_E4M3;
+        sh_act = cv.take((size_t)c->T * c->shared_F * (fp8 ? 1 : elem_bytes(c->act_dtype)));
+        if (fp8) sh_act_scales = (float*)cv.take((size_t)c->T * (c->shared_F / 128) * 4);
     }
-    Segment r1 = {x_perm, x_perm_scales, offsets, c->E, 0, gate_perm, w13, w13_scales,
-                  act, act_scales, z_out};
-    Segment r2 = {act, act_scales, offsets, c->E, 0, nullptr, w2, w2_scales, y_perm, nullptr,
-                  nullptr};
-    const bool fused_shared = c->shared_F == c->F;
-    if (!c->shared_F || fused_shared) {
-        Segment g1[2] = {r1, {}}, g2[2] = {r2, {}};
-        int nseg = 1;
-        if (c->shared_F) {
-            g1[1] = Segment{x_shared, x_shared_scales, nullptr, 1, c->T, nullptr, ws13,
-                            ws13_scales, sh_act, sh_act_scales, nullptr};
-            g2[1] = Segment{sh_act, sh_act_scales, nullptr, 1, c->T, nullptr, ws2, ws2_scales,
-                            shared_y, nullptr, nullptr};
-            nseg = 2;
-        }
-        hipError_t e = moe::launch_grouped_gemm(0, dt, g1, nseg, rows, 2 * c->F, c->H, sched, stream);
-        if (e == hipSuccess)
-            e = moe::launch_grouped_gemm(1, dt, g2, nseg, rows, c->H, c->F, sched, stream);
-        return hip_status(e);
-    }
-    // shared expert of another width: its own launches
-    hipError_t e = moe::launch_grouped_gemm(0, dt, &r1, 1, A, 2 * c->F, c->H, sched, stream);
-    if (e == hipSuccess) e = moe::launch_grouped_gemm(1, dt, &r2, 1, A, c->H, c->F, sched, stream);
-    Segment s1g = {x_shared, x_shared_scales, nullptr, 1, c->T, nullptr, ws13, ws13_scales,
-                   sh_act, sh_act_scales, nullptr};
-    Segment s2g = {sh_act, sh_act_scales, nullptr, 1, c->T, nullptr, ws2, ws2_scales, shared_y,
-                   nullptr, nullptr};
-    if (e == hipSuccess)
-        e = moe::launch_grouped_gemm(0, dt, &s1g, 1, c->T, 2 * c->shared_F, c->H, sched, stream);
-    if (e == hipSuccess)
-        e = moe::launch_grouped_gemm(1, dt, &s2g, 1, c->T, c->H, c->shared_F, sched, stream);
-    return hip_status(e);
+    int st = run_up(c, x_perm, x_perm_scales, offsets, gate_perm, w13, w13_scales, x_shared,
+                    x_shared_scales, ws13, ws13_scales, act, act_scales, sh_act, sh_act_scales,
+                    z_out, sched, stream);
+    if (st) return st;
+    return run_down(c, act, act_scales, offsets, w2, w2_scales, sh_act, sh_act_scales, ws2,
+                    ws2_scales, y_perm, shared_y, sched, stream);
 }
 
 }  // namespace
@@ -288,6 +312,64 @@ int moe_grouped_gemm_swiglu(const moe_config* cfg, const void* x_perm,
     return run_experts(cfg, x_perm, x_perm_scales, offsets, gate_perm, w13, w13_scales, w2,
                        w2_scales, x_shared, x_shared_scales, ws13, ws13_scales, ws2,
                        ws2_scales, act, act_scales, y_perm, shared_y, z_out, ws, stream);
+}
+
+static int check_gemm_dtypes(const moe_config* cfg, const float* a_scales,
+                             const float* w_scales, const float* out_scales,
+                             const float* sh_a_scales, const float* sh_w_scales,
+                             const float* sh_out_scales) {
+    if (cfg->w_dtype == MOE_E4M3) {
+        if (!a_scales || !w_scales) return MOE_ERR_INVALID_ARG;
+        return MOE_ERR_UNSUPPORTED;          // e4m3 expert GEMMs: see moe_config.w_dtype
+    }
+    if (a_scales || w_scales || out_scales || sh_a_scales || sh_w_scales || sh_out_scales)
+        return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
+int moe_grouped_gemm_up(const moe_config* cfg, const void* x_perm, const float* x_perm_scales,
+                        const int32_t* offsets, const float* gate_perm, const void* w13,
+                        const float* w13_scales, const void* x_shared,
+                        const float* x_shared_scales, const void* ws13,
+                        const float* ws13_scales, void* act, float* act_scales,
+                        void* shared_act, float* shared_act_scales, void* z_out, void* ws,
+                        size_t ws_bytes, hipStream_t stream) {
+    int st = check_cfg(cfg);
+    if (st) return st;
+    if (!x_perm || !offsets || !gate_perm || !w13 || !act || !ws) return MOE_ERR_INVALID_ARG;
+    if (cfg->shared_F) {
+        if (!x_shared || !ws13 || !shared_act) return MOE_ERR_INVALID_ARG;
+    } else if (x_shared || ws13 || shared_act) {
+        return MOE_ERR_INVALID_ARG;
+    }
+    st = check_gemm_dtypes(cfg, x_perm_scales, w13_scales, act_scales, x_shared_scales,
+                           ws13_scales, shared_act_scales);
+    if (st) return st;
+    if (ws_bytes < sched_ws_bytes(cfg)) return MOE_ERR_WORKSPACE;
+    return run_up(cfg, x_perm, x_perm_scales, offsets, gate_perm, w13, w13_scales, x_shared,
+                  x_shared_scales, ws13, ws13_scales, act, act_scales, shared_act,
+                  shared_act_scales, z_out, ws, stream);
+}
+
+int moe_grouped_gemm_down(const moe_config* cfg, const void* act, const float* act_scales,
+                          const int32_t* offsets, const void* w2, const float* w2_scales,
+                          const void* shared_act, const float* shared_act_scales,
+                          const void* ws2, const float* ws2_scales, void* y_perm,
+                          void* shared_y, void* ws, size_t ws_bytes, hipStream_t stream) {
+    int st = check_cfg(cfg);
+    if (st) return st;
+    if (!act || !offsets || !w2 || !y_perm || !ws) return MOE_ERR_INVALID_ARG;
+    if (cfg->shared_F) {
+        if (!shared_act || !ws2 || !shared_y) return MOE_ERR_INVALID_ARG;
+    } else if (shared_act || ws2 || shared_y) {
+        return MOE_ERR_INVALID_ARG;
+    }
+    st = check_gemm_dtypes(cfg, act_scales, w2_scales, nullptr, shared_act_scales, ws2_scales,
+                           nullptr);
+    if (st) return st;
+    if (ws_bytes < sched_ws_bytes(cfg)) return MOE_ERR_WORKSPACE;
+    return run_down(cfg, act, act_scales, offsets, w2, w2_scales, shared_act,
+                    shared_act_scales, ws2, ws2_scales, y_perm, shared_y, ws, stream);
 }
 
 int moe_unpermute_combine(const moe_config* cfg, const void* y_perm, const int32_t* pos,
