@@ -3,8 +3,10 @@
 One step = one moe_layer_forward call over one batch of seeded synthetic inputs already
 resident in HBM: router GEMM -> top-k routing -> permute -> grouped GEMM up (gate/up +
 SwiGLU, gate folded) -> grouped GEMM down -> combine, for the routed experts and the shared
-expert. The default workload is the DeepSeek-V3-shaped bf16 layer (T=8192 tokens,
-hidden 7168, 256 routed experts in 8 groups, top-8, SwiGLU width 2048, one shared expert).
+expert. The expert weights are stored in the library's K-blocked layout (moe_pack_kblock,
+run once before timing, like loading a checkpoint); the step itself starts from x. The
+default workload is the DeepSeek-V3-shaped bf16 layer (T=8192 tokens, hidden 7168, 256
+routed experts in 8 groups, top-8, SwiGLU width 2048, one shared expert).
 
 Prints progress to stderr and ONE JSON line to stdout.
 
@@ -103,6 +105,8 @@ def main():
     import routing_grouped_expert_softmax_amd as moe
 
     cfg = mi.CONFIGS[args.workload]
+    if cfg.act_dtype != mi.F32:
+        cfg = cfg.replace(a_layout=1, w_layout=1)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     log(f"[bench] generating {cfg.name} inputs ...")
@@ -112,6 +116,10 @@ def main():
     g = lambda t: None if t is None else t.to(dev, non_blocking=False)  # noqa: E731
     x, wr, w13, w2 = g(inp.x), g(inp.w_router), g(inp.w13), g(inp.w2)
     ws13, ws2, lb, sb = g(inp.ws13), g(inp.ws2), g(inp.logit_bias), g(inp.sel_bias)
+    if cfg.w_layout:
+        pk = lambda t: None if t is None else moe.pack_kblock(t)  # noqa: E731
+        w13, w2, ws13, ws2 = pk(w13), pk(w2), pk(ws13), pk(ws2)
+        torch.cuda.synchronize()
     y = torch.empty(cfg.T, cfg.H, dtype=moe.act_torch_dtype(cfg), device=dev)
     ws = moe.workspace(cfg, moe.OP_LAYER_FORWARD, dev)
     counts = torch.empty(cfg.E, dtype=torch.int32, device=dev)
@@ -220,6 +228,7 @@ def main():
                    "router": "softmax_topk" if cfg.router == 0 else
                    f"sigmoid_group_topk(groups={cfg.n_groups},keep={cfg.topk_groups},"
                    f"scale={cfg.route_scale})",
+                   "weights": "K-blocked" if cfg.w_layout else "row-major",
                    "parallelism": "single GPU"},
         "roofline": {"kernel": "grouped GEMM up (gate/up + SwiGLU, gate folded)",
                      "bound": bound, "achieved": round(achieved, 1), "peak": peak,

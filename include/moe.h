@@ -26,8 +26,15 @@
  *    are not validated on the device: topk_idx must come from moe_route or lie in [0, E).
  *  - Every output is overwritten, never accumulated into. Results are deterministic:
  *    bit-identical across runs (no floating-point atomics, no split-K).
- *  - Layouts are row-major and contiguous. Both GEMM operands keep K contiguous, so each
- *    expert GEMM is C = A B^T. fp8 scale tensors are fp32, row-major over blocks.
+ *  - Layouts: every matrix keeps K (its last index) contiguous, so each expert GEMM is
+ *    C = A B^T. A matrix [R, C] is either row-major (MOE_LAYOUT_ROWS) or K-blocked
+ *    (MOE_LAYOUT_KBLOCK): stored as [C * eb / 64][R][64 bytes] (eb = element bytes), i.e.
+ *    the 64-byte K slice j of row r is at byte (j * R + r) * 64, so one K slice of
+ *    consecutive rows is one contiguous run. Stacked weights [E, N, K] are K-blocked per
+ *    expert. moe_config.a_layout selects the layout of the expert-grouped activations
+ *    (x_perm, act, a shared expert's act) and w_layout that of the expert weights
+ *    (w13, w2, ws13, ws2); everything else (x, y, y_perm, z, scales) is row-major.
+ *    fp8 scale tensors are fp32, row-major over blocks.
  *  - Calls on different streams may overlap if their outputs and workspaces are disjoint.
  */
 #ifndef MOE_AMD_H
@@ -51,6 +58,8 @@ typedef enum {
 } moe_status;
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_E4M3 = 2 } moe_dtype;
+
+typedef enum { MOE_LAYOUT_ROWS = 0, MOE_LAYOUT_KBLOCK = 1 } moe_layout;
 
 typedef enum {
     /* select on the logits (ties to the lower expert index); gates = softmax over the k
@@ -86,6 +95,8 @@ typedef struct {
                              MOE_E4M3 (with act BF16: 1x128 activation scales, 128x128
                              weight scales, fp32 accumulation) */
     int32_t shared_F;     /* width of the always-on shared expert, 0 = none */
+    int32_t a_layout;     /* moe_layout of x_perm / act in the standalone calls (bf16, e4m3) */
+    int32_t w_layout;     /* moe_layout of the expert weights (bf16, e4m3) */
 } moe_config;
 
 /* Name of a status code (static string; never NULL). */
@@ -187,8 +198,10 @@ int moe_unpermute_combine(const moe_config* cfg, const void* y_perm, const int32
 
 /* The whole layer: router GEMM (skipped when logits_in != NULL), route, permute, grouped
  * GEMM with the shared expert, combine. x [T, H] and w_router [E, H] in act_dtype; weights
- * as in moe_grouped_gemm_swiglu; y [T, H] in act_dtype. Optional outputs (NULL = skip):
- * logits_out [T, E], topk_idx_out [T, k], topk_gate_out [T, k], counts_out [E]. */
+ * as in moe_grouped_gemm_swiglu (in cfg->w_layout); y [T, H] in act_dtype. The expert-grouped
+ * activations live in the workspace, K-blocked for bf16/e4m3 whatever cfg->a_layout says.
+ * Optional outputs (NULL = skip): logits_out [T, E], topk_idx_out [T, k],
+ * topk_gate_out [T, k], counts_out [E]. */
 int moe_layer_forward(const moe_config* cfg, const void* x, const void* w_router,
                       const float* logit_bias, const float* sel_bias, const float* logits_in,
                       const void* w13, const float* w13_scales, const void* w2,
@@ -214,6 +227,13 @@ int moe_grouped_gemm_swiglu_bwd(const moe_config* cfg, const void* dy_perm,
                                 const int32_t* offsets, const void* w13, const void* w2,
                                 void* dx_perm, void* dw13, void* dw2, float* dgate_perm,
                                 void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Re-layout of n_mat row-major matrices [rows, cols] of elem_bytes-byte elements into the
+ * K-blocked layout [n_mat][cols * elem_bytes / 64][rows][64 bytes] (see Layouts). A pure
+ * data movement, for expert weights that are stored once and used by many calls; in and
+ * out must not overlap. cols * elem_bytes must be a multiple of 64. */
+int moe_pack_kblock(const void* in, int64_t n_mat, int32_t rows, int32_t cols,
+                    int32_t elem_bytes, void* out, hipStream_t stream);
 
 /* e4m3 block quantisation of n_mat matrices [rows, cols] (bf16 or fp32 input):
  * one fp32 scale per block_rows x block_cols block, s = fp32(amax / 448) (1 for an

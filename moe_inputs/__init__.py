@@ -55,6 +55,8 @@ class MoEConfig:
     shared_F: int = 0
     zipf_alpha: float = 0.0        # > 0: add a Zipf-shaped per-expert logit bias
     backward: bool = False
+    a_layout: int = 0              # 0 row-major, 1 K-blocked (expert-grouped activations)
+    w_layout: int = 0              # 0 row-major, 1 K-blocked (expert weights)
 
     def replace(self, **kw) -> "MoEConfig":
         d = asdict(self)

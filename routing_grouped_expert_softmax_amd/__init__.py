@@ -7,7 +7,10 @@ happens in the HIP kernels; there is no fallback of any kind, and importing this
 fails loudly when the library has not been built.
 
 A config is any object with the attributes T, H, E, k, F, router, n_groups, topk_groups,
-route_scale, act_dtype, w_dtype, shared_F (dtype codes: 0 fp32, 1 bf16, 2 e4m3).
+route_scale, act_dtype, w_dtype, shared_F (dtype codes: 0 fp32, 1 bf16, 2 e4m3) and
+optionally a_layout, w_layout (0 row-major, 1 K-blocked; default 0). A K-blocked [R, C]
+tensor keeps its torch shape [R, C]; only the order of its bytes differs
+([C * eb / 64][R][64 bytes]).
 """
 from __future__ import annotations
 
@@ -21,6 +24,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe_amd.so")
 
 F32, BF16, E4M3 = 0, 1, 2
 SOFTMAX_TOPK, SIGMOID_GROUP_TOPK = 0, 1
+LAYOUT_ROWS, LAYOUT_KBLOCK = 0, 1
 OP_PERMUTE, OP_GROUPED_GEMM, OP_LAYER_FORWARD, OP_GROUPED_GEMM_BWD = 0, 1, 2, 3
 
 if not os.path.exists(LIB_PATH):
@@ -33,7 +37,8 @@ class MoeConfigC(C.Structure):
     _fields_ = [("T", C.c_int32), ("H", C.c_int32), ("E", C.c_int32), ("k", C.c_int32),
                 ("F", C.c_int32), ("n_groups", C.c_int32), ("topk_groups", C.c_int32),
                 ("router", C.c_int32), ("route_scale", C.c_float), ("act_dtype", C.c_int32),
-                ("w_dtype", C.c_int32), ("shared_F", C.c_int32)]
+                ("w_dtype", C.c_int32), ("shared_F", C.c_int32), ("a_layout", C.c_int32),
+                ("w_layout", C.c_int32)]
 
 
 class MoeError(RuntimeError):
@@ -64,6 +69,7 @@ _SIGS = {
     "moe_layer_forward": [CFG, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
     "moe_grouped_gemm_swiglu_bwd": [CFG, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
     "moe_quantize_e4m3": [P, I32, I64, I32, I32, I32, I32, P, P, P],
+    "moe_pack_kblock": [P, I64, I32, I32, I32, P, P],
 }
 for _name, _args in _SIGS.items():
     getattr(_lib, _name).argtypes = _args
@@ -83,7 +89,7 @@ def status_string(status: int) -> str:
 def make_config(cfg) -> MoeConfigC:
     return MoeConfigC(cfg.T, cfg.H, cfg.E, cfg.k, cfg.F, cfg.n_groups, cfg.topk_groups,
                       cfg.router, float(cfg.route_scale), cfg.act_dtype, cfg.w_dtype,
-                      cfg.shared_F)
+                      cfg.shared_F, getattr(cfg, "a_layout", 0), getattr(cfg, "w_layout", 0))
 
 
 def _check(fn: str, status: int):
@@ -385,3 +391,16 @@ def quantize_e4m3(t, block_rows: int, stream=None):
         _ptr(t, name="input"), dt, n, rows, cols, block_rows, 128, _ptr(q), _ptr(s),
         _stream(stream)))
     return q, s
+
+
+def pack_kblock(t, out=None, stream=None):
+    """Row-major [rows, cols] or [n, rows, cols] -> the same shape in the K-blocked layout
+    (moe_pack_kblock)."""
+    shape = tuple(t.shape)
+    n, rows, cols = (1,) + shape if len(shape) == 2 else shape
+    if out is None:
+        out = torch.empty_like(t)
+    _ptr(out, t.dtype, shape, "out")
+    _check("moe_pack_kblock", _lib.moe_pack_kblock(
+        _ptr(t, name="input"), n, rows, cols, t.element_size(), _ptr(out), _stream(stream)))
+    return out

@@ -36,6 +36,10 @@ int check_cfg(const moe_config* c) {
         return MOE_ERR_INVALID_ARG;
     }
     if (!(c->route_scale > 0.0f) || c->route_scale != c->route_scale) return MOE_ERR_INVALID_ARG;
+    if ((c->a_layout != MOE_LAYOUT_ROWS && c->a_layout != MOE_LAYOUT_KBLOCK) ||
+        (c->w_layout != MOE_LAYOUT_ROWS && c->w_layout != MOE_LAYOUT_KBLOCK))
+        return MOE_ERR_INVALID_ARG;
+    if (c->act_dtype == MOE_F32 && (c->a_layout || c->w_layout)) return MOE_ERR_UNSUPPORTED;
     if (c->act_dtype == MOE_F32) {
         if (c->w_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
         if (c->H % 64 || c->F % 32 || (c->shared_F && c->shared_F % 32)) return MOE_ERR_UNSUPPORTED;
@@ -139,7 +143,7 @@ size_t sched_ws_bytes(const moe_config* c) {
 // GEMM1 of the experts (gate/up projection + SwiGLU with the gate folded in): routed
 // experts as segment 0 and, when shared_F == F, the shared expert as segment 1 of the same
 // launch; a shared expert of another width gets its own launch.
-int run_up(const moe_config* c, const void* x_perm, const float* x_perm_scales,
+int run_up(const moe_config* c, int a_kb, const void* x_perm, const float* x_perm_scales,
            const int32_t* offsets, const float* gate_perm, const void* w13,
            const float* w13_scales, const void* x_shared, const float* x_shared_scales,
            const void* ws13, const float* ws13_scales, void* act, float* act_scales,
@@ -148,9 +152,9 @@ int run_up(const moe_config* c, const void* x_perm, const float* x_perm_scales,
     const int dt = c->w_dtype;
     const int A = c->T * c->k;
     Segment r1 = {x_perm, x_perm_scales, offsets, c->E, 0, gate_perm, w13, w13_scales,
-                  act, act_scales, z_out};
+                  act, act_scales, z_out, A, a_kb, c->w_layout, a_kb};
     Segment s1 = {x_shared, x_shared_scales, nullptr, 1, c->T, nullptr, ws13, ws13_scales,
-                  shared_act, shared_act_scales, nullptr};
+                  shared_act, shared_act_scales, nullptr, c->T, 0, c->w_layout, a_kb};
     if (!c->shared_F)
         return hip_status(moe::launch_grouped_gemm(0, dt, &r1, 1, A, 2 * c->F, c->H, sched, stream));
     if (c->shared_F == c->F) {
@@ -165,7 +169,7 @@ int run_up(const moe_config* c, const void* x_perm, const float* x_perm_scales,
 }
 
 // GEMM2 of the experts (down projection), same segment layout as run_up.
-int run_down(const moe_config* c, const void* act, const float* act_scales,
+int run_down(const moe_config* c, int a_kb, const void* act, const float* act_scales,
              const int32_t* offsets, const void* w2, const float* w2_scales,
              const void* shared_act, const float* shared_act_scales, const void* ws2,
              const float* ws2_scales, void* y_perm, void* shared_y, void* sched,
@@ -173,9 +177,9 @@ int run_down(const moe_config* c, const void* act, const float* act_scales,
     const int dt = c->w_dtype;
     const int A = c->T * c->k;
     Segment r2 = {act, act_scales, offsets, c->E, 0, nullptr, w2, w2_scales, y_perm, nullptr,
-                  nullptr};
+                  nullptr, A, a_kb, c->w_layout, 0};
     Segment s2 = {shared_act, shared_act_scales, nullptr, 1, c->T, nullptr, ws2, ws2_scales,
-                  shared_y, nullptr, nullptr};
+                  shared_y, nullptr, nullptr, c->T, a_kb, c->w_layout, 0};
     if (!c->shared_F)
         return hip_status(moe::launch_grouped_gemm(1, dt, &r2, 1, A, c->H, c->F, sched, stream));
     if (c->shared_F == c->F) {
@@ -190,7 +194,7 @@ int run_down(const moe_config* c, const void* act, const float* act_scales,
 }
 
 // Both GEMMs; the shared expert's activation lives in the workspace after the schedule.
-int run_experts(const moe_config* c, const void* x_perm, const float* x_perm_scales,
+int run_experts(const moe_config* c, int a_kb, const void* x_perm, const float* x_perm_scales,
                 const int32_t* offsets, const float* gate_perm, const void* w13,
                 const float* w13_scales, const void* w2, const float* w2_scales,
                 const void* x_shared, const float* x_shared_scales, const void* ws13,
@@ -206,11 +210,11 @@ int run_experts(const moe_config* c, const void* x_perm, const float* x_perm_sca
         sh_act = cv.take((size_t)c->T * c->shared_F * (fp8 ? 1 : elem_bytes(c->act_dtype)));
         if (fp8) sh_act_scales = (float*)cv.take((size_t)c->T * (c->shared_F / 128) * 4);
     }
-    int st = run_up(c, x_perm, x_perm_scales, offsets, gate_perm, w13, w13_scales, x_shared,
+    int st = run_up(c, a_kb, x_perm, x_perm_scales, offsets, gate_perm, w13, w13_scales, x_shared,
                     x_shared_scales, ws13, ws13_scales, act, act_scales, sh_act, sh_act_scales,
                     z_out, sched, stream);
     if (st) return st;
-    return run_down(c, act, act_scales, offsets, w2, w2_scales, sh_act, sh_act_scales, ws2,
+    return run_down(c, a_kb, act, act_scales, offsets, w2, w2_scales, sh_act, sh_act_scales, ws2,
                     ws2_scales, y_perm, shared_y, sched, stream);
 }
 
@@ -277,9 +281,10 @@ int moe_permute(const moe_config* cfg, const void* x, const int32_t* topk_idx,
     if ((x_q == nullptr) != (x_q_scales == nullptr)) return MOE_ERR_INVALID_ARG;
     if (ws_bytes < moe::permute_ws_bytes(cfg->T, cfg->k, cfg->E)) return MOE_ERR_WORKSPACE;
     const int mode = fp8 ? 2 : (cfg->act_dtype == MOE_F32 ? 0 : 1);
-    return hip_status(moe::launch_permute(mode, x, topk_idx, topk_gate, cfg->T, cfg->H, cfg->E,
-                                          cfg->k, counts, offsets, pos, src, gate_perm, x_perm,
-                                          x_perm_scales, x_q, x_q_scales, ws, stream));
+    return hip_status(moe::launch_permute(mode, cfg->a_layout, x, topk_idx, topk_gate, cfg->T,
+                                          cfg->H, cfg->E, cfg->k, counts, offsets, pos, src,
+                                          gate_perm, x_perm, x_perm_scales, x_q, x_q_scales, ws,
+                                          stream));
 }
 
 int moe_grouped_gemm_swiglu(const moe_config* cfg, const void* x_perm,
@@ -309,7 +314,7 @@ int moe_grouped_gemm_swiglu(const moe_config* cfg, const void* x_perm,
         return MOE_ERR_INVALID_ARG;
     }
     if (ws_bytes < gemm_ws_bytes(cfg)) return MOE_ERR_WORKSPACE;
-    return run_experts(cfg, x_perm, x_perm_scales, offsets, gate_perm, w13, w13_scales, w2,
+    return run_experts(cfg, cfg->a_layout, x_perm, x_perm_scales, offsets, gate_perm, w13, w13_scales, w2,
                        w2_scales, x_shared, x_shared_scales, ws13, ws13_scales, ws2,
                        ws2_scales, act, act_scales, y_perm, shared_y, z_out, ws, stream);
 }
@@ -346,7 +351,7 @@ int moe_grouped_gemm_up(const moe_config* cfg, const void* x_perm, const float* 
                            ws13_scales, shared_act_scales);
     if (st) return st;
     if (ws_bytes < sched_ws_bytes(cfg)) return MOE_ERR_WORKSPACE;
-    return run_up(cfg, x_perm, x_perm_scales, offsets, gate_perm, w13, w13_scales, x_shared,
+    return run_up(cfg, cfg->a_layout, x_perm, x_perm_scales, offsets, gate_perm, w13, w13_scales, x_shared,
                   x_shared_scales, ws13, ws13_scales, act, act_scales, shared_act,
                   shared_act_scales, z_out, ws, stream);
 }
@@ -368,7 +373,7 @@ int moe_grouped_gemm_down(const moe_config* cfg, const void* act, const float* a
                            nullptr);
     if (st) return st;
     if (ws_bytes < sched_ws_bytes(cfg)) return MOE_ERR_WORKSPACE;
-    return run_down(cfg, act, act_scales, offsets, w2, w2_scales, shared_act,
+    return run_down(cfg, cfg->a_layout, act, act_scales, offsets, w2, w2_scales, shared_act,
                     shared_act_scales, ws2, ws2_scales, y_perm, shared_y, ws, stream);
 }
 
@@ -415,12 +420,15 @@ int moe_layer_forward(const moe_config* cfg, const void* x, const void* w_router
                           cfg->n_groups, cfg->topk_groups, cfg->route_scale, idx, gate, stream);
     if (e != hipSuccess) return MOE_ERR_HIP;
     const int mode = fp8 ? 2 : (cfg->act_dtype == MOE_F32 ? 0 : 1);
-    e = moe::launch_permute(mode, x, idx, gate, cfg->T, cfg->H, cfg->E, cfg->k, counts,
+    // internal activations (x_perm, act, the shared expert's act) are K-blocked: every
+    // 128-byte K slice of consecutive rows is contiguous, so each tile load is one run
+    const int a_kb = cfg->act_dtype == MOE_F32 ? 0 : 1;
+    e = moe::launch_permute(mode, a_kb, x, idx, gate, cfg->T, cfg->H, cfg->E, cfg->k, counts,
                             L.offsets, L.pos, L.src, L.gate_perm, L.x_perm, L.x_perm_scales,
                             L.x_q, L.x_q_scales, L.scratch, stream);
     if (e != hipSuccess) return MOE_ERR_HIP;
     const void* xs = fp8 ? L.x_q : x;
-    st = run_experts(cfg, L.x_perm, L.x_perm_scales, L.offsets, L.gate_perm, w13, w13_scales,
+    st = run_experts(cfg, a_kb, L.x_perm, L.x_perm_scales, L.offsets, L.gate_perm, w13, w13_scales,
                      w2, w2_scales, cfg->shared_F ? xs : nullptr, fp8 ? L.x_q_scales : nullptr,
                      ws13, ws13_scales, ws2, ws2_scales, L.act, L.act_scales, L.y_perm,
                      L.shared_y, nullptr, L.scratch, stream);
@@ -440,6 +448,15 @@ int moe_grouped_gemm_swiglu_bwd(const moe_config* cfg, const void* dy_perm, cons
     int st = check_cfg(cfg);
     if (st) return st;
     return MOE_ERR_UNSUPPORTED;
+}
+
+int moe_pack_kblock(const void* in, int64_t n_mat, int32_t rows, int32_t cols,
+                    int32_t elem_bytes, void* out, hipStream_t stream) {
+    if (!in || !out || in == out) return MOE_ERR_INVALID_ARG;
+    if (n_mat < 1 || rows < 1 || cols < 1) return MOE_ERR_INVALID_ARG;
+    if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4) return MOE_ERR_INVALID_ARG;
+    if (((int64_t)cols * elem_bytes) % 64) return MOE_ERR_INVALID_ARG;
+    return hip_status(moe::launch_pack_kblock(in, n_mat, rows, cols, elem_bytes, out, stream));
 }
 
 int moe_quantize_e4m3(const void* in, int32_t in_dtype, int64_t n_mat, int32_t rows,

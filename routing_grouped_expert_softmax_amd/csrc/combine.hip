@@ -157,7 +157,37 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(const void* __restric
     if (threadIdx.x == 0) scales[blk] = sc;
 }
 
+// K-blocked re-layout: one wavefront per (matrix, 64-byte K slice, 16 rows); lane l copies
+// 16 bytes: row 16 * blockrow + l / 4, chunk l % 4. Reads are 64-byte row pieces, writes one
+// contiguous kilobyte.
+__global__ __launch_bounds__(256) void pack_kblock_kernel(const uint4* __restrict__ in,
+                                                          int64_t n_mat, int rows,
+                                                          int row_chunks, uint4* __restrict__ out) {
+    const int lane = threadIdx.x % kWave;
+    const int64_t w = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+    const int row_groups = (rows + 15) / 16;
+    const int slices = row_chunks / 4;
+    const int64_t total = n_mat * slices * row_groups;
+    if (w >= total) return;
+    const int64_t mat = w / ((int64_t)slices * row_groups);
+    const int rem = (int)(w % ((int64_t)slices * row_groups));
+    const int j = rem / row_groups, rg = rem % row_groups;
+    const int r = rg * 16 + lane / 4, c = lane % 4;
+    if (r >= rows) return;
+    const size_t mbase = (size_t)mat * rows * row_chunks;
+    out[mbase + ((size_t)j * rows + r) * 4 + c] = in[mbase + (size_t)r * row_chunks + j * 4 + c];
+}
+
 }  // namespace
+
+hipError_t launch_pack_kblock(const void* in, int64_t n_mat, int rows, int cols, int elem_bytes,
+                              void* out, hipStream_t s) {
+    const int row_chunks = (int)((int64_t)cols * elem_bytes / 16);
+    const int64_t waves = n_mat * (row_chunks / 4) * (int64_t)((rows + 15) / 16);
+    pack_kblock_kernel<<<(unsigned)((waves + 3) / 4), 256, 0, s>>>((const uint4*)in, n_mat, rows,
+                                                                   row_chunks, (uint4*)out);
+    return hipGetLastError();
+}
 
 hipError_t launch_combine(int act_dtype, const void* y_perm, const int32_t* pos,
                           const void* shared_y, int T, int H, int k, void* y, hipStream_t s) {

@@ -35,6 +35,13 @@ struct SegDev {
     void* out;
     float* out_scales;
     void* z_out;
+    // operand addressing in bytes: row r, 64-byte K slice j of `a` is at
+    // a + r * a_row + j * a_kstep (row-major: a_row = K * eb, a_kstep = 64; K-blocked:
+    // a_row = 64, a_kstep = rows_total * 64); the same for each group's weight, whose
+    // group g starts at w + g * w_mat
+    size_t a_row, a_kstep, w_row, w_kstep, w_mat;
+    int rows_total;
+    int out_kblock;
 };
 
 struct SchedArgs {
@@ -124,11 +131,15 @@ MOE_DEVICE bool pick_tile(const GemmArgs& ga, int& mt, int& nt) {
 // ---------------------------------------------------------------------------------------
 // bf16 MFMA kernel
 //
-// LDS holds STAGES stages of [BM A rows | BN B rows] x 128 bytes (64 bf16 of K). Tiles are
-// filled by direct global -> LDS loads (global_load_lds_dwordx4: no staging registers),
-// each wave instruction filling 8 rows = 1 KB. Within a row the 16-byte chunks are
-// XOR-swizzled (physical chunk = logical chunk ^ (row & 7)) so that the 32 rows one MFMA
-// operand read touches spread over the LDS banks. Prefetch distance is STAGES - 1 K steps.
+// LDS holds STAGES stages of [BM A rows | BN B rows] x BK bf16 (64 or 128 bytes per row).
+// Tiles are filled by direct global -> LDS loads (global_load_lds_dwordx4: no staging
+// registers); one wave instruction fills 1 KB = 1024 / (2 BK) rows. Within a row the
+// 16-byte chunks are XOR-swizzled (physical chunk = logical chunk ^ swz(row)) so that the
+// 32 rows one MFMA operand read touches spread over the LDS banks. The prefetch distance is
+// STAGES - 1 K steps.
+//
+// Ragged tails: a wave skips the loads and MFMAs of its 32-row sub-tiles that lie wholly
+// past the expert's last row, so a tile with few live rows costs few MFMA cycles.
 // ---------------------------------------------------------------------------------------
 #define MOE_LDS __attribute__((address_space(3)))
 
@@ -148,28 +159,146 @@ MOE_DEVICE void block_sync() {
     asm volatile("" ::: "memory");
 }
 
-template <int KIND, int BM, int BN, int WM, int WN, int STAGES>
+constexpr int cmin(int a, int b) { return a < b ? a : b; }
+
+// Chunk swizzle of a tile row (depends on the row's low 4 bits only, so a 32-row operand
+// read sees the same pattern at every 32-row offset). 8 chunks (128-byte rows): rows 0..7
+// of one logical chunk land in 8 different chunks. 4 chunks (64-byte rows): rows of one
+// parity among any 4 consecutive even (odd) rows, and rows 4 apart, land in different
+// chunks.
+template <int CPR>
+MOE_DEVICE int chunk_swz(int r) {
+    if (CPR == 8) return r & 7;
+    return ((r >> 1) & 3) ^ ((r >> 3) & 1);
+}
+
+template <int KIND, int BM, int BN, int BK, int WM, int WN, int STAGES, int LOADREG = 0>
 struct BfCfg {
+    static constexpr int kLoadReg = LOADREG;
     static constexpr int kThreads = WM * WN * kWave;
     static constexpr int kWaves = WM * WN;
-    static constexpr int kBK = 64;                          // bf16 per row per stage
-    static constexpr int kRowBytes = 128;
+    static constexpr int kRowBytes = BK * 2;
+    static constexpr int kCpr = kRowBytes / 16;             // 16-byte chunks per row
+    static constexpr int kRowsPerDma = kWave / kCpr;        // rows one wave DMA fills
     static constexpr int kRows = BM + BN;
     static constexpr int kStageBytes = kRows * kRowBytes;
-    static constexpr int kDma = kRows / 8 / kWaves;         // DMA instructions per wave/stage
+    static constexpr int kDma = kRows / kRowsPerDma / kWaves;   // DMAs per wave per stage
     static constexpr int kTM = BM / WM / 32;                // 32x32 tiles per wave (M)
     static constexpr int kTN = BN / WN / 32;                // 32x32 tiles per wave (N)
+    static constexpr int kSub = BK / 16;                    // MFMA K steps per stage
+    static constexpr int kSlices = kRowBytes / 64;          // 64-byte K slices per stage
+    static constexpr int kStages = STAGES;
     static constexpr size_t kLds = (size_t)STAGES * kStageBytes;
-    static_assert(kRows % (8 * kWaves) == 0, "DMA split");
-    static_assert(BM % (8 * kWaves) == 0 || true, "");
+    static_assert(BK == 32 || BK == 64, "BK");
+    static_assert(kRows % (kRowsPerDma * kWaves) == 0, "DMA split");
     static_assert(KIND == 1 || kTN % 2 == 0, "GEMM1 needs gate/up tile pairs");
     static_assert(kLds <= 160 * 1024, "LDS");
-    static_assert((STAGES - 2) * kDma < 64, "vmcnt");
+    static_assert(STAGES >= 2 && (STAGES - 2) * kDma < 64, "vmcnt");
+    static_assert(!LOADREG || STAGES == 2, "register-staged loads use a 2-stage ring");
 };
 
-template <int KIND, int BM, int BN, int WM, int WN, int STAGES>
+// MFMAs of one LDS stage for a wave's NV live 32-row sub-tiles. Operand fragments are
+// double-buffered in registers: the LDS reads of sub-step s + 1 are placed between the
+// MFMAs of sub-step s (sched_group_barrier: MFMA / DS-read interleave).
+template <class C, int NV>
+MOE_DEVICE void bf16_stage_mma(const uint8_t* base, const int (&a_off)[C::kTM],
+                               const int (&b_off)[C::kTN], const int (&chunk_off)[C::kSub],
+                               f32x16_t (&acc)[C::kTM][C::kTN]) {
+    if (NV == 0) return;
+    constexpr int NVv = NV > 0 ? NV : 1;
+    bf16x8_t av[2][NVv], bv[2][C::kTN];
+#pragma unroll
+    for (int j = 0; j < C::kTN; ++j) bv[0][j] = *(const bf16x8_t*)(base + b_off[j] + chunk_off[0]);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) av[0][i] = *(const bf16x8_t*)(base + a_off[i] + chunk_off[0]);
+#pragma unroll
+    for (int s = 0; s < C::kSub; ++s) {
+        const int cur = s & 1, nxt = cur ^ 1;
+        if (s + 1 < C::kSub) {
+#pragma unroll
+            for (int j = 0; j < C::kTN; ++j)
+                bv[nxt][j] = *(const bf16x8_t*)(base + b_off[j] + chunk_off[s + 1]);
+#pragma unroll
+            for (int i = 0; i < NV; ++i)
+                av[nxt][i] = *(const bf16x8_t*)(base + a_off[i] + chunk_off[s + 1]);
+        }
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+#pragma unroll
+            for (int j = 0; j < C::kTN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[cur][i], bv[cur][j],
+                                                                    acc[i][j], 0, 0, 0);
+    }
+#ifndef MOE_NO_SCHED_INTERLEAVE
+    constexpr int kReads = C::kTN + NVv;
+    constexpr int kMfma = NVv * C::kTN;
+    __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
+#pragma unroll
+    for (int s = 0; s < C::kSub; ++s) {
+#pragma unroll
+        for (int x = 0; x < kMfma; ++x) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (s + 1 < C::kSub && x < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+    }
+#endif
+}
+
+// K loop with direct global -> LDS loads, STAGES-deep ring (prefetch distance STAGES - 1).
+template <class C, int NV, class Issue>
+MOE_DEVICE void bf16_kloop(int nk, const uint8_t* lds, Issue& issue,
+                           const int (&a_off)[C::kTM], const int (&b_off)[C::kTN],
+                           const int (&chunk_off)[C::kSub],
+                           f32x16_t (&acc)[C::kTM][C::kTN]) {
+    constexpr int STAGES = C::kStages;
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s)
+        if (s < nk) issue(s, s);
+    int stage = 0;
+    for (int kt = 0; kt < nk; ++kt) {
+        // stage kt has landed once at most min(STAGES - 2, nk - 1 - kt) later groups remain
+        const int later = nk - 1 - kt;
+        if (later >= STAGES - 2) wait_vm_lgkm0<(STAGES - 2) * C::kDma>();
+        else if (later >= 2) wait_vm_lgkm0<cmin(2, STAGES - 2) * C::kDma>();
+        else if (later >= 1) wait_vm_lgkm0<cmin(1, STAGES - 2) * C::kDma>();
+        else wait_vm_lgkm0<0>();
+        block_sync();
+        {
+            const int kn = kt + STAGES - 1;
+            int sn = stage + STAGES - 1;
+            if (sn >= STAGES) sn -= STAGES;
+            if (kn < nk) issue(kn, sn);
+        }
+        bf16_stage_mma<C, NV>(lds + stage * C::kStageBytes, a_off, b_off, chunk_off, acc);
+        if (++stage == STAGES) stage = 0;
+    }
+}
+
+// K loop with register-staged loads (global -> VGPR -> ds_write) into a 2-stage LDS ring:
+// the global loads of step kt + 2 are in flight while step kt + 1 is computed.
+template <class C, int NV, class Load, class Store>
+MOE_DEVICE void bf16_kloop_reg(int nk, const uint8_t* lds, Load& load, Store& store,
+                               const int (&a_off)[C::kTM], const int (&b_off)[C::kTN],
+                               const int (&chunk_off)[C::kSub],
+                               f32x16_t (&acc)[C::kTM][C::kTN]) {
+    uint4 r[C::kDma];
+    load(r, 0);
+    store(r, 0);
+    if (nk > 1) load(r, 1);
+    wait_vm_lgkm0<63>();
+    block_sync();
+    for (int kt = 0; kt < nk; ++kt) {
+        bf16_stage_mma<C, NV>(lds + (kt & 1) * C::kStageBytes, a_off, b_off, chunk_off, acc);
+        if (kt + 1 < nk) store(r, (kt + 1) & 1);
+        if (kt + 2 < nk) load(r, kt + 2);
+        __builtin_amdgcn_s_waitcnt(0xC07F);          // lgkmcnt(0): this wave's LDS writes
+        block_sync();
+    }
+}
+
+template <int KIND, int BM, int BN, int BK, int WM, int WN, int STAGES, int LOADREG>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs ga) {
-    using C = BfCfg<KIND, BM, BN, WM, WN, STAGES>;
+    using C = BfCfg<KIND, BM, BN, BK, WM, WN, STAGES, LOADREG>;
     extern __shared__ __align__(16) uint8_t lds[];
     int mt, nt;
     if (!pick_tile(ga, mt, nt)) return;
@@ -180,17 +309,23 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs ga) {
     const int N = ga.N, K = ga.K;
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int wm = wave / WN, wn = wave % WN;
+    // live rows of the tile, and this wave's live 32-row sub-tiles
+    const int live = Mg - m0 < BM ? Mg - m0 : BM;
+    int nvi = (live - wm * (BM / WM) + 31) / 32;
+    nvi = nvi < 0 ? 0 : (nvi > C::kTM ? C::kTM : nvi);
+    nvi = __builtin_amdgcn_readfirstlane(nvi);
 
-    // ---- DMA sources: instruction q of this wave fills tile rows 8*(wave + q*kWaves) .. +7
+    // ---- DMA sources: instruction q of this wave fills tile rows
+    //      kRowsPerDma * (wave + q * kWaves) + [0, kRowsPerDma)
     const uint8_t* src[C::kDma];
 #pragma unroll
     for (int q = 0; q < C::kDma; ++q) {
-        const int r = 8 * (wave + q * C::kWaves) + lane / 8;      // tile row
-        const int c = (lane % 8) ^ (r & 7);                        // logical 16-byte chunk
+        const int r = C::kRowsPerDma * (wave + q * C::kWaves) + lane / C::kCpr;   // tile row
+        const int c = (lane % C::kCpr) ^ chunk_swz<C::kCpr>(r);    // logical 16-byte chunk
         const uint8_t* rowp;
         if (r < BM) {
             const int rr = m0 + r < Mg ? m0 + r : Mg - 1;          // clamp the ragged tail
-            rowp = (const uint8_t*)S.a + ((size_t)(rbase + rr) * K) * 2;
+            rowp = (const uint8_t*)S.a + (size_t)(rbase + rr) * S.a_row;
         } else {
             const int rb = r - BM;
             int wrow;
@@ -198,23 +333,40 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs ga) {
                 wrow = rb < BN / 2 ? nt * (BN / 2) + rb : N / 2 + nt * (BN / 2) + (rb - BN / 2);
             else
                 wrow = nt * BN + rb;
-            rowp = (const uint8_t*)S.w + ((size_t)g * N + wrow) * (size_t)K * 2;
+            rowp = (const uint8_t*)S.w + (size_t)g * S.w_mat + (size_t)wrow * S.w_row;
         }
-        src[q] = rowp + c * 16;
+        const size_t step = r < BM ? S.a_kstep : S.w_kstep;
+        src[q] = rowp + (size_t)(c / 4) * step + (c % 4) * 16;
     }
+    // bytes per 64-byte K slice: instruction q holds A rows only or B rows only
+    const size_t a_step = S.a_kstep, w_step = S.w_kstep;
     auto issue = [&](int kstep, int stage) {
         MOE_LDS uint8_t* base = (MOE_LDS uint8_t*)lds + stage * C::kStageBytes;
 #pragma unroll
         for (int q = 0; q < C::kDma; ++q)
             __builtin_amdgcn_global_load_lds(
-                (const void*)(src[q] + (size_t)kstep * C::kRowBytes),
+                (const void*)(src[q] + (size_t)kstep * C::kSlices *
+                                           (q * C::kRowsPerDma * C::kWaves < BM ? a_step : w_step)),
                 (MOE_LDS void*)(base + (wave + q * C::kWaves) * 1024), 16, 0, 0);
+    };
+    auto load = [&](uint4 (&r)[C::kDma], int kstep) {
+#pragma unroll
+        for (int q = 0; q < C::kDma; ++q)
+            r[q] = *(const uint4*)(src[q] + (size_t)kstep * C::kSlices *
+                                                (q * C::kRowsPerDma * C::kWaves < BM ? a_step : w_step));
+    };
+    auto store = [&](const uint4 (&r)[C::kDma], int stage) {
+        uint8_t* base = lds + stage * C::kStageBytes;
+#pragma unroll
+        for (int q = 0; q < C::kDma; ++q)
+            *(uint4*)(base + (wave + q * C::kWaves) * 1024 + lane * 16) = r[q];
     };
 
     // ---- MFMA operand addresses (bytes within a stage)
     int a_off[C::kTM], b_off[C::kTN];
 #pragma unroll
-    for (int i = 0; i < C::kTM; ++i) a_off[i] = (wm * (BM / WM) + i * 32 + lane % 32) * C::kRowBytes;
+    for (int i = 0; i < C::kTM; ++i)
+        a_off[i] = (wm * (BM / WM) + i * 32 + lane % 32) * C::kRowBytes;
 #pragma unroll
     for (int j = 0; j < C::kTN; ++j) {
         int row;
@@ -227,10 +379,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs ga) {
         }
         b_off[j] = row * C::kRowBytes;
     }
-    // physical chunk of logical chunk (kk/8 + lane/32) of a row whose (row & 7) == lane & 7
-    int chunk_off[4];
+    // physical chunk of logical chunk (2 s + lane / 32) of a row whose low bits are lane % 32
+    int chunk_off[C::kSub];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) chunk_off[s] = (((2 * s + lane / 32) ^ (lane & 7)) * 16);
+    for (int s = 0; s < C::kSub; ++s)
+        chunk_off[s] = ((2 * s + lane / 32) ^ chunk_swz<C::kCpr>(lane % 32)) * 16;
 
     f32x16_t acc[C::kTM][C::kTN];
 #pragma unroll
@@ -238,39 +391,31 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs ga) {
 #pragma unroll
         for (int j = 0; j < C::kTN; ++j) acc[i][j] = f32x16_t{};
 
-    const int nk = K / C::kBK;
-#pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s)
-        if (s < nk) issue(s, s);
-    int stage = 0;
-    for (int kt = 0; kt < nk; ++kt) {
-        if (kt + STAGES - 2 < nk) wait_vm_lgkm0<(STAGES - 2) * C::kDma>();
-        else wait_vm_lgkm0<0>();
-        block_sync();
-        {
-            const int kn = kt + STAGES - 1;
-            int sn = stage + STAGES - 1;
-            if (sn >= STAGES) sn -= STAGES;
-            if (kn < nk) issue(kn, sn);
-        }
-        const uint8_t* base = lds + stage * C::kStageBytes;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            bf16x8_t av[C::kTM], bv[C::kTN];
-#pragma unroll
-            for (int i = 0; i < C::kTM; ++i)
-                av[i] = *(const bf16x8_t*)(base + a_off[i] + chunk_off[s]);
-#pragma unroll
-            for (int j = 0; j < C::kTN; ++j)
-                bv[j] = *(const bf16x8_t*)(base + b_off[j] + chunk_off[s]);
-#pragma unroll
-            for (int i = 0; i < C::kTM; ++i)
-#pragma unroll
-                for (int j = 0; j < C::kTN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j],
-                                                                        acc[i][j], 0, 0, 0);
-        }
-        if (++stage == STAGES) stage = 0;
+    // one branch-free K loop per count of live sub-tiles (every variant has the same
+    // barriers, so waves of one block may take different variants)
+    const int nk = K / BK;
+    switch (nvi) {
+#define MOE_KLOOP_CASE(V)                                                                   \
+    case V:                                                                                 \
+        if (V <= C::kTM) {                                                                  \
+            constexpr int NV = V <= C::kTM ? V : C::kTM;                                    \
+            if (LOADREG)                                                                    \
+                bf16_kloop_reg<C, NV>(nk, lds, load, store, a_off, b_off, chunk_off, acc);  \
+            else                                                                            \
+                bf16_kloop<C, NV>(nk, lds, issue, a_off, b_off, chunk_off, acc);            \
+        }                                                                                   \
+        break;
+    MOE_KLOOP_CASE(0)
+    MOE_KLOOP_CASE(1)
+    MOE_KLOOP_CASE(2)
+    MOE_KLOOP_CASE(3)
+    MOE_KLOOP_CASE(4)
+    MOE_KLOOP_CASE(5)
+    MOE_KLOOP_CASE(6)
+    MOE_KLOOP_CASE(7)
+    MOE_KLOOP_CASE(8)
+#undef MOE_KLOOP_CASE
+    default: break;
     }
 
     // epilogue. 32x32 accumulator layout: element r of lane l is
@@ -282,6 +427,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs ga) {
         uint16_t* zo = (uint16_t*)S.z_out;
 #pragma unroll
         for (int i = 0; i < C::kTM; ++i) {
+            if (i >= nvi) continue;
 #pragma unroll
             for (int jj = 0; jj < half; ++jj) {
                 const int col = nt * (BN / 2) + wn * (BN / 2 / WN) + jj * 32 + lane % 32;
@@ -292,7 +438,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs ga) {
                     const size_t grow = (size_t)rbase + m0 + row;
                     const float zg = acc[i][jj][r], zu = acc[i][half + jj][r];
                     const float gt = S.gate ? S.gate[grow] : 1.0f;
-                    out[grow * F + col] = f32_to_bf16(gt * (silu_f32(zg) * zu));
+                    const size_t oi = S.out_kblock
+                        ? ((size_t)(col / 32) * S.rows_total + grow) * 32 + col % 32
+                        : grow * F + col;
+                    out[oi] = f32_to_bf16(gt * (silu_f32(zg) * zu));
                     if (zo) {
                         zo[grow * N + col] = f32_to_bf16(zg);
                         zo[grow * N + F + col] = f32_to_bf16(zu);
@@ -304,6 +453,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs ga) {
         uint16_t* out = (uint16_t*)S.out;
 #pragma unroll
         for (int i = 0; i < C::kTM; ++i) {
+            if (i >= nvi) continue;
 #pragma unroll
             for (int j = 0; j < C::kTN; ++j) {
                 const int col = nt * BN + wn * (BN / WN) + j * 32 + lane % 32;
@@ -409,26 +559,44 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs ga) {
 // ---------------------------------------------------------------------------------------
 // configurations
 // ---------------------------------------------------------------------------------------
-// bf16: BM=256, BN=256 (GEMM1: 128 act columns), 8 waves as 2 (M) x 4 (N), 2 stages.
-#define MOE_BF_CFG(KIND) KIND, 256, 256, 2, 4, 2
+// bf16 tile configurations (BM, BN, BK, WM, WN, STAGES, register-staged loads). GEMM1's BN counts gate + up rows
+// (BN / 2 act columns).
+#ifndef MOE_BF_UP_CFG
+#define MOE_BF_UP_CFG 256, 256, 64, 2, 4, 2, 0
+#endif
+#ifndef MOE_BF_DOWN_CFG
+#define MOE_BF_DOWN_CFG 256, 256, 64, 2, 4, 2, 0
+#endif
 
-template <int KIND, int BM, int BN, int WM, int WN, int STAGES>
+template <int KIND, int BM, int BN, int BK, int WM, int WN, int STAGES, int LOADREG>
 hipError_t run_bf16(const GemmArgs& ga, int nblocks, hipStream_t s) {
-    using C = BfCfg<KIND, BM, BN, WM, WN, STAGES>;
+    using C = BfCfg<KIND, BM, BN, BK, WM, WN, STAGES, LOADREG>;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(
-            (const void*)gemm_bf16_kernel<KIND, BM, BN, WM, WN, STAGES>,
+            (const void*)gemm_bf16_kernel<KIND, BM, BN, BK, WM, WN, STAGES, LOADREG>,
             hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::kLds);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    gemm_bf16_kernel<KIND, BM, BN, WM, WN, STAGES><<<nblocks, C::kThreads, C::kLds, s>>>(ga);
+    gemm_bf16_kernel<KIND, BM, BN, BK, WM, WN, STAGES, LOADREG>
+        <<<nblocks, C::kThreads, C::kLds, s>>>(ga);
     return hipGetLastError();
 }
 
-int bm_for(int dtype) { return dtype == 0 ? kF32BM : 256; }
-int bn_for(int kind, int dtype) { (void)kind; return dtype == 0 ? 64 : 256; }
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int LOADREG>
+constexpr int cfg_bm() { return BM; }
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int LOADREG>
+constexpr int cfg_bn() { return BN; }
+
+int bm_for(int kind, int dtype) {
+    if (dtype == 0) return kF32BM;
+    return kind == 0 ? cfg_bm<MOE_BF_UP_CFG>() : cfg_bm<MOE_BF_DOWN_CFG>();
+}
+int bn_for(int kind, int dtype) {
+    if (dtype == 0) return 64;
+    return kind == 0 ? cfg_bn<MOE_BF_UP_CFG>() : cfg_bn<MOE_BF_DOWN_CFG>();
+}
 
 size_t max_mtiles(int max_rows_total, int groups_total, int bm) {
     return (size_t)(max_rows_total + bm - 1) / bm + (size_t)groups_total;
@@ -440,14 +608,14 @@ GemmPlan grouped_gemm_plan(int kind, int dtype, int max_rows_total, int groups_t
                            int K) {
     (void)kind; (void)N; (void)K;
     GemmPlan p;
-    p.bm = bm_for(dtype);
+    p.bm = bm_for(kind, dtype);
     p.ws_bytes = 256 + max_mtiles(max_rows_total, groups_total, p.bm) * sizeof(int4);
     return p;
 }
 
 hipError_t launch_grouped_gemm(int kind, int dtype, const Segment* segs, int nseg,
                                int max_rows_total, int N, int K, void* ws, hipStream_t s) {
-    const int bm = bm_for(dtype), bn = bn_for(kind, dtype);
+    const int bm = bm_for(kind, dtype), bn = bn_for(kind, dtype);
     int groups_total = 0;
     SchedArgs sa = {};
     GemmArgs ga = {};
@@ -456,8 +624,19 @@ hipError_t launch_grouped_gemm(int kind, int dtype, const Segment* segs, int nse
         sa.groups[i] = segs[i].groups;
         sa.rows[i] = segs[i].rows;
         groups_total += segs[i].groups;
-        ga.seg[i] = SegDev{segs[i].a, segs[i].a_scales, segs[i].gate, segs[i].w,
-                           segs[i].w_scales, segs[i].out, segs[i].out_scales, segs[i].z_out};
+        const size_t eb = dtype == 0 ? 4 : dtype == 1 ? 2 : 1;
+        const Segment& g = segs[i];
+        SegDev d;
+        d.a = g.a; d.a_scales = g.a_scales; d.gate = g.gate; d.w = g.w;
+        d.w_scales = g.w_scales; d.out = g.out; d.out_scales = g.out_scales; d.z_out = g.z_out;
+        d.a_row = g.a_kblock ? 64 : (size_t)K * eb;
+        d.a_kstep = g.a_kblock ? (size_t)g.rows_total * 64 : 64;
+        d.w_row = g.w_kblock ? 64 : (size_t)K * eb;
+        d.w_kstep = g.w_kblock ? (size_t)N * 64 : 64;
+        d.w_mat = (size_t)N * K * eb;
+        d.rows_total = g.rows_total;
+        d.out_kblock = g.out_kblock;
+        ga.seg[i] = d;
     }
     sa.nseg = nseg;
     int* total = (int*)ws;
@@ -478,8 +657,8 @@ hipError_t launch_grouped_gemm(int kind, int dtype, const Segment* segs, int nse
         return hipGetLastError();
     }
     if (dtype == 1) {
-        if (kind == 0) return run_bf16<MOE_BF_CFG(0)>(ga, (int)nblocks, s);
-        return run_bf16<MOE_BF_CFG(1)>(ga, (int)nblocks, s);
+        if (kind == 0) return run_bf16<0, MOE_BF_UP_CFG>(ga, (int)nblocks, s);
+        return run_bf16<1, MOE_BF_DOWN_CFG>(ga, (int)nblocks, s);
     }
     return hipErrorInvalidValue;
 }

@@ -21,7 +21,8 @@ hipError_t launch_route(int router, const float* logits, const float* logit_bias
 // ---- permute ---------------------------------------------------------------------------
 constexpr int kPermChunk = 512;   // assignments per counting block
 size_t permute_ws_bytes(int T, int k, int E);
-hipError_t launch_permute(int mode /*0 f32, 1 bf16, 2 e4m3 from bf16*/, const void* x,
+hipError_t launch_permute(int mode /*0 f32, 1 bf16, 2 e4m3 from bf16*/,
+                          int kblock /*1: x_perm K-blocked*/, const void* x,
                           const int32_t* topk_idx, const float* topk_gate, int T, int H,
                           int E, int k, int32_t* counts, int32_t* offsets, int32_t* pos,
                           int32_t* src, float* gate_perm, void* x_perm,
@@ -31,6 +32,10 @@ hipError_t launch_permute(int mode /*0 f32, 1 bf16, 2 e4m3 from bf16*/, const vo
 // ---- combine ---------------------------------------------------------------------------
 hipError_t launch_combine(int act_dtype, const void* y_perm, const int32_t* pos,
                           const void* shared_y, int T, int H, int k, void* y, hipStream_t s);
+
+// ---- K-blocked re-layout: [n, rows, cols] -> [n][cols*eb/128][rows][128 bytes] ----------
+hipError_t launch_pack_kblock(const void* in, int64_t n_mat, int rows, int cols, int elem_bytes,
+                              void* out, hipStream_t s);
 
 // ---- quantise --------------------------------------------------------------------------
 hipError_t launch_quantize(const void* in, int in_dtype, int64_t n_mat, int rows, int cols,
@@ -51,6 +56,10 @@ struct Segment {
     void* out;                 // GEMM1: act [rows, N/2]; GEMM2: y [rows, N]
     float* out_scales;         // GEMM1 e4m3: act scales [rows, N/2/128]
     void* z_out;               // GEMM1 optional: Z [rows, N] in the activation dtype
+    int rows_total;            // rows of `a` (and of `out`)
+    int a_kblock;              // 1: `a` is K-blocked ([K*eb/128][rows_total][128 bytes])
+    int w_kblock;              // 1: each group's [N, K] weight is K-blocked
+    int out_kblock;            // 1: GEMM1's `out` (act) is K-blocked
 };
 
 struct GemmPlan {

@@ -110,11 +110,13 @@ __global__ __launch_bounds__(64) void perm_rank_kernel(const int32_t* __restrict
     }
 }
 
-// Row copy: 4 tokens per 256-thread block, 16-byte chunks.
+// Row copy: 4 tokens per 256-thread block, 16-byte chunks. K-blocked x_perm: 16-byte chunk
+// c of row r goes to chunk (c / 4) * A * 4 + r * 4 + c % 4 (64-byte K slices).
 __global__ __launch_bounds__(256) void perm_copy_kernel(const uint4* __restrict__ x,
                                                         const int32_t* __restrict__ pos,
-                                                        int T, int row_chunks, int k,
+                                                        int T, int row_chunks, int k, int kblock,
                                                         uint4* __restrict__ x_perm) {
+    const size_t A = (size_t)T * k;
     const int lane = threadIdx.x % kWave;
     const int t = blockIdx.x * 4 + threadIdx.x / kWave;
     if (t >= T) return;
@@ -127,17 +129,21 @@ __global__ __launch_bounds__(256) void perm_copy_kernel(const uint4* __restrict_
         uint4 v = ok ? xr[c] : make_uint4(0, 0, 0, 0);
         for (int j = 0; j < k; ++j) {
             int r = __shfl(my_pos, j);
-            if (ok) x_perm[(size_t)r * row_chunks + c] = v;
+            const size_t o = kblock ? ((size_t)(c / 4) * A + r) * 4 + c % 4
+                                    : (size_t)r * row_chunks + c;
+            if (ok) x_perm[o] = v;
         }
     }
 }
 
 // e4m3 row quantise + copy. A wavefront covers 512 columns per step: 16 lanes per
 // 128-column block, 8 bf16 values (16 bytes) per lane.
+// K-blocked x_perm: 8-byte chunk c of row r goes to chunk (c / 8) * A * 8 + r * 8 + c % 8.
 __global__ __launch_bounds__(256) void perm_quant_copy_kernel(
     const uint4* __restrict__ x, const int32_t* __restrict__ pos, int T, int H, int k,
-    uint2* __restrict__ x_perm, float* __restrict__ x_perm_scales, uint2* __restrict__ x_q,
-    float* __restrict__ x_q_scales) {
+    int kblock, uint2* __restrict__ x_perm, float* __restrict__ x_perm_scales,
+    uint2* __restrict__ x_q, float* __restrict__ x_q_scales) {
+    const size_t A = (size_t)T * k;
     const int lane = threadIdx.x % kWave;
     const int t = blockIdx.x * 4 + threadIdx.x / kWave;
     if (t >= T) return;
@@ -179,7 +185,9 @@ __global__ __launch_bounds__(256) void perm_quant_copy_kernel(
         for (int j = 0; j < k; ++j) {
             int r = __shfl(my_pos, j);
             if (ok) {
-                x_perm[(size_t)r * row_chunks + c] = packed;
+                const size_t o = kblock ? ((size_t)(c / 8) * A + r) * 8 + c % 8
+                                        : (size_t)r * row_chunks + c;
+                x_perm[o] = packed;
                 if (leader) x_perm_scales[(size_t)r * nblk + blk] = sc;
             }
         }
@@ -194,7 +202,7 @@ size_t permute_ws_bytes(int T, int k, int E) {
     return nchunk * (size_t)E * sizeof(int32_t);
 }
 
-hipError_t launch_permute(int mode, const void* x, const int32_t* topk_idx,
+hipError_t launch_permute(int mode, int kblock, const void* x, const int32_t* topk_idx,
                           const float* topk_gate, int T, int H, int E, int k,
                           int32_t* counts, int32_t* offsets, int32_t* pos, int32_t* src,
                           float* gate_perm, void* x_perm, float* x_perm_scales, void* x_q,
@@ -211,13 +219,13 @@ hipError_t launch_permute(int mode, const void* x, const int32_t* topk_idx,
                                                              gate_perm);
     const int blocks = (T + 3) / 4;
     if (mode == 2) {
-        perm_quant_copy_kernel<<<blocks, 256, 0, s>>>((const uint4*)x, pos, T, H, k,
+        perm_quant_copy_kernel<<<blocks, 256, 0, s>>>((const uint4*)x, pos, T, H, k, kblock,
                                                       (uint2*)x_perm, x_perm_scales,
                                                       (uint2*)x_q, x_q_scales);
     } else {
         const int elem = mode == 0 ? 4 : 2;
         perm_copy_kernel<<<blocks, 256, 0, s>>>((const uint4*)x, pos, T, H * elem / 16, k,
-                                                (uint4*)x_perm);
+                                                kblock, (uint4*)x_perm);
     }
     return hipGetLastError();
 }

@@ -45,3 +45,23 @@ def sample_rows(offsets, extra_per_group=1, seed=0):
         if b > a:
             rows += [a, b - 1] + list(rng.integers(a, b, extra_per_group))
     return np.unique(np.array(rows, np.int64))
+
+
+def unblock(t, rows: int, cols: int):
+    """K-blocked [rows, cols] tensor -> row-major copy (torch, any device): the inverse of
+    the layout [cols * eb / 64][rows][64 bytes], written with plain reshapes."""
+    eb = t.element_size()
+    b = t.contiguous().view(torch.uint8).reshape(-1)
+    n = b.numel() // (rows * cols * eb)
+    b = b.reshape(n, cols * eb // 64, rows, 64).permute(0, 2, 1, 3).reshape(n, rows, cols * eb)
+    out = b.contiguous().view(t.dtype).reshape(n, rows, cols)
+    return out[0] if t.dim() == 2 else out
+
+
+def block(t):
+    """Row-major [.., rows, cols] tensor -> K-blocked copy (the forward re-layout, reshapes)."""
+    eb = t.element_size()
+    rows, cols = t.shape[-2], t.shape[-1]
+    b = t.contiguous().view(torch.uint8).reshape(-1, rows, cols * eb // 64, 64)
+    b = b.permute(0, 2, 1, 3).contiguous().reshape(-1)
+    return b.view(t.dtype).reshape(t.shape)

@@ -135,3 +135,21 @@ def test_quantize_argument_checks(moe):
     assert L.moe_quantize_e4m3(d, 1, 1, 100, 128, 128, 128, d, d, None) == 1
     assert L.moe_quantize_e4m3(d, 1, 1, 128, 128, 64, 128, d, d, None) == 2
     assert L.moe_quantize_e4m3(d, 5, 1, 128, 128, 1, 128, d, d, None) == 1
+
+
+def test_layout_validation(moe):
+    """Layout fields: only 0/1; fp32 supports row-major only; the pack call checks sizes."""
+    c = cfgc(moe, a_layout=2)
+    assert ws_size(moe, c, moe.OP_PERMUTE)[0] == 1               # MOE_ERR_INVALID_ARG
+    c = cfgc(moe, base="tiny_fp32", w_layout=1)
+    assert ws_size(moe, c, moe.OP_PERMUTE)[0] == 2               # MOE_ERR_UNSUPPORTED
+    c = cfgc(moe, a_layout=1, w_layout=1)
+    st, n = ws_size(moe, c, moe.OP_LAYER_FORWARD)
+    assert st == 0 and n > 0
+    L = moe.lib()
+    p = C.c_void_p(0x1000)
+    q = C.c_void_p(0x2000)
+    assert L.moe_pack_kblock(p, 1, 16, 24, 2, q, None) == 1      # 48 bytes per row: not 64k
+    assert L.moe_pack_kblock(p, 1, 16, 32, 3, q, None) == 1      # element size
+    assert L.moe_pack_kblock(p, 0, 16, 32, 2, q, None) == 1      # no matrices
+    assert L.moe_pack_kblock(p, 1, 16, 32, 2, p, None) == 1      # in place

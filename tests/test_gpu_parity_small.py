@@ -172,3 +172,90 @@ def test_deterministic(moe, name):
     y2, _ = moe.layer_forward(*args, **kw)
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
+
+
+# ---------------------------------------------------------------------------------------
+# K-blocked layouts (expert-grouped activations and packed expert weights)
+# ---------------------------------------------------------------------------------------
+from helpers import block, unblock  # noqa: E402
+
+BF_NAMES = [n for n in NAMES if SMALL[n].act_dtype != mi.F32]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.uint8, torch.float32])
+def test_pack_kblock_matches_reshape(moe, dtype):
+    print(f"[pack_kblock] {dtype}", flush=True)
+    g = torch.Generator().manual_seed(3)
+    t = (torch.randn(3, 40, 256, generator=g) * 7).to(dtype)
+    got = moe.pack_kblock(t.cuda())
+    torch.cuda.synchronize()
+    assert torch.equal(got.cpu(), block(t))
+    assert torch.equal(unblock(got.cpu(), 40, 256), t)
+
+
+@pytest.mark.parametrize("name", BF_NAMES)
+def test_permute_kblock(moe, name):
+    c = case(name)
+    cfg, inp, perm = c["cfg"].replace(a_layout=1), c["inp"], c["perm"]
+    print(f"[permute kblock] {name}", flush=True)
+    out = moe.permute(cfg, inp.x.cuda(), torch.from_numpy(c["idx"]).cuda(),
+                      torch.from_numpy(c["gate"]).cuda())
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out["pos"].cpu().numpy(), perm["pos"])
+    got = unblock(out["x_perm"].cpu(), cfg.A, cfg.H)
+    x_ref = oracle.gather_rows(oracle.as_np(inp.x)[0], perm["pos"])
+    np.testing.assert_array_equal(oracle.as_np(got)[0], x_ref)
+
+
+@pytest.mark.parametrize("name", BF_NAMES)
+def test_grouped_gemm_kblock(moe, name):
+    """K-blocked x_perm / act and packed weights give the oracle's results, and exactly the
+    row-major path's results (same MFMA order)."""
+    c = case(name)
+    base = c["cfg"]
+    cfg = base.replace(a_layout=1, w_layout=1)
+    inp, perm = c["inp"], c["perm"]
+    print(f"[grouped_gemm kblock] {name}", flush=True)
+    xp = oracle_x_perm(c)
+    offs = torch.from_numpy(perm["offsets"]).cuda()
+    gp = torch.from_numpy(perm["gate_perm"]).cuda()
+    w13, w2 = inp.w13.cuda(), inp.w2.cuda()
+    sh = dict(x_shared=inp.x.cuda(), ws13=inp.ws13.cuda(), ws2=inp.ws2.cuda()) if cfg.shared_F else {}
+    ref_rows = moe.grouped_gemm_swiglu(base, xp.cuda(), offs, gp, w13, w2, **sh)
+    shb = dict(x_shared=inp.x.cuda(), ws13=moe.pack_kblock(inp.ws13.cuda()),
+               ws2=moe.pack_kblock(inp.ws2.cuda())) if cfg.shared_F else {}
+    out = moe.grouped_gemm_swiglu(cfg, moe.pack_kblock(xp.cuda()), offs, gp,
+                                  moe.pack_kblock(w13), moe.pack_kblock(w2), **shb)
+    torch.cuda.synchronize()
+    act = unblock(out["act"].cpu(), cfg.A, cfg.F)
+    assert torch.equal(act, ref_rows["act"].cpu())
+    assert torch.equal(out["y_perm"].cpu(), ref_rows["y_perm"].cpu())
+    if cfg.shared_F:
+        assert torch.equal(out["shared_y"].cpu(), ref_rows["shared_y"].cpu())
+    rows = np.arange(cfg.A)
+    _, act_ref, y_ref = oracle.expert_rows(xp, perm["offsets"], perm["gate_perm"], inp.w13,
+                                           inp.w2, rows)
+    assert rel_err(act, act_ref) <= tol(cfg)
+    assert rel_err(out["y_perm"], y_ref) <= tol(cfg)
+
+
+@pytest.mark.parametrize("name", BF_NAMES)
+def test_layer_forward_packed_weights(moe, name):
+    c = case(name)
+    cfg, inp = c["cfg"].replace(w_layout=1), c["inp"]
+    print(f"[layer_forward packed] {name}", flush=True)
+    pk = lambda t: None if t is None else moe.pack_kblock(t.cuda())  # noqa: E731
+    y, ex = moe.layer_forward(cfg, inp.x.cuda(), inp.w_router.cuda(), pk(inp.w13), pk(inp.w2),
+                              to_dev(inp.logit_bias), to_dev(inp.sel_bias),
+                              torch.from_numpy(c["logits"]).cuda(), ws13=pk(inp.ws13),
+                              ws2=pk(inp.ws2), want=("topk_idx",))
+    y0, _ = moe.layer_forward(c["cfg"], inp.x.cuda(), inp.w_router.cuda(), inp.w13.cuda(),
+                              inp.w2.cuda(), to_dev(inp.logit_bias), to_dev(inp.sel_bias),
+                              torch.from_numpy(c["logits"]).cuda(), ws13=to_dev(inp.ws13),
+                              ws2=to_dev(inp.ws2))
+    torch.cuda.synchronize()
+    assert torch.equal(y, y0)
+    np.testing.assert_array_equal(ex["topk_idx"].cpu().numpy(), c["idx"])
+    ref = oracle.layer_tokens(inp.x, c["idx"], c["gate"], inp.w13, inp.w2, np.arange(cfg.T),
+                              inp.ws13, inp.ws2)
+    assert rel_err(y, ref) <= tol(cfg)
