@@ -137,7 +137,9 @@ def zipf_logit_bias(cfg: MoEConfig, c: float | None = None) -> np.ndarray:
     E = cfg.E
     if c is None:
         with open(zipf_scale_path()) as f:
-            c = float(json.load(f)[cfg.name]["c"])
+            table = json.load(f)
+        key = cfg.name if cfg.name in table else cfg.name.split("_small")[0]
+        c = float(table[key]["c"])
     ranks = _rng(cfg.cfg_id, TAG_ZIPF).permutation(E) + 1          # rank of expert e, 1-based
     p = np.arange(1, E + 1, dtype=np.float64) ** (-cfg.zipf_alpha)
     p /= p.sum()

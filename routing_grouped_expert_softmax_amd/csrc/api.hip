@@ -302,12 +302,16 @@ int moe_grouped_gemm_swiglu(const moe_config* cfg, const void* x_perm,
         return MOE_ERR_INVALID_ARG;
     const bool fp8 = cfg->w_dtype == MOE_E4M3;
     if (fp8) {
-        if (!x_perm_scales || !w13_scales || !w2_scales || !act_scales) return MOE_ERR_INVALID_ARG;
-        return MOE_ERR_UNSUPPORTED;          // e4m3 expert GEMMs: see moe_config.w_dtype
-    }
-    if (x_perm_scales || w13_scales || w2_scales || act_scales || x_shared_scales ||
-        ws13_scales || ws2_scales)
+        if (!x_perm_scales || !w13_scales || !w2_scales || !act_scales || z_out)
+            return MOE_ERR_INVALID_ARG;
+        if (cfg->shared_F && (!x_shared_scales || !ws13_scales || !ws2_scales))
+            return MOE_ERR_INVALID_ARG;
+        if (!cfg->shared_F && (x_shared_scales || ws13_scales || ws2_scales))
+            return MOE_ERR_INVALID_ARG;
+    } else if (x_perm_scales || w13_scales || w2_scales || act_scales || x_shared_scales ||
+               ws13_scales || ws2_scales) {
         return MOE_ERR_INVALID_ARG;
+    }
     if (cfg->shared_F) {
         if (!x_shared || !ws13 || !ws2 || !shared_y) return MOE_ERR_INVALID_ARG;
     } else if (x_shared || ws13 || ws2 || shared_y) {
@@ -319,13 +323,20 @@ int moe_grouped_gemm_swiglu(const moe_config* cfg, const void* x_perm,
                        ws2_scales, act, act_scales, y_perm, shared_y, z_out, ws, stream);
 }
 
-static int check_gemm_dtypes(const moe_config* cfg, const float* a_scales,
+// Scale pointers of one GEMM half: required exactly in e4m3 mode (out_scales only when the
+// half writes e4m3, i.e. GEMM1's act).
+static int check_gemm_dtypes(const moe_config* cfg, bool e4m3_out, const float* a_scales,
                              const float* w_scales, const float* out_scales,
                              const float* sh_a_scales, const float* sh_w_scales,
                              const float* sh_out_scales) {
     if (cfg->w_dtype == MOE_E4M3) {
         if (!a_scales || !w_scales) return MOE_ERR_INVALID_ARG;
-        return MOE_ERR_UNSUPPORTED;          // e4m3 expert GEMMs: see moe_config.w_dtype
+        if (e4m3_out != (out_scales != nullptr)) return MOE_ERR_INVALID_ARG;
+        if (cfg->shared_F && (!sh_a_scales || !sh_w_scales)) return MOE_ERR_INVALID_ARG;
+        if (cfg->shared_F && e4m3_out != (sh_out_scales != nullptr)) return MOE_ERR_INVALID_ARG;
+        if (!cfg->shared_F && (sh_a_scales || sh_w_scales || sh_out_scales))
+            return MOE_ERR_INVALID_ARG;
+        return MOE_OK;
     }
     if (a_scales || w_scales || out_scales || sh_a_scales || sh_w_scales || sh_out_scales)
         return MOE_ERR_INVALID_ARG;
@@ -347,8 +358,9 @@ int moe_grouped_gemm_up(const moe_config* cfg, const void* x_perm, const float* 
     } else if (x_shared || ws13 || shared_act) {
         return MOE_ERR_INVALID_ARG;
     }
-    st = check_gemm_dtypes(cfg, x_perm_scales, w13_scales, act_scales, x_shared_scales,
+    st = check_gemm_dtypes(cfg, true, x_perm_scales, w13_scales, act_scales, x_shared_scales,
                            ws13_scales, shared_act_scales);
+    if (!st && cfg->w_dtype == MOE_E4M3 && z_out) st = MOE_ERR_INVALID_ARG;
     if (st) return st;
     if (ws_bytes < sched_ws_bytes(cfg)) return MOE_ERR_WORKSPACE;
     return run_up(cfg, cfg->a_layout, x_perm, x_perm_scales, offsets, gate_perm, w13, w13_scales, x_shared,
@@ -369,8 +381,8 @@ int moe_grouped_gemm_down(const moe_config* cfg, const void* act, const float* a
     } else if (shared_act || ws2 || shared_y) {
         return MOE_ERR_INVALID_ARG;
     }
-    st = check_gemm_dtypes(cfg, act_scales, w2_scales, nullptr, shared_act_scales, ws2_scales,
-                           nullptr);
+    st = check_gemm_dtypes(cfg, false, act_scales, w2_scales, nullptr, shared_act_scales,
+                           ws2_scales, nullptr);
     if (st) return st;
     if (ws_bytes < sched_ws_bytes(cfg)) return MOE_ERR_WORKSPACE;
     return run_down(cfg, cfg->a_layout, act, act_scales, offsets, w2, w2_scales, shared_act,
@@ -399,8 +411,9 @@ int moe_layer_forward(const moe_config* cfg, const void* x, const void* w_router
     if (!logits_in && !w_router) return MOE_ERR_INVALID_ARG;
     const bool fp8 = cfg->w_dtype == MOE_E4M3;
     if (fp8 && (!w13_scales || !w2_scales)) return MOE_ERR_INVALID_ARG;
-    if (fp8) return MOE_ERR_UNSUPPORTED;
+    if (!fp8 && (w13_scales || w2_scales || ws13_scales || ws2_scales)) return MOE_ERR_INVALID_ARG;
     if (cfg->shared_F && (!ws13 || !ws2)) return MOE_ERR_INVALID_ARG;
+    if (fp8 && cfg->shared_F && (!ws13_scales || !ws2_scales)) return MOE_ERR_INVALID_ARG;
     LayerWs L = carve_layer(cfg, nullptr);
     if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
     L = carve_layer(cfg, ws);

@@ -470,6 +470,300 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs ga) {
 }
 
 // ---------------------------------------------------------------------------------------
+// e4m3 MFMA kernel: block-scaled fp8 operands (1 x 128 activation scales, 128 x 128 weight
+// scales), fp32 accumulation.
+//
+// One LDS stage holds one 128-wide K block: [BM A rows | BN B rows] x 128 bytes plus the
+// fp32 scales of the BM A rows for that block (each wave DMAs 16 of them). The MFMA
+// (v_mfma_scale_f32_32x32x64_f8f6f4 with unit E8M0 scales) sums the K block into a partial
+// tile, which is then promoted into the accumulator with the block's two scales:
+//   acc[m][n] += partial[m][n] * s_a[m][kb] * s_w[n / 128][kb].
+// GEMM1's tile spans 128 act columns, i.e. exactly one 1 x 128 quantisation block of act,
+// so the epilogue folds the gate in, reduces each row's amax across lanes and waves (LDS),
+// and writes the e4m3 codes and their scale directly.
+// ---------------------------------------------------------------------------------------
+template <int KIND, int BM, int BN, int WM, int WN, int STAGES>
+struct F8Cfg {
+    static constexpr int kThreads = WM * WN * kWave;
+    static constexpr int kWaves = WM * WN;
+    static constexpr int kRowBytes = 128;                   // 128 e4m3 of K
+    static constexpr int kRows = BM + BN;
+    static constexpr int kTileBytes = kRows * kRowBytes;
+    static constexpr int kScaleBytes = kWaves * 256;        // 64 floats per wave (16 used)
+    static constexpr int kStageBytes = kTileBytes + kScaleBytes;
+    static constexpr int kDma = kRows / 8 / kWaves;         // tile DMAs per wave per stage
+    static constexpr int kVm = kDma + 1;                    // + the scale DMA
+    static constexpr int kTM = BM / WM / 32;
+    static constexpr int kTN = BN / WN / 32;
+    static constexpr int kStages = STAGES;
+    static constexpr size_t kLds = (size_t)STAGES * kStageBytes;
+    static_assert(BM == 16 * kWaves, "one 16-row scale group per wave");
+    static_assert(kRows % (8 * kWaves) == 0, "DMA split");
+    static_assert(KIND == 1 || (kTN == 2 && BN == 256), "GEMM1: one 128-column act block");
+    static_assert(kLds <= 160 * 1024, "LDS");
+    static_assert(STAGES >= 2 && (STAGES - 2) * kVm < 64, "vmcnt");
+    static_assert(BM * WN * 4 <= kStageBytes, "epilogue amax buffer");
+};
+
+MOE_DEVICE i32x8_t lds_frag32(const uint8_t* p0, const uint8_t* p1) {
+    const i32x4_t lo = *(const i32x4_t*)p0, hi = *(const i32x4_t*)p1;
+    return i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+template <class C, int NV, class Issue>
+MOE_DEVICE void e4m3_kloop(int nk, const uint8_t* lds, Issue& issue, const int (&a_off)[C::kTM],
+                           const int (&b_off)[C::kTN], const int (&co)[2][2],
+                           const int (&srow)[C::kTM][4], const float* __restrict__ wsc,
+                           const int (&wsc_off)[C::kTN], f32x16_t (&acc)[C::kTM][C::kTN]) {
+    constexpr int STAGES = C::kStages;
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s)
+        if (s < nk) issue(s, s);
+    int stage = 0;
+    for (int kt = 0; kt < nk; ++kt) {
+        const int later = nk - 1 - kt;
+        if (later >= STAGES - 2) wait_vm_lgkm0<(STAGES - 2) * C::kVm>();
+        else if (later >= 2) wait_vm_lgkm0<cmin(2, STAGES - 2) * C::kVm>();
+        else if (later >= 1) wait_vm_lgkm0<cmin(1, STAGES - 2) * C::kVm>();
+        else wait_vm_lgkm0<0>();
+        block_sync();
+        {
+            const int kn = kt + STAGES - 1;
+            int sn = stage + STAGES - 1;
+            if (sn >= STAGES) sn -= STAGES;
+            if (kn < nk) issue(kn, sn);
+        }
+        if (NV > 0) {
+            constexpr int NVv = NV > 0 ? NV : 1;
+            const uint8_t* base = lds + stage * C::kStageBytes;
+            const float* sa_l = (const float*)(base + C::kTileBytes);
+            float sw[C::kTN];
+#pragma unroll
+            for (int j = 0; j < C::kTN; ++j) sw[j] = wsc[wsc_off[j] + kt];
+            i32x8_t bv[2][C::kTN];
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                for (int j = 0; j < C::kTN; ++j)
+                    bv[s2][j] = lds_frag32(base + b_off[j] + co[s2][0], base + b_off[j] + co[s2][1]);
+#pragma unroll
+            for (int i = 0; i < NVv; ++i) {
+                const i32x8_t a0 = lds_frag32(base + a_off[i] + co[0][0], base + a_off[i] + co[0][1]);
+                const i32x8_t a1 = lds_frag32(base + a_off[i] + co[1][0], base + a_off[i] + co[1][1]);
+                float sa[16];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f32x4_t v = *(const f32x4_t*)(sa_l + srow[i][q]);
+                    sa[4 * q + 0] = v[0]; sa[4 * q + 1] = v[1];
+                    sa[4 * q + 2] = v[2]; sa[4 * q + 3] = v[3];
+                }
+#pragma unroll
+                for (int j = 0; j < C::kTN; ++j) {
+                    f32x16_t pt = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        a0, bv[0][j], f32x16_t{}, 0, 0, 0, 0x7F7F7F7F, 0, 0x7F7F7F7F);
+                    pt = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        a1, bv[1][j], pt, 0, 0, 0, 0x7F7F7F7F, 0, 0x7F7F7F7F);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        acc[i][j][r] = fmaf(pt[r], sa[r] * sw[j], acc[i][j][r]);
+                }
+            }
+        }
+        if (++stage == STAGES) stage = 0;
+    }
+}
+
+template <int KIND, int BM, int BN, int WM, int WN, int STAGES>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_e4m3_kernel(GemmArgs ga) {
+    using C = F8Cfg<KIND, BM, BN, WM, WN, STAGES>;
+    extern __shared__ __align__(16) uint8_t lds[];
+    int mt, nt;
+    if (!pick_tile(ga, mt, nt)) return;
+    const int4 ti = ga.tiles[mt];
+    const int seg = ti.x >> 20, g = ti.x & 0xFFFFF;
+    const int m0 = ti.y, Mg = ti.z, rbase = ti.w;
+    const SegDev S = seg == 0 ? ga.seg[0] : ga.seg[1];
+    const int N = ga.N, K = ga.K, KB = K / 128;
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int wm = wave / WN, wn = wave % WN;
+    const int live = Mg - m0 < BM ? Mg - m0 : BM;
+    int nvi = (live - wm * (BM / WM) + 31) / 32;
+    nvi = nvi < 0 ? 0 : (nvi > C::kTM ? C::kTM : nvi);
+    nvi = __builtin_amdgcn_readfirstlane(nvi);
+
+    // ---- tile DMA sources (as the bf16 kernel, 128-byte stage rows)
+    const uint8_t* src[C::kDma];
+#pragma unroll
+    for (int q = 0; q < C::kDma; ++q) {
+        const int r = 8 * (wave + q * C::kWaves) + lane / 8;
+        const int c = (lane % 8) ^ (r & 7);
+        const uint8_t* rowp;
+        if (r < BM) {
+            const int rr = m0 + r < Mg ? m0 + r : Mg - 1;
+            rowp = (const uint8_t*)S.a + (size_t)(rbase + rr) * S.a_row;
+        } else {
+            const int rb = r - BM;
+            int wrow;
+            if (KIND == 0)
+                wrow = rb < BN / 2 ? nt * (BN / 2) + rb : N / 2 + nt * (BN / 2) + (rb - BN / 2);
+            else
+                wrow = nt * BN + rb;
+            rowp = (const uint8_t*)S.w + (size_t)g * S.w_mat + (size_t)wrow * S.w_row;
+        }
+        const size_t step = r < BM ? S.a_kstep : S.w_kstep;
+        src[q] = rowp + (size_t)(c / 4) * step + (c % 4) * 16;
+    }
+    const size_t a_step = S.a_kstep, w_step = S.w_kstep;
+    // A-row scales: wave w loads rows 16 w + lane % 16 of this tile
+    const float* ssrc;
+    {
+        const int r = 16 * wave + lane % 16;
+        const int rr = m0 + r < Mg ? m0 + r : Mg - 1;
+        ssrc = S.a_scales + (size_t)(rbase + rr) * KB;
+    }
+    auto issue = [&](int kstep, int stage) {
+        MOE_LDS uint8_t* base = (MOE_LDS uint8_t*)lds + stage * C::kStageBytes;
+#pragma unroll
+        for (int q = 0; q < C::kDma; ++q)
+            __builtin_amdgcn_global_load_lds(
+                (const void*)(src[q] + (size_t)kstep * 2 * (q * 8 * C::kWaves < BM ? a_step : w_step)),
+                (MOE_LDS void*)(base + (wave + q * C::kWaves) * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(ssrc + kstep),
+                                         (MOE_LDS void*)(base + C::kTileBytes + wave * 256), 4, 0, 0);
+    };
+
+    int a_off[C::kTM], b_off[C::kTN];
+#pragma unroll
+    for (int i = 0; i < C::kTM; ++i) a_off[i] = (wm * (BM / WM) + i * 32 + lane % 32) * 128;
+#pragma unroll
+    for (int j = 0; j < C::kTN; ++j) {
+        int row;
+        if (KIND == 0) {
+            constexpr int half = C::kTN / 2;
+            const int col = wn * (BN / 2 / WN) + (j % half) * 32 + lane % 32;
+            row = BM + (j < half ? col : BN / 2 + col);
+        } else {
+            row = BM + wn * (BN / WN) + j * 32 + lane % 32;
+        }
+        b_off[j] = row * 128;
+    }
+    // the lane's 32 bytes of K sub-step s: logical chunks 4 s + 2 h, 4 s + 2 h + 1
+    int co[2][2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) co[s][u] = (((4 * s + 2 * (lane / 32) + u) ^ (lane & 7)) * 16);
+    // LDS float index of the scales of rows (r/4)*8 + (l/32)*4 + [0,4) of sub-tile i
+    int srow[C::kTM][4];
+#pragma unroll
+    for (int i = 0; i < C::kTM; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int row = wm * (BM / WM) + i * 32 + q * 8 + (lane / 32) * 4;
+            srow[i][q] = (row / 16) * 64 + row % 16;
+        }
+    // weight-scale offsets (per sub-tile j): [g][n_block][kb]
+    const int nbn = N / 128;
+    int wsc_off[C::kTN];
+#pragma unroll
+    for (int j = 0; j < C::kTN; ++j) {
+        int nb;
+        if (KIND == 0) nb = j < C::kTN / 2 ? nt : N / 256 + nt;   // gate block nt, up block F/128 + nt
+        else nb = (nt * BN + wn * (BN / WN) + j * 32) / 128;
+        wsc_off[j] = (g * nbn + nb) * KB;
+    }
+
+    f32x16_t acc[C::kTM][C::kTN];
+#pragma unroll
+    for (int i = 0; i < C::kTM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::kTN; ++j) acc[i][j] = f32x16_t{};
+    switch (nvi) {
+#define MOE_F8_CASE(V)                                                                      \
+    case V:                                                                                 \
+        if (V <= C::kTM) {                                                                  \
+            constexpr int NV = V <= C::kTM ? V : C::kTM;                                    \
+            e4m3_kloop<C, NV>(KB, lds, issue, a_off, b_off, co, srow, S.w_scales, wsc_off,  \
+                              acc);                                                         \
+        }                                                                                   \
+        break;
+    MOE_F8_CASE(0)
+    MOE_F8_CASE(1)
+    MOE_F8_CASE(2)
+    MOE_F8_CASE(3)
+    MOE_F8_CASE(4)
+#undef MOE_F8_CASE
+    default: break;
+    }
+
+    if (KIND == 1) {
+        uint16_t* out = (uint16_t*)S.out;
+#pragma unroll
+        for (int i = 0; i < C::kTM; ++i) {
+            if (i >= nvi) continue;
+#pragma unroll
+            for (int j = 0; j < C::kTN; ++j) {
+                const int col = nt * BN + wn * (BN / WN) + j * 32 + lane % 32;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = wm * (BM / WM) + i * 32 + (r / 4) * 8 + (lane / 32) * 4 + r % 4;
+                    if (m0 + row >= Mg) continue;
+                    const size_t grow = (size_t)rbase + m0 + row;
+                    out[grow * N + col] = f32_to_bf16(acc[i][j][r]);
+                }
+            }
+        }
+        return;
+    }
+    // ---- GEMM1: act = gate * silu(Z_g) * Z_u, quantised per row over this tile's 128
+    // act columns (one 1 x 128 block): amax over lanes (shuffles), then over waves (LDS)
+    const int F = N / 2;
+    float av[C::kTM][16];
+    float* amax_l = (float*)lds;                       // [WN][BM]
+#pragma unroll
+    for (int i = 0; i < C::kTM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = wm * (BM / WM) + i * 32 + (r / 4) * 8 + (lane / 32) * 4 + r % 4;
+            const int lr = m0 + row < Mg ? row : live - 1;
+            const float gt = S.gate ? S.gate[(size_t)rbase + m0 + lr] : 1.0f;
+            av[i][r] = gt * (silu_f32(acc[i][0][r]) * acc[i][1][r]);
+        }
+    block_sync();                                      // every wave is done with the stages
+#pragma unroll
+    for (int i = 0; i < C::kTM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float m = fabsf(av[i][r]);
+#pragma unroll
+            for (int off = 1; off < 32; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+            const int row = wm * (BM / WM) + i * 32 + (r / 4) * 8 + (lane / 32) * 4 + r % 4;
+            if (lane % 32 == 0) amax_l[wn * BM + row] = m;
+        }
+    __syncthreads();
+    uint8_t* outq = (uint8_t*)S.out;
+    const int col = nt * (BN / 2) + wn * (BN / 2 / WN) + lane % 32;    // act column
+#pragma unroll
+    for (int i = 0; i < C::kTM; ++i) {
+        if (i >= nvi) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = wm * (BM / WM) + i * 32 + (r / 4) * 8 + (lane / 32) * 4 + r % 4;
+            if (m0 + row >= Mg) continue;
+            float m = 0.0f;
+#pragma unroll
+            for (int w = 0; w < WN; ++w) m = fmaxf(m, amax_l[w * BM + row]);
+            const float sc = e4m3_scale(m);
+            const size_t grow = (size_t)rbase + m0 + row;
+            const size_t oi = S.out_kblock ? ((size_t)(col / 64) * S.rows_total + grow) * 64 + col % 64
+                                           : grow * F + col;
+            outq[oi] = (uint8_t)e4m3_rne_sat(av[i][r] / sc);
+            if (wn == 0 && lane % 32 == 0) S.out_scales[grow * (F / 128) + nt] = sc;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
 // fp32 kernel (FMA): 64 rows x 64 columns per 256-thread block, K in steps of 16.
 // GEMM1: the 64 columns are 32 gate + the 32 matching up columns; thread (ty, tx) computes
 // rows 4ty..4ty+3 and act columns 2tx, 2tx+1 (gate and up each).
@@ -589,12 +883,39 @@ constexpr int cfg_bm() { return BM; }
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, int LOADREG>
 constexpr int cfg_bn() { return BN; }
 
+// e4m3 tile configuration (BM, BN, WM, WN, STAGES), both GEMMs
+#ifndef MOE_F8_CFG
+#define MOE_F8_CFG 128, 256, 2, 4, 3
+#endif
+
+template <int KIND, int BM, int BN, int WM, int WN, int STAGES>
+hipError_t run_e4m3(const GemmArgs& ga, int nblocks, hipStream_t s) {
+    using C = F8Cfg<KIND, BM, BN, WM, WN, STAGES>;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(
+            (const void*)gemm_e4m3_kernel<KIND, BM, BN, WM, WN, STAGES>,
+            hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::kLds);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    gemm_e4m3_kernel<KIND, BM, BN, WM, WN, STAGES><<<nblocks, C::kThreads, C::kLds, s>>>(ga);
+    return hipGetLastError();
+}
+
+template <int BM, int BN, int WM, int WN, int STAGES>
+constexpr int f8_bm() { return BM; }
+template <int BM, int BN, int WM, int WN, int STAGES>
+constexpr int f8_bn() { return BN; }
+
 int bm_for(int kind, int dtype) {
     if (dtype == 0) return kF32BM;
+    if (dtype == 2) return f8_bm<MOE_F8_CFG>();
     return kind == 0 ? cfg_bm<MOE_BF_UP_CFG>() : cfg_bm<MOE_BF_DOWN_CFG>();
 }
 int bn_for(int kind, int dtype) {
     if (dtype == 0) return 64;
+    if (dtype == 2) return f8_bn<MOE_F8_CFG>();
     return kind == 0 ? cfg_bn<MOE_BF_UP_CFG>() : cfg_bn<MOE_BF_DOWN_CFG>();
 }
 
@@ -659,6 +980,10 @@ hipError_t launch_grouped_gemm(int kind, int dtype, const Segment* segs, int nse
     if (dtype == 1) {
         if (kind == 0) return run_bf16<0, MOE_BF_UP_CFG>(ga, (int)nblocks, s);
         return run_bf16<1, MOE_BF_DOWN_CFG>(ga, (int)nblocks, s);
+    }
+    if (dtype == 2) {
+        if (kind == 0) return run_e4m3<0, MOE_F8_CFG>(ga, (int)nblocks, s);
+        return run_e4m3<1, MOE_F8_CFG>(ga, (int)nblocks, s);
     }
     return hipErrorInvalidValue;
 }

@@ -31,6 +31,14 @@ SMALL = {
                                         shared_F=384),
 }
 
+# Small copies of the skewed e4m3 workload (same Zipf-biased router, e4m3 expert GEMMs).
+SMALL_FP8 = {
+    "dsv3_fp8_small": mi.scaled(mi.CONFIGS["dsv3_fp8_skew"], T=520, H=512, F=256,
+                                shared_F=256),
+    "dsv3_fp8_small_kblock": mi.scaled(mi.CONFIGS["dsv3_fp8_skew"], T=300, H=768, F=384,
+                                       shared_F=128, a_layout=1, w_layout=1),
+}
+
 
 def to_dev(t):
     return None if t is None else t.cuda()
