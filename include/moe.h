@@ -211,22 +211,28 @@ int moe_layer_forward(const moe_config* cfg, const void* x, const void* w_router
                       void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Backward of the grouped expert MLP with the gate fold (bf16 operands, fp32
- * accumulation), data and weight gradients as separate grouped GEMMs (the W/D split of
- * the technical summary, section 2.3). Per expert rows R_e, with h = silu(Z_g) * Z_u and
- * act = g * h recomputed from the saved z:
- *   dA     = dy_perm W2_e                      dg[r] = sum_f dA[r, f] h[r, f]
- *   dZ_g   = g dA Z_u silu'(Z_g)               dZ_u  = g dA silu(Z_g)
- *   dx_perm = dZ W13_e                          [M_e, H]
- *   dW2_e  = dy_perm[R_e]^T act[R_e]            [H, F]
- *   dW13_e = dZ[R_e]^T x_perm[R_e]              [2F, H]
- * dy_perm [A, H], x_perm [A, H], z [A, 2F], w13, w2 in bf16 (cfg->act_dtype == MOE_BF16);
- * outputs dx_perm [A, H], dw13 [E, 2F, H], dw2 [E, H, F] bf16 and dgate_perm [A] fp32.
- * Experts with no rows get zero weight gradients. */
+ * accumulation), data and weight gradients as separate grouped GEMMs (the W/D split of the
+ * technical summary, section 2.3). Per expert rows R_e = [offsets[e], offsets[e+1]), with
+ * h = silu(Z_g) * Z_u from the saved z and g = gate_perm[r]:
+ *   dA      = dy_perm W2_e                    dg[r] = sum_f dA[r, f] h[r, f]
+ *   dZ_g    = g dA Z_u silu'(Z_g)             dZ_u  = g dA silu(Z_g)
+ *   dx_perm = dZ W13_e                        [M_e, H]
+ *   dW2_e   = dy_perm[R_e]^T act[R_e]         [H, F]
+ *   dW13_e  = dZ[R_e]^T x_perm[R_e]           [2F, H]
+ * All tensors bf16 and row-major (cfg->act_dtype == MOE_BF16, a_layout = w_layout = 0;
+ * cfg->w_dtype is not used: the backward runs on the bf16 weights): dy_perm [A, H],
+ * x_perm [A, H], z [A, 2F] and act [A, F] (the forward's saved Z and g * h), w13 [E, 2F, H],
+ * w2 [E, H, F]. Outputs dx_perm [A, H], dw13 [E, 2F, H], dw2 [E, H, F] bf16 and
+ * dgate_perm [A] fp32 (may be NULL). gate_perm may be NULL (gate 1 for every row: a shared
+ * expert is one group whose offsets are {0, T}). Experts with no rows get zero weight
+ * gradients. Deterministic: dg is summed per tile, then over tiles in a fixed order.
+ * Workspace: moe_workspace_size(cfg, MOE_OP_GROUPED_GEMM_BWD). */
 int moe_grouped_gemm_swiglu_bwd(const moe_config* cfg, const void* dy_perm,
-                                const void* x_perm, const void* z, const float* gate_perm,
-                                const int32_t* offsets, const void* w13, const void* w2,
-                                void* dx_perm, void* dw13, void* dw2, float* dgate_perm,
-                                void* ws, size_t ws_bytes, hipStream_t stream);
+                                const void* x_perm, const void* z, const void* act,
+                                const float* gate_perm, const int32_t* offsets, const void* w13,
+                                const void* w2, void* dx_perm, void* dw13, void* dw2,
+                                float* dgate_perm, void* ws, size_t ws_bytes,
+                                hipStream_t stream);
 
 /* Re-layout of n_mat row-major matrices [rows, cols] of elem_bytes-byte elements into the
  * K-blocked layout [n_mat][cols * elem_bytes / 64][rows][64 bytes] (see Layouts). A pure

@@ -67,7 +67,7 @@ _SIGS = {
     "moe_grouped_gemm_down": [CFG, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
     "moe_unpermute_combine": [CFG, P, P, P, P, P],
     "moe_layer_forward": [CFG, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
-    "moe_grouped_gemm_swiglu_bwd": [CFG, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
+    "moe_grouped_gemm_swiglu_bwd": [CFG, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
     "moe_quantize_e4m3": [P, I32, I64, I32, I32, I32, I32, P, P, P],
     "moe_pack_kblock": [P, I64, I32, I32, I32, P, P],
 }
@@ -356,8 +356,10 @@ def layer_forward(cfg, x, w_router, w13, w2, logit_bias=None, sel_bias=None, log
     return y, extras
 
 
-def grouped_gemm_swiglu_bwd(cfg, dy_perm, x_perm, z, gate_perm, offsets, w13, w2, ws=None,
-                            stream=None):
+def grouped_gemm_swiglu_bwd(cfg, dy_perm, x_perm, z, act, gate_perm, offsets, w13, w2,
+                            want_dgate=True, ws=None, stream=None):
+    """Backward of the grouped expert MLP (moe_grouped_gemm_swiglu_bwd). gate_perm may be
+    None (gate 1). Returns dict dx_perm, dw13, dw2, dgate_perm (None unless want_dgate)."""
     dev = dy_perm.device
     T, H, E, k, F = cfg.T, cfg.H, cfg.E, cfg.k, cfg.F
     A = T * k
@@ -365,13 +367,14 @@ def grouped_gemm_swiglu_bwd(cfg, dy_perm, x_perm, z, gate_perm, offsets, w13, w2
     out = dict(dx_perm=torch.empty(A, H, dtype=bf, device=dev),
                dw13=torch.empty(E, 2 * F, H, dtype=bf, device=dev),
                dw2=torch.empty(E, H, F, dtype=bf, device=dev),
-               dgate_perm=torch.empty(A, dtype=torch.float32, device=dev))
+               dgate_perm=torch.empty(A, dtype=torch.float32, device=dev) if want_dgate else None)
     if ws is None:
         ws = workspace(cfg, OP_GROUPED_GEMM_BWD, dev)
     c = make_config(cfg)
     _check("moe_grouped_gemm_swiglu_bwd", _lib.moe_grouped_gemm_swiglu_bwd(
         C.byref(c), _ptr(dy_perm, bf, (A, H), "dy_perm"), _ptr(x_perm, bf, (A, H), "x_perm"),
-        _ptr(z, bf, (A, 2 * F), "z"), _ptr(gate_perm, torch.float32, (A,), "gate_perm"),
+        _ptr(z, bf, (A, 2 * F), "z"), _ptr(act, bf, (A, F), "act"),
+        _ptr(gate_perm, torch.float32, (A,), "gate_perm"),
         _ptr(offsets, torch.int32, (E + 1,), "offsets"), _ptr(w13, bf, (E, 2 * F, H), "w13"),
         _ptr(w2, bf, (E, H, F), "w2"), _ptr(out["dx_perm"]), _ptr(out["dw13"]),
         _ptr(out["dw2"]), _ptr(out["dgate_perm"]), _ptr(ws), ws.numel(), _stream(stream)))

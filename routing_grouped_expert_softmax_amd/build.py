@@ -15,7 +15,8 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe_amd.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.hip", "route.hip", "permute.hip", "combine.hip", "grouped_gemm.hip"]
+SOURCES = ["api.hip", "route.hip", "permute.hip", "combine.hip", "grouped_gemm.hip",
+           "grouped_gemm_bwd.hip"]
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

@@ -241,7 +241,10 @@ int moe_workspace_size(const moe_config* cfg, int op, size_t* bytes) {
     case MOE_OP_PERMUTE: *bytes = moe::permute_ws_bytes(cfg->T, cfg->k, cfg->E); break;
     case MOE_OP_GROUPED_GEMM: *bytes = gemm_ws_bytes(cfg); break;
     case MOE_OP_LAYER_FORWARD: *bytes = carve_layer(cfg, nullptr).total; break;
-    case MOE_OP_GROUPED_GEMM_BWD: return MOE_ERR_UNSUPPORTED;
+    case MOE_OP_GROUPED_GEMM_BWD:
+        if (cfg->act_dtype != MOE_BF16 || cfg->a_layout || cfg->w_layout) return MOE_ERR_UNSUPPORTED;
+        *bytes = moe::bwd_ws_bytes(cfg->T, cfg->k, cfg->E, cfg->H, cfg->F);
+        break;
     default: return MOE_ERR_INVALID_ARG;
     }
     return MOE_OK;
@@ -451,16 +454,22 @@ int moe_layer_forward(const moe_config* cfg, const void* x, const void* w_router
 }
 
 int moe_grouped_gemm_swiglu_bwd(const moe_config* cfg, const void* dy_perm, const void* x_perm,
-                                const void* z, const float* gate_perm, const int32_t* offsets,
-                                const void* w13, const void* w2, void* dx_perm, void* dw13,
-                                void* dw2, float* dgate_perm, void* ws, size_t ws_bytes,
-                                hipStream_t stream) {
-    (void)dy_perm; (void)x_perm; (void)z; (void)gate_perm; (void)offsets; (void)w13; (void)w2;
-    (void)dx_perm; (void)dw13; (void)dw2; (void)dgate_perm; (void)ws; (void)ws_bytes;
-    (void)stream;
+                                const void* z, const void* act, const float* gate_perm,
+                                const int32_t* offsets, const void* w13, const void* w2,
+                                void* dx_perm, void* dw13, void* dw2, float* dgate_perm,
+                                void* ws, size_t ws_bytes, hipStream_t stream) {
     int st = check_cfg(cfg);
     if (st) return st;
-    return MOE_ERR_UNSUPPORTED;
+    if (cfg->act_dtype != MOE_BF16 || cfg->a_layout || cfg->w_layout) return MOE_ERR_UNSUPPORTED;
+    if (!dy_perm || !x_perm || !z || !act || !offsets || !w13 || !w2 || !dx_perm || !dw13 ||
+        !dw2 || !ws)
+        return MOE_ERR_INVALID_ARG;
+    if (ws_bytes < moe::bwd_ws_bytes(cfg->T, cfg->k, cfg->E, cfg->H, cfg->F))
+        return MOE_ERR_WORKSPACE;
+    return hip_status(moe::launch_grouped_gemm_bwd(dy_perm, x_perm, z, act, gate_perm, offsets,
+                                                   w13, w2, cfg->T * cfg->k, cfg->E, cfg->H,
+                                                   cfg->F, dx_perm, dw13, dw2, dgate_perm, ws,
+                                                   stream));
 }
 
 int moe_pack_kblock(const void* in, int64_t n_mat, int32_t rows, int32_t cols,

@@ -92,3 +92,37 @@ MOE_DEVICE int rank_key_index(uint64_t rk) { return (int)(0xFFFFFFFFu - (uint32_
 MOE_DEVICE float rank_key_value(uint64_t rk) { return float_from_order_key((uint32_t)(rk >> 32)); }
 
 MOE_DEVICE float silu_f32(float u) { return u / (1.0f + expf(-u)); }
+
+// ---------------------------------------------------------------------------------------
+// LDS pipeline helpers of the MFMA kernels
+// ---------------------------------------------------------------------------------------
+#define MOE_LDS __attribute__((address_space(3)))
+
+// s_waitcnt with vmcnt <= N, lgkmcnt == 0 (gfx9 encoding; expcnt not waited for).
+template <int N>
+MOE_DEVICE void wait_vm_lgkm0() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
+// Workgroup barrier without a memory fence: the pipelines order their LDS traffic with
+// explicit waits; the empty asm statements keep the compiler from moving memory accesses
+// across the barrier.
+MOE_DEVICE void block_sync() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+constexpr int cmin(int a, int b) { return a < b ? a : b; }
+
+// Chunk swizzle of a K-contiguous tile row (depends on the row's low 4 bits only, so a
+// 32-row operand read sees the same pattern at every 32-row offset). 8 chunks (128-byte
+// rows): rows 0..7 of one logical chunk land in 8 different chunks. 4 chunks (64-byte rows):
+// rows of one parity among any 4 consecutive even (odd) rows, and rows 4 apart, land in
+// different chunks.
+template <int CPR>
+MOE_DEVICE int chunk_swz(int r) {
+    if (CPR == 8) return r & 7;
+    return ((r >> 1) & 3) ^ ((r >> 3) & 1);
+}

@@ -141,36 +141,6 @@ MOE_DEVICE bool pick_tile(const GemmArgs& ga, int& mt, int& nt) {
 // Ragged tails: a wave skips the loads and MFMAs of its 32-row sub-tiles that lie wholly
 // past the expert's last row, so a tile with few live rows costs few MFMA cycles.
 // ---------------------------------------------------------------------------------------
-#define MOE_LDS __attribute__((address_space(3)))
-
-// s_waitcnt with vmcnt <= N, lgkmcnt == 0 (gfx9 encoding; expcnt not waited for).
-template <int N>
-MOE_DEVICE void wait_vm_lgkm0() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
-}
-
-// Workgroup barrier without a memory fence: the pipeline orders its LDS traffic itself with
-// explicit waits; the empty asm statements keep the compiler from moving memory accesses
-// across the barrier.
-MOE_DEVICE void block_sync() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-constexpr int cmin(int a, int b) { return a < b ? a : b; }
-
-// Chunk swizzle of a tile row (depends on the row's low 4 bits only, so a 32-row operand
-// read sees the same pattern at every 32-row offset). 8 chunks (128-byte rows): rows 0..7
-// of one logical chunk land in 8 different chunks. 4 chunks (64-byte rows): rows of one
-// parity among any 4 consecutive even (odd) rows, and rows 4 apart, land in different
-// chunks.
-template <int CPR>
-MOE_DEVICE int chunk_swz(int r) {
-    if (CPR == 8) return r & 7;
-    return ((r >> 1) & 3) ^ ((r >> 3) & 1);
-}
 
 template <int KIND, int BM, int BN, int BK, int WM, int WN, int STAGES, int LOADREG = 0>
 struct BfCfg {
@@ -924,6 +894,19 @@ size_t max_mtiles(int max_rows_total, int groups_total, int bm) {
 }
 
 }  // namespace
+
+hipError_t launch_schedule(const int32_t* offsets, int groups, int bm, void* ws, hipStream_t s) {
+    SchedArgs sa = {};
+    sa.offsets[0] = offsets;
+    sa.groups[0] = groups;
+    sa.nseg = 1;
+    schedule_kernel<<<1, 1024, 0, s>>>(sa, bm, (int4*)((char*)ws + 256), (int*)ws);
+    return hipGetLastError();
+}
+
+size_t schedule_ws_bytes(int max_rows, int groups, int bm) {
+    return 256 + max_mtiles(max_rows, groups, bm) * sizeof(int4);
+}
 
 GemmPlan grouped_gemm_plan(int kind, int dtype, int max_rows_total, int groups_total, int N,
                            int K) {

@@ -69,6 +69,20 @@ struct GemmPlan {
 
 // kind: 0 = GEMM1 (gate/up + SwiGLU * gate), 1 = GEMM2 (plain).  dtype: moe_dtype of the
 // operands (F32, BF16, E4M3). N = output columns of the GEMM before the SwiGLU pairing.
+// Tile list of one segment (groups with device-resident row offsets) for M tiles of `bm`
+// rows, written to ws: *(int*)ws = count, (int4*)(ws + 256) = {group, first row, rows,
+// group's first global row}.
+hipError_t launch_schedule(const int32_t* offsets, int groups, int bm, void* ws, hipStream_t s);
+size_t schedule_ws_bytes(int max_rows, int groups, int bm);
+
+// ---- grouped GEMM backward (bf16) ----------------------------------------------------
+size_t bwd_ws_bytes(int T, int k, int E, int H, int F);
+hipError_t launch_grouped_gemm_bwd(const void* dy_perm, const void* x_perm, const void* z,
+                                   const void* act, const float* gate_perm,
+                                   const int32_t* offsets, const void* w13, const void* w2,
+                                   int A, int E, int H, int F, void* dx_perm, void* dw13,
+                                   void* dw2, float* dgate_perm, void* ws, hipStream_t s);
+
 GemmPlan grouped_gemm_plan(int kind, int dtype, int max_rows_total, int groups_total, int N,
                            int K);
 hipError_t launch_grouped_gemm(int kind, int dtype, const Segment* segs, int nseg,
