@@ -25,7 +25,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM = 8.0e12          # MI355X HBM3E, bytes/s
-PEAK_MFMA = {"bf16": 2.5e15, "fp32": 157.3e12, "fp8": 5.0e15}   # dense, FLOP/s
+PEAK_MFMA = {"bf16": 2.5e15, "fp32": 157.3e12, "e4m3": 5.0e15}   # dense, FLOP/s
+
+# HBM traffic of the dominant kernel, from rocprofv3 FETCH_SIZE / WRITE_SIZE passes scaled by
+# a plain copy of known size (see the file); used only while the kernel sources are unchanged
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_up_dsv3_bf16_traffic.txt")
+TRAFFIC_SOURCES = [os.path.join(ROOT, "routing_grouped_expert_softmax_amd", "csrc", f)
+                   for f in ("grouped_gemm.hip", "common.h", "kernels.h")]
 
 
 def log(*a):
@@ -58,6 +64,52 @@ def algorithmic(cfg):
     return d
 
 
+def sources_sha256() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload: str):
+    """Bytes per launch of the up GEMM recorded with the counters, or None when absent, for
+    another workload, or when the kernel sources changed since the counters were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    rec = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                rec[k.strip()] = v.strip()
+    if rec.get("workload") != workload or rec.get("source_sha256") != sources_sha256():
+        return None
+    return int(float(rec["fetch_bytes_per_launch"]) + float(rec["write_bytes_per_launch"]))
+
+
+def pmc_summary(dbs):
+    """Per-kernel averages of the counters in rocprofv3 databases (sqlite), as text."""
+    import collections
+    import sqlite3
+    for db in dbs:
+        c = sqlite3.connect(db)
+        vals = collections.defaultdict(lambda: collections.defaultdict(float))
+        disp = collections.defaultdict(dict)
+        for kn, d, cn, v, dur in c.execute(
+                "select kernel_name, dispatch_id, counter_name, value, duration "
+                "from counters_collection"):
+            vals[kn][cn] += v
+            disp[kn][d] = dur
+        print(f"# {db}")
+        for kn in sorted(vals):
+            n = len(disp[kn])
+            avg = sum(disp[kn].values()) / n / 1e3
+            cs = ", ".join(f"{cn}={v / n:.6g}" for cn, v in sorted(vals[kn].items()))
+            print(f"{kn[:110]} | dispatches {n} | avg us {avg:.1f} | {cs}")
+
+
 def cpu_baseline(cfg, inp, sample: int):
     """The oracle, as it stands, end to end on `sample` seeded tokens of the same workload."""
     import numpy as np
@@ -68,19 +120,61 @@ def cpu_baseline(cfg, inp, sample: int):
     sub = cfg.replace(T=len(toks))
     xs = inp.x[toks]
     oracle.lib()
+    if cfg.w_dtype == 2:      # weights quantised once, outside the timed sample (like loading)
+        q13, q2 = oracle.quant_weight(inp.w13), oracle.quant_weight(inp.w2)
+        s13, s2 = oracle.quant_weight(inp.ws13), oracle.quant_weight(inp.ws2)
     t0 = time.perf_counter()
     logits = oracle.router_logits(xs, inp.w_router)
     lb = None if inp.logit_bias is None else inp.logit_bias.numpy()
     sb = None if inp.sel_bias is None else inp.sel_bias.numpy()
     idx, gate = oracle.route_cfg(sub, logits, lb, sb)
     oracle.permute(idx, gate, cfg.E)
-    oracle.layer_tokens(xs, idx, gate, inp.w13, inp.w2, np.arange(len(toks)), inp.ws13, inp.ws2)
+    if cfg.w_dtype == 2:
+        oracle.layer_tokens(xs, idx, gate, q13[0], q2[0], np.arange(len(toks)), s13[0], s2[0],
+                            fp8=True, w13_scales=q13[1], w2_scales=q2[1], ws13_scales=s13[1],
+                            ws2_scales=s2[1])
+    else:
+        oracle.layer_tokens(xs, idx, gate, inp.w13, inp.w2, np.arange(len(toks)), inp.ws13,
+                            inp.ws2)
     dt = time.perf_counter() - t0
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return {"value": len(toks) / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"{len(toks)} seeded tokens of the same workload, end to end (router "
                       f"logits, routing, permutation of the sub-batch, expert MLPs, shared "
                       f"expert) in {dt:.1f} s; tokens are independent, so tokens/s scales"}
+
+
+def time_backward(moe, mi, cfg, dev, x, inp, idx, gate, w13_bf, w2_bf, reps):
+    """The grouped-GEMM backward of the routed experts (bf16 weights; Z and act saved by a bf16
+    forward of the same routing; dY ~ N(0,1) seeded), timed on its own."""
+    import torch
+    bcfg = cfg.replace(w_dtype=mi.BF16, a_layout=0, w_layout=0)
+    pb = moe.permute(bcfg, x, idx, gate)
+    A, F = cfg.T * cfg.k, cfg.F
+    act = torch.empty(A, F, dtype=torch.bfloat16, device=dev)
+    z = torch.empty(A, 2 * F, dtype=torch.bfloat16, device=dev)
+    nsh = bcfg.replace(shared_F=0)
+    moe.grouped_gemm_up(nsh, pb["x_perm"], pb["offsets"], pb["gate_perm"], w13_bf, act, z=z)
+    dyp = moe.permute(bcfg, inp.dy.to(dev), idx, gate)["x_perm"]
+    bws = moe.workspace(nsh, moe.OP_GROUPED_GEMM_BWD, dev)
+
+    def bwd():
+        return moe.grouped_gemm_swiglu_bwd(nsh, dyp, pb["x_perm"], z, act, pb["gate_perm"],
+                                           pb["offsets"], w13_bf, w2_bf, ws=bws)
+    bwd()
+    torch.cuda.synchronize()
+    t = 0.0
+    for _ in range(max(1, reps)):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        bwd()
+        b.record()
+        torch.cuda.synchronize()
+        t += a.elapsed_time(b) / max(1, reps)
+    flops = 12 * A * cfg.H * F
+    return {"what": "grouped-GEMM backward of the routed experts (dgrad + wgrad, bf16)",
+            "ms": round(t, 4), "TFLOP/s": round(flops / (t * 1e-3) / 1e12, 1),
+            "frac_bf16_peak": round(flops / (t * 1e-3) / PEAK_MFMA["bf16"], 4)}
 
 
 def main():
@@ -92,7 +186,15 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=1024)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--stage-reps", type=int, default=5)
+    ap.add_argument("--calib-copy-gib", type=float, default=0.0,
+                    help="issue one device copy of this many GiB before the steps (a plain copy "
+                         "of known size for scaling the traffic counters)")
+    ap.add_argument("--pmc-summary", nargs="+", metavar="DB",
+                    help="print per-kernel counter averages of rocprofv3 databases and exit")
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary)
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (this build "
@@ -116,17 +218,36 @@ def main():
     g = lambda t: None if t is None else t.to(dev, non_blocking=False)  # noqa: E731
     x, wr, w13, w2 = g(inp.x), g(inp.w_router), g(inp.w13), g(inp.w2)
     ws13, ws2, lb, sb = g(inp.ws13), g(inp.ws2), g(inp.logit_bias), g(inp.sel_bias)
+    fp8 = cfg.w_dtype == mi.E4M3
+    sc = dict(w13_scales=None, w2_scales=None, ws13_scales=None, ws2_scales=None)
+    w13_bf, w2_bf = w13, w2
+    if fp8:       # e4m3 weights with 128 x 128 block scales, quantised once (like loading)
+        w13, sc["w13_scales"] = moe.quantize_e4m3(w13, 128)
+        w2, sc["w2_scales"] = moe.quantize_e4m3(w2, 128)
+        ws13, sc["ws13_scales"] = moe.quantize_e4m3(ws13, 128)
+        ws2, sc["ws2_scales"] = moe.quantize_e4m3(ws2, 128)
+        if not cfg.backward:
+            w13_bf = w2_bf = None
     if cfg.w_layout:
         pk = lambda t: None if t is None else moe.pack_kblock(t)  # noqa: E731
         w13, w2, ws13, ws2 = pk(w13), pk(w2), pk(ws13), pk(ws2)
         torch.cuda.synchronize()
+    if args.calib_copy_gib > 0:
+        nb = int(args.calib_copy_gib * (1 << 30))
+        src_c = torch.empty(nb, dtype=torch.uint8, device=dev)
+        dst_c = torch.empty(nb, dtype=torch.uint8, device=dev)
+        dst_c.copy_(src_c)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy of {nb} bytes issued")
+        del src_c, dst_c
     y = torch.empty(cfg.T, cfg.H, dtype=moe.act_torch_dtype(cfg), device=dev)
     ws = moe.workspace(cfg, moe.OP_LAYER_FORWARD, dev)
     counts = torch.empty(cfg.E, dtype=torch.int32, device=dev)
     torch.cuda.synchronize()
 
     def step():
-        moe.layer_forward(cfg, x, wr, w13, w2, lb, sb, None, ws13=ws13, ws2=ws2, y=y, ws=ws)
+        moe.layer_forward(cfg, x, wr, w13, w2, lb, sb, None, ws13=ws13, ws2=ws2, y=y, ws=ws,
+                          **sc)
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -158,17 +279,32 @@ def main():
     y_perm = torch.empty(A, cfg.H, dtype=ad, device=dev)
     sh_act = torch.empty(cfg.T, cfg.shared_F, dtype=gd, device=dev) if cfg.shared_F else None
     sh_y = torch.empty(cfg.T, cfg.H, dtype=ad, device=dev) if cfg.shared_F else None
+    f32 = torch.float32
+    act_sc = torch.empty(A, cfg.F // 128, dtype=f32, device=dev) if fp8 else None
+    sh_act_sc = (torch.empty(cfg.T, cfg.shared_F // 128, dtype=f32, device=dev)
+                 if fp8 and cfg.shared_F else None)
     perm = {}
+
+    def x_sh():
+        if not cfg.shared_F:
+            return None, None
+        return (perm["x_q"], perm["x_q_scales"]) if fp8 else (x, None)
+
     stages = {
         "router_logits": lambda: moe.router_logits(cfg, x, wr, logits),
         "route": lambda: moe.route(cfg, logits, lb, sb, idx, gate),
-        "permute": lambda: perm.update(moe.permute(cfg, x, idx, gate, ws=pws)),
+        "permute": lambda: perm.update(moe.permute(cfg, x, idx, gate, ws=pws,
+                                                   want_x_q=fp8 and bool(cfg.shared_F))),
         "grouped_gemm_up": lambda: moe.grouped_gemm_up(
             cfg, perm["x_perm"], perm["offsets"], perm["gate_perm"], w13, act,
-            x_shared=x if cfg.shared_F else None, ws13=ws13, shared_act=sh_act, ws=gws),
+            x_perm_scales=perm["x_perm_scales"], w13_scales=sc["w13_scales"],
+            x_shared=x_sh()[0], x_shared_scales=x_sh()[1], ws13=ws13,
+            ws13_scales=sc["ws13_scales"], act_scales=act_sc, shared_act=sh_act,
+            shared_act_scales=sh_act_sc, ws=gws),
         "grouped_gemm_down": lambda: moe.grouped_gemm_down(
-            cfg, act, perm["offsets"], w2, y_perm, shared_act=sh_act, ws2=ws2, shared_y=sh_y,
-            ws=gws),
+            cfg, act, perm["offsets"], w2, y_perm, act_scales=act_sc,
+            w2_scales=sc["w2_scales"], shared_act=sh_act, shared_act_scales=sh_act_sc,
+            ws2=ws2, ws2_scales=sc["ws2_scales"], shared_y=sh_y, ws=gws),
         "combine": lambda: moe.unpermute_combine(cfg, y_perm, perm["pos"], sh_y, y),
     }
     times = {k: 0.0 for k in stages}
@@ -181,15 +317,17 @@ def main():
             torch.cuda.synchronize()
             if rep > 0:
                 times[name] += a.elapsed_time(b) / args.stage_reps
-    moe.layer_forward(cfg, x, wr, w13, w2, lb, sb, None, ws13=ws13, ws2=ws2, y=y, ws=ws,
-                      want=("counts",))
     _, ex = moe.layer_forward(cfg, x, wr, w13, w2, lb, sb, None, ws13=ws13, ws2=ws2, y=y,
-                              ws=ws, want=("counts",))
+                              ws=ws, want=("counts",), **sc)
     cnt = ex["counts"].cpu().double()
     torch.cuda.synchronize()
 
+    backward = None
+    if cfg.backward:
+        backward = time_backward(moe, mi, cfg, dev, x, inp, idx, gate, w13_bf, w2_bf,
+                                 args.stage_reps)
     alg = algorithmic(cfg)
-    dtype = {0: "fp32", 1: "bf16", 2: "fp8"}[cfg.w_dtype]
+    dtype = {0: "fp32", 1: "bf16", 2: "e4m3"}[cfg.w_dtype]
     per_stage = {}
     for name, t in times.items():
         s = t * 1e-3
@@ -233,7 +371,7 @@ def main():
         "roofline": {"kernel": "grouped GEMM up (gate/up + SwiGLU, gate folded)",
                      "bound": bound, "achieved": round(achieved, 1), "peak": peak,
                      "unit": unit, "frac": round(achieved / peak, 4),
-                     "traffic": None},
+                     "traffic": recorded_traffic(cfg.name)},
         "grouped_gemm": {"TFLOP/s": round(gemm_flops / gemm_t / 1e12, 1),
                          "frac_mfma_peak": round(gemm_flops / gemm_t / PEAK_MFMA[dtype], 4)},
         "permute_GB/s": per_stage["permute"]["GB/s"],
@@ -241,6 +379,8 @@ def main():
         "load": {"max_over_mean": round(float(cnt.max() / cnt.mean()), 3),
                  "min_over_mean": round(float(cnt.min() / cnt.mean()), 3)},
     }
+    if backward:
+        result["backward"] = backward
     if not args.no_cpu:
         log(f"[bench] cpu baseline: oracle on {args.cpu_sample} tokens ...")
         result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample)
