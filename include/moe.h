@@ -133,8 +133,11 @@ int moe_route(const moe_config* cfg, const float* logits, const float* logit_bia
  * With cfg->w_dtype == MOE_E4M3, x (bf16) is quantised per 1 x 128 block
  * (s = fp32(amax / 448), q = e4m3_rne_saturate(fp32(x / s))): x_perm holds the e4m3
  * codes and x_perm_scales [A, H/128] the scales; x_q [T, H] / x_q_scales [T, H/128]
- * optionally (may be NULL) receive the quantised x in token order (for a shared expert).
- * Otherwise x_perm has cfg->act_dtype and the scale pointers must be NULL. */
+ * optionally (may be NULL) receive the quantised x in token order (for a shared expert;
+ * with a K-blocked x_perm they also let each token be quantised once and then gathered).
+ * Otherwise x_perm has cfg->act_dtype and the scale pointers must be NULL.
+ * x_perm is in cfg->a_layout; a K-blocked x_perm is written by a gather over src so that
+ * every store is a contiguous kilobyte. */
 int moe_permute(const moe_config* cfg, const void* x, const int32_t* topk_idx,
                 const float* topk_gate, int32_t* counts, int32_t* offsets, int32_t* pos,
                 int32_t* src, float* gate_perm, void* x_perm, float* x_perm_scales,

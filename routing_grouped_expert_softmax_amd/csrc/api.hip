@@ -118,8 +118,8 @@ LayerWs carve_layer(const moe_config* c, void* ws) {
     L.gate_perm = (float*)cv.take(A * 4);
     L.x_perm = cv.take(A * H * gb);
     L.x_perm_scales = fp8 ? (float*)cv.take(A * (H / 128) * 4) : nullptr;
-    L.x_q = (fp8 && c->shared_F) ? cv.take(T * H) : nullptr;
-    L.x_q_scales = (fp8 && c->shared_F) ? (float*)cv.take(T * (H / 128) * 4) : nullptr;
+    L.x_q = fp8 ? cv.take(T * H) : nullptr;                // token-order e4m3 x (the
+    L.x_q_scales = fp8 ? (float*)cv.take(T * (H / 128) * 4) : nullptr;   // gather's source)
     L.act = cv.take(A * F * gb);
     L.act_scales = fp8 ? (float*)cv.take(A * (F / 128) * 4) : nullptr;
     L.y_perm = cv.take(A * H * ab);

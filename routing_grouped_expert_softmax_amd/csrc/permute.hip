@@ -43,10 +43,17 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t* __restrict__ c
     const int e = threadIdx.x;
     int run = 0;
     if (e < E) {
-        for (int c = 0; c < nchunk; ++c) {
-            int v = chunk_counts[(size_t)c * E + e];
-            chunk_counts[(size_t)c * E + e] = run;
-            run += v;
+        // batches of 16 independent loads, then the running sum over them
+        for (int c0 = 0; c0 < nchunk; c0 += 16) {
+            int v[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                v[u] = c0 + u < nchunk ? chunk_counts[(size_t)(c0 + u) * E + e] : 0;
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                if (c0 + u < nchunk) chunk_counts[(size_t)(c0 + u) * E + e] = run;
+                run += v[u];
+            }
         }
         counts[e] = run;
     }
@@ -67,8 +74,10 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t* __restrict__ c
     if (e < E) offsets[e] = excl;
     if (e == 0) offsets[E] = A;
     __syncthreads();
-    if (e < E)
-        for (int c = 0; c < nchunk; ++c) chunk_counts[(size_t)c * E + e] += tot[e];
+    if (e < E) {
+        const int base = tot[e];
+        for (int c = 0; c < nchunk; ++c) chunk_counts[(size_t)c * E + e] += base;
+    }
 }
 
 // One wavefront per chunk.
@@ -194,6 +203,38 @@ __global__ __launch_bounds__(256) void perm_quant_copy_kernel(
     }
 }
 
+// K-blocked x_perm as a gather: one wavefront per (16 consecutive x_perm rows, up to
+// kGatherSlices 64-byte K slices); lane l copies 16 bytes (chunk l % 4 of each slice) of row
+// r0 + l / 4 from the row of its token src[r], so every store instruction writes one
+// contiguous kilobyte of x_perm. Row bytes: H * 2 (bf16) or H (e4m3 codes, with their
+// 1 x 128 scales gathered alongside).
+constexpr int kGatherSlices = 16;
+__global__ __launch_bounds__(256) void perm_gather_kblock_kernel(
+    const uint8_t* __restrict__ xin, const int32_t* __restrict__ src, int A, int row_bytes,
+    uint8_t* __restrict__ x_perm, const float* __restrict__ in_scales, int nsc,
+    float* __restrict__ out_scales) {
+    const int lane = threadIdx.x % kWave;
+    const int64_t w = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+    const int slices = row_bytes / 64;
+    const int sgroups = (slices + kGatherSlices - 1) / kGatherSlices;
+    const int64_t rblocks = (A + 15) / 16;
+    if (w >= rblocks * sgroups) return;
+    const int rb = (int)(w / sgroups), sg = (int)(w % sgroups);
+    const int r = rb * 16 + lane / 4;
+    if (r >= A) return;
+    const int t = src[r];
+    const uint8_t* in = xin + (size_t)t * row_bytes + (lane % 4) * 16;
+    uint8_t* out = x_perm + (size_t)r * 64 + (lane % 4) * 16;
+    const int j0 = sg * kGatherSlices;
+    const int j1 = j0 + kGatherSlices < slices ? j0 + kGatherSlices : slices;
+#pragma unroll 4
+    for (int j = j0; j < j1; ++j)
+        *(uint4*)(out + (size_t)j * A * 64) = *(const uint4*)(in + (size_t)j * 64);
+    if (out_scales && sg == 0 && lane % 4 == 0)
+        for (int b = 0; b < nsc; ++b)
+            out_scales[(size_t)r * nsc + b] = in_scales[(size_t)t * nsc + b];
+}
+
 }  // namespace
 
 size_t permute_ws_bytes(int T, int k, int E) {
@@ -218,6 +259,23 @@ hipError_t launch_permute(int mode, int kblock, const void* x, const int32_t* to
                                                              nbits, chunk_counts, pos, src,
                                                              gate_perm);
     const int blocks = (T + 3) / 4;
+    auto gather = [&](const void* in, int row_bytes, const float* in_sc, float* out_sc) {
+        const int64_t waves = (int64_t)((A + 15) / 16) *
+                              ((row_bytes / 64 + kGatherSlices - 1) / kGatherSlices);
+        perm_gather_kblock_kernel<<<(unsigned)((waves + 3) / 4), 256, 0, s>>>(
+            (const uint8_t*)in, src, A, row_bytes, (uint8_t*)x_perm, in_sc, H / 128, out_sc);
+    };
+    if (kblock && mode == 1) {
+        gather(x, H * 2, nullptr, nullptr);
+        return hipGetLastError();
+    }
+    if (kblock && mode == 2 && x_q) {
+        // quantise each token once (token order), then gather codes and scales
+        hipError_t e = launch_quantize(x, 1, 1, T, H, 1, (uint8_t*)x_q, x_q_scales, s);
+        if (e != hipSuccess) return e;
+        gather(x_q, H, x_q_scales, x_perm_scales);
+        return hipGetLastError();
+    }
     if (mode == 2) {
         perm_quant_copy_kernel<<<blocks, 256, 0, s>>>((const uint4*)x, pos, T, H, k, kblock,
                                                       (uint2*)x_perm, x_perm_scales,

@@ -185,19 +185,26 @@ __global__ __launch_bounds__(256) void router_logits_f32_kernel(
 
 // ---------------------------------------------------------------------------------------
 // router GEMM, bf16 operands on MFMA 16x16x32 (fp32 accumulate).
-// Block: 256 threads (4 waves) computes 64 tokens x 64 experts; wave w owns tokens
-// [16w, 16w+16) x all 64 experts (4 MFMA column tiles). Operands are read straight from
-// global memory (K contiguous, 16 B per lane); x is read once per 64-expert column block,
-// and w (E x H, at most a few MB) stays in L2.
+// Block: 64 tokens x 64 experts, 4 x S waves: wave (tg, kq) owns tokens [16 tg, 16 tg + 16)
+// x all 64 experts (4 MFMA column tiles) over the K range kq * H / S .. (kq + 1) * H / S.
+// The S partial tiles are summed through LDS in a fixed order (deterministic). Operands are
+// read straight from global memory (K contiguous, 16 B per lane): x is read once per
+// 64-expert column block and w (E x H, a few MB) stays in L2; each step issues the loads of
+// kRouterU K chunks before their MFMAs. Splitting K raises the waves per CU (latency hiding)
+// without adding traffic.
 // ---------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void router_logits_bf16_kernel(
+constexpr int kRouterU = 8;      // 32-wide K chunks per load batch
+
+template <int S>
+__global__ __launch_bounds__(256 * S) void router_logits_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int T, int H, int E,
     float* __restrict__ logits) {
+    __shared__ float red[(S > 1 ? S - 1 : 1) * 4 * 64 * 16];
     const int lane = threadIdx.x % kWave;
     const int wave = threadIdx.x / kWave;
-    const int t0 = blockIdx.x * 64 + wave * 16;
+    const int tg = wave % 4, kq = wave / 4;
+    const int t0 = blockIdx.x * 64 + tg * 16;
     const int e_base = blockIdx.y * 64;
-    // operand rows for this lane (clamped into range; clamped rows are not stored)
     int tr = t0 + (lane % 16);
     tr = tr < T ? tr : T - 1;
     const uint16_t* xa = x + (size_t)tr * H + 8 * (lane / 16);
@@ -209,12 +216,38 @@ __global__ __launch_bounds__(256) void router_logits_bf16_kernel(
         wb[j] = w + (size_t)er * H + 8 * (lane / 16);
     }
     f32x4_t acc[4] = {};
-    for (int h = 0; h < H; h += 32) {
-        bf16x8_t a = *(const bf16x8_t*)(xa + h);
+    const int hq = H / S;
+    for (int h = kq * hq; h < (kq + 1) * hq; h += 32 * kRouterU) {
+        bf16x8_t a[kRouterU], b[kRouterU][4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            bf16x8_t b = *(const bf16x8_t*)(wb[j] + h);
-            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
+        for (int u = 0; u < kRouterU; ++u) {
+            a[u] = *(const bf16x8_t*)(xa + h + 32 * u);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) b[u][j] = *(const bf16x8_t*)(wb[j] + h + 32 * u);
+        }
+#pragma unroll
+        for (int u = 0; u < kRouterU; ++u)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b[u][j], acc[j], 0, 0, 0);
+    }
+    if (S > 1) {
+        if (kq > 0) {
+            float* dst = red + (((kq - 1) * 4 + tg) * 64 + lane) * 16;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dst[j * 4 + i] = acc[j][i];
+        }
+        __syncthreads();
+        if (kq > 0) return;
+#pragma unroll
+        for (int q = 1; q < S; ++q) {
+            const float* p = red + (((q - 1) * 4 + tg) * 64 + lane) * 16;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[j][i] += p[j * 4 + i];
         }
     }
     // 16x16 output: lane holds rows 4*(lane/16)+i, column lane%16
@@ -239,9 +272,14 @@ hipError_t launch_router_logits(int act_dtype, const void* x, const void* w_rout
                                                              logits);
     } else {
         dim3 grid((T + 63) / 64, (E + 63) / 64);
-        router_logits_bf16_kernel<<<grid, 256, 0, s>>>((const uint16_t*)x,
-                                                       (const uint16_t*)w_router, T, H, E,
-                                                       logits);
+        const uint16_t* xb = (const uint16_t*)x;
+        const uint16_t* wb = (const uint16_t*)w_router;
+        if (H % (4 * 32 * kRouterU) == 0)
+            router_logits_bf16_kernel<4><<<grid, 1024, 0, s>>>(xb, wb, T, H, E, logits);
+        else if (H % (2 * 32 * kRouterU) == 0)
+            router_logits_bf16_kernel<2><<<grid, 512, 0, s>>>(xb, wb, T, H, E, logits);
+        else
+            router_logits_bf16_kernel<1><<<grid, 256, 0, s>>>(xb, wb, T, H, E, logits);
     }
     return hipGetLastError();
 }
