@@ -142,55 +142,63 @@ MOE_DEVICE bool pick_tile(const GemmArgs& ga, int& mt, int& nt) {
 // past the expert's last row, so a tile with few live rows costs few MFMA cycles.
 // ---------------------------------------------------------------------------------------
 
-template <int KIND, int BM, int BN, int BK, int WM, int WN, int STAGES, int LOADREG = 0>
+template <int KIND, int BM, int BN, int BK, int WM, int WN, int SA, int SB>
 struct BfCfg {
-    static constexpr int kLoadReg = LOADREG;
     static constexpr int kThreads = WM * WN * kWave;
     static constexpr int kWaves = WM * WN;
     static constexpr int kRowBytes = BK * 2;
     static constexpr int kCpr = kRowBytes / 16;             // 16-byte chunks per row
     static constexpr int kRowsPerDma = kWave / kCpr;        // rows one wave DMA fills
-    static constexpr int kRows = BM + BN;
-    static constexpr int kStageBytes = kRows * kRowBytes;
-    static constexpr int kDma = kRows / kRowsPerDma / kWaves;   // DMAs per wave per stage
+    static constexpr int kDmaA = BM / kRowsPerDma / kWaves; // A DMAs per wave per step
+    static constexpr int kDmaB = BN / kRowsPerDma / kWaves; // B DMAs per wave per step
+    static constexpr int kASlot = BM * kRowBytes;           // one A ring slot
+    static constexpr int kBSlot = BN * kRowBytes;           // one B ring slot
+    static constexpr int kBRing = SA * kASlot;              // B ring offset in LDS
     static constexpr int kTM = BM / WM / 32;                // 32x32 tiles per wave (M)
     static constexpr int kTN = BN / WN / 32;                // 32x32 tiles per wave (N)
     static constexpr int kSub = BK / 16;                    // MFMA K steps per stage
     static constexpr int kSlices = kRowBytes / 64;          // 64-byte K slices per stage
-    static constexpr int kStages = STAGES;
-    static constexpr size_t kLds = (size_t)STAGES * kStageBytes;
+    static constexpr int kSA = SA, kSB = SB;
+    static constexpr int kEpCols = KIND == 0 ? BN / 2 : BN;       // output columns of a tile
+    static constexpr int kEpStride = kEpCols + 8;                 // bf16, padded row
+    static constexpr size_t kLdsLoop = (size_t)SA * kASlot + (size_t)SB * kBSlot;
+    static constexpr size_t kLdsEp = (size_t)BM * kEpStride * 2;
+    static constexpr size_t kLds = kLdsLoop > kLdsEp ? kLdsLoop : kLdsEp;
     static_assert(BK == 32 || BK == 64, "BK");
-    static_assert(kRows % (kRowsPerDma * kWaves) == 0, "DMA split");
+    static_assert(kDmaA * kRowsPerDma * kWaves == BM && kDmaB * kRowsPerDma * kWaves == BN,
+                  "DMA split");
     static_assert(KIND == 1 || kTN % 2 == 0, "GEMM1 needs gate/up tile pairs");
     static_assert(kLds <= 160 * 1024, "LDS");
-    static_assert(STAGES >= 2 && (STAGES - 2) * kDma < 64, "vmcnt");
-    static_assert(!LOADREG || STAGES == 2, "register-staged loads use a 2-stage ring");
+    static_assert(SA >= 2 && SB >= SA && (SB == SA || SA == 2), "ring depths");
+    static_assert((SA - 2) * (kDmaA + kDmaB) + kDmaB < 64, "vmcnt");
 };
 
-// MFMAs of one LDS stage for a wave's NV live 32-row sub-tiles. Operand fragments are
-// double-buffered in registers: the LDS reads of sub-step s + 1 are placed between the
-// MFMAs of sub-step s (sched_group_barrier: MFMA / DS-read interleave).
+// MFMAs of one K step for a wave's NV live 32-row sub-tiles (A rows in one ring slot, B
+// rows in another). Operand fragments are double-buffered in registers: the LDS reads of
+// sub-step s + 1 are placed between the MFMAs of sub-step s (sched_group_barrier: MFMA /
+// DS-read interleave).
 template <class C, int NV>
-MOE_DEVICE void bf16_stage_mma(const uint8_t* base, const int (&a_off)[C::kTM],
-                               const int (&b_off)[C::kTN], const int (&chunk_off)[C::kSub],
+MOE_DEVICE void bf16_stage_mma(const uint8_t* base_a, const uint8_t* base_b,
+                               const int (&a_off)[C::kTM], const int (&b_off)[C::kTN],
+                               const int (&chunk_off)[C::kSub],
                                f32x16_t (&acc)[C::kTM][C::kTN]) {
     if (NV == 0) return;
     constexpr int NVv = NV > 0 ? NV : 1;
     bf16x8_t av[2][NVv], bv[2][C::kTN];
 #pragma unroll
-    for (int j = 0; j < C::kTN; ++j) bv[0][j] = *(const bf16x8_t*)(base + b_off[j] + chunk_off[0]);
+    for (int j = 0; j < C::kTN; ++j) bv[0][j] = *(const bf16x8_t*)(base_b + b_off[j] + chunk_off[0]);
 #pragma unroll
-    for (int i = 0; i < NV; ++i) av[0][i] = *(const bf16x8_t*)(base + a_off[i] + chunk_off[0]);
+    for (int i = 0; i < NV; ++i) av[0][i] = *(const bf16x8_t*)(base_a + a_off[i] + chunk_off[0]);
 #pragma unroll
     for (int s = 0; s < C::kSub; ++s) {
         const int cur = s & 1, nxt = cur ^ 1;
         if (s + 1 < C::kSub) {
 #pragma unroll
             for (int j = 0; j < C::kTN; ++j)
-                bv[nxt][j] = *(const bf16x8_t*)(base + b_off[j] + chunk_off[s + 1]);
+                bv[nxt][j] = *(const bf16x8_t*)(base_b + b_off[j] + chunk_off[s + 1]);
 #pragma unroll
             for (int i = 0; i < NV; ++i)
-                av[nxt][i] = *(const bf16x8_t*)(base + a_off[i] + chunk_off[s + 1]);
+                av[nxt][i] = *(const bf16x8_t*)(base_a + a_off[i] + chunk_off[s + 1]);
         }
 #pragma unroll
         for (int i = 0; i < NV; ++i)
@@ -214,61 +222,62 @@ MOE_DEVICE void bf16_stage_mma(const uint8_t* base, const int (&a_off)[C::kTM],
 #endif
 }
 
-// K loop with direct global -> LDS loads, STAGES-deep ring (prefetch distance STAGES - 1).
-template <class C, int NV, class Issue>
-MOE_DEVICE void bf16_kloop(int nk, const uint8_t* lds, Issue& issue,
+// K loop with direct global -> LDS loads into two rings: A (activations) SA slots deep,
+// B (weights) SB >= SA slots deep. Step t issues A(t + SA - 1) and then B(t + SB - 1), so the
+// weight stream -- which carries most of the HBM misses -- is prefetched further ahead.
+// vmcnt: loads complete in issue order, so step kt may proceed once at most the loads issued
+// after the later of A(kt), B(kt) remain.
+template <class C, int NV, class IssueA, class IssueB>
+MOE_DEVICE void bf16_kloop(int nk, const uint8_t* lds, IssueA& issue_a, IssueB& issue_b,
                            const int (&a_off)[C::kTM], const int (&b_off)[C::kTN],
                            const int (&chunk_off)[C::kSub],
                            f32x16_t (&acc)[C::kTM][C::kTN]) {
-    constexpr int STAGES = C::kStages;
+    constexpr int SA = C::kSA, SB = C::kSB;
+    constexpr int kStep = C::kDmaA + C::kDmaB;
+    if (SB == SA) {
 #pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s)
-        if (s < nk) issue(s, s);
-    int stage = 0;
+        for (int s = 0; s < SA - 1; ++s)
+            if (s < nk) { issue_a(s, s); issue_b(s, s); }
+    } else {            // SA == 2: B(0) .. B(SB - 3), A(0), B(SB - 2)
+#pragma unroll
+        for (int s = 0; s < SB - 2; ++s)
+            if (s < nk) issue_b(s, s);
+        issue_a(0, 0);
+        if (SB - 2 < nk) issue_b(SB - 2, SB - 2);
+    }
+    int sa = 0, sb = 0;
     for (int kt = 0; kt < nk; ++kt) {
-        // stage kt has landed once at most min(STAGES - 2, nk - 1 - kt) later groups remain
-        const int later = nk - 1 - kt;
-        if (later >= STAGES - 2) wait_vm_lgkm0<(STAGES - 2) * C::kDma>();
-        else if (later >= 2) wait_vm_lgkm0<cmin(2, STAGES - 2) * C::kDma>();
-        else if (later >= 1) wait_vm_lgkm0<cmin(1, STAGES - 2) * C::kDma>();
-        else wait_vm_lgkm0<0>();
+        if (SB == SA) {
+            // stage kt has landed once at most min(SA - 2, nk - 1 - kt) later steps remain
+            const int later = nk - 1 - kt;
+            if (later >= SA - 2) wait_vm_lgkm0<(SA - 2) * kStep>();
+            else if (later >= 2) wait_vm_lgkm0<cmin(2, SA - 2) * kStep>();
+            else if (later >= 1) wait_vm_lgkm0<cmin(1, SA - 2) * kStep>();
+            else wait_vm_lgkm0<0>();
+        } else {
+            // after A(kt) only B(kt + SB - 2) was issued, if it exists
+            if (kt + SB - 2 < nk) wait_vm_lgkm0<C::kDmaB>();
+            else wait_vm_lgkm0<0>();
+        }
         block_sync();
         {
-            const int kn = kt + STAGES - 1;
-            int sn = stage + STAGES - 1;
-            if (sn >= STAGES) sn -= STAGES;
-            if (kn < nk) issue(kn, sn);
+            int na = sa + SA - 1;
+            if (na >= SA) na -= SA;
+            int nb = sb + SB - 1;
+            if (nb >= SB) nb -= SB;
+            if (kt + SA - 1 < nk) issue_a(kt + SA - 1, na);
+            if (kt + SB - 1 < nk) issue_b(kt + SB - 1, nb);
         }
-        bf16_stage_mma<C, NV>(lds + stage * C::kStageBytes, a_off, b_off, chunk_off, acc);
-        if (++stage == STAGES) stage = 0;
+        bf16_stage_mma<C, NV>(lds + sa * C::kASlot, lds + C::kBRing + sb * C::kBSlot, a_off,
+                              b_off, chunk_off, acc);
+        if (++sa == SA) sa = 0;
+        if (++sb == SB) sb = 0;
     }
 }
 
-// K loop with register-staged loads (global -> VGPR -> ds_write) into a 2-stage LDS ring:
-// the global loads of step kt + 2 are in flight while step kt + 1 is computed.
-template <class C, int NV, class Load, class Store>
-MOE_DEVICE void bf16_kloop_reg(int nk, const uint8_t* lds, Load& load, Store& store,
-                               const int (&a_off)[C::kTM], const int (&b_off)[C::kTN],
-                               const int (&chunk_off)[C::kSub],
-                               f32x16_t (&acc)[C::kTM][C::kTN]) {
-    uint4 r[C::kDma];
-    load(r, 0);
-    store(r, 0);
-    if (nk > 1) load(r, 1);
-    wait_vm_lgkm0<63>();
-    block_sync();
-    for (int kt = 0; kt < nk; ++kt) {
-        bf16_stage_mma<C, NV>(lds + (kt & 1) * C::kStageBytes, a_off, b_off, chunk_off, acc);
-        if (kt + 1 < nk) store(r, (kt + 1) & 1);
-        if (kt + 2 < nk) load(r, kt + 2);
-        __builtin_amdgcn_s_waitcnt(0xC07F);          // lgkmcnt(0): this wave's LDS writes
-        block_sync();
-    }
-}
-
-template <int KIND, int BM, int BN, int BK, int WM, int WN, int STAGES, int LOADREG>
+template <int KIND, int BM, int BN, int BK, int WM, int WN, int SA, int SB>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs ga) {
-    using C = BfCfg<KIND, BM, BN, BK, WM, WN, STAGES, LOADREG>;
+    using C = BfCfg<KIND, BM, BN, BK, WM, WN, SA, SB>;
     extern __shared__ __align__(16) uint8_t lds[];
     int mt, nt;
     if (!pick_tile(ga, mt, nt)) return;
@@ -286,50 +295,46 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs ga) {
     nvi = __builtin_amdgcn_readfirstlane(nvi);
 
     // ---- DMA sources: instruction q of this wave fills tile rows
-    //      kRowsPerDma * (wave + q * kWaves) + [0, kRowsPerDma)
-    const uint8_t* src[C::kDma];
+    //      kRowsPerDma * (wave + q * kWaves) + [0, kRowsPerDma) of A or of B
+    const uint8_t* srcA[C::kDmaA];
+    const uint8_t* srcB[C::kDmaB];
 #pragma unroll
-    for (int q = 0; q < C::kDma; ++q) {
-        const int r = C::kRowsPerDma * (wave + q * C::kWaves) + lane / C::kCpr;   // tile row
-        const int c = (lane % C::kCpr) ^ chunk_swz<C::kCpr>(r);    // logical 16-byte chunk
-        const uint8_t* rowp;
-        if (r < BM) {
-            const int rr = m0 + r < Mg ? m0 + r : Mg - 1;          // clamp the ragged tail
-            rowp = (const uint8_t*)S.a + (size_t)(rbase + rr) * S.a_row;
-        } else {
-            const int rb = r - BM;
-            int wrow;
-            if (KIND == 0)
-                wrow = rb < BN / 2 ? nt * (BN / 2) + rb : N / 2 + nt * (BN / 2) + (rb - BN / 2);
-            else
-                wrow = nt * BN + rb;
-            rowp = (const uint8_t*)S.w + (size_t)g * S.w_mat + (size_t)wrow * S.w_row;
-        }
-        const size_t step = r < BM ? S.a_kstep : S.w_kstep;
-        src[q] = rowp + (size_t)(c / 4) * step + (c % 4) * 16;
+    for (int q = 0; q < C::kDmaA; ++q) {
+        const int r = C::kRowsPerDma * (wave + q * C::kWaves) + lane / C::kCpr;
+        const int c = (lane % C::kCpr) ^ chunk_swz<C::kCpr>(r);
+        const int rr = m0 + r < Mg ? m0 + r : Mg - 1;              // clamp the ragged tail
+        const uint8_t* rowp = (const uint8_t*)S.a + (size_t)(rbase + rr) * S.a_row;
+        srcA[q] = rowp + (size_t)(c / 4) * S.a_kstep + (c % 4) * 16;
     }
-    // bytes per 64-byte K slice: instruction q holds A rows only or B rows only
-    const size_t a_step = S.a_kstep, w_step = S.w_kstep;
-    auto issue = [&](int kstep, int stage) {
-        MOE_LDS uint8_t* base = (MOE_LDS uint8_t*)lds + stage * C::kStageBytes;
 #pragma unroll
-        for (int q = 0; q < C::kDma; ++q)
-            __builtin_amdgcn_global_load_lds(
-                (const void*)(src[q] + (size_t)kstep * C::kSlices *
-                                           (q * C::kRowsPerDma * C::kWaves < BM ? a_step : w_step)),
-                (MOE_LDS void*)(base + (wave + q * C::kWaves) * 1024), 16, 0, 0);
+    for (int q = 0; q < C::kDmaB; ++q) {
+        const int rb = C::kRowsPerDma * (wave + q * C::kWaves) + lane / C::kCpr;
+        const int c = (lane % C::kCpr) ^ chunk_swz<C::kCpr>(rb);
+        int wrow;
+        if (KIND == 0)
+            wrow = rb < BN / 2 ? nt * (BN / 2) + rb : N / 2 + nt * (BN / 2) + (rb - BN / 2);
+        else
+            wrow = nt * BN + rb;
+        const uint8_t* rowp = (const uint8_t*)S.w + (size_t)g * S.w_mat + (size_t)wrow * S.w_row;
+        srcB[q] = rowp + (size_t)(c / 4) * S.w_kstep + (c % 4) * 16;
+    }
+    // bytes per K step (64-byte K slices per step times the slice stride)
+    const size_t a_step = (size_t)C::kSlices * S.a_kstep, w_step = (size_t)C::kSlices * S.w_kstep;
+    auto issue_a = [&](int kstep, int slot) {
+        MOE_LDS uint8_t* base = (MOE_LDS uint8_t*)lds + slot * C::kASlot;
+#pragma unroll
+        for (int q = 0; q < C::kDmaA; ++q)
+            __builtin_amdgcn_global_load_lds((const void*)(srcA[q] + (size_t)kstep * a_step),
+                                             (MOE_LDS void*)(base + (wave + q * C::kWaves) * 1024),
+                                             16, 0, 0);
     };
-    auto load = [&](uint4 (&r)[C::kDma], int kstep) {
+    auto issue_b = [&](int kstep, int slot) {
+        MOE_LDS uint8_t* base = (MOE_LDS uint8_t*)lds + C::kBRing + slot * C::kBSlot;
 #pragma unroll
-        for (int q = 0; q < C::kDma; ++q)
-            r[q] = *(const uint4*)(src[q] + (size_t)kstep * C::kSlices *
-                                                (q * C::kRowsPerDma * C::kWaves < BM ? a_step : w_step));
-    };
-    auto store = [&](const uint4 (&r)[C::kDma], int stage) {
-        uint8_t* base = lds + stage * C::kStageBytes;
-#pragma unroll
-        for (int q = 0; q < C::kDma; ++q)
-            *(uint4*)(base + (wave + q * C::kWaves) * 1024 + lane * 16) = r[q];
+        for (int q = 0; q < C::kDmaB; ++q)
+            __builtin_amdgcn_global_load_lds((const void*)(srcB[q] + (size_t)kstep * w_step),
+                                             (MOE_LDS void*)(base + (wave + q * C::kWaves) * 1024),
+                                             16, 0, 0);
     };
 
     // ---- MFMA operand addresses (bytes within a stage)
@@ -343,11 +348,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs ga) {
         if (KIND == 0) {
             constexpr int half = C::kTN / 2;
             const int col = wn * (BN / 2 / WN) + (j % half) * 32 + lane % 32;
-            row = BM + (j < half ? col : BN / 2 + col);
+            row = j < half ? col : BN / 2 + col;
         } else {
-            row = BM + wn * (BN / WN) + j * 32 + lane % 32;
+            row = wn * (BN / WN) + j * 32 + lane % 32;
         }
-        b_off[j] = row * C::kRowBytes;
+        b_off[j] = row * C::kRowBytes;                      // within a B ring slot
     }
     // physical chunk of logical chunk (2 s + lane / 32) of a row whose low bits are lane % 32
     int chunk_off[C::kSub];
@@ -369,10 +374,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs ga) {
     case V:                                                                                 \
         if (V <= C::kTM) {                                                                  \
             constexpr int NV = V <= C::kTM ? V : C::kTM;                                    \
-            if (LOADREG)                                                                    \
-                bf16_kloop_reg<C, NV>(nk, lds, load, store, a_off, b_off, chunk_off, acc);  \
-            else                                                                            \
-                bf16_kloop<C, NV>(nk, lds, issue, a_off, b_off, chunk_off, acc);            \
+            bf16_kloop<C, NV>(nk, lds, issue_a, issue_b, a_off, b_off, chunk_off, acc);     \
         }                                                                                   \
         break;
     MOE_KLOOP_CASE(0)
@@ -389,30 +391,32 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs ga) {
     }
 
     // epilogue. 32x32 accumulator layout: element r of lane l is
-    // row (r/4)*8 + (l/32)*4 + r%4, column l%32.
+    // row (r/4)*8 + (l/32)*4 + r%4, column l%32. The bf16 output tile (GEMM1: act) is staged
+    // in LDS as [BM][kEpCols + 8] and then written with 16-byte row chunks per lane, so every
+    // store is coalesced (a K-blocked act slice of the tile is one contiguous run).
+    constexpr int kEpCols = C::kEpCols, kEpStride = C::kEpStride;
+    block_sync();                                   // every wave is done with the stages
+    uint16_t* ep = (uint16_t*)lds;
     if (KIND == 0) {
         constexpr int half = C::kTN / 2;
         const int F = N / 2;
-        uint16_t* out = (uint16_t*)S.out;
         uint16_t* zo = (uint16_t*)S.z_out;
 #pragma unroll
         for (int i = 0; i < C::kTM; ++i) {
             if (i >= nvi) continue;
 #pragma unroll
             for (int jj = 0; jj < half; ++jj) {
-                const int col = nt * (BN / 2) + wn * (BN / 2 / WN) + jj * 32 + lane % 32;
+                const int lcol = wn * (BN / 2 / WN) + jj * 32 + lane % 32;
+                const int col = nt * (BN / 2) + lcol;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int row = wm * (BM / WM) + i * 32 + (r / 4) * 8 + (lane / 32) * 4 + r % 4;
-                    if (m0 + row >= Mg) continue;
-                    const size_t grow = (size_t)rbase + m0 + row;
+                    const int lr = m0 + row < Mg ? row : live - 1;     // dead rows: any gate
+                    const size_t grow = (size_t)rbase + m0 + lr;
                     const float zg = acc[i][jj][r], zu = acc[i][half + jj][r];
                     const float gt = S.gate ? S.gate[grow] : 1.0f;
-                    const size_t oi = S.out_kblock
-                        ? ((size_t)(col / 32) * S.rows_total + grow) * 32 + col % 32
-                        : grow * F + col;
-                    out[oi] = f32_to_bf16(gt * (silu_f32(zg) * zu));
-                    if (zo) {
+                    ep[row * kEpStride + lcol] = f32_to_bf16(gt * (silu_f32(zg) * zu));
+                    if (zo && m0 + row < Mg) {
                         zo[grow * N + col] = f32_to_bf16(zg);
                         zo[grow * N + F + col] = f32_to_bf16(zu);
                     }
@@ -420,21 +424,37 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs ga) {
             }
         }
     } else {
-        uint16_t* out = (uint16_t*)S.out;
 #pragma unroll
         for (int i = 0; i < C::kTM; ++i) {
             if (i >= nvi) continue;
 #pragma unroll
             for (int j = 0; j < C::kTN; ++j) {
-                const int col = nt * BN + wn * (BN / WN) + j * 32 + lane % 32;
+                const int lcol = wn * (BN / WN) + j * 32 + lane % 32;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int row = wm * (BM / WM) + i * 32 + (r / 4) * 8 + (lane / 32) * 4 + r % 4;
-                    if (m0 + row >= Mg) continue;
-                    const size_t grow = (size_t)rbase + m0 + row;
-                    out[grow * N + col] = f32_to_bf16(acc[i][j][r]);
+                    ep[row * kEpStride + lcol] = f32_to_bf16(acc[i][j][r]);
                 }
             }
+        }
+    }
+    __syncthreads();
+    {
+        constexpr int kChunks = kEpCols / 8;        // 16-byte chunks per tile row
+        const int Nout = KIND == 0 ? N / 2 : N;
+        const int c0 = nt * kEpCols;                // first output column of the tile
+        uint16_t* out = (uint16_t*)S.out;
+        for (int c = tid; c < live * kChunks; c += C::kThreads) {
+            const int row = c / kChunks, cc = c % kChunks;
+            const uint4 v = *(const uint4*)(ep + row * kEpStride + cc * 8);
+            const size_t grow = (size_t)rbase + m0 + row;
+            const int col = c0 + cc * 8;
+            size_t oi;
+            if (KIND == 0 && S.out_kblock)
+                oi = ((size_t)(col / 32) * S.rows_total + grow) * 32 + col % 32;
+            else
+                oi = grow * Nout + col;
+            *(uint4*)(out + oi) = v;
         }
     }
 }
@@ -823,34 +843,33 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs ga) {
 // ---------------------------------------------------------------------------------------
 // configurations
 // ---------------------------------------------------------------------------------------
-// bf16 tile configurations (BM, BN, BK, WM, WN, STAGES, register-staged loads). GEMM1's BN counts gate + up rows
+// bf16 tile configurations (BM, BN, BK, WM, WN, A ring depth, B ring depth). GEMM1's BN counts gate + up rows
 // (BN / 2 act columns).
 #ifndef MOE_BF_UP_CFG
-#define MOE_BF_UP_CFG 256, 256, 64, 2, 4, 2, 0
+#define MOE_BF_UP_CFG 256, 256, 64, 2, 4, 2, 2
 #endif
 #ifndef MOE_BF_DOWN_CFG
-#define MOE_BF_DOWN_CFG 256, 256, 64, 2, 4, 2, 0
+#define MOE_BF_DOWN_CFG 256, 256, 64, 2, 4, 2, 2
 #endif
 
-template <int KIND, int BM, int BN, int BK, int WM, int WN, int STAGES, int LOADREG>
+template <int KIND, int BM, int BN, int BK, int WM, int WN, int SA, int SB>
 hipError_t run_bf16(const GemmArgs& ga, int nblocks, hipStream_t s) {
-    using C = BfCfg<KIND, BM, BN, BK, WM, WN, STAGES, LOADREG>;
+    using C = BfCfg<KIND, BM, BN, BK, WM, WN, SA, SB>;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(
-            (const void*)gemm_bf16_kernel<KIND, BM, BN, BK, WM, WN, STAGES, LOADREG>,
+            (const void*)gemm_bf16_kernel<KIND, BM, BN, BK, WM, WN, SA, SB>,
             hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::kLds);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    gemm_bf16_kernel<KIND, BM, BN, BK, WM, WN, STAGES, LOADREG>
-        <<<nblocks, C::kThreads, C::kLds, s>>>(ga);
+    gemm_bf16_kernel<KIND, BM, BN, BK, WM, WN, SA, SB><<<nblocks, C::kThreads, C::kLds, s>>>(ga);
     return hipGetLastError();
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int STAGES, int LOADREG>
+template <int BM, int BN, int BK, int WM, int WN, int SA, int SB>
 constexpr int cfg_bm() { return BM; }
-template <int BM, int BN, int BK, int WM, int WN, int STAGES, int LOADREG>
+template <int BM, int BN, int BK, int WM, int WN, int SA, int SB>
 constexpr int cfg_bn() { return BN; }
 
 // e4m3 tile configuration (BM, BN, WM, WN, STAGES), both GEMMs
