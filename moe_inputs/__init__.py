@@ -5,9 +5,11 @@ This module holds no step of the method: it only draws random numbers and rounds
 to the storage type (fp32 -> bf16 by round-to-nearest-even, done by torch's cast).
 Nothing here routes, permutes, multiplies or quantises.
 
-Every tensor comes from its own numpy PCG64 stream, keyed by
-SeedSequence([BASE_SEED, config id, tensor tag, expert]); one stream per expert lets a
-caller regenerate a single expert's weights and lets generation run in threads.
+Every tensor comes from its own seeded stream, keyed by
+SeedSequence([BASE_SEED, config id, tensor tag, expert]): numpy PCG64 for x, the router
+weight and the biases; for the expert weights (the bulk of the bytes) a torch CPU generator
+seeded with that key's 63-bit state, one stream per expert, so a single expert can be
+regenerated alone and generation can run in threads.
 
 Layouts (row-major, K contiguous for both GEMM operands):
   x        [T, H]          activations, N(0, 1)
@@ -97,6 +99,19 @@ def _normal(cfg_id: int, tag: int, expert: int, shape, sigma: float) -> np.ndarr
     return a
 
 
+def _torch_seed(cfg_id: int, tag: int, expert: int) -> int:
+    st = np.random.SeedSequence([BASE_SEED, cfg_id, tag, expert]).generate_state(1, np.uint64)
+    return int(st[0]) & ((1 << 63) - 1)
+
+
+def _normal_torch(cfg_id: int, tag: int, expert: int, shape, sigma: float) -> torch.Tensor:
+    g = torch.Generator().manual_seed(_torch_seed(cfg_id, tag, expert))
+    a = torch.randn(tuple(shape), generator=g, dtype=torch.float32)
+    if sigma != 1.0:
+        a.mul_(sigma)
+    return a
+
+
 def _to_storage(a: np.ndarray, dtype: int) -> torch.Tensor:
     t = torch.from_numpy(a)
     if dtype == F32:
@@ -110,7 +125,7 @@ def _stacked(cfg_id, tag, n, shape, sigma, dtype, threads) -> torch.Tensor:
     out = torch.empty((n,) + tuple(shape), dtype=tdt)
 
     def one(e):
-        out[e].copy_(_to_storage(_normal(cfg_id, tag, e, shape, sigma), dtype))
+        out[e].copy_(_normal_torch(cfg_id, tag, e, shape, sigma))
 
     if n == 1 or threads <= 1:
         for e in range(n):
@@ -180,8 +195,8 @@ def make_inputs(cfg: MoEConfig, weights: bool = True, threads: int | None = None
         inp.w13 = _stacked(cfg.cfg_id, TAG_W13, cfg.E, (2 * cfg.F, cfg.H), 0.02, sd, threads)
         inp.w2 = _stacked(cfg.cfg_id, TAG_W2, cfg.E, (cfg.H, cfg.F), 0.02, sd, threads)
         if cfg.shared_F:
-            inp.ws13 = _to_storage(_normal(cfg.cfg_id, TAG_WS13, 0, (2 * cfg.shared_F, cfg.H), 0.02), sd)
-            inp.ws2 = _to_storage(_normal(cfg.cfg_id, TAG_WS2, 0, (cfg.H, cfg.shared_F), 0.02), sd)
+            inp.ws13 = _stacked(cfg.cfg_id, TAG_WS13, 1, (2 * cfg.shared_F, cfg.H), 0.02, sd, 1)[0]
+            inp.ws2 = _stacked(cfg.cfg_id, TAG_WS2, 1, (cfg.H, cfg.shared_F), 0.02, sd, 1)[0]
     if cfg.backward:
         inp.dy = _to_storage(_normal(cfg.cfg_id, TAG_DY, 0, (cfg.T, cfg.H), 1.0), BF16)
     return inp

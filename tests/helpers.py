@@ -73,3 +73,39 @@ def block(t):
     b = t.contiguous().view(torch.uint8).reshape(-1, rows, cols * eb // 64, 64)
     b = b.permute(0, 2, 1, 3).contiguous().reshape(-1)
     return b.view(t.dtype).reshape(t.shape)
+
+
+def e4m3_rank(q):
+    """Signed position of an e4m3 code on the number line (codes are sign-magnitude)."""
+    q = np.asarray(q).astype(np.int32)
+    mag = q & 0x7F
+    return np.where(q & 0x80, -mag, mag)
+
+
+def e4m3_step(v):
+    """Spacing of e4m3 values at |v| (v in units of the block scale): 2^(e - 3) for normal
+    values (2^-6 <= |v| < 448, e = floor(log2 |v|)), 2^-9 below."""
+    a = np.minimum(np.abs(np.asarray(v, np.float64)), 448.0)
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -6)))
+    return np.where(a < 2.0 ** -6, 2.0 ** -9, 2.0 ** (e - 3))
+
+
+def e4m3_codes_close(q_gpu, s_gpu, act_ref_f64, err=1e-3):
+    """Compare quantised rows (codes + 1 x 128 scales) with the oracle's unquantised
+    activation act_ref. The GPU quantises its own fp32 value, which differs from the
+    oracle's by accumulation rounding, so each dequantised element must lie within one e4m3
+    step of act_ref (the quantisation error) plus err of the block's scale range (the
+    propagated rounding). Returns (max |error| / bound, fraction of codes differing from the
+    oracle's own quantisation, max scale rel diff)."""
+    import oracle
+    ref32 = np.asarray(act_ref_f64, np.float64).astype(np.float32)
+    q_ref, s_ref = oracle.quant_rows(ref32)
+    s_ref_e = np.repeat(np.asarray(s_ref, np.float64), 128, axis=1)
+    s_gpu_e = np.repeat(np.asarray(s_gpu, np.float64), 128, axis=1)
+    v_ref = ref32.astype(np.float64) / s_ref_e
+    v_gpu = oracle.e4m3_decode_array(np.asarray(q_gpu)) * s_gpu_e / s_ref_e
+    bound = e4m3_step(v_ref) + err * 448.0
+    ratio = float(np.max(np.abs(v_gpu - v_ref) / bound))
+    frac = float((np.asarray(q_gpu) != q_ref).mean())
+    srel = float(np.max(np.abs(np.asarray(s_gpu, np.float64) - s_ref) / np.maximum(np.abs(s_ref), 1e-30)))
+    return ratio, frac, srel

@@ -11,9 +11,14 @@ def test_deterministic_and_per_expert_streams():
     b = mi.make_inputs(cfg, threads=1)
     for n in ("x", "w_router", "w13", "w2"):
         assert torch.equal(getattr(a, n), getattr(b, n))
-    # one expert can be regenerated alone
-    e3 = mi._normal(cfg.cfg_id, mi.TAG_W13, 3, (2 * cfg.F, cfg.H), 0.02)
-    assert np.array_equal(a.w13[3].numpy(), e3)
+    # one expert can be regenerated alone (its own seeded stream)
+    e3 = mi._normal_torch(cfg.cfg_id, mi.TAG_W13, 3, (2 * cfg.F, cfg.H), 0.02)
+    assert torch.equal(a.w13[3], e3)
+    assert not torch.equal(a.w13[3], a.w13[4])
+    # bf16 storage of a weight is the round-to-nearest-even of the same fp32 draw
+    c = mi.CONFIGS["qwen3_bf16"].replace(T=8, H=256, E=4, k=2, F=128)
+    w = mi.make_inputs(c).w13
+    assert torch.equal(w[2], mi._normal_torch(c.cfg_id, mi.TAG_W13, 2, (2 * c.F, c.H), 0.02).to(torch.bfloat16))
     assert a.x.dtype == torch.float32 and a.x.shape == (256, 128)
 
 

@@ -108,3 +108,24 @@ def test_quant_weight_matches_definition():
     q_ref = _torch_quant_blocks(wb, s_ref[:, :, :, None, None])
     q_ref = q_ref.permute(0, 1, 3, 2, 4).reshape(2, 256, 384).numpy()
     np.testing.assert_array_equal(q, q_ref)
+
+
+def test_e4m3_rank_orders_codes_like_their_values():
+    """The code-distance helper used for quantised tensors: sorting finite codes by rank
+    sorts them by value, and neighbouring ranks are neighbouring representable values."""
+    from helpers import e4m3_rank
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)   # no NaN
+    vals = oracle.e4m3_decode_array(codes)
+    r = e4m3_rank(codes)
+    order = np.argsort(r, kind="stable")
+    assert np.all(np.diff(vals[order]) >= 0)
+    pos = codes[(codes & 0x80) == 0]
+    assert np.all(np.diff(oracle.e4m3_decode_array(np.sort(pos))) > 0)
+
+
+def test_e4m3_step_matches_the_code_table():
+    """e4m3_step(v) is the gap between the two representable values around v."""
+    from helpers import e4m3_step
+    vals = np.sort(oracle.e4m3_decode_array(np.arange(0, 127, dtype=np.uint8)))
+    gaps = np.diff(vals)
+    np.testing.assert_array_equal(e4m3_step(vals[:-1]), gaps)
