@@ -110,6 +110,46 @@ def pmc_summary(dbs):
             print(f"{kn[:110]} | dispatches {n} | avg us {avg:.1f} | {cs}")
 
 
+def write_traffic(fetch_db, write_db, copy_gib, workload, cmd):
+    """Bytes per launch of the up GEMM from two counter runs (FETCH_SIZE, then WRITE_SIZE, in
+    KiB per dispatch), each scaled by what the same counter read for the plain copy of
+    copy_gib GiB issued by --calib-copy-gib in the same run; written to TRAFFIC_FILE."""
+    import sqlite3
+
+    def per_dispatch(db, counter):
+        c = sqlite3.connect(db)
+        rows = c.execute("select kernel_name, dispatch_id, sum(value) from counters_collection "
+                         "where counter_name = ? group by dispatch_id", (counter,)).fetchall()
+        copy = max(v for kn, _, v in rows if "copyBuffer" in kn)
+        up = [v for kn, _, v in rows if "gemm_bf16_kernel<0," in kn]
+        return copy, sum(up) / len(up), len(up)
+
+    nbytes = copy_gib * (1 << 30)
+    fc, fu, nf = per_dispatch(fetch_db, "FETCH_SIZE")
+    wc, wu, nw = per_dispatch(write_db, "WRITE_SIZE")
+    ff, fw = nbytes / (fc * 1024), nbytes / (wc * 1024)
+    lines = [
+        "# HBM traffic of one launch of the grouped GEMM up (gemm_bf16_kernel<0, ...>)",
+        "# counters: rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE (KiB per dispatch), each",
+        "# scaled by the factor that maps the same counter onto a plain device copy of known",
+        "# size issued in the same run (bytes copied / counter bytes)",
+        f"# command: {cmd}",
+        f"workload: {workload}",
+        f"source_sha256: {sources_sha256()}",
+        f"calibration_copy_bytes: {nbytes}",
+        f"fetch_factor: {ff:.5f}",
+        f"write_factor: {fw:.5f}",
+        f"up_dispatches: {nf} / {nw}",
+        f"fetch_kib_per_launch_raw: {fu:.1f}",
+        f"write_kib_per_launch_raw: {wu:.1f}",
+        f"fetch_bytes_per_launch: {fu * 1024 * ff:.0f}",
+        f"write_bytes_per_launch: {wu * 1024 * fw:.0f}",
+    ]
+    with open(TRAFFIC_FILE, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def cpu_baseline(cfg, inp, sample: int):
     """The oracle, as it stands, end to end on `sample` seeded tokens of the same workload."""
     import numpy as np
@@ -185,13 +225,27 @@ def main():
     ap.add_argument("--workload", default="dsv3_bf16")
     ap.add_argument("--cpu-sample", type=int, default=1024)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--stage-reps", type=int, default=5)
+    ap.add_argument("--bwd-reps", type=int, default=5,
+                    help="timed repetitions of the backward (workloads that have one)")
     ap.add_argument("--calib-copy-gib", type=float, default=0.0,
                     help="issue one device copy of this many GiB before the steps (a plain copy "
                          "of known size for scaling the traffic counters)")
     ap.add_argument("--pmc-summary", nargs="+", metavar="DB",
                     help="print per-kernel counter averages of rocprofv3 databases and exit")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
+                    help="record the up GEMM's bytes per launch from two counter databases "
+                         "of runs made with --calib-copy-gib, then exit")
     args = ap.parse_args()
+    if args.write_traffic:
+        run = ("-- python -u bench.py --workload " + args.workload + " --steps 2 --warmup 1 "
+               f"--no-cpu --calib-copy-gib {args.calib_copy_gib:g}")
+        rx = "--kernel-include-regex 'gemm_bf16|copyBuffer|elementwise'"
+        cmd = (f"export TMPDIR=/tmp; rocprofv3 --pmc FETCH_SIZE {rx} -d <dir> -o f {run}; "
+               f"rocprofv3 --pmc WRITE_SIZE TCC_HIT_sum TCC_MISS_sum {rx} -d <dir> -o w {run}; "
+               f"python bench.py --write-traffic <dir>/f_results.db <dir>/w_results.db "
+               f"--calib-copy-gib {args.calib_copy_gib:g}")
+        write_traffic(*args.write_traffic, args.calib_copy_gib, args.workload, cmd)
+        return
     if args.pmc_summary:
         pmc_summary(args.pmc_summary)
         return
@@ -242,7 +296,6 @@ def main():
         del src_c, dst_c
     y = torch.empty(cfg.T, cfg.H, dtype=moe.act_torch_dtype(cfg), device=dev)
     ws = moe.workspace(cfg, moe.OP_LAYER_FORWARD, dev)
-    counts = torch.empty(cfg.E, dtype=torch.int32, device=dev)
     torch.cuda.synchronize()
 
     def step():
@@ -254,78 +307,40 @@ def main():
         step()
     torch.cuda.synchronize()
     log(f"[bench] timing {args.steps} steps")
+    # every step records 7 events at its stage boundaries on the stream the library launches
+    # on (torch's current stream), so each kernel's duration is measured inside the timed steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(moe.N_STAGE_EVENTS)]
+          for _ in range(args.steps)]
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for evs in ev:              # create the HIP events before the timed region
+        moe.set_stage_events(evs)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     e0.record()
-    for _ in range(args.steps):
+    for evs in ev:
+        moe.set_stage_events(evs)
         step()
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
+    moe.set_stage_events(None)
     ms = e0.elapsed_time(e1) / args.steps
     log(f"[bench] {ms:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f} ms/step)")
+    times = {name: sum(evs[i].elapsed_time(evs[i + 1]) for evs in ev) / args.steps
+             for i, name in enumerate(moe.STAGES)}
+    log("[bench] stages (ms, mean over the timed steps): " +
+        ", ".join(f"{k} {v:.3f}" for k, v in times.items()))
 
-    # ---- per-stage times: the same work as one step, one C-ABI call per stage, each
-    # bracketed by events on the stream the library launches on
-    A = cfg.T * cfg.k
-    logits = torch.empty(cfg.T, cfg.E, dtype=torch.float32, device=dev)
-    idx = torch.empty(cfg.T, cfg.k, dtype=torch.int32, device=dev)
-    gate = torch.empty(cfg.T, cfg.k, dtype=torch.float32, device=dev)
-    pws = moe.workspace(cfg, moe.OP_PERMUTE, dev)
-    gws = moe.workspace(cfg, moe.OP_GROUPED_GEMM, dev)
-    gd, ad = moe.gemm_torch_dtype(cfg), moe.act_torch_dtype(cfg)
-    act = torch.empty(A, cfg.F, dtype=gd, device=dev)
-    y_perm = torch.empty(A, cfg.H, dtype=ad, device=dev)
-    sh_act = torch.empty(cfg.T, cfg.shared_F, dtype=gd, device=dev) if cfg.shared_F else None
-    sh_y = torch.empty(cfg.T, cfg.H, dtype=ad, device=dev) if cfg.shared_F else None
-    f32 = torch.float32
-    act_sc = torch.empty(A, cfg.F // 128, dtype=f32, device=dev) if fp8 else None
-    sh_act_sc = (torch.empty(cfg.T, cfg.shared_F // 128, dtype=f32, device=dev)
-                 if fp8 and cfg.shared_F else None)
-    perm = {}
-
-    def x_sh():
-        if not cfg.shared_F:
-            return None, None
-        return (perm["x_q"], perm["x_q_scales"]) if fp8 else (x, None)
-
-    stages = {
-        "router_logits": lambda: moe.router_logits(cfg, x, wr, logits),
-        "route": lambda: moe.route(cfg, logits, lb, sb, idx, gate),
-        "permute": lambda: perm.update(moe.permute(cfg, x, idx, gate, ws=pws,
-                                                   want_x_q=fp8 and bool(cfg.shared_F))),
-        "grouped_gemm_up": lambda: moe.grouped_gemm_up(
-            cfg, perm["x_perm"], perm["offsets"], perm["gate_perm"], w13, act,
-            x_perm_scales=perm["x_perm_scales"], w13_scales=sc["w13_scales"],
-            x_shared=x_sh()[0], x_shared_scales=x_sh()[1], ws13=ws13,
-            ws13_scales=sc["ws13_scales"], act_scales=act_sc, shared_act=sh_act,
-            shared_act_scales=sh_act_sc, ws=gws),
-        "grouped_gemm_down": lambda: moe.grouped_gemm_down(
-            cfg, act, perm["offsets"], w2, y_perm, act_scales=act_sc,
-            w2_scales=sc["w2_scales"], shared_act=sh_act, shared_act_scales=sh_act_sc,
-            ws2=ws2, ws2_scales=sc["ws2_scales"], shared_y=sh_y, ws=gws),
-        "combine": lambda: moe.unpermute_combine(cfg, y_perm, perm["pos"], sh_y, y),
-    }
-    times = {k: 0.0 for k in stages}
-    for rep in range(args.stage_reps + 1):
-        for name, fn in stages.items():
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            fn()
-            b.record()
-            torch.cuda.synchronize()
-            if rep > 0:
-                times[name] += a.elapsed_time(b) / args.stage_reps
     _, ex = moe.layer_forward(cfg, x, wr, w13, w2, lb, sb, None, ws13=ws13, ws2=ws2, y=y,
-                              ws=ws, want=("counts",), **sc)
+                              ws=ws, want=("counts", "topk_idx", "topk_gate"), **sc)
     cnt = ex["counts"].cpu().double()
+    idx, gate = ex["topk_idx"], ex["topk_gate"]
     torch.cuda.synchronize()
 
     backward = None
     if cfg.backward:
         backward = time_backward(moe, mi, cfg, dev, x, inp, idx, gate, w13_bf, w2_bf,
-                                 args.stage_reps)
+                                 args.bwd_reps)
     alg = algorithmic(cfg)
     dtype = {0: "fp32", 1: "bf16", 2: "e4m3"}[cfg.w_dtype]
     per_stage = {}

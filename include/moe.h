@@ -213,6 +213,18 @@ int moe_layer_forward(const moe_config* cfg, const void* x, const void* w_router
                       int32_t* topk_idx_out, float* topk_gate_out, int32_t* counts_out,
                       void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Stage timing of moe_layer_forward (instrumentation; computes nothing). Not from the
+ * pages: it lets a caller time each kernel of the layer on the stream it runs on.
+ * events: MOE_N_STAGE_EVENTS hipEvent_t handles that the caller created (with timing) and
+ * keeps alive. Until the next call on the same host thread, every moe_layer_forward on that
+ * thread records events[i] on its stream when stage i starts and events[6] when the last one
+ * ends; stages: 0 router logits (no kernel when logits_in is given), 1 top-k routing,
+ * 2 permutation, 3 grouped GEMM up (gate/up + SwiGLU), 4 grouped GEMM down, 5 combine.
+ * events == NULL turns recording off. n_events other than MOE_N_STAGE_EVENTS, or a NULL
+ * handle, gives MOE_ERR_INVALID_ARG and leaves the previous setting. */
+#define MOE_N_STAGE_EVENTS 7
+int moe_set_stage_events(void* const* events, int32_t n_events);
+
 /* Backward of the grouped expert MLP with the gate fold (bf16 operands, fp32
  * accumulation), data and weight gradients as separate grouped GEMMs (the W/D split of the
  * technical summary, section 2.3). Per expert rows R_e = [offsets[e], offsets[e+1]), with

@@ -70,6 +70,7 @@ _SIGS = {
     "moe_grouped_gemm_swiglu_bwd": [CFG, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
     "moe_quantize_e4m3": [P, I32, I64, I32, I32, I32, I32, P, P, P],
     "moe_pack_kblock": [P, I64, I32, I32, I32, P, P],
+    "moe_set_stage_events": [P, I32],
 }
 for _name, _args in _SIGS.items():
     getattr(_lib, _name).argtypes = _args
@@ -407,3 +408,24 @@ def pack_kblock(t, out=None, stream=None):
     _check("moe_pack_kblock", _lib.moe_pack_kblock(
         _ptr(t, name="input"), n, rows, cols, t.element_size(), _ptr(out), _stream(stream)))
     return out
+
+
+N_STAGE_EVENTS = 7
+STAGES = ("router_logits", "route", "permute", "grouped_gemm_up", "grouped_gemm_down",
+          "combine")
+
+
+def set_stage_events(events):
+    """Make later layer_forward calls on this thread record the given torch.cuda.Event
+    objects (7, with timing) on their stream at each stage boundary (moe_set_stage_events);
+    None stops. The events must outlive their use."""
+    if events is None:
+        _check("moe_set_stage_events", _lib.moe_set_stage_events(None, 0))
+        return
+    if len(events) != N_STAGE_EVENTS:
+        raise ValueError(f"need {N_STAGE_EVENTS} events, got {len(events)}")
+    for ev in events:
+        if not ev.cuda_event:       # torch creates the HIP event on its first record
+            ev.record()
+    arr = (C.c_void_p * N_STAGE_EVENTS)(*[ev.cuda_event for ev in events])
+    _check("moe_set_stage_events", _lib.moe_set_stage_events(arr, N_STAGE_EVENTS))

@@ -55,6 +55,14 @@ int check_cfg(const moe_config* c) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// Stage events of moe_layer_forward (instrumentation): per host thread, caller-owned handles.
+thread_local hipEvent_t g_stage_ev[MOE_N_STAGE_EVENTS];
+thread_local bool g_stage_on = false;
+
+hipError_t stage_mark(int i, hipStream_t s) {
+    return g_stage_on ? hipEventRecord(g_stage_ev[i], s) : hipSuccess;
+}
+
 // ---- workspace layouts -------------------------------------------------------------------
 struct Carve {
     char* base;
@@ -200,7 +208,7 @@ int run_experts(const moe_config* c, int a_kb, const void* x_perm, const float* 
                 const void* x_shared, const float* x_shared_scales, const void* ws13,
                 const float* ws13_scales, const void* ws2, const float* ws2_scales, void* act,
                 float* act_scales, void* y_perm, void* shared_y, void* z_out, void* ws,
-                hipStream_t stream) {
+                hipStream_t stream, int mid_mark = -1) {
     Carve cv(ws);
     void* sched = cv.take(sched_ws_bytes(c));
     void* sh_act = nullptr;
@@ -214,6 +222,7 @@ int run_experts(const moe_config* c, int a_kb, const void* x_perm, const float* 
                     x_shared_scales, ws13, ws13_scales, act, act_scales, sh_act, sh_act_scales,
                     z_out, sched, stream);
     if (st) return st;
+    if (mid_mark >= 0 && stage_mark(mid_mark, stream) != hipSuccess) return MOE_ERR_HIP;
     return run_down(c, a_kb, act, act_scales, offsets, w2, w2_scales, sh_act, sh_act_scales, ws2,
                     ws2_scales, y_perm, shared_y, sched, stream);
 }
@@ -424,16 +433,18 @@ int moe_layer_forward(const moe_config* cfg, const void* x, const void* w_router
     int32_t* idx = topk_idx_out ? topk_idx_out : L.idx;
     float* gate = topk_gate_out ? topk_gate_out : L.gate;
     int32_t* counts = counts_out ? counts_out : L.counts;
-    hipError_t e = hipSuccess;
+    hipError_t e = stage_mark(0, stream);
     const float* lg = logits_in;
-    if (!lg) {
+    if (e == hipSuccess && !lg) {
         e = moe::launch_router_logits(cfg->act_dtype, x, w_router, cfg->T, cfg->H, cfg->E,
                                       logits, stream);
         lg = logits;
     }
+    if (e == hipSuccess) e = stage_mark(1, stream);
     if (e != hipSuccess) return MOE_ERR_HIP;
     e = moe::launch_route(cfg->router, lg, logit_bias, sel_bias, cfg->T, cfg->E, cfg->k,
                           cfg->n_groups, cfg->topk_groups, cfg->route_scale, idx, gate, stream);
+    if (e == hipSuccess) e = stage_mark(2, stream);
     if (e != hipSuccess) return MOE_ERR_HIP;
     const int mode = fp8 ? 2 : (cfg->act_dtype == MOE_F32 ? 0 : 1);
     // internal activations (x_perm, act, the shared expert's act) are K-blocked: every
@@ -442,15 +453,33 @@ int moe_layer_forward(const moe_config* cfg, const void* x, const void* w_router
     e = moe::launch_permute(mode, a_kb, x, idx, gate, cfg->T, cfg->H, cfg->E, cfg->k, counts,
                             L.offsets, L.pos, L.src, L.gate_perm, L.x_perm, L.x_perm_scales,
                             L.x_q, L.x_q_scales, L.scratch, stream);
+    if (e == hipSuccess) e = stage_mark(3, stream);
     if (e != hipSuccess) return MOE_ERR_HIP;
     const void* xs = fp8 ? L.x_q : x;
     st = run_experts(cfg, a_kb, L.x_perm, L.x_perm_scales, L.offsets, L.gate_perm, w13, w13_scales,
                      w2, w2_scales, cfg->shared_F ? xs : nullptr, fp8 ? L.x_q_scales : nullptr,
                      ws13, ws13_scales, ws2, ws2_scales, L.act, L.act_scales, L.y_perm,
-                     L.shared_y, nullptr, L.scratch, stream);
+                     L.shared_y, nullptr, L.scratch, stream, 4);
     if (st) return st;
-    return hip_status(moe::launch_combine(cfg->act_dtype, L.y_perm, L.pos, L.shared_y, cfg->T,
-                                          cfg->H, cfg->k, y, stream));
+    e = stage_mark(5, stream);
+    if (e == hipSuccess)
+        e = moe::launch_combine(cfg->act_dtype, L.y_perm, L.pos, L.shared_y, cfg->T, cfg->H,
+                                cfg->k, y, stream);
+    if (e == hipSuccess) e = stage_mark(6, stream);
+    return hip_status(e);
+}
+
+int moe_set_stage_events(void* const* events, int32_t n_events) {
+    if (!events) {
+        g_stage_on = false;
+        return MOE_OK;
+    }
+    if (n_events != MOE_N_STAGE_EVENTS) return MOE_ERR_INVALID_ARG;
+    for (int i = 0; i < MOE_N_STAGE_EVENTS; ++i)
+        if (!events[i]) return MOE_ERR_INVALID_ARG;
+    for (int i = 0; i < MOE_N_STAGE_EVENTS; ++i) g_stage_ev[i] = (hipEvent_t)events[i];
+    g_stage_on = true;
+    return MOE_OK;
 }
 
 int moe_grouped_gemm_swiglu_bwd(const moe_config* cfg, const void* dy_perm, const void* x_perm,

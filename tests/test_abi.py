@@ -153,3 +153,15 @@ def test_layout_validation(moe):
     assert L.moe_pack_kblock(p, 1, 16, 32, 3, q, None) == 1      # element size
     assert L.moe_pack_kblock(p, 0, 16, 32, 2, q, None) == 1      # no matrices
     assert L.moe_pack_kblock(p, 1, 16, 32, 2, p, None) == 1      # in place
+
+
+def test_stage_event_argument_checks(moe):
+    """moe_set_stage_events: NULL turns recording off; a wrong count or a NULL handle is an
+    invalid argument (host-side checks only, no HIP call is made)."""
+    L = moe.lib()
+    assert L.moe_set_stage_events(None, 0) == 0
+    arr = (C.c_void_p * 7)(*([0x1000] * 7))
+    assert L.moe_set_stage_events(arr, 6) == 1
+    arr[3] = None
+    assert L.moe_set_stage_events(arr, 7) == 1
+    assert L.moe_set_stage_events(None, 0) == 0

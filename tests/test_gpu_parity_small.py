@@ -174,6 +174,30 @@ def test_deterministic(moe, name):
     assert torch.equal(y1, y2)
 
 
+@pytest.mark.parametrize("name", ["dsv3_small", "mixtral_small"])
+def test_stage_events_leave_results_unchanged(moe, name):
+    """With stage events set, the layer gives the same bits, every event completes, and the
+    stage durations add up to the span of the call."""
+    c = case(name)
+    cfg, inp = c["cfg"], c["inp"]
+    args = (cfg, inp.x.cuda(), inp.w_router.cuda(), inp.w13.cuda(), inp.w2.cuda(),
+            to_dev(inp.logit_bias), to_dev(inp.sel_bias))
+    kw = dict(ws13=to_dev(inp.ws13), ws2=to_dev(inp.ws2))
+    y1, _ = moe.layer_forward(*args, **kw)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(moe.N_STAGE_EVENTS)]
+    moe.set_stage_events(evs)
+    try:
+        y2, _ = moe.layer_forward(*args, **kw)
+    finally:
+        moe.set_stage_events(None)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    assert all(e.query() for e in evs)
+    parts = [evs[i].elapsed_time(evs[i + 1]) for i in range(moe.N_STAGE_EVENTS - 1)]
+    assert min(parts) >= 0.0
+    assert abs(sum(parts) - evs[0].elapsed_time(evs[-1])) <= 1e-2
+
+
 # ---------------------------------------------------------------------------------------
 # K-blocked layouts (expert-grouped activations and packed expert weights)
 # ---------------------------------------------------------------------------------------
