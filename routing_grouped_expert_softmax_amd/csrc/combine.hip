@@ -6,48 +6,74 @@
 // e4m3 block quantisation (the FP8 E4M3 format of "万亿参数MoE模型训练的技术挑战",
 // section 2.1) of weights (128 x 128 blocks) and activations (1 x 128 blocks) lives here
 // too: both are HBM-streaming kernels.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
+
+#ifndef MOE_COMBINE_NT
+#define MOE_COMBINE_NT 1
+#endif
 
 namespace moe {
 namespace {
 
-// bf16: one wavefront per token, 8 values (16 bytes) per lane per step.
+MOE_DEVICE void add_bf16x8(float (&acc)[8], const uint4 v) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        acc[2 * i] += bf16_to_f32((uint16_t)(w[i] & 0xFFFFu));
+        acc[2 * i + 1] += bf16_to_f32((uint16_t)(w[i] >> 16));
+    }
+}
+
+MOE_DEVICE uint4 load_stream(const uint4* p) {
+#if MOE_COMBINE_NT
+    const i32x4_t q = __builtin_nontemporal_load((const i32x4_t*)p);
+    return uint4{(uint32_t)q.x, (uint32_t)q.y, (uint32_t)q.z, (uint32_t)q.w};
+#else
+    return *p;
+#endif
+}
+
+// bf16: one wavefront per token, 8 values (16 bytes) per lane per step. KC > 0 is k known at
+// compile time: the k row loads of a step are all issued before the first add, so a wave
+// keeps k * 1 KB in flight. KC == 0 takes k at run time, one row at a time. Either way the
+// adds run in slot order j = 0 .. k - 1, then the shared expert's row.
+template <int KC>
 __global__ __launch_bounds__(256) void combine_bf16_kernel(const uint4* __restrict__ y_perm,
                                                            const int32_t* __restrict__ pos,
                                                            const uint4* __restrict__ shared_y,
-                                                           int T, int row_chunks, int k,
+                                                           int T, int row_chunks, int k_rt,
                                                            uint4* __restrict__ y) {
+    const int k = KC > 0 ? KC : k_rt;
     const int lane = threadIdx.x % kWave;
     const int t = blockIdx.x * 4 + threadIdx.x / kWave;
     if (t >= T) return;
-    int my_pos = lane < k ? pos[(size_t)t * k + lane] : 0;
+    const int my_pos = lane < k ? pos[(size_t)t * k + lane] : 0;
     for (int c0 = 0; c0 < row_chunks; c0 += kWave) {
         const int c = c0 + lane;
         const bool ok = c < row_chunks;
         float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        for (int j = 0; j < k; ++j) {
-            int r = __shfl(my_pos, j);
-            if (ok) {
-                uint4 v = y_perm[(size_t)r * row_chunks + c];
-                uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        if (KC > 0) {
+            uint4 v[KC > 0 ? KC : 1];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    acc[2 * i] += bf16_to_f32((uint16_t)(w[i] & 0xFFFFu));
-                    acc[2 * i + 1] += bf16_to_f32((uint16_t)(w[i] >> 16));
-                }
+            for (int j = 0; j < KC; ++j) {
+                const int r = __shfl(my_pos, j);
+                v[j] = ok ? load_stream(y_perm + (size_t)r * row_chunks + c) : uint4{};
             }
+            const uint4 sv = shared_y && ok ? shared_y[(size_t)t * row_chunks + c] : uint4{};
+#pragma unroll
+            for (int j = 0; j < KC; ++j) add_bf16x8(acc, v[j]);
+            if (shared_y) add_bf16x8(acc, sv);
+        } else {
+            for (int j = 0; j < k; ++j) {
+                const int r = __shfl(my_pos, j);
+                if (ok) add_bf16x8(acc, y_perm[(size_t)r * row_chunks + c]);
+            }
+            if (shared_y && ok) add_bf16x8(acc, shared_y[(size_t)t * row_chunks + c]);
         }
         if (!ok) continue;
-        if (shared_y) {
-            uint4 v = shared_y[(size_t)t * row_chunks + c];
-            uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                acc[2 * i] += bf16_to_f32((uint16_t)(w[i] & 0xFFFFu));
-                acc[2 * i + 1] += bf16_to_f32((uint16_t)(w[i] >> 16));
-            }
-        }
         uint4 o;
         o.x = pack_bf16x2(acc[0], acc[1]);
         o.y = pack_bf16x2(acc[2], acc[3]);
@@ -196,10 +222,20 @@ hipError_t launch_combine(int act_dtype, const void* y_perm, const int32_t* pos,
         combine_f32_kernel<<<blocks, 256, 0, s>>>((const float4*)y_perm, pos,
                                                   (const float4*)shared_y, T, H / 4, k,
                                                   (float4*)y);
-    else
-        combine_bf16_kernel<<<blocks, 256, 0, s>>>((const uint4*)y_perm, pos,
-                                                   (const uint4*)shared_y, T, H / 8, k,
-                                                   (uint4*)y);
+    else {
+        auto run = [&](auto kc) {
+            combine_bf16_kernel<decltype(kc)::value><<<blocks, 256, 0, s>>>(
+                (const uint4*)y_perm, pos, (const uint4*)shared_y, T, H / 8, k, (uint4*)y);
+        };
+        switch (k) {
+        case 1: run(std::integral_constant<int, 1>{}); break;
+        case 2: run(std::integral_constant<int, 2>{}); break;
+        case 4: run(std::integral_constant<int, 4>{}); break;
+        case 6: run(std::integral_constant<int, 6>{}); break;
+        case 8: run(std::integral_constant<int, 8>{}); break;
+        default: run(std::integral_constant<int, 0>{}); break;
+        }
+    }
     return hipGetLastError();
 }
 

@@ -112,9 +112,22 @@ struct GemmArgs {
     int N, K;          // GEMM N (before SwiGLU pairing) and K
     int ntn;           // N tiles
     int per_xcd_max;   // launched blocks / 8
+    int bm;            // M tile rows
+    int mgroup;        // M tiles of one group visited together per N tile
 };
 
-// Map this workgroup to a live tile (XCD-aware); false when there is none.
+// Map this workgroup to a live tile; false when there is none.
+//
+// Tile order. The tiles of one group (expert) form a block [its M tiles] x [ntn N tiles]
+// that occupies the same run of linear ids whatever the order inside it. Inside, M tiles go
+// in bands of up to mgroup, and within a band the M index runs fastest: the M tiles that
+// read the same weight tile get neighbouring ids, so they start together and the later
+// readers find that weight in L2 (or the memory-side cache) instead of HBM. Each N tile
+// of a band still reuses the band's activation rows from one XCD's L2.
+//
+// XCD-aware launch: the hardware deals workgroups round-robin over 8 XCDs, so workgroup b
+// runs on XCD b % 8; it takes linear id (b % 8) * per + b / 8, which gives every XCD one
+// contiguous run of ids.
 MOE_DEVICE bool pick_tile(const GemmArgs& ga, int& mt, int& nt) {
     const int b = blockIdx.x;
     const int xcd = b % 8, i = b / 8;
@@ -123,8 +136,16 @@ MOE_DEVICE bool pick_tile(const GemmArgs& ga, int& mt, int& nt) {
     if (i >= per) return false;
     const int L = xcd * per + i;
     if (L >= total) return false;
-    mt = L / ga.ntn;
-    nt = L % ga.ntn;
+    const int ntn = ga.ntn, bm = ga.bm;
+    const int4 t = ga.tiles[L / ntn];                 // some M tile of L's group
+    const int mt0 = L / ntn - t.y / bm;               // the group's first M tile
+    const int me = (t.z + bm - 1) / bm;               // the group's M tiles
+    const int local = L - mt0 * ntn;
+    const int band = local / (ga.mgroup * ntn) * ga.mgroup;
+    const int mb = me - band < ga.mgroup ? me - band : ga.mgroup;
+    const int r = local - band * ntn;
+    mt = mt0 + band + r % mb;
+    nt = r / mb;
     return true;
 }
 
@@ -141,6 +162,10 @@ MOE_DEVICE bool pick_tile(const GemmArgs& ga, int& mt, int& nt) {
 // Ragged tails: a wave skips the loads and MFMAs of its 32-row sub-tiles that lie wholly
 // past the expert's last row, so a tile with few live rows costs few MFMA cycles.
 // ---------------------------------------------------------------------------------------
+
+#ifndef MOE_BF_INTERLEAVE
+#define MOE_BF_INTERLEAVE 1
+#endif
 
 template <int KIND, int BM, int BN, int BK, int WM, int WN, int SA, int SB>
 struct BfCfg {
@@ -159,6 +184,13 @@ struct BfCfg {
     static constexpr int kSub = BK / 16;                    // MFMA K steps per stage
     static constexpr int kSlices = kRowBytes / 64;          // 64-byte K slices per stage
     static constexpr int kSA = SA, kSB = SB;
+    // Row order of the waves' 32-row sub-tiles: interleaved (sub-tile i of wave row wm at
+    // rows (i * WM + wm) * 32), so a ragged tile's live rows spread over all the waves, or
+    // blocked (wm * BM / WM + i * 32).
+    static constexpr bool kInterleave = MOE_BF_INTERLEAVE != 0;
+    static constexpr MOE_DEVICE int sub_row(int wm, int i) {
+        return kInterleave ? (i * WM + wm) * 32 : wm * (BM / WM) + i * 32;
+    }
     static constexpr int kEpCols = KIND == 0 ? BN / 2 : BN;       // output columns of a tile
     static constexpr int kEpStride = kEpCols + 8;                 // bf16, padded row
     static constexpr size_t kLdsLoop = (size_t)SA * kASlot + (size_t)SB * kBSlot;
@@ -288,9 +320,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs ga) {
     const int N = ga.N, K = ga.K;
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int wm = wave / WN, wn = wave % WN;
-    // live rows of the tile, and this wave's live 32-row sub-tiles
+    // live rows of the tile, and this wave's live 32-row sub-tiles (its sub-tile i is tile
+    // rows C::sub_row(wm, i) + [0, 32); the live ones are a prefix i < nvi)
     const int live = Mg - m0 < BM ? Mg - m0 : BM;
-    int nvi = (live - wm * (BM / WM) + 31) / 32;
+    int nvi = C::kInterleave ? ((live + 31) / 32 - wm + WM - 1) / WM
+                             : (live - wm * (BM / WM) + 31) / 32;
     nvi = nvi < 0 ? 0 : (nvi > C::kTM ? C::kTM : nvi);
     nvi = __builtin_amdgcn_readfirstlane(nvi);
 
@@ -341,7 +375,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs ga) {
     int a_off[C::kTM], b_off[C::kTN];
 #pragma unroll
     for (int i = 0; i < C::kTM; ++i)
-        a_off[i] = (wm * (BM / WM) + i * 32 + lane % 32) * C::kRowBytes;
+        a_off[i] = (C::sub_row(wm, i) + lane % 32) * C::kRowBytes;
 #pragma unroll
     for (int j = 0; j < C::kTN; ++j) {
         int row;
@@ -410,7 +444,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs ga) {
                 const int col = nt * (BN / 2) + lcol;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int row = wm * (BM / WM) + i * 32 + (r / 4) * 8 + (lane / 32) * 4 + r % 4;
+                    const int row = C::sub_row(wm, i) + (r / 4) * 8 + (lane / 32) * 4 + r % 4;
                     const int lr = m0 + row < Mg ? row : live - 1;     // dead rows: any gate
                     const size_t grow = (size_t)rbase + m0 + lr;
                     const float zg = acc[i][jj][r], zu = acc[i][half + jj][r];
@@ -432,7 +466,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs ga) {
                 const int lcol = wn * (BN / WN) + j * 32 + lane % 32;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int row = wm * (BM / WM) + i * 32 + (r / 4) * 8 + (lane / 32) * 4 + r % 4;
+                    const int row = C::sub_row(wm, i) + (r / 4) * 8 + (lane / 32) * 4 + r % 4;
                     ep[row * kEpStride + lcol] = f32_to_bf16(acc[i][j][r]);
                 }
             }
@@ -843,6 +877,11 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs ga) {
 // ---------------------------------------------------------------------------------------
 // configurations
 // ---------------------------------------------------------------------------------------
+// M tiles of one expert visited together per N tile (see pick_tile).
+#ifndef MOE_TILE_MGROUP
+#define MOE_TILE_MGROUP 4
+#endif
+
 // bf16 tile configurations (BM, BN, BK, WM, WN, A ring depth, B ring depth). GEMM1's BN counts gate + up rows
 // (BN / 2 act columns).
 #ifndef MOE_BF_UP_CFG
@@ -970,6 +1009,8 @@ hipError_t launch_grouped_gemm(int kind, int dtype, const Segment* segs, int nse
     ga.N = N;
     ga.K = K;
     ga.ntn = N / bn;
+    ga.bm = bm;
+    ga.mgroup = MOE_TILE_MGROUP;
     size_t mtiles = max_mtiles(max_rows_total, groups_total, bm);
     size_t nblocks = mtiles * ga.ntn;
     nblocks = (nblocks + 7) / 8 * 8;

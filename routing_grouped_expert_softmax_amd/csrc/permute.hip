@@ -5,14 +5,16 @@
 //
 //   1. count:  per chunk of kPermChunk assignments, an LDS histogram over experts.
 //   2. scan:   per expert, an exclusive scan over chunks (chunk bases) and the totals;
-//              offsets = exclusive scan of the totals; chunk bases += offsets.
+//              offsets = exclusive scan of the totals.
 //   3. rank:   one wavefront per chunk walks its assignments in order, 64 at a time; lanes
 //              with the same expert are found with log2(E) ballots, so a row is
-//              chunk base + running count + rank among equal lanes: a stable, atomic-free
-//              counting sort (rows of an expert in ascending token order).
-//   4. copy:   one wavefront per token reads the x row once and writes it to its k rows
-//              (16-byte accesses); in e4m3 mode the row is quantised per 1 x 128 block in
-//              registers first and the codes and scales are written instead.
+//              offset + chunk base + running count + rank among equal lanes: a stable,
+//              atomic-free counting sort (rows of an expert in ascending token order).
+//   4. copy:   row-major x_perm: one wavefront per token reads the x row once and writes it
+//              to its k rows (16-byte accesses); in e4m3 mode the row is quantised per
+//              1 x 128 block in registers first and the codes and scales are written instead.
+//              K-blocked x_perm: a gather by destination rows (perm_gather_kblock_kernel),
+//              after a token-order e4m3 quantisation in e4m3 mode.
 #include "common.h"
 #include "kernels.h"
 
@@ -38,19 +40,18 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t* __restrict__ c
                                                          int nchunk, int E, int A,
                                                          int32_t* __restrict__ counts,
                                                          int32_t* __restrict__ offsets) {
-    __shared__ int32_t tot[1024];
     __shared__ int32_t wsum[16];
     const int e = threadIdx.x;
     int run = 0;
     if (e < E) {
-        // batches of 16 independent loads, then the running sum over them
-        for (int c0 = 0; c0 < nchunk; c0 += 16) {
-            int v[16];
+        // batches of 32 independent loads, then the running sum over them
+        for (int c0 = 0; c0 < nchunk; c0 += 32) {
+            int v[32];
 #pragma unroll
-            for (int u = 0; u < 16; ++u)
+            for (int u = 0; u < 32; ++u)
                 v[u] = c0 + u < nchunk ? chunk_counts[(size_t)(c0 + u) * E + e] : 0;
 #pragma unroll
-            for (int u = 0; u < 16; ++u) {
+            for (int u = 0; u < 32; ++u) {
                 if (c0 + u < nchunk) chunk_counts[(size_t)(c0 + u) * E + e] = run;
                 run += v[u];
             }
@@ -70,14 +71,8 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t* __restrict__ c
     int before = 0;
     for (int w = 0; w < wave; ++w) before += wsum[w];
     int excl = before + v - run;
-    tot[e] = excl;
     if (e < E) offsets[e] = excl;
     if (e == 0) offsets[E] = A;
-    __syncthreads();
-    if (e < E) {
-        const int base = tot[e];
-        for (int c = 0; c < nchunk; ++c) chunk_counts[(size_t)c * E + e] += base;
-    }
 }
 
 // One wavefront per chunk.
@@ -85,12 +80,14 @@ __global__ __launch_bounds__(64) void perm_rank_kernel(const int32_t* __restrict
                                                        const float* __restrict__ gate, int A,
                                                        int E, int k, int nbits,
                                                        const int32_t* __restrict__ chunk_base,
+                                                       const int32_t* __restrict__ offsets,
                                                        int32_t* __restrict__ pos,
                                                        int32_t* __restrict__ src,
                                                        float* __restrict__ gate_perm) {
     extern __shared__ int32_t running[];
     const int lane = threadIdx.x;
-    for (int e = lane; e < E; e += kWave) running[e] = chunk_base[(size_t)blockIdx.x * E + e];
+    for (int e = lane; e < E; e += kWave)
+        running[e] = offsets[e] + chunk_base[(size_t)blockIdx.x * E + e];
     __syncthreads();
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     const int a0 = blockIdx.x * kPermChunk;
@@ -208,7 +205,13 @@ __global__ __launch_bounds__(256) void perm_quant_copy_kernel(
 // r0 + l / 4 from the row of its token src[r], so every store instruction writes one
 // contiguous kilobyte of x_perm. Row bytes: H * 2 (bf16) or H (e4m3 codes, with their
 // 1 x 128 scales gathered alongside).
-constexpr int kGatherSlices = 16;
+#ifndef MOE_GATHER_SLICES
+#define MOE_GATHER_SLICES 8
+#endif
+#ifndef MOE_GATHER_NT
+#define MOE_GATHER_NT 1
+#endif
+constexpr int kGatherSlices = MOE_GATHER_SLICES;
 __global__ __launch_bounds__(256) void perm_gather_kblock_kernel(
     const uint8_t* __restrict__ xin, const int32_t* __restrict__ src, int A, int row_bytes,
     uint8_t* __restrict__ x_perm, const float* __restrict__ in_scales, int nsc,
@@ -227,9 +230,26 @@ __global__ __launch_bounds__(256) void perm_gather_kblock_kernel(
     uint8_t* out = x_perm + (size_t)r * 64 + (lane % 4) * 16;
     const int j0 = sg * kGatherSlices;
     const int j1 = j0 + kGatherSlices < slices ? j0 + kGatherSlices : slices;
-#pragma unroll 4
-    for (int j = j0; j < j1; ++j)
-        *(uint4*)(out + (size_t)j * A * 64) = *(const uint4*)(in + (size_t)j * 64);
+    if (j1 - j0 == kGatherSlices) {
+        // whole group: every load in flight before the first store
+        uint4 v[kGatherSlices];
+#pragma unroll
+        for (int j = 0; j < kGatherSlices; ++j)
+            v[j] = *(const uint4*)(in + (size_t)(j0 + j) * 64);
+#pragma unroll
+        for (int j = 0; j < kGatherSlices; ++j) {
+            uint4* o = (uint4*)(out + (size_t)(j0 + j) * A * 64);
+#if MOE_GATHER_NT
+            const i32x4_t q = {(int)v[j].x, (int)v[j].y, (int)v[j].z, (int)v[j].w};
+            __builtin_nontemporal_store(q, (i32x4_t*)o);
+#else
+            *o = v[j];
+#endif
+        }
+    } else {
+        for (int j = j0; j < j1; ++j)
+            *(uint4*)(out + (size_t)j * A * 64) = *(const uint4*)(in + (size_t)j * 64);
+    }
     if (out_scales && sg == 0 && lane % 4 == 0)
         for (int b = 0; b < nsc; ++b)
             out_scales[(size_t)r * nsc + b] = in_scales[(size_t)t * nsc + b];
@@ -256,8 +276,8 @@ hipError_t launch_permute(int mode, int kblock, const void* x, const int32_t* to
     perm_count_kernel<<<nchunk, 256, E * sizeof(int32_t), s>>>(topk_idx, A, E, chunk_counts);
     perm_scan_kernel<<<1, 1024, 0, s>>>(chunk_counts, nchunk, E, A, counts, offsets);
     perm_rank_kernel<<<nchunk, 64, E * sizeof(int32_t), s>>>(topk_idx, topk_gate, A, E, k,
-                                                             nbits, chunk_counts, pos, src,
-                                                             gate_perm);
+                                                             nbits, chunk_counts, offsets, pos,
+                                                             src, gate_perm);
     const int blocks = (T + 3) / 4;
     auto gather = [&](const void* in, int row_bytes, const float* in_sc, float* out_sc) {
         const int64_t waves = (int64_t)((A + 15) / 16) *
