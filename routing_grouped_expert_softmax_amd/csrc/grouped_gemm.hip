@@ -8,10 +8,13 @@
 //  * one launch covers every (M tile, N tile) of every expert (and of the shared expert);
 //    workgroups past the live tile count exit at once;
 //  * workgroups are remapped so that each XCD (the hardware deals workgroups round-robin
-//    over 8 XCDs) works through one contiguous run of tiles, N fastest: the N tiles of one
-//    M tile share its activation rows in that XCD's L2;
-//  * bf16 tiles go global -> registers -> LDS (double buffered, padded rows) and into
-//    v_mfma_f32_32x32x16_bf16 with fp32 accumulation;
+//    over 8 XCDs) works through one contiguous run of tiles; within an expert the M tiles
+//    that share a weight tile are neighbours and the N tiles of a band share its
+//    activation rows in that XCD's L2 (pick_tile);
+//  * bf16 tiles go global -> LDS by direct DMA (two-slot rings, XOR-swizzled 16-byte
+//    chunks) and into v_mfma_f32_32x32x16_bf16 with fp32 accumulation; e4m3 tiles into
+//    the block-scaled v_mfma_scale_f32_32x32x64_f8f6f4, with the fp32 block scales applied
+//    per 128-deep K block;
 //  * GEMM1 loads the gate rows [n0, n0+BN/2) and the matching up rows [F+n0, ...) of W13
 //    into one B tile, so a lane holds Z_gate and Z_up of the same (row, column) and the
 //    epilogue writes act = g * silu(Z_gate) * Z_up directly: the gate is folded into the
@@ -152,12 +155,12 @@ MOE_DEVICE bool pick_tile(const GemmArgs& ga, int& mt, int& nt) {
 // ---------------------------------------------------------------------------------------
 // bf16 MFMA kernel
 //
-// LDS holds STAGES stages of [BM A rows | BN B rows] x BK bf16 (64 or 128 bytes per row).
-// Tiles are filled by direct global -> LDS loads (global_load_lds_dwordx4: no staging
-// registers); one wave instruction fills 1 KB = 1024 / (2 BK) rows. Within a row the
-// 16-byte chunks are XOR-swizzled (physical chunk = logical chunk ^ swz(row)) so that the
-// 32 rows one MFMA operand read touches spread over the LDS banks. The prefetch distance is
-// STAGES - 1 K steps.
+// LDS holds a ring of SA slots of BM A rows and a ring of SB slots of BN B rows, each row
+// BK bf16 (64 or 128 bytes). Tiles are filled by direct global -> LDS loads
+// (global_load_lds_dwordx4: no staging registers); one wave instruction fills 1 KB =
+// 1024 / (2 BK) rows. Within a row the 16-byte chunks are XOR-swizzled (physical chunk =
+// logical chunk ^ swz(row)) so that the 32 rows one MFMA operand read touches spread over
+// the LDS banks. The prefetch distance is SA - 1 K steps for A and SB - 1 for B.
 //
 // Ragged tails: a wave skips the loads and MFMAs of its 32-row sub-tiles that lie wholly
 // past the expert's last row, so a tile with few live rows costs few MFMA cycles.
