@@ -264,6 +264,10 @@ int moe_router_logits(const moe_config* cfg, const void* x, const void* w_router
     int st = check_cfg(cfg);
     if (st) return st;
     if (!x || !w_router || !logits) return MOE_ERR_INVALID_ARG;
+    // bf16: the MFMA router GEMM without a K split (no partial-sum space here)
+    if (cfg->act_dtype == MOE_BF16 && moe::router_gemm_ksplit(cfg->T, cfg->H, cfg->E, 0) == 1)
+        return hip_status(moe::launch_router_gemm(x, w_router, cfg->T, cfg->H, cfg->E, 1,
+                                                  nullptr, logits, stream));
     return hip_status(moe::launch_router_logits(cfg->act_dtype, x, w_router, cfg->T, cfg->H,
                                                 cfg->E, logits, stream));
 }
@@ -436,8 +440,18 @@ int moe_layer_forward(const moe_config* cfg, const void* x, const void* w_router
     hipError_t e = stage_mark(0, stream);
     const float* lg = logits_in;
     if (e == hipSuccess && !lg) {
-        e = moe::launch_router_logits(cfg->act_dtype, x, w_router, cfg->T, cfg->H, cfg->E,
-                                      logits, stream);
+        // bf16: split-K MFMA GEMM whose partial sums borrow the y_perm region (unused until
+        // the down projection)
+        const size_t yp_bytes = (size_t)cfg->T * cfg->k * cfg->H * elem_bytes(cfg->act_dtype);
+        const int ks = cfg->act_dtype == MOE_BF16
+                           ? moe::router_gemm_ksplit(cfg->T, cfg->H, cfg->E, yp_bytes)
+                           : 0;
+        if (ks > 0)
+            e = moe::launch_router_gemm(x, w_router, cfg->T, cfg->H, cfg->E, ks,
+                                        (float*)L.y_perm, logits, stream);
+        else
+            e = moe::launch_router_logits(cfg->act_dtype, x, w_router, cfg->T, cfg->H,
+                                          cfg->E, logits, stream);
         lg = logits;
     }
     if (e == hipSuccess) e = stage_mark(1, stream);

@@ -954,7 +954,159 @@ size_t max_mtiles(int max_rows_total, int groups_total, int bm) {
     return (size_t)(max_rows_total + bm - 1) / bm + (size_t)groups_total;
 }
 
+// ---------------------------------------------------------------------------------------
+// Router scores as a split-K GEMM: logits[t, e] = sum_h x[t, h] w[e, h] (bf16 operands, fp32
+// accumulation). One workgroup per (256 tokens, 256 experts, K range); the K ranges are dealt
+// round-robin over the XCDs (block b runs on XCD b % 8), so with 8 ranges each XCD streams one
+// eighth of the router weight, which stays in its L2, while the tokens' rows are read once.
+// Each range writes an fp32 partial tile; the partials are then summed in range order
+// (deterministic). Same DMA rings and MFMA loop as the expert GEMMs.
+// ---------------------------------------------------------------------------------------
+using RouterCfg = BfCfg<1, 256, 256, 64, 2, 4, 2, 2>;
+
+struct RouterArgs {
+    const uint8_t* x;   // [T, H] bf16
+    const uint8_t* w;   // [E, H] bf16
+    float* part;        // [ksplit][T][E]
+    int T, H, E, ksplit, ntn;
+};
+
+__global__ __launch_bounds__(RouterCfg::kThreads) void router_gemm_kernel(RouterArgs ra) {
+    using C = RouterCfg;
+    extern __shared__ __align__(16) uint8_t lds[];
+    const int b = blockIdx.x;
+    const int ks = b % ra.ksplit, rest = b / ra.ksplit;
+    const int nt = rest % ra.ntn, mt = rest / ra.ntn;
+    const int m0 = mt * 256, n0 = nt * 256;
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int wm = wave / 4, wn = wave % 4;
+    const int klen = ra.H / ra.ksplit;                       // elements of this K range
+    const size_t row_bytes = (size_t)ra.H * 2;
+    const size_t kofs = (size_t)ks * klen * 2;
+
+    const uint8_t* srcA[C::kDmaA];
+    const uint8_t* srcB[C::kDmaB];
+#pragma unroll
+    for (int q = 0; q < C::kDmaA; ++q) {
+        const int r = C::kRowsPerDma * (wave + q * C::kWaves) + lane / C::kCpr;
+        const int c = (lane % C::kCpr) ^ chunk_swz<C::kCpr>(r);
+        const int t = m0 + r < ra.T ? m0 + r : ra.T - 1;
+        srcA[q] = ra.x + (size_t)t * row_bytes + kofs + c * 16;
+    }
+#pragma unroll
+    for (int q = 0; q < C::kDmaB; ++q) {
+        const int r = C::kRowsPerDma * (wave + q * C::kWaves) + lane / C::kCpr;
+        const int c = (lane % C::kCpr) ^ chunk_swz<C::kCpr>(r);
+        const int e = n0 + r < ra.E ? n0 + r : ra.E - 1;
+        srcB[q] = ra.w + (size_t)e * row_bytes + kofs + c * 16;
+    }
+    auto issue_a = [&](int kstep, int slot) {
+        MOE_LDS uint8_t* base = (MOE_LDS uint8_t*)lds + slot * C::kASlot;
+#pragma unroll
+        for (int q = 0; q < C::kDmaA; ++q)
+            __builtin_amdgcn_global_load_lds((const void*)(srcA[q] + (size_t)kstep * 128),
+                                             (MOE_LDS void*)(base + (wave + q * C::kWaves) * 1024),
+                                             16, 0, 0);
+    };
+    auto issue_b = [&](int kstep, int slot) {
+        MOE_LDS uint8_t* base = (MOE_LDS uint8_t*)lds + C::kBRing + slot * C::kBSlot;
+#pragma unroll
+        for (int q = 0; q < C::kDmaB; ++q)
+            __builtin_amdgcn_global_load_lds((const void*)(srcB[q] + (size_t)kstep * 128),
+                                             (MOE_LDS void*)(base + (wave + q * C::kWaves) * 1024),
+                                             16, 0, 0);
+    };
+    int a_off[C::kTM], b_off[C::kTN];
+#pragma unroll
+    for (int i = 0; i < C::kTM; ++i) a_off[i] = (C::sub_row(wm, i) + lane % 32) * C::kRowBytes;
+#pragma unroll
+    for (int j = 0; j < C::kTN; ++j) b_off[j] = (wn * 64 + j * 32 + lane % 32) * C::kRowBytes;
+    int chunk_off[C::kSub];
+#pragma unroll
+    for (int s = 0; s < C::kSub; ++s)
+        chunk_off[s] = ((2 * s + lane / 32) ^ chunk_swz<C::kCpr>(lane % 32)) * 16;
+    f32x16_t acc[C::kTM][C::kTN];
+#pragma unroll
+    for (int i = 0; i < C::kTM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::kTN; ++j) acc[i][j] = f32x16_t{};
+    bf16_kloop<C, C::kTM>(klen / 64, lds, issue_a, issue_b, a_off, b_off, chunk_off, acc);
+
+    // 32x32 accumulator: element r of lane l is row (r/4)*8 + (l/32)*4 + r%4, column l%32
+    float* out = ra.part + (size_t)ks * ra.T * ra.E;
+#pragma unroll
+    for (int i = 0; i < C::kTM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::kTN; ++j) {
+            const int e = n0 + wn * 64 + j * 32 + lane % 32;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int t = m0 + C::sub_row(wm, i) + (r / 4) * 8 + (lane / 32) * 4 + r % 4;
+                if (t < ra.T && e < ra.E) out[(size_t)t * ra.E + e] = acc[i][j][r];
+            }
+        }
+}
+
+// logits = sum over the K ranges of the partial tiles, in range order.
+__global__ __launch_bounds__(256) void router_reduce_kernel(const float* __restrict__ part,
+                                                            int64_t n, int ksplit,
+                                                            float* __restrict__ logits) {
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i + 4 <= n) {
+        float4 a = *(const float4*)(part + i);
+        for (int k = 1; k < ksplit; ++k) {
+            const float4 v = *(const float4*)(part + (size_t)k * n + i);
+            a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
+        }
+        *(float4*)(logits + i) = a;
+    } else {
+        for (int64_t j = i; j < n; ++j) {
+            float a = part[j];
+            for (int k = 1; k < ksplit; ++k) a += part[(size_t)k * n + j];
+            logits[j] = a;
+        }
+    }
+}
+
 }  // namespace
+
+int router_gemm_ksplit(int T, int H, int E, size_t scratch_bytes) {
+    if (E < 64 || E % 4 || H % 64) return 0;
+    const int steps = H / 64;
+    for (int ks = 8; ks >= 2; ks /= 2)
+        if (steps % ks == 0 && (size_t)ks * T * E * sizeof(float) <= scratch_bytes) return ks;
+    return 1;
+}
+
+hipError_t launch_router_gemm(const void* x, const void* w_router, int T, int H, int E,
+                              int ksplit, float* part, float* logits, hipStream_t s) {
+    using C = RouterCfg;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)router_gemm_kernel,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)C::kLdsLoop);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    RouterArgs ra;
+    ra.x = (const uint8_t*)x;
+    ra.w = (const uint8_t*)w_router;
+    ra.part = ksplit > 1 ? part : logits;
+    ra.T = T;
+    ra.H = H;
+    ra.E = E;
+    ra.ksplit = ksplit;
+    ra.ntn = (E + 255) / 256;
+    const unsigned blocks = (unsigned)((T + 255) / 256) * ra.ntn * ksplit;
+    router_gemm_kernel<<<blocks, C::kThreads, C::kLdsLoop, s>>>(ra);
+    if (ksplit > 1) {
+        const int64_t n = (int64_t)T * E;
+        router_reduce_kernel<<<(unsigned)((n / 4 + 255) / 256 + 1), 256, 0, s>>>(part, n,
+                                                                               ksplit, logits);
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_schedule(const int32_t* offsets, int groups, int bm, void* ws, hipStream_t s) {
     SchedArgs sa = {};

@@ -13,6 +13,14 @@ namespace moe {
 hipError_t launch_router_logits(int act_dtype, const void* x, const void* w_router, int T,
                                 int H, int E, float* logits, hipStream_t s);
 
+// bf16 router scores as a split-K MFMA GEMM (grouped_gemm.hip). router_gemm_ksplit gives the
+// number of K ranges to use with scratch_bytes of partial-sum space (1: no partials, the
+// kernel writes logits directly; 0: the shape is not supported, use launch_router_logits).
+// part holds ksplit * T * E floats when ksplit > 1.
+int router_gemm_ksplit(int T, int H, int E, size_t scratch_bytes);
+hipError_t launch_router_gemm(const void* x, const void* w_router, int T, int H, int E,
+                              int ksplit, float* part, float* logits, hipStream_t s);
+
 hipError_t launch_route(int router, const float* logits, const float* logit_bias,
                         const float* sel_bias, int T, int E, int k, int n_groups,
                         int topk_groups, float route_scale, int32_t* topk_idx,
