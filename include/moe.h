@@ -202,7 +202,9 @@ int moe_unpermute_combine(const moe_config* cfg, const void* y_perm, const int32
 /* The whole layer: router GEMM (skipped when logits_in != NULL), route, permute, grouped
  * GEMM with the shared expert, combine. x [T, H] and w_router [E, H] in act_dtype; weights
  * as in moe_grouped_gemm_swiglu (in cfg->w_layout); y [T, H] in act_dtype. The expert-grouped
- * activations live in the workspace, K-blocked for bf16/e4m3 whatever cfg->a_layout says.
+ * activations live in the workspace, row-major whatever cfg->a_layout says (cfg->a_layout
+ * applies to the stand-alone calls only). For bf16, the router's split-K partial sums use the
+ * workspace's y_perm region before the down projection writes it.
  * Optional outputs (NULL = skip): logits_out [T, E], topk_idx_out [T, k],
  * topk_gate_out [T, k], counts_out [E]. */
 int moe_layer_forward(const moe_config* cfg, const void* x, const void* w_router,

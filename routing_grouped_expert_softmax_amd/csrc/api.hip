@@ -6,6 +6,12 @@
 #include "../../include/moe.h"
 #include "kernels.h"
 
+// Layout of the layer's internal activations (x_perm, act): row-major (0) measured as fast
+// in the grouped GEMMs as K-blocked (1) and makes the permute a one-read, k-write scatter.
+#ifndef MOE_LAYER_ACT_KBLOCK
+#define MOE_LAYER_ACT_KBLOCK 0
+#endif
+
 namespace {
 
 using moe::Segment;
@@ -461,9 +467,8 @@ int moe_layer_forward(const moe_config* cfg, const void* x, const void* w_router
     if (e == hipSuccess) e = stage_mark(2, stream);
     if (e != hipSuccess) return MOE_ERR_HIP;
     const int mode = fp8 ? 2 : (cfg->act_dtype == MOE_F32 ? 0 : 1);
-    // internal activations (x_perm, act, the shared expert's act) are K-blocked: every
-    // 128-byte K slice of consecutive rows is contiguous, so each tile load is one run
-    const int a_kb = cfg->act_dtype == MOE_F32 ? 0 : 1;
+    // layout of the internal activations (x_perm, act, the shared expert's act)
+    const int a_kb = cfg->act_dtype == MOE_F32 ? 0 : MOE_LAYER_ACT_KBLOCK;
     e = moe::launch_permute(mode, a_kb, x, idx, gate, cfg->T, cfg->H, cfg->E, cfg->k, counts,
                             L.offsets, L.pos, L.src, L.gate_perm, L.x_perm, L.x_perm_scales,
                             L.x_q, L.x_q_scales, L.scratch, stream);

@@ -18,6 +18,13 @@
 #include "common.h"
 #include "kernels.h"
 
+#ifndef MOE_GATHER_SLICES
+#define MOE_GATHER_SLICES 8
+#endif
+#ifndef MOE_GATHER_NT
+#define MOE_GATHER_NT 1
+#endif
+
 namespace moe {
 namespace {
 
@@ -122,6 +129,7 @@ __global__ __launch_bounds__(256) void perm_copy_kernel(const uint4* __restrict_
                                                         const int32_t* __restrict__ pos,
                                                         int T, int row_chunks, int k, int kblock,
                                                         uint4* __restrict__ x_perm) {
+    constexpr int U = 8;            // 16-byte chunks per lane loaded before the stores
     const size_t A = (size_t)T * k;
     const int lane = threadIdx.x % kWave;
     const int t = blockIdx.x * 4 + threadIdx.x / kWave;
@@ -129,15 +137,28 @@ __global__ __launch_bounds__(256) void perm_copy_kernel(const uint4* __restrict_
     int my_pos = lane < k ? pos[(size_t)t * k + lane] : 0;
     const uint4* xr = x + (size_t)t * row_chunks;
     // every lane runs every iteration so that the shuffles read active lanes only
-    for (int c0 = 0; c0 < row_chunks; c0 += kWave) {
-        const int c = c0 + lane;
-        const bool ok = c < row_chunks;
-        uint4 v = ok ? xr[c] : make_uint4(0, 0, 0, 0);
+    for (int c0 = 0; c0 < row_chunks; c0 += U * kWave) {
+        uint4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = c0 + u * kWave + lane;
+            v[u] = c < row_chunks ? xr[c] : make_uint4(0, 0, 0, 0);
+        }
         for (int j = 0; j < k; ++j) {
-            int r = __shfl(my_pos, j);
-            const size_t o = kblock ? ((size_t)(c / 4) * A + r) * 4 + c % 4
-                                    : (size_t)r * row_chunks + c;
-            if (ok) x_perm[o] = v;
+            const int r = __shfl(my_pos, j);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int c = c0 + u * kWave + lane;
+                if (c >= row_chunks) continue;
+                const size_t o = kblock ? ((size_t)(c / 4) * A + r) * 4 + c % 4
+                                        : (size_t)r * row_chunks + c;
+#if MOE_GATHER_NT
+                const i32x4_t q = {(int)v[u].x, (int)v[u].y, (int)v[u].z, (int)v[u].w};
+                __builtin_nontemporal_store(q, (i32x4_t*)(x_perm + o));
+#else
+                x_perm[o] = v[u];
+#endif
+            }
         }
     }
 }
@@ -205,12 +226,6 @@ __global__ __launch_bounds__(256) void perm_quant_copy_kernel(
 // r0 + l / 4 from the row of its token src[r], so every store instruction writes one
 // contiguous kilobyte of x_perm. Row bytes: H * 2 (bf16) or H (e4m3 codes, with their
 // 1 x 128 scales gathered alongside).
-#ifndef MOE_GATHER_SLICES
-#define MOE_GATHER_SLICES 8
-#endif
-#ifndef MOE_GATHER_NT
-#define MOE_GATHER_NT 1
-#endif
 constexpr int kGatherSlices = MOE_GATHER_SLICES;
 __global__ __launch_bounds__(256) void perm_gather_kblock_kernel(
     const uint8_t* __restrict__ xin, const int32_t* __restrict__ src, int A, int row_bytes,
