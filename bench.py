@@ -31,7 +31,7 @@ PEAK_MFMA = {"bf16": 2.5e15, "fp32": 157.3e12, "e4m3": 5.0e15}   # dense, FLOP/s
 # a plain copy of known size (see the file); used only while the kernel sources are unchanged
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_up_dsv3_bf16_traffic.txt")
 TRAFFIC_SOURCES = [os.path.join(ROOT, "routing_grouped_expert_softmax_amd", "csrc", f)
-                   for f in ("grouped_gemm.hip", "common.h", "kernels.h")]
+                   for f in ("grouped_gemm.hip", "common.h", "kernels.h", "api.hip")]
 
 
 def log(*a):
