@@ -24,12 +24,33 @@
 namespace moe {
 namespace {
 
-constexpr int kBM = 128, kBN = 128, kBK = 32, kStages = 3;
-constexpr int kWaves = 4, kThreads = kWaves * 64;          // 2 x 2 waves of 64 x 64
-constexpr int kOpBytes = 8192;                             // one operand tile per stage
-constexpr int kStageBytes = 2 * kOpBytes;
-constexpr int kTN = 2, kTM = 2;                            // 32 x 32 sub-tiles per wave
+#ifndef MOE_BWD_LARGE
+#define MOE_BWD_LARGE 1
+#endif
+
+
+constexpr int kBK = 32, kStages = 3;
 constexpr int kZeroBytes = 1024;
+
+// Tile configuration: BM x BN output tile, WM x WN waves, each wave (BM / WM) x (BN / WN) in
+// 32 x 32 MFMA sub-tiles; K step 32 (64-byte operand rows), 3-stage LDS ring.
+template <int BM_, int BN_, int WM_, int WN_>
+struct BwdCfg {
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+    static constexpr int kWaves = WM * WN, kThreads = kWaves * 64;
+    static constexpr int kTM = BM / WM / 32, kTN = BN / WN / 32;
+    static constexpr int kABytes = BM * kBK * 2, kBBytes = BN * kBK * 2;
+    static constexpr int kStageBytes = kABytes + kBBytes;
+    static constexpr int kLdsLoop = kStages * kStageBytes;
+    static constexpr int kLdsEp = BM * (BN + 8) * 2;          // bf16 epilogue staging
+    static constexpr int kLds = kLdsLoop > kLdsEp ? kLdsLoop : kLdsEp;
+    static_assert(kLds <= 160 * 1024, "LDS");
+    static constexpr int kDmaA = kABytes / 1024 / kWaves, kDmaB = kBBytes / 1024 / kWaves;
+    static_assert(kDmaA * 1024 * kWaves == kABytes && kDmaB * 1024 * kWaves == kBBytes, "DMA");
+    static_assert(kTM >= 1 && kTN >= 1, "waves");
+};
+using BwdSmall = BwdCfg<128, 128, 2, 2>;      // 4 waves of 64 x 64
+using BwdLarge = BwdCfg<256, 256, 2, 4>;      // 8 waves of 128 x 64
 
 enum { OPK = 0, OPT = 1 };        // operand rows hold K (contiguous) / hold M or N
 
@@ -73,20 +94,15 @@ MOE_DEVICE bf16x8_t tr_frag(const uint8_t* lo, const uint8_t* hi) {
 
 // RAGGED_K = 0: tiles of ragged M from the schedule, K fixed. RAGGED_K = 1: tiles of every
 // group's [M, N], K = the group's rows. EPI 0: bf16 store; EPI 1: SwiGLU backward.
-template <int AO, int BO, int RAGGED_K, int EPI>
-__global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(BwdArgs ba) {
-    extern __shared__ __align__(16) uint8_t lds[];
+template <class CF, int AO, int BO, int RAGGED_K, int EPI>
+MOE_DEVICE void bwd_tile(const BwdArgs& ba, int L, uint8_t* lds) {
+    constexpr int kBM = CF::BM, kBN = CF::BN, kTM = CF::kTM, kTN = CF::kTN;
+    constexpr int kWaves = CF::kWaves, kOpBytes = CF::kABytes;
     const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
-    const int wm = wave / 2, wn = wave % 2;
+    const int wm = wave / CF::WN, wn = wave % CF::WN;
     // ---- tile
     int g, m0, Mg, rbase, mt, nt;
     {
-        const int b = blockIdx.x, xcd = b % 8, i = b / 8;
-        const int total = RAGGED_K ? ba.groups * ba.ntm * ba.ntn : *ba.total * ba.ntn;
-        const int per = (total + 7) / 8;
-        if (i >= per) return;
-        const int L = xcd * per + i;
-        if (L >= total) return;
         if (RAGGED_K) {
             g = L / (ba.ntm * ba.ntn);
             const int rem = L % (ba.ntm * ba.ntn);
@@ -108,12 +124,14 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(BwdArgs ba) {
     const int nk = RAGGED_K ? (Mg + kBK - 1) / kBK : ba.K / kBK;
     const int live = RAGGED_K ? kBM : (Mg - m0 < kBM ? Mg - m0 : kBM);
 
-    // ---- DMA sources. Operand tile = 8 instructions of 1 KB; wave w issues q = w, w + 4.
-    // OPK tile [128 rows][32 k]: instruction q fills rows 16 q + lane / 4.
-    // OPT tile [32 k][128 cols]: instruction q fills k rows 4 q + lane / 16.
-    const uint8_t* srcA[2];
-    const uint8_t* srcB[2];
-    int ka[2], kb[2];               // OPT: the k row each instruction fills (ragged K)
+    // ---- DMA sources. An operand tile is made of 1 KB instructions; wave w issues
+    // q = w + kWaves u.
+    // OPK tile [rows][32 k]: instruction q fills rows 16 q + lane / 4.
+    // OPT tile [32 k][C cols] (C = BM for A, BN for B; C / 8 16-byte chunks per k row):
+    // instruction q fills k rows (512 / C) q + lane / (C / 8).
+    const uint8_t* srcA[CF::kDmaA];
+    const uint8_t* srcB[CF::kDmaB];
+    int ka[CF::kDmaA], kb[CF::kDmaB];   // OPT: the k row each instruction fills (ragged K)
     auto op_src = [&](const Operand& op, int o, bool is_a, int q, const uint8_t*& src, int& krow) {
         if (o == OPK) {
             const int r = 16 * q + lane / 4;
@@ -128,8 +146,9 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(BwdArgs ba) {
             src = (const uint8_t*)(op.p + (size_t)g * op.gstride + row * op.ld) + c * 16;
             krow = 0;
         } else {
-            const int kr = 4 * q + lane / 16;
-            const int c = (lane % 16) ^ swz_t(kr);
+            const int cpr = (is_a ? kBM : kBN) / 8;
+            const int kr = (64 / cpr) * q + lane / cpr;
+            const int c = (lane % cpr) ^ swz_t(kr);
             const size_t col = (size_t)(is_a ? mt * kBM : nt * kBN) + c * 8;
             if (RAGGED_K)
                 src = (const uint8_t*)(op.p + (size_t)rbase * op.ld + col);   // + k * ld
@@ -139,33 +158,34 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(BwdArgs ba) {
         }
     };
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        op_src(ba.a, AO, true, wave + 4 * u, srcA[u], ka[u]);
-        op_src(ba.b, BO, false, wave + 4 * u, srcB[u], kb[u]);
-    }
-    auto issue = [&](int kstep, int stage) {
-        MOE_LDS uint8_t* base = (MOE_LDS uint8_t*)lds + stage * kStageBytes;
+    for (int u = 0; u < CF::kDmaA; ++u) op_src(ba.a, AO, true, wave + kWaves * u, srcA[u], ka[u]);
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int q = wave + 4 * u;
-            // A
+    for (int u = 0; u < CF::kDmaB; ++u) op_src(ba.b, BO, false, wave + kWaves * u, srcB[u], kb[u]);
+    auto issue = [&](int kstep, int stage) {
+        MOE_LDS uint8_t* base = (MOE_LDS uint8_t*)lds + stage * CF::kStageBytes;
+#pragma unroll
+        for (int u = 0; u < CF::kDmaA; ++u) {
+            const int q = wave + kWaves * u;
             const uint8_t* sa;
             if (AO == OPK) {
                 sa = srcA[u] + (size_t)kstep * kBK * 2;
             } else {
                 const int kk = kstep * kBK + ka[u];
-                sa = (RAGGED_K && kk >= Mg) ? ba.zero + (lane % 16) * 16
+                sa = (RAGGED_K && kk >= Mg) ? ba.zero + (lane % (kBM / 8)) * 16
                                             : srcA[u] + (size_t)kk * ba.a.ld * 2;
             }
             __builtin_amdgcn_global_load_lds((const void*)sa, (MOE_LDS void*)(base + q * 1024),
                                              16, 0, 0);
-            // B
+        }
+#pragma unroll
+        for (int u = 0; u < CF::kDmaB; ++u) {
+            const int q = wave + kWaves * u;
             const uint8_t* sb;
             if (BO == OPK) {
                 sb = srcB[u] + (size_t)kstep * kBK * 2;
             } else {
                 const int kk = kstep * kBK + kb[u];
-                sb = (RAGGED_K && kk >= Mg) ? ba.zero + (lane % 16) * 16
+                sb = (RAGGED_K && kk >= Mg) ? ba.zero + (lane % (kBN / 8)) * 16
                                             : srcB[u] + (size_t)kk * ba.b.ld * 2;
             }
             __builtin_amdgcn_global_load_lds((const void*)sb,
@@ -180,7 +200,7 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(BwdArgs ba) {
     int offK[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) offK[s] = ((2 * s + lane / 32) ^ chunk_swz<4>(lane % 32)) * 16;
-    auto frag = [&](const uint8_t* tile, int o, int sub_base, int s) -> bf16x8_t {
+    auto frag = [&](const uint8_t* tile, int o, int cols, int sub_base, int s) -> bf16x8_t {
         if (o == OPK) {
             return *(const bf16x8_t*)(tile + (sub_base + lane % 32) * 64 + offK[s]);
         } else {
@@ -188,7 +208,7 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(BwdArgs ba) {
             const int col = sub_base + 16 * (h16 % 2) + 4 * (u16 % 4);
             const int chunk = (col / 8) ^ swz_t(k0);          // k0 and k0 + 4 share swz_t
             const int off = chunk * 16 + (col % 8) * 2;
-            return tr_frag(tile + k0 * 256 + off, tile + (k0 + 4) * 256 + off);
+            return tr_frag(tile + k0 * cols * 2 + off, tile + (k0 + 4) * cols * 2 + off);
         }
     };
 
@@ -197,7 +217,7 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(BwdArgs ba) {
     for (int i = 0; i < kTM; ++i)
 #pragma unroll
         for (int j = 0; j < kTN; ++j) acc[i][j] = f32x16_t{};
-    int nvi = (live - wm * 64 + 31) / 32;
+    int nvi = (live - wm * (kBM / CF::WM) + 31) / 32;
     nvi = nvi < 0 ? 0 : (nvi > kTM ? kTM : nvi);
     nvi = __builtin_amdgcn_readfirstlane(nvi);
 
@@ -207,7 +227,7 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(BwdArgs ba) {
     int stage = 0;
     for (int kt = 0; kt < nk; ++kt) {
         const int later = nk - 1 - kt;
-        if (later >= 1) wait_vm_lgkm0<4>();
+        if (later >= 1) wait_vm_lgkm0<CF::kDmaA + CF::kDmaB>();
         else wait_vm_lgkm0<0>();
         block_sync();
         {
@@ -216,16 +236,18 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(BwdArgs ba) {
             if (sn >= kStages) sn -= kStages;
             if (kn < nk) issue(kn, sn);
         }
-        const uint8_t* ta = lds + stage * kStageBytes;
+        const uint8_t* ta = lds + stage * CF::kStageBytes;
         const uint8_t* tb = ta + kOpBytes;
         if (nvi > 0) {
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
                 bf16x8_t av[kTM], bv[kTN];
 #pragma unroll
-                for (int j = 0; j < kTN; ++j) bv[j] = frag(tb, BO, wn * 64 + j * 32, s);
+                for (int j = 0; j < kTN; ++j)
+                    bv[j] = frag(tb, BO, kBN, wn * (kBN / CF::WN) + j * 32, s);
 #pragma unroll
-                for (int i = 0; i < kTM; ++i) av[i] = frag(ta, AO, wm * 64 + i * 32, s);
+                for (int i = 0; i < kTM; ++i)
+                    av[i] = frag(ta, AO, kBM, wm * (kBM / CF::WM) + i * 32, s);
 #pragma unroll
                 for (int i = 0; i < kTM; ++i)
 #pragma unroll
@@ -240,26 +262,32 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(BwdArgs ba) {
     // ---- epilogue. 32x32 layout: element r of lane l is row (r/4)*8 + (l/32)*4 + r%4,
     // column l % 32.
     if (EPI == 0) {
-        uint16_t* out = ba.out + (RAGGED_K ? (size_t)g * ba.out_gstride : 0);
+        // stage the bf16 tile in LDS ([BM][BN + 8]), then write 16-byte row chunks
+        constexpr int kEpStride = kBN + 8;
+        block_sync();                               // every wave is done with the stages
+        uint16_t* ep = (uint16_t*)lds;
 #pragma unroll
         for (int i = 0; i < kTM; ++i) {
             if (i >= nvi) continue;
 #pragma unroll
             for (int j = 0; j < kTN; ++j) {
-                const int col = nt * kBN + wn * 64 + j * 32 + lane % 32;
+                const int lcol = wn * (kBN / CF::WN) + j * 32 + lane % 32;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int row = wm * 64 + i * 32 + (r / 4) * 8 + (lane / 32) * 4 + r % 4;
-                    size_t orow;
-                    if (RAGGED_K) {
-                        orow = (size_t)mt * kBM + row;
-                    } else {
-                        if (m0 + row >= Mg) continue;
-                        orow = (size_t)rbase + m0 + row;
-                    }
-                    out[orow * ba.out_ld + col] = f32_to_bf16(acc[i][j][r]);
+                    const int row = wm * (kBM / CF::WM) + i * 32 + (r / 4) * 8 + (lane / 32) * 4 + r % 4;
+                    ep[row * kEpStride + lcol] = f32_to_bf16(acc[i][j][r]);
                 }
             }
+        }
+        __syncthreads();
+        uint16_t* out = ba.out + (RAGGED_K ? (size_t)g * ba.out_gstride : 0);
+        constexpr int kChunks = kBN / 8;
+        const int rows = RAGGED_K ? kBM : live;
+        for (int c = threadIdx.x; c < rows * kChunks; c += CF::kThreads) {
+            const int row = c / kChunks, cc = c % kChunks;
+            const uint4 v = *(const uint4*)(ep + row * kEpStride + cc * 8);
+            const size_t orow = RAGGED_K ? (size_t)mt * kBM + row : (size_t)rbase + m0 + row;
+            *(uint4*)(out + orow * ba.out_ld + (size_t)nt * kBN + cc * 8) = v;
         }
         return;
     }
@@ -271,13 +299,13 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(BwdArgs ba) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             dgp[i][r] = 0.0f;
-            const int row = wm * 64 + i * 32 + (r / 4) * 8 + (lane / 32) * 4 + r % 4;
+            const int row = wm * (kBM / CF::WM) + i * 32 + (r / 4) * 8 + (lane / 32) * 4 + r % 4;
             if (i >= nvi || m0 + row >= Mg) continue;
             const size_t grow = (size_t)rbase + m0 + row;
             const float gt = ba.gate ? ba.gate[grow] : 1.0f;
 #pragma unroll
             for (int j = 0; j < kTN; ++j) {
-                const int f = nt * kBN + wn * 64 + j * 32 + lane % 32;
+                const int f = nt * kBN + wn * (kBN / CF::WN) + j * 32 + lane % 32;
                 const float zg = bf16_to_f32(ba.z[grow * 2 * F + f]);
                 const float zu = bf16_to_f32(ba.z[grow * 2 * F + F + f]);
                 const float sg = 1.0f / (1.0f + expf(-zg));
@@ -290,10 +318,10 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(BwdArgs ba) {
                 dgp[i][r] += da * (si * zu);
             }
         }
-    // rows' partial sums: over the 32 lanes of each half (columns), then over the two waves
+    // rows' partial sums: over the 32 lanes of each half (columns), then over the WN waves
     // of a row band (LDS), in a fixed order
     block_sync();
-    float* red = (float*)lds;                          // [2][kBM]
+    float* red = (float*)lds;                          // [WN][kBM]
 #pragma unroll
     for (int i = 0; i < kTM; ++i)
 #pragma unroll
@@ -301,7 +329,7 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(BwdArgs ba) {
             float v = dgp[i][r];
 #pragma unroll
             for (int off = 1; off < 32; off <<= 1) v += __shfl_xor(v, off);
-            const int row = wm * 64 + i * 32 + (r / 4) * 8 + (lane / 32) * 4 + r % 4;
+            const int row = wm * (kBM / CF::WM) + i * 32 + (r / 4) * 8 + (lane / 32) * 4 + r % 4;
             if (lane % 32 == 0) red[wn * kBM + row] = v;
         }
     __syncthreads();
@@ -309,9 +337,26 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(BwdArgs ba) {
         const int row = threadIdx.x;
         if (m0 + row < Mg) {
             const size_t grow = (size_t)rbase + m0 + row;
-            ba.dg_part[grow * ba.ntn + nt] = red[row] + red[kBM + row];
+            float v = red[row];
+#pragma unroll
+            for (int w = 1; w < CF::WN; ++w) v += red[w * kBM + row];
+            ba.dg_part[grow * ba.ntn + nt] = v;
         }
     }
+}
+
+// One tile per workgroup. The hardware deals workgroups round-robin over the 8 XCDs, so
+// workgroup b (on XCD b % 8) takes tile (b % 8) * per + b / 8: each XCD walks one contiguous
+// run of tiles.
+template <class CF, int AO, int BO, int RAGGED_K, int EPI>
+__global__ __launch_bounds__(CF::kThreads) void bwd_gemm_kernel(BwdArgs ba) {
+    extern __shared__ __align__(16) uint8_t lds[];
+    const int xcd = blockIdx.x % 8, i = blockIdx.x / 8;
+    const int total = RAGGED_K ? ba.groups * ba.ntm * ba.ntn : *ba.total * ba.ntn;
+    const int per = (total + 7) / 8;
+    const int L = xcd * per + i;
+    if (i >= per || L >= total) return;
+    bwd_tile<CF, AO, BO, RAGGED_K, EPI>(ba, L, lds);
 }
 
 __global__ __launch_bounds__(256) void dg_reduce_kernel(const float* __restrict__ part, int A,
@@ -328,18 +373,18 @@ __global__ __launch_bounds__(256) void zero_fill_kernel(uint32_t* p, int n) {
     if (i < n) p[i] = 0u;
 }
 
-template <int AO, int BO, int RAGGED_K, int EPI>
+template <class CF, int AO, int BO, int RAGGED_K, int EPI>
 hipError_t run_bwd(const BwdArgs& ba, int nblocks, hipStream_t s) {
     static bool attr_set = false;
-    constexpr int lds_bytes = kStages * kStageBytes;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)bwd_gemm_kernel<AO, BO, RAGGED_K, EPI>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+        hipError_t e = hipFuncSetAttribute(
+            (const void*)bwd_gemm_kernel<CF, AO, BO, RAGGED_K, EPI>,
+            hipFuncAttributeMaxDynamicSharedMemorySize, CF::kLds);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
     if (nblocks > 0)
-        bwd_gemm_kernel<AO, BO, RAGGED_K, EPI><<<nblocks, kThreads, lds_bytes, s>>>(ba);
+        bwd_gemm_kernel<CF, AO, BO, RAGGED_K, EPI><<<nblocks, CF::kThreads, CF::kLds, s>>>(ba);
     return hipGetLastError();
 }
 
@@ -353,36 +398,29 @@ struct BwdWs {
 
 size_t al(size_t v) { return (v + 255) / 256 * 256; }
 
+// sized for the smaller tiles (more M tiles, more dg partials per row)
 BwdWs carve_bwd(void* ws, int A, int E, int F) {
     BwdWs w;
     char* p = (char*)ws;
     size_t off = 0;
     w.sched = p ? p + off : nullptr;
-    off += al(schedule_ws_bytes(A, E, kBM));
+    off += al(schedule_ws_bytes(A, E, BwdSmall::BM));
     w.zero = p ? (uint8_t*)(p + off) : nullptr;
     off += al(kZeroBytes);
     w.dz = p ? (uint16_t*)(p + off) : nullptr;
     off += al((size_t)A * 2 * F * 2);
     w.dg_part = p ? (float*)(p + off) : nullptr;
-    off += al((size_t)A * (F / kBN) * 4);
+    off += al((size_t)A * (F / BwdSmall::BN) * 4);
     w.total = off;
     return w;
 }
 
-}  // namespace
-
-size_t bwd_ws_bytes(int T, int k, int E, int H, int F) {
-    (void)H;
-    return carve_bwd(nullptr, T * k, E, F).total;
-}
-
-hipError_t launch_grouped_gemm_bwd(const void* dy_perm, const void* x_perm, const void* z,
-                                   const void* act, const float* gate_perm,
-                                   const int32_t* offsets, const void* w13, const void* w2,
-                                   int A, int E, int H, int F, void* dx_perm, void* dw13,
-                                   void* dw2, float* dgate_perm, void* ws, hipStream_t s) {
-    BwdWs w = carve_bwd(ws, A, E, F);
-    zero_fill_kernel<<<1, 256, 0, s>>>((uint32_t*)w.zero, kZeroBytes / 4);
+template <class CF>
+hipError_t bwd_all(const BwdWs& w, const void* dy_perm, const void* x_perm, const void* z,
+                   const void* act, const float* gate_perm, const int32_t* offsets,
+                   const void* w13, const void* w2, int A, int E, int H, int F, void* dx_perm,
+                   void* dw13, void* dw2, float* dgate_perm, hipStream_t s) {
+    constexpr int kBM = CF::BM, kBN = CF::BN;
     hipError_t e = launch_schedule(offsets, E, kBM, w.sched, s);
     if (e != hipSuccess) return e;
     const int4* tiles = (const int4*)((char*)w.sched + 256);
@@ -402,7 +440,7 @@ hipError_t launch_grouped_gemm_bwd(const void* dy_perm, const void* x_perm, cons
     d1.N = F; d1.K = H; d1.ntn = F / kBN; d1.groups = E;
     d1.z = (const uint16_t*)z; d1.gate = gate_perm; d1.dz = w.dz; d1.dg_part = w.dg_part;
     d1.F = F; d1.zero = w.zero;
-    e = run_bwd<OPK, OPT, 0, 1>(d1, round8(max_tiles * d1.ntn), s);
+    e = run_bwd<CF, OPK, OPT, 0, 1>(d1, round8(max_tiles * d1.ntn), s);
     if (e != hipSuccess) return e;
     if (dgate_perm) {
         dg_reduce_kernel<<<(A + 255) / 256, 256, 0, s>>>(w.dg_part, A, F / kBN, dgate_perm);
@@ -416,25 +454,47 @@ hipError_t launch_grouped_gemm_bwd(const void* dy_perm, const void* x_perm, cons
     d2.offsets = offsets; d2.tiles = tiles; d2.total = total;
     d2.N = H; d2.K = 2 * F; d2.ntn = H / kBN; d2.groups = E;
     d2.out = (uint16_t*)dx_perm; d2.out_ld = H; d2.zero = w.zero;
-    e = run_bwd<OPK, OPT, 0, 0>(d2, round8(max_tiles * d2.ntn), s);
+    e = run_bwd<CF, OPK, OPT, 0, 0>(d2, round8(max_tiles * d2.ntn), s);
     if (e != hipSuccess) return e;
     // wgrad 2: dW2_e [H, F] = dy_perm[R_e]^T act[R_e]
     BwdArgs w2a = {};
     w2a.a = {DY, (size_t)H, 0};
     w2a.b = {(const uint16_t*)act, (size_t)F, 0};
-    w2a.offsets = offsets; w2a.M = H; w2a.N = F; w2a.ntm = H / kBM; w2a.ntn = F / kBN;
+    w2a.offsets = offsets; w2a.M = H; w2a.N = F; w2a.ntm = H / CF::BM; w2a.ntn = F / CF::BN;
     w2a.groups = E; w2a.out = (uint16_t*)dw2; w2a.out_ld = F; w2a.out_gstride = (size_t)H * F;
     w2a.zero = w.zero;
-    e = run_bwd<OPT, OPT, 1, 0>(w2a, round8((size_t)E * w2a.ntm * w2a.ntn), s);
+    e = run_bwd<CF, OPT, OPT, 1, 0>(w2a, round8((size_t)E * w2a.ntm * w2a.ntn), s);
     if (e != hipSuccess) return e;
     // wgrad 1: dW13_e [2F, H] = dZ[R_e]^T x_perm[R_e]
     BwdArgs w1 = {};
     w1.a = {w.dz, (size_t)2 * F, 0};
     w1.b = {X, (size_t)H, 0};
-    w1.offsets = offsets; w1.M = 2 * F; w1.N = H; w1.ntm = 2 * F / kBM; w1.ntn = H / kBN;
+    w1.offsets = offsets; w1.M = 2 * F; w1.N = H; w1.ntm = 2 * F / CF::BM; w1.ntn = H / CF::BN;
     w1.groups = E; w1.out = (uint16_t*)dw13; w1.out_ld = H; w1.out_gstride = (size_t)2 * F * H;
     w1.zero = w.zero;
-    return run_bwd<OPT, OPT, 1, 0>(w1, round8((size_t)E * w1.ntm * w1.ntn), s);
+    return run_bwd<CF, OPT, OPT, 1, 0>(w1, round8((size_t)E * w1.ntm * w1.ntn), s);
+}
+
+}  // namespace
+
+size_t bwd_ws_bytes(int T, int k, int E, int H, int F) {
+    (void)H;
+    return carve_bwd(nullptr, T * k, E, F).total;
+}
+
+hipError_t launch_grouped_gemm_bwd(const void* dy_perm, const void* x_perm, const void* z,
+                                   const void* act, const float* gate_perm,
+                                   const int32_t* offsets, const void* w13, const void* w2,
+                                   int A, int E, int H, int F, void* dx_perm, void* dw13,
+                                   void* dw2, float* dgate_perm, void* ws, hipStream_t s) {
+    BwdWs w = carve_bwd(ws, A, E, F);
+    zero_fill_kernel<<<1, 256, 0, s>>>((uint32_t*)w.zero, kZeroBytes / 4);
+    // 256 x 256 tiles when every GEMM dimension divides by 256 (F, 2F and H), else 128 x 128
+    if (F % BwdLarge::BN == 0 && H % BwdLarge::BN == 0 && MOE_BWD_LARGE)
+        return bwd_all<BwdLarge>(w, dy_perm, x_perm, z, act, gate_perm, offsets, w13, w2, A, E,
+                                 H, F, dx_perm, dw13, dw2, dgate_perm, s);
+    return bwd_all<BwdSmall>(w, dy_perm, x_perm, z, act, gate_perm, offsets, w13, w2, A, E, H,
+                             F, dx_perm, dw13, dw2, dgate_perm, s);
 }
 
 }  // namespace moe
