@@ -516,7 +516,8 @@ struct F8Cfg {
     static constexpr int kRowBytes = 128;                   // 128 e4m3 of K
     static constexpr int kRows = BM + BN;
     static constexpr int kTileBytes = kRows * kRowBytes;
-    static constexpr int kScaleBytes = kWaves * 256;        // 64 floats per wave (16 used)
+    static constexpr int kRpw = BM / kWaves;                // A-row scales DMA'd per wave
+    static constexpr int kScaleBytes = kWaves * 256;        // 64 floats per wave (kRpw used)
     static constexpr int kStageBytes = kTileBytes + kScaleBytes;
     static constexpr int kDma = kRows / 8 / kWaves;         // tile DMAs per wave per stage
     static constexpr int kVm = kDma + 1;                    // + the scale DMA
@@ -524,7 +525,7 @@ struct F8Cfg {
     static constexpr int kTN = BN / WN / 32;
     static constexpr int kStages = STAGES;
     static constexpr size_t kLds = (size_t)STAGES * kStageBytes;
-    static_assert(BM == 16 * kWaves, "one 16-row scale group per wave");
+    static_assert(BM % kWaves == 0 && kRpw <= 64, "one scale group of kRpw rows per wave");
     static_assert(kRows % (8 * kWaves) == 0, "DMA split");
     static_assert(KIND == 1 || (kTN == 2 && BN == 256), "GEMM1: one 128-column act block");
     static_assert(kLds <= 160 * 1024, "LDS");
@@ -539,8 +540,8 @@ MOE_DEVICE i32x8_t lds_frag32(const uint8_t* p0, const uint8_t* p1) {
 
 template <class C, int NV, class Issue>
 MOE_DEVICE void e4m3_kloop(int nk, const uint8_t* lds, Issue& issue, const int (&a_off)[C::kTM],
-                           const int (&b_off)[C::kTN], const int (&co)[2][2],
-                           const int (&srow)[C::kTM][4], const float* __restrict__ wsc,
+                           const int (&b_off)[C::kTN], const int (&co)[2][2], int srow0,
+                           const float* __restrict__ wsc,
                            const int (&wsc_off)[C::kTN], f32x16_t (&acc)[C::kTM][C::kTN]) {
     constexpr int STAGES = C::kStages;
 #pragma unroll
@@ -577,13 +578,6 @@ MOE_DEVICE void e4m3_kloop(int nk, const uint8_t* lds, Issue& issue, const int (
             for (int i = 0; i < NVv; ++i) {
                 const i32x8_t a0 = lds_frag32(base + a_off[i] + co[0][0], base + a_off[i] + co[0][1]);
                 const i32x8_t a1 = lds_frag32(base + a_off[i] + co[1][0], base + a_off[i] + co[1][1]);
-                float sa[16];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const f32x4_t v = *(const f32x4_t*)(sa_l + srow[i][q]);
-                    sa[4 * q + 0] = v[0]; sa[4 * q + 1] = v[1];
-                    sa[4 * q + 2] = v[2]; sa[4 * q + 3] = v[3];
-                }
 #pragma unroll
                 for (int j = 0; j < C::kTN; ++j) {
                     f32x16_t pt = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
@@ -591,8 +585,16 @@ MOE_DEVICE void e4m3_kloop(int nk, const uint8_t* lds, Issue& issue, const int (
                     pt = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                         a1, bv[1][j], pt, 0, 0, 0, 0x7F7F7F7F, 0, 0x7F7F7F7F);
 #pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        acc[i][j][r] = fmaf(pt[r], sa[r] * sw[j], acc[i][j][r]);
+                    for (int q = 0; q < 4; ++q) {
+                        // scales of rows q * 8 + (l / 32) * 4 + [0, 4) of sub-tile i
+                        const int row = srow0 + i * 32 + q * 8;   // this lane's 4 rows
+                        const f32x4_t v =
+                            *(const f32x4_t*)(sa_l + (row / C::kRpw) * 64 + row % C::kRpw);
+#pragma unroll
+                        for (int u = 0; u < 4; ++u)
+                            acc[i][j][4 * q + u] =
+                                fmaf(pt[4 * q + u], v[u] * sw[j], acc[i][j][4 * q + u]);
+                    }
                 }
             }
         }
@@ -618,16 +620,19 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_e4m3_kernel(GemmArgs ga) {
     nvi = nvi < 0 ? 0 : (nvi > C::kTM ? C::kTM : nvi);
     nvi = __builtin_amdgcn_readfirstlane(nvi);
 
-    // ---- tile DMA sources (as the bf16 kernel, 128-byte stage rows)
-    const uint8_t* src[C::kDma];
+    // ---- tile DMA sources (as the bf16 kernel, 128-byte stage rows): 32-bit offsets from the
+    // segment's activation base and the group's weight base
+    const uint8_t* abase = (const uint8_t*)S.a;
+    const uint8_t* wbase = (const uint8_t*)S.w + (size_t)g * S.w_mat;
+    uint32_t src[C::kDma];
 #pragma unroll
     for (int q = 0; q < C::kDma; ++q) {
         const int r = 8 * (wave + q * C::kWaves) + lane / 8;
         const int c = (lane % 8) ^ (r & 7);
-        const uint8_t* rowp;
+        size_t rowp;
         if (r < BM) {
             const int rr = m0 + r < Mg ? m0 + r : Mg - 1;
-            rowp = (const uint8_t*)S.a + (size_t)(rbase + rr) * S.a_row;
+            rowp = (size_t)(rbase + rr) * S.a_row;
         } else {
             const int rb = r - BM;
             int wrow;
@@ -635,16 +640,16 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_e4m3_kernel(GemmArgs ga) {
                 wrow = rb < BN / 2 ? nt * (BN / 2) + rb : N / 2 + nt * (BN / 2) + (rb - BN / 2);
             else
                 wrow = nt * BN + rb;
-            rowp = (const uint8_t*)S.w + (size_t)g * S.w_mat + (size_t)wrow * S.w_row;
+            rowp = (size_t)wrow * S.w_row;
         }
         const size_t step = r < BM ? S.a_kstep : S.w_kstep;
-        src[q] = rowp + (size_t)(c / 4) * step + (c % 4) * 16;
+        src[q] = (uint32_t)(rowp + (size_t)(c / 4) * step + (c % 4) * 16);
     }
     const size_t a_step = S.a_kstep, w_step = S.w_kstep;
-    // A-row scales: wave w loads rows 16 w + lane % 16 of this tile
+    // A-row scales: wave w loads rows kRpw w + lane % kRpw of this tile
     const float* ssrc;
     {
-        const int r = 16 * wave + lane % 16;
+        const int r = C::kRpw * wave + lane % C::kRpw;
         const int rr = m0 + r < Mg ? m0 + r : Mg - 1;
         ssrc = S.a_scales + (size_t)(rbase + rr) * KB;
     }
@@ -653,7 +658,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_e4m3_kernel(GemmArgs ga) {
 #pragma unroll
         for (int q = 0; q < C::kDma; ++q)
             __builtin_amdgcn_global_load_lds(
-                (const void*)(src[q] + (size_t)kstep * 2 * (q * 8 * C::kWaves < BM ? a_step : w_step)),
+                (const void*)((q * 8 * C::kWaves < BM ? abase : wbase) + src[q] +
+                              (size_t)kstep * 2 * (q * 8 * C::kWaves < BM ? a_step : w_step)),
                 (MOE_LDS void*)(base + (wave + q * C::kWaves) * 1024), 16, 0, 0);
         __builtin_amdgcn_global_load_lds((const void*)(ssrc + kstep),
                                          (MOE_LDS void*)(base + C::kTileBytes + wave * 256), 4, 0, 0);
@@ -680,15 +686,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_e4m3_kernel(GemmArgs ga) {
     for (int s = 0; s < 2; ++s)
 #pragma unroll
         for (int u = 0; u < 2; ++u) co[s][u] = (((4 * s + 2 * (lane / 32) + u) ^ (lane & 7)) * 16);
-    // LDS float index of the scales of rows (r/4)*8 + (l/32)*4 + [0,4) of sub-tile i
-    int srow[C::kTM][4];
-#pragma unroll
-    for (int i = 0; i < C::kTM; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int row = wm * (BM / WM) + i * 32 + q * 8 + (lane / 32) * 4;
-            srow[i][q] = (row / 16) * 64 + row % 16;
-        }
+    // first of the rows (r/4)*8 + (l/32)*4 + [0,4) whose scales this lane applies
+    const int srow0 = wm * (BM / WM) + (lane / 32) * 4;
     // weight-scale offsets (per sub-tile j): [g][n_block][kb]
     const int nbn = N / 128;
     int wsc_off[C::kTN];
@@ -710,7 +709,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_e4m3_kernel(GemmArgs ga) {
     case V:                                                                                 \
         if (V <= C::kTM) {                                                                  \
             constexpr int NV = V <= C::kTM ? V : C::kTM;                                    \
-            e4m3_kloop<C, NV>(KB, lds, issue, a_off, b_off, co, srow, S.w_scales, wsc_off,  \
+            e4m3_kloop<C, NV>(KB, lds, issue, a_off, b_off, co, srow0, S.w_scales, wsc_off, \
                               acc);                                                         \
         }                                                                                   \
         break;
@@ -915,8 +914,11 @@ template <int BM, int BN, int BK, int WM, int WN, int SA, int SB>
 constexpr int cfg_bn() { return BN; }
 
 // e4m3 tile configuration (BM, BN, WM, WN, STAGES), both GEMMs
-#ifndef MOE_F8_CFG
-#define MOE_F8_CFG 128, 256, 2, 4, 3
+#ifndef MOE_F8_UP_CFG
+#define MOE_F8_UP_CFG 128, 256, 2, 4, 3
+#endif
+#ifndef MOE_F8_DOWN_CFG
+#define MOE_F8_DOWN_CFG 128, 256, 2, 4, 3
 #endif
 
 template <int KIND, int BM, int BN, int WM, int WN, int STAGES>
@@ -941,12 +943,12 @@ constexpr int f8_bn() { return BN; }
 
 int bm_for(int kind, int dtype) {
     if (dtype == 0) return kF32BM;
-    if (dtype == 2) return f8_bm<MOE_F8_CFG>();
+    if (dtype == 2) return kind == 0 ? f8_bm<MOE_F8_UP_CFG>() : f8_bm<MOE_F8_DOWN_CFG>();
     return kind == 0 ? cfg_bm<MOE_BF_UP_CFG>() : cfg_bm<MOE_BF_DOWN_CFG>();
 }
 int bn_for(int kind, int dtype) {
     if (dtype == 0) return 64;
-    if (dtype == 2) return f8_bn<MOE_F8_CFG>();
+    if (dtype == 2) return kind == 0 ? f8_bn<MOE_F8_UP_CFG>() : f8_bn<MOE_F8_DOWN_CFG>();
     return kind == 0 ? cfg_bn<MOE_BF_UP_CFG>() : cfg_bn<MOE_BF_DOWN_CFG>();
 }
 
@@ -1180,8 +1182,8 @@ hipError_t launch_grouped_gemm(int kind, int dtype, const Segment* segs, int nse
         return run_bf16<1, MOE_BF_DOWN_CFG>(ga, (int)nblocks, s);
     }
     if (dtype == 2) {
-        if (kind == 0) return run_e4m3<0, MOE_F8_CFG>(ga, (int)nblocks, s);
-        return run_e4m3<1, MOE_F8_CFG>(ga, (int)nblocks, s);
+        if (kind == 0) return run_e4m3<0, MOE_F8_UP_CFG>(ga, (int)nblocks, s);
+        return run_e4m3<1, MOE_F8_DOWN_CFG>(ga, (int)nblocks, s);
     }
     return hipErrorInvalidValue;
 }
