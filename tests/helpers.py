@@ -37,6 +37,9 @@ SMALL_FP8 = {
                                 shared_F=256),
     "dsv3_fp8_small_kblock": mi.scaled(mi.CONFIGS["dsv3_fp8_skew"], T=300, H=768, F=384,
                                        shared_F=128, a_layout=1, w_layout=1),
+    # one token: one live row per GEMM tile, most experts empty
+    "dsv3_fp8_one_token": mi.scaled(mi.CONFIGS["dsv3_fp8_skew"], T=1, H=256, F=128,
+                                    shared_F=128),
 }
 
 

@@ -16,6 +16,8 @@ TOL = 2e-2
 BWD = {
     "dsv3_bwd_small": mi.scaled(mi.CONFIGS["dsv3_fp8_skew"], T=520, H=512, F=256, shared_F=256),
     "dsv3_bwd_small2": mi.scaled(mi.CONFIGS["dsv3_fp8_skew"], T=300, H=768, F=384, shared_F=384),
+    # one token: 248 of 256 experts get no rows (zero weight gradients), K = 1 row for the rest
+    "dsv3_bwd_one_token": mi.scaled(mi.CONFIGS["dsv3_fp8_skew"], T=1, H=256, F=128, shared_F=128),
 }
 
 
