@@ -27,16 +27,26 @@ namespace {
 #ifndef MOE_BWD_LARGE
 #define MOE_BWD_LARGE 1
 #endif
+#ifndef MOE_BWD_LARGE_BK
+#define MOE_BWD_LARGE_BK 64
+#endif
+#ifndef MOE_BWD_LARGE_STAGES
+#define MOE_BWD_LARGE_STAGES 2
+#endif
 
 
-constexpr int kBK = 32, kStages = 3;
 constexpr int kZeroBytes = 1024;
 
 // Tile configuration: BM x BN output tile, WM x WN waves, each wave (BM / WM) x (BN / WN) in
-// 32 x 32 MFMA sub-tiles; K step 32 (64-byte operand rows), 3-stage LDS ring.
-template <int BM_, int BN_, int WM_, int WN_>
+// 32 x 32 MFMA sub-tiles; K step BK (32 or 64), an LDS ring of STAGES steps.
+template <int BM_, int BN_, int WM_, int WN_, int BK_ = 32, int STAGES_ = 3>
 struct BwdCfg {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+    static constexpr int kBK = BK_, kStages = STAGES_;
+    static constexpr int kCpr = kBK / 8;                  // 16-byte chunks of a K-major row
+    static constexpr int kSub = kBK / 16;                 // MFMA K steps per stage
+    static_assert(kBK == 32 || kBK == 64, "BK");
+    static_assert(kStages >= 2, "stages");
     static constexpr int kWaves = WM * WN, kThreads = kWaves * 64;
     static constexpr int kTM = BM / WM / 32, kTN = BN / WN / 32;
     static constexpr int kABytes = BM * kBK * 2, kBBytes = BN * kBK * 2;
@@ -50,7 +60,7 @@ struct BwdCfg {
     static_assert(kTM >= 1 && kTN >= 1, "waves");
 };
 using BwdSmall = BwdCfg<128, 128, 2, 2>;      // 4 waves of 64 x 64
-using BwdLarge = BwdCfg<256, 256, 2, 4>;      // 8 waves of 128 x 64
+using BwdLarge = BwdCfg<256, 256, 2, 4, MOE_BWD_LARGE_BK, MOE_BWD_LARGE_STAGES>;  // 8 waves
 
 enum { OPK = 0, OPT = 1 };        // operand rows hold K (contiguous) / hold M or N
 
@@ -121,21 +131,23 @@ MOE_DEVICE void bwd_tile(const BwdArgs& ba, int L, uint8_t* lds) {
             mt = 0;
         }
     }
+    constexpr int kBK = CF::kBK, kStages = CF::kStages, kCpr = CF::kCpr;
     const int nk = RAGGED_K ? (Mg + kBK - 1) / kBK : ba.K / kBK;
     const int live = RAGGED_K ? kBM : (Mg - m0 < kBM ? Mg - m0 : kBM);
 
     // ---- DMA sources. An operand tile is made of 1 KB instructions; wave w issues
     // q = w + kWaves u.
-    // OPK tile [rows][32 k]: instruction q fills rows 16 q + lane / 4.
-    // OPT tile [32 k][C cols] (C = BM for A, BN for B; C / 8 16-byte chunks per k row):
+    // OPK tile [rows][BK k] (BK / 8 16-byte chunks per row): instruction q fills rows
+    // (512 / BK) q + lane / (BK / 8).
+    // OPT tile [BK k][C cols] (C = BM for A, BN for B; C / 8 16-byte chunks per k row):
     // instruction q fills k rows (512 / C) q + lane / (C / 8).
     const uint8_t* srcA[CF::kDmaA];
     const uint8_t* srcB[CF::kDmaB];
     int ka[CF::kDmaA], kb[CF::kDmaB];   // OPT: the k row each instruction fills (ragged K)
     auto op_src = [&](const Operand& op, int o, bool is_a, int q, const uint8_t*& src, int& krow) {
         if (o == OPK) {
-            const int r = 16 * q + lane / 4;
-            const int c = (lane % 4) ^ chunk_swz<4>(r);
+            const int r = (64 / kCpr) * q + lane / kCpr;
+            const int c = (lane % kCpr) ^ chunk_swz<kCpr>(r);
             size_t row;
             if (is_a) {                       // ragged-M activations: global rows, clamped
                 const int rr = m0 + r < Mg ? m0 + r : Mg - 1;
@@ -197,12 +209,13 @@ MOE_DEVICE void bwd_tile(const BwdArgs& ba, int L, uint8_t* lds) {
     // OPK: row (sub-tile base + lane % 32), chunk (2 s + lane / 32) ^ swz
     // OPT: k rows 16 s + 8 (h / 2) + u / 4 (+ 4), column base + 16 (h % 2) + 4 (u % 4)
     const int h16 = lane / 16, u16 = lane % 16;
-    int offK[2];
+    int offK[CF::kSub];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) offK[s] = ((2 * s + lane / 32) ^ chunk_swz<4>(lane % 32)) * 16;
+    for (int s = 0; s < CF::kSub; ++s)
+        offK[s] = ((2 * s + lane / 32) ^ chunk_swz<kCpr>(lane % 32)) * 16;
     auto frag = [&](const uint8_t* tile, int o, int cols, int sub_base, int s) -> bf16x8_t {
         if (o == OPK) {
-            return *(const bf16x8_t*)(tile + (sub_base + lane % 32) * 64 + offK[s]);
+            return *(const bf16x8_t*)(tile + (sub_base + lane % 32) * (kBK * 2) + offK[s]);
         } else {
             const int k0 = 16 * s + 8 * (h16 / 2) + u16 / 4;
             const int col = sub_base + 16 * (h16 % 2) + 4 * (u16 % 4);
@@ -226,8 +239,11 @@ MOE_DEVICE void bwd_tile(const BwdArgs& ba, int L, uint8_t* lds) {
         if (s < nk) issue(s, s);
     int stage = 0;
     for (int kt = 0; kt < nk; ++kt) {
+        // stage kt has landed once at most min(kStages - 2, later) younger stages remain
         const int later = nk - 1 - kt;
-        if (later >= 1) wait_vm_lgkm0<CF::kDmaA + CF::kDmaB>();
+        constexpr int kStep = CF::kDmaA + CF::kDmaB;
+        if (later >= kStages - 2) wait_vm_lgkm0<(kStages - 2) * kStep>();
+        else if (later >= 1) wait_vm_lgkm0<cmin(1, kStages - 2) * kStep>();
         else wait_vm_lgkm0<0>();
         block_sync();
         {
@@ -240,7 +256,7 @@ MOE_DEVICE void bwd_tile(const BwdArgs& ba, int L, uint8_t* lds) {
         const uint8_t* tb = ta + kOpBytes;
         if (nvi > 0) {
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
+            for (int s = 0; s < CF::kSub; ++s) {
                 bf16x8_t av[kTM], bv[kTN];
 #pragma unroll
                 for (int j = 0; j < kTN; ++j)
