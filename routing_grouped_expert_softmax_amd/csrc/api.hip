@@ -11,6 +11,9 @@
 #ifndef MOE_LAYER_ACT_KBLOCK
 #define MOE_LAYER_ACT_KBLOCK 0
 #endif
+#ifndef MOE_LAYER_FUSED_GATHER
+#define MOE_LAYER_FUSED_GATHER 1
+#endif
 
 namespace {
 
@@ -162,11 +165,11 @@ int run_up(const moe_config* c, int a_kb, const void* x_perm, const float* x_per
            const float* w13_scales, const void* x_shared, const float* x_shared_scales,
            const void* ws13, const float* ws13_scales, void* act, float* act_scales,
            void* shared_act, float* shared_act_scales, void* z_out, void* sched,
-           hipStream_t stream) {
+           hipStream_t stream, const int32_t* a_rows = nullptr) {
     const int dt = c->w_dtype;
     const int A = c->T * c->k;
     Segment r1 = {x_perm, x_perm_scales, offsets, c->E, 0, gate_perm, w13, w13_scales,
-                  act, act_scales, z_out, A, a_kb, c->w_layout, a_kb};
+                  act, act_scales, z_out, A, a_kb, c->w_layout, a_kb, a_rows};
     Segment s1 = {x_shared, x_shared_scales, nullptr, 1, c->T, nullptr, ws13, ws13_scales,
                   shared_act, shared_act_scales, nullptr, c->T, 0, c->w_layout, a_kb};
     if (!c->shared_F)
@@ -214,7 +217,7 @@ int run_experts(const moe_config* c, int a_kb, const void* x_perm, const float* 
                 const void* x_shared, const float* x_shared_scales, const void* ws13,
                 const float* ws13_scales, const void* ws2, const float* ws2_scales, void* act,
                 float* act_scales, void* y_perm, void* shared_y, void* z_out, void* ws,
-                hipStream_t stream, int mid_mark = -1) {
+                hipStream_t stream, int mid_mark = -1, const int32_t* a_rows = nullptr) {
     Carve cv(ws);
     void* sched = cv.take(sched_ws_bytes(c));
     void* sh_act = nullptr;
@@ -226,7 +229,7 @@ int run_experts(const moe_config* c, int a_kb, const void* x_perm, const float* 
     }
     int st = run_up(c, a_kb, x_perm, x_perm_scales, offsets, gate_perm, w13, w13_scales, x_shared,
                     x_shared_scales, ws13, ws13_scales, act, act_scales, sh_act, sh_act_scales,
-                    z_out, sched, stream);
+                    z_out, sched, stream, a_rows);
     if (st) return st;
     if (mid_mark >= 0 && stage_mark(mid_mark, stream) != hipSuccess) return MOE_ERR_HIP;
     return run_down(c, a_kb, act, act_scales, offsets, w2, w2_scales, sh_act, sh_act_scales, ws2,
@@ -469,16 +472,21 @@ int moe_layer_forward(const moe_config* cfg, const void* x, const void* w_router
     const int mode = fp8 ? 2 : (cfg->act_dtype == MOE_F32 ? 0 : 1);
     // layout of the internal activations (x_perm, act, the shared expert's act)
     const int a_kb = cfg->act_dtype == MOE_F32 ? 0 : MOE_LAYER_ACT_KBLOCK;
-    e = moe::launch_permute(mode, a_kb, x, idx, gate, cfg->T, cfg->H, cfg->E, cfg->k, counts,
-                            L.offsets, L.pos, L.src, L.gate_perm, L.x_perm, L.x_perm_scales,
-                            L.x_q, L.x_q_scales, L.scratch, stream);
+    // bf16 / e4m3 with row-major activations: no x_perm copy; GEMM1 gathers its A rows
+    // straight from x (e4m3: from the token-order codes x_q) through src
+    const bool gather = MOE_LAYER_FUSED_GATHER && cfg->act_dtype != MOE_F32 && a_kb == 0;
+    e = moe::launch_permute(mode, gather ? -1 : a_kb, x, idx, gate, cfg->T, cfg->H, cfg->E,
+                            cfg->k, counts, L.offsets, L.pos, L.src, L.gate_perm, L.x_perm,
+                            L.x_perm_scales, L.x_q, L.x_q_scales, L.scratch, stream);
     if (e == hipSuccess) e = stage_mark(3, stream);
     if (e != hipSuccess) return MOE_ERR_HIP;
     const void* xs = fp8 ? L.x_q : x;
-    st = run_experts(cfg, a_kb, L.x_perm, L.x_perm_scales, L.offsets, L.gate_perm, w13, w13_scales,
+    const void* a1 = gather ? xs : L.x_perm;
+    const float* a1_scales = gather ? (fp8 ? L.x_q_scales : nullptr) : L.x_perm_scales;
+    st = run_experts(cfg, a_kb, a1, a1_scales, L.offsets, L.gate_perm, w13, w13_scales,
                      w2, w2_scales, cfg->shared_F ? xs : nullptr, fp8 ? L.x_q_scales : nullptr,
                      ws13, ws13_scales, ws2, ws2_scales, L.act, L.act_scales, L.y_perm,
-                     L.shared_y, nullptr, L.scratch, stream, 4);
+                     L.shared_y, nullptr, L.scratch, stream, 4, gather ? L.src : nullptr);
     if (st) return st;
     e = stage_mark(5, stream);
     if (e == hipSuccess)

@@ -45,6 +45,7 @@ struct SegDev {
     size_t a_row, a_kstep, w_row, w_kstep, w_mat;
     int rows_total;
     int out_kblock;
+    const int32_t* a_rows;   // nullptr, or the source row of each launch row (a gather)
 };
 
 struct SchedArgs {
@@ -340,7 +341,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs ga) {
         const int r = C::kRowsPerDma * (wave + q * C::kWaves) + lane / C::kCpr;
         const int c = (lane % C::kCpr) ^ chunk_swz<C::kCpr>(r);
         const int rr = m0 + r < Mg ? m0 + r : Mg - 1;              // clamp the ragged tail
-        const uint8_t* rowp = (const uint8_t*)S.a + (size_t)(rbase + rr) * S.a_row;
+        const int arow = S.a_rows ? S.a_rows[rbase + rr] : rbase + rr;
+        const uint8_t* rowp = (const uint8_t*)S.a + (size_t)arow * S.a_row;
         srcA[q] = rowp + (size_t)(c / 4) * S.a_kstep + (c % 4) * 16;
     }
 #pragma unroll
@@ -632,7 +634,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_e4m3_kernel(GemmArgs ga) {
         size_t rowp;
         if (r < BM) {
             const int rr = m0 + r < Mg ? m0 + r : Mg - 1;
-            rowp = (size_t)(rbase + rr) * S.a_row;
+            rowp = (size_t)(S.a_rows ? S.a_rows[rbase + rr] : rbase + rr) * S.a_row;
         } else {
             const int rb = r - BM;
             int wrow;
@@ -651,7 +653,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_e4m3_kernel(GemmArgs ga) {
     {
         const int r = C::kRpw * wave + lane % C::kRpw;
         const int rr = m0 + r < Mg ? m0 + r : Mg - 1;
-        ssrc = S.a_scales + (size_t)(rbase + rr) * KB;
+        ssrc = S.a_scales + (size_t)(S.a_rows ? S.a_rows[rbase + rr] : rbase + rr) * KB;
     }
     auto issue = [&](int kstep, int stage) {
         MOE_LDS uint8_t* base = (MOE_LDS uint8_t*)lds + stage * C::kStageBytes;
@@ -1155,6 +1157,7 @@ hipError_t launch_grouped_gemm(int kind, int dtype, const Segment* segs, int nse
         d.w_mat = (size_t)N * K * eb;
         d.rows_total = g.rows_total;
         d.out_kblock = g.out_kblock;
+        d.a_rows = g.a_rows;
         ga.seg[i] = d;
     }
     sa.nseg = nseg;

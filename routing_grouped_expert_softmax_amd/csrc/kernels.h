@@ -30,7 +30,9 @@ hipError_t launch_route(int router, const float* logits, const float* logit_bias
 constexpr int kPermChunk = 512;   // assignments per counting block
 size_t permute_ws_bytes(int T, int k, int E);
 hipError_t launch_permute(int mode /*0 f32, 1 bf16, 2 e4m3 from bf16*/,
-                          int kblock /*1: x_perm K-blocked*/, const void* x,
+                          int kblock /*1: x_perm K-blocked; -1: no x_perm (routing metadata,
+                                       and for e4m3 the token-order x_q, only)*/,
+                          const void* x,
                           const int32_t* topk_idx, const float* topk_gate, int T, int H,
                           int E, int k, int32_t* counts, int32_t* offsets, int32_t* pos,
                           int32_t* src, float* gate_perm, void* x_perm,
@@ -41,7 +43,7 @@ hipError_t launch_permute(int mode /*0 f32, 1 bf16, 2 e4m3 from bf16*/,
 hipError_t launch_combine(int act_dtype, const void* y_perm, const int32_t* pos,
                           const void* shared_y, int T, int H, int k, void* y, hipStream_t s);
 
-// ---- K-blocked re-layout: [n, rows, cols] -> [n][cols*eb/128][rows][128 bytes] ----------
+// ---- K-blocked re-layout: [n, rows, cols] -> [n][cols*eb/64][rows][64 bytes] ------------
 hipError_t launch_pack_kblock(const void* in, int64_t n_mat, int rows, int cols, int elem_bytes,
                               void* out, hipStream_t s);
 
@@ -65,9 +67,11 @@ struct Segment {
     float* out_scales;         // GEMM1 e4m3: act scales [rows, N/2/128]
     void* z_out;               // GEMM1 optional: Z [rows, N] in the activation dtype
     int rows_total;            // rows of `a` (and of `out`)
-    int a_kblock;              // 1: `a` is K-blocked ([K*eb/128][rows_total][128 bytes])
+    int a_kblock;              // 1: `a` is K-blocked ([K*eb/64][rows_total][64 bytes])
     int w_kblock;              // 1: each group's [N, K] weight is K-blocked
     int out_kblock;            // 1: GEMM1's `out` (act) is K-blocked
+    const int32_t* a_rows;     // nullptr, or: row r reads row a_rows[r] of a row-major `a`
+                               // (and of a_scales): the permutation fused into the A loads
 };
 
 struct GemmPlan {

@@ -293,6 +293,11 @@ hipError_t launch_permute(int mode, int kblock, const void* x, const int32_t* to
     perm_rank_kernel<<<nchunk, 64, E * sizeof(int32_t), s>>>(topk_idx, topk_gate, A, E, k,
                                                              nbits, chunk_counts, offsets, pos,
                                                              src, gate_perm);
+    if (kblock < 0) {           // metadata only (the GEMM gathers the rows itself)
+        if (mode == 2)
+            return launch_quantize(x, 1, 1, T, H, 1, (uint8_t*)x_q, x_q_scales, s);
+        return hipGetLastError();
+    }
     const int blocks = (T + 3) / 4;
     auto gather = [&](const void* in, int row_bytes, const float* in_sc, float* out_sc) {
         const int64_t waves = (int64_t)((A + 15) / 16) *
