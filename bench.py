@@ -47,14 +47,26 @@ def algorithmic(cfg):
     d = {}
     d["router_logits"] = dict(bytes=T * H * b + E * H * b + T * E * 4, flops=2 * T * H * E)
     d["route"] = dict(bytes=T * E * 4 + 2 * A * 4, flops=0)
-    # x read once, written k times; idx/gate read; pos/src/gate_perm written
-    d["permute"] = dict(bytes=T * H * b + A * H * wb + 2 * A * 4 + 3 * A * 4, flops=0)
-    up_b = E * 2 * F * H * wb + A * H * wb + A * F * wb + A * 4
+    # bf16 / e4m3: the layer moves no rows here (GEMM1 gathers them from x): idx and gates
+    # read, pos / src / gate_perm written, and for e4m3 x quantised once (read x, write the
+    # codes and 1 x 128 scales). fp32: x read once and written k times.
+    meta = 2 * A * 4 + 3 * A * 4
+    if cfg.act_dtype == 0:
+        d["permute"] = dict(bytes=T * H * b + A * H * b + meta, flops=0)
+    elif cfg.w_dtype == 2:
+        d["permute"] = dict(bytes=T * H * b + T * H + T * (H // 128) * 4 + meta, flops=0)
+    else:
+        d["permute"] = dict(bytes=meta, flops=0)
+    # GEMM1 reads the tokens' rows (x, or its e4m3 codes) once: the routed rows are gathered
+    # from the same T rows the shared expert reads
+    up_b = E * 2 * F * H * wb + T * H * wb + A * F * wb + A * 4
+    if cfg.act_dtype == 0:
+        up_b += A * H * wb - T * H * wb                 # fp32 keeps the x_perm copy
     up_f = 2 * A * 2 * F * H
     dn_b = E * H * F * wb + A * F * wb + A * H * b
     dn_f = 2 * A * H * F
     if sF:
-        up_b += 2 * sF * H * wb + T * H * wb + T * sF * wb
+        up_b += 2 * sF * H * wb + T * sF * wb
         up_f += 2 * T * 2 * sF * H
         dn_b += H * sF * wb + T * sF * wb + T * H * b
         dn_f += 2 * T * H * sF
@@ -390,6 +402,9 @@ def main():
         "grouped_gemm": {"TFLOP/s": round(gemm_flops / gemm_t / 1e12, 1),
                          "frac_mfma_peak": round(gemm_flops / gemm_t / PEAK_MFMA[dtype], 4)},
         "permute_GB/s": per_stage["permute"]["GB/s"],
+        "permute_note": ("x rows copied to x_perm" if cfg.act_dtype == mi.F32 else
+                         "routing metadata" + (" + e4m3 quantisation of x" if fp8 else "") +
+                         "; GEMM1 gathers the rows from x (no x_perm copy)"),
         "stages": per_stage,
         "load": {"max_over_mean": round(float(cnt.max() / cnt.mean()), 3),
                  "min_over_mean": round(float(cnt.min() / cnt.mean()), 3)},

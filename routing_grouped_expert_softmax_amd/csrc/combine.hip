@@ -113,8 +113,23 @@ __global__ __launch_bounds__(256) void combine_f32_kernel(const float4* __restri
     }
 }
 
-MOE_DEVICE float load_as_f32(const void* p, int dtype, size_t i) {
-    return dtype == 0 ? ((const float*)p)[i] : bf16_to_f32(((const uint16_t*)p)[i]);
+// Eight consecutive values from element i (i a multiple of 8) as fp32: one 16-byte load for
+// bf16, two for fp32.
+MOE_DEVICE void load8_f32(const void* p, int dtype, size_t i, float (&f)[8]) {
+    if (dtype == 0) {
+        const float4 a = *(const float4*)((const float*)p + i);
+        const float4 b = *(const float4*)((const float*)p + i + 4);
+        f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+        f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+    } else {
+        const uint4 v = *(const uint4*)((const uint16_t*)p + i);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            f[2 * u] = bf16_to_f32((uint16_t)(w[u] & 0xFFFFu));
+            f[2 * u + 1] = bf16_to_f32((uint16_t)(w[u] >> 16));
+        }
+    }
 }
 
 // Activation quantiser, 1 x 128 blocks: one wavefront per 128-column block... per row:
@@ -130,9 +145,8 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict_
     const int64_t r = ok ? gblk / nblk_row : 0;
     const int64_t b = ok ? gblk % nblk_row : 0;
     const size_t base = (size_t)r * cols + (size_t)b * 128 + sub * 8;
-    float f[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) f[i] = ok ? load_as_f32(in, in_dtype, base + i) : 0.0f;
+    float f[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (ok) load8_f32(in, in_dtype, base, f);
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
@@ -165,20 +179,32 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(const void* __restric
     const int r = br * 128 + threadIdx.x / 2;
     const int c0 = bc * 128 + (threadIdx.x % 2) * 64;
     const size_t base = ((size_t)mat * rows + r) * (size_t)cols + c0;
+    float f[64];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        float g[8];
+        load8_f32(in, in_dtype, base + 8 * u, g);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[8 * u + i] = g[i];
+    }
     float amax = 0.0f;
-    for (int i = 0; i < 64; ++i) amax = fmaxf(amax, fabsf(load_as_f32(in, in_dtype, base + i)));
+#pragma unroll
+    for (int i = 0; i < 64; ++i) amax = fmaxf(amax, fabsf(f[i]));
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
     if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = amax;
     __syncthreads();
     amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     const float sc = e4m3_scale(amax);
-    for (int i = 0; i < 64; i += 4) {
-        uint32_t c0v = e4m3_rne_sat(load_as_f32(in, in_dtype, base + i) / sc);
-        uint32_t c1v = e4m3_rne_sat(load_as_f32(in, in_dtype, base + i + 1) / sc);
-        uint32_t c2v = e4m3_rne_sat(load_as_f32(in, in_dtype, base + i + 2) / sc);
-        uint32_t c3v = e4m3_rne_sat(load_as_f32(in, in_dtype, base + i + 3) / sc);
-        *(uint32_t*)(q + base + i) = c0v | (c1v << 8) | (c2v << 16) | (c3v << 24);
+#pragma unroll
+    for (int i = 0; i < 64; i += 16) {
+        uint32_t w[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            w[u] = e4m3_rne_sat(f[i + 4 * u] / sc) | (e4m3_rne_sat(f[i + 4 * u + 1] / sc) << 8) |
+                   (e4m3_rne_sat(f[i + 4 * u + 2] / sc) << 16) |
+                   (e4m3_rne_sat(f[i + 4 * u + 3] / sc) << 24);
+        *(uint4*)(q + base + i) = make_uint4(w[0], w[1], w[2], w[3]);
     }
     if (threadIdx.x == 0) scales[blk] = sc;
 }
