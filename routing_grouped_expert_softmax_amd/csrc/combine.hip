@@ -14,6 +14,9 @@
 #ifndef MOE_COMBINE_NT
 #define MOE_COMBINE_NT 1
 #endif
+#ifndef MOE_COMBINE_U
+#define MOE_COMBINE_U 2
+#endif
 
 namespace moe {
 namespace {
@@ -51,28 +54,50 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(const uint4* __restri
     const int t = blockIdx.x * 4 + threadIdx.x / kWave;
     if (t >= T) return;
     const int my_pos = lane < k ? pos[(size_t)t * k + lane] : 0;
+    if (KC > 0) {
+        // U chunks per lane per step: U * (KC + 1) loads in flight before the first add
+        constexpr int U = MOE_COMBINE_U;
+        for (int c0 = 0; c0 < row_chunks; c0 += U * kWave) {
+            uint4 v[U][KC > 0 ? KC : 1], sv[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int c = c0 + u * kWave + lane;
+                const bool ok = c < row_chunks;
+#pragma unroll
+                for (int j = 0; j < KC; ++j) {
+                    const int r = __shfl(my_pos, j);
+                    v[u][j] = ok ? load_stream(y_perm + (size_t)r * row_chunks + c) : uint4{};
+                }
+                sv[u] = shared_y && ok ? load_stream(shared_y + (size_t)t * row_chunks + c)
+                                       : uint4{};
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int c = c0 + u * kWave + lane;
+                if (c >= row_chunks) continue;
+                float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+                for (int j = 0; j < KC; ++j) add_bf16x8(acc, v[u][j]);
+                if (shared_y) add_bf16x8(acc, sv[u]);
+                uint4 o;
+                o.x = pack_bf16x2(acc[0], acc[1]);
+                o.y = pack_bf16x2(acc[2], acc[3]);
+                o.z = pack_bf16x2(acc[4], acc[5]);
+                o.w = pack_bf16x2(acc[6], acc[7]);
+                y[(size_t)t * row_chunks + c] = o;
+            }
+        }
+        return;
+    }
     for (int c0 = 0; c0 < row_chunks; c0 += kWave) {
         const int c = c0 + lane;
         const bool ok = c < row_chunks;
         float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (KC > 0) {
-            uint4 v[KC > 0 ? KC : 1];
-#pragma unroll
-            for (int j = 0; j < KC; ++j) {
-                const int r = __shfl(my_pos, j);
-                v[j] = ok ? load_stream(y_perm + (size_t)r * row_chunks + c) : uint4{};
-            }
-            const uint4 sv = shared_y && ok ? shared_y[(size_t)t * row_chunks + c] : uint4{};
-#pragma unroll
-            for (int j = 0; j < KC; ++j) add_bf16x8(acc, v[j]);
-            if (shared_y) add_bf16x8(acc, sv);
-        } else {
-            for (int j = 0; j < k; ++j) {
-                const int r = __shfl(my_pos, j);
-                if (ok) add_bf16x8(acc, y_perm[(size_t)r * row_chunks + c]);
-            }
-            if (shared_y && ok) add_bf16x8(acc, shared_y[(size_t)t * row_chunks + c]);
+        for (int j = 0; j < k; ++j) {
+            const int r = __shfl(my_pos, j);
+            if (ok) add_bf16x8(acc, y_perm[(size_t)r * row_chunks + c]);
         }
+        if (shared_y && ok) add_bf16x8(acc, shared_y[(size_t)t * row_chunks + c]);
         if (!ok) continue;
         uint4 o;
         o.x = pack_bf16x2(acc[0], acc[1]);
