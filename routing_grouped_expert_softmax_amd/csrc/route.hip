@@ -101,6 +101,44 @@ __global__ __launch_bounds__(256) void route_sigmoid_group_kernel(
             key[v] = sel_bias ? s + sel_bias[e] : s;
         }
     }
+    int kept = 0;
+    if (per == 32 && E == VPL * kWave) {
+        // groups are the 32-lane halves of the key registers (group 2 v + lane / 32 in v):
+        // the two largest keys of every group come from butterflies inside each half, all
+        // groups at once; then every lane ranks the group scores itself
+        uint64_t gk[VPL];
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) {
+            const uint64_t rk = rank_key(key[v], v * kWave + lane);
+            uint64_t b1 = rk;
+#pragma unroll
+            for (int off = 1; off < 32; off <<= 1) {
+                const uint64_t o = __shfl_xor(b1, off);
+                b1 = o > b1 ? o : b1;
+            }
+            uint64_t b2 = rk == b1 ? 0 : rk;
+#pragma unroll
+            for (int off = 1; off < 32; off <<= 1) {
+                const uint64_t o = __shfl_xor(b2, off);
+                b2 = o > b2 ? o : b2;
+            }
+            gk[v] = rank_key(rank_key_value(b1) + rank_key_value(b2), 2 * v + lane / 32);
+        }
+        // group g's key sits in register g / 2 of lane 32 (g % 2); kept: fewer than
+        // topk_groups groups rank above it (score desc, then group asc)
+        uint64_t gkey[2 * VPL];
+#pragma unroll
+        for (int g = 0; g < 2 * VPL; ++g) gkey[g] = __shfl(gk[g / 2], (g % 2) * 32);
+        uint32_t kept_mask = 0;
+#pragma unroll
+        for (int g = 0; g < 2 * VPL; ++g) {
+            int above = 0;
+#pragma unroll
+            for (int h = 0; h < 2 * VPL; ++h) above += gkey[h] > gkey[g];
+            kept_mask |= (above < topk_groups ? 1u : 0u) << g;
+        }
+        kept = (lane < n_groups) ? (int)((kept_mask >> lane) & 1u) : 0;
+    } else {
     // group score = sum of the two largest keys of the group; lane g keeps group g's score
     uint64_t my_group_rk = 0;
     for (int g = 0; g < n_groups; ++g) {
@@ -125,13 +163,13 @@ __global__ __launch_bounds__(256) void route_sigmoid_group_kernel(
         if (lane == g) my_group_rk = rank_key(score, g);
     }
     // keep the topk_groups best groups; lane g learns whether group g is kept
-    int kept = 0;
     for (int i = 0; i < topk_groups; ++i) {
         uint64_t best = wave_max_u64(my_group_rk);
         if (lane == rank_key_index(best)) {
             kept = 1;
             my_group_rk = 0;
         }
+    }
     }
     uint64_t rk[VPL];
 #pragma unroll
