@@ -9,9 +9,10 @@ it with gcc when no up-to-date build exists and wraps each entry point with nump
 Which part of the pages each function follows is stated in the C source.
 
 Parity status: every function here is pinned by tests under tests/ (marked "not gpu")
-against library routines, closed forms, brute force on tiny inputs or the OCP e4m3
-specification, except absolute output values for the full-size workloads, which no page
-prints ("parity unpinned" for those values; they rest on the pinned pieces).
+against library routines, closed forms, brute force on tiny inputs, the OCP e4m3
+specification, or (layer_backward) torch.autograd of an independently written forward and
+central finite differences; except absolute output values for the full-size workloads,
+which no page prints ("parity unpinned" for those values; they rest on the pinned pieces).
 """
 from __future__ import annotations
 
@@ -340,3 +341,89 @@ def expert_wgrad_entries(dy_perm, z, act, x_perm, offsets, e, gate_perm, w2, w13
                                    r13.shape[0], _p(dw13), _p(r2), _p(c2), r2.shape[0],
                                    _p(dw2))
     return dw13, dw2
+
+
+# ---------------------------------------------------------------------------------------
+# Backward of the whole layer (numpy, float64). It follows the forward of the study notes'
+# case 1 (per token: y = sum_j g_j Expert_{e_j}(x), plus the shared expert) with the gate
+# folded into the activation (technical summary, section 2.2), differentiated by the chain
+# rule; the data and weight gradients are the W/D split of section 2.3. The expert choice
+# is a selection and carries no gradient; logit_bias and sel_bias are constants.
+# ---------------------------------------------------------------------------------------
+def _as_f64(t):
+    """torch tensor (fp32 / bf16) or numpy array -> float64 numpy array of its values."""
+    if t is None:
+        return None
+    if isinstance(t, np.ndarray):
+        return t.astype(np.float64)
+    return t.detach().to("cpu").double().numpy()
+
+
+def _silu(u):
+    return u / (1.0 + np.exp(-u))
+
+
+def _dsilu(u):
+    s = 1.0 / (1.0 + np.exp(-u))
+    return s * (1.0 + u * (1.0 - s))
+
+
+def _expert_fwd_bwd(xe, w13e, w2e, g, dye):
+    """One expert on its n rows: returns (dx [n, H], dW13 [2F, H], dW2 [H, F], dg [n])."""
+    F = w13e.shape[0] // 2
+    zg = xe @ w13e[:F].T
+    zu = xe @ w13e[F:].T
+    h = _silu(zg) * zu                       # unweighted hidden
+    da = dye @ w2e                           # dL/d(g h)
+    dg = np.sum(da * h, axis=1)
+    dh = g[:, None] * da
+    dz = np.concatenate([dh * zu * _dsilu(zg), dh * _silu(zg)], axis=1)
+    return dz @ w13e, dz.T @ xe, dye.T @ (g[:, None] * h), dg
+
+
+def layer_backward(x, w_router, logits, topk_idx, w13, w2, dy, router=SOFTMAX_TOPK,
+                   route_scale=1.0, logit_bias=None, ws13=None, ws2=None):
+    """All gradients of the layer for the routing topk_idx (fixed) -> dict of float64
+    arrays: dx [T, H], dw_router [E, H], dw13, dw2, dws13, dws2 (None without a shared
+    expert), dlogits [T, E] and dgate [T, k]. Gates are recomputed in float64 from the
+    logits: softmax over the selected (biased) logits, or route_scale * s / sum s with
+    s = sigmoid(logit + bias) of the selected experts."""
+    X, Wr, W13, W2, DY = (_as_f64(v) for v in (x, w_router, w13, w2, dy))
+    L = _as_f64(logits) + (0.0 if logit_bias is None else _as_f64(logit_bias)[None, :])
+    idx = np.asarray(topk_idx, np.int64)
+    T, H = X.shape
+    E, k = W13.shape[0], idx.shape[1]
+    sel = np.take_along_axis(L, idx, axis=1)                  # [T, k]
+    if router == SOFTMAX_TOPK:
+        p = np.exp(sel - sel.max(axis=1, keepdims=True))
+        gate = p / p.sum(axis=1, keepdims=True)
+    else:
+        s = 1.0 / (1.0 + np.exp(-sel))
+        gate = route_scale * s / s.sum(axis=1, keepdims=True)
+    dx = np.zeros((T, H))
+    dw13, dw2 = np.zeros_like(W13), np.zeros_like(W2)
+    dgate = np.zeros((T, k))
+    for e in range(E):
+        t, j = np.nonzero(idx == e)          # a token selects an expert at most once
+        if t.size == 0:
+            continue
+        dxe, dw13[e], dw2[e], dgate[t, j] = _expert_fwd_bwd(X[t], W13[e], W2[e], gate[t, j],
+                                                            DY[t])
+        dx[t] += dxe
+    dws13 = dws2 = None
+    if ws13 is not None:
+        dxs, dws13, dws2, _ = _expert_fwd_bwd(X, _as_f64(ws13), _as_f64(ws2), np.ones(T), DY)
+        dx += dxs
+    # gates -> selected logits
+    if router == SOFTMAX_TOPK:
+        dsel = gate * (dgate - np.sum(gate * dgate, axis=1, keepdims=True))
+    else:
+        ssum = s.sum(axis=1, keepdims=True)
+        ds = (route_scale / ssum) * (dgate - np.sum(dgate * gate, axis=1, keepdims=True)
+                                     / route_scale)
+        dsel = ds * s * (1.0 - s)
+    dlogits = np.zeros((T, E))
+    np.put_along_axis(dlogits, idx, dsel, axis=1)
+    dx += dlogits @ Wr
+    return dict(dx=dx, dw_router=dlogits.T @ X, dw13=dw13, dw2=dw2, dws13=dws13, dws2=dws2,
+                dlogits=dlogits, dgate=dgate)
