@@ -76,7 +76,8 @@ typedef enum {
     MOE_OP_PERMUTE = 0,
     MOE_OP_GROUPED_GEMM = 1,
     MOE_OP_LAYER_FORWARD = 2,
-    MOE_OP_GROUPED_GEMM_BWD = 3
+    MOE_OP_GROUPED_GEMM_BWD = 3,
+    MOE_OP_LAYER_BACKWARD = 4
 } moe_op;
 
 /* Layer shape and numerics. Host memory, read only during a call. */
@@ -250,6 +251,32 @@ int moe_grouped_gemm_swiglu_bwd(const moe_config* cfg, const void* dy_perm,
                                 const void* w2, void* dx_perm, void* dw13, void* dw2,
                                 float* dgate_perm, void* ws, size_t ws_bytes,
                                 hipStream_t stream);
+
+/* Backward of the whole layer (bf16 operands, fp32 accumulation, bf16 gradients): the
+ * forward of the study notes' case 1 (y = sum_j g_j Expert_{e_j}(x) + shared(x), gate folded
+ * into the activation as in the technical summary, section 2.2) differentiated by the chain
+ * rule, data and weight gradients as separate GEMMs (section 2.3). The expert selection is a
+ * choice and carries no gradient; logit_bias and sel_bias are constants.
+ * Inputs are the forward's: x [T, H], w_router [E, H], logits [T, E] (fp32, before
+ * logit_bias), logit_bias [E] or NULL, topk_idx / topk_gate [T, k] (moe_route's outputs),
+ * w13 [E, 2F, H], w2 [E, H, F], ws13 / ws2 (shared expert, NULL when shared_F == 0), and
+ * dy [T, H]. Z and act are recomputed (one extra GEMM1), so nothing of the forward's
+ * workspace is needed. Gates to logits:
+ *   softmax: dl_j = g_j (dg_j - sum_i g_i dg_i)
+ *   sigmoid: dl_j = (c / S) (dg_j - sum_i dg_i g_i / c) s_j (1 - s_j),  S = sum_i s_i,
+ * zero for unselected experts; dW_r = dl^T x, and dx collects the experts' rows (combine),
+ * the shared expert and dl W_r. Outputs (all overwritten): dx [T, H], dw_router [E, H],
+ * dw13, dw2 (zero for experts without rows), dws13, dws2 (NULL without a shared expert) in
+ * bf16, and dlogits_out [T, E] fp32 (optional, NULL = skip). dl passes through bf16 on its
+ * way to the router GEMMs. Requires act_dtype = w_dtype = MOE_BF16, row-major layouts and
+ * E % 128 == 0 (else MOE_ERR_UNSUPPORTED). Deterministic.
+ * Workspace: moe_workspace_size(cfg, MOE_OP_LAYER_BACKWARD). */
+int moe_layer_backward(const moe_config* cfg, const void* x, const void* w_router,
+                       const float* logits, const float* logit_bias, const int32_t* topk_idx,
+                       const float* topk_gate, const void* w13, const void* w2,
+                       const void* ws13, const void* ws2, const void* dy, void* dx,
+                       void* dw_router, void* dw13, void* dw2, void* dws13, void* dws2,
+                       float* dlogits_out, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Re-layout of n_mat row-major matrices [rows, cols] of elem_bytes-byte elements into the
  * K-blocked layout [n_mat][cols * elem_bytes / 64][rows][64 bytes] (see Layouts). A pure

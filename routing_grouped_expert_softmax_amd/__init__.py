@@ -25,7 +25,8 @@ LIB_PATH = os.path.join(_HERE, "libmoe_amd.so")
 F32, BF16, E4M3 = 0, 1, 2
 SOFTMAX_TOPK, SIGMOID_GROUP_TOPK = 0, 1
 LAYOUT_ROWS, LAYOUT_KBLOCK = 0, 1
-OP_PERMUTE, OP_GROUPED_GEMM, OP_LAYER_FORWARD, OP_GROUPED_GEMM_BWD = 0, 1, 2, 3
+OP_PERMUTE, OP_GROUPED_GEMM, OP_LAYER_FORWARD, OP_GROUPED_GEMM_BWD, OP_LAYER_BACKWARD = \
+    0, 1, 2, 3, 4
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -71,6 +72,7 @@ _SIGS = {
     "moe_quantize_e4m3": [P, I32, I64, I32, I32, I32, I32, P, P, P],
     "moe_pack_kblock": [P, I64, I32, I32, I32, P, P],
     "moe_set_stage_events": [P, I32],
+    "moe_layer_backward": [CFG, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
 }
 for _name, _args in _SIGS.items():
     getattr(_lib, _name).argtypes = _args
@@ -379,6 +381,37 @@ def grouped_gemm_swiglu_bwd(cfg, dy_perm, x_perm, z, act, gate_perm, offsets, w1
         _ptr(offsets, torch.int32, (E + 1,), "offsets"), _ptr(w13, bf, (E, 2 * F, H), "w13"),
         _ptr(w2, bf, (E, H, F), "w2"), _ptr(out["dx_perm"]), _ptr(out["dw13"]),
         _ptr(out["dw2"]), _ptr(out["dgate_perm"]), _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def layer_backward(cfg, x, w_router, logits, topk_idx, topk_gate, w13, w2, dy,
+                   logit_bias=None, ws13=None, ws2=None, want_dlogits=False, ws=None,
+                   stream=None):
+    """Gradients of the whole layer (moe_layer_backward) for the forward's routing. Returns
+    dict dx, dw_router, dw13, dw2, dws13, dws2 (None without a shared expert), dlogits
+    (fp32, None unless want_dlogits)."""
+    dev = x.device
+    T, H, E, k, F, sF = cfg.T, cfg.H, cfg.E, cfg.k, cfg.F, cfg.shared_F
+    bf, f32 = torch.bfloat16, torch.float32
+    out = dict(dx=torch.empty(T, H, dtype=bf, device=dev),
+               dw_router=torch.empty(E, H, dtype=bf, device=dev),
+               dw13=torch.empty(E, 2 * F, H, dtype=bf, device=dev),
+               dw2=torch.empty(E, H, F, dtype=bf, device=dev),
+               dws13=torch.empty(2 * sF, H, dtype=bf, device=dev) if sF else None,
+               dws2=torch.empty(H, sF, dtype=bf, device=dev) if sF else None,
+               dlogits=torch.empty(T, E, dtype=f32, device=dev) if want_dlogits else None)
+    if ws is None:
+        ws = workspace(cfg, OP_LAYER_BACKWARD, dev)
+    c = make_config(cfg)
+    _check("moe_layer_backward", _lib.moe_layer_backward(
+        C.byref(c), _ptr(x, bf, (T, H), "x"), _ptr(w_router, bf, (E, H), "w_router"),
+        _ptr(logits, f32, (T, E), "logits"), _ptr(logit_bias, f32, (E,), "logit_bias"),
+        _ptr(topk_idx, torch.int32, (T, k), "topk_idx"),
+        _ptr(topk_gate, f32, (T, k), "topk_gate"), _ptr(w13, bf, (E, 2 * F, H), "w13"),
+        _ptr(w2, bf, (E, H, F), "w2"), _ptr(ws13, bf, (2 * sF, H), "ws13"),
+        _ptr(ws2, bf, (H, sF), "ws2"), _ptr(dy, bf, (T, H), "dy"), _ptr(out["dx"]),
+        _ptr(out["dw_router"]), _ptr(out["dw13"]), _ptr(out["dw2"]), _ptr(out["dws13"]),
+        _ptr(out["dws2"]), _ptr(out["dlogits"]), _ptr(ws), ws.numel(), _stream(stream)))
     return out
 
 

@@ -148,6 +148,60 @@ LayerWs carve_layer(const moe_config* c, void* ws) {
     return L;
 }
 
+// Workspace of the whole-layer backward: the routing metadata (twice: for x and for dY),
+// the expert-grouped x and dY, the recomputed Z and act (routed and shared), the data
+// gradients before they are combined, dl, and the scratch of every launch.
+struct LayerBwdWs {
+    int32_t *counts, *offsets, *pos, *src, *counts2, *offsets2, *pos2, *src2, *offs_one;
+    float *gate_perm, *gate_perm2, *dgate_perm;
+    void *x_perm, *dy_perm, *z, *act, *zs, *acts, *dx_perm, *dxs, *dxr, *dl;
+    void *perm_scratch, *sched, *bws, *bws_s, *rws;
+    size_t total;
+};
+
+size_t sched_ws_bytes(const moe_config* c);
+
+LayerBwdWs carve_layer_bwd(const moe_config* c, void* ws) {
+    LayerBwdWs L = {};
+    Carve cv(ws);
+    const size_t T = c->T, H = c->H, E = c->E, k = c->k, F = c->F, sF = c->shared_F, A = T * k;
+    for (int rep = 0; rep < 2; ++rep) {
+        int32_t* counts = (int32_t*)cv.take(E * 4);
+        int32_t* offsets = (int32_t*)cv.take((E + 1) * 4);
+        int32_t* pos = (int32_t*)cv.take(A * 4);
+        int32_t* src = (int32_t*)cv.take(A * 4);
+        float* gp = (float*)cv.take(A * 4);
+        if (rep == 0) { L.counts = counts; L.offsets = offsets; L.pos = pos; L.src = src; L.gate_perm = gp; }
+        else { L.counts2 = counts; L.offsets2 = offsets; L.pos2 = pos; L.src2 = src; L.gate_perm2 = gp; }
+    }
+    L.offs_one = (int32_t*)cv.take(2 * 4);
+    L.dgate_perm = (float*)cv.take(A * 4);
+    L.x_perm = cv.take(A * H * 2);
+    L.dy_perm = cv.take(A * H * 2);
+    L.z = cv.take(A * 2 * F * 2);
+    L.act = cv.take(A * F * 2);
+    L.zs = sF ? cv.take(T * 2 * sF * 2) : nullptr;
+    L.acts = sF ? cv.take(T * sF * 2) : nullptr;
+    L.dx_perm = cv.take(A * H * 2);
+    L.dxs = sF ? cv.take(T * H * 2) : nullptr;
+    L.dxr = cv.take(T * H * 2);
+    L.dl = cv.take(T * E * 2);
+    L.perm_scratch = cv.take(moe::permute_ws_bytes(c->T, c->k, c->E));
+    L.sched = cv.take(sched_ws_bytes(c));
+    L.bws = cv.take(moe::bwd_ws_bytes(c->T, c->k, c->E, c->H, c->F));
+    L.bws_s = sF ? cv.take(moe::bwd_ws_bytes(c->T, 1, 1, c->H, c->shared_F)) : nullptr;
+    L.rws = cv.take(moe::router_bwd_ws_bytes(c->T));
+    L.total = cv.off;
+    return L;
+}
+
+int check_layer_bwd(const moe_config* c) {
+    if (c->act_dtype != MOE_BF16 || c->w_dtype != MOE_BF16 || c->a_layout || c->w_layout)
+        return MOE_ERR_UNSUPPORTED;
+    if (c->E % 128) return MOE_ERR_UNSUPPORTED;          // router GEMM tiles
+    return MOE_OK;
+}
+
 size_t sched_ws_bytes(const moe_config* c) {
     const int dt = c->w_dtype;
     const int seg_groups = c->E + (c->shared_F ? 1 : 0);
@@ -262,6 +316,11 @@ int moe_workspace_size(const moe_config* cfg, int op, size_t* bytes) {
     case MOE_OP_GROUPED_GEMM_BWD:
         if (cfg->act_dtype != MOE_BF16 || cfg->a_layout || cfg->w_layout) return MOE_ERR_UNSUPPORTED;
         *bytes = moe::bwd_ws_bytes(cfg->T, cfg->k, cfg->E, cfg->H, cfg->F);
+        break;
+    case MOE_OP_LAYER_BACKWARD:
+        st = check_layer_bwd(cfg);
+        if (st) return st;
+        *bytes = carve_layer_bwd(cfg, nullptr).total;
         break;
     default: return MOE_ERR_INVALID_ARG;
     }
@@ -526,6 +585,73 @@ int moe_grouped_gemm_swiglu_bwd(const moe_config* cfg, const void* dy_perm, cons
                                                    w13, w2, cfg->T * cfg->k, cfg->E, cfg->H,
                                                    cfg->F, dx_perm, dw13, dw2, dgate_perm, ws,
                                                    stream));
+}
+
+int moe_layer_backward(const moe_config* cfg, const void* x, const void* w_router,
+                       const float* logits, const float* logit_bias, const int32_t* topk_idx,
+                       const float* topk_gate, const void* w13, const void* w2,
+                       const void* ws13, const void* ws2, const void* dy, void* dx,
+                       void* dw_router, void* dw13, void* dw2, void* dws13, void* dws2,
+                       float* dlogits_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+    int st = check_cfg(cfg);
+    if (st) return st;
+    st = check_layer_bwd(cfg);
+    if (st) return st;
+    if (!x || !w_router || !logits || !topk_idx || !topk_gate || !w13 || !w2 || !dy || !dx ||
+        !dw_router || !dw13 || !dw2 || !ws)
+        return MOE_ERR_INVALID_ARG;
+    if (cfg->shared_F) {
+        if (!ws13 || !ws2 || !dws13 || !dws2) return MOE_ERR_INVALID_ARG;
+    } else if (ws13 || ws2 || dws13 || dws2) {
+        return MOE_ERR_INVALID_ARG;
+    }
+    LayerBwdWs L = carve_layer_bwd(cfg, nullptr);
+    if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    L = carve_layer_bwd(cfg, ws);
+    const int T = cfg->T, H = cfg->H, E = cfg->E, k = cfg->k, F = cfg->F, sF = cfg->shared_F;
+    const int A = T * k;
+    // expert-grouped x and dY (the permute of dY is the backward of the combine)
+    hipError_t e = moe::launch_permute(1, 0, x, topk_idx, topk_gate, T, H, E, k, L.counts,
+                                       L.offsets, L.pos, L.src, L.gate_perm, L.x_perm, nullptr,
+                                       nullptr, nullptr, L.perm_scratch, stream);
+    if (e == hipSuccess)
+        e = moe::launch_permute(1, 0, dy, topk_idx, topk_gate, T, H, E, k, L.counts2,
+                                L.offsets2, L.pos2, L.src2, L.gate_perm2, L.dy_perm, nullptr,
+                                nullptr, nullptr, L.perm_scratch, stream);
+    // recompute Z and act of GEMM1 (routed, then the shared expert)
+    if (e == hipSuccess) {
+        Segment r1 = {L.x_perm, nullptr, L.offsets, E, 0, L.gate_perm, w13, nullptr, L.act,
+                      nullptr, L.z, A, 0, 0, 0, nullptr};
+        e = moe::launch_grouped_gemm(0, MOE_BF16, &r1, 1, A, 2 * F, H, L.sched, stream);
+    }
+    if (e == hipSuccess) e = moe::launch_offsets2(L.offs_one, T, stream);
+    if (e == hipSuccess && sF) {
+        Segment s1 = {x, nullptr, nullptr, 1, T, nullptr, ws13, nullptr, L.acts, nullptr, L.zs,
+                      T, 0, 0, 0, nullptr};
+        e = moe::launch_grouped_gemm(0, MOE_BF16, &s1, 1, T, 2 * sF, H, L.sched, stream);
+    }
+    // expert gradients (routed: dgate through the fold; shared: gate 1)
+    if (e == hipSuccess)
+        e = moe::launch_grouped_gemm_bwd(L.dy_perm, L.x_perm, L.z, L.act, L.gate_perm,
+                                         L.offsets, w13, w2, A, E, H, F, L.dx_perm, dw13, dw2,
+                                         L.dgate_perm, L.bws, stream);
+    if (e == hipSuccess && sF)
+        e = moe::launch_grouped_gemm_bwd(dy, x, L.zs, L.acts, nullptr, L.offs_one, ws13, ws2,
+                                         T, 1, H, sF, L.dxs, dws13, dws2, nullptr, L.bws_s,
+                                         stream);
+    // gates -> logits -> router weight and x
+    if (e == hipSuccess)
+        e = moe::launch_route_backward(cfg->router, logits, logit_bias, topk_idx, topk_gate,
+                                       L.dgate_perm, L.pos, T, E, k, cfg->route_scale,
+                                       (uint16_t*)L.dl, dlogits_out, stream);
+    if (e == hipSuccess)
+        e = moe::launch_router_bwd(L.dl, x, w_router, T, E, H, dw_router, L.dxr, L.rws, stream);
+    // dx = combine of the experts' rows (+ the shared expert's) + the router's part
+    if (e == hipSuccess)
+        e = moe::launch_combine(MOE_BF16, L.dx_perm, L.pos, sF ? L.dxs : nullptr, T, H, k, dx,
+                                stream);
+    if (e == hipSuccess) e = moe::launch_add_bf16(dx, L.dxr, (int64_t)T * H, stream);
+    return hip_status(e);
 }
 
 int moe_pack_kblock(const void* in, int64_t n_mat, int32_t rows, int32_t cols,

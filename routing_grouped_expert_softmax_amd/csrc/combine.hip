@@ -255,6 +255,23 @@ __global__ __launch_bounds__(256) void pack_kblock_kernel(const uint4* __restric
     out[mbase + ((size_t)j * rows + r) * 4 + c] = in[mbase + (size_t)r * row_chunks + j * 4 + c];
 }
 
+// y += a, elementwise over n bf16 values (n % 8 == 0), summed in fp32 and rounded once.
+__global__ __launch_bounds__(256) void add_bf16_kernel(uint4* __restrict__ y,
+                                                       const uint4* __restrict__ a,
+                                                       int64_t n8) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n8) return;
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    add_bf16x8(acc, y[i]);
+    add_bf16x8(acc, a[i]);
+    uint4 o;
+    o.x = pack_bf16x2(acc[0], acc[1]);
+    o.y = pack_bf16x2(acc[2], acc[3]);
+    o.z = pack_bf16x2(acc[4], acc[5]);
+    o.w = pack_bf16x2(acc[6], acc[7]);
+    y[i] = o;
+}
+
 }  // namespace
 
 hipError_t launch_pack_kblock(const void* in, int64_t n_mat, int rows, int cols, int elem_bytes,
@@ -301,6 +318,12 @@ hipError_t launch_quantize(const void* in, int in_dtype, int64_t n_mat, int rows
         quant_weight_kernel<<<(unsigned)nblocks, 256, 0, s>>>(in, in_dtype, rows, cols, q,
                                                               scales);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_add_bf16(void* y, const void* a, int64_t n, hipStream_t s) {
+    const int64_t n8 = n / 8;
+    add_bf16_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, s>>>((uint4*)y, (const uint4*)a, n8);
     return hipGetLastError();
 }
 

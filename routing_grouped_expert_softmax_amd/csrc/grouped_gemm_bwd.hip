@@ -384,6 +384,14 @@ __global__ __launch_bounds__(256) void dg_reduce_kernel(const float* __restrict_
     dg[r] = s;
 }
 
+// offsets {0, T} of a single group, and a zeroed page
+__global__ __launch_bounds__(256) void fill_offsets2_kernel(int32_t* offs, int T, uint32_t* z,
+                                                            int nz) {
+    const int i = threadIdx.x;
+    if (i < 2) offs[i] = i == 0 ? 0 : T;
+    for (int j = i; j < nz; j += 256) z[j] = 0u;
+}
+
 __global__ __launch_bounds__(256) void zero_fill_kernel(uint32_t* p, int n) {
     const int i = blockIdx.x * 256 + threadIdx.x;
     if (i < n) p[i] = 0u;
@@ -491,6 +499,37 @@ hipError_t bwd_all(const BwdWs& w, const void* dy_perm, const void* x_perm, cons
     return run_bwd<CF, OPT, OPT, 1, 0>(w1, round8((size_t)E * w1.ntm * w1.ntn), s);
 }
 
+// Router weight and data gradients as one-group GEMMs of the same kernel:
+//   dW_r [E, H] = dl^T x      (K = the T token rows, both operands read as [k][m])
+//   dx_r [T, H] = dl W_r      (ragged-M mode with a single group of T rows, K = E)
+template <class CF>
+hipError_t router_bwd_all(const void* dl, const void* x, const void* w_router, int T, int E,
+                          int H, const int32_t* offs2, void* sched, const uint8_t* zero,
+                          void* dw_router, void* dx_router, hipStream_t s) {
+    const uint16_t* DL = (const uint16_t*)dl;
+    auto round8 = [](size_t n) { return (int)((n + 7) / 8 * 8); };
+    BwdArgs wa = {};
+    wa.a = {DL, (size_t)E, 0};
+    wa.b = {(const uint16_t*)x, (size_t)H, 0};
+    wa.offsets = offs2; wa.M = E; wa.N = H; wa.ntm = E / CF::BM; wa.ntn = H / CF::BN;
+    wa.groups = 1; wa.out = (uint16_t*)dw_router; wa.out_ld = H; wa.out_gstride = 0;
+    wa.zero = zero;
+    hipError_t e = run_bwd<CF, OPT, OPT, 1, 0>(wa, round8((size_t)wa.ntm * wa.ntn), s);
+    if (e != hipSuccess) return e;
+    e = launch_schedule(offs2, 1, CF::BM, sched, s);
+    if (e != hipSuccess) return e;
+    BwdArgs da = {};
+    da.a = {DL, (size_t)E, 0};
+    da.b = {(const uint16_t*)w_router, (size_t)H, 0};
+    da.offsets = offs2;
+    da.tiles = (const int4*)((char*)sched + 256);
+    da.total = (const int*)sched;
+    da.N = H; da.K = E; da.ntn = H / CF::BN; da.groups = 1;
+    da.out = (uint16_t*)dx_router; da.out_ld = H; da.zero = zero;
+    const size_t max_tiles = (size_t)(T + CF::BM - 1) / CF::BM + 1;
+    return run_bwd<CF, OPK, OPT, 0, 0>(da, round8(max_tiles * da.ntn), s);
+}
+
 }  // namespace
 
 size_t bwd_ws_bytes(int T, int k, int E, int H, int F) {
@@ -511,6 +550,31 @@ hipError_t launch_grouped_gemm_bwd(const void* dy_perm, const void* x_perm, cons
                                  H, F, dx_perm, dw13, dw2, dgate_perm, s);
     return bwd_all<BwdSmall>(w, dy_perm, x_perm, z, act, gate_perm, offsets, w13, w2, A, E, H,
                              F, dx_perm, dw13, dw2, dgate_perm, s);
+}
+
+size_t router_bwd_ws_bytes(int T) {
+    return 256 + kZeroBytes + schedule_ws_bytes(T, 1, BwdSmall::BM);
+}
+
+// ws: {0, T} offsets (256 bytes), a zero page, the tile schedule
+hipError_t launch_router_bwd(const void* dl, const void* x, const void* w_router, int T, int E,
+                             int H, void* dw_router, void* dx_router, void* ws, hipStream_t s) {
+    int32_t* offs2 = (int32_t*)ws;
+    uint8_t* zero = (uint8_t*)ws + 256;
+    void* sched = (char*)ws + 256 + kZeroBytes;
+    fill_offsets2_kernel<<<1, 256, 0, s>>>(offs2, T, (uint32_t*)zero, kZeroBytes / 4);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (E % BwdLarge::BM == 0 && H % BwdLarge::BN == 0 && MOE_BWD_LARGE)
+        return router_bwd_all<BwdLarge>(dl, x, w_router, T, E, H, offs2, sched, zero,
+                                        dw_router, dx_router, s);
+    return router_bwd_all<BwdSmall>(dl, x, w_router, T, E, H, offs2, sched, zero, dw_router,
+                                    dx_router, s);
+}
+
+hipError_t launch_offsets2(int32_t* offs, int T, hipStream_t s) {
+    fill_offsets2_kernel<<<1, 256, 0, s>>>(offs, T, nullptr, 0);
+    return hipGetLastError();
 }
 
 }  // namespace moe

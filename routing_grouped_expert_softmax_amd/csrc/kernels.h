@@ -26,6 +26,14 @@ hipError_t launch_route(int router, const float* logits, const float* logit_bias
                         int topk_groups, float route_scale, int32_t* topk_idx,
                         float* topk_gate, hipStream_t s);
 
+// gates -> logits: dl [T, E] (bf16, and fp32 when dl_f32 != nullptr) from the gates'
+// gradient in expert-grouped order (dgate_perm [T*k], read through pos)
+hipError_t launch_route_backward(int router, const float* logits, const float* logit_bias,
+                                 const int32_t* topk_idx, const float* topk_gate,
+                                 const float* dgate_perm, const int32_t* pos, int T, int E,
+                                 int k, float route_scale, uint16_t* dl_bf16, float* dl_f32,
+                                 hipStream_t s);
+
 // ---- permute ---------------------------------------------------------------------------
 constexpr int kPermChunk = 512;   // assignments per counting block
 size_t permute_ws_bytes(int T, int k, int E);
@@ -42,6 +50,9 @@ hipError_t launch_permute(int mode /*0 f32, 1 bf16, 2 e4m3 from bf16*/,
 // ---- combine ---------------------------------------------------------------------------
 hipError_t launch_combine(int act_dtype, const void* y_perm, const int32_t* pos,
                           const void* shared_y, int T, int H, int k, void* y, hipStream_t s);
+
+// y += a over n bf16 values (n % 8 == 0), fp32 sum, one rounding
+hipError_t launch_add_bf16(void* y, const void* a, int64_t n, hipStream_t s);
 
 // ---- K-blocked re-layout: [n, rows, cols] -> [n][cols*eb/64][rows][64 bytes] ------------
 hipError_t launch_pack_kblock(const void* in, int64_t n_mat, int rows, int cols, int elem_bytes,
@@ -94,6 +105,15 @@ hipError_t launch_grouped_gemm_bwd(const void* dy_perm, const void* x_perm, cons
                                    const int32_t* offsets, const void* w13, const void* w2,
                                    int A, int E, int H, int F, void* dx_perm, void* dw13,
                                    void* dw2, float* dgate_perm, void* ws, hipStream_t s);
+
+// offsets {0, T} of a single group of T rows
+hipError_t launch_offsets2(int32_t* offs, int T, hipStream_t s);
+
+// Router backward GEMMs (bf16): dW_r = dl^T x [E, H] and dx_r = dl W_r [T, H] from
+// dl [T, E]; E and H multiples of 128. Workspace: router_bwd_ws_bytes(T).
+size_t router_bwd_ws_bytes(int T);
+hipError_t launch_router_bwd(const void* dl, const void* x, const void* w_router, int T, int E,
+                             int H, void* dw_router, void* dx_router, void* ws, hipStream_t s);
 
 GemmPlan grouped_gemm_plan(int kind, int dtype, int max_rows_total, int groups_total, int N,
                            int K);

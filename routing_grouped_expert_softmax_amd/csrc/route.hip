@@ -300,6 +300,59 @@ __global__ __launch_bounds__(256 * S) void router_logits_bf16_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// Backward of the gates to the logits (one wavefront per token). The expert choice carries
+// no gradient; lane j < k holds slot j. With dg_j = dL/dg_j:
+//   softmax: dl_j = g_j (dg_j - sum_i g_i dg_i)
+//   sigmoid: s_j = sigmoid(l_j + bias), S = sum_i s_i, g_j = c s_j / S,
+//            dl_j = (c / S) (dg_j - sum_i dg_i g_i / c) s_j (1 - s_j)
+// Unselected experts get 0. dl is written in bf16 (the router GEMMs' operand) and, when
+// asked, in fp32.
+// ---------------------------------------------------------------------------------------
+template <int VPL>
+__global__ __launch_bounds__(256) void route_backward_kernel(
+    const float* __restrict__ logits, const float* __restrict__ logit_bias,
+    const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_gate,
+    const float* __restrict__ dgate_perm, const int32_t* __restrict__ pos, int T, int E,
+    int k, int router, float route_scale, uint16_t* __restrict__ dl_bf16,
+    float* __restrict__ dl_f32) {
+    const int lane = threadIdx.x % kWave;
+    const int t = blockIdx.x * kRouteWaves + threadIdx.x / kWave;
+    if (t >= T) return;
+    const bool mine = lane < k;
+    const int e = mine ? topk_idx[(size_t)t * k + lane] : 0;
+    const float g = mine ? topk_gate[(size_t)t * k + lane] : 0.0f;
+    const float dg = mine ? dgate_perm[pos[(size_t)t * k + lane]] : 0.0f;
+    const float dot = wave_sum_f32(g * dg);
+    float dl = 0.0f;
+    if (router == 0) {
+        dl = g * (dg - dot);
+    } else {
+        float sv = 0.0f;
+        if (mine) {
+            const float l = logits[(size_t)t * E + e] + (logit_bias ? logit_bias[e] : 0.0f);
+            sv = sigmoid_rounded(l);
+        }
+        const float ssum = wave_sum_f32(sv);
+        dl = (route_scale / ssum) * (dg - dot / route_scale) * sv * (1.0f - sv);
+    }
+    // row t: every expert column, 0 unless selected (k <= 32 distinct experts)
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+        const int c = v * kWave + lane;
+        float val = 0.0f;
+        for (int j = 0; j < k; ++j) {
+            const int ej = __shfl(e, j);
+            const float dj = __shfl(dl, j);
+            if (ej == c) val = dj;
+        }
+        if (c < E) {
+            dl_bf16[(size_t)t * E + c] = f32_to_bf16(val);
+            if (dl_f32) dl_f32[(size_t)t * E + c] = val;
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_router_logits(int act_dtype, const void* x, const void* w_router, int T,
@@ -354,6 +407,34 @@ hipError_t launch_route(int router, const float* logits, const float* logit_bias
     MOE_ROUTE_CASE(8)
     MOE_ROUTE_CASE(16)
 #undef MOE_ROUTE_CASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace moe
+
+namespace moe {
+
+hipError_t launch_route_backward(int router, const float* logits, const float* logit_bias,
+                                 const int32_t* topk_idx, const float* topk_gate,
+                                 const float* dgate_perm, const int32_t* pos, int T, int E,
+                                 int k, float route_scale, uint16_t* dl_bf16, float* dl_f32,
+                                 hipStream_t s) {
+    const int blocks = (T + kRouteWaves - 1) / kRouteWaves;
+    const int vpl = (E + kWave - 1) / kWave;
+#define MOE_RB_CASE(V)                                                                      \
+    if (vpl <= V) {                                                                         \
+        route_backward_kernel<V><<<blocks, 256, 0, s>>>(logits, logit_bias, topk_idx,      \
+                                                        topk_gate, dgate_perm, pos, T, E,  \
+                                                        k, router, route_scale, dl_bf16,   \
+                                                        dl_f32);                           \
+        return hipGetLastError();                                                           \
+    }
+    MOE_RB_CASE(1)
+    MOE_RB_CASE(2)
+    MOE_RB_CASE(4)
+    MOE_RB_CASE(8)
+    MOE_RB_CASE(16)
+#undef MOE_RB_CASE
     return hipErrorInvalidValue;
 }
 

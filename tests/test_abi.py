@@ -165,3 +165,21 @@ def test_stage_event_argument_checks(moe):
     arr[3] = None
     assert L.moe_set_stage_events(arr, 7) == 1
     assert L.moe_set_stage_events(None, 0) == 0
+
+
+def test_layer_backward_argument_checks(moe):
+    """Workspace query and host-side rejections of moe_layer_backward (no GPU call)."""
+    c = cfgc(moe, base="dsv3_bf16")
+    st, n = ws_size(moe, c, moe.OP_LAYER_BACKWARD)
+    assert st == 0 and n > 0
+    assert ws_size(moe, cfgc(moe, base="mixtral_bf16"), moe.OP_LAYER_BACKWARD)[0] == 2  # E = 8
+    assert ws_size(moe, cfgc(moe, base="tiny_fp32"), moe.OP_LAYER_BACKWARD)[0] == 2    # fp32
+    L = moe.lib()
+    p = C.c_void_p(0x1000)
+    args = [p] * 19
+    # missing dy
+    a = list(args)
+    a[10] = None
+    assert L.moe_layer_backward(C.byref(c), *a, C.c_size_t(n), None) == 1
+    # workspace too small
+    assert L.moe_layer_backward(C.byref(c), *args, C.c_size_t(n - 1), None) == 3

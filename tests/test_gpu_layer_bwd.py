@@ -1,0 +1,83 @@
+"""Whole-layer backward (moe_layer_backward) through the C ABI against the oracle's float64
+layer backward, on the routing the GPU forward chose. Tolerance: bf16 (2e-2 of the largest
+reference value per tensor)."""
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+import oracle
+from helpers import rel_err, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def moe():
+    import routing_grouped_expert_softmax_amd as m
+    return m
+
+
+BF = mi.BF16
+CASES = {
+    # DeepSeek-style router (sigmoid, groups, x2.5) with a shared expert
+    "dsv3": mi.scaled(mi.CONFIGS["dsv3_bf16"], T=300, H=512, F=256, shared_F=256),
+    # the skewed config's router: a Zipf logit bias on top (bf16 expert weights)
+    "dsv3_skew": mi.scaled(mi.CONFIGS["dsv3_fp8_skew"], T=260, H=256, F=128, shared_F=128,
+                           w_dtype=BF, backward=True),
+    # softmax router, no shared expert, F not a multiple of 256 (128 x 128 tiles)
+    "qwen3": mi.scaled(mi.CONFIGS["qwen3_bf16"], T=200, H=256, F=384),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_layer_backward(moe, name):
+    cfg = CASES[name]
+    print(f"[layer bwd] {name}: T={cfg.T} H={cfg.H} E={cfg.E} k={cfg.k} F={cfg.F} "
+          f"shared={cfg.shared_F}", flush=True)
+    inp = mi.make_inputs(cfg)
+    rng = np.random.default_rng(97)
+    dy = torch.from_numpy(rng.standard_normal((cfg.T, cfg.H)).astype(np.float32)).to(
+        torch.bfloat16)
+    d = dict(x=inp.x.cuda(), wr=inp.w_router.cuda(), w13=inp.w13.cuda(), w2=inp.w2.cuda(),
+             lb=to_dev(inp.logit_bias), sb=to_dev(inp.sel_bias), ws13=to_dev(inp.ws13),
+             ws2=to_dev(inp.ws2))
+    _, ex = moe.layer_forward(cfg, d["x"], d["wr"], d["w13"], d["w2"], d["lb"], d["sb"],
+                              ws13=d["ws13"], ws2=d["ws2"],
+                              want=("logits", "topk_idx", "topk_gate"))
+    g = moe.layer_backward(cfg, d["x"], d["wr"], ex["logits"], ex["topk_idx"],
+                           ex["topk_gate"], d["w13"], d["w2"], dy.cuda(),
+                           logit_bias=d["lb"], ws13=d["ws13"], ws2=d["ws2"],
+                           want_dlogits=True)
+    torch.cuda.synchronize()
+    ref = oracle.layer_backward(inp.x, inp.w_router, ex["logits"].cpu().numpy(),
+                                ex["topk_idx"].cpu().numpy(), inp.w13, inp.w2, dy,
+                                cfg.router, cfg.route_scale,
+                                None if inp.logit_bias is None else inp.logit_bias.numpy(),
+                                inp.ws13, inp.ws2)
+    names = ["dx", "dw_router", "dw13", "dw2", "dlogits"] + (
+        ["dws13", "dws2"] if cfg.shared_F else [])
+    for n in names:
+        err = rel_err(g[n].float().cpu(), ref[n])
+        print(f"[layer bwd] {name}: {n} rel err {err:.3e}", flush=True)
+        assert err <= 2e-2, n
+    # experts that received no rows get zero weight gradients
+    counts = np.bincount(ex["topk_idx"].cpu().numpy().ravel(), minlength=cfg.E)
+    empty = np.nonzero(counts == 0)[0]
+    if empty.size:
+        assert torch.count_nonzero(g["dw13"][torch.from_numpy(empty).cuda()]) == 0
+
+
+def test_layer_backward_deterministic(moe):
+    cfg = CASES["dsv3"]
+    inp = mi.make_inputs(cfg)
+    dy = torch.ones(cfg.T, cfg.H, dtype=torch.bfloat16).cuda()
+    x, wr, w13, w2 = inp.x.cuda(), inp.w_router.cuda(), inp.w13.cuda(), inp.w2.cuda()
+    ws13, ws2, sb = to_dev(inp.ws13), to_dev(inp.ws2), to_dev(inp.sel_bias)
+    _, ex = moe.layer_forward(cfg, x, wr, w13, w2, None, sb, ws13=ws13, ws2=ws2,
+                              want=("logits", "topk_idx", "topk_gate"))
+    outs = [moe.layer_backward(cfg, x, wr, ex["logits"], ex["topk_idx"], ex["topk_gate"], w13,
+                               w2, dy, ws13=ws13, ws2=ws2) for _ in range(2)]
+    torch.cuda.synchronize()
+    for n in ("dx", "dw_router", "dw13", "dw2", "dws13", "dws2"):
+        assert torch.equal(outs[0][n], outs[1][n]), n
