@@ -1,5 +1,5 @@
 """Full-size parity: every bf16/e4m3 workload at its full size, in the launch configuration
-bench.py times (expert weights packed K-blocked, K-blocked activations inside the layer),
+bench.py times (expert weights packed K-blocked; inside the layer GEMM1 gathers its rows),
 checked against the CPU oracle on outputs it can compute one by one (sampled tokens and
 rows) and on properties that hold at any size. All GPU work goes through the C ABI; the
 oracle only ever sees seeded inputs and its own results."""
@@ -292,3 +292,79 @@ def test_full_backward_dsv3_fp8_skew(moe):
     log(f"dsv3_fp8_skew backward: dx {e_dx:.3e}, dg {e_dg:.3e}, dW (experts {experts}) "
         f"{worst:.3e}")
     assert e_dx <= TOL[mi.BF16] and e_dg <= TOL[mi.BF16] and worst <= TOL[mi.BF16]
+
+
+def test_full_layer_backward_dsv3(moe):
+    """Whole-layer backward at the DeepSeek-V3 bf16 size on the oracle's routing: dx and
+    dlogits of sampled tokens (the oracle on that sub-batch), sampled entries of dW_r (from
+    the GPU's own dlogits), the full dW13 / dW2 of the hottest and the coldest expert, and
+    sampled entries of the shared expert's weight gradients."""
+    c = full_case(moe, "dsv3_bf16")
+    cfg, inp = c["cfg"].replace(a_layout=0, w_layout=0), c["inp"]
+    T, H, F, sF = cfg.T, cfg.H, cfg.F, cfg.shared_F
+    log("dsv3_bf16: layer backward")
+    rng = np.random.default_rng(5)
+    dy = torch.from_numpy(rng.standard_normal((T, H)).astype(np.float32)).to(torch.bfloat16)
+    dev = {n: getattr(inp, n).cuda() for n in ("w13", "w2", "ws13", "ws2")}
+    g = moe.layer_backward(cfg, inp.x.cuda(), inp.w_router.cuda(),
+                           torch.from_numpy(c["logits"]).cuda(),
+                           torch.from_numpy(np.ascontiguousarray(c["idx"])).cuda(),
+                           torch.from_numpy(np.ascontiguousarray(c["gate"])).cuda(),
+                           dev["w13"], dev["w2"], dy.cuda(), ws13=dev["ws13"],
+                           ws2=dev["ws2"], want_dlogits=True)
+    torch.cuda.synchronize()
+    del dev
+    # per-token gradients on a sub-batch
+    toks = sample_tokens(c, n=16, seed=3)
+    sub = oracle.layer_backward(inp.x[toks], inp.w_router, c["logits"][toks], c["idx"][toks],
+                                inp.w13, inp.w2, dy[toks], cfg.router, cfg.route_scale,
+                                None, inp.ws13, inp.ws2)
+    e_dx = rel_err(g["dx"][torch.from_numpy(toks).cuda()].float().cpu(), sub["dx"])
+    e_dl = rel_err(g["dlogits"][torch.from_numpy(toks).cuda()].cpu(), sub["dlogits"])
+    log(f"dsv3_bf16 backward: dx {e_dx:.3e}, dlogits {e_dl:.3e} on {len(toks)} tokens")
+    assert e_dx <= 2e-2 and e_dl <= 2e-2
+    # dW_r = dl^T x on sampled entries, from the GPU's dlogits
+    dl = g["dlogits"].cpu().double().numpy()
+    X = inp.x.double().numpy()
+    es, hs = rng.integers(0, cfg.E, 32), rng.integers(0, H, 32)
+    ref = np.einsum("te,te->e", dl[:, es], X[:, hs])
+    got = g["dw_router"].float().cpu().numpy()[es, hs]
+    e_wr = float(np.max(np.abs(got - ref)) / np.max(np.abs(ref)))
+    log(f"dsv3_bf16 backward: dW_r sampled {e_wr:.3e}")
+    assert e_wr <= 2e-2
+    # the hottest and the coldest expert's weight gradients in full
+    counts = c["perm"]["counts"]
+    nz = np.nonzero(counts)[0]
+    for e in (int(np.argmax(counts)), int(nz[np.argmin(counts[nz])])):
+        t, j = np.nonzero(c["idx"] == e)
+        W13 = inp.w13[e].double().numpy()
+        W2 = inp.w2[e].double().numpy()
+        sel = np.take_along_axis(c["logits"].astype(np.float64), c["idx"].astype(np.int64), 1)
+        s = 1.0 / (1.0 + np.exp(-sel[t]))
+        gate = cfg.route_scale * s[np.arange(len(t)), j] / s.sum(1)
+        _, dw13, dw2, _ = oracle._expert_fwd_bwd(X[t], W13, W2, gate,
+                                                  dy[torch.from_numpy(t)].double().numpy())
+        e13 = rel_err(g["dw13"][e].float().cpu(), dw13)
+        e2 = rel_err(g["dw2"][e].float().cpu(), dw2)
+        log(f"dsv3_bf16 backward: expert {e} ({len(t)} rows) dW13 {e13:.3e} dW2 {e2:.3e}")
+        assert e13 <= 2e-2 and e2 <= 2e-2
+    # shared expert: sampled columns f of its hidden layer, every token
+    Ws13 = inp.ws13.double().numpy()
+    Ws2 = inp.ws2.double().numpy()
+    DY = dy.double().numpy()
+    fs, hh = rng.integers(0, sF, 4), rng.integers(0, H, 8)
+    zg, zu = X @ Ws13[fs].T, X @ Ws13[sF + fs].T                 # [T, 4]
+    da = DY @ Ws2[:, fs]                                         # [T, 4]
+    sg = 1.0 / (1.0 + np.exp(-zg))
+    hsh = zg * sg * zu
+    ref13g = (da * zu * sg * (1.0 + zg * (1.0 - sg))).T @ X[:, hh]   # [4, 8]
+    ref13u = (da * zg * sg).T @ X[:, hh]
+    ref2 = DY[:, hh].T @ hsh                                     # [8, 4]
+    got13 = g["dws13"].float().cpu().numpy()
+    got2 = g["dws2"].float().cpu().numpy()
+    for name, gv, rv in (("dWs13 gate", got13[np.ix_(fs, hh)], ref13g),
+                         ("dWs13 up", got13[np.ix_(sF + fs, hh)], ref13u),
+                         ("dWs2", got2[np.ix_(hh, fs)], ref2)):
+        err = float(np.max(np.abs(gv - rv)) / np.max(np.abs(rv)))
+        log(f"dsv3_bf16 backward: {name} sampled {err:.3e}")
+        assert err <= 2e-2
