@@ -229,6 +229,38 @@ def time_backward(moe, mi, cfg, dev, x, inp, idx, gate, w13_bf, w2_bf, reps):
             "frac_bf16_peak": round(flops / (t * 1e-3) / PEAK_MFMA["bf16"], 4)}
 
 
+def time_layer_backward(moe, mi, cfg, dev, x, wr, logits, idx, gate, w13, w2, ws13, ws2, lb,
+                        reps):
+    """The whole-layer backward (moe_layer_backward) for the forward's routing, dY ~ N(0,1)
+    seeded, bf16 row-major weights; timed on its own. Its FLOPs count the backward GEMMs only
+    (experts, shared expert, router), not the GEMM1 recompute it also runs."""
+    import torch
+    bcfg = cfg.replace(w_dtype=mi.BF16, a_layout=0, w_layout=0)
+    gen = torch.Generator().manual_seed(20261202)
+    dy = torch.randn(cfg.T, cfg.H, generator=gen).to(torch.bfloat16).to(dev)
+    lws = moe.workspace(bcfg, moe.OP_LAYER_BACKWARD, dev)
+
+    def run():
+        return moe.layer_backward(bcfg, x, wr, logits, idx, gate, w13, w2, dy, logit_bias=lb,
+                                  ws13=ws13, ws2=ws2, ws=lws)
+    run()
+    torch.cuda.synchronize()
+    t = 0.0
+    for _ in range(max(1, reps)):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        run()
+        b.record()
+        torch.cuda.synchronize()
+        t += a.elapsed_time(b) / max(1, reps)
+    A = cfg.T * cfg.k
+    flops = 12 * (A * cfg.H * cfg.F + cfg.T * cfg.H * cfg.shared_F) + 4 * cfg.T * cfg.E * cfg.H
+    return {"what": "whole-layer backward (experts, shared expert, gates, router; recomputes "
+                    "GEMM1), bf16", "ms": round(t, 4),
+            "TFLOP/s": round(flops / (t * 1e-3) / 1e12, 1),
+            "tokens/s": round(cfg.T / (t * 1e-3), 1)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -237,6 +269,8 @@ def main():
     ap.add_argument("--workload", default="dsv3_bf16")
     ap.add_argument("--cpu-sample", type=int, default=1024)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-layer-bwd", action="store_true",
+                    help="skip timing the whole-layer backward")
     ap.add_argument("--bwd-reps", type=int, default=5,
                     help="timed repetitions of the backward (workloads that have one)")
     ap.add_argument("--calib-copy-gib", type=float, default=0.0,
@@ -286,14 +320,15 @@ def main():
     ws13, ws2, lb, sb = g(inp.ws13), g(inp.ws2), g(inp.logit_bias), g(inp.sel_bias)
     fp8 = cfg.w_dtype == mi.E4M3
     sc = dict(w13_scales=None, w2_scales=None, ws13_scales=None, ws2_scales=None)
-    w13_bf, w2_bf = w13, w2
+    w13_bf, w2_bf, ws13_bf, ws2_bf = w13, w2, ws13, ws2     # row-major bf16 (backward)
+    layer_bwd = (not args.no_layer_bwd and cfg.act_dtype == mi.BF16 and cfg.E % 128 == 0)
     if fp8:       # e4m3 weights with 128 x 128 block scales, quantised once (like loading)
         w13, sc["w13_scales"] = moe.quantize_e4m3(w13, 128)
         w2, sc["w2_scales"] = moe.quantize_e4m3(w2, 128)
         ws13, sc["ws13_scales"] = moe.quantize_e4m3(ws13, 128)
         ws2, sc["ws2_scales"] = moe.quantize_e4m3(ws2, 128)
-        if not cfg.backward:
-            w13_bf = w2_bf = None
+        if not cfg.backward and not layer_bwd:
+            w13_bf = w2_bf = ws13_bf = ws2_bf = None
     if cfg.w_layout:
         pk = lambda t: None if t is None else moe.pack_kblock(t)  # noqa: E731
         w13, w2, ws13, ws2 = pk(w13), pk(w2), pk(ws13), pk(ws2)
@@ -344,7 +379,7 @@ def main():
         ", ".join(f"{k} {v:.3f}" for k, v in times.items()))
 
     _, ex = moe.layer_forward(cfg, x, wr, w13, w2, lb, sb, None, ws13=ws13, ws2=ws2, y=y,
-                              ws=ws, want=("counts", "topk_idx", "topk_gate"), **sc)
+                              ws=ws, want=("counts", "topk_idx", "topk_gate", "logits"), **sc)
     cnt = ex["counts"].cpu().double()
     idx, gate = ex["topk_idx"], ex["topk_gate"]
     torch.cuda.synchronize()
@@ -353,6 +388,13 @@ def main():
     if cfg.backward:
         backward = time_backward(moe, mi, cfg, dev, x, inp, idx, gate, w13_bf, w2_bf,
                                  args.bwd_reps)
+    layer_backward = None
+    if layer_bwd:
+        del ws
+        torch.cuda.empty_cache()
+        layer_backward = time_layer_backward(moe, mi, cfg, dev, x, wr, ex["logits"], idx, gate,
+                                             w13_bf, w2_bf, ws13_bf, ws2_bf, lb,
+                                             args.bwd_reps)
     alg = algorithmic(cfg)
     dtype = {0: "fp32", 1: "bf16", 2: "e4m3"}[cfg.w_dtype]
     per_stage = {}
@@ -411,6 +453,8 @@ def main():
     }
     if backward:
         result["backward"] = backward
+    if layer_backward:
+        result["layer_backward"] = layer_backward
     if not args.no_cpu:
         log(f"[bench] cpu baseline: oracle on {args.cpu_sample} tokens ...")
         result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample)
