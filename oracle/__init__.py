@@ -59,6 +59,7 @@ def lib():
             L.orc_e4m3_encode.restype = C.c_uint8
             L.orc_e4m3_encode.argtypes = [C.c_float]
             L.orc_quant_rows.argtypes = [P, I32, I64, I32, P, P]
+            L.orc_mx_quant.argtypes = [P, I32, I64, I32, P, P]
             L.orc_quant_weight.argtypes = [P, I32, I64, I32, I32, P, P]
             L.orc_router_logits.argtypes = [P, P, I32, I32, I32, I32, P]
             L.orc_route.argtypes = [P, P, P, I32, I32, I32, I32, I32, I32, C.c_double, P, P, P]
@@ -151,6 +152,26 @@ def quant_rows(v, block: int = 128):
     s = np.empty((rows, cols // 128), np.float32)
     lib().orc_quant_rows(_p(a), dt, rows, cols, _p(q), _p(s))
     return q, s
+
+
+def mx_quant(v):
+    """MXFP8 block quantisation of [rows, cols] (or [n, rows, cols]) along the last axis,
+    32 values per block -> (codes uint8, E8M0 scale codes uint8 [..., cols / 32])."""
+    a, dt = as_np(v)
+    shape = a.shape
+    cols = shape[-1]
+    rows = int(np.prod(shape[:-1]))
+    q = np.empty(shape, np.uint8)
+    s = np.empty(shape[:-1] + (cols // 32,), np.uint8)
+    lib().orc_mx_quant(_p(a), dt, rows, cols, _p(q), _p(s))
+    return q, s
+
+
+def mx_dequant(q, s):
+    """Values of MX codes: e4m3(q) * 2^(s - 127) per 32-value block -> float64."""
+    v = e4m3_decode_array(np.asarray(q))
+    sc = np.exp2(np.asarray(s, np.float64) - 127.0)
+    return v * np.repeat(sc, 32, axis=-1)
 
 
 def quant_weight(w):

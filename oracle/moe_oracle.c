@@ -121,6 +121,38 @@ void orc_quant_rows(const void* v, int dtype, int64_t rows, int cols, uint8_t* q
     }
 }
 
+/* MX block quantisation: the MXFP8 format of the OCP Microscaling specification with E4M3
+ * elements (named on the pages as MXFP8), one block per 32 consecutive values of a row.
+ * Shared exponent X = floor(log2(amax)) - 8 (8: the exponent of E4M3's largest normal,
+ * 448 = 1.75 * 2^8), clamped to [-127, 127] and stored as the E8M0 code X + 127; elements
+ * q = e4m3(v / 2^X), nearest even, saturating at 448 (a block's largest value lands in
+ * [256, 512), so only values of [448, 512) saturate). An all-zero block has X = -127. */
+void orc_mx_quant(const void* v, int dtype, int64_t rows, int cols, uint8_t* q, uint8_t* s) {
+    init_tables();
+    int nb = cols / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int b = 0; b < nb; ++b) {
+            double amax = 0.0;
+            for (int c = b * 32; c < b * 32 + 32; ++c) {
+                double a = fabs(load(v, dtype, r * cols + c));
+                if (a > amax) amax = a;
+            }
+            int X = -127;
+            if (amax > 0.0) {
+                int e;
+                frexp(amax, &e);              /* amax = m 2^e, m in [0.5, 1) */
+                X = e - 1 - 8;
+                if (X < -127) X = -127;
+                if (X > 127) X = 127;
+            }
+            s[r * nb + b] = (uint8_t)(X + 127);
+            for (int c = b * 32; c < b * 32 + 32; ++c)
+                q[r * cols + c] = orc_e4m3_encode((float)ldexp(load(v, dtype, r * cols + c), -X));
+        }
+    }
+}
+
 /* Quantise nmat matrices [rows, cols] to e4m3 with one fp32 scale per 128 x 128 block;
  * scales are laid out [nmat, rows/128, cols/128]. */
 void orc_quant_weight(const void* w, int dtype, int64_t nmat, int rows, int cols,
