@@ -29,7 +29,7 @@ _LIB = os.path.join(_HERE, "libmoe_oracle.so")
 _lock = threading.Lock()
 _lib = None
 
-F32, BF16, E4M3 = 0, 1, 2
+F32, BF16, E4M3, MXFP8 = 0, 1, 2, 3
 SOFTMAX_TOPK, SIGMOID_GROUP_TOPK = 0, 1
 
 
@@ -116,6 +116,14 @@ def _p(a):
 
 def _f32(a):
     return None if a is None else np.ascontiguousarray(np.asarray(a, dtype=np.float32))
+
+
+def _sc(a):
+    """Block scales: fp32 (1 x 128 / 128 x 128 e4m3 scales) or uint8 E8M0 codes (MXFP8)."""
+    if a is None:
+        return None
+    a = np.asarray(a)
+    return np.ascontiguousarray(a if a.dtype == np.uint8 else a.astype(np.float32))
 
 
 def _i32(a):
@@ -270,13 +278,19 @@ def combine(y_perm, pos, shared_y=None):
 # ------------------------------------------------------------------------------------
 
 def expert_rows(x_perm, offsets, gate_perm, w13, w2, rows, x_scales=None, w13_scales=None,
-                w2_scales=None, quant_act=False, want_z=False):
+                w2_scales=None, quant_act=False, want_z=False, mx=False):
     """Expert math for selected rows of the expert-grouped buffer.
+    mx: the uint8 operands are MXFP8 codes with E8M0 scales per 1 x 32 block (else e4m3 with
+    fp32 1 x 128 / 128 x 128 scales), and quant_act quantises the activation the same way.
     Returns (z or None, act, y_perm) as float64 arrays [n, 2F], [n, F], [n, H]."""
     xa, xdt = as_np(x_perm)
     w13a, wdt = as_np(w13)
     w2a, wdt2 = as_np(w2)
     assert wdt == wdt2
+    if mx:
+        assert wdt == E4M3
+        wdt = MXFP8
+        xdt = MXFP8 if xdt == E4M3 else xdt
     if w13a.ndim == 2:
         w13a, w2a = w13a[None], w2a[None]
     E, F2, H = w13a.shape
@@ -286,9 +300,10 @@ def expert_rows(x_perm, offsets, gate_perm, w13, w2, rows, x_scales=None, w13_sc
     z = np.empty((n, 2 * F)) if want_z else None
     act = np.empty((n, F))
     y = np.empty((n, H))
-    lib().orc_expert_rows(H, F, E, _p(xa), xdt, _p(_f32(x_scales)), _p(_i32(offsets)),
+    lib().orc_expert_rows(H, F, E, _p(xa), xdt, _p(_sc(x_scales)), _p(_i32(offsets)),
                           _p(_f32(gate_perm)), _p(w13a), _p(w2a), wdt,
-                          _p(_f32(w13_scales)), _p(_f32(w2_scales)), int(quant_act),
+                          _p(_sc(w13_scales)), _p(_sc(w2_scales)),
+                          (2 if mx else 1) if quant_act else 0,
                           _p(rows), n, _p(z), _p(act), _p(y))
     return z, act, y
 
@@ -296,7 +311,9 @@ def expert_rows(x_perm, offsets, gate_perm, w13, w2, rows, x_scales=None, w13_sc
 def layer_tokens(x, topk_idx, topk_gate, w13, w2, tokens, ws13=None, ws2=None, fp8=False,
                  w13_scales=None, w2_scales=None, ws13_scales=None, ws2_scales=None,
                  fold=True):
-    """The per-token loop for selected tokens -> y [n, H] float64."""
+    """The per-token loop for selected tokens -> y [n, H] float64.
+    fp8: False; True (e4m3, 1 x 128 activation / 128 x 128 weight scales); or "mx" (MXFP8:
+    e4m3 codes with an E8M0 scale per 1 x 32 block for x, the activation and the weights)."""
     xa, xdt = as_np(x)
     T, H = xa.shape
     idx = _i32(topk_idx)
@@ -314,10 +331,14 @@ def layer_tokens(x, topk_idx, topk_gate, w13, w2, tokens, ws13=None, ws2=None, f
     tokens = _i64(tokens)
     n = tokens.shape[0]
     y = np.empty((n, H))
-    lib().orc_layer_tokens(T, H, E, k, F, sF, _p(xa), xdt, int(fp8), _p(idx),
-                           _p(_f32(topk_gate)), _p(w13a), _p(w2a), wdt, _p(_f32(w13_scales)),
-                           _p(_f32(w2_scales)), _p(s13a), _p(s2a), _p(_f32(ws13_scales)),
-                           _p(_f32(ws2_scales)), int(fold), _p(tokens), n, _p(y))
+    mode = 2 if fp8 == "mx" else int(bool(fp8))
+    if mode == 2:
+        assert wdt == E4M3
+        wdt = MXFP8
+    lib().orc_layer_tokens(T, H, E, k, F, sF, _p(xa), xdt, mode, _p(idx),
+                           _p(_f32(topk_gate)), _p(w13a), _p(w2a), wdt, _p(_sc(w13_scales)),
+                           _p(_sc(w2_scales)), _p(s13a), _p(s2a), _p(_sc(ws13_scales)),
+                           _p(_sc(ws2_scales)), int(fold), _p(tokens), n, _p(y))
     return y
 
 

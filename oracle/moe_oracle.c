@@ -23,7 +23,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_E4M3 = 2 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_E4M3 = 2, ORC_MXFP8 = 3 };
 enum { ORC_SOFTMAX_TOPK = 0, ORC_SIGMOID_GROUP_TOPK = 1 };
 
 /* ------------------------------------------------------------------------------------ */
@@ -127,6 +127,18 @@ void orc_quant_rows(const void* v, int dtype, int64_t rows, int cols, uint8_t* q
  * 448 = 1.75 * 2^8), clamped to [-127, 127] and stored as the E8M0 code X + 127; elements
  * q = e4m3(v / 2^X), nearest even, saturating at 448 (a block's largest value lands in
  * [256, 512), so only values of [448, 512) saturate). An all-zero block has X = -127. */
+static int mx_exponent(double amax) {
+    int X = -127;
+    if (amax > 0.0) {
+        int e;
+        frexp(amax, &e);                      /* amax = m 2^e, m in [0.5, 1) */
+        X = e - 1 - 8;
+        if (X < -127) X = -127;
+        if (X > 127) X = 127;
+    }
+    return X;
+}
+
 void orc_mx_quant(const void* v, int dtype, int64_t rows, int cols, uint8_t* q, uint8_t* s) {
     init_tables();
     int nb = cols / 32;
@@ -138,14 +150,7 @@ void orc_mx_quant(const void* v, int dtype, int64_t rows, int cols, uint8_t* q, 
                 double a = fabs(load(v, dtype, r * cols + c));
                 if (a > amax) amax = a;
             }
-            int X = -127;
-            if (amax > 0.0) {
-                int e;
-                frexp(amax, &e);              /* amax = m 2^e, m in [0.5, 1) */
-                X = e - 1 - 8;
-                if (X < -127) X = -127;
-                if (X > 127) X = 127;
-            }
+            int X = mx_exponent(amax);
             s[r * nb + b] = (uint8_t)(X + 127);
             for (int c = b * 32; c < b * 32 + 32; ++c)
                 q[r * cols + c] = orc_e4m3_encode((float)ldexp(load(v, dtype, r * cols + c), -X));
@@ -182,11 +187,13 @@ void orc_quant_weight(const void* w, int dtype, int64_t nmat, int rows, int cols
 }
 
 /* Value of element (r, c) of matrix m of a stacked weight [nmat, rows, cols]. For e4m3 the
- * value is the code's value times its 128 x 128 block scale. */
+ * value is the code's value times its 128 x 128 block scale (fp32, [nmat, rows/128,
+ * cols/128]); for MXFP8, times 2^(S - 127) with S the E8M0 code of its 1 x 32 block along
+ * the row ([nmat, rows, cols/32] bytes). */
 typedef struct {
     const void* p;
     int dtype;
-    const float* scales;
+    const void* scales;
     int rows, cols;
 } wmat;
 
@@ -194,8 +201,12 @@ static double wval(const wmat* w, int64_t m, int r, int c) {
     int64_t i = ((int64_t)m * w->rows + r) * (int64_t)w->cols + c;
     if (w->dtype == ORC_E4M3) {
         int nbr = w->rows / 128, nbc = w->cols / 128;
-        double sc = w->scales[((int64_t)m * nbr + r / 128) * nbc + c / 128];
+        double sc = ((const float*)w->scales)[((int64_t)m * nbr + r / 128) * nbc + c / 128];
         return g_e4m3_val[((const uint8_t*)w->p)[i]] * sc;
+    }
+    if (w->dtype == ORC_MXFP8) {
+        int e8 = ((const uint8_t*)w->scales)[((int64_t)m * w->rows + r) * (w->cols / 32) + c / 32];
+        return ldexp(g_e4m3_val[((const uint8_t*)w->p)[i]], e8 - 127);
     }
     return load(w->p, w->dtype, i);
 }
@@ -354,6 +365,19 @@ void orc_permute(const int32_t* topk_idx, const float* topk_gate, int T, int k, 
 /* Expert MLP (step "gate(e) * Expert_e(x)")                                            */
 /* ------------------------------------------------------------------------------------ */
 
+/* MXFP8 "quantise then dequantise" of one row of n values given as fp32, 1 x 32 blocks
+ * (the block rule of orc_mx_quant). */
+static void fake_mx_row(const float* v, int n, double* out) {
+    for (int b = 0; b < n / 32; ++b) {
+        double amax = 0.0;
+        for (int c = b * 32; c < b * 32 + 32; ++c)
+            if (fabs((double)v[c]) > amax) amax = fabs((double)v[c]);
+        int X = mx_exponent(amax);
+        for (int c = b * 32; c < b * 32 + 32; ++c)
+            out[c] = ldexp(g_e4m3_val[orc_e4m3_encode((float)ldexp((double)v[c], -X))], X);
+    }
+}
+
 /* SwiGLU expert without biases: Expert(x) = W2 (silu(W_gate x) * (W_up x)),
  * silu(u) = u / (1 + exp(-u)); W13 holds W_gate in rows 0..F-1 and W_up in rows F..2F-1. */
 static double silu(double u) { return u / (1.0 + exp(-u)); }
@@ -381,21 +405,29 @@ static void expert_down(const wmat* w2, int64_t m, const double* a, int H, int F
     }
 }
 
-/* In fp8 mode the activation entering the down projection is quantised per 1 x 128 block
- * after the gate fold (a rounded to fp32, then e4m3 with an fp32 scale). */
-static void quantise_act(double* a, int F, float* tmp) {
+/* In fp8 modes the activation entering the down projection is quantised after the gate
+ * fold: it is rounded to fp32, then to e4m3 with an fp32 scale per 1 x 128 block
+ * (mode 1) or with an E8M0 scale per 1 x 32 block (mode 2, MXFP8). */
+static void quantise_act(double* a, int F, float* tmp, int mode) {
     for (int f = 0; f < F; ++f) tmp[f] = (float)a[f];
-    fake_quant_row(tmp, F, a);
+    if (mode == 2) fake_mx_row(tmp, F, a);
+    else fake_quant_row(tmp, F, a);
 }
 
-/* Load one activation row as doubles: fp32/bf16 values, or e4m3 codes times their
- * 1 x 128 block scales. */
-static void load_row(const void* x, int dtype, const float* scales, int64_t row, int H,
+/* Load one activation row as doubles: fp32/bf16 values, e4m3 codes times their 1 x 128
+ * block scales (fp32), or MXFP8 codes times 2^(S - 127) of their 1 x 32 block. */
+static void load_row(const void* x, int dtype, const void* scales, int64_t row, int H,
                      double* out) {
     if (dtype == ORC_E4M3) {
         const uint8_t* q = (const uint8_t*)x + row * H;
+        const float* sc = (const float*)scales;
         for (int h = 0; h < H; ++h)
-            out[h] = g_e4m3_val[q[h]] * (double)scales[row * (H / 128) + h / 128];
+            out[h] = g_e4m3_val[q[h]] * (double)sc[row * (H / 128) + h / 128];
+    } else if (dtype == ORC_MXFP8) {
+        const uint8_t* q = (const uint8_t*)x + row * H;
+        const uint8_t* sc = (const uint8_t*)scales;
+        for (int h = 0; h < H; ++h)
+            out[h] = ldexp(g_e4m3_val[q[h]], sc[row * (H / 32) + h / 32] - 127);
     } else {
         for (int h = 0; h < H; ++h) out[h] = load(x, dtype, row * H + h);
     }
@@ -407,9 +439,9 @@ static void load_row(const void* x, int dtype, const float* scales, int64_t row,
  * (NULL means gate 1). Outputs per selected row: z [2F] (optional), the activation fed to the
  * down projection [F] (after the fp8 round trip when quant_act), and y_perm [H]. */
 void orc_expert_rows(int H, int F, int E, const void* x_perm, int x_dtype,
-                     const float* x_scales, const int32_t* offsets, const float* gate_perm,
-                     const void* w13, const void* w2, int w_dtype, const float* w13_scales,
-                     const float* w2_scales, int quant_act, const int64_t* rows,
+                     const void* x_scales, const int32_t* offsets, const float* gate_perm,
+                     const void* w13, const void* w2, int w_dtype, const void* w13_scales,
+                     const void* w2_scales, int quant_act, const int64_t* rows,
                      int64_t n_rows, double* z_out, double* act_out, double* y_out) {
     init_tables();
     wmat W13 = {w13, w_dtype, w13_scales, 2 * F, H};
@@ -429,7 +461,7 @@ void orc_expert_rows(int H, int F, int E, const void* x_perm, int x_dtype,
             double g = gate_perm ? (double)gate_perm[r] : 1.0;
             load_row(x_perm, x_dtype, x_scales, r, H, x);
             expert_hidden(&W13, e, x, H, F, g, z, a);
-            if (quant_act) quantise_act(a, F, tmp);
+            if (quant_act) quantise_act(a, F, tmp, quant_act);
             if (z_out) memcpy(z_out + i * 2 * F, z, sizeof(double) * (size_t)(2 * F));
             memcpy(act_out + i * F, a, sizeof(double) * (size_t)F);
             expert_down(&W2, e, a, H, F, y_out + i * H);
@@ -444,12 +476,13 @@ void orc_expert_rows(int H, int F, int E, const void* x_perm, int x_dtype,
  * fold = 1 computes W2 (g h); fold = 0 computes g (W2 h) (the unfolded form, kept to check
  * that the fold is a pure rearrangement). fp8 = 1: x is quantised per 1 x 128 block, the
  * weights are e4m3 codes with 128 x 128 block scales, and the folded activation is
- * quantised per 1 x 128 block before the down projection. */
+ * quantised per 1 x 128 block before the down projection. fp8 = 2 (MXFP8): the same with
+ * 1 x 32 blocks and E8M0 scales for x, the activation and the weights (w_dtype MXFP8). */
 void orc_layer_tokens(int T, int H, int E, int k, int F, int shared_F, const void* x_in,
                       int x_dtype, int fp8, const int32_t* topk_idx, const float* topk_gate,
-                      const void* w13, const void* w2, int w_dtype, const float* w13_scales,
-                      const float* w2_scales, const void* ws13, const void* ws2,
-                      const float* ws13_scales, const float* ws2_scales, int fold,
+                      const void* w13, const void* w2, int w_dtype, const void* w13_scales,
+                      const void* w2_scales, const void* ws13, const void* ws2,
+                      const void* ws13_scales, const void* ws2_scales, int fold,
                       const int64_t* tokens, int64_t n_tokens, double* y_out) {
     (void)T;
     init_tables();
@@ -471,7 +504,8 @@ void orc_layer_tokens(int T, int H, int E, int k, int F, int shared_F, const voi
             double* y = y_out + i * H;
             if (fp8) {
                 for (int h = 0; h < H; ++h) tmp[h] = (float)load(x_in, x_dtype, t * H + h);
-                fake_quant_row(tmp, H, x);
+                if (fp8 == 2) fake_mx_row(tmp, H, x);
+                else fake_quant_row(tmp, H, x);
             } else {
                 load_row(x_in, x_dtype, NULL, t, H, x);
             }
@@ -480,13 +514,13 @@ void orc_layer_tokens(int T, int H, int E, int k, int F, int shared_F, const voi
                 int e = topk_idx[t * k + j];
                 double g = (double)topk_gate[t * k + j];
                 expert_hidden(&W13, e, x, H, F, fold ? g : 1.0, z, a);
-                if (fp8) quantise_act(a, F, tmp);
+                if (fp8) quantise_act(a, F, tmp, fp8);
                 expert_down(&W2, e, a, H, F, ye);
                 for (int h = 0; h < H; ++h) y[h] += fold ? ye[h] : g * ye[h];
             }
             if (shared_F > 0) {
                 expert_hidden(&S13, 0, x, H, shared_F, 1.0, z, a);
-                if (fp8) quantise_act(a, shared_F, tmp);
+                if (fp8) quantise_act(a, shared_F, tmp, fp8);
                 expert_down(&S2, 0, a, H, shared_F, ye);
                 for (int h = 0; h < H; ++h) y[h] += ye[h];
             }
