@@ -34,7 +34,8 @@
  *    expert. moe_config.a_layout selects the layout of the expert-grouped activations
  *    (x_perm, act, a shared expert's act) and w_layout that of the expert weights
  *    (w13, w2, ws13, ws2); everything else (x, y, y_perm, z, scales) is row-major.
- *    fp8 scale tensors are fp32, row-major over blocks.
+ *    fp8 scale tensors are row-major over blocks: fp32 for MOE_E4M3, one E8M0 byte per
+ *    block for MOE_MXFP8 (scale arguments are therefore `void*`).
  *  - Calls on different streams may overlap if their outputs and workspaces are disjoint.
  */
 #ifndef MOE_AMD_H
@@ -57,7 +58,14 @@ typedef enum {
     MOE_ERR_HIP = 4            /* a HIP launch failed */
 } moe_status;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_E4M3 = 2 } moe_dtype;
+/* MOE_MXFP8: the MXFP8 format of the OCP Microscaling (MX) specification, named among the
+ * low-precision recipes of "使用 Megatron Core 大规模训练混合专家模型（MoE）" (section 3, key
+ * contributions; FP8 expert GEMMs in section 2.4): OCP E4M3 elements in blocks of 32
+ * consecutive values along K, each block with one E8M0 scale byte S (the power of two
+ * 2^(S - 127)). Quantising a block with largest magnitude amax: X = floor(log2 amax) - 8
+ * (8 = exponent of E4M3's largest normal), clamped to [-127, 127], X = -127 for an all-zero
+ * block; S = X + 127; q = e4m3_rne_saturate(v * 2^-X). */
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_E4M3 = 2, MOE_MXFP8 = 3 } moe_dtype;
 
 typedef enum { MOE_LAYOUT_ROWS = 0, MOE_LAYOUT_KBLOCK = 1 } moe_layout;
 
@@ -92,9 +100,11 @@ typedef struct {
     int32_t router;       /* moe_router */
     float route_scale;    /* gate multiplier (1 for softmax, 2.5 DeepSeek-V3 style) */
     int32_t act_dtype;    /* MOE_F32 or MOE_BF16: x, router weight, y_perm, y */
-    int32_t w_dtype;      /* expert GEMM operands: MOE_F32 (with act F32), MOE_BF16 or
+    int32_t w_dtype;      /* expert GEMM operands: MOE_F32 (with act F32), MOE_BF16,
                              MOE_E4M3 (with act BF16: 1x128 activation scales, 128x128
-                             weight scales, fp32 accumulation) */
+                             weight scales, fp32 accumulation) or MOE_MXFP8 (with act BF16
+                             and row-major layouts: 1x32 E8M0 scales along K for the
+                             activations and the weights, fp32 accumulation) */
     int32_t shared_F;     /* width of the always-on shared expert, 0 = none */
     int32_t a_layout;     /* moe_layout of x_perm / act in the standalone calls (bf16, e4m3) */
     int32_t w_layout;     /* moe_layout of the expert weights (bf16, e4m3) */
@@ -136,13 +146,15 @@ int moe_route(const moe_config* cfg, const float* logits, const float* logit_bia
  * codes and x_perm_scales [A, H/128] the scales; x_q [T, H] / x_q_scales [T, H/128]
  * optionally (may be NULL) receive the quantised x in token order (for a shared expert;
  * with a K-blocked x_perm they also let each token be quantised once and then gathered).
+ * With MOE_MXFP8, the same with 1 x 32 blocks: x_perm_scales [A, H/32] and x_q_scales
+ * [T, H/32] hold E8M0 bytes (a_layout must be row-major).
  * Otherwise x_perm has cfg->act_dtype and the scale pointers must be NULL.
  * x_perm is in cfg->a_layout; a K-blocked x_perm is written by a gather over src so that
  * every store is a contiguous kilobyte. */
 int moe_permute(const moe_config* cfg, const void* x, const int32_t* topk_idx,
                 const float* topk_gate, int32_t* counts, int32_t* offsets, int32_t* pos,
-                int32_t* src, float* gate_perm, void* x_perm, float* x_perm_scales,
-                void* x_q, float* x_q_scales, void* ws, size_t ws_bytes,
+                int32_t* src, float* gate_perm, void* x_perm, void* x_perm_scales,
+                void* x_q, void* x_q_scales, void* ws, size_t ws_bytes,
                 hipStream_t stream);
 
 /* SwiGLU experts as one grouped GEMM over the expert-grouped rows (ragged per-expert M).
@@ -154,20 +166,23 @@ int moe_permute(const moe_config* cfg, const void* x, const int32_t* topk_idx,
  * w13 [E, 2F, H] (rows 0..F-1 gate, F..2F-1 up), w2 [E, H, F]. With MOE_E4M3 weights,
  * w13_scales [E, 2F/128, H/128] and w2_scales [E, H/128, F/128] are the 128 x 128 block
  * scales, x_perm is e4m3 with x_perm_scales [A, H/128], and act is stored as e4m3 with
- * act_scales [A, F/128] (quantised per 1 x 128 after the fold); otherwise all scale
- * pointers must be NULL and act has cfg->act_dtype. y_perm has cfg->act_dtype.
+ * act_scales [A, F/128] (quantised per 1 x 128 after the fold). With MOE_MXFP8 every
+ * operand has E8M0 bytes per 1 x 32 block along K instead: x_perm_scales [A, H/32],
+ * w13_scales [E, 2F, H/32], w2_scales [E, H, F/32], act_scales [A, F/32] (act quantised per
+ * 1 x 32 after the fold), and the shared expert's likewise. Otherwise all scale pointers
+ * must be NULL and act has cfg->act_dtype. y_perm has cfg->act_dtype.
  * Shared expert (cfg->shared_F > 0): the same SwiGLU with weight 1 applied to every token
  * of x_shared [T, H] (e4m3 + x_shared_scales in fp8 mode), weights ws13 [2*shared_F, H],
  * ws2 [H, shared_F] (+ scales), output shared_y [T, H] in cfg->act_dtype. Pass NULL for
  * all shared arguments when shared_F == 0.
  * z_out [A, 2F] (optional, NULL = not saved): Z rounded to cfg->act_dtype, for a backward. */
 int moe_grouped_gemm_swiglu(const moe_config* cfg, const void* x_perm,
-                            const float* x_perm_scales, const int32_t* offsets,
-                            const float* gate_perm, const void* w13, const float* w13_scales,
-                            const void* w2, const float* w2_scales, const void* x_shared,
-                            const float* x_shared_scales, const void* ws13,
-                            const float* ws13_scales, const void* ws2,
-                            const float* ws2_scales, void* act, float* act_scales,
+                            const void* x_perm_scales, const int32_t* offsets,
+                            const float* gate_perm, const void* w13, const void* w13_scales,
+                            const void* w2, const void* w2_scales, const void* x_shared,
+                            const void* x_shared_scales, const void* ws13,
+                            const void* ws13_scales, const void* ws2,
+                            const void* ws2_scales, void* act, void* act_scales,
                             void* y_perm, void* shared_y, void* z_out, void* ws,
                             size_t ws_bytes, hipStream_t stream);
 
@@ -176,21 +191,22 @@ int moe_grouped_gemm_swiglu(const moe_config* cfg, const void* x_perm,
  * weight-gradient split of a backward.
  * moe_grouped_gemm_up:   act (and optionally z_out) from x_perm and w13; with a shared
  *                        expert, shared_act [T, shared_F] (+ shared_act_scales
- *                        [T, shared_F/128] in e4m3 mode) from x_shared and ws13.
+ *                        [T, shared_F/128] in e4m3 mode, [T, shared_F/32] E8M0 in
+ *                        MXFP8 mode) from x_shared and ws13.
  * moe_grouped_gemm_down: y_perm from act and w2; with a shared expert, shared_y from
  *                        shared_act and ws2.
  * Both need a workspace of moe_workspace_size(cfg, MOE_OP_GROUPED_GEMM) bytes. */
-int moe_grouped_gemm_up(const moe_config* cfg, const void* x_perm, const float* x_perm_scales,
+int moe_grouped_gemm_up(const moe_config* cfg, const void* x_perm, const void* x_perm_scales,
                         const int32_t* offsets, const float* gate_perm, const void* w13,
-                        const float* w13_scales, const void* x_shared,
-                        const float* x_shared_scales, const void* ws13,
-                        const float* ws13_scales, void* act, float* act_scales,
-                        void* shared_act, float* shared_act_scales, void* z_out, void* ws,
+                        const void* w13_scales, const void* x_shared,
+                        const void* x_shared_scales, const void* ws13,
+                        const void* ws13_scales, void* act, void* act_scales,
+                        void* shared_act, void* shared_act_scales, void* z_out, void* ws,
                         size_t ws_bytes, hipStream_t stream);
-int moe_grouped_gemm_down(const moe_config* cfg, const void* act, const float* act_scales,
-                          const int32_t* offsets, const void* w2, const float* w2_scales,
-                          const void* shared_act, const float* shared_act_scales,
-                          const void* ws2, const float* ws2_scales, void* y_perm,
+int moe_grouped_gemm_down(const moe_config* cfg, const void* act, const void* act_scales,
+                          const int32_t* offsets, const void* w2, const void* w2_scales,
+                          const void* shared_act, const void* shared_act_scales,
+                          const void* ws2, const void* ws2_scales, void* y_perm,
                           void* shared_y, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Unpermute / combine: y[t, :] = sum_{j<k} y_perm[pos[t*k+j], :] (+ shared_y[t, :]),
@@ -210,9 +226,9 @@ int moe_unpermute_combine(const moe_config* cfg, const void* y_perm, const int32
  * topk_gate_out [T, k], counts_out [E]. */
 int moe_layer_forward(const moe_config* cfg, const void* x, const void* w_router,
                       const float* logit_bias, const float* sel_bias, const float* logits_in,
-                      const void* w13, const float* w13_scales, const void* w2,
-                      const float* w2_scales, const void* ws13, const float* ws13_scales,
-                      const void* ws2, const float* ws2_scales, void* y, float* logits_out,
+                      const void* w13, const void* w13_scales, const void* w2,
+                      const void* w2_scales, const void* ws13, const void* ws13_scales,
+                      const void* ws2, const void* ws2_scales, void* y, float* logits_out,
                       int32_t* topk_idx_out, float* topk_gate_out, int32_t* counts_out,
                       void* ws, size_t ws_bytes, hipStream_t stream);
 
@@ -295,6 +311,14 @@ int moe_pack_kblock(const void* in, int64_t n_mat, int32_t rows, int32_t cols,
 int moe_quantize_e4m3(const void* in, int32_t in_dtype, int64_t n_mat, int32_t rows,
                       int32_t cols, int32_t block_rows, int32_t block_cols, uint8_t* q,
                       float* scales, hipStream_t stream);
+
+/* MXFP8 quantisation (see MOE_MXFP8) of a row-major [rows, cols] matrix (bf16 or fp32
+ * input; stacked weights [E, N, K] pass rows = E * N): 32-value blocks along each row.
+ * q [rows, cols] uint8 e4m3 codes, scales [rows, cols/32] E8M0 bytes. cols must be a
+ * multiple of 32. (MXFP8 recipe: "使用 Megatron Core 大规模训练混合专家模型（MoE）",
+ * section 3.) */
+int moe_quantize_mx(const void* in, int32_t in_dtype, int64_t rows, int32_t cols, uint8_t* q,
+                    uint8_t* scales, hipStream_t stream);
 
 #ifdef __cplusplus
 }

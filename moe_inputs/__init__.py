@@ -35,7 +35,7 @@ BASE_SEED = 20261202
 
 TAG_X, TAG_WR, TAG_SELB, TAG_W13, TAG_W2, TAG_WS13, TAG_WS2, TAG_DY, TAG_ZIPF = range(9)
 
-F32, BF16, E4M3 = 0, 1, 2          # dtype codes shared with the C interfaces
+F32, BF16, E4M3, MXFP8 = 0, 1, 2, 3   # dtype codes shared with the C interfaces
 SOFTMAX_TOPK, SIGMOID_GROUP_TOPK = 0, 1
 
 
@@ -71,7 +71,9 @@ class MoEConfig:
 
 
 # The five workloads: a tiny fp32 layer and layers shaped like Mixtral-8x7B,
-# Qwen3-235B-A22B and DeepSeek-V3 (bf16, and fp8 with a skewed expert load).
+# Qwen3-235B-A22B and DeepSeek-V3 (bf16, and fp8 with a skewed expert load); plus the
+# DeepSeek-V3 bf16 layer with MXFP8 expert GEMMs (the same seed family, hence the same x,
+# router and weights as the bf16 layer: only the expert GEMMs' number format differs).
 CONFIGS = {
     "tiny_fp32": MoEConfig("tiny_fp32", 0, T=256, H=128, E=8, k=2, F=256,
                            act_dtype=F32, w_dtype=F32),
@@ -84,6 +86,9 @@ CONFIGS = {
                                router=SIGMOID_GROUP_TOPK, n_groups=8, topk_groups=4,
                                route_scale=2.5, shared_F=2048, w_dtype=E4M3,
                                zipf_alpha=1.2, backward=True),
+    "dsv3_mxfp8": MoEConfig("dsv3_mxfp8", 3, T=8192, H=7168, E=256, k=8, F=2048,
+                            router=SIGMOID_GROUP_TOPK, n_groups=8, topk_groups=4,
+                            route_scale=2.5, shared_F=2048, w_dtype=MXFP8),
 }
 
 

@@ -22,7 +22,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_amd.so")
 
-F32, BF16, E4M3 = 0, 1, 2
+F32, BF16, E4M3, MXFP8 = 0, 1, 2, 3
 SOFTMAX_TOPK, SIGMOID_GROUP_TOPK = 0, 1
 LAYOUT_ROWS, LAYOUT_KBLOCK = 0, 1
 OP_PERMUTE, OP_GROUPED_GEMM, OP_LAYER_FORWARD, OP_GROUPED_GEMM_BWD, OP_LAYER_BACKWARD = \
@@ -70,6 +70,7 @@ _SIGS = {
     "moe_layer_forward": [CFG, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
     "moe_grouped_gemm_swiglu_bwd": [CFG, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
     "moe_quantize_e4m3": [P, I32, I64, I32, I32, I32, I32, P, P, P],
+    "moe_quantize_mx": [P, I32, I64, I32, P, P, P],
     "moe_pack_kblock": [P, I64, I32, I32, I32, P, P],
     "moe_set_stage_events": [P, I32],
     "moe_layer_backward": [CFG, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
@@ -122,15 +123,37 @@ def _ptr(t, dtype=None, shape=None, name="tensor"):
 
 
 def torch_dtype(code: int):
-    return {F32: torch.float32, BF16: torch.bfloat16, E4M3: torch.uint8}[code]
+    return {F32: torch.float32, BF16: torch.bfloat16, E4M3: torch.uint8, MXFP8: torch.uint8}[code]
 
 
 def act_torch_dtype(cfg):
     return torch_dtype(cfg.act_dtype)
 
 
+def is_fp8(cfg):
+    return cfg.w_dtype in (E4M3, MXFP8)
+
+
 def gemm_torch_dtype(cfg):
-    return torch.uint8 if cfg.w_dtype == E4M3 else act_torch_dtype(cfg)
+    return torch.uint8 if is_fp8(cfg) else act_torch_dtype(cfg)
+
+
+def act_scale_spec(cfg, rows, cols):
+    """(dtype, shape) of the block scales of an fp8 activation [rows, cols]."""
+    if cfg.w_dtype == MXFP8:
+        return torch.uint8, (rows, cols // 32)
+    return torch.float32, (rows, cols // 128)
+
+
+def weight_scale_spec(cfg, lead, rows, cols):
+    """(dtype, shape) of the block scales of fp8 weights lead + [rows, cols]."""
+    if cfg.w_dtype == MXFP8:
+        return torch.uint8, tuple(lead) + (rows, cols // 32)
+    return torch.float32, tuple(lead) + (rows // 128, cols // 128)
+
+
+def _psc(t, spec, name):
+    return _ptr(t, spec[0], spec[1], name)
 
 
 def workspace_size(cfg, op: int) -> int:
@@ -181,7 +204,9 @@ def permute(cfg, x, topk_idx, topk_gate, want_x_q=False, ws=None, stream=None):
     dev = x.device
     T, H, E, k = cfg.T, cfg.H, cfg.E, cfg.k
     A = T * k
-    fp8 = cfg.w_dtype == E4M3
+    fp8 = is_fp8(cfg)
+    xsd, xss = act_scale_spec(cfg, A, H)
+    qsd, qss = act_scale_spec(cfg, T, H)
     out = dict(
         counts=torch.empty(E, dtype=torch.int32, device=dev),
         offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
@@ -189,10 +214,9 @@ def permute(cfg, x, topk_idx, topk_gate, want_x_q=False, ws=None, stream=None):
         src=torch.empty(A, dtype=torch.int32, device=dev),
         gate_perm=torch.empty(A, dtype=torch.float32, device=dev),
         x_perm=torch.empty(A, H, dtype=gemm_torch_dtype(cfg), device=dev),
-        x_perm_scales=torch.empty(A, H // 128, dtype=torch.float32, device=dev) if fp8 else None,
+        x_perm_scales=torch.empty(xss, dtype=xsd, device=dev) if fp8 else None,
         x_q=torch.empty(T, H, dtype=torch.uint8, device=dev) if (fp8 and want_x_q) else None,
-        x_q_scales=(torch.empty(T, H // 128, dtype=torch.float32, device=dev)
-                    if (fp8 and want_x_q) else None),
+        x_q_scales=torch.empty(qss, dtype=qsd, device=dev) if (fp8 and want_x_q) else None,
     )
     if ws is None:
         ws = workspace(cfg, OP_PERMUTE, dev)
@@ -216,12 +240,13 @@ def grouped_gemm_swiglu(cfg, x_perm, offsets, gate_perm, w13, w2, x_perm_scales=
     A = T * k
     gd = gemm_torch_dtype(cfg)
     ad = act_torch_dtype(cfg)
-    fp8 = cfg.w_dtype == E4M3
+    fp8 = is_fp8(cfg)
     sF = cfg.shared_F
     if out is None:
+        asd, ass = act_scale_spec(cfg, A, F)
         out = dict(
             act=torch.empty(A, F, dtype=gd, device=dev),
-            act_scales=torch.empty(A, F // 128, dtype=torch.float32, device=dev) if fp8 else None,
+            act_scales=torch.empty(ass, dtype=asd, device=dev) if fp8 else None,
             y_perm=torch.empty(A, H, dtype=ad, device=dev),
             shared_y=torch.empty(T, H, dtype=ad, device=dev) if sF else None,
             z=torch.empty(A, 2 * F, dtype=ad, device=dev) if save_z else None,
@@ -231,19 +256,19 @@ def grouped_gemm_swiglu(cfg, x_perm, offsets, gate_perm, w13, w2, x_perm_scales=
     c = make_config(cfg)
     _check("moe_grouped_gemm_swiglu", _lib.moe_grouped_gemm_swiglu(
         C.byref(c), _ptr(x_perm, gd, (A, H), "x_perm"),
-        _ptr(x_perm_scales, torch.float32, (A, H // 128), "x_perm_scales"),
+        _psc(x_perm_scales, act_scale_spec(cfg, A, H), "x_perm_scales"),
         _ptr(offsets, torch.int32, (E + 1,), "offsets"),
         _ptr(gate_perm, torch.float32, (A,), "gate_perm"),
         _ptr(w13, gd, (E, 2 * F, H), "w13"),
-        _ptr(w13_scales, torch.float32, (E, 2 * F // 128, H // 128), "w13_scales"),
+        _psc(w13_scales, weight_scale_spec(cfg, (E,), 2 * F, H), "w13_scales"),
         _ptr(w2, gd, (E, H, F), "w2"),
-        _ptr(w2_scales, torch.float32, (E, H // 128, F // 128), "w2_scales"),
+        _psc(w2_scales, weight_scale_spec(cfg, (E,), H, F), "w2_scales"),
         _ptr(x_shared, gd, (T, H), "x_shared"),
-        _ptr(x_shared_scales, torch.float32, (T, H // 128), "x_shared_scales"),
+        _psc(x_shared_scales, act_scale_spec(cfg, T, H), "x_shared_scales"),
         _ptr(ws13, gd, (2 * sF, H), "ws13"),
-        _ptr(ws13_scales, torch.float32, (2 * sF // 128, H // 128), "ws13_scales"),
+        _psc(ws13_scales, weight_scale_spec(cfg, (), 2 * sF, H), "ws13_scales"),
         _ptr(ws2, gd, (H, sF), "ws2"),
-        _ptr(ws2_scales, torch.float32, (H // 128, sF // 128), "ws2_scales"),
+        _psc(ws2_scales, weight_scale_spec(cfg, (), H, sF), "ws2_scales"),
         _ptr(out["act"]), _ptr(out["act_scales"]), _ptr(out["y_perm"]), _ptr(out["shared_y"]),
         _ptr(out["z"]), _ptr(ws), ws.numel(), _stream(stream)))
     return out
@@ -263,18 +288,18 @@ def grouped_gemm_up(cfg, x_perm, offsets, gate_perm, w13, act, x_perm_scales=Non
     c = make_config(cfg)
     _check("moe_grouped_gemm_up", _lib.moe_grouped_gemm_up(
         C.byref(c), _ptr(x_perm, gd, (A, H), "x_perm"),
-        _ptr(x_perm_scales, torch.float32, (A, H // 128), "x_perm_scales"),
+        _psc(x_perm_scales, act_scale_spec(cfg, A, H), "x_perm_scales"),
         _ptr(offsets, torch.int32, (E + 1,), "offsets"),
         _ptr(gate_perm, torch.float32, (A,), "gate_perm"),
         _ptr(w13, gd, (E, 2 * F, H), "w13"),
-        _ptr(w13_scales, torch.float32, (E, 2 * F // 128, H // 128), "w13_scales"),
+        _psc(w13_scales, weight_scale_spec(cfg, (E,), 2 * F, H), "w13_scales"),
         _ptr(x_shared, gd, (T, H), "x_shared"),
-        _ptr(x_shared_scales, torch.float32, (T, H // 128), "x_shared_scales"),
+        _psc(x_shared_scales, act_scale_spec(cfg, T, H), "x_shared_scales"),
         _ptr(ws13, gd, (2 * sF, H), "ws13"),
-        _ptr(ws13_scales, torch.float32, (2 * sF // 128, H // 128), "ws13_scales"),
-        _ptr(act, gd, (A, F), "act"), _ptr(act_scales, torch.float32, (A, F // 128), "act_scales"),
+        _psc(ws13_scales, weight_scale_spec(cfg, (), 2 * sF, H), "ws13_scales"),
+        _ptr(act, gd, (A, F), "act"), _psc(act_scales, act_scale_spec(cfg, A, F), "act_scales"),
         _ptr(shared_act, gd, (T, sF), "shared_act"),
-        _ptr(shared_act_scales, torch.float32, (T, sF // 128), "shared_act_scales"),
+        _psc(shared_act_scales, act_scale_spec(cfg, T, sF), "shared_act_scales"),
         _ptr(z, ad, (A, 2 * F), "z"), _ptr(ws), ws.numel(), _stream(stream)))
 
 
@@ -291,14 +316,14 @@ def grouped_gemm_down(cfg, act, offsets, w2, y_perm, act_scales=None, w2_scales=
     c = make_config(cfg)
     _check("moe_grouped_gemm_down", _lib.moe_grouped_gemm_down(
         C.byref(c), _ptr(act, gd, (A, F), "act"),
-        _ptr(act_scales, torch.float32, (A, F // 128), "act_scales"),
+        _psc(act_scales, act_scale_spec(cfg, A, F), "act_scales"),
         _ptr(offsets, torch.int32, (E + 1,), "offsets"),
         _ptr(w2, gd, (E, H, F), "w2"),
-        _ptr(w2_scales, torch.float32, (E, H // 128, F // 128), "w2_scales"),
+        _psc(w2_scales, weight_scale_spec(cfg, (E,), H, F), "w2_scales"),
         _ptr(shared_act, gd, (T, sF), "shared_act"),
-        _ptr(shared_act_scales, torch.float32, (T, sF // 128), "shared_act_scales"),
+        _psc(shared_act_scales, act_scale_spec(cfg, T, sF), "shared_act_scales"),
         _ptr(ws2, gd, (H, sF), "ws2"),
-        _ptr(ws2_scales, torch.float32, (H // 128, sF // 128), "ws2_scales"),
+        _psc(ws2_scales, weight_scale_spec(cfg, (), H, sF), "ws2_scales"),
         _ptr(y_perm, ad, (A, H), "y_perm"), _ptr(shared_y, ad, (T, H), "shared_y"),
         _ptr(ws), ws.numel(), _stream(stream)))
 
@@ -346,13 +371,13 @@ def layer_forward(cfg, x, w_router, w13, w2, logit_bias=None, sel_bias=None, log
         _ptr(sel_bias, torch.float32, (E,), "sel_bias"),
         _ptr(logits_in, torch.float32, (T, E), "logits_in"),
         _ptr(w13, gd, (E, 2 * F, H), "w13"),
-        _ptr(w13_scales, torch.float32, (E, 2 * F // 128, H // 128), "w13_scales"),
+        _psc(w13_scales, weight_scale_spec(cfg, (E,), 2 * F, H), "w13_scales"),
         _ptr(w2, gd, (E, H, F), "w2"),
-        _ptr(w2_scales, torch.float32, (E, H // 128, F // 128), "w2_scales"),
+        _psc(w2_scales, weight_scale_spec(cfg, (E,), H, F), "w2_scales"),
         _ptr(ws13, gd, (2 * sF, H), "ws13"),
-        _ptr(ws13_scales, torch.float32, (2 * sF // 128, H // 128), "ws13_scales"),
+        _psc(ws13_scales, weight_scale_spec(cfg, (), 2 * sF, H), "ws13_scales"),
         _ptr(ws2, gd, (H, sF), "ws2"),
-        _ptr(ws2_scales, torch.float32, (H // 128, sF // 128), "ws2_scales"),
+        _psc(ws2_scales, weight_scale_spec(cfg, (), H, sF), "ws2_scales"),
         _ptr(y, ad, (T, H), "y"), _ptr(extras.get("logits")), _ptr(extras.get("topk_idx")),
         _ptr(extras.get("topk_gate")), _ptr(extras.get("counts")), _ptr(ws), ws.numel(),
         _stream(stream)))
@@ -427,6 +452,20 @@ def quantize_e4m3(t, block_rows: int, stream=None):
     _check("moe_quantize_e4m3", _lib.moe_quantize_e4m3(
         _ptr(t, name="input"), dt, n, rows, cols, block_rows, 128, _ptr(q), _ptr(s),
         _stream(stream)))
+    return q, s
+
+
+def quantize_mx(t, stream=None):
+    """MXFP8 quantisation along the last axis of a bf16 / fp32 tensor (32-value blocks) ->
+    (codes uint8 of the same shape, E8M0 scale codes uint8 [..., cols/32])."""
+    dt = {torch.float32: F32, torch.bfloat16: BF16}[t.dtype]
+    shape = tuple(t.shape)
+    cols = shape[-1]
+    rows = t.numel() // cols
+    q = torch.empty(shape, dtype=torch.uint8, device=t.device)
+    s = torch.empty(shape[:-1] + (cols // 32,), dtype=torch.uint8, device=t.device)
+    _check("moe_quantize_mx", _lib.moe_quantize_mx(
+        _ptr(t, name="input"), dt, rows, cols, _ptr(q), _ptr(s), _stream(stream)))
     return q, s
 
 

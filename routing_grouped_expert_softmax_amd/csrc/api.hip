@@ -24,6 +24,15 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 size_t elem_bytes(int dtype) { return dtype == MOE_F32 ? 4 : dtype == MOE_BF16 ? 2 : 1; }
 
+// fp8 expert operands: e4m3 with fp32 block scales, or MXFP8 with E8M0 block scales
+bool is_fp8(int w_dtype) { return w_dtype == MOE_E4M3 || w_dtype == MOE_MXFP8; }
+
+// Bytes of the block scales of a [rows, cols] fp8 activation: fp32 per 1 x 128 (e4m3) or one
+// E8M0 byte per 1 x 32 (MXFP8)
+size_t act_scale_bytes(int w_dtype, size_t rows, size_t cols) {
+    return w_dtype == MOE_MXFP8 ? rows * (cols / 32) : rows * (cols / 128) * 4;
+}
+
 // Validation of the configuration itself (shapes and numerics).
 int check_cfg(const moe_config* c) {
     if (!c) return MOE_ERR_INVALID_ARG;
@@ -53,7 +62,8 @@ int check_cfg(const moe_config* c) {
         if (c->w_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
         if (c->H % 64 || c->F % 32 || (c->shared_F && c->shared_F % 32)) return MOE_ERR_UNSUPPORTED;
     } else if (c->act_dtype == MOE_BF16) {
-        if (c->w_dtype != MOE_BF16 && c->w_dtype != MOE_E4M3) return MOE_ERR_UNSUPPORTED;
+        if (c->w_dtype != MOE_BF16 && !is_fp8(c->w_dtype)) return MOE_ERR_UNSUPPORTED;
+        if (c->w_dtype == MOE_MXFP8 && (c->a_layout || c->w_layout)) return MOE_ERR_UNSUPPORTED;
         if (c->H % 256 || c->F % 128 || (c->shared_F && c->shared_F % 128))
             return MOE_ERR_UNSUPPORTED;
     } else {
@@ -89,10 +99,10 @@ size_t sched_ws_bytes(const moe_config* c);
 size_t gemm_ws_bytes(const moe_config* c) {
     size_t shared = 0;
     if (c->shared_F) {
-        const size_t eb = c->w_dtype == MOE_E4M3 ? 1 : elem_bytes(c->act_dtype);
+        const bool q8 = is_fp8(c->w_dtype);
+        const size_t eb = q8 ? 1 : elem_bytes(c->act_dtype);
         shared += align_up((size_t)c->T * c->shared_F * eb);                // shared act
-        if (c->w_dtype == MOE_E4M3)
-            shared += align_up((size_t)c->T * (c->shared_F / 128) * 4);      // its scales
+        if (q8) shared += align_up(act_scale_bytes(c->w_dtype, c->T, c->shared_F));   // scales
     }
     return align_up(sched_ws_bytes(c)) + shared;
 }
@@ -107,11 +117,11 @@ struct LayerWs {
     int32_t* src;
     float* gate_perm;
     void* x_perm;
-    float* x_perm_scales;
+    void* x_perm_scales;
     void* x_q;
-    float* x_q_scales;
+    void* x_q_scales;
     void* act;
-    float* act_scales;
+    void* act_scales;
     void* y_perm;
     void* shared_y;
     void* scratch;       // permute / grouped-GEMM scratch (used one after the other)
@@ -122,7 +132,8 @@ LayerWs carve_layer(const moe_config* c, void* ws) {
     LayerWs L = {};
     Carve cv(ws);
     const size_t T = c->T, H = c->H, E = c->E, k = c->k, F = c->F, A = T * k;
-    const bool fp8 = c->w_dtype == MOE_E4M3;
+    const bool fp8 = is_fp8(c->w_dtype);
+    const int wd = c->w_dtype;
     const size_t ab = elem_bytes(c->act_dtype);
     const size_t gb = fp8 ? 1 : ab;       // GEMM operand bytes
     L.logits = (float*)cv.take(T * E * 4);
@@ -134,11 +145,11 @@ LayerWs carve_layer(const moe_config* c, void* ws) {
     L.src = (int32_t*)cv.take(A * 4);
     L.gate_perm = (float*)cv.take(A * 4);
     L.x_perm = cv.take(A * H * gb);
-    L.x_perm_scales = fp8 ? (float*)cv.take(A * (H / 128) * 4) : nullptr;
-    L.x_q = fp8 ? cv.take(T * H) : nullptr;                // token-order e4m3 x (the
-    L.x_q_scales = fp8 ? (float*)cv.take(T * (H / 128) * 4) : nullptr;   // gather's source)
+    L.x_perm_scales = fp8 ? cv.take(act_scale_bytes(wd, A, H)) : nullptr;
+    L.x_q = fp8 ? cv.take(T * H) : nullptr;                // token-order fp8 x (the
+    L.x_q_scales = fp8 ? cv.take(act_scale_bytes(wd, T, H)) : nullptr;   // gather's source)
     L.act = cv.take(A * F * gb);
-    L.act_scales = fp8 ? (float*)cv.take(A * (F / 128) * 4) : nullptr;
+    L.act_scales = fp8 ? cv.take(act_scale_bytes(wd, A, F)) : nullptr;
     L.y_perm = cv.take(A * H * ab);
     L.shared_y = c->shared_F ? cv.take(T * H * ab) : nullptr;
     size_t p = moe::permute_ws_bytes(c->T, c->k, c->E);
@@ -214,11 +225,11 @@ size_t sched_ws_bytes(const moe_config* c) {
 // GEMM1 of the experts (gate/up projection + SwiGLU with the gate folded in): routed
 // experts as segment 0 and, when shared_F == F, the shared expert as segment 1 of the same
 // launch; a shared expert of another width gets its own launch.
-int run_up(const moe_config* c, int a_kb, const void* x_perm, const float* x_perm_scales,
+int run_up(const moe_config* c, int a_kb, const void* x_perm, const void* x_perm_scales,
            const int32_t* offsets, const float* gate_perm, const void* w13,
-           const float* w13_scales, const void* x_shared, const float* x_shared_scales,
-           const void* ws13, const float* ws13_scales, void* act, float* act_scales,
-           void* shared_act, float* shared_act_scales, void* z_out, void* sched,
+           const void* w13_scales, const void* x_shared, const void* x_shared_scales,
+           const void* ws13, const void* ws13_scales, void* act, void* act_scales,
+           void* shared_act, void* shared_act_scales, void* z_out, void* sched,
            hipStream_t stream, const int32_t* a_rows = nullptr) {
     const int dt = c->w_dtype;
     const int A = c->T * c->k;
@@ -240,10 +251,10 @@ int run_up(const moe_config* c, int a_kb, const void* x_perm, const float* x_per
 }
 
 // GEMM2 of the experts (down projection), same segment layout as run_up.
-int run_down(const moe_config* c, int a_kb, const void* act, const float* act_scales,
-             const int32_t* offsets, const void* w2, const float* w2_scales,
-             const void* shared_act, const float* shared_act_scales, const void* ws2,
-             const float* ws2_scales, void* y_perm, void* shared_y, void* sched,
+int run_down(const moe_config* c, int a_kb, const void* act, const void* act_scales,
+             const int32_t* offsets, const void* w2, const void* w2_scales,
+             const void* shared_act, const void* shared_act_scales, const void* ws2,
+             const void* ws2_scales, void* y_perm, void* shared_y, void* sched,
              hipStream_t stream) {
     const int dt = c->w_dtype;
     const int A = c->T * c->k;
@@ -265,21 +276,21 @@ int run_down(const moe_config* c, int a_kb, const void* act, const float* act_sc
 }
 
 // Both GEMMs; the shared expert's activation lives in the workspace after the schedule.
-int run_experts(const moe_config* c, int a_kb, const void* x_perm, const float* x_perm_scales,
+int run_experts(const moe_config* c, int a_kb, const void* x_perm, const void* x_perm_scales,
                 const int32_t* offsets, const float* gate_perm, const void* w13,
-                const float* w13_scales, const void* w2, const float* w2_scales,
-                const void* x_shared, const float* x_shared_scales, const void* ws13,
-                const float* ws13_scales, const void* ws2, const float* ws2_scales, void* act,
-                float* act_scales, void* y_perm, void* shared_y, void* z_out, void* ws,
+                const void* w13_scales, const void* w2, const void* w2_scales,
+                const void* x_shared, const void* x_shared_scales, const void* ws13,
+                const void* ws13_scales, const void* ws2, const void* ws2_scales, void* act,
+                void* act_scales, void* y_perm, void* shared_y, void* z_out, void* ws,
                 hipStream_t stream, int mid_mark = -1, const int32_t* a_rows = nullptr) {
     Carve cv(ws);
     void* sched = cv.take(sched_ws_bytes(c));
     void* sh_act = nullptr;
-    float* sh_act_scales = nullptr;
+    void* sh_act_scales = nullptr;
     if (c->shared_F) {
-        const bool fp8 = c->w_dtype == MOE_E4M3;
+        const bool fp8 = is_fp8(c->w_dtype);
         sh_act = cv.take((size_t)c->T * c->shared_F * (fp8 ? 1 : elem_bytes(c->act_dtype)));
-        if (fp8) sh_act_scales = (float*)cv.take((size_t)c->T * (c->shared_F / 128) * 4);
+        if (fp8) sh_act_scales = cv.take(act_scale_bytes(c->w_dtype, c->T, c->shared_F));
     }
     int st = run_up(c, a_kb, x_perm, x_perm_scales, offsets, gate_perm, w13, w13_scales, x_shared,
                     x_shared_scales, ws13, ws13_scales, act, act_scales, sh_act, sh_act_scales,
@@ -352,19 +363,19 @@ int moe_route(const moe_config* cfg, const float* logits, const float* logit_bia
 
 int moe_permute(const moe_config* cfg, const void* x, const int32_t* topk_idx,
                 const float* topk_gate, int32_t* counts, int32_t* offsets, int32_t* pos,
-                int32_t* src, float* gate_perm, void* x_perm, float* x_perm_scales, void* x_q,
-                float* x_q_scales, void* ws, size_t ws_bytes, hipStream_t stream) {
+                int32_t* src, float* gate_perm, void* x_perm, void* x_perm_scales, void* x_q,
+                void* x_q_scales, void* ws, size_t ws_bytes, hipStream_t stream) {
     int st = check_cfg(cfg);
     if (st) return st;
     if (!x || !topk_idx || !topk_gate || !counts || !offsets || !pos || !src || !gate_perm ||
         !x_perm || !ws)
         return MOE_ERR_INVALID_ARG;
-    const bool fp8 = cfg->w_dtype == MOE_E4M3;
+    const bool fp8 = is_fp8(cfg->w_dtype);
     if (fp8 != (x_perm_scales != nullptr)) return MOE_ERR_INVALID_ARG;
     if (!fp8 && (x_q || x_q_scales)) return MOE_ERR_INVALID_ARG;
     if ((x_q == nullptr) != (x_q_scales == nullptr)) return MOE_ERR_INVALID_ARG;
     if (ws_bytes < moe::permute_ws_bytes(cfg->T, cfg->k, cfg->E)) return MOE_ERR_WORKSPACE;
-    const int mode = fp8 ? 2 : (cfg->act_dtype == MOE_F32 ? 0 : 1);
+    const int mode = cfg->w_dtype == MOE_MXFP8 ? 3 : fp8 ? 2 : (cfg->act_dtype == MOE_F32 ? 0 : 1);
     return hip_status(moe::launch_permute(mode, cfg->a_layout, x, topk_idx, topk_gate, cfg->T,
                                           cfg->H, cfg->E, cfg->k, counts, offsets, pos, src,
                                           gate_perm, x_perm, x_perm_scales, x_q, x_q_scales, ws,
@@ -372,19 +383,19 @@ int moe_permute(const moe_config* cfg, const void* x, const int32_t* topk_idx,
 }
 
 int moe_grouped_gemm_swiglu(const moe_config* cfg, const void* x_perm,
-                            const float* x_perm_scales, const int32_t* offsets,
-                            const float* gate_perm, const void* w13, const float* w13_scales,
-                            const void* w2, const float* w2_scales, const void* x_shared,
-                            const float* x_shared_scales, const void* ws13,
-                            const float* ws13_scales, const void* ws2,
-                            const float* ws2_scales, void* act, float* act_scales,
+                            const void* x_perm_scales, const int32_t* offsets,
+                            const float* gate_perm, const void* w13, const void* w13_scales,
+                            const void* w2, const void* w2_scales, const void* x_shared,
+                            const void* x_shared_scales, const void* ws13,
+                            const void* ws13_scales, const void* ws2,
+                            const void* ws2_scales, void* act, void* act_scales,
                             void* y_perm, void* shared_y, void* z_out, void* ws,
                             size_t ws_bytes, hipStream_t stream) {
     int st = check_cfg(cfg);
     if (st) return st;
     if (!x_perm || !offsets || !gate_perm || !w13 || !w2 || !act || !y_perm || !ws)
         return MOE_ERR_INVALID_ARG;
-    const bool fp8 = cfg->w_dtype == MOE_E4M3;
+    const bool fp8 = is_fp8(cfg->w_dtype);
     if (fp8) {
         if (!x_perm_scales || !w13_scales || !w2_scales || !act_scales || z_out)
             return MOE_ERR_INVALID_ARG;
@@ -407,13 +418,13 @@ int moe_grouped_gemm_swiglu(const moe_config* cfg, const void* x_perm,
                        ws2_scales, act, act_scales, y_perm, shared_y, z_out, ws, stream);
 }
 
-// Scale pointers of one GEMM half: required exactly in e4m3 mode (out_scales only when the
-// half writes e4m3, i.e. GEMM1's act).
-static int check_gemm_dtypes(const moe_config* cfg, bool e4m3_out, const float* a_scales,
-                             const float* w_scales, const float* out_scales,
-                             const float* sh_a_scales, const float* sh_w_scales,
-                             const float* sh_out_scales) {
-    if (cfg->w_dtype == MOE_E4M3) {
+// Scale pointers of one GEMM half: required exactly in the fp8 modes (out_scales only when
+// the half writes fp8, i.e. GEMM1's act).
+static int check_gemm_dtypes(const moe_config* cfg, bool e4m3_out, const void* a_scales,
+                             const void* w_scales, const void* out_scales,
+                             const void* sh_a_scales, const void* sh_w_scales,
+                             const void* sh_out_scales) {
+    if (is_fp8(cfg->w_dtype)) {
         if (!a_scales || !w_scales) return MOE_ERR_INVALID_ARG;
         if (e4m3_out != (out_scales != nullptr)) return MOE_ERR_INVALID_ARG;
         if (cfg->shared_F && (!sh_a_scales || !sh_w_scales)) return MOE_ERR_INVALID_ARG;
@@ -427,12 +438,12 @@ static int check_gemm_dtypes(const moe_config* cfg, bool e4m3_out, const float* 
     return MOE_OK;
 }
 
-int moe_grouped_gemm_up(const moe_config* cfg, const void* x_perm, const float* x_perm_scales,
+int moe_grouped_gemm_up(const moe_config* cfg, const void* x_perm, const void* x_perm_scales,
                         const int32_t* offsets, const float* gate_perm, const void* w13,
-                        const float* w13_scales, const void* x_shared,
-                        const float* x_shared_scales, const void* ws13,
-                        const float* ws13_scales, void* act, float* act_scales,
-                        void* shared_act, float* shared_act_scales, void* z_out, void* ws,
+                        const void* w13_scales, const void* x_shared,
+                        const void* x_shared_scales, const void* ws13,
+                        const void* ws13_scales, void* act, void* act_scales,
+                        void* shared_act, void* shared_act_scales, void* z_out, void* ws,
                         size_t ws_bytes, hipStream_t stream) {
     int st = check_cfg(cfg);
     if (st) return st;
@@ -444,7 +455,7 @@ int moe_grouped_gemm_up(const moe_config* cfg, const void* x_perm, const float* 
     }
     st = check_gemm_dtypes(cfg, true, x_perm_scales, w13_scales, act_scales, x_shared_scales,
                            ws13_scales, shared_act_scales);
-    if (!st && cfg->w_dtype == MOE_E4M3 && z_out) st = MOE_ERR_INVALID_ARG;
+    if (!st && is_fp8(cfg->w_dtype) && z_out) st = MOE_ERR_INVALID_ARG;
     if (st) return st;
     if (ws_bytes < sched_ws_bytes(cfg)) return MOE_ERR_WORKSPACE;
     return run_up(cfg, cfg->a_layout, x_perm, x_perm_scales, offsets, gate_perm, w13, w13_scales, x_shared,
@@ -452,10 +463,10 @@ int moe_grouped_gemm_up(const moe_config* cfg, const void* x_perm, const float* 
                   shared_act_scales, z_out, ws, stream);
 }
 
-int moe_grouped_gemm_down(const moe_config* cfg, const void* act, const float* act_scales,
-                          const int32_t* offsets, const void* w2, const float* w2_scales,
-                          const void* shared_act, const float* shared_act_scales,
-                          const void* ws2, const float* ws2_scales, void* y_perm,
+int moe_grouped_gemm_down(const moe_config* cfg, const void* act, const void* act_scales,
+                          const int32_t* offsets, const void* w2, const void* w2_scales,
+                          const void* shared_act, const void* shared_act_scales,
+                          const void* ws2, const void* ws2_scales, void* y_perm,
                           void* shared_y, void* ws, size_t ws_bytes, hipStream_t stream) {
     int st = check_cfg(cfg);
     if (st) return st;
@@ -484,16 +495,16 @@ int moe_unpermute_combine(const moe_config* cfg, const void* y_perm, const int32
 
 int moe_layer_forward(const moe_config* cfg, const void* x, const void* w_router,
                       const float* logit_bias, const float* sel_bias, const float* logits_in,
-                      const void* w13, const float* w13_scales, const void* w2,
-                      const float* w2_scales, const void* ws13, const float* ws13_scales,
-                      const void* ws2, const float* ws2_scales, void* y, float* logits_out,
+                      const void* w13, const void* w13_scales, const void* w2,
+                      const void* w2_scales, const void* ws13, const void* ws13_scales,
+                      const void* ws2, const void* ws2_scales, void* y, float* logits_out,
                       int32_t* topk_idx_out, float* topk_gate_out, int32_t* counts_out,
                       void* ws, size_t ws_bytes, hipStream_t stream) {
     int st = check_cfg(cfg);
     if (st) return st;
     if (!x || !w13 || !w2 || !y || !ws) return MOE_ERR_INVALID_ARG;
     if (!logits_in && !w_router) return MOE_ERR_INVALID_ARG;
-    const bool fp8 = cfg->w_dtype == MOE_E4M3;
+    const bool fp8 = is_fp8(cfg->w_dtype);
     if (fp8 && (!w13_scales || !w2_scales)) return MOE_ERR_INVALID_ARG;
     if (!fp8 && (w13_scales || w2_scales || ws13_scales || ws2_scales)) return MOE_ERR_INVALID_ARG;
     if (cfg->shared_F && (!ws13 || !ws2)) return MOE_ERR_INVALID_ARG;
@@ -528,11 +539,11 @@ int moe_layer_forward(const moe_config* cfg, const void* x, const void* w_router
                           cfg->n_groups, cfg->topk_groups, cfg->route_scale, idx, gate, stream);
     if (e == hipSuccess) e = stage_mark(2, stream);
     if (e != hipSuccess) return MOE_ERR_HIP;
-    const int mode = fp8 ? 2 : (cfg->act_dtype == MOE_F32 ? 0 : 1);
+    const int mode = cfg->w_dtype == MOE_MXFP8 ? 3 : fp8 ? 2 : (cfg->act_dtype == MOE_F32 ? 0 : 1);
     // layout of the internal activations (x_perm, act, the shared expert's act)
     const int a_kb = cfg->act_dtype == MOE_F32 ? 0 : MOE_LAYER_ACT_KBLOCK;
-    // bf16 / e4m3 with row-major activations: no x_perm copy; GEMM1 gathers its A rows
-    // straight from x (e4m3: from the token-order codes x_q) through src
+    // bf16 / fp8 with row-major activations: no x_perm copy; GEMM1 gathers its A rows
+    // straight from x (fp8: from the token-order codes x_q and their scales) through src
     const bool gather = MOE_LAYER_FUSED_GATHER && cfg->act_dtype != MOE_F32 && a_kb == 0;
     e = moe::launch_permute(mode, gather ? -1 : a_kb, x, idx, gate, cfg->T, cfg->H, cfg->E,
                             cfg->k, counts, L.offsets, L.pos, L.src, L.gate_perm, L.x_perm,
@@ -541,7 +552,7 @@ int moe_layer_forward(const moe_config* cfg, const void* x, const void* w_router
     if (e != hipSuccess) return MOE_ERR_HIP;
     const void* xs = fp8 ? L.x_q : x;
     const void* a1 = gather ? xs : L.x_perm;
-    const float* a1_scales = gather ? (fp8 ? L.x_q_scales : nullptr) : L.x_perm_scales;
+    const void* a1_scales = gather ? (fp8 ? L.x_q_scales : nullptr) : L.x_perm_scales;
     st = run_experts(cfg, a_kb, a1, a1_scales, L.offsets, L.gate_perm, w13, w13_scales,
                      w2, w2_scales, cfg->shared_F ? xs : nullptr, fp8 ? L.x_q_scales : nullptr,
                      ws13, ws13_scales, ws2, ws2_scales, L.act, L.act_scales, L.y_perm,
@@ -661,6 +672,15 @@ int moe_pack_kblock(const void* in, int64_t n_mat, int32_t rows, int32_t cols,
     if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4) return MOE_ERR_INVALID_ARG;
     if (((int64_t)cols * elem_bytes) % 64) return MOE_ERR_INVALID_ARG;
     return hip_status(moe::launch_pack_kblock(in, n_mat, rows, cols, elem_bytes, out, stream));
+}
+
+int moe_quantize_mx(const void* in, int32_t in_dtype, int64_t rows, int32_t cols, uint8_t* q,
+                    uint8_t* scales, hipStream_t stream) {
+    if (!in || !q || !scales) return MOE_ERR_INVALID_ARG;
+    if (in_dtype != MOE_F32 && in_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+    if (rows < 1 || cols < 1 || cols % 32) return MOE_ERR_INVALID_ARG;
+    return hip_status(moe::launch_quantize_mx(in, in_dtype, rows * (int64_t)cols, q, scales,
+                                              stream));
 }
 
 int moe_quantize_e4m3(const void* in, int32_t in_dtype, int64_t n_mat, int32_t rows,

@@ -189,6 +189,35 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict_
     if (sub == 0) scales[gblk] = sc;
 }
 
+// MXFP8 quantiser, 1 x 32 blocks along the rows (activations and weights alike): four lanes
+// per block, eight values per lane; the block's amax takes two butterflies.
+__global__ __launch_bounds__(256) void quant_mx_kernel(const void* __restrict__ in, int in_dtype,
+                                                       int64_t nblk, uint8_t* __restrict__ q,
+                                                       uint8_t* __restrict__ scales) {
+    const int64_t blk = (int64_t)blockIdx.x * 64 + threadIdx.x / 4;   // 32-value block
+    const int sub = threadIdx.x % 4;
+    const bool ok = blk < nblk;
+    const size_t base = (size_t)(ok ? blk : 0) * 32 + sub * 8;
+    float f[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (ok) load8_f32(in, in_dtype, base, f);
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1));
+    amax = fmaxf(amax, __shfl_xor(amax, 2));
+    if (!ok) return;
+    const int X = mx_exponent(amax);
+    const float inv = exp2_neg(X);
+    uint32_t c[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = e4m3_rne_sat(f[i] * inv);
+    uint2 packed;
+    packed.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+    packed.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+    *(uint2*)(q + base) = packed;
+    if (sub == 0) scales[blk] = (uint8_t)(X + 127);
+}
+
 // Weight quantiser, 128 x 128 blocks: one 256-thread block per quantisation block; each
 // thread handles half a row (64 values) of the block.
 __global__ __launch_bounds__(256) void quant_weight_kernel(const void* __restrict__ in,
@@ -318,6 +347,15 @@ hipError_t launch_quantize(const void* in, int in_dtype, int64_t n_mat, int rows
         quant_weight_kernel<<<(unsigned)nblocks, 256, 0, s>>>(in, in_dtype, rows, cols, q,
                                                               scales);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_mx(const void* in, int in_dtype, int64_t n_values, uint8_t* q,
+                              uint8_t* scales, hipStream_t s) {
+    const int64_t nblk = n_values / 32;
+    if (nblk > 0)
+        quant_mx_kernel<<<(unsigned)((nblk + 63) / 64), 256, 0, s>>>(in, in_dtype, nblk, q,
+                                                                     scales);
     return hipGetLastError();
 }
 

@@ -54,6 +54,20 @@ MOE_DEVICE uint32_t e4m3_rne_sat(float v) {
 // e4m3 block scale: fp32(amax / 448), 1 for an all-zero block.
 MOE_DEVICE float e4m3_scale(float amax) { return amax == 0.0f ? 1.0f : amax / 448.0f; }
 
+// MXFP8 (OCP Microscaling, E4M3 elements, 32-value blocks): the shared exponent of a block
+// whose largest magnitude is amax is floor(log2 amax) - 8 (8 being the exponent of E4M3's
+// largest normal, 448 = 1.75 * 2^8), clamped to [-127, 127]; zero and fp32-subnormal maxima
+// give -127. The block's E8M0 code is X + 127 and its elements e4m3_rne_sat(v * 2^-X), so the
+// largest lands in [256, 512) and only [448, 512) saturates. For finite amax, X <= 119.
+MOE_DEVICE int mx_exponent(float amax) {
+    const int X = (int)((__float_as_uint(amax) >> 23) & 0xFFu) - 127 - 8;
+    return X < -127 ? -127 : X;
+}
+
+// 2^-X as fp32 for X in [-127, 119] (an exact power of two: the scaling is exact unless the
+// product is an fp32 subnormal, far below E4M3's smallest subnormal)
+MOE_DEVICE float exp2_neg(int X) { return __uint_as_float((uint32_t)(127 - X) << 23); }
+
 // ---------------------------------------------------------------------------------------
 // Wavefront reductions (deterministic butterflies)
 // ---------------------------------------------------------------------------------------

@@ -31,12 +31,12 @@ namespace {
 // ---------------------------------------------------------------------------------------
 struct SegDev {
     const void* a;
-    const float* a_scales;
+    const void* a_scales;      // e4m3: fp32 per 1 x 128; MXFP8: E8M0 bytes per 1 x 32
     const float* gate;
     const void* w;
-    const float* w_scales;
+    const void* w_scales;      // e4m3: fp32 per 128 x 128; MXFP8: E8M0 bytes per 1 x 32
     void* out;
-    float* out_scales;
+    void* out_scales;          // GEMM1 act scales, as a_scales
     void* z_out;
     // operand addressing in bytes: row r, 64-byte K slice j of `a` is at
     // a + r * a_row + j * a_kstep (row-major: a_row = K * eb, a_kstep = 64; K-blocked:
@@ -653,7 +653,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_e4m3_kernel(GemmArgs ga) {
     {
         const int r = C::kRpw * wave + lane % C::kRpw;
         const int rr = m0 + r < Mg ? m0 + r : Mg - 1;
-        ssrc = S.a_scales + (size_t)(S.a_rows ? S.a_rows[rbase + rr] : rbase + rr) * KB;
+        ssrc = (const float*)S.a_scales + (size_t)(S.a_rows ? S.a_rows[rbase + rr] : rbase + rr) * KB;
     }
     auto issue = [&](int kstep, int stage) {
         MOE_LDS uint8_t* base = (MOE_LDS uint8_t*)lds + stage * C::kStageBytes;
@@ -711,7 +711,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_e4m3_kernel(GemmArgs ga) {
     case V:                                                                                 \
         if (V <= C::kTM) {                                                                  \
             constexpr int NV = V <= C::kTM ? V : C::kTM;                                    \
-            e4m3_kloop<C, NV>(KB, lds, issue, a_off, b_off, co, srow0, S.w_scales, wsc_off, \
+            e4m3_kloop<C, NV>(KB, lds, issue, a_off, b_off, co, srow0, (const float*)S.w_scales, wsc_off, \
                               acc);                                                         \
         }                                                                                   \
         break;
@@ -786,8 +786,295 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_e4m3_kernel(GemmArgs ga) {
             const size_t oi = S.out_kblock ? ((size_t)(col / 64) * S.rows_total + grow) * 64 + col % 64
                                            : grow * F + col;
             outq[oi] = (uint8_t)e4m3_rne_sat(av[i][r] / sc);
-            if (wn == 0 && lane % 32 == 0) S.out_scales[grow * (F / 128) + nt] = sc;
+            if (wn == 0 && lane % 32 == 0) ((float*)S.out_scales)[grow * (F / 128) + nt] = sc;
         }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// MXFP8 MFMA kernel: e4m3 operands with one E8M0 scale (a power of two) per 1 x 32 block
+// along K, for the activations and for the weights alike.
+//
+// v_mfma_scale_f32_32x32x64_f8f6f4 applies block scales itself: of the 64 K of one step,
+// K [0, 32) takes its scale from lanes 0-31 (row / column l % 32) and K [32, 64) from lanes
+// 32-63, and a lane of half h holds K [16 h, 16 h + 16) in its first 16 bytes and
+// K [32 + 16 h, 48 + 16 h) in its other 16 (measured on gfx950 with distinct per-lane scales;
+// the scale operand's byte is picked by op_sel). So with each 32-byte MX block laid on one
+// hardware block, a half-wave's lanes pass their rows' scale byte of that block and the
+// products go straight into the fp32 accumulator: no partial tile, no promotion step.
+//
+// One LDS stage holds 128 K: [BM A rows | BN B rows] x 128 bytes (16-byte chunks XOR-swizzled
+// by the row's low bits, as the other kernels), then one 4-byte word per tile row: the E8M0
+// codes of the row's four blocks of those 128 K (byte b = block b), DMA'd by one 4-byte load
+// per lane and wave.
+// GEMM1's epilogue folds the gate in and quantises act per 1 x 32 block: one block is the 32
+// columns of a 32 x 32 sub-tile in one row, held by the 32 lanes of a half-wave, so its
+// amax takes five butterflies and no cross-wave step.
+// ---------------------------------------------------------------------------------------
+template <int KIND, int BM, int BN, int WM, int WN, int STAGES>
+struct MxCfg {
+    static constexpr int kThreads = WM * WN * kWave;
+    static constexpr int kWaves = WM * WN;
+    static constexpr int kRowBytes = 128;                   // 128 e4m3 of K per stage
+    static constexpr int kRows = BM + BN;
+    static constexpr int kTileBytes = kRows * kRowBytes;
+    static constexpr int kScaleBytes = kWaves * 256;        // 64 words per wave
+    static constexpr int kStageBytes = kTileBytes + kScaleBytes;
+    static constexpr int kDma = kRows / 8 / kWaves;         // tile DMAs per wave per stage
+    static constexpr int kVm = kDma + 1;                    // + the scale-word DMA
+    static constexpr int kTM = BM / WM / 32;
+    static constexpr int kTN = BN / WN / 32;
+    static constexpr int kStages = STAGES;
+    static constexpr size_t kLds = (size_t)STAGES * kStageBytes;
+    // epilogue staging: GEMM1 act codes [BM][BN/2 + 16] bytes and scale codes [BM][BN/64];
+    // GEMM2 bf16 [BM][BN + 8]
+    static constexpr int kEpStride = KIND == 0 ? BN / 2 + 16 : BN + 8;
+    static constexpr size_t kEpBytes =
+        KIND == 0 ? (size_t)BM * kEpStride + (size_t)BM * (BN / 64) : (size_t)BM * kEpStride * 2;
+    static_assert(kRows <= kWaves * 64, "one scale DMA per wave covers the tile's rows");
+    static_assert(kRows % (8 * kWaves) == 0, "DMA split");
+    static_assert(KIND == 1 || kTN % 2 == 0, "GEMM1: gate and up sub-tiles in pairs");
+    static_assert(kLds <= 160 * 1024 && kEpBytes <= kLds, "LDS");
+    static_assert(STAGES >= 2 && (STAGES - 2) * kVm < 64, "vmcnt");
+};
+
+template <class C, int NV, class Issue>
+MOE_DEVICE void mx_kloop(int nk, const uint8_t* lds, Issue& issue, const int (&a_off)[C::kTM],
+                         const int (&b_off)[C::kTN], const int (&co)[2][2], int half,
+                         f32x16_t (&acc)[C::kTM][C::kTN]) {
+    constexpr int STAGES = C::kStages;
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s)
+        if (s < nk) issue(s, s);
+    int stage = 0;
+    for (int kt = 0; kt < nk; ++kt) {
+        const int later = nk - 1 - kt;
+        if (later >= STAGES - 2) wait_vm_lgkm0<(STAGES - 2) * C::kVm>();
+        else if (later >= 2) wait_vm_lgkm0<cmin(2, STAGES - 2) * C::kVm>();
+        else if (later >= 1) wait_vm_lgkm0<cmin(1, STAGES - 2) * C::kVm>();
+        else wait_vm_lgkm0<0>();
+        block_sync();
+        {
+            const int kn = kt + STAGES - 1;
+            int sn = stage + STAGES - 1;
+            if (sn >= STAGES) sn -= STAGES;
+            if (kn < nk) issue(kn, sn);
+        }
+        if (NV > 0) {
+            constexpr int NVv = NV > 0 ? NV : 1;
+            const uint8_t* base = lds + stage * C::kStageBytes;
+            const uint32_t* words = (const uint32_t*)(base + C::kTileBytes);
+            // this lane's scale bytes: block 2 s + half of its row, as byte 2 s after the shift
+            uint32_t sb[C::kTN], sa[NVv];
+#pragma unroll
+            for (int j = 0; j < C::kTN; ++j) sb[j] = words[b_off[j] >> 7] >> (8 * half);
+#pragma unroll
+            for (int i = 0; i < NVv; ++i) sa[i] = words[a_off[i] >> 7] >> (8 * half);
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                i32x8_t bv[C::kTN];
+#pragma unroll
+                for (int j = 0; j < C::kTN; ++j)
+                    bv[j] = lds_frag32(base + b_off[j] + co[s][0], base + b_off[j] + co[s][1]);
+#pragma unroll
+                for (int i = 0; i < NVv; ++i) {
+                    const i32x8_t av =
+                        lds_frag32(base + a_off[i] + co[s][0], base + a_off[i] + co[s][1]);
+#pragma unroll
+                    for (int j = 0; j < C::kTN; ++j) {
+                        if (s == 0)
+                            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                                av, bv[j], acc[i][j], 0, 0, 0, sa[i], 0, sb[j]);
+                        else
+                            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                                av, bv[j], acc[i][j], 0, 0, 2, sa[i], 2, sb[j]);
+                    }
+                }
+            }
+        }
+        if (++stage == STAGES) stage = 0;
+    }
+}
+
+template <int KIND, int BM, int BN, int WM, int WN, int STAGES>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmArgs ga) {
+    using C = MxCfg<KIND, BM, BN, WM, WN, STAGES>;
+    extern __shared__ __align__(16) uint8_t lds[];
+    int mt, nt;
+    if (!pick_tile(ga, mt, nt)) return;
+    const int4 ti = ga.tiles[mt];
+    const int seg = ti.x >> 20, g = ti.x & 0xFFFFF;
+    const int m0 = ti.y, Mg = ti.z, rbase = ti.w;
+    const SegDev S = seg == 0 ? ga.seg[0] : ga.seg[1];
+    const int N = ga.N, K = ga.K, KB = K / 32;          // KB: scale bytes per row
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int wm = wave / WN, wn = wave % WN, half = lane / 32;
+    const int live = Mg - m0 < BM ? Mg - m0 : BM;
+    int nvi = (live - wm * (BM / WM) + 31) / 32;
+    nvi = nvi < 0 ? 0 : (nvi > C::kTM ? C::kTM : nvi);
+    nvi = __builtin_amdgcn_readfirstlane(nvi);
+
+    // weight row of tile row rb (GEMM1: gate rows, then the matching up rows)
+    auto wrow_of = [&](int rb) {
+        if (KIND == 0)
+            return rb < BN / 2 ? nt * (BN / 2) + rb : N / 2 + nt * (BN / 2) + (rb - BN / 2);
+        return nt * BN + rb;
+    };
+    auto arow_of = [&](int r) {
+        const int rr = m0 + r < Mg ? m0 + r : Mg - 1;
+        return S.a_rows ? S.a_rows[rbase + rr] : rbase + rr;
+    };
+    // ---- tile DMA sources: 32-bit offsets from the activation base and the group's weights
+    const uint8_t* abase = (const uint8_t*)S.a;
+    const uint8_t* wbase = (const uint8_t*)S.w + (size_t)g * S.w_mat;
+    uint32_t src[C::kDma];
+#pragma unroll
+    for (int q = 0; q < C::kDma; ++q) {
+        const int r = 8 * (wave + q * C::kWaves) + lane / 8;
+        const int c = (lane % 8) ^ (r & 7);
+        const size_t rowp = r < BM ? (size_t)arow_of(r) * S.a_row : (size_t)wrow_of(r - BM) * S.w_row;
+        const size_t step = r < BM ? S.a_kstep : S.w_kstep;
+        src[q] = (uint32_t)(rowp + (size_t)(c / 4) * step + (c % 4) * 16);
+    }
+    const size_t a_step = S.a_kstep, w_step = S.w_kstep;
+    // scale words: wave w DMAs those of tile rows 64 w + lane (lanes past the tile's rows
+    // fetch the last row's word into the unused tail of the area)
+    const uint8_t* ssrc;
+    {
+        int r = 64 * wave + lane;
+        if (r >= C::kRows) r = C::kRows - 1;
+        if (r < BM)
+            ssrc = (const uint8_t*)S.a_scales + (size_t)arow_of(r) * KB;
+        else
+            ssrc = (const uint8_t*)S.w_scales + ((size_t)g * N + wrow_of(r - BM)) * KB;
+    }
+    auto issue = [&](int kstep, int stage) {
+        MOE_LDS uint8_t* base = (MOE_LDS uint8_t*)lds + stage * C::kStageBytes;
+#pragma unroll
+        for (int q = 0; q < C::kDma; ++q)
+            __builtin_amdgcn_global_load_lds(
+                (const void*)((q * 8 * C::kWaves < BM ? abase : wbase) + src[q] +
+                              (size_t)kstep * 2 * (q * 8 * C::kWaves < BM ? a_step : w_step)),
+                (MOE_LDS void*)(base + (wave + q * C::kWaves) * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(ssrc + kstep * 4),
+                                         (MOE_LDS void*)(base + C::kTileBytes + wave * 256), 4, 0, 0);
+    };
+
+    int a_off[C::kTM], b_off[C::kTN];
+#pragma unroll
+    for (int i = 0; i < C::kTM; ++i) a_off[i] = (wm * (BM / WM) + i * 32 + lane % 32) * 128;
+#pragma unroll
+    for (int j = 0; j < C::kTN; ++j) {
+        int row;
+        if (KIND == 0) {
+            constexpr int hf = C::kTN / 2;
+            const int col = wn * (BN / 2 / WN) + (j % hf) * 32 + lane % 32;
+            row = BM + (j < hf ? col : BN / 2 + col);
+        } else {
+            row = BM + wn * (BN / WN) + j * 32 + lane % 32;
+        }
+        b_off[j] = row * 128;
+    }
+    // the lane's bytes of K sub-step s (64 K): K [16 h, 16 h + 16) and [32 + 16 h, 48 + 16 h)
+    // of it, i.e. logical chunks 4 s + h and 4 s + 2 + h of the 128-byte stage row
+    int co[2][2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) co[s][u] = (((4 * s + 2 * u + half) ^ (lane & 7)) * 16);
+
+    f32x16_t acc[C::kTM][C::kTN];
+#pragma unroll
+    for (int i = 0; i < C::kTM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::kTN; ++j) acc[i][j] = f32x16_t{};
+    const int nk = K / 128;
+    switch (nvi) {
+#define MOE_MX_CASE(V)                                                                      \
+    case V:                                                                                 \
+        if (V <= C::kTM) {                                                                  \
+            constexpr int NV = V <= C::kTM ? V : C::kTM;                                    \
+            mx_kloop<C, NV>(nk, lds, issue, a_off, b_off, co, half, acc);                   \
+        }                                                                                   \
+        break;
+    MOE_MX_CASE(0)
+    MOE_MX_CASE(1)
+    MOE_MX_CASE(2)
+    MOE_MX_CASE(3)
+    MOE_MX_CASE(4)
+#undef MOE_MX_CASE
+    default: break;
+    }
+
+    // ---- epilogue (accumulator element r of lane l: row (r/4)*8 + (l/32)*4 + r%4, column
+    // l%32), staged in LDS so that every global store is a 16-byte (GEMM1 scales: 4-byte) run
+    block_sync();                                      // every wave is done with the stages
+    if (KIND == 1) {
+        uint16_t* ep = (uint16_t*)lds;
+#pragma unroll
+        for (int i = 0; i < C::kTM; ++i) {
+            if (i >= nvi) continue;
+#pragma unroll
+            for (int j = 0; j < C::kTN; ++j) {
+                const int lcol = wn * (BN / WN) + j * 32 + lane % 32;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = wm * (BM / WM) + i * 32 + (r / 4) * 8 + half * 4 + r % 4;
+                    ep[row * C::kEpStride + lcol] = f32_to_bf16(acc[i][j][r]);
+                }
+            }
+        }
+        __syncthreads();
+        constexpr int kChunks = BN / 8;
+        uint16_t* out = (uint16_t*)S.out;
+        for (int c = tid; c < live * kChunks; c += C::kThreads) {
+            const int row = c / kChunks, cc = c % kChunks;
+            const uint4 v = *(const uint4*)(ep + row * C::kEpStride + cc * 8);
+            *(uint4*)(out + ((size_t)rbase + m0 + row) * N + nt * BN + cc * 8) = v;
+        }
+        return;
+    }
+    // GEMM1: act = gate * silu(Z_g) * Z_u, quantised per 1 x 32 block
+    constexpr int hf = C::kTN / 2;
+    constexpr int kSc = BN / 64;                       // act blocks per tile row
+    uint8_t* ep = (uint8_t*)lds;
+    uint8_t* eps = ep + BM * C::kEpStride;             // [BM][kSc] scale codes
+#pragma unroll
+    for (int i = 0; i < C::kTM; ++i) {
+        if (i >= nvi) continue;
+#pragma unroll
+        for (int jj = 0; jj < hf; ++jj) {
+            const int lcol = wn * (BN / 2 / WN) + jj * 32 + lane % 32;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = wm * (BM / WM) + i * 32 + (r / 4) * 8 + half * 4 + r % 4;
+                const int lr = m0 + row < Mg ? row : live - 1;     // dead rows: any gate
+                const float gt = S.gate ? S.gate[(size_t)rbase + m0 + lr] : 1.0f;
+                const float v = gt * (silu_f32(acc[i][jj][r]) * acc[i][hf + jj][r]);
+                float m = fabsf(v);
+#pragma unroll
+                for (int off = 1; off < 32; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+                const int X = mx_exponent(m);
+                ep[row * C::kEpStride + lcol] = (uint8_t)e4m3_rne_sat(v * exp2_neg(X));
+                if (lane % 32 == 0) eps[row * kSc + lcol / 32] = (uint8_t)(X + 127);
+            }
+        }
+    }
+    __syncthreads();
+    {
+        const int F = N / 2;
+        constexpr int kChunks = BN / 2 / 16;           // 16-byte chunks of act per tile row
+        uint8_t* outq = (uint8_t*)S.out;
+        for (int c = tid; c < live * kChunks; c += C::kThreads) {
+            const int row = c / kChunks, cc = c % kChunks;
+            const uint4 v = *(const uint4*)(ep + row * C::kEpStride + cc * 16);
+            *(uint4*)(outq + ((size_t)rbase + m0 + row) * F + nt * (BN / 2) + cc * 16) = v;
+        }
+        uint8_t* outs = (uint8_t*)S.out_scales;
+        static_assert(kSc == 4, "one 4-byte scale run per tile row");
+        for (int row = tid; row < live; row += C::kThreads)
+            *(uint32_t*)(outs + ((size_t)rbase + m0 + row) * (F / 32) + nt * kSc) =
+                *(const uint32_t*)(eps + row * kSc);
     }
 }
 
@@ -938,6 +1225,29 @@ hipError_t run_e4m3(const GemmArgs& ga, int nblocks, hipStream_t s) {
     return hipGetLastError();
 }
 
+// MXFP8 tile configuration (BM, BN, WM, WN, STAGES), both GEMMs
+#ifndef MOE_MX_UP_CFG
+#define MOE_MX_UP_CFG 256, 256, 2, 4, 2
+#endif
+#ifndef MOE_MX_DOWN_CFG
+#define MOE_MX_DOWN_CFG 256, 256, 2, 4, 2
+#endif
+
+template <int KIND, int BM, int BN, int WM, int WN, int STAGES>
+hipError_t run_mx(const GemmArgs& ga, int nblocks, hipStream_t s) {
+    using C = MxCfg<KIND, BM, BN, WM, WN, STAGES>;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(
+            (const void*)gemm_mx_kernel<KIND, BM, BN, WM, WN, STAGES>,
+            hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::kLds);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    gemm_mx_kernel<KIND, BM, BN, WM, WN, STAGES><<<nblocks, C::kThreads, C::kLds, s>>>(ga);
+    return hipGetLastError();
+}
+
 template <int BM, int BN, int WM, int WN, int STAGES>
 constexpr int f8_bm() { return BM; }
 template <int BM, int BN, int WM, int WN, int STAGES>
@@ -946,11 +1256,13 @@ constexpr int f8_bn() { return BN; }
 int bm_for(int kind, int dtype) {
     if (dtype == 0) return kF32BM;
     if (dtype == 2) return kind == 0 ? f8_bm<MOE_F8_UP_CFG>() : f8_bm<MOE_F8_DOWN_CFG>();
+    if (dtype == 3) return kind == 0 ? f8_bm<MOE_MX_UP_CFG>() : f8_bm<MOE_MX_DOWN_CFG>();
     return kind == 0 ? cfg_bm<MOE_BF_UP_CFG>() : cfg_bm<MOE_BF_DOWN_CFG>();
 }
 int bn_for(int kind, int dtype) {
     if (dtype == 0) return 64;
     if (dtype == 2) return kind == 0 ? f8_bn<MOE_F8_UP_CFG>() : f8_bn<MOE_F8_DOWN_CFG>();
+    if (dtype == 3) return kind == 0 ? f8_bn<MOE_MX_UP_CFG>() : f8_bn<MOE_MX_DOWN_CFG>();
     return kind == 0 ? cfg_bn<MOE_BF_UP_CFG>() : cfg_bn<MOE_BF_DOWN_CFG>();
 }
 
@@ -1187,6 +1499,10 @@ hipError_t launch_grouped_gemm(int kind, int dtype, const Segment* segs, int nse
     if (dtype == 2) {
         if (kind == 0) return run_e4m3<0, MOE_F8_UP_CFG>(ga, (int)nblocks, s);
         return run_e4m3<1, MOE_F8_DOWN_CFG>(ga, (int)nblocks, s);
+    }
+    if (dtype == 3) {
+        if (kind == 0) return run_mx<0, MOE_MX_UP_CFG>(ga, (int)nblocks, s);
+        return run_mx<1, MOE_MX_DOWN_CFG>(ga, (int)nblocks, s);
     }
     return hipErrorInvalidValue;
 }

@@ -37,14 +37,15 @@ hipError_t launch_route_backward(int router, const float* logits, const float* l
 // ---- permute ---------------------------------------------------------------------------
 constexpr int kPermChunk = 512;   // assignments per counting block
 size_t permute_ws_bytes(int T, int k, int E);
-hipError_t launch_permute(int mode /*0 f32, 1 bf16, 2 e4m3 from bf16*/,
-                          int kblock /*1: x_perm K-blocked; -1: no x_perm (routing metadata,
-                                       and for e4m3 the token-order x_q, only)*/,
+hipError_t launch_permute(int mode /*0 f32, 1 bf16, 2 e4m3 from bf16, 3 MXFP8 from bf16*/,
+                          int kblock /*1: x_perm K-blocked (not with MXFP8); -1: no x_perm
+                                       (routing metadata, and in the fp8 modes the token-order
+                                       x_q, only)*/,
                           const void* x,
                           const int32_t* topk_idx, const float* topk_gate, int T, int H,
                           int E, int k, int32_t* counts, int32_t* offsets, int32_t* pos,
                           int32_t* src, float* gate_perm, void* x_perm,
-                          float* x_perm_scales, void* x_q, float* x_q_scales, void* ws,
+                          void* x_perm_scales, void* x_q, void* x_q_scales, void* ws,
                           hipStream_t s);
 
 // ---- combine ---------------------------------------------------------------------------
@@ -61,21 +62,27 @@ hipError_t launch_pack_kblock(const void* in, int64_t n_mat, int rows, int cols,
 // ---- quantise --------------------------------------------------------------------------
 hipError_t launch_quantize(const void* in, int in_dtype, int64_t n_mat, int rows, int cols,
                            int block_rows, uint8_t* q, float* scales, hipStream_t s);
+// MXFP8: n_values (a multiple of 32) consecutive values in 1 x 32 blocks -> e4m3 codes q and
+// one E8M0 code per block (rows of a row-major matrix whose width is a multiple of 32 are
+// blocked along the row)
+hipError_t launch_quantize_mx(const void* in, int in_dtype, int64_t n_values, uint8_t* q,
+                              uint8_t* scales, hipStream_t s);
 
 // ---- grouped GEMM ----------------------------------------------------------------------
 // One expert segment of a grouped GEMM launch: `groups` groups whose rows are
 // [offsets[g], offsets[g+1]) of `a` (offsets == nullptr: one group of `rows` rows).
 struct Segment {
     const void* a;             // [rows_total, K] activations (dtype of the launch)
-    const float* a_scales;     // e4m3: [rows_total, K/128]
+    const void* a_scales;      // e4m3: fp32 [rows_total, K/128]; MXFP8: E8M0 [rows_total, K/32]
     const int32_t* offsets;    // [groups+1] device, or nullptr
     int groups;
     int rows;                  // rows when offsets == nullptr
     const float* gate;         // per-row gate (GEMM1 fold), nullptr = 1
     const void* w;             // [groups, N, K]
-    const float* w_scales;     // e4m3: [groups, N/128, K/128]
+    const void* w_scales;      // e4m3: fp32 [groups, N/128, K/128]; MXFP8: E8M0 [groups, N, K/32]
     void* out;                 // GEMM1: act [rows, N/2]; GEMM2: y [rows, N]
-    float* out_scales;         // GEMM1 e4m3: act scales [rows, N/2/128]
+    void* out_scales;          // GEMM1 act scales: e4m3 fp32 [rows, N/2/128]; MXFP8 E8M0
+                               // [rows, N/2/32]
     void* z_out;               // GEMM1 optional: Z [rows, N] in the activation dtype
     int rows_total;            // rows of `a` (and of `out`)
     int a_kblock;              // 1: `a` is K-blocked ([K*eb/64][rows_total][64 bytes])
@@ -91,7 +98,8 @@ struct GemmPlan {
 };
 
 // kind: 0 = GEMM1 (gate/up + SwiGLU * gate), 1 = GEMM2 (plain).  dtype: moe_dtype of the
-// operands (F32, BF16, E4M3). N = output columns of the GEMM before the SwiGLU pairing.
+// operands (F32, BF16, E4M3, MXFP8; MXFP8 needs row-major scales, K % 128 == 0 and for
+// GEMM1 N % 256 == 0). N = output columns of the GEMM before the SwiGLU pairing.
 // Tile list of one segment (groups with device-resident row offsets) for M tiles of `bm`
 // rows, written to ws: *(int*)ws = count, (int4*)(ws + 256) = {group, first row, rows,
 // group's first global row}.

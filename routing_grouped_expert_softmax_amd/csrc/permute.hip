@@ -12,9 +12,12 @@
 //              atomic-free counting sort (rows of an expert in ascending token order).
 //   4. copy:   row-major x_perm: one wavefront per token reads the x row once and writes it
 //              to its k rows (16-byte accesses); in e4m3 mode the row is quantised per
-//              1 x 128 block in registers first and the codes and scales are written instead.
+//              1 x 128 block (MXFP8 mode: per 1 x 32 block with an E8M0 scale) in registers
+//              first and the codes and scales are written instead.
 //              K-blocked x_perm: a gather by destination rows (perm_gather_kblock_kernel),
 //              after a token-order e4m3 quantisation in e4m3 mode.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -166,20 +169,25 @@ __global__ __launch_bounds__(256) void perm_copy_kernel(const uint4* __restrict_
 // e4m3 row quantise + copy. A wavefront covers 512 columns per step: 16 lanes per
 // 128-column block, 8 bf16 values (16 bytes) per lane.
 // K-blocked x_perm: 8-byte chunk c of row r goes to chunk (c / 8) * A * 8 + r * 8 + c % 8.
+// MX = false: e4m3 with an fp32 scale per 1 x 128 block (16 lanes per block);
+// MX = true:  MXFP8, an E8M0 scale per 1 x 32 block (4 lanes per block).
+template <bool MX>
 __global__ __launch_bounds__(256) void perm_quant_copy_kernel(
     const uint4* __restrict__ x, const int32_t* __restrict__ pos, int T, int H, int k,
-    int kblock, uint2* __restrict__ x_perm, float* __restrict__ x_perm_scales,
-    uint2* __restrict__ x_q, float* __restrict__ x_q_scales) {
+    int kblock, uint2* __restrict__ x_perm, void* __restrict__ x_perm_scales,
+    uint2* __restrict__ x_q, void* __restrict__ x_q_scales) {
+    using Sc = typename std::conditional<MX, uint8_t, float>::type;
+    constexpr int kLanesPerBlk = MX ? 4 : 16;
     const size_t A = (size_t)T * k;
     const int lane = threadIdx.x % kWave;
     const int t = blockIdx.x * 4 + threadIdx.x / kWave;
     if (t >= T) return;
     int my_pos = lane < k ? pos[(size_t)t * k + lane] : 0;
     const int row_chunks = H / 8;
-    const int nblk = H / 128;
+    const int nblk = H / (8 * kLanesPerBlk);
     const uint4* xr = x + (size_t)t * row_chunks;
-    // every lane runs every iteration (shuffles read active lanes only); 16-lane groups
-    // stay aligned to 128-column blocks because H % 128 == 0
+    // every lane runs every iteration (shuffles read active lanes only); lane groups stay
+    // aligned to the blocks because H % 128 == 0
     for (int c0 = 0; c0 < row_chunks; c0 += kWave) {
         const int c = c0 + lane;
         const bool ok = c < row_chunks;
@@ -195,19 +203,29 @@ __global__ __launch_bounds__(256) void perm_quant_copy_kernel(
 #pragma unroll
         for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
 #pragma unroll
-        for (int off = 1; off < 16; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-        float sc = e4m3_scale(amax);
+        for (int off = 1; off < kLanesPerBlk; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
         uint32_t q[8];
+        Sc sc;
+        if (MX) {
+            const int X = mx_exponent(amax);
+            const float inv = exp2_neg(X);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) q[i] = e4m3_rne_sat(f[i] / sc);
+            for (int i = 0; i < 8; ++i) q[i] = e4m3_rne_sat(f[i] * inv);
+            sc = (Sc)(X + 127);
+        } else {
+            const float s = e4m3_scale(amax);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) q[i] = e4m3_rne_sat(f[i] / s);
+            sc = (Sc)s;
+        }
         uint2 packed;
         packed.x = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
         packed.y = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
-        const int blk = c / 16;
-        const bool leader = (c % 16) == 0;
+        const int blk = c / kLanesPerBlk;
+        const bool leader = (c % kLanesPerBlk) == 0;
         if (x_q && ok) {
             x_q[(size_t)t * row_chunks + c] = packed;
-            if (leader) x_q_scales[(size_t)t * nblk + blk] = sc;
+            if (leader) ((Sc*)x_q_scales)[(size_t)t * nblk + blk] = sc;
         }
         for (int j = 0; j < k; ++j) {
             int r = __shfl(my_pos, j);
@@ -215,7 +233,7 @@ __global__ __launch_bounds__(256) void perm_quant_copy_kernel(
                 const size_t o = kblock ? ((size_t)(c / 8) * A + r) * 8 + c % 8
                                         : (size_t)r * row_chunks + c;
                 x_perm[o] = packed;
-                if (leader) x_perm_scales[(size_t)r * nblk + blk] = sc;
+                if (leader) ((Sc*)x_perm_scales)[(size_t)r * nblk + blk] = sc;
             }
         }
     }
@@ -281,8 +299,8 @@ size_t permute_ws_bytes(int T, int k, int E) {
 hipError_t launch_permute(int mode, int kblock, const void* x, const int32_t* topk_idx,
                           const float* topk_gate, int T, int H, int E, int k,
                           int32_t* counts, int32_t* offsets, int32_t* pos, int32_t* src,
-                          float* gate_perm, void* x_perm, float* x_perm_scales, void* x_q,
-                          float* x_q_scales, void* ws, hipStream_t s) {
+                          float* gate_perm, void* x_perm, void* x_perm_scales, void* x_q,
+                          void* x_q_scales, void* ws, hipStream_t s) {
     const int A = T * k;
     const int nchunk = (A + kPermChunk - 1) / kPermChunk;
     int32_t* chunk_counts = (int32_t*)ws;
@@ -295,7 +313,9 @@ hipError_t launch_permute(int mode, int kblock, const void* x, const int32_t* to
                                                              src, gate_perm);
     if (kblock < 0) {           // metadata only (the GEMM gathers the rows itself)
         if (mode == 2)
-            return launch_quantize(x, 1, 1, T, H, 1, (uint8_t*)x_q, x_q_scales, s);
+            return launch_quantize(x, 1, 1, T, H, 1, (uint8_t*)x_q, (float*)x_q_scales, s);
+        if (mode == 3)
+            return launch_quantize_mx(x, 1, (int64_t)T * H, (uint8_t*)x_q, (uint8_t*)x_q_scales, s);
         return hipGetLastError();
     }
     const int blocks = (T + 3) / 4;
@@ -311,15 +331,20 @@ hipError_t launch_permute(int mode, int kblock, const void* x, const int32_t* to
     }
     if (kblock && mode == 2 && x_q) {
         // quantise each token once (token order), then gather codes and scales
-        hipError_t e = launch_quantize(x, 1, 1, T, H, 1, (uint8_t*)x_q, x_q_scales, s);
+        hipError_t e = launch_quantize(x, 1, 1, T, H, 1, (uint8_t*)x_q, (float*)x_q_scales, s);
         if (e != hipSuccess) return e;
-        gather(x_q, H, x_q_scales, x_perm_scales);
+        gather(x_q, H, (const float*)x_q_scales, (float*)x_perm_scales);
         return hipGetLastError();
     }
     if (mode == 2) {
-        perm_quant_copy_kernel<<<blocks, 256, 0, s>>>((const uint4*)x, pos, T, H, k, kblock,
-                                                      (uint2*)x_perm, x_perm_scales,
-                                                      (uint2*)x_q, x_q_scales);
+        perm_quant_copy_kernel<false><<<blocks, 256, 0, s>>>((const uint4*)x, pos, T, H, k,
+                                                             kblock, (uint2*)x_perm,
+                                                             x_perm_scales, (uint2*)x_q,
+                                                             x_q_scales);
+    } else if (mode == 3) {     // row-major only (the ABI rejects a K-blocked MXFP8 x_perm)
+        perm_quant_copy_kernel<true><<<blocks, 256, 0, s>>>((const uint4*)x, pos, T, H, k, 0,
+                                                            (uint2*)x_perm, x_perm_scales,
+                                                            (uint2*)x_q, x_q_scales);
     } else {
         const int elem = mode == 0 ? 4 : 2;
         perm_copy_kernel<<<blocks, 256, 0, s>>>((const uint4*)x, pos, T, H * elem / 16, k,

@@ -4,7 +4,7 @@ import torch
 
 import moe_inputs as mi
 
-TOL = {mi.F32: 1e-5, mi.BF16: 2e-2, mi.E4M3: 6e-2}
+TOL = {mi.F32: 1e-5, mi.BF16: 2e-2, mi.E4M3: 6e-2, mi.MXFP8: 6e-2}
 
 
 def rel_err(got, ref) -> float:
@@ -17,7 +17,7 @@ def rel_err(got, ref) -> float:
 
 
 def tol(cfg) -> float:
-    return TOL[cfg.w_dtype if cfg.w_dtype == mi.E4M3 else cfg.act_dtype]
+    return TOL[cfg.w_dtype if cfg.w_dtype in (mi.E4M3, mi.MXFP8) else cfg.act_dtype]
 
 
 # Small copies of each workload: same router, dtypes and structure, sizes the oracle finishes
@@ -40,6 +40,19 @@ SMALL_FP8 = {
     # one token: one live row per GEMM tile, most experts empty
     "dsv3_fp8_one_token": mi.scaled(mi.CONFIGS["dsv3_fp8_skew"], T=1, H=256, F=128,
                                     shared_F=128),
+}
+
+
+# Small copies of the DeepSeek-V3 layer with MXFP8 expert GEMMs (1 x 32 E8M0 scales): several
+# M and N tiles, ragged tails, a shared expert in the same launch (shared_F == F) and in a
+# launch of its own, K of 2 to 6 stages, one token.
+SMALL_MX = {
+    "dsv3_mx_small": mi.scaled(mi.CONFIGS["dsv3_mxfp8"], T=520, H=512, F=256, shared_F=256),
+    "dsv3_mx_wide": mi.scaled(mi.CONFIGS["dsv3_mxfp8"], T=300, H=768, F=384, shared_F=128),
+    # 16 experts: 300+ rows per expert, i.e. two M tiles of 256 with a ragged second one
+    "dsv3_mx_deep": mi.scaled(mi.CONFIGS["dsv3_mxfp8"], T=1500, H=256, F=128, E=16, k=4,
+                              n_groups=4, topk_groups=2, shared_F=128),
+    "dsv3_mx_one_token": mi.scaled(mi.CONFIGS["dsv3_mxfp8"], T=1, H=256, F=128, shared_F=128),
 }
 
 
@@ -112,3 +125,31 @@ def e4m3_codes_close(q_gpu, s_gpu, act_ref_f64, err=1e-3):
     frac = float((np.asarray(q_gpu) != q_ref).mean())
     srel = float(np.max(np.abs(np.asarray(s_gpu, np.float64) - s_ref) / np.maximum(np.abs(s_ref), 1e-30)))
     return ratio, frac, srel
+
+
+def mx_codes_close(q_gpu, s_gpu, act_ref_f64, err=1e-3):
+    """Compare MXFP8-quantised rows (codes + E8M0 scale codes per 1 x 32 block) with the
+    oracle's unquantised activation act_ref, as e4m3_codes_close does for 1 x 128 blocks:
+    each dequantised element must lie within one e4m3 step (at the oracle's own block scale)
+    of act_ref, plus its saturation error, plus err of that block's range. The MX rule maps a
+    block's largest value into [256, 512) and clamps [448, 512) to 448; when a block's
+    maximum sits at a power of two, the GPU's fp32 value may fall on the other side of it
+    and take the scale one below the oracle's, and then elements of the block saturate at
+    the GPU's scale, so the saturation allowance is taken at both scales. Returns
+    (max |error| / bound, fraction of codes differing from the oracle's own quantisation,
+    max |scale code difference|, fraction of scale codes differing)."""
+    import oracle
+    ref32 = np.asarray(act_ref_f64, np.float64).astype(np.float32)
+    q_ref, s_ref = oracle.mx_quant(ref32)
+    sc_ref = np.repeat(np.exp2(np.asarray(s_ref, np.float64) - 127.0), 32, axis=-1)
+    sc_gpu = np.repeat(np.exp2(np.asarray(s_gpu, np.float64) - 127.0), 32, axis=-1)
+    v_ref = ref32.astype(np.float64)
+    v_gpu = oracle.e4m3_decode_array(np.asarray(q_gpu)) * sc_gpu
+    u = np.abs(v_ref / sc_ref)
+    ug = np.abs(v_ref / sc_gpu)
+    bound = ((e4m3_step(u) + np.maximum(u - 448.0, 0.0) + err * 448.0) * sc_ref
+             + np.maximum(ug - 448.0, 0.0) * sc_gpu)
+    ratio = float(np.max(np.abs(v_gpu - v_ref) / bound))
+    frac = float((np.asarray(q_gpu) != q_ref).mean())
+    ds = np.asarray(s_gpu, np.int32) - np.asarray(s_ref, np.int32)
+    return ratio, frac, int(np.max(np.abs(ds))), float((ds != 0).mean())
