@@ -25,7 +25,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM = 8.0e12          # MI355X HBM3E, bytes/s
-PEAK_MFMA = {"bf16": 2.5e15, "fp32": 157.3e12, "e4m3": 5.0e15}   # dense, FLOP/s
+PEAK_MFMA = {"bf16": 2.5e15, "fp32": 157.3e12, "e4m3": 5.0e15, "mxfp8": 5.0e15}  # dense, FLOP/s
 
 # HBM traffic of the dominant kernel, from rocprofv3 FETCH_SIZE / WRITE_SIZE passes scaled by
 # a plain copy of known size (see the file); used only while the kernel sources are unchanged
@@ -43,7 +43,10 @@ def algorithmic(cfg):
     T, H, E, k, F, sF = cfg.T, cfg.H, cfg.E, cfg.k, cfg.F, cfg.shared_F
     A = T * k
     b = 4 if cfg.act_dtype == 0 else 2
-    wb = 1 if cfg.w_dtype == 2 else b
+    wb = 1 if cfg.w_dtype in (2, 3) else b
+    # MXFP8 scale bytes per operand byte (one E8M0 byte per 32 codes); the e4m3 path's fp32
+    # 128 x 128 weight scales are negligible and its 1 x 128 activation scales are counted
+    sx = 1 / 32 if cfg.w_dtype == 3 else 0
     d = {}
     d["router_logits"] = dict(bytes=T * H * b + E * H * b + T * E * 4, flops=2 * T * H * E)
     d["route"] = dict(bytes=T * E * 4 + 2 * A * 4, flops=0)
@@ -55,20 +58,22 @@ def algorithmic(cfg):
         d["permute"] = dict(bytes=T * H * b + A * H * b + meta, flops=0)
     elif cfg.w_dtype == 2:
         d["permute"] = dict(bytes=T * H * b + T * H + T * (H // 128) * 4 + meta, flops=0)
+    elif cfg.w_dtype == 3:
+        d["permute"] = dict(bytes=T * H * b + T * H + T * (H // 32) + meta, flops=0)
     else:
         d["permute"] = dict(bytes=meta, flops=0)
     # GEMM1 reads the tokens' rows (x, or its e4m3 codes) once: the routed rows are gathered
     # from the same T rows the shared expert reads
-    up_b = E * 2 * F * H * wb + T * H * wb + A * F * wb + A * 4
+    up_b = (E * 2 * F * H * wb + T * H * wb + A * F * wb) * (1 + sx) + A * 4
     if cfg.act_dtype == 0:
         up_b += A * H * wb - T * H * wb                 # fp32 keeps the x_perm copy
     up_f = 2 * A * 2 * F * H
-    dn_b = E * H * F * wb + A * F * wb + A * H * b
+    dn_b = (E * H * F * wb + A * F * wb) * (1 + sx) + A * H * b
     dn_f = 2 * A * H * F
     if sF:
-        up_b += 2 * sF * H * wb + T * sF * wb
+        up_b += (2 * sF * H * wb + T * sF * wb) * (1 + sx)
         up_f += 2 * T * 2 * sF * H
-        dn_b += H * sF * wb + T * sF * wb + T * H * b
+        dn_b += (H * sF * wb + T * sF * wb) * (1 + sx) + T * H * b
         dn_f += 2 * T * H * sF
     d["grouped_gemm_up"] = dict(bytes=up_b, flops=up_f)
     d["grouped_gemm_down"] = dict(bytes=dn_b, flops=dn_f)
@@ -172,19 +177,20 @@ def cpu_baseline(cfg, inp, sample: int):
     sub = cfg.replace(T=len(toks))
     xs = inp.x[toks]
     oracle.lib()
-    if cfg.w_dtype == 2:      # weights quantised once, outside the timed sample (like loading)
-        q13, q2 = oracle.quant_weight(inp.w13), oracle.quant_weight(inp.w2)
-        s13, s2 = oracle.quant_weight(inp.ws13), oracle.quant_weight(inp.ws2)
+    if cfg.w_dtype in (2, 3):  # weights quantised once, outside the timed sample (like loading)
+        qw = oracle.quant_weight if cfg.w_dtype == 2 else oracle.mx_quant
+        q13, q2 = qw(inp.w13), qw(inp.w2)
+        s13, s2 = qw(inp.ws13), qw(inp.ws2)
     t0 = time.perf_counter()
     logits = oracle.router_logits(xs, inp.w_router)
     lb = None if inp.logit_bias is None else inp.logit_bias.numpy()
     sb = None if inp.sel_bias is None else inp.sel_bias.numpy()
     idx, gate = oracle.route_cfg(sub, logits, lb, sb)
     oracle.permute(idx, gate, cfg.E)
-    if cfg.w_dtype == 2:
+    if cfg.w_dtype in (2, 3):
         oracle.layer_tokens(xs, idx, gate, q13[0], q2[0], np.arange(len(toks)), s13[0], s2[0],
-                            fp8=True, w13_scales=q13[1], w2_scales=q2[1], ws13_scales=s13[1],
-                            ws2_scales=s2[1])
+                            fp8=True if cfg.w_dtype == 2 else "mx", w13_scales=q13[1],
+                            w2_scales=q2[1], ws13_scales=s13[1], ws2_scales=s2[1])
     else:
         oracle.layer_tokens(xs, idx, gate, inp.w13, inp.w2, np.arange(len(toks)), inp.ws13,
                             inp.ws2)
@@ -307,8 +313,8 @@ def main():
     import routing_grouped_expert_softmax_amd as moe
 
     cfg = mi.CONFIGS[args.workload]
-    if cfg.act_dtype != mi.F32:
-        cfg = cfg.replace(a_layout=1, w_layout=1)
+    if cfg.act_dtype != mi.F32:      # K-blocked weights (MXFP8: row-major activations)
+        cfg = cfg.replace(a_layout=0 if cfg.w_dtype == mi.MXFP8 else 1, w_layout=1)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     log(f"[bench] generating {cfg.name} inputs ...")
@@ -318,11 +324,19 @@ def main():
     g = lambda t: None if t is None else t.to(dev, non_blocking=False)  # noqa: E731
     x, wr, w13, w2 = g(inp.x), g(inp.w_router), g(inp.w13), g(inp.w2)
     ws13, ws2, lb, sb = g(inp.ws13), g(inp.ws2), g(inp.logit_bias), g(inp.sel_bias)
-    fp8 = cfg.w_dtype == mi.E4M3
+    fp8 = cfg.w_dtype in (mi.E4M3, mi.MXFP8)
     sc = dict(w13_scales=None, w2_scales=None, ws13_scales=None, ws2_scales=None)
     w13_bf, w2_bf, ws13_bf, ws2_bf = w13, w2, ws13, ws2     # row-major bf16 (backward)
-    layer_bwd = (not args.no_layer_bwd and cfg.act_dtype == mi.BF16 and cfg.E % 128 == 0)
-    if fp8:       # e4m3 weights with 128 x 128 block scales, quantised once (like loading)
+    # the whole-layer backward (bf16) is timed with the bf16 and e4m3 workloads
+    layer_bwd = (not args.no_layer_bwd and cfg.act_dtype == mi.BF16 and cfg.E % 128 == 0
+                 and cfg.w_dtype != mi.MXFP8)
+    if cfg.w_dtype == mi.MXFP8:   # E8M0 scales per 1 x 32 along K, quantised once
+        w13, sc["w13_scales"] = moe.quantize_mx(w13)
+        w2, sc["w2_scales"] = moe.quantize_mx(w2)
+        ws13, sc["ws13_scales"] = moe.quantize_mx(ws13)
+        ws2, sc["ws2_scales"] = moe.quantize_mx(ws2)
+        w13_bf = w2_bf = ws13_bf = ws2_bf = None
+    if cfg.w_dtype == mi.E4M3:   # 128 x 128 block scales, quantised once (like loading)
         w13, sc["w13_scales"] = moe.quantize_e4m3(w13, 128)
         w2, sc["w2_scales"] = moe.quantize_e4m3(w2, 128)
         ws13, sc["ws13_scales"] = moe.quantize_e4m3(ws13, 128)
@@ -396,7 +410,7 @@ def main():
                                              w13_bf, w2_bf, ws13_bf, ws2_bf, lb,
                                              args.bwd_reps)
     alg = algorithmic(cfg)
-    dtype = {0: "fp32", 1: "bf16", 2: "e4m3"}[cfg.w_dtype]
+    dtype = {0: "fp32", 1: "bf16", 2: "e4m3", 3: "mxfp8"}[cfg.w_dtype]
     per_stage = {}
     for name, t in times.items():
         s = t * 1e-3
@@ -445,7 +459,8 @@ def main():
                          "frac_mfma_peak": round(gemm_flops / gemm_t / PEAK_MFMA[dtype], 4)},
         "permute_GB/s": per_stage["permute"]["GB/s"],
         "permute_note": ("x rows copied to x_perm" if cfg.act_dtype == mi.F32 else
-                         "routing metadata" + (" + e4m3 quantisation of x" if fp8 else "") +
+                         "routing metadata" +
+                         (" + " + dtype + " quantisation of x" if fp8 else "") +
                          "; GEMM1 gathers the rows from x (no x_perm copy)"),
         "stages": per_stage,
         "load": {"max_over_mean": round(float(cnt.max() / cnt.mean()), 3),

@@ -103,8 +103,9 @@ typedef struct {
     int32_t w_dtype;      /* expert GEMM operands: MOE_F32 (with act F32), MOE_BF16,
                              MOE_E4M3 (with act BF16: 1x128 activation scales, 128x128
                              weight scales, fp32 accumulation) or MOE_MXFP8 (with act BF16
-                             and row-major layouts: 1x32 E8M0 scales along K for the
-                             activations and the weights, fp32 accumulation) */
+                             and row-major activations: 1x32 E8M0 scales along K for the
+                             activations and the weights, fp32 accumulation; the weight
+                             codes may be K-blocked, their scales stay row-major) */
     int32_t shared_F;     /* width of the always-on shared expert, 0 = none */
     int32_t a_layout;     /* moe_layout of x_perm / act in the standalone calls (bf16, e4m3) */
     int32_t w_layout;     /* moe_layout of the expert weights (bf16, e4m3) */

@@ -63,7 +63,7 @@ int check_cfg(const moe_config* c) {
         if (c->H % 64 || c->F % 32 || (c->shared_F && c->shared_F % 32)) return MOE_ERR_UNSUPPORTED;
     } else if (c->act_dtype == MOE_BF16) {
         if (c->w_dtype != MOE_BF16 && !is_fp8(c->w_dtype)) return MOE_ERR_UNSUPPORTED;
-        if (c->w_dtype == MOE_MXFP8 && (c->a_layout || c->w_layout)) return MOE_ERR_UNSUPPORTED;
+        if (c->w_dtype == MOE_MXFP8 && c->a_layout) return MOE_ERR_UNSUPPORTED;
         if (c->H % 256 || c->F % 128 || (c->shared_F && c->shared_F % 128))
             return MOE_ERR_UNSUPPORTED;
     } else {

@@ -803,24 +803,29 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_e4m3_kernel(GemmArgs ga) {
 // hardware block, a half-wave's lanes pass their rows' scale byte of that block and the
 // products go straight into the fp32 accumulator: no partial tile, no promotion step.
 //
-// One LDS stage holds 128 K: [BM A rows | BN B rows] x 128 bytes (16-byte chunks XOR-swizzled
-// by the row's low bits, as the other kernels), then one 4-byte word per tile row: the E8M0
-// codes of the row's four blocks of those 128 K (byte b = block b), DMA'd by one 4-byte load
-// per lane and wave.
+// One LDS stage holds BK (128 or 64) K: [BM A rows | BN B rows] x BK bytes, its 16-byte chunks
+// XOR-swizzled so that the eight lanes of a ds_read_b128 phase hit distinct banks (128-byte
+// rows: chunk ^ row % 8; 64-byte rows, two per bank line: chunk ^ (row / 2) % 4), then one
+// 4-byte word per tile row: the E8M0 codes of the row's four blocks of the 128 K that hold
+// the stage (byte b = block b), DMA'd by one 4-byte load per lane and wave. 64-K stages take
+// half the LDS each, so twice as many fit and more loads are in flight per workgroup.
 // GEMM1's epilogue folds the gate in and quantises act per 1 x 32 block: one block is the 32
 // columns of a 32 x 32 sub-tile in one row, held by the 32 lanes of a half-wave, so its
 // amax takes five butterflies and no cross-wave step.
 // ---------------------------------------------------------------------------------------
-template <int KIND, int BM, int BN, int WM, int WN, int STAGES>
+template <int KIND, int BM, int BN, int WM, int WN, int STAGES, int BK>
 struct MxCfg {
     static constexpr int kThreads = WM * WN * kWave;
     static constexpr int kWaves = WM * WN;
-    static constexpr int kRowBytes = 128;                   // 128 e4m3 of K per stage
+    static constexpr int kRowBytes = BK;                    // BK e4m3 of K per stage
+    static constexpr int kChunks = BK / 16;                 // 16-byte chunks per stage row
+    static constexpr int kRpi = 1024 / BK;                  // stage rows per 1 KB DMA
+    static constexpr int kSub = BK / 64;                    // MFMA K steps per stage
     static constexpr int kRows = BM + BN;
     static constexpr int kTileBytes = kRows * kRowBytes;
     static constexpr int kScaleBytes = kWaves * 256;        // 64 words per wave
     static constexpr int kStageBytes = kTileBytes + kScaleBytes;
-    static constexpr int kDma = kRows / 8 / kWaves;         // tile DMAs per wave per stage
+    static constexpr int kDma = kRows / kRpi / kWaves;      // tile DMAs per wave per stage
     static constexpr int kVm = kDma + 1;                    // + the scale-word DMA
     static constexpr int kTM = BM / WM / 32;
     static constexpr int kTN = BN / WN / 32;
@@ -831,12 +836,17 @@ struct MxCfg {
     static constexpr int kEpStride = KIND == 0 ? BN / 2 + 16 : BN + 8;
     static constexpr size_t kEpBytes =
         KIND == 0 ? (size_t)BM * kEpStride + (size_t)BM * (BN / 64) : (size_t)BM * kEpStride * 2;
+    static_assert(BK == 64 || BK == 128, "stage depth");
     static_assert(kRows <= kWaves * 64, "one scale DMA per wave covers the tile's rows");
-    static_assert(kRows % (8 * kWaves) == 0, "DMA split");
+    static_assert(kRows % (kRpi * kWaves) == 0 && BM % (kRpi * kWaves) == 0, "DMA split");
     static_assert(KIND == 1 || kTN % 2 == 0, "GEMM1: gate and up sub-tiles in pairs");
     static_assert(kLds <= 160 * 1024 && kEpBytes <= kLds, "LDS");
     static_assert(STAGES >= 2 && (STAGES - 2) * kVm < 64, "vmcnt");
 };
+
+// physical 16-byte chunk of logical chunk c in stage row r
+template <int BK>
+MOE_DEVICE int mx_swz(int c, int r) { return BK == 128 ? c ^ (r & 7) : c ^ ((r >> 1) & 3); }
 
 template <class C, int NV, class Issue>
 MOE_DEVICE void mx_kloop(int nk, const uint8_t* lds, Issue& issue, const int (&a_off)[C::kTM],
@@ -864,14 +874,16 @@ MOE_DEVICE void mx_kloop(int nk, const uint8_t* lds, Issue& issue, const int (&a
             constexpr int NVv = NV > 0 ? NV : 1;
             const uint8_t* base = lds + stage * C::kStageBytes;
             const uint32_t* words = (const uint32_t*)(base + C::kTileBytes);
-            // this lane's scale bytes: block 2 s + half of its row, as byte 2 s after the shift
+            // this lane's scale bytes: block 2 s + half of its row within the stage's 128 K
+            // (a 64-K stage is the (kt % 2)-th half of it), as byte 2 s after the shift
+            const int sh = 8 * half + (C::kSub == 1 ? 16 * (kt & 1) : 0);
             uint32_t sb[C::kTN], sa[NVv];
 #pragma unroll
-            for (int j = 0; j < C::kTN; ++j) sb[j] = words[b_off[j] >> 7] >> (8 * half);
+            for (int j = 0; j < C::kTN; ++j) sb[j] = words[b_off[j] / C::kRowBytes] >> sh;
 #pragma unroll
-            for (int i = 0; i < NVv; ++i) sa[i] = words[a_off[i] >> 7] >> (8 * half);
+            for (int i = 0; i < NVv; ++i) sa[i] = words[a_off[i] / C::kRowBytes] >> sh;
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
+            for (int s = 0; s < C::kSub; ++s) {
                 i32x8_t bv[C::kTN];
 #pragma unroll
                 for (int j = 0; j < C::kTN; ++j)
@@ -896,9 +908,9 @@ MOE_DEVICE void mx_kloop(int nk, const uint8_t* lds, Issue& issue, const int (&a
     }
 }
 
-template <int KIND, int BM, int BN, int WM, int WN, int STAGES>
+template <int KIND, int BM, int BN, int WM, int WN, int STAGES, int BK>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmArgs ga) {
-    using C = MxCfg<KIND, BM, BN, WM, WN, STAGES>;
+    using C = MxCfg<KIND, BM, BN, WM, WN, STAGES, BK>;
     extern __shared__ __align__(16) uint8_t lds[];
     int mt, nt;
     if (!pick_tile(ga, mt, nt)) return;
@@ -930,8 +942,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmArgs ga) {
     uint32_t src[C::kDma];
 #pragma unroll
     for (int q = 0; q < C::kDma; ++q) {
-        const int r = 8 * (wave + q * C::kWaves) + lane / 8;
-        const int c = (lane % 8) ^ (r & 7);
+        const int r = C::kRpi * (wave + q * C::kWaves) + lane / C::kChunks;
+        const int c = mx_swz<BK>(lane % C::kChunks, r);       // logical chunk this lane loads
         const size_t rowp = r < BM ? (size_t)arow_of(r) * S.a_row : (size_t)wrow_of(r - BM) * S.w_row;
         const size_t step = r < BM ? S.a_kstep : S.w_kstep;
         src[q] = (uint32_t)(rowp + (size_t)(c / 4) * step + (c % 4) * 16);
@@ -951,18 +963,21 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmArgs ga) {
     auto issue = [&](int kstep, int stage) {
         MOE_LDS uint8_t* base = (MOE_LDS uint8_t*)lds + stage * C::kStageBytes;
 #pragma unroll
-        for (int q = 0; q < C::kDma; ++q)
+        for (int q = 0; q < C::kDma; ++q) {
+            constexpr int kSl = BK / 64;                       // 64-byte K slices per stage
+            const bool is_a = q * C::kRpi * C::kWaves < BM;
             __builtin_amdgcn_global_load_lds(
-                (const void*)((q * 8 * C::kWaves < BM ? abase : wbase) + src[q] +
-                              (size_t)kstep * 2 * (q * 8 * C::kWaves < BM ? a_step : w_step)),
+                (const void*)((is_a ? abase : wbase) + src[q] +
+                              (size_t)kstep * kSl * (is_a ? a_step : w_step)),
                 (MOE_LDS void*)(base + (wave + q * C::kWaves) * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)(ssrc + kstep * 4),
+        }
+        __builtin_amdgcn_global_load_lds((const void*)(ssrc + (kstep * BK / 128) * 4),
                                          (MOE_LDS void*)(base + C::kTileBytes + wave * 256), 4, 0, 0);
     };
 
     int a_off[C::kTM], b_off[C::kTN];
 #pragma unroll
-    for (int i = 0; i < C::kTM; ++i) a_off[i] = (wm * (BM / WM) + i * 32 + lane % 32) * 128;
+    for (int i = 0; i < C::kTM; ++i) a_off[i] = (wm * (BM / WM) + i * 32 + lane % 32) * C::kRowBytes;
 #pragma unroll
     for (int j = 0; j < C::kTN; ++j) {
         int row;
@@ -973,22 +988,23 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmArgs ga) {
         } else {
             row = BM + wn * (BN / WN) + j * 32 + lane % 32;
         }
-        b_off[j] = row * 128;
+        b_off[j] = row * C::kRowBytes;
     }
     // the lane's bytes of K sub-step s (64 K): K [16 h, 16 h + 16) and [32 + 16 h, 48 + 16 h)
-    // of it, i.e. logical chunks 4 s + h and 4 s + 2 + h of the 128-byte stage row
+    // of it, i.e. logical chunks 4 s + h and 4 s + 2 + h of the stage row (every row the lane
+    // reads has the low bits of lane % 32)
     int co[2][2];
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
-        for (int u = 0; u < 2; ++u) co[s][u] = (((4 * s + 2 * u + half) ^ (lane & 7)) * 16);
+        for (int u = 0; u < 2; ++u) co[s][u] = mx_swz<BK>(4 * s + 2 * u + half, lane % 32) * 16;
 
     f32x16_t acc[C::kTM][C::kTN];
 #pragma unroll
     for (int i = 0; i < C::kTM; ++i)
 #pragma unroll
         for (int j = 0; j < C::kTN; ++j) acc[i][j] = f32x16_t{};
-    const int nk = K / 128;
+    const int nk = K / BK;
     switch (nvi) {
 #define MOE_MX_CASE(V)                                                                      \
     case V:                                                                                 \
@@ -1225,28 +1241,33 @@ hipError_t run_e4m3(const GemmArgs& ga, int nblocks, hipStream_t s) {
     return hipGetLastError();
 }
 
-// MXFP8 tile configuration (BM, BN, WM, WN, STAGES), both GEMMs
+// MXFP8 tile configuration (BM, BN, WM, WN, STAGES, BK), both GEMMs
 #ifndef MOE_MX_UP_CFG
-#define MOE_MX_UP_CFG 256, 256, 2, 4, 2
+#define MOE_MX_UP_CFG 256, 256, 2, 4, 2, 128
 #endif
 #ifndef MOE_MX_DOWN_CFG
-#define MOE_MX_DOWN_CFG 256, 256, 2, 4, 2
+#define MOE_MX_DOWN_CFG 256, 256, 2, 4, 2, 128
 #endif
 
-template <int KIND, int BM, int BN, int WM, int WN, int STAGES>
+template <int KIND, int BM, int BN, int WM, int WN, int STAGES, int BK>
 hipError_t run_mx(const GemmArgs& ga, int nblocks, hipStream_t s) {
-    using C = MxCfg<KIND, BM, BN, WM, WN, STAGES>;
+    using C = MxCfg<KIND, BM, BN, WM, WN, STAGES, BK>;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(
-            (const void*)gemm_mx_kernel<KIND, BM, BN, WM, WN, STAGES>,
+            (const void*)gemm_mx_kernel<KIND, BM, BN, WM, WN, STAGES, BK>,
             hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::kLds);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    gemm_mx_kernel<KIND, BM, BN, WM, WN, STAGES><<<nblocks, C::kThreads, C::kLds, s>>>(ga);
+    gemm_mx_kernel<KIND, BM, BN, WM, WN, STAGES, BK><<<nblocks, C::kThreads, C::kLds, s>>>(ga);
     return hipGetLastError();
 }
+
+template <int BM, int BN, int WM, int WN, int STAGES, int BK>
+constexpr int mx_bm() { return BM; }
+template <int BM, int BN, int WM, int WN, int STAGES, int BK>
+constexpr int mx_bn() { return BN; }
 
 template <int BM, int BN, int WM, int WN, int STAGES>
 constexpr int f8_bm() { return BM; }
@@ -1256,13 +1277,13 @@ constexpr int f8_bn() { return BN; }
 int bm_for(int kind, int dtype) {
     if (dtype == 0) return kF32BM;
     if (dtype == 2) return kind == 0 ? f8_bm<MOE_F8_UP_CFG>() : f8_bm<MOE_F8_DOWN_CFG>();
-    if (dtype == 3) return kind == 0 ? f8_bm<MOE_MX_UP_CFG>() : f8_bm<MOE_MX_DOWN_CFG>();
+    if (dtype == 3) return kind == 0 ? mx_bm<MOE_MX_UP_CFG>() : mx_bm<MOE_MX_DOWN_CFG>();
     return kind == 0 ? cfg_bm<MOE_BF_UP_CFG>() : cfg_bm<MOE_BF_DOWN_CFG>();
 }
 int bn_for(int kind, int dtype) {
     if (dtype == 0) return 64;
     if (dtype == 2) return kind == 0 ? f8_bn<MOE_F8_UP_CFG>() : f8_bn<MOE_F8_DOWN_CFG>();
-    if (dtype == 3) return kind == 0 ? f8_bn<MOE_MX_UP_CFG>() : f8_bn<MOE_MX_DOWN_CFG>();
+    if (dtype == 3) return kind == 0 ? mx_bn<MOE_MX_UP_CFG>() : mx_bn<MOE_MX_DOWN_CFG>();
     return kind == 0 ? cfg_bn<MOE_BF_UP_CFG>() : cfg_bn<MOE_BF_DOWN_CFG>();
 }
 

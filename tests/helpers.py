@@ -53,6 +53,9 @@ SMALL_MX = {
     "dsv3_mx_deep": mi.scaled(mi.CONFIGS["dsv3_mxfp8"], T=1500, H=256, F=128, E=16, k=4,
                               n_groups=4, topk_groups=2, shared_F=128),
     "dsv3_mx_one_token": mi.scaled(mi.CONFIGS["dsv3_mxfp8"], T=1, H=256, F=128, shared_F=128),
+    # K-blocked weight codes (scales row-major)
+    "dsv3_mx_wkblock": mi.scaled(mi.CONFIGS["dsv3_mxfp8"], T=300, H=512, F=256, shared_F=256,
+                                 w_layout=1),
 }
 
 

@@ -118,12 +118,14 @@ def test_grouped_gemm_mx(moe, name):
     xp_q = oracle.gather_rows(xq, perm["pos"])
     xp_s = oracle.gather_rows(xs, perm["pos"])
     T8 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    W = {k: T8(q[k][0]) for k in ("w13", "w2", "ws13", "ws2")}
+    if cfg.w_layout:
+        W = {k: moe.pack_kblock(v) for k, v in W.items()}
     out = moe.grouped_gemm_swiglu(
-        cfg, T8(xp_q), T8(perm["offsets"]), T8(perm["gate_perm"]), T8(q["w13"][0]),
-        T8(q["w2"][0]), x_perm_scales=T8(xp_s), w13_scales=T8(q["w13"][1]),
-        w2_scales=T8(q["w2"][1]), x_shared=T8(xq), x_shared_scales=T8(xs),
-        ws13=T8(q["ws13"][0]), ws13_scales=T8(q["ws13"][1]), ws2=T8(q["ws2"][0]),
-        ws2_scales=T8(q["ws2"][1]))
+        cfg, T8(xp_q), T8(perm["offsets"]), T8(perm["gate_perm"]), W["w13"], W["w2"],
+        x_perm_scales=T8(xp_s), w13_scales=T8(q["w13"][1]), w2_scales=T8(q["w2"][1]),
+        x_shared=T8(xq), x_shared_scales=T8(xs), ws13=W["ws13"],
+        ws13_scales=T8(q["ws13"][1]), ws2=W["ws2"], ws2_scales=T8(q["ws2"][1]))
     torch.cuda.synchronize()
     rows = np.arange(cfg.A)
     kw = dict(x_scales=xp_s, w13_scales=q["w13"][1], w2_scales=q["w2"][1], mx=True)
@@ -151,6 +153,8 @@ def test_layer_forward_mx(moe, name):
     cfg, inp, q = c["cfg"], c["inp"], c["q"]
     print(f"[mx layer forward] {name}", flush=True)
     w = {k: moe.quantize_mx(getattr(inp, k).cuda()) for k in ("w13", "w2", "ws13", "ws2")}
+    if cfg.w_layout:
+        w = {k: (moe.pack_kblock(v[0]), v[1]) for k, v in w.items()}
     y, ex = moe.layer_forward(cfg, inp.x.cuda(), inp.w_router.cuda(), w["w13"][0], w["w2"][0],
                               to_dev(inp.logit_bias), to_dev(inp.sel_bias),
                               torch.from_numpy(c["logits"]).cuda(), w13_scales=w["w13"][1],
