@@ -21,6 +21,8 @@ import os
 import subprocess
 import threading
 
+import math
+
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -73,6 +75,7 @@ def lib():
             L.orc_expert_wgrad_entries.argtypes = [I32, I32, P, P, P, P, I32, P, I32, P, P,
                                                    P, P, I64, P, P, P, I64, P]
             L.orc_combine.argtypes = [P, P, I32, P, I32, I32, I32, P]
+            L.orc_permute_capacity.argtypes = [P, P, I32, I32, I32, I32, P, P, P, P, P]
             for f in ("orc_quant_rows", "orc_quant_weight", "orc_router_logits", "orc_route",
                       "orc_permute", "orc_expert_rows", "orc_layer_tokens",
                       "orc_expert_bwd_rows", "orc_expert_wgrad_entries", "orc_combine"):
@@ -233,18 +236,59 @@ def route_cfg(cfg, logits, logit_bias=None, sel_bias=None, return_scores=False):
                  cfg.topk_groups, cfg.route_scale, return_scores)
 
 
-def permute(topk_idx, topk_gate, E):
+def permute(topk_idx, topk_gate, E, capacity=None):
+    """Routing metadata. capacity (assignments per expert, or None = dropless): experts accept
+    their assignments in token order while they have slots; dropped ones get pos = -1, and
+    src / gate_perm are filled for rows [0, offsets[E]) only."""
     idx = _i32(topk_idx)
     T, k = idx.shape
     g = _f32(topk_gate)
     counts = np.empty(E, np.int32)
     offsets = np.empty(E + 1, np.int32)
     pos = np.empty((T, k), np.int32)
-    src = np.empty(T * k, np.int32)
-    gp = np.empty(T * k, np.float32)
-    lib().orc_permute(_p(idx), _p(g), T, k, E, _p(counts), _p(offsets), _p(pos), _p(src),
-                      _p(gp))
+    src = np.full(T * k, -1, np.int32)
+    gp = np.zeros(T * k, np.float32)
+    if capacity is None:
+        lib().orc_permute(_p(idx), _p(g), T, k, E, _p(counts), _p(offsets), _p(pos), _p(src),
+                          _p(gp))
+    else:
+        lib().orc_permute_capacity(_p(idx), _p(g), T, k, E, int(capacity), _p(counts),
+                                   _p(offsets), _p(pos), _p(src), _p(gp))
     return dict(counts=counts, offsets=offsets, pos=pos, src=src, gate_perm=gp)
+
+
+def expert_capacity(capacity_factor, T, k, E):
+    """Expert capacity ceil(cf * T * k / E) in double, with cf first rounded to fp32 (the
+    type of the configuration field); None for cf == 0 (dropless)."""
+    cf = float(np.float32(capacity_factor))
+    if cf == 0.0:
+        return None
+    return min(T * k, math.ceil(cf * float(T * k) / float(E)))
+
+
+def drop_slots(topk_idx, pos):
+    """topk_idx with the slots dropped by a capacity (pos < 0) set to -1, the form
+    layer_tokens takes for them."""
+    idx = np.array(_i32(topk_idx), copy=True)
+    idx[np.asarray(pos) < 0] = -1
+    return idx
+
+
+def route_prob_mean(cfg, logits, logit_bias=None):
+    """Mean router probability per expert over the T tokens, float64: p = softmax(l) over all
+    E experts (softmax router) or p = s / sum s with s = fp32(sigmoid(l)) (sigmoid router),
+    l = fp32(logits + logit_bias) as in the routing."""
+    l = np.asarray(logits, np.float32)
+    if logit_bias is not None:
+        l = (l + np.asarray(logit_bias, np.float32)).astype(np.float32)
+    l = l.astype(np.float64)
+    if cfg.router == SOFTMAX_TOPK:
+        z = np.exp(l - l.max(axis=1, keepdims=True))
+        p = z / z.sum(axis=1, keepdims=True)
+    else:
+        s = (1.0 / (1.0 + np.exp(-l))).astype(np.float32).astype(np.float64)
+        p = s / s.sum(axis=1, keepdims=True)
+    return p.mean(axis=0)
 
 
 def gather_rows(x, pos):

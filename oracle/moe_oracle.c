@@ -361,6 +361,36 @@ void orc_permute(const int32_t* topk_idx, const float* topk_gate, int T, int k, 
     free(next);
 }
 
+/* Token-dropping permutation with an expert capacity of cap assignments (the capacity
+ * factor of the study notes, 案例 3 / 踩过的坑: an expert with more assignments than slots
+ * overflows and the surplus is dropped). Each expert accepts the assignments routed to it in
+ * token order (t, then slot j) while it has a free slot; later ones are dropped, pos = -1.
+ * counts = the demand per expert; offsets = exclusive prefix sum of the accepted counts. */
+void orc_permute_capacity(const int32_t* topk_idx, const float* topk_gate, int T, int k, int E,
+                          int cap, int32_t* counts, int32_t* offsets, int32_t* pos,
+                          int32_t* src, float* gate_perm) {
+    for (int e = 0; e < E; ++e) counts[e] = 0;
+    for (int64_t a = 0; a < (int64_t)T * k; ++a) counts[topk_idx[a]] += 1;
+    offsets[0] = 0;
+    for (int e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + (counts[e] < cap ? counts[e] : cap);
+    int32_t* taken = (int32_t*)calloc((size_t)E, sizeof(int32_t));
+    for (int t = 0; t < T; ++t) {
+        for (int j = 0; j < k; ++j) {
+            int64_t a = (int64_t)t * k + j;
+            int e = topk_idx[a];
+            if (taken[e] < cap) {
+                int32_t row = offsets[e] + taken[e]++;
+                pos[a] = row;
+                src[row] = t;
+                gate_perm[row] = topk_gate[a];
+            } else {
+                pos[a] = -1;
+            }
+        }
+    }
+    free(taken);
+}
+
 /* ------------------------------------------------------------------------------------ */
 /* Expert MLP (step "gate(e) * Expert_e(x)")                                            */
 /* ------------------------------------------------------------------------------------ */
@@ -512,6 +542,7 @@ void orc_layer_tokens(int T, int H, int E, int k, int F, int shared_F, const voi
             for (int h = 0; h < H; ++h) y[h] = 0.0;
             for (int j = 0; j < k; ++j) {
                 int e = topk_idx[t * k + j];
+                if (e < 0) continue;                  /* slot dropped by an expert capacity */
                 double g = (double)topk_gate[t * k + j];
                 expert_hidden(&W13, e, x, H, F, fold ? g : 1.0, z, a);
                 if (fp8) quantise_act(a, F, tmp, fp8);
@@ -671,8 +702,10 @@ void orc_combine(const void* y_perm, const void* shared_y, int dtype, const int3
     for (int t = 0; t < T; ++t) {
         for (int h = 0; h < H; ++h) {
             double acc = 0.0;
-            for (int j = 0; j < k; ++j)
-                acc += load(y_perm, dtype, (int64_t)pos[(int64_t)t * k + j] * H + h);
+            for (int j = 0; j < k; ++j) {
+                int64_t r = pos[(int64_t)t * k + j];
+                if (r >= 0) acc += load(y_perm, dtype, r * H + h);   /* < 0: dropped slot */
+            }
             if (shared_y) acc += load(shared_y, dtype, (int64_t)t * H + h);
             y[(int64_t)t * H + h] = acc;
         }
