@@ -85,7 +85,8 @@ typedef enum {
     MOE_OP_GROUPED_GEMM = 1,
     MOE_OP_LAYER_FORWARD = 2,
     MOE_OP_GROUPED_GEMM_BWD = 3,
-    MOE_OP_LAYER_BACKWARD = 4
+    MOE_OP_LAYER_BACKWARD = 4,
+    MOE_OP_ROUTE_STATS = 5
 } moe_op;
 
 /* Layer shape and numerics. Host memory, read only during a call. */
@@ -109,6 +110,13 @@ typedef struct {
     int32_t shared_F;     /* width of the always-on shared expert, 0 = none */
     int32_t a_layout;     /* moe_layout of x_perm / act in the standalone calls (bf16, e4m3) */
     int32_t w_layout;     /* moe_layout of the expert weights (bf16, e4m3) */
+    float capacity_factor;/* 0: dropless (every assignment is computed). > 0: token-dropping
+                             routing with an expert capacity of
+                             C = ceil(capacity_factor * T * k / E) assignments (evaluated in
+                             double); each expert keeps its first C assignments in token
+                             order and drops the rest (the capacity factor / overflowing
+                             expert slots of the study notes, 案例 3 and 踩过的坑). The
+                             backward entry points require 0. */
 } moe_config;
 
 /* Name of a status code (static string; never NULL). */
@@ -133,12 +141,31 @@ int moe_route(const moe_config* cfg, const float* logits, const float* logit_bia
               const float* sel_bias, int32_t* topk_idx, float* topk_gate,
               hipStream_t stream);
 
+/* moe_route plus the load-balancing statistics of the routing, computed in the same kernel
+ * (the expert-utilisation view the study notes ask for before tuning capacity and the
+ * auxiliary loss, 案例 3; the per-expert assignment counts come from moe_permute):
+ *   prob_mean[e] = (1/T) sum_t p[t, e]                                      [E] fp32
+ * with p the router's normalised probabilities of token t over all E experts, from
+ * l = fp32(logits + logit_bias): the softmax router's p = softmax(l); the sigmoid router's
+ * p = s / sum_e s with s = sigmoid(l) as in moe_route (the selection bias excluded).
+ * p is evaluated in fp32 per token; the sums run in a fixed order (per 4-token block, then
+ * over blocks), so the result is deterministic. No loss formula is applied: counts and
+ * prob_mean are the inputs of the usual balance losses. Workspace:
+ * moe_workspace_size(cfg, MOE_OP_ROUTE_STATS). topk_idx / topk_gate as moe_route. */
+int moe_route_stats(const moe_config* cfg, const float* logits, const float* logit_bias,
+                    const float* sel_bias, int32_t* topk_idx, float* topk_gate,
+                    float* prob_mean, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Permute (the routing metadata -- indices, counts, offsets -- and the grouped copy of x),
  * computed on the device without any host synchronisation. Dropless: exactly A = T*k rows.
  *   counts[e]   = number of (t, j) with topk_idx[t, j] == e              [E]    int32
  *   offsets     = exclusive prefix sum of counts (offsets[E] = A)          [E+1]  int32
  *   pos[t*k+j]  = row of assignment (t, j); rows of one expert are in ascending token
  *                 order (a stable counting sort)                           [A]    int32
+ * With cfg->capacity_factor > 0 (capacity C, see moe_config): counts stay the demand, but
+ * offsets scan the kept counts min(counts[e], C), so offsets[E] = A - dropped; an
+ * assignment whose rank in its expert (token order) is >= C gets pos = -1 and no row, and
+ * src / gate_perm / x_perm are written for rows [0, offsets[E]) only.
  *   src[row]    = token of a row                                           [A]    int32
  *   gate_perm[row] = topk_gate of the assignment                           [A]    fp32
  *   x_perm[pos[t*k+j], :] = x[t, :]                                        [A, H]
@@ -210,7 +237,8 @@ int moe_grouped_gemm_down(const moe_config* cfg, const void* act, const void* ac
                           const void* ws2, const void* ws2_scales, void* y_perm,
                           void* shared_y, void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* Unpermute / combine: y[t, :] = sum_{j<k} y_perm[pos[t*k+j], :] (+ shared_y[t, :]),
+/* Unpermute / combine: y[t, :] = sum_{j<k} y_perm[pos[t*k+j], :] (+ shared_y[t, :]), where a
+ * slot with pos < 0 (dropped by an expert capacity) contributes nothing,
  * summed in fp32 in slot order and rounded once to cfg->act_dtype. The gates were folded
  * in before the down projection, so no weight is applied here. A gather: no atomics.
  * shared_y may be NULL. */
@@ -224,7 +252,8 @@ int moe_unpermute_combine(const moe_config* cfg, const void* y_perm, const int32
  * applies to the stand-alone calls only). For bf16, the router's split-K partial sums use the
  * workspace's y_perm region before the down projection writes it.
  * Optional outputs (NULL = skip): logits_out [T, E], topk_idx_out [T, k],
- * topk_gate_out [T, k], counts_out [E]. */
+ * topk_gate_out [T, k], counts_out [E] (the demand per expert, before any capacity).
+ * With cfg->capacity_factor > 0, dropped assignments (see moe_permute) add nothing to y. */
 int moe_layer_forward(const moe_config* cfg, const void* x, const void* w_router,
                       const float* logit_bias, const float* sel_bias, const float* logits_in,
                       const void* w13, const void* w13_scales, const void* w2,

@@ -59,6 +59,7 @@ class MoEConfig:
     backward: bool = False
     a_layout: int = 0              # 0 row-major, 1 K-blocked (expert-grouped activations)
     w_layout: int = 0              # 0 row-major, 1 K-blocked (expert weights)
+    capacity_factor: float = 0.0   # 0 dropless; > 0: expert capacity ceil(cf * T * k / E)
 
     def replace(self, **kw) -> "MoEConfig":
         d = asdict(self)

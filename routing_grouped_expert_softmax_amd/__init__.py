@@ -27,6 +27,7 @@ SOFTMAX_TOPK, SIGMOID_GROUP_TOPK = 0, 1
 LAYOUT_ROWS, LAYOUT_KBLOCK = 0, 1
 OP_PERMUTE, OP_GROUPED_GEMM, OP_LAYER_FORWARD, OP_GROUPED_GEMM_BWD, OP_LAYER_BACKWARD = \
     0, 1, 2, 3, 4
+OP_ROUTE_STATS = 5
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -39,7 +40,7 @@ class MoeConfigC(C.Structure):
                 ("F", C.c_int32), ("n_groups", C.c_int32), ("topk_groups", C.c_int32),
                 ("router", C.c_int32), ("route_scale", C.c_float), ("act_dtype", C.c_int32),
                 ("w_dtype", C.c_int32), ("shared_F", C.c_int32), ("a_layout", C.c_int32),
-                ("w_layout", C.c_int32)]
+                ("w_layout", C.c_int32), ("capacity_factor", C.c_float)]
 
 
 class MoeError(RuntimeError):
@@ -61,6 +62,7 @@ _SIGS = {
     "moe_workspace_size": [CFG, C.c_int, C.POINTER(C.c_size_t)],
     "moe_router_logits": [CFG, P, P, P, P],
     "moe_route": [CFG, P, P, P, P, P, P],
+    "moe_route_stats": [CFG, P, P, P, P, P, P, P, SZ, P],
     "moe_permute": [CFG, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
     "moe_grouped_gemm_swiglu": [CFG, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P,
                                 P, SZ, P],
@@ -93,7 +95,8 @@ def status_string(status: int) -> str:
 def make_config(cfg) -> MoeConfigC:
     return MoeConfigC(cfg.T, cfg.H, cfg.E, cfg.k, cfg.F, cfg.n_groups, cfg.topk_groups,
                       cfg.router, float(cfg.route_scale), cfg.act_dtype, cfg.w_dtype,
-                      cfg.shared_F, getattr(cfg, "a_layout", 0), getattr(cfg, "w_layout", 0))
+                      cfg.shared_F, getattr(cfg, "a_layout", 0), getattr(cfg, "w_layout", 0),
+                      float(getattr(cfg, "capacity_factor", 0.0)))
 
 
 def _check(fn: str, status: int):
@@ -198,6 +201,24 @@ def route(cfg, logits, logit_bias=None, sel_bias=None, topk_idx=None, topk_gate=
         _ptr(topk_idx, torch.int32, (cfg.T, cfg.k), "topk_idx"),
         _ptr(topk_gate, torch.float32, (cfg.T, cfg.k), "topk_gate"), _stream(stream)))
     return topk_idx, topk_gate
+
+
+def route_stats(cfg, logits, logit_bias=None, sel_bias=None, ws=None, stream=None):
+    """moe_route with the fused load-balancing statistics -> (topk_idx, topk_gate,
+    prob_mean [E])."""
+    dev = logits.device
+    topk_idx = torch.empty(cfg.T, cfg.k, dtype=torch.int32, device=dev)
+    topk_gate = torch.empty(cfg.T, cfg.k, dtype=torch.float32, device=dev)
+    prob_mean = torch.empty(cfg.E, dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = workspace(cfg, OP_ROUTE_STATS, dev)
+    c = make_config(cfg)
+    _check("moe_route_stats", _lib.moe_route_stats(
+        C.byref(c), _ptr(logits, torch.float32, (cfg.T, cfg.E), "logits"),
+        _ptr(logit_bias, torch.float32, (cfg.E,), "logit_bias"),
+        _ptr(sel_bias, torch.float32, (cfg.E,), "sel_bias"), _ptr(topk_idx), _ptr(topk_gate),
+        _ptr(prob_mean), _ptr(ws), ws.numel(), _stream(stream)))
+    return topk_idx, topk_gate, prob_mean
 
 
 def permute(cfg, x, topk_idx, topk_gate, want_x_q=False, ws=None, stream=None):

@@ -1,6 +1,8 @@
 // C ABI of the MoE-layer forward: host-side validation, workspace carving, launches.
 // Every entry point validates before it enqueues anything, never allocates device memory,
 // never synchronises and never copies device -> host.
+#include <limits.h>
+#include <math.h>
 #include <string.h>
 
 #include "../../include/moe.h"
@@ -54,6 +56,7 @@ int check_cfg(const moe_config* c) {
         return MOE_ERR_INVALID_ARG;
     }
     if (!(c->route_scale > 0.0f) || c->route_scale != c->route_scale) return MOE_ERR_INVALID_ARG;
+    if (!(c->capacity_factor >= 0.0f) || !isfinite(c->capacity_factor)) return MOE_ERR_INVALID_ARG;
     if ((c->a_layout != MOE_LAYOUT_ROWS && c->a_layout != MOE_LAYOUT_KBLOCK) ||
         (c->w_layout != MOE_LAYOUT_ROWS && c->w_layout != MOE_LAYOUT_KBLOCK))
         return MOE_ERR_INVALID_ARG;
@@ -73,6 +76,14 @@ int check_cfg(const moe_config* c) {
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// Expert capacity in assignments: ceil(capacity_factor * T * k / E), evaluated in double;
+// INT_MAX when capacity_factor == 0 (dropless).
+int capacity_of(const moe_config* c) {
+    if (c->capacity_factor == 0.0f) return INT_MAX;
+    const double cap = ceil((double)c->capacity_factor * ((double)c->T * (double)c->k) / (double)c->E);
+    return cap >= (double)c->T * c->k ? c->T * c->k : (int)cap;
+}
 
 // Stage events of moe_layer_forward (instrumentation): per host thread, caller-owned handles.
 thread_local hipEvent_t g_stage_ev[MOE_N_STAGE_EVENTS];
@@ -209,6 +220,7 @@ LayerBwdWs carve_layer_bwd(const moe_config* c, void* ws) {
 int check_layer_bwd(const moe_config* c) {
     if (c->act_dtype != MOE_BF16 || c->w_dtype != MOE_BF16 || c->a_layout || c->w_layout)
         return MOE_ERR_UNSUPPORTED;
+    if (c->capacity_factor != 0.0f) return MOE_ERR_UNSUPPORTED;     // dropless only
     if (c->E % 128) return MOE_ERR_UNSUPPORTED;          // router GEMM tiles
     return MOE_OK;
 }
@@ -326,8 +338,10 @@ int moe_workspace_size(const moe_config* cfg, int op, size_t* bytes) {
     case MOE_OP_LAYER_FORWARD: *bytes = carve_layer(cfg, nullptr).total; break;
     case MOE_OP_GROUPED_GEMM_BWD:
         if (cfg->act_dtype != MOE_BF16 || cfg->a_layout || cfg->w_layout) return MOE_ERR_UNSUPPORTED;
+        if (cfg->capacity_factor != 0.0f) return MOE_ERR_UNSUPPORTED;
         *bytes = moe::bwd_ws_bytes(cfg->T, cfg->k, cfg->E, cfg->H, cfg->F);
         break;
+    case MOE_OP_ROUTE_STATS: *bytes = moe::route_stats_ws_bytes(cfg->T, cfg->E); break;
     case MOE_OP_LAYER_BACKWARD:
         st = check_layer_bwd(cfg);
         if (st) return st;
@@ -361,6 +375,19 @@ int moe_route(const moe_config* cfg, const float* logits, const float* logit_bia
                                         cfg->route_scale, topk_idx, topk_gate, stream));
 }
 
+int moe_route_stats(const moe_config* cfg, const float* logits, const float* logit_bias,
+                    const float* sel_bias, int32_t* topk_idx, float* topk_gate,
+                    float* prob_mean, void* ws, size_t ws_bytes, hipStream_t stream) {
+    int st = check_cfg(cfg);
+    if (st) return st;
+    if (!logits || !topk_idx || !topk_gate || !prob_mean || !ws) return MOE_ERR_INVALID_ARG;
+    if (ws_bytes < moe::route_stats_ws_bytes(cfg->T, cfg->E)) return MOE_ERR_WORKSPACE;
+    return hip_status(moe::launch_route_stats(cfg->router, logits, logit_bias, sel_bias, cfg->T,
+                                              cfg->E, cfg->k, cfg->n_groups, cfg->topk_groups,
+                                              cfg->route_scale, topk_idx, topk_gate, prob_mean,
+                                              ws, stream));
+}
+
 int moe_permute(const moe_config* cfg, const void* x, const int32_t* topk_idx,
                 const float* topk_gate, int32_t* counts, int32_t* offsets, int32_t* pos,
                 int32_t* src, float* gate_perm, void* x_perm, void* x_perm_scales, void* x_q,
@@ -376,7 +403,8 @@ int moe_permute(const moe_config* cfg, const void* x, const int32_t* topk_idx,
     if ((x_q == nullptr) != (x_q_scales == nullptr)) return MOE_ERR_INVALID_ARG;
     if (ws_bytes < moe::permute_ws_bytes(cfg->T, cfg->k, cfg->E)) return MOE_ERR_WORKSPACE;
     const int mode = cfg->w_dtype == MOE_MXFP8 ? 3 : fp8 ? 2 : (cfg->act_dtype == MOE_F32 ? 0 : 1);
-    return hip_status(moe::launch_permute(mode, cfg->a_layout, x, topk_idx, topk_gate, cfg->T,
+    return hip_status(moe::launch_permute(mode, cfg->a_layout, capacity_of(cfg), x, topk_idx,
+                                          topk_gate, cfg->T,
                                           cfg->H, cfg->E, cfg->k, counts, offsets, pos, src,
                                           gate_perm, x_perm, x_perm_scales, x_q, x_q_scales, ws,
                                           stream));
@@ -545,7 +573,8 @@ int moe_layer_forward(const moe_config* cfg, const void* x, const void* w_router
     // bf16 / fp8 with row-major activations: no x_perm copy; GEMM1 gathers its A rows
     // straight from x (fp8: from the token-order codes x_q and their scales) through src
     const bool gather = MOE_LAYER_FUSED_GATHER && cfg->act_dtype != MOE_F32 && a_kb == 0;
-    e = moe::launch_permute(mode, gather ? -1 : a_kb, x, idx, gate, cfg->T, cfg->H, cfg->E,
+    e = moe::launch_permute(mode, gather ? -1 : a_kb, capacity_of(cfg), x, idx, gate, cfg->T,
+                            cfg->H, cfg->E,
                             cfg->k, counts, L.offsets, L.pos, L.src, L.gate_perm, L.x_perm,
                             L.x_perm_scales, L.x_q, L.x_q_scales, L.scratch, stream);
     if (e == hipSuccess) e = stage_mark(3, stream);
@@ -587,6 +616,7 @@ int moe_grouped_gemm_swiglu_bwd(const moe_config* cfg, const void* dy_perm, cons
     int st = check_cfg(cfg);
     if (st) return st;
     if (cfg->act_dtype != MOE_BF16 || cfg->a_layout || cfg->w_layout) return MOE_ERR_UNSUPPORTED;
+    if (cfg->capacity_factor != 0.0f) return MOE_ERR_UNSUPPORTED;      // dropless only
     if (!dy_perm || !x_perm || !z || !act || !offsets || !w13 || !w2 || !dx_perm || !dw13 ||
         !dw2 || !ws)
         return MOE_ERR_INVALID_ARG;
@@ -622,11 +652,11 @@ int moe_layer_backward(const moe_config* cfg, const void* x, const void* w_route
     const int T = cfg->T, H = cfg->H, E = cfg->E, k = cfg->k, F = cfg->F, sF = cfg->shared_F;
     const int A = T * k;
     // expert-grouped x and dY (the permute of dY is the backward of the combine)
-    hipError_t e = moe::launch_permute(1, 0, x, topk_idx, topk_gate, T, H, E, k, L.counts,
+    hipError_t e = moe::launch_permute(1, 0, INT_MAX, x, topk_idx, topk_gate, T, H, E, k, L.counts,
                                        L.offsets, L.pos, L.src, L.gate_perm, L.x_perm, nullptr,
                                        nullptr, nullptr, L.perm_scratch, stream);
     if (e == hipSuccess)
-        e = moe::launch_permute(1, 0, dy, topk_idx, topk_gate, T, H, E, k, L.counts2,
+        e = moe::launch_permute(1, 0, INT_MAX, dy, topk_idx, topk_gate, T, H, E, k, L.counts2,
                                 L.offsets2, L.pos2, L.src2, L.gate_perm2, L.dy_perm, nullptr,
                                 nullptr, nullptr, L.perm_scratch, stream);
     // recompute Z and act of GEMM1 (routed, then the shared expert)

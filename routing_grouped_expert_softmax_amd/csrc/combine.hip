@@ -1,5 +1,6 @@
 // Unpermute / combine: y[t] = sum_j y_perm[pos[t, j]] (+ shared_y[t]), fp32 sum in slot
-// order, one rounding to the output dtype. The gates were folded into the activations
+// order, one rounding to the output dtype; slots dropped by an expert capacity (pos < 0)
+// contribute nothing. The gates were folded into the activations
 // before the down projection (memory-efficient permutation, technical summary section
 // 2.2), so this is a pure gather-sum: no weights, no atomics, deterministic.
 //
@@ -55,6 +56,10 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(const uint4* __restri
     if (t >= T) return;
     const int my_pos = lane < k ? pos[(size_t)t * k + lane] : 0;
     if (KC > 0) {
+        // the k rows of the token, read from lanes 0 .. k-1 while every lane is active
+        int rj[KC > 0 ? KC : 1];
+#pragma unroll
+        for (int j = 0; j < KC; ++j) rj[j] = __shfl(my_pos, j);
         // U chunks per lane per step: U * (KC + 1) loads in flight before the first add
         constexpr int U = MOE_COMBINE_U;
         for (int c0 = 0; c0 < row_chunks; c0 += U * kWave) {
@@ -64,10 +69,10 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(const uint4* __restri
                 const int c = c0 + u * kWave + lane;
                 const bool ok = c < row_chunks;
 #pragma unroll
-                for (int j = 0; j < KC; ++j) {
-                    const int r = __shfl(my_pos, j);
-                    v[u][j] = ok ? load_stream(y_perm + (size_t)r * row_chunks + c) : uint4{};
-                }
+                for (int j = 0; j < KC; ++j)
+                    v[u][j] = ok && rj[j] >= 0
+                                  ? load_stream(y_perm + (size_t)rj[j] * row_chunks + c)
+                                  : uint4{};
                 sv[u] = shared_y && ok ? load_stream(shared_y + (size_t)t * row_chunks + c)
                                        : uint4{};
             }
@@ -77,7 +82,8 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(const uint4* __restri
                 if (c >= row_chunks) continue;
                 float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-                for (int j = 0; j < KC; ++j) add_bf16x8(acc, v[u][j]);
+                for (int j = 0; j < KC; ++j)
+                    if (rj[j] >= 0) add_bf16x8(acc, v[u][j]);
                 if (shared_y) add_bf16x8(acc, sv[u]);
                 uint4 o;
                 o.x = pack_bf16x2(acc[0], acc[1]);
@@ -95,7 +101,7 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(const uint4* __restri
         float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
         for (int j = 0; j < k; ++j) {
             const int r = __shfl(my_pos, j);
-            if (ok) add_bf16x8(acc, y_perm[(size_t)r * row_chunks + c]);
+            if (ok && r >= 0) add_bf16x8(acc, y_perm[(size_t)r * row_chunks + c]);
         }
         if (shared_y && ok) add_bf16x8(acc, shared_y[(size_t)t * row_chunks + c]);
         if (!ok) continue;
@@ -124,7 +130,7 @@ __global__ __launch_bounds__(256) void combine_f32_kernel(const float4* __restri
         float4 acc = make_float4(0, 0, 0, 0);
         for (int j = 0; j < k; ++j) {
             int r = __shfl(my_pos, j);
-            if (ok) {
+            if (ok && r >= 0) {
                 float4 v = y_perm[(size_t)r * row_chunks + c];
                 acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
             }

@@ -26,6 +26,16 @@ hipError_t launch_route(int router, const float* logits, const float* logit_bias
                         int topk_groups, float route_scale, int32_t* topk_idx,
                         float* topk_gate, hipStream_t s);
 
+// launch_route plus the load-balancing statistics: prob_mean[e] = (1/T) sum_t p[t, e] with p
+// the router's normalised probabilities (softmax router: softmax of l over all E; sigmoid
+// router: s / sum s), per-block sums reduced in a fixed order. Workspace:
+// route_stats_ws_bytes(T, E).
+size_t route_stats_ws_bytes(int T, int E);
+hipError_t launch_route_stats(int router, const float* logits, const float* logit_bias,
+                              const float* sel_bias, int T, int E, int k, int n_groups,
+                              int topk_groups, float route_scale, int32_t* topk_idx,
+                              float* topk_gate, float* prob_mean, void* ws, hipStream_t s);
+
 // gates -> logits: dl [T, E] (bf16, and fp32 when dl_f32 != nullptr) from the gates'
 // gradient in expert-grouped order (dgate_perm [T*k], read through pos)
 hipError_t launch_route_backward(int router, const float* logits, const float* logit_bias,
@@ -41,6 +51,9 @@ hipError_t launch_permute(int mode /*0 f32, 1 bf16, 2 e4m3 from bf16, 3 MXFP8 fr
                           int kblock /*1: x_perm K-blocked (not with MXFP8); -1: no x_perm
                                        (routing metadata, and in the fp8 modes the token-order
                                        x_q, only)*/,
+                          int cap /*expert capacity: assignments of rank >= cap within their
+                                    expert (token order) are dropped, pos = -1; INT_MAX =
+                                    dropless*/,
                           const void* x,
                           const int32_t* topk_idx, const float* topk_gate, int T, int H,
                           int E, int k, int32_t* counts, int32_t* offsets, int32_t* pos,

@@ -45,9 +45,10 @@ __global__ __launch_bounds__(256) void perm_count_kernel(const int32_t* __restri
         chunk_counts[(size_t)blockIdx.x * E + e] = hist[e];
 }
 
-// Single block of 1024 threads (E <= 1024 is validated by the ABI).
+// Single block of 1024 threads (E <= 1024 is validated by the ABI). counts[e] is expert e's
+// demand; offsets scan the kept counts min(counts[e], cap), and offsets[E] is their total.
 __global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t* __restrict__ chunk_counts,
-                                                         int nchunk, int E, int A,
+                                                         int nchunk, int E, int cap,
                                                          int32_t* __restrict__ counts,
                                                          int32_t* __restrict__ offsets) {
     __shared__ int32_t wsum[16];
@@ -68,9 +69,10 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t* __restrict__ c
         }
         counts[e] = run;
     }
-    // exclusive scan of the totals over experts: wavefront inclusive scans, then wave sums
+    const int kept = run < cap ? run : cap;
+    // exclusive scan of the kept totals over experts: wavefront inclusive scans, then wave sums
     const int lane = e % kWave, wave = e / kWave;
-    int v = run;
+    int v = kept;
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
         int o = __shfl_up(v, off);
@@ -80,15 +82,16 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t* __restrict__ c
     __syncthreads();
     int before = 0;
     for (int w = 0; w < wave; ++w) before += wsum[w];
-    int excl = before + v - run;
+    int excl = before + v - kept;
     if (e < E) offsets[e] = excl;
-    if (e == 0) offsets[E] = A;
+    if (e == E - 1) offsets[E] = excl + kept;
 }
 
-// One wavefront per chunk.
+// One wavefront per chunk. An assignment whose rank among its expert's assignments (token
+// order) reaches cap is dropped: pos = -1, and it takes no row.
 __global__ __launch_bounds__(64) void perm_rank_kernel(const int32_t* __restrict__ idx,
                                                        const float* __restrict__ gate, int A,
-                                                       int E, int k, int nbits,
+                                                       int E, int k, int nbits, int cap,
                                                        const int32_t* __restrict__ chunk_base,
                                                        const int32_t* __restrict__ offsets,
                                                        int32_t* __restrict__ pos,
@@ -96,8 +99,7 @@ __global__ __launch_bounds__(64) void perm_rank_kernel(const int32_t* __restrict
                                                        float* __restrict__ gate_perm) {
     extern __shared__ int32_t running[];
     const int lane = threadIdx.x;
-    for (int e = lane; e < E; e += kWave)
-        running[e] = offsets[e] + chunk_base[(size_t)blockIdx.x * E + e];
+    for (int e = lane; e < E; e += kWave) running[e] = chunk_base[(size_t)blockIdx.x * E + e];
     __syncthreads();
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     const int a0 = blockIdx.x * kPermChunk;
@@ -117,10 +119,15 @@ __global__ __launch_bounds__(64) void perm_rank_kernel(const int32_t* __restrict
         if (active && (same >> lane) == 1ull) running[e] = base + __popcll(same);
         __builtin_amdgcn_wave_barrier();
         if (active) {
-            int row = base + rank;
-            pos[a] = row;
-            src[row] = a / k;
-            gate_perm[row] = gate[a];
+            const int rin = base + rank;                  // rank within the expert
+            if (rin < cap) {
+                const int row = offsets[e] + rin;
+                pos[a] = row;
+                src[row] = a / k;
+                gate_perm[row] = gate[a];
+            } else {
+                pos[a] = -1;
+            }
         }
         if (a0 + it + kWave >= A) break;
     }
@@ -149,6 +156,7 @@ __global__ __launch_bounds__(256) void perm_copy_kernel(const uint4* __restrict_
         }
         for (int j = 0; j < k; ++j) {
             const int r = __shfl(my_pos, j);
+            if (r < 0) continue;                          // dropped by the capacity
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int c = c0 + u * kWave + lane;
@@ -229,7 +237,7 @@ __global__ __launch_bounds__(256) void perm_quant_copy_kernel(
         }
         for (int j = 0; j < k; ++j) {
             int r = __shfl(my_pos, j);
-            if (ok) {
+            if (ok && r >= 0) {
                 const size_t o = kblock ? ((size_t)(c / 8) * A + r) * 8 + c % 8
                                         : (size_t)r * row_chunks + c;
                 x_perm[o] = packed;
@@ -246,9 +254,9 @@ __global__ __launch_bounds__(256) void perm_quant_copy_kernel(
 // 1 x 128 scales gathered alongside).
 constexpr int kGatherSlices = MOE_GATHER_SLICES;
 __global__ __launch_bounds__(256) void perm_gather_kblock_kernel(
-    const uint8_t* __restrict__ xin, const int32_t* __restrict__ src, int A, int row_bytes,
-    uint8_t* __restrict__ x_perm, const float* __restrict__ in_scales, int nsc,
-    float* __restrict__ out_scales) {
+    const uint8_t* __restrict__ xin, const int32_t* __restrict__ src, int A,
+    const int32_t* __restrict__ live_rows, int row_bytes, uint8_t* __restrict__ x_perm,
+    const float* __restrict__ in_scales, int nsc, float* __restrict__ out_scales) {
     const int lane = threadIdx.x % kWave;
     const int64_t w = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
     const int slices = row_bytes / 64;
@@ -257,7 +265,7 @@ __global__ __launch_bounds__(256) void perm_gather_kblock_kernel(
     if (w >= rblocks * sgroups) return;
     const int rb = (int)(w / sgroups), sg = (int)(w % sgroups);
     const int r = rb * 16 + lane / 4;
-    if (r >= A) return;
+    if (r >= *live_rows) return;                      // A, less any dropped assignments
     const int t = src[r];
     const uint8_t* in = xin + (size_t)t * row_bytes + (lane % 4) * 16;
     uint8_t* out = x_perm + (size_t)r * 64 + (lane % 4) * 16;
@@ -296,7 +304,7 @@ size_t permute_ws_bytes(int T, int k, int E) {
     return nchunk * (size_t)E * sizeof(int32_t);
 }
 
-hipError_t launch_permute(int mode, int kblock, const void* x, const int32_t* topk_idx,
+hipError_t launch_permute(int mode, int kblock, int cap, const void* x, const int32_t* topk_idx,
                           const float* topk_gate, int T, int H, int E, int k,
                           int32_t* counts, int32_t* offsets, int32_t* pos, int32_t* src,
                           float* gate_perm, void* x_perm, void* x_perm_scales, void* x_q,
@@ -307,10 +315,10 @@ hipError_t launch_permute(int mode, int kblock, const void* x, const int32_t* to
     int nbits = 0;
     while ((1 << nbits) < E) ++nbits;
     perm_count_kernel<<<nchunk, 256, E * sizeof(int32_t), s>>>(topk_idx, A, E, chunk_counts);
-    perm_scan_kernel<<<1, 1024, 0, s>>>(chunk_counts, nchunk, E, A, counts, offsets);
+    perm_scan_kernel<<<1, 1024, 0, s>>>(chunk_counts, nchunk, E, cap, counts, offsets);
     perm_rank_kernel<<<nchunk, 64, E * sizeof(int32_t), s>>>(topk_idx, topk_gate, A, E, k,
-                                                             nbits, chunk_counts, offsets, pos,
-                                                             src, gate_perm);
+                                                             nbits, cap, chunk_counts, offsets,
+                                                             pos, src, gate_perm);
     if (kblock < 0) {           // metadata only (the GEMM gathers the rows itself)
         if (mode == 2)
             return launch_quantize(x, 1, 1, T, H, 1, (uint8_t*)x_q, (float*)x_q_scales, s);
@@ -323,7 +331,8 @@ hipError_t launch_permute(int mode, int kblock, const void* x, const int32_t* to
         const int64_t waves = (int64_t)((A + 15) / 16) *
                               ((row_bytes / 64 + kGatherSlices - 1) / kGatherSlices);
         perm_gather_kblock_kernel<<<(unsigned)((waves + 3) / 4), 256, 0, s>>>(
-            (const uint8_t*)in, src, A, row_bytes, (uint8_t*)x_perm, in_sc, H / 128, out_sc);
+            (const uint8_t*)in, src, A, offsets + E, row_bytes, (uint8_t*)x_perm, in_sc,
+            H / 128, out_sc);
     };
     if (kblock && mode == 1) {
         gather(x, H * 2, nullptr, nullptr);

@@ -13,6 +13,34 @@ namespace moe {
 namespace {
 
 constexpr int kRouteWaves = 4;      // tokens per 256-thread block
+constexpr int kStatsMaxE = 1024;    // E limit of the ABI
+
+MOE_DEVICE float wave_max_f32(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+    return v;
+}
+
+// Load-balancing statistics (STATS): the block's sum over its kRouteWaves tokens of the
+// router probabilities p[t, :] (each wave's token in LDS, then summed in wave order per
+// expert) -> prob_part[block, E]. Tokens past T add zeros.
+template <int VPL>
+MOE_DEVICE void stats_block_sum(const float (&p)[VPL], bool valid, int E, int lane, int wave,
+                                float* __restrict__ prob_part) {
+    __shared__ float pl[kRouteWaves][kStatsMaxE];
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+        const int e = v * kWave + lane;
+        if (e < E) pl[wave][e] = valid ? p[v] : 0.0f;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += kRouteWaves * kWave) {
+        float acc = pl[0][e];
+#pragma unroll
+        for (int w = 1; w < kRouteWaves; ++w) acc += pl[w][e];
+        prob_part[(size_t)blockIdx.x * E + e] = acc;
+    }
+}
 
 // ---------------------------------------------------------------------------------------
 // top-k over the keys a wavefront holds; returns, in lane j < k, the j-th expert
@@ -37,24 +65,48 @@ MOE_DEVICE int wave_topk(uint64_t (&rk)[VPL], int k, int lane) {
 // ---------------------------------------------------------------------------------------
 // softmax router: select on l = logit + bias; gates = softmax over the selected logits
 // ---------------------------------------------------------------------------------------
-template <int VPL>
+// STATS: also the block's part of the mean router probability, p = softmax of l over all E
+// experts (fp32: max, exp, wave sum, divide).
+template <int VPL, bool STATS>
 __global__ __launch_bounds__(256) void route_softmax_kernel(
     const float* __restrict__ logits, const float* __restrict__ logit_bias, int T, int E,
-    int k, int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate) {
-    const int lane = threadIdx.x % kWave;
-    const int t = blockIdx.x * kRouteWaves + threadIdx.x / kWave;
-    if (t >= T) return;
-    const float* row = logits + (size_t)t * E;
+    int k, int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate,
+    float* __restrict__ prob_part) {
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int t = blockIdx.x * kRouteWaves + wave;
+    const bool valid = t < T;
+    if (!STATS && !valid) return;
+    const float* row = logits + (size_t)(valid ? t : 0) * E;
     uint64_t rk[VPL];
+    float lv[VPL];
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
         int e = v * kWave + lane;
         rk[v] = 0;
+        lv[v] = -INFINITY;
         if (e < E) {
             float l = row[e];
             if (logit_bias) l = l + logit_bias[e];
             rk[v] = rank_key(l, e);
+            lv[v] = l;
         }
+    }
+    if (STATS) {
+        float m = lv[0];
+#pragma unroll
+        for (int v = 1; v < VPL; ++v) m = fmaxf(m, lv[v]);
+        m = wave_max_f32(m);
+        float p[VPL], den = 0.0f;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) {
+            p[v] = v * kWave + lane < E ? expf(lv[v] - m) : 0.0f;
+            den += p[v];
+        }
+        den = wave_sum_f32(den);
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) p[v] = p[v] / den;
+        stats_block_sum<VPL>(p, valid, E, lane, wave, prob_part);
+        if (!valid) return;
     }
     int e = wave_topk<VPL>(rk, k, lane);
     float l = 0.0f;
@@ -79,27 +131,44 @@ MOE_DEVICE float sigmoid_rounded(float l) {
 // ---------------------------------------------------------------------------------------
 // sigmoid + group-limited router (DeepSeek-V3 style)
 // ---------------------------------------------------------------------------------------
-template <int VPL>
+// STATS: also the block's part of the mean router probability, p = s / sum_e s over all E
+// experts (s = the sigmoid score without the selection bias; fp32 wave sum, divide).
+template <int VPL, bool STATS>
 __global__ __launch_bounds__(256) void route_sigmoid_group_kernel(
     const float* __restrict__ logits, const float* __restrict__ logit_bias,
     const float* __restrict__ sel_bias, int T, int E, int k, int n_groups, int topk_groups,
-    float route_scale, int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate) {
-    const int lane = threadIdx.x % kWave;
-    const int t = blockIdx.x * kRouteWaves + threadIdx.x / kWave;
-    if (t >= T) return;
-    const float* row = logits + (size_t)t * E;
+    float route_scale, int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate,
+    float* __restrict__ prob_part) {
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int t = blockIdx.x * kRouteWaves + wave;
+    const bool valid = t < T;
+    if (!STATS && !valid) return;
+    const float* row = logits + (size_t)(valid ? t : 0) * E;
     const int per = E / n_groups;
-    float key[VPL];
+    float key[VPL], sv[VPL];
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
         int e = v * kWave + lane;
         key[v] = 0.0f;
+        sv[v] = 0.0f;
         if (e < E) {
             float l = row[e];
             if (logit_bias) l = l + logit_bias[e];
             float s = sigmoid_rounded(l);
+            sv[v] = s;
             key[v] = sel_bias ? s + sel_bias[e] : s;
         }
+    }
+    if (STATS) {
+        float den = 0.0f;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) den += sv[v];
+        den = wave_sum_f32(den);
+        float p[VPL];
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) p[v] = sv[v] / den;
+        stats_block_sum<VPL>(p, valid, E, lane, wave, prob_part);
+        if (!valid) return;
     }
     int kept = 0;
     if (per == 32 && E == VPL * kWave) {
@@ -379,26 +448,52 @@ template <int VPL>
 static void route_launch(int router, const float* logits, const float* logit_bias,
                          const float* sel_bias, int T, int E, int k, int n_groups,
                          int topk_groups, float route_scale, int32_t* topk_idx,
-                         float* topk_gate, hipStream_t s) {
+                         float* topk_gate, float* prob_part, hipStream_t s) {
     int blocks = (T + kRouteWaves - 1) / kRouteWaves;
-    if (router == 0)
-        route_softmax_kernel<VPL><<<blocks, 256, 0, s>>>(logits, logit_bias, T, E, k,
-                                                         topk_idx, topk_gate);
-    else
-        route_sigmoid_group_kernel<VPL><<<blocks, 256, 0, s>>>(
-            logits, logit_bias, sel_bias, T, E, k, n_groups, topk_groups, route_scale,
-            topk_idx, topk_gate);
+    if (router == 0) {
+        if (prob_part)
+            route_softmax_kernel<VPL, true><<<blocks, 256, 0, s>>>(logits, logit_bias, T, E, k,
+                                                                   topk_idx, topk_gate, prob_part);
+        else
+            route_softmax_kernel<VPL, false><<<blocks, 256, 0, s>>>(logits, logit_bias, T, E, k,
+                                                                    topk_idx, topk_gate, nullptr);
+    } else {
+        if (prob_part)
+            route_sigmoid_group_kernel<VPL, true><<<blocks, 256, 0, s>>>(
+                logits, logit_bias, sel_bias, T, E, k, n_groups, topk_groups, route_scale,
+                topk_idx, topk_gate, prob_part);
+        else
+            route_sigmoid_group_kernel<VPL, false><<<blocks, 256, 0, s>>>(
+                logits, logit_bias, sel_bias, T, E, k, n_groups, topk_groups, route_scale,
+                topk_idx, topk_gate, nullptr);
+    }
 }
 
-hipError_t launch_route(int router, const float* logits, const float* logit_bias,
-                        const float* sel_bias, int T, int E, int k, int n_groups,
-                        int topk_groups, float route_scale, int32_t* topk_idx,
-                        float* topk_gate, hipStream_t s) {
+// Deterministic column sums: out[blockIdx.y, c] = scale * sum of rows
+// [blockIdx.y * rpb, min((blockIdx.y + 1) * rpb, R)) of in[R, C], added in row order.
+__global__ __launch_bounds__(256) void colsum_kernel(const float* __restrict__ in, int R, int C,
+                                                     int rpb, float inv,
+                                                     float* __restrict__ out) {
+    const int c = blockIdx.x * 256 + threadIdx.x;
+    if (c >= C) return;
+    const int r0 = blockIdx.y * rpb;
+    const int r1 = r0 + rpb < R ? r0 + rpb : R;
+    float acc = 0.0f;
+    for (int r = r0; r < r1; ++r) acc += in[(size_t)r * C + c];
+    out[(size_t)blockIdx.y * C + c] = acc * inv;
+}
+
+constexpr int kStatsRpb = 64;       // first-level rows per column-sum block
+
+hipError_t route_dispatch(int router, const float* logits, const float* logit_bias,
+                          const float* sel_bias, int T, int E, int k, int n_groups,
+                          int topk_groups, float route_scale, int32_t* topk_idx,
+                          float* topk_gate, float* prob_part, hipStream_t s) {
     int vpl = (E + kWave - 1) / kWave;
 #define MOE_ROUTE_CASE(V)                                                                   \
     if (vpl <= V) {                                                                         \
         route_launch<V>(router, logits, logit_bias, sel_bias, T, E, k, n_groups,            \
-                        topk_groups, route_scale, topk_idx, topk_gate, s);                  \
+                        topk_groups, route_scale, topk_idx, topk_gate, prob_part, s);       \
         return hipGetLastError();                                                           \
     }
     MOE_ROUTE_CASE(1)
@@ -408,6 +503,37 @@ hipError_t launch_route(int router, const float* logits, const float* logit_bias
     MOE_ROUTE_CASE(16)
 #undef MOE_ROUTE_CASE
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_route(int router, const float* logits, const float* logit_bias,
+                        const float* sel_bias, int T, int E, int k, int n_groups,
+                        int topk_groups, float route_scale, int32_t* topk_idx,
+                        float* topk_gate, hipStream_t s) {
+    return route_dispatch(router, logits, logit_bias, sel_bias, T, E, k, n_groups, topk_groups,
+                          route_scale, topk_idx, topk_gate, nullptr, s);
+}
+
+size_t route_stats_ws_bytes(int T, int E) {
+    const size_t R = (size_t)(T + kRouteWaves - 1) / kRouteWaves;
+    const size_t R2 = (R + kStatsRpb - 1) / kStatsRpb;
+    return ((R + R2) * (size_t)E * sizeof(float) + 255) / 256 * 256;
+}
+
+hipError_t launch_route_stats(int router, const float* logits, const float* logit_bias,
+                              const float* sel_bias, int T, int E, int k, int n_groups,
+                              int topk_groups, float route_scale, int32_t* topk_idx,
+                              float* topk_gate, float* prob_mean, void* ws, hipStream_t s) {
+    const int R = (T + kRouteWaves - 1) / kRouteWaves;
+    const int R2 = (R + kStatsRpb - 1) / kStatsRpb;
+    float* part = (float*)ws;
+    float* part2 = part + (size_t)R * E;
+    hipError_t e = route_dispatch(router, logits, logit_bias, sel_bias, T, E, k, n_groups,
+                                  topk_groups, route_scale, topk_idx, topk_gate, part, s);
+    if (e != hipSuccess) return e;
+    const unsigned cb = (unsigned)((E + 255) / 256);
+    colsum_kernel<<<dim3(cb, (unsigned)R2), 256, 0, s>>>(part, R, E, kStatsRpb, 1.0f, part2);
+    colsum_kernel<<<dim3(cb, 1), 256, 0, s>>>(part2, R2, E, R2, 1.0f / (float)T, prob_mean);
+    return hipGetLastError();
 }
 
 }  // namespace moe
