@@ -346,6 +346,8 @@ def main():
     if cfg.w_layout:
         pk = lambda t: None if t is None else moe.pack_kblock(t)  # noqa: E731
         w13, w2, ws13, ws2 = pk(w13), pk(w2), pk(ws13), pk(ws2)
+        if cfg.w_dtype == mi.MXFP8:      # K-blocked codes take blocked scales
+            sc = {k: moe.pack_mx_scales(v) for k, v in sc.items()}
         torch.cuda.synchronize()
     if args.calib_copy_gib > 0:
         nb = int(args.calib_copy_gib * (1 << 30))

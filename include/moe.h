@@ -105,8 +105,8 @@ typedef struct {
                              MOE_E4M3 (with act BF16: 1x128 activation scales, 128x128
                              weight scales, fp32 accumulation) or MOE_MXFP8 (with act BF16
                              and row-major activations: 1x32 E8M0 scales along K for the
-                             activations and the weights, fp32 accumulation; the weight
-                             codes may be K-blocked, their scales stay row-major) */
+                             activations and the weights, fp32 accumulation; K-blocked
+                             weight codes take scales packed by moe_pack_mx_scales) */
     int32_t shared_F;     /* width of the always-on shared expert, 0 = none */
     int32_t a_layout;     /* moe_layout of x_perm / act in the standalone calls (bf16, e4m3) */
     int32_t w_layout;     /* moe_layout of the expert weights (bf16, e4m3) */
@@ -197,7 +197,8 @@ int moe_permute(const moe_config* cfg, const void* x, const int32_t* topk_idx,
  * act_scales [A, F/128] (quantised per 1 x 128 after the fold). With MOE_MXFP8 every
  * operand has E8M0 bytes per 1 x 32 block along K instead: x_perm_scales [A, H/32],
  * w13_scales [E, 2F, H/32], w2_scales [E, H, F/32], act_scales [A, F/32] (act quantised per
- * 1 x 32 after the fold), and the shared expert's likewise. Otherwise all scale pointers
+ * 1 x 32 after the fold), and the shared expert's likewise; with K-blocked weights
+ * (w_layout) the weight scales are in the order of moe_pack_mx_scales. Otherwise all scale pointers
  * must be NULL and act has cfg->act_dtype. y_perm has cfg->act_dtype.
  * Shared expert (cfg->shared_F > 0): the same SwiGLU with weight 1 applied to every token
  * of x_shared [T, H] (e4m3 + x_shared_scales in fp8 mode), weights ws13 [2*shared_F, H],
@@ -349,6 +350,15 @@ int moe_quantize_e4m3(const void* in, int32_t in_dtype, int64_t n_mat, int32_t r
  * section 3.) */
 int moe_quantize_mx(const void* in, int32_t in_dtype, int64_t rows, int32_t cols, uint8_t* q,
                     uint8_t* scales, hipStream_t stream);
+
+/* Re-layout of MXFP8 weight scales for K-blocked weights: n_mat matrices of E8M0 bytes
+ * [rows, cols] (cols = K/32, a multiple of 4) -> [n_mat][cols/4][rows][4 bytes], i.e. the four
+ * block codes of one row's 128 K form a word and the words of consecutive rows are adjacent,
+ * so that a GEMM tile's scales for one 128-K step are one contiguous run. Weights in
+ * MOE_LAYOUT_KBLOCK (cfg->w_layout) take their MXFP8 scales in this order; in and out must
+ * not overlap. A pure data movement, run once per weight set. */
+int moe_pack_mx_scales(const uint8_t* in, int64_t n_mat, int32_t rows, int32_t cols,
+                       uint8_t* out, hipStream_t stream);
 
 #ifdef __cplusplus
 }

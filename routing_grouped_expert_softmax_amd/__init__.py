@@ -73,6 +73,7 @@ _SIGS = {
     "moe_grouped_gemm_swiglu_bwd": [CFG, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
     "moe_quantize_e4m3": [P, I32, I64, I32, I32, I32, I32, P, P, P],
     "moe_quantize_mx": [P, I32, I64, I32, P, P, P],
+    "moe_pack_mx_scales": [P, I64, I32, I32, P, P],
     "moe_pack_kblock": [P, I64, I32, I32, I32, P, P],
     "moe_set_stage_events": [P, I32],
     "moe_layer_backward": [CFG, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
@@ -488,6 +489,18 @@ def quantize_mx(t, stream=None):
     _check("moe_quantize_mx", _lib.moe_quantize_mx(
         _ptr(t, name="input"), dt, rows, cols, _ptr(q), _ptr(s), _stream(stream)))
     return q, s
+
+
+def pack_mx_scales(s, stream=None):
+    """MXFP8 weight scales [..., rows, cols] (uint8 E8M0, cols = K/32) -> the blocked order of
+    K-blocked weights, [..., cols/4, rows, 4] stored in a tensor of the input's shape."""
+    shape = tuple(s.shape)
+    rows, cols = shape[-2], shape[-1]
+    n = s.numel() // (rows * cols)
+    out = torch.empty_like(s)
+    _check("moe_pack_mx_scales", _lib.moe_pack_mx_scales(
+        _ptr(s, torch.uint8, name="scales"), n, rows, cols, _ptr(out), _stream(stream)))
+    return out
 
 
 def pack_kblock(t, out=None, stream=None):

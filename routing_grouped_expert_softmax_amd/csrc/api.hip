@@ -242,13 +242,22 @@ int run_up(const moe_config* c, int a_kb, const void* x_perm, const void* x_perm
            const void* w13_scales, const void* x_shared, const void* x_shared_scales,
            const void* ws13, const void* ws13_scales, void* act, void* act_scales,
            void* shared_act, void* shared_act_scales, void* z_out, void* sched,
-           hipStream_t stream, const int32_t* a_rows = nullptr) {
+           hipStream_t stream, const int32_t* a_rows = nullptr, bool mx_blocked = false) {
     const int dt = c->w_dtype;
     const int A = c->T * c->k;
     Segment r1 = {x_perm, x_perm_scales, offsets, c->E, 0, gate_perm, w13, w13_scales,
                   act, act_scales, z_out, A, a_kb, c->w_layout, a_kb, a_rows};
     Segment s1 = {x_shared, x_shared_scales, nullptr, 1, c->T, nullptr, ws13, ws13_scales,
                   shared_act, shared_act_scales, nullptr, c->T, 0, c->w_layout, a_kb};
+    if (dt == MOE_MXFP8) {
+        // K-blocked weights carry blocked scales; the layer keeps its activation scales
+        // blocked too, the routed ones already in expert order
+        r1.w_sc_blocked = s1.w_sc_blocked = c->w_layout;
+        if (mx_blocked) {
+            r1.a_sc_blocked = 1; r1.a_sc_rows = A; r1.a_sc_direct = 1; r1.out_sc_blocked = 1;
+            s1.a_sc_blocked = 1; s1.a_sc_rows = c->T; s1.out_sc_blocked = 1;
+        }
+    }
     if (!c->shared_F)
         return hip_status(moe::launch_grouped_gemm(0, dt, &r1, 1, A, 2 * c->F, c->H, sched, stream));
     if (c->shared_F == c->F) {
@@ -267,13 +276,20 @@ int run_down(const moe_config* c, int a_kb, const void* act, const void* act_sca
              const int32_t* offsets, const void* w2, const void* w2_scales,
              const void* shared_act, const void* shared_act_scales, const void* ws2,
              const void* ws2_scales, void* y_perm, void* shared_y, void* sched,
-             hipStream_t stream) {
+             hipStream_t stream, bool mx_blocked = false) {
     const int dt = c->w_dtype;
     const int A = c->T * c->k;
     Segment r2 = {act, act_scales, offsets, c->E, 0, nullptr, w2, w2_scales, y_perm, nullptr,
                   nullptr, A, a_kb, c->w_layout, 0};
     Segment s2 = {shared_act, shared_act_scales, nullptr, 1, c->T, nullptr, ws2, ws2_scales,
                   shared_y, nullptr, nullptr, c->T, a_kb, c->w_layout, 0};
+    if (dt == MOE_MXFP8) {
+        r2.w_sc_blocked = s2.w_sc_blocked = c->w_layout;
+        if (mx_blocked) {
+            r2.a_sc_blocked = 1; r2.a_sc_rows = A;
+            s2.a_sc_blocked = 1; s2.a_sc_rows = c->T;
+        }
+    }
     if (!c->shared_F)
         return hip_status(moe::launch_grouped_gemm(1, dt, &r2, 1, A, c->H, c->F, sched, stream));
     if (c->shared_F == c->F) {
@@ -294,7 +310,8 @@ int run_experts(const moe_config* c, int a_kb, const void* x_perm, const void* x
                 const void* x_shared, const void* x_shared_scales, const void* ws13,
                 const void* ws13_scales, const void* ws2, const void* ws2_scales, void* act,
                 void* act_scales, void* y_perm, void* shared_y, void* z_out, void* ws,
-                hipStream_t stream, int mid_mark = -1, const int32_t* a_rows = nullptr) {
+                hipStream_t stream, int mid_mark = -1, const int32_t* a_rows = nullptr,
+                bool mx_blocked = false) {
     Carve cv(ws);
     void* sched = cv.take(sched_ws_bytes(c));
     void* sh_act = nullptr;
@@ -306,11 +323,11 @@ int run_experts(const moe_config* c, int a_kb, const void* x_perm, const void* x
     }
     int st = run_up(c, a_kb, x_perm, x_perm_scales, offsets, gate_perm, w13, w13_scales, x_shared,
                     x_shared_scales, ws13, ws13_scales, act, act_scales, sh_act, sh_act_scales,
-                    z_out, sched, stream, a_rows);
+                    z_out, sched, stream, a_rows, mx_blocked);
     if (st) return st;
     if (mid_mark >= 0 && stage_mark(mid_mark, stream) != hipSuccess) return MOE_ERR_HIP;
     return run_down(c, a_kb, act, act_scales, offsets, w2, w2_scales, sh_act, sh_act_scales, ws2,
-                    ws2_scales, y_perm, shared_y, sched, stream);
+                    ws2_scales, y_perm, shared_y, sched, stream, mx_blocked);
 }
 
 }  // namespace
@@ -581,11 +598,14 @@ int moe_layer_forward(const moe_config* cfg, const void* x, const void* w_router
     if (e != hipSuccess) return MOE_ERR_HIP;
     const void* xs = fp8 ? L.x_q : x;
     const void* a1 = gather ? xs : L.x_perm;
-    const void* a1_scales = gather ? (fp8 ? L.x_q_scales : nullptr) : L.x_perm_scales;
+    // MXFP8: scales blocked throughout, the routed rows' scales permuted to expert order by
+    // the permute (so a tile's scale words are adjacent); the codes are gathered from x_q
+    const bool mx = cfg->w_dtype == MOE_MXFP8;
+    const void* a1_scales = gather && !mx ? (fp8 ? L.x_q_scales : nullptr) : L.x_perm_scales;
     st = run_experts(cfg, a_kb, a1, a1_scales, L.offsets, L.gate_perm, w13, w13_scales,
                      w2, w2_scales, cfg->shared_F ? xs : nullptr, fp8 ? L.x_q_scales : nullptr,
                      ws13, ws13_scales, ws2, ws2_scales, L.act, L.act_scales, L.y_perm,
-                     L.shared_y, nullptr, L.scratch, stream, 4, gather ? L.src : nullptr);
+                     L.shared_y, nullptr, L.scratch, stream, 4, gather ? L.src : nullptr, mx);
     if (st) return st;
     e = stage_mark(5, stream);
     if (e == hipSuccess)
@@ -709,8 +729,14 @@ int moe_quantize_mx(const void* in, int32_t in_dtype, int64_t rows, int32_t cols
     if (!in || !q || !scales) return MOE_ERR_INVALID_ARG;
     if (in_dtype != MOE_F32 && in_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
     if (rows < 1 || cols < 1 || cols % 32) return MOE_ERR_INVALID_ARG;
-    return hip_status(moe::launch_quantize_mx(in, in_dtype, rows * (int64_t)cols, q, scales,
-                                              stream));
+    return hip_status(moe::launch_quantize_mx(in, in_dtype, rows, cols, 0, q, scales, stream));
+}
+
+int moe_pack_mx_scales(const uint8_t* in, int64_t n_mat, int32_t rows, int32_t cols,
+                       uint8_t* out, hipStream_t stream) {
+    if (!in || !out || in == out) return MOE_ERR_INVALID_ARG;
+    if (n_mat < 1 || rows < 1 || cols < 1 || cols % 4) return MOE_ERR_INVALID_ARG;
+    return hip_status(moe::launch_pack_mx_scales(in, n_mat, rows, cols, out, stream));
 }
 
 int moe_quantize_e4m3(const void* in, int32_t in_dtype, int64_t n_mat, int32_t rows,

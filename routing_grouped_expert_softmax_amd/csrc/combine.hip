@@ -196,9 +196,13 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict_
 }
 
 // MXFP8 quantiser, 1 x 32 blocks along the rows (activations and weights alike): four lanes
-// per block, eight values per lane; the block's amax takes two butterflies.
+// per block, eight values per lane; the block's amax takes two butterflies. Scale bytes are
+// row-major [R, cols/32] (blocked_rows == 0) or blocked [cols/128][R][4] (blocked_rows = R):
+// the four codes of one row's 128 columns form one word, and the words of consecutive rows
+// are adjacent.
 __global__ __launch_bounds__(256) void quant_mx_kernel(const void* __restrict__ in, int in_dtype,
-                                                       int64_t nblk, uint8_t* __restrict__ q,
+                                                       int64_t nblk, int cols, int blocked_rows,
+                                                       uint8_t* __restrict__ q,
                                                        uint8_t* __restrict__ scales) {
     const int64_t blk = (int64_t)blockIdx.x * 64 + threadIdx.x / 4;   // 32-value block
     const int sub = threadIdx.x % 4;
@@ -221,7 +225,29 @@ __global__ __launch_bounds__(256) void quant_mx_kernel(const void* __restrict__ 
     packed.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
     packed.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
     *(uint2*)(q + base) = packed;
-    if (sub == 0) scales[blk] = (uint8_t)(X + 127);
+    if (sub == 0) {
+        size_t si = (size_t)blk;
+        if (blocked_rows > 0) {
+            const int nb = cols / 32;
+            const int64_t r = blk / nb;
+            const int b = (int)(blk % nb);
+            si = ((size_t)(b / 4) * blocked_rows + r) * 4 + b % 4;
+        }
+        scales[si] = (uint8_t)(X + 127);
+    }
+}
+
+// [n, rows, cols4] 4-byte words -> [n][cols4][rows]: MXFP8 weight scales (one word = a row's
+// four block codes of 128 K) into the blocked order of K-blocked weights.
+__global__ __launch_bounds__(256) void pack_mx_scales_kernel(const uint32_t* __restrict__ in,
+                                                             int64_t total, int rows, int cols4,
+                                                             uint32_t* __restrict__ out) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= total) return;
+    const int64_t per = (int64_t)rows * cols4;
+    const int64_t m = i / per, rem = i % per;
+    const int kb = (int)(rem / rows), r = (int)(rem % rows);
+    out[i] = in[(m * rows + r) * cols4 + kb];
 }
 
 // Weight quantiser, 128 x 128 blocks: one 256-thread block per quantisation block; each
@@ -356,12 +382,21 @@ hipError_t launch_quantize(const void* in, int in_dtype, int64_t n_mat, int rows
     return hipGetLastError();
 }
 
-hipError_t launch_quantize_mx(const void* in, int in_dtype, int64_t n_values, uint8_t* q,
-                              uint8_t* scales, hipStream_t s) {
-    const int64_t nblk = n_values / 32;
+hipError_t launch_quantize_mx(const void* in, int in_dtype, int64_t rows, int cols,
+                              int blocked, uint8_t* q, uint8_t* scales, hipStream_t s) {
+    const int64_t nblk = rows * (cols / 32);
     if (nblk > 0)
-        quant_mx_kernel<<<(unsigned)((nblk + 63) / 64), 256, 0, s>>>(in, in_dtype, nblk, q,
-                                                                     scales);
+        quant_mx_kernel<<<(unsigned)((nblk + 63) / 64), 256, 0, s>>>(
+            in, in_dtype, nblk, cols, blocked ? (int)rows : 0, q, scales);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_mx_scales(const uint8_t* in, int64_t n_mat, int rows, int cols,
+                                 uint8_t* out, hipStream_t s) {
+    const int64_t total = n_mat * rows * (int64_t)(cols / 4);
+    if (total > 0)
+        pack_mx_scales_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(
+            (const uint32_t*)in, total, rows, cols / 4, (uint32_t*)out);
     return hipGetLastError();
 }
 

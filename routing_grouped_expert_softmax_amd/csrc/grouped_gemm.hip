@@ -46,6 +46,11 @@ struct SegDev {
     int rows_total;
     int out_kblock;
     const int32_t* a_rows;   // nullptr, or the source row of each launch row (a gather)
+    // MXFP8 scale addressing in bytes: the word (four block codes of 128 K) of row r, K block
+    // kb is at a_scales + r * sa_row + kb * sa_kb (row-major: K/32, 4; blocked: 4, rows * 4);
+    // the same for each group's w_scales (group stride N * K/32) and for GEMM1's out_scales
+    uint32_t sa_row, sa_kb, sw_row, sw_kb, so_row, so_kb;
+    int a_sc_direct;         // scales of launch row r at row r even when a_rows gathers codes
 };
 
 struct SchedArgs {
@@ -952,13 +957,20 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmArgs ga) {
     // scale words: wave w DMAs those of tile rows 64 w + lane (lanes past the tile's rows
     // fetch the last row's word into the unused tail of the area)
     const uint8_t* ssrc;
+    uint32_t s_kb;
     {
         int r = 64 * wave + lane;
         if (r >= C::kRows) r = C::kRows - 1;
-        if (r < BM)
-            ssrc = (const uint8_t*)S.a_scales + (size_t)arow_of(r) * KB;
-        else
-            ssrc = (const uint8_t*)S.w_scales + ((size_t)g * N + wrow_of(r - BM)) * KB;
+        if (r < BM) {
+            const int rr = m0 + r < Mg ? m0 + r : Mg - 1;
+            const int srow = S.a_sc_direct ? rbase + rr : arow_of(r);
+            ssrc = (const uint8_t*)S.a_scales + (size_t)srow * S.sa_row;
+            s_kb = S.sa_kb;
+        } else {
+            ssrc = (const uint8_t*)S.w_scales + (size_t)g * N * KB +
+                   (size_t)wrow_of(r - BM) * S.sw_row;
+            s_kb = S.sw_kb;
+        }
     }
     auto issue = [&](int kstep, int stage) {
         MOE_LDS uint8_t* base = (MOE_LDS uint8_t*)lds + stage * C::kStageBytes;
@@ -971,7 +983,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmArgs ga) {
                               (size_t)kstep * kSl * (is_a ? a_step : w_step)),
                 (MOE_LDS void*)(base + (wave + q * C::kWaves) * 1024), 16, 0, 0);
         }
-        __builtin_amdgcn_global_load_lds((const void*)(ssrc + (kstep * BK / 128) * 4),
+        __builtin_amdgcn_global_load_lds((const void*)(ssrc + (size_t)(kstep * BK / 128) * s_kb),
                                          (MOE_LDS void*)(base + C::kTileBytes + wave * 256), 4, 0, 0);
     };
 
@@ -1087,9 +1099,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmArgs ga) {
             *(uint4*)(outq + ((size_t)rbase + m0 + row) * F + nt * (BN / 2) + cc * 16) = v;
         }
         uint8_t* outs = (uint8_t*)S.out_scales;
-        static_assert(kSc == 4, "one 4-byte scale run per tile row");
+        static_assert(kSc == 4, "one scale word (128 act columns) per tile row");
         for (int row = tid; row < live; row += C::kThreads)
-            *(uint32_t*)(outs + ((size_t)rbase + m0 + row) * (F / 32) + nt * kSc) =
+            *(uint32_t*)(outs + ((size_t)rbase + m0 + row) * S.so_row + (size_t)nt * S.so_kb) =
                 *(const uint32_t*)(eps + row * kSc);
     }
 }
@@ -1491,6 +1503,19 @@ hipError_t launch_grouped_gemm(int kind, int dtype, const Segment* segs, int nse
         d.rows_total = g.rows_total;
         d.out_kblock = g.out_kblock;
         d.a_rows = g.a_rows;
+        if (dtype == 3) {          // MXFP8 scale strides (bytes)
+            const uint32_t kbr = (uint32_t)(K / 32), obr = (uint32_t)(N / 2 / 32);
+            d.sa_row = g.a_sc_blocked ? 4u : kbr;
+            d.sa_kb = g.a_sc_blocked ? (uint32_t)g.a_sc_rows * 4u : 4u;
+            d.sw_row = g.w_sc_blocked ? 4u : kbr;
+            d.sw_kb = g.w_sc_blocked ? (uint32_t)N * 4u : 4u;
+            d.so_row = g.out_sc_blocked ? 4u : obr;
+            d.so_kb = g.out_sc_blocked ? (uint32_t)g.rows_total * 4u : 4u;
+            d.a_sc_direct = g.a_sc_direct;
+        } else {
+            d.sa_row = d.sa_kb = d.sw_row = d.sw_kb = d.so_row = d.so_kb = 0;
+            d.a_sc_direct = 0;
+        }
         ga.seg[i] = d;
     }
     sa.nseg = nseg;

@@ -47,6 +47,9 @@ hipError_t launch_route_backward(int router, const float* logits, const float* l
 // ---- permute ---------------------------------------------------------------------------
 constexpr int kPermChunk = 512;   // assignments per counting block
 size_t permute_ws_bytes(int T, int k, int E);
+// With mode 3 and kblock -1 (the layer's MXFP8 path) x_q_scales are written blocked
+// ([H/128][T][4]) and, when x_perm_scales != nullptr, gathered into expert order there (blocked
+// [H/128][A][4], rows [0, offsets[E])).
 hipError_t launch_permute(int mode /*0 f32, 1 bf16, 2 e4m3 from bf16, 3 MXFP8 from bf16*/,
                           int kblock /*1: x_perm K-blocked (not with MXFP8); -1: no x_perm
                                        (routing metadata, and in the fp8 modes the token-order
@@ -75,11 +78,14 @@ hipError_t launch_pack_kblock(const void* in, int64_t n_mat, int rows, int cols,
 // ---- quantise --------------------------------------------------------------------------
 hipError_t launch_quantize(const void* in, int in_dtype, int64_t n_mat, int rows, int cols,
                            int block_rows, uint8_t* q, float* scales, hipStream_t s);
-// MXFP8: n_values (a multiple of 32) consecutive values in 1 x 32 blocks -> e4m3 codes q and
-// one E8M0 code per block (rows of a row-major matrix whose width is a multiple of 32 are
-// blocked along the row)
-hipError_t launch_quantize_mx(const void* in, int in_dtype, int64_t n_values, uint8_t* q,
-                              uint8_t* scales, hipStream_t s);
+// MXFP8: a row-major [rows, cols] matrix (cols % 32 == 0) in 1 x 32 blocks along the rows ->
+// e4m3 codes q and one E8M0 code per block, row-major [rows, cols/32] or, with blocked (cols
+// % 128 == 0), in the blocked scale order [cols/128][rows][4 bytes]
+hipError_t launch_quantize_mx(const void* in, int in_dtype, int64_t rows, int cols,
+                              int blocked, uint8_t* q, uint8_t* scales, hipStream_t s);
+// MXFP8 scale bytes [n, rows, cols] (cols % 4 == 0) -> blocked [n][cols/4][rows][4 bytes]
+hipError_t launch_pack_mx_scales(const uint8_t* in, int64_t n_mat, int rows, int cols,
+                                 uint8_t* out, hipStream_t s);
 
 // ---- grouped GEMM ----------------------------------------------------------------------
 // One expert segment of a grouped GEMM launch: `groups` groups whose rows are
@@ -103,6 +109,13 @@ struct Segment {
     int out_kblock;            // 1: GEMM1's `out` (act) is K-blocked
     const int32_t* a_rows;     // nullptr, or: row r reads row a_rows[r] of a row-major `a`
                                // (and of a_scales): the permutation fused into the A loads
+    // MXFP8 scale layouts (0 = row-major [rows, K/32] bytes; 1 = blocked [K/128][rows][4])
+    int a_sc_blocked;          // a_scales blocked, with a_sc_rows rows
+    int a_sc_rows;
+    int a_sc_direct;           // 1: a_scales row r belongs to launch row r even when a_rows
+                               //    gathers the codes (scales permuted beforehand)
+    int w_sc_blocked;          // each group's w_scales blocked ([K/128][N][4])
+    int out_sc_blocked;        // GEMM1's out_scales blocked, rows_total rows
 };
 
 struct GemmPlan {

@@ -296,6 +296,18 @@ __global__ __launch_bounds__(256) void perm_gather_kblock_kernel(
             out_scales[(size_t)r * nsc + b] = in_scales[(size_t)t * nsc + b];
 }
 
+// MXFP8 scale words into expert order: out[kb][r] = in[kb][src[r]] for the live rows (both
+// blocked; one word = a row's four block codes of 128 columns)
+__global__ __launch_bounds__(256) void perm_mx_scale_gather_kernel(
+    const uint32_t* __restrict__ in, const int32_t* __restrict__ src,
+    const int32_t* __restrict__ live_rows, int A, int T, int nkb, uint32_t* __restrict__ out) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)nkb * A) return;
+    const int kb = (int)(i / A), r = (int)(i % A);
+    if (r >= *live_rows) return;
+    out[i] = in[(size_t)kb * T + src[r]];
+}
+
 }  // namespace
 
 size_t permute_ws_bytes(int T, int k, int E) {
@@ -322,8 +334,15 @@ hipError_t launch_permute(int mode, int kblock, int cap, const void* x, const in
     if (kblock < 0) {           // metadata only (the GEMM gathers the rows itself)
         if (mode == 2)
             return launch_quantize(x, 1, 1, T, H, 1, (uint8_t*)x_q, (float*)x_q_scales, s);
-        if (mode == 3)
-            return launch_quantize_mx(x, 1, (int64_t)T * H, (uint8_t*)x_q, (uint8_t*)x_q_scales, s);
+        if (mode == 3) {
+            hipError_t e = launch_quantize_mx(x, 1, T, H, 1, (uint8_t*)x_q,
+                                              (uint8_t*)x_q_scales, s);
+            if (e != hipSuccess || !x_perm_scales) return e;
+            const int64_t n = (int64_t)(H / 128) * A;
+            perm_mx_scale_gather_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(
+                (const uint32_t*)x_q_scales, src, offsets + E, A, T, H / 128,
+                (uint32_t*)x_perm_scales);
+        }
         return hipGetLastError();
     }
     const int blocks = (T + 3) / 4;

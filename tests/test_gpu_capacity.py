@@ -101,6 +101,8 @@ def _weights(moe, cfg, inp):
     W = {k: (None if v is None else v.cuda()) for k, v in W.items()}
     if cfg.w_layout:
         W = {k: (None if v is None else moe.pack_kblock(v)) for k, v in W.items()}
+        if cfg.w_dtype == mi.MXFP8:
+            sc = {k: (None if v is None else moe.pack_mx_scales(v)) for k, v in sc.items()}
     return W, sc, q
 
 

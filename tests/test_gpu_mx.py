@@ -119,13 +119,15 @@ def test_grouped_gemm_mx(moe, name):
     xp_s = oracle.gather_rows(xs, perm["pos"])
     T8 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
     W = {k: T8(q[k][0]) for k in ("w13", "w2", "ws13", "ws2")}
-    if cfg.w_layout:
+    S = {k: T8(q[k][1]) for k in ("w13", "w2", "ws13", "ws2")}
+    if cfg.w_layout:           # K-blocked codes take blocked scales
         W = {k: moe.pack_kblock(v) for k, v in W.items()}
+        S = {k: moe.pack_mx_scales(v) for k, v in S.items()}
     out = moe.grouped_gemm_swiglu(
         cfg, T8(xp_q), T8(perm["offsets"]), T8(perm["gate_perm"]), W["w13"], W["w2"],
-        x_perm_scales=T8(xp_s), w13_scales=T8(q["w13"][1]), w2_scales=T8(q["w2"][1]),
+        x_perm_scales=T8(xp_s), w13_scales=S["w13"], w2_scales=S["w2"],
         x_shared=T8(xq), x_shared_scales=T8(xs), ws13=W["ws13"],
-        ws13_scales=T8(q["ws13"][1]), ws2=W["ws2"], ws2_scales=T8(q["ws2"][1]))
+        ws13_scales=S["ws13"], ws2=W["ws2"], ws2_scales=S["ws2"])
     torch.cuda.synchronize()
     rows = np.arange(cfg.A)
     kw = dict(x_scales=xp_s, w13_scales=q["w13"][1], w2_scales=q["w2"][1], mx=True)
@@ -154,7 +156,7 @@ def test_layer_forward_mx(moe, name):
     print(f"[mx layer forward] {name}", flush=True)
     w = {k: moe.quantize_mx(getattr(inp, k).cuda()) for k in ("w13", "w2", "ws13", "ws2")}
     if cfg.w_layout:
-        w = {k: (moe.pack_kblock(v[0]), v[1]) for k, v in w.items()}
+        w = {k: (moe.pack_kblock(v[0]), moe.pack_mx_scales(v[1])) for k, v in w.items()}
     y, ex = moe.layer_forward(cfg, inp.x.cuda(), inp.w_router.cuda(), w["w13"][0], w["w2"][0],
                               to_dev(inp.logit_bias), to_dev(inp.sel_bias),
                               torch.from_numpy(c["logits"]).cuda(), w13_scales=w["w13"][1],
@@ -171,3 +173,13 @@ def test_layer_forward_mx(moe, name):
     e = rel_err(y, ref)
     print(f"   y {e:.3e}", flush=True)
     assert e <= TOL8
+
+
+def test_pack_mx_scales_bit_exact(moe):
+    """[n, rows, cols] scale bytes -> [n][cols/4][rows][4]: a numpy transpose of 4-byte words."""
+    rng = np.random.default_rng(12)
+    a = rng.integers(0, 256, size=(3, 40, 28), dtype=np.uint8)
+    out = moe.pack_mx_scales(torch.from_numpy(a).cuda())
+    torch.cuda.synchronize()
+    ref = a.reshape(3, 40, 7, 4).transpose(0, 2, 1, 3).reshape(3, 40, 28)
+    np.testing.assert_array_equal(out.cpu().numpy(), ref)
