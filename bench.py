@@ -202,6 +202,34 @@ def cpu_baseline(cfg, inp, sample: int):
                       f"expert) in {dt:.1f} s; tokens are independent, so tokens/s scales"}
 
 
+def time_route_stats(moe, cfg, logits, lb, sb, reps=20):
+    """moe_route alone vs moe_route_stats (routing + fused load-balancing statistics) on the
+    step's logits, HIP events on the current stream."""
+    import torch
+    ti = torch.empty(cfg.T, cfg.k, dtype=torch.int32, device=logits.device)
+    tg = torch.empty(cfg.T, cfg.k, dtype=torch.float32, device=logits.device)
+    ws = moe.workspace(cfg, moe.OP_ROUTE_STATS, logits.device)
+
+    def timed(fn):
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    t_route = timed(lambda: moe.route(cfg, logits, lb, sb, topk_idx=ti, topk_gate=tg))
+    t_stats = timed(lambda: moe.route_stats(cfg, logits, lb, sb, ws=ws))
+    _, _, pm = moe.route_stats(cfg, logits, lb, sb, ws=ws)
+    torch.cuda.synchronize()
+    return {"what": "routing with the fused load-balancing statistics (mean router "
+                    "probability per expert) vs routing alone",
+            "ms": round(t_stats, 4), "route_ms": round(t_route, 4),
+            "prob_mean_max_over_mean": round(float(pm.max() / pm.mean()), 3)}
+
+
 def time_backward(moe, mi, cfg, dev, x, inp, idx, gate, w13_bf, w2_bf, reps):
     """The grouped-GEMM backward of the routed experts (bf16 weights; Z and act saved by a bf16
     forward of the same routing; dY ~ N(0,1) seeded), timed on its own."""
@@ -273,6 +301,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="dsv3_bf16")
+    ap.add_argument("--capacity-factor", type=float, default=0.0,
+                    help="token-dropping routing with this expert capacity factor (0: dropless)")
     ap.add_argument("--cpu-sample", type=int, default=1024)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-layer-bwd", action="store_true",
@@ -313,6 +343,8 @@ def main():
     import routing_grouped_expert_softmax_amd as moe
 
     cfg = mi.CONFIGS[args.workload]
+    if args.capacity_factor > 0:
+        cfg = cfg.replace(capacity_factor=args.capacity_factor)
     if cfg.act_dtype != mi.F32:      # K-blocked weights (MXFP8: row-major activations)
         cfg = cfg.replace(a_layout=0 if cfg.w_dtype == mi.MXFP8 else 1, w_layout=1)
     dev = torch.device("cuda", 0)
@@ -399,6 +431,7 @@ def main():
     cnt = ex["counts"].cpu().double()
     idx, gate = ex["topk_idx"], ex["topk_gate"]
     torch.cuda.synchronize()
+    route_stats = time_route_stats(moe, cfg, ex["logits"], lb, sb)
 
     backward = None
     if cfg.backward:
@@ -467,7 +500,16 @@ def main():
         "stages": per_stage,
         "load": {"max_over_mean": round(float(cnt.max() / cnt.mean()), 3),
                  "min_over_mean": round(float(cnt.min() / cnt.mean()), 3)},
+        "route_stats": route_stats,
     }
+    if cfg.capacity_factor > 0:
+        import math
+        import struct
+        cf32 = struct.unpack("f", struct.pack("f", cfg.capacity_factor))[0]   # the fp32 field
+        cap = math.ceil(cf32 * float(cfg.T * cfg.k) / cfg.E)
+        kept = float(cnt.clamp(max=cap).sum())
+        result["config"]["capacity_factor"] = cfg.capacity_factor
+        result["dropped_fraction"] = round(1.0 - kept / (cfg.T * cfg.k), 4)
     if backward:
         result["backward"] = backward
     if layer_backward:

@@ -52,11 +52,13 @@ double orc_e4m3_value(uint8_t code) {
 
 static double g_e4m3_mag[127];   /* magnitudes of codes 0..126, strictly increasing */
 static double g_e4m3_val[256];
+static double g_e8m0_val[256];        /* E8M0 scale code S -> 2^(S - 127) */
 static int g_tables_ready = 0;
 
 static void init_tables(void) {
     if (g_tables_ready) return;
     for (int c = 0; c < 256; ++c) g_e4m3_val[c] = orc_e4m3_value((uint8_t)c);
+    for (int c = 0; c < 256; ++c) g_e8m0_val[c] = ldexp(1.0, c - 127);
     for (int c = 0; c < 127; ++c) g_e4m3_mag[c] = orc_e4m3_value((uint8_t)c);
     g_tables_ready = 1;
 }
@@ -197,7 +199,7 @@ typedef struct {
     int rows, cols;
 } wmat;
 
-static double wval(const wmat* w, int64_t m, int r, int c) {
+static inline double wval(const wmat* w, int64_t m, int r, int c) {
     int64_t i = ((int64_t)m * w->rows + r) * (int64_t)w->cols + c;
     if (w->dtype == ORC_E4M3) {
         int nbr = w->rows / 128, nbc = w->cols / 128;
@@ -205,8 +207,8 @@ static double wval(const wmat* w, int64_t m, int r, int c) {
         return g_e4m3_val[((const uint8_t*)w->p)[i]] * sc;
     }
     if (w->dtype == ORC_MXFP8) {
-        int e8 = ((const uint8_t*)w->scales)[((int64_t)m * w->rows + r) * (w->cols / 32) + c / 32];
-        return ldexp(g_e4m3_val[((const uint8_t*)w->p)[i]], e8 - 127);
+        uint8_t e8 = ((const uint8_t*)w->scales)[((int64_t)m * w->rows + r) * (w->cols / 32) + c / 32];
+        return g_e4m3_val[((const uint8_t*)w->p)[i]] * g_e8m0_val[e8];
     }
     return load(w->p, w->dtype, i);
 }
@@ -457,7 +459,7 @@ static void load_row(const void* x, int dtype, const void* scales, int64_t row, 
         const uint8_t* q = (const uint8_t*)x + row * H;
         const uint8_t* sc = (const uint8_t*)scales;
         for (int h = 0; h < H; ++h)
-            out[h] = ldexp(g_e4m3_val[q[h]], sc[row * (H / 32) + h / 32] - 127);
+            out[h] = g_e4m3_val[q[h]] * g_e8m0_val[sc[row * (H / 32) + h / 32]];
     } else {
         for (int h = 0; h < H; ++h) out[h] = load(x, dtype, row * H + h);
     }
