@@ -1,4 +1,4 @@
-"""Full-size parity: every bf16/e4m3 workload at its full size, in the launch configuration
+"""Full-size parity: every bf16/e4m3/MXFP8 workload at its full size, in the launch configuration
 bench.py times (expert weights packed K-blocked; inside the layer GEMM1 gathers its rows),
 checked against the CPU oracle on outputs it can compute one by one (sampled tokens and
 rows) and on properties that hold at any size. All GPU work goes through the C ABI; the
@@ -16,6 +16,8 @@ from helpers import TOL, e4m3_codes_close, rel_err, tol, to_dev
 pytestmark = pytest.mark.gpu
 
 FULL = ["mixtral_bf16", "qwen3_bf16", "dsv3_bf16", "dsv3_fp8_skew"]
+# the whole-layer tests also run the MXFP8 widening of the DeepSeek-V3 layer
+FULL_LAYER = FULL + ["dsv3_mxfp8"]
 _STATE = {}
 
 
@@ -36,7 +38,8 @@ def full_case(moe, name):
     _STATE.clear()
     gc.collect()
     torch.cuda.empty_cache()
-    cfg = mi.CONFIGS[name].replace(a_layout=1, w_layout=1)
+    mx = mi.CONFIGS[name].w_dtype == mi.MXFP8
+    cfg = mi.CONFIGS[name].replace(a_layout=0 if mx else 1, w_layout=1)
     log(f"{name}: generating inputs")
     inp = mi.make_inputs(cfg)
     log(f"{name}: oracle router logits and routing")
@@ -53,6 +56,10 @@ def full_case(moe, name):
         t = getattr(inp, kname).cuda()
         if cfg.w_dtype == mi.E4M3:
             t, sc[kname + "_scales"] = moe.quantize_e4m3(t, 128)
+        elif cfg.w_dtype == mi.MXFP8:      # K-blocked codes, blocked scales
+            t, s8 = moe.quantize_mx(t)
+            sc[kname + "_scales"] = moe.pack_mx_scales(s8)
+            del s8
         dev[kname] = moe.pack_kblock(t)
         del t
     torch.cuda.synchronize()
@@ -79,19 +86,21 @@ def oracle_tokens(c, toks):
     quantiser) only the experts those tokens use."""
     cfg, inp = c["cfg"], c["inp"]
     idx = c["idx"]
-    if cfg.w_dtype != mi.E4M3:
+    if cfg.w_dtype not in (mi.E4M3, mi.MXFP8):
         return oracle.layer_tokens(inp.x, idx, c["gate"], inp.w13, inp.w2, toks, inp.ws13,
                                    inp.ws2)
+    mx = cfg.w_dtype == mi.MXFP8
     used = np.unique(idx[toks])
     remap = np.full(cfg.E, -1, np.int32)
     remap[used] = np.arange(len(used), dtype=np.int32)
     sub_idx = np.zeros_like(idx)
     sub_idx[toks] = remap[idx[toks]]
-    q13 = oracle.quant_weight(inp.w13[torch.from_numpy(used)])
-    q2 = oracle.quant_weight(inp.w2[torch.from_numpy(used)])
-    s13, s2 = oracle.quant_weight(inp.ws13), oracle.quant_weight(inp.ws2)
+    qw = oracle.mx_quant if mx else oracle.quant_weight
+    q13 = qw(inp.w13[torch.from_numpy(used)])
+    q2 = qw(inp.w2[torch.from_numpy(used)])
+    s13, s2 = qw(inp.ws13), qw(inp.ws2)
     return oracle.layer_tokens(inp.x, sub_idx, c["gate"], q13[0], q2[0], toks, s13[0], s2[0],
-                               fp8=True, w13_scales=q13[1], w2_scales=q2[1],
+                               fp8="mx" if mx else True, w13_scales=q13[1], w2_scales=q2[1],
                                ws13_scales=s13[1], ws2_scales=s2[1])
 
 
@@ -102,7 +111,7 @@ def kblock_rows(t, rows, n_rows, cols_bytes):
     return b[:, r, :].permute(1, 0, 2).reshape(len(rows), cols_bytes).cpu()
 
 
-@pytest.mark.parametrize("name", FULL)
+@pytest.mark.parametrize("name", FULL_LAYER)
 def test_full_layer_on_oracle_logits(moe, name):
     c = full_case(moe, name)
     cfg, inp, dev = c["cfg"], c["inp"], c["dev"]
@@ -124,7 +133,7 @@ def test_full_layer_on_oracle_logits(moe, name):
     assert e <= tol(cfg)
 
 
-@pytest.mark.parametrize("name", FULL)
+@pytest.mark.parametrize("name", FULL_LAYER)
 def test_full_router_gemm_and_routing_on_gpu(moe, name):
     """Router GEMM on the GPU too: logits within 1e-5 of the oracle's; tokens whose expert set
     changes (fp32 rounding on a near-tie) are counted, must be rare, and are excluded."""
