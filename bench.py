@@ -320,7 +320,7 @@ def main():
     args = ap.parse_args()
     if args.write_traffic:
         run = ("-- python -u bench.py --workload " + args.workload + " --steps 2 --warmup 1 "
-               f"--no-cpu --calib-copy-gib {args.calib_copy_gib:g}")
+               f"--no-cpu --no-layer-bwd --calib-copy-gib {args.calib_copy_gib:g}")
         rx = "--kernel-include-regex 'gemm_bf16|copyBuffer|elementwise'"
         cmd = (f"export TMPDIR=/tmp; rocprofv3 --pmc FETCH_SIZE {rx} -d <dir> -o f {run}; "
                f"rocprofv3 --pmc WRITE_SIZE TCC_HIT_sum TCC_MISS_sum {rx} -d <dir> -o w {run}; "
