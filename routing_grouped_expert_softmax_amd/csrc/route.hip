@@ -479,11 +479,19 @@ __global__ __launch_bounds__(256) void colsum_kernel(const float* __restrict__ i
     const int r0 = blockIdx.y * rpb;
     const int r1 = r0 + rpb < R ? r0 + rpb : R;
     float acc = 0.0f;
-    for (int r = r0; r < r1; ++r) acc += in[(size_t)r * C + c];
+    int r = r0;
+    for (; r + 8 <= r1; r += 8) {      // eight loads in flight, then the adds in row order
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = in[(size_t)(r + u) * C + c];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc += v[u];
+    }
+    for (; r < r1; ++r) acc += in[(size_t)r * C + c];
     out[(size_t)blockIdx.y * C + c] = acc * inv;
 }
 
-constexpr int kStatsRpb = 64;       // first-level rows per column-sum block
+constexpr int kStatsRpb = 16;       // first-level rows per column-sum block
 
 hipError_t route_dispatch(int router, const float* logits, const float* logit_bias,
                           const float* sel_bias, int T, int E, int k, int n_groups,
