@@ -1232,10 +1232,10 @@ constexpr int cfg_bn() { return BN; }
 
 // e4m3 tile configuration (BM, BN, WM, WN, STAGES), both GEMMs
 #ifndef MOE_F8_UP_CFG
-#define MOE_F8_UP_CFG 128, 256, 2, 4, 3
+#define MOE_F8_UP_CFG 256, 256, 2, 4, 2
 #endif
 #ifndef MOE_F8_DOWN_CFG
-#define MOE_F8_DOWN_CFG 128, 256, 2, 4, 3
+#define MOE_F8_DOWN_CFG 256, 256, 2, 4, 2
 #endif
 
 template <int KIND, int BM, int BN, int WM, int WN, int STAGES>
