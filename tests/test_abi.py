@@ -184,3 +184,40 @@ def test_layer_backward_argument_checks(moe):
     assert L.moe_layer_backward(C.byref(c), *a, C.c_size_t(n), None) == 1
     # workspace too small
     assert L.moe_layer_backward(C.byref(c), *args, C.c_size_t(n - 1), None) == 3
+
+
+def test_capacity_and_stats_argument_checks(moe):
+    """capacity_factor must be finite and >= 0; the backward calls need it 0; moe_route_stats
+    sizes and checks its workspace (host-side checks only)."""
+    assert ws_size(moe, cfgc(moe, capacity_factor=-1.0), moe.OP_PERMUTE)[0] == 1
+    assert ws_size(moe, cfgc(moe, capacity_factor=float("inf")), moe.OP_PERMUTE)[0] == 1
+    assert ws_size(moe, cfgc(moe, capacity_factor=float("nan")), moe.OP_PERMUTE)[0] == 1
+    assert ws_size(moe, cfgc(moe, capacity_factor=1.25), moe.OP_LAYER_FORWARD)[0] == 0
+    assert ws_size(moe, cfgc(moe, capacity_factor=1.25), moe.OP_LAYER_BACKWARD)[0] == 2
+    assert ws_size(moe, cfgc(moe, capacity_factor=1.25), moe.OP_GROUPED_GEMM_BWD)[0] == 2
+    c = cfgc(moe)
+    st, n = ws_size(moe, c, moe.OP_ROUTE_STATS)
+    # per-block sums of 4 tokens, then of 16 of those, E floats each
+    T, E = c.T, c.E
+    r1 = (T + 3) // 4
+    assert st == 0 and n >= (r1 + (r1 + 15) // 16) * E * 4
+    L = moe.lib()
+    d = C.c_void_p(16)
+    assert L.moe_route_stats(C.byref(c), d, None, None, d, d, d, d, n - 1, None) == 3
+    assert L.moe_route_stats(C.byref(c), d, None, None, d, d, None, d, n, None) == 1
+
+
+def test_mxfp8_argument_checks(moe):
+    """MXFP8 takes row-major activations (any weight layout); the quantiser and the scale
+    packing check their sizes (host-side checks only)."""
+    assert ws_size(moe, cfgc(moe, w_dtype=mi.MXFP8), moe.OP_LAYER_FORWARD)[0] == 0
+    assert ws_size(moe, cfgc(moe, w_dtype=mi.MXFP8, w_layout=1), moe.OP_LAYER_FORWARD)[0] == 0
+    assert ws_size(moe, cfgc(moe, w_dtype=mi.MXFP8, a_layout=1), moe.OP_PERMUTE)[0] == 2
+    L = moe.lib()
+    p, q = C.c_void_p(0x1000), C.c_void_p(0x2000)
+    assert L.moe_quantize_mx(p, 1, 4, 48, q, q, None) == 1          # cols not a multiple of 32
+    assert L.moe_quantize_mx(p, 7, 4, 64, q, q, None) == 1          # input dtype
+    assert L.moe_quantize_mx(None, 1, 4, 64, q, q, None) == 1
+    assert L.moe_pack_mx_scales(p, 1, 16, 6, q, None) == 1          # cols not a multiple of 4
+    assert L.moe_pack_mx_scales(p, 1, 16, 8, p, None) == 1          # in place
+    assert L.moe_pack_mx_scales(p, 0, 16, 8, q, None) == 1          # no matrices

@@ -144,6 +144,9 @@ STATS = {
     "sigmoid_skew_T1": (mi.scaled(mi.CONFIGS["dsv3_fp8_skew"], T=1, H=256, F=128), None),
     "sigmoid_E48_T99": (mi.scaled(mi.CONFIGS["dsv3_bf16"], T=99, H=256, F=128, E=48, k=4,
                                   n_groups=4, topk_groups=2), None),
+    # the largest E the ABI takes: 16 keys per lane, a 16 KB LDS block sum
+    "softmax_E1024_T37": (mi.scaled(mi.CONFIGS["qwen3_bf16"], T=37, H=256, F=128, E=1024,
+                                    k=8), None),
 }
 
 
