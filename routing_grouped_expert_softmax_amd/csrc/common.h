@@ -132,11 +132,15 @@ constexpr int cmin(int a, int b) { return a < b ? a : b; }
 
 // Chunk swizzle of a K-contiguous tile row (depends on the row's low 4 bits only, so a
 // 32-row operand read sees the same pattern at every 32-row offset). 8 chunks (128-byte
-// rows): rows 0..7 of one logical chunk land in 8 different chunks. 4 chunks (64-byte rows):
-// rows of one parity among any 4 consecutive even (odd) rows, and rows 4 apart, land in
-// different chunks.
+// rows): a ds_read_b128 serves 16 lanes (16 rows) per 256-byte bank line, and two 128-byte
+// rows share a line, so rows 0..15 of one logical chunk must land on 16 different 16-byte
+// bank groups: (row parity, physical chunk) all distinct. (r & 7) alone gives rows r and r + 8
+// the same group, a 2-way conflict that SQ_LDS_BANK_CONFLICT measured at half of the LDS's
+// busy cycles; flipping bit 0 on rows 8..15 separates them, and rows 0..7 stay distinct.
+// 4 chunks (64-byte rows): rows of one parity among any 4 consecutive even (odd) rows, and
+// rows 4 apart, land in different chunks.
 template <int CPR>
 MOE_DEVICE int chunk_swz(int r) {
-    if (CPR == 8) return r & 7;
+    if (CPR == 8) return (r & 7) ^ ((r >> 3) & 1);
     return ((r >> 1) & 3) ^ ((r >> 3) & 1);
 }

@@ -635,7 +635,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_e4m3_kernel(GemmArgs ga) {
 #pragma unroll
     for (int q = 0; q < C::kDma; ++q) {
         const int r = 8 * (wave + q * C::kWaves) + lane / 8;
-        const int c = (lane % 8) ^ (r & 7);
+        const int c = (lane % 8) ^ chunk_swz<8>(r);
         size_t rowp;
         if (r < BM) {
             const int rr = m0 + r < Mg ? m0 + r : Mg - 1;
@@ -692,7 +692,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_e4m3_kernel(GemmArgs ga) {
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
-        for (int u = 0; u < 2; ++u) co[s][u] = (((4 * s + 2 * (lane / 32) + u) ^ (lane & 7)) * 16);
+        for (int u = 0; u < 2; ++u)
+            co[s][u] = ((4 * s + 2 * (lane / 32) + u) ^ chunk_swz<8>(lane % 32)) * 16;
     // first of the rows (r/4)*8 + (l/32)*4 + [0,4) whose scales this lane applies
     const int srow0 = wm * (BM / WM) + (lane / 32) * 4;
     // weight-scale offsets (per sub-tile j): [g][n_block][kb]
@@ -809,8 +810,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_e4m3_kernel(GemmArgs ga) {
 // products go straight into the fp32 accumulator: no partial tile, no promotion step.
 //
 // One LDS stage holds BK (128 or 64) K: [BM A rows | BN B rows] x BK bytes, its 16-byte chunks
-// XOR-swizzled so that the eight lanes of a ds_read_b128 phase hit distinct banks (128-byte
-// rows: chunk ^ row % 8; 64-byte rows, two per bank line: chunk ^ (row / 2) % 4), then one
+// XOR-swizzled so that the lanes of a ds_read_b128 phase hit distinct banks (128-byte rows:
+// chunk_swz<8>; 64-byte rows, four per bank line: chunk ^ (row / 2) % 4), then one
 // 4-byte word per tile row: the E8M0 codes of the row's four blocks of the 128 K that hold
 // the stage (byte b = block b), DMA'd by one 4-byte load per lane and wave. 64-K stages take
 // half the LDS each, so twice as many fit and more loads are in flight per workgroup.
@@ -851,7 +852,7 @@ struct MxCfg {
 
 // physical 16-byte chunk of logical chunk c in stage row r
 template <int BK>
-MOE_DEVICE int mx_swz(int c, int r) { return BK == 128 ? c ^ (r & 7) : c ^ ((r >> 1) & 3); }
+MOE_DEVICE int mx_swz(int c, int r) { return BK == 128 ? c ^ chunk_swz<8>(r) : c ^ ((r >> 1) & 3); }
 
 template <class C, int NV, class Issue>
 MOE_DEVICE void mx_kloop(int nk, const uint8_t* lds, Issue& issue, const int (&a_off)[C::kTM],
