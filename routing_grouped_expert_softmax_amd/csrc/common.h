@@ -17,6 +17,25 @@ constexpr int kWave = 64;
 // ---------------------------------------------------------------------------------------
 // bf16 <-> fp32
 // ---------------------------------------------------------------------------------------
+// Row split of a ragged group into M tiles. A group of `rows` rows takes
+// me = ceil(rows / bm) tiles as always, but the rows are dealt out evenly: every tile but the
+// last spans tile_span(rows, bm) rows (a multiple of 32, at most bm). The tiles of a group
+// then carry about the same work, so the tiles that read the same weight tile run in step
+// and the later readers find it in L2; with a bm-row first tile and a short tail the short
+// tile runs far ahead and both stream the weights from HBM. ceil(rows / span) == me always:
+// span <= bm gives at least me tiles and span >= rows / me at most me.
+__host__ __device__ __forceinline__ int tile_span(int rows, int bm) {
+    const int me = (rows + bm - 1) / bm;
+    if (me <= 1) return bm;
+    const int per = (rows + me - 1) / me;
+    return (per + 31) / 32 * 32;
+}
+// end row (exclusive, within the group) of the tile that starts at row m0
+__host__ __device__ __forceinline__ int tile_end(int m0, int rows, int bm) {
+    const int e = m0 + tile_span(rows, bm);
+    return e < rows ? e : rows;
+}
+
 MOE_DEVICE float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 // fp32 -> bf16, round to nearest even (inputs are finite).

@@ -61,7 +61,8 @@ struct SchedArgs {
 };
 
 // tiles[i] = {seg << 20 | group, first row within the group, rows of the group,
-//             global row of the group's first row}; *total = number of M tiles.
+//             global row of the group's first row}; *total = number of M tiles. A group's
+// rows are dealt evenly over its tiles (tile_span), so a tile spans [m0, tile_end(m0, ..)).
 // One block of 1024 threads; each thread owns two consecutive group slots.
 __global__ __launch_bounds__(1024) void schedule_kernel(SchedArgs sa, int bm,
                                                         int4* __restrict__ tiles,
@@ -108,8 +109,8 @@ __global__ __launch_bounds__(1024) void schedule_kernel(SchedArgs sa, int bm,
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
         for (int i = 0; i < nt_of[q]; ++i)
-            tiles[start + i] = make_int4((seg_of[q] << 20) | grp_of[q], i * bm, m_of[q],
-                                         base_of[q]);
+            tiles[start + i] = make_int4((seg_of[q] << 20) | grp_of[q],
+                                         i * tile_span(m_of[q], bm), m_of[q], base_of[q]);
         start += nt_of[q];
     }
 }
@@ -147,7 +148,7 @@ MOE_DEVICE bool pick_tile(const GemmArgs& ga, int& mt, int& nt) {
     if (L >= total) return false;
     const int ntn = ga.ntn, bm = ga.bm;
     const int4 t = ga.tiles[L / ntn];                 // some M tile of L's group
-    const int mt0 = L / ntn - t.y / bm;               // the group's first M tile
+    const int mt0 = L / ntn - t.y / tile_span(t.z, bm);   // the group's first M tile
     const int me = (t.z + bm - 1) / bm;               // the group's M tiles
     const int local = L - mt0 * ntn;
     const int band = local / (ga.mgroup * ntn) * ga.mgroup;
@@ -324,7 +325,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs ga) {
     if (!pick_tile(ga, mt, nt)) return;
     const int4 ti = ga.tiles[mt];
     const int seg = ti.x >> 20, g = ti.x & 0xFFFFF;
-    const int m0 = ti.y, Mg = ti.z, rbase = ti.w;
+    const int m0 = ti.y, Mg = tile_end(ti.y, ti.z, ga.bm), rbase = ti.w;   // Mg: tile end
     const SegDev S = seg == 0 ? ga.seg[0] : ga.seg[1];
     const int N = ga.N, K = ga.K;
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
@@ -617,7 +618,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_e4m3_kernel(GemmArgs ga) {
     if (!pick_tile(ga, mt, nt)) return;
     const int4 ti = ga.tiles[mt];
     const int seg = ti.x >> 20, g = ti.x & 0xFFFFF;
-    const int m0 = ti.y, Mg = ti.z, rbase = ti.w;
+    const int m0 = ti.y, Mg = tile_end(ti.y, ti.z, ga.bm), rbase = ti.w;   // Mg: tile end
     const SegDev S = seg == 0 ? ga.seg[0] : ga.seg[1];
     const int N = ga.N, K = ga.K, KB = K / 128;
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
@@ -922,7 +923,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmArgs ga) {
     if (!pick_tile(ga, mt, nt)) return;
     const int4 ti = ga.tiles[mt];
     const int seg = ti.x >> 20, g = ti.x & 0xFFFFF;
-    const int m0 = ti.y, Mg = ti.z, rbase = ti.w;
+    const int m0 = ti.y, Mg = tile_end(ti.y, ti.z, ga.bm), rbase = ti.w;   // Mg: tile end
     const SegDev S = seg == 0 ? ga.seg[0] : ga.seg[1];
     const int N = ga.N, K = ga.K, KB = K / 32;          // KB: scale bytes per row
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
@@ -1123,7 +1124,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs ga) {
     if (!pick_tile(ga, mt, nt)) return;
     const int4 ti = ga.tiles[mt];
     const int seg = ti.x >> 20, g = ti.x & 0xFFFFF;
-    const int m0 = ti.y, Mg = ti.z, rbase = ti.w;
+    const int m0 = ti.y, Mg = tile_end(ti.y, ti.z, ga.bm), rbase = ti.w;   // Mg: tile end
     const SegDev S = seg == 0 ? ga.seg[0] : ga.seg[1];
     const int N = ga.N, K = ga.K;
     const int tid = threadIdx.x, tx = tid % 16, ty = tid / 16;

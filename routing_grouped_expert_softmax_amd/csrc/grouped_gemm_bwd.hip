@@ -126,7 +126,7 @@ MOE_DEVICE void bwd_tile(const BwdArgs& ba, int L, uint8_t* lds) {
             nt = L % ba.ntn;
             g = ti.x & 0xFFFFF;
             m0 = ti.y;
-            Mg = ti.z;
+            Mg = tile_end(ti.y, ti.z, kBM);   // the tile's end row within the group
             rbase = ti.w;
             mt = 0;
         }
