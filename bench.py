@@ -295,6 +295,40 @@ def time_layer_backward(moe, mi, cfg, dev, x, wr, logits, idx, gate, w13, w2, ws
             "tokens/s": round(cfg.T / (t * 1e-3), 1)}
 
 
+def dense_ceiling(cfg, reps: int = 20):
+    """Context, not the path: time the vendor library's dense bf16 GEMM (torch.matmul, which
+    runs hipBLASLt on this image) on dense problems of the workload's expert-GEMM shapes, one
+    weight for all rows, so the grouped kernels' TFLOP/s can be read against what the same chip
+    reaches on a plain GEMM. Prints one JSON line per shape."""
+    import torch
+    A = cfg.T * cfg.k
+    mean_rows = max(1, A // cfg.E)
+    shapes = [("up, all routed rows, one weight", A, cfg.H, 2 * cfg.F),
+              ("down, all routed rows, one weight", A, cfg.F, cfg.H),
+              ("up, one expert's mean rows", mean_rows, cfg.H, 2 * cfg.F),
+              ("down, one expert's mean rows", mean_rows, cfg.F, cfg.H)]
+    g = torch.Generator(device="cuda").manual_seed(0)
+    for what, M, K, N in shapes:
+        a = torch.randn(M, K, device="cuda", dtype=torch.bfloat16, generator=g)
+        b = torch.randn(N, K, device="cuda", dtype=torch.bfloat16, generator=g)
+        for _ in range(3):
+            c = a @ b.t()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            c = a @ b.t()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        tf = 2.0 * M * K * N / ms / 1e9
+        print(json.dumps({"dense_ceiling": what, "M": M, "K": K, "N": N, "ms": round(ms, 4),
+                          "TFLOP/s": round(tf, 1), "frac_bf16_peak": round(tf / 2500.0, 4)}),
+              flush=True)
+        del a, b, c
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -312,6 +346,9 @@ def main():
     ap.add_argument("--calib-copy-gib", type=float, default=0.0,
                     help="issue one device copy of this many GiB before the steps (a plain copy "
                          "of known size for scaling the traffic counters)")
+    ap.add_argument("--dense-ceiling", action="store_true",
+                    help="time the vendor library's dense bf16 GEMM on the workload's expert "
+                         "shapes (context for the grouped kernels) and exit")
     ap.add_argument("--pmc-summary", nargs="+", metavar="DB",
                     help="print per-kernel counter averages of rocprofv3 databases and exit")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
@@ -343,6 +380,9 @@ def main():
     import routing_grouped_expert_softmax_amd as moe
 
     cfg = mi.CONFIGS[args.workload]
+    if args.dense_ceiling:
+        dense_ceiling(cfg)
+        return
     if args.capacity_factor > 0:
         cfg = cfg.replace(capacity_factor=args.capacity_factor)
     if cfg.act_dtype != mi.F32:      # K-blocked weights (MXFP8: row-major activations)
