@@ -11,8 +11,10 @@
 //    over 8 XCDs) works through one contiguous run of tiles; within an expert the M tiles
 //    that share a weight tile are neighbours and the N tiles of a band share its
 //    activation rows in that XCD's L2 (pick_tile);
-//  * bf16 tiles go global -> LDS by direct DMA (two-slot rings, XOR-swizzled 16-byte
-//    chunks) and into v_mfma_f32_32x32x16_bf16 with fp32 accumulation; e4m3 tiles into
+//  * bf16 tiles go global -> LDS by direct DMA (rings of 32-K slots, XOR-swizzled 16-byte
+//    chunks) and into v_mfma_f32_32x32x16_bf16 with fp32 accumulation, the two waves of
+//    every SIMD in opposite phases (one reads operands and issues DMAs while the other runs
+//    its MFMAs, bf16_kloop_pp); e4m3 tiles into
 //    the block-scaled v_mfma_scale_f32_32x32x64_f8f6f4, with the fp32 block scales applied
 //    per 128-deep K block;
 //  * GEMM1 loads the gate rows [n0, n0+BN/2) and the matching up rows [F+n0, ...) of W13
@@ -176,6 +178,10 @@ MOE_DEVICE bool pick_tile(const GemmArgs& ga, int& mt, int& nt) {
 #ifndef MOE_BF_INTERLEAVE
 #define MOE_BF_INTERLEAVE 1
 #endif
+// Ping-pong K loop (bf16_kloop_pp) for 8-wave 256 x 256 tiles with K step 32 and >= 3 slots.
+#ifndef MOE_BF_PINGPONG
+#define MOE_BF_PINGPONG 1
+#endif
 
 template <int KIND, int BM, int BN, int BK, int WM, int WN, int SA, int SB>
 struct BfCfg {
@@ -317,6 +323,87 @@ MOE_DEVICE void bf16_kloop(int nk, const uint8_t* lds, IssueA& issue_a, IssueB& 
     }
 }
 
+// Ping-pong K loop. The 8 waves form two groups of four, one wave of each group on every
+// SIMD (waves w and w + 4 share a SIMD). A K step (one ring slot: 32 K of A and of B) is two
+// phases per group: M (LDS reads of the step's two MFMA sub-steps into registers, plus this
+// group's DMAs of step s + S - 1: group 0 fills the A slot, group 1 the B slot) and C (the
+// step's MFMAs, from registers). Group 1 starts one barrier late, so between any two
+// barriers one group runs MFMAs while the other reads and issues loads, and every SIMD's
+// matrix unit has one wave feeding it in every phase. Every wave passes the same number of
+// barriers (group 1's extra one first, group 0's last). Slot s % S is last read in interval
+// 2s + 1 and refilled (step s + S) from interval 2s + 2; a group waits for its own DMAs of
+// step s + 1 before the barrier that ends interval 2s + 1.
+template <class C, int NV>
+MOE_DEVICE void bf16_kloop_pp(int nst, const uint8_t* lds, const uint8_t* const (&src)[4],
+                              size_t step_bytes, int grp, int gw,
+                              const int (&a_off)[C::kTM], const int (&b_off)[C::kTN],
+                              const int (&chunk_off)[C::kSub],
+                              f32x16_t (&acc)[C::kTM][C::kTN]) {
+    constexpr int S = C::kSA;
+    constexpr int kQ = 4;                        // DMAs per wave per step (16 KB / 1 KB / 4)
+    static_assert(C::kSA == C::kSB && S >= 3 && C::kSub == 2 && C::kWaves == 8 &&
+                  C::kASlot == 16384 && C::kBSlot == 16384 && (S - 1) * kQ < 64, "ping-pong");
+    constexpr int NVv = NV > 0 ? NV : 1;
+    bf16x8_t av[2][NVv], bv[2][C::kTN];
+    const int ring = grp == 0 ? 0 : C::kBRing;
+    auto issue = [&](int st) {
+        MOE_LDS uint8_t* base = (MOE_LDS uint8_t*)lds + ring + (st % S) * 16384;
+#pragma unroll
+        for (int q = 0; q < kQ; ++q)
+            __builtin_amdgcn_global_load_lds((const void*)(src[q] + (size_t)st * step_bytes),
+                                             (MOE_LDS void*)(base + (gw + q * 4) * 1024), 16,
+                                             0, 0);
+    };
+    auto read = [&](int st) {
+        if (NV == 0) return;
+        const uint8_t* ca = lds + (st % S) * C::kASlot;
+        const uint8_t* cb = lds + C::kBRing + (st % S) * C::kBSlot;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+#pragma unroll
+            for (int j = 0; j < C::kTN; ++j)
+                bv[u][j] = *(const bf16x8_t*)(cb + b_off[j] + chunk_off[u]);
+#pragma unroll
+            for (int i = 0; i < NV; ++i)
+                av[u][i] = *(const bf16x8_t*)(ca + a_off[i] + chunk_off[u]);
+        }
+    };
+    auto mma = [&]() {
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int i = 0; i < NV; ++i)
+#pragma unroll
+                for (int j = 0; j < C::kTN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[u][i], bv[u][j],
+                                                                        acc[i][j], 0, 0, 0);
+    };
+    // this group's DMAs of step s + 1 have landed (later steps may still be in flight)
+    auto wait_next = [&](int st) {
+        if (st + S - 1 < nst) wait_vm_lgkm0<(S - 2) * kQ>();
+        else wait_vm_lgkm0<0>();
+    };
+#pragma unroll
+    for (int st = 0; st < S - 1; ++st)
+        if (st < nst) issue(st);
+    if (nst - 1 >= S - 2) wait_vm_lgkm0<(S - 2) * kQ>();
+    else wait_vm_lgkm0<0>();
+    block_sync();                                // step 0 visible
+    if (grp == 1) block_sync();
+    for (int st = 0; st < nst; ++st) {
+        read(st);                                // M
+        if (st + S - 1 < nst) issue(st + S - 1);
+        if (grp == 0) wait_vm_lgkm0<63>();       // LDS reads only
+        else wait_next(st);
+        block_sync();
+        mma();                                   // C
+        if (grp == 0) wait_next(st);
+        block_sync();
+    }
+    if (grp == 0) block_sync();
+    wait_vm_lgkm0<0>();
+}
+
 template <int KIND, int BM, int BN, int BK, int WM, int WN, int SA, int SB>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs ga) {
     using C = BfCfg<KIND, BM, BN, BK, WM, WN, SA, SB>;
@@ -414,12 +501,46 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs ga) {
     // one branch-free K loop per count of live sub-tiles (every variant has the same
     // barriers, so waves of one block may take different variants)
     const int nk = K / BK;
+    // ping-pong: one group of four waves fills the A slots, the other the B slots
+    constexpr bool kPP = MOE_BF_PINGPONG && BM == 256 && BN == 256 && BK == 32 && SA == SB &&
+                         SA >= 3 && WM * WN == 8;
+    // wave-uniform (scalar) so the group's extra barrier is a scalar branch: s_barrier does
+    // not look at the exec mask
+    const int grp = __builtin_amdgcn_readfirstlane(wave / 4);
+    const int gw = __builtin_amdgcn_readfirstlane(wave % 4);
+    const uint8_t* src[4];
+    if (kPP) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int r = C::kRowsPerDma * (gw + q * 4) + lane / C::kCpr;
+            const int c = (lane % C::kCpr) ^ chunk_swz<C::kCpr>(r);
+            if (grp == 0) {
+                const int rr = m0 + r < Mg ? m0 + r : Mg - 1;
+                const int arow = S.a_rows ? S.a_rows[rbase + rr] : rbase + rr;
+                src[q] = (const uint8_t*)S.a + (size_t)arow * S.a_row +
+                         (size_t)(c / 4) * S.a_kstep + (c % 4) * 16;
+            } else {
+                int wrow;
+                if (KIND == 0)
+                    wrow = r < BN / 2 ? nt * (BN / 2) + r : N / 2 + nt * (BN / 2) + (r - BN / 2);
+                else
+                    wrow = nt * BN + r;
+                src[q] = (const uint8_t*)S.w + (size_t)g * S.w_mat + (size_t)wrow * S.w_row +
+                         (size_t)(c / 4) * S.w_kstep + (c % 4) * 16;
+            }
+        }
+    }
+    const size_t pp_step = grp == 0 ? a_step : w_step;
     switch (nvi) {
 #define MOE_KLOOP_CASE(V)                                                                   \
     case V:                                                                                 \
         if (V <= C::kTM) {                                                                  \
             constexpr int NV = V <= C::kTM ? V : C::kTM;                                    \
-            bf16_kloop<C, NV>(nk, lds, issue_a, issue_b, a_off, b_off, chunk_off, acc);     \
+            if constexpr (kPP)                                                              \
+                bf16_kloop_pp<C, NV>(nk, lds, src, pp_step, grp, gw, a_off, b_off,          \
+                                     chunk_off, acc);                                       \
+            else                                                                            \
+                bf16_kloop<C, NV>(nk, lds, issue_a, issue_b, a_off, b_off, chunk_off, acc); \
         }                                                                                   \
         break;
     MOE_KLOOP_CASE(0)
@@ -1206,10 +1327,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs ga) {
 // bf16 tile configurations (BM, BN, BK, WM, WN, A ring depth, B ring depth). GEMM1's BN counts gate + up rows
 // (BN / 2 act columns).
 #ifndef MOE_BF_UP_CFG
-#define MOE_BF_UP_CFG 256, 256, 64, 2, 4, 2, 2
+#define MOE_BF_UP_CFG 256, 256, 32, 2, 4, 4, 4
 #endif
 #ifndef MOE_BF_DOWN_CFG
-#define MOE_BF_DOWN_CFG 256, 256, 64, 2, 4, 2, 2
+#define MOE_BF_DOWN_CFG 256, 256, 32, 2, 4, 4, 4
 #endif
 
 template <int KIND, int BM, int BN, int BK, int WM, int WN, int SA, int SB>
