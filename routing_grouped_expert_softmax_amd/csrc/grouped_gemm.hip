@@ -183,6 +183,7 @@ MOE_DEVICE bool pick_tile(const GemmArgs& ga, int& mt, int& nt) {
 #define MOE_BF_PINGPONG 1
 #endif
 
+
 template <int KIND, int BM, int BN, int BK, int WM, int WN, int SA, int SB>
 struct BfCfg {
     static constexpr int kThreads = WM * WN * kWave;
@@ -341,6 +342,10 @@ MOE_DEVICE void bf16_kloop_pp(int nst, const uint8_t* lds, const uint8_t* const 
                               f32x16_t (&acc)[C::kTM][C::kTN]) {
     constexpr int S = C::kSA;
     constexpr int kQ = 4;                        // DMAs per wave per step (16 KB / 1 KB / 4)
+    // DMA look-ahead in steps: slot (s - 1) % S is refilled (step s + S - 1) in the M phase
+    // of step s, after its last reader (group 1's M phase of step s - 1)
+    constexpr int LA = S - 1;
+    static_assert(LA >= 1, "look-ahead");
     static_assert(C::kSA == C::kSB && S >= 3 && C::kSub == 2 && C::kWaves == 8 &&
                   C::kASlot == 16384 && C::kBSlot == 16384 && (S - 1) * kQ < 64, "ping-pong");
     constexpr int NVv = NV > 0 ? NV : 1;
@@ -380,19 +385,19 @@ MOE_DEVICE void bf16_kloop_pp(int nst, const uint8_t* lds, const uint8_t* const 
     };
     // this group's DMAs of step s + 1 have landed (later steps may still be in flight)
     auto wait_next = [&](int st) {
-        if (st + S - 1 < nst) wait_vm_lgkm0<(S - 2) * kQ>();
+        if (st + LA < nst) wait_vm_lgkm0<(LA - 1) * kQ>();
         else wait_vm_lgkm0<0>();
     };
 #pragma unroll
-    for (int st = 0; st < S - 1; ++st)
+    for (int st = 0; st < LA; ++st)
         if (st < nst) issue(st);
-    if (nst - 1 >= S - 2) wait_vm_lgkm0<(S - 2) * kQ>();
+    if (nst - 1 >= LA - 1) wait_vm_lgkm0<(LA - 1) * kQ>();
     else wait_vm_lgkm0<0>();
     block_sync();                                // step 0 visible
     if (grp == 1) block_sync();
     for (int st = 0; st < nst; ++st) {
         read(st);                                // M
-        if (st + S - 1 < nst) issue(st + S - 1);
+        if (st + LA < nst) issue(st + LA);
         if (grp == 0) wait_vm_lgkm0<63>();       // LDS reads only
         else wait_next(st);
         block_sync();
