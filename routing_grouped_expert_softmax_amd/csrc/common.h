@@ -5,6 +5,9 @@
 #include <stdint.h>
 
 #define MOE_DEVICE __device__ __forceinline__
+#ifndef MOE_FAST_SILU
+#define MOE_FAST_SILU 1
+#endif
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -125,6 +128,21 @@ MOE_DEVICE int rank_key_index(uint64_t rk) { return (int)(0xFFFFFFFFu - (uint32_
 MOE_DEVICE float rank_key_value(uint64_t rk) { return float_from_order_key((uint32_t)(rk >> 32)); }
 
 MOE_DEVICE float silu_f32(float u) { return u / (1.0f + expf(-u)); }
+
+// SiLU for the forward GEMM1 epilogues, written from its definition
+// silu(u) = u / (1 + e^-u) with e^-u = 2^(-u log2 e): the hardware exp2 and reciprocal are
+// each within about 1 ulp of fp32, far below the bf16 (or e4m3) rounding of the stored
+// activation, and take a few instructions instead of a full-precision expf and an IEEE
+// division. Large -u gives exp2 = +inf and a result of -0 (the exact value is below bf16's
+// smallest normal); large +u gives u.
+MOE_DEVICE float silu_fast(float u) {
+#if MOE_FAST_SILU
+    const float e = __builtin_amdgcn_exp2f(-u * 1.44269504088896340736f);
+    return u * __builtin_amdgcn_rcpf(1.0f + e);
+#else
+    return silu_f32(u);
+#endif
+}
 
 // ---------------------------------------------------------------------------------------
 // LDS pipeline helpers of the MFMA kernels

@@ -586,7 +586,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs ga) {
                     const size_t grow = (size_t)rbase + m0 + lr;
                     const float zg = acc[i][jj][r], zu = acc[i][half + jj][r];
                     const float gt = S.gate ? S.gate[grow] : 1.0f;
-                    ep[row * kEpStride + lcol] = f32_to_bf16(gt * (silu_f32(zg) * zu));
+                    ep[row * kEpStride + lcol] = f32_to_bf16(gt * (silu_fast(zg) * zu));
                     if (zo && m0 + row < Mg) {
                         zo[grow * N + col] = f32_to_bf16(zg);
                         zo[grow * N + F + col] = f32_to_bf16(zu);
@@ -888,7 +888,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_e4m3_kernel(GemmArgs ga) {
             const int row = wm * (BM / WM) + i * 32 + (r / 4) * 8 + (lane / 32) * 4 + r % 4;
             const int lr = m0 + row < Mg ? row : live - 1;
             const float gt = S.gate ? S.gate[(size_t)rbase + m0 + lr] : 1.0f;
-            av[i][r] = gt * (silu_f32(acc[i][0][r]) * acc[i][1][r]);
+            av[i][r] = gt * (silu_fast(acc[i][0][r]) * acc[i][1][r]);
         }
     block_sync();                                      // every wave is done with the stages
 #pragma unroll
@@ -1206,7 +1206,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmArgs ga) {
                 const int row = wm * (BM / WM) + i * 32 + (r / 4) * 8 + half * 4 + r % 4;
                 const int lr = m0 + row < Mg ? row : live - 1;     // dead rows: any gate
                 const float gt = S.gate ? S.gate[(size_t)rbase + m0 + lr] : 1.0f;
-                const float v = gt * (silu_f32(acc[i][jj][r]) * acc[i][hf + jj][r]);
+                const float v = gt * (silu_fast(acc[i][jj][r]) * acc[i][hf + jj][r]);
                 float m = fabsf(v);
 #pragma unroll
                 for (int off = 1; off < 32; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
