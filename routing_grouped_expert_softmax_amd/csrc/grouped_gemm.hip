@@ -212,7 +212,10 @@ struct BfCfg {
     static constexpr int kEpStride = kEpCols + 8;                 // bf16, padded row
     static constexpr size_t kLdsLoop = (size_t)SA * kASlot + (size_t)SB * kBSlot;
     static constexpr size_t kLdsEp = (size_t)BM * kEpStride * 2;
-    static constexpr size_t kLds = kLdsLoop > kLdsEp ? kLdsLoop : kLdsEp;
+    // GEMM1: the tile's row gates, staged at tile start past the ring and the epilogue
+    // staging (one 4-byte word per tile row)
+    static constexpr size_t kGateOff = ((kLdsLoop > kLdsEp ? kLdsLoop : kLdsEp) + 15) / 16 * 16;
+    static constexpr size_t kLds = kGateOff + (KIND == 0 ? (size_t)BM * 4 : 0);
     static_assert(BK == 32 || BK == 64, "BK");
     static_assert(kDmaA * kRowsPerDma * kWaves == BM && kDmaB * kRowsPerDma * kWaves == BN,
                   "DMA split");
@@ -503,6 +506,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs ga) {
 #pragma unroll
         for (int j = 0; j < C::kTN; ++j) acc[i][j] = f32x16_t{};
 
+    // GEMM1: the gates of the tile's live rows into LDS (read by the epilogue, after the
+    // K loop's barriers), loaded while the first operand tiles are in flight
+    float* gate_lds = (float*)(lds + C::kGateOff);
+    if (KIND == 0 && tid < live) gate_lds[tid] = S.gate ? S.gate[rbase + m0 + tid] : 1.0f;
+
     // one branch-free K loop per count of live sub-tiles (every variant has the same
     // barriers, so waves of one block may take different variants)
     const int nk = K / BK;
@@ -585,7 +593,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs ga) {
                     const int lr = m0 + row < Mg ? row : live - 1;     // dead rows: any gate
                     const size_t grow = (size_t)rbase + m0 + lr;
                     const float zg = acc[i][jj][r], zu = acc[i][half + jj][r];
-                    const float gt = S.gate ? S.gate[grow] : 1.0f;
+                    const float gt = gate_lds[lr];
                     ep[row * kEpStride + lcol] = f32_to_bf16(gt * (silu_fast(zg) * zu));
                     if (zo && m0 + row < Mg) {
                         zo[grow * N + col] = f32_to_bf16(zg);
