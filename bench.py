@@ -167,39 +167,113 @@ def write_traffic(fetch_db, write_db, copy_gib, workload, cmd):
     print("\n".join(lines))
 
 
-def cpu_baseline(cfg, inp, sample: int):
-    """The oracle, as it stands, end to end on `sample` seeded tokens of the same workload."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(cfg, inp, sample: int, sample_1t: int):
+    """The oracle, as it stands, end to end on `sample` seeded tokens of the same workload
+    with all of its OpenMP threads, then on the first `sample_1t` of them with one thread."""
     import numpy as np
     import oracle
 
     rng = np.random.default_rng(7)
     toks = np.sort(rng.choice(cfg.T, size=min(sample, cfg.T), replace=False))
-    sub = cfg.replace(T=len(toks))
-    xs = inp.x[toks]
     oracle.lib()
     if cfg.w_dtype in (2, 3):  # weights quantised once, outside the timed sample (like loading)
         qw = oracle.quant_weight if cfg.w_dtype == 2 else oracle.mx_quant
         q13, q2 = qw(inp.w13), qw(inp.w2)
         s13, s2 = qw(inp.ws13), qw(inp.ws2)
-    t0 = time.perf_counter()
-    logits = oracle.router_logits(xs, inp.w_router)
     lb = None if inp.logit_bias is None else inp.logit_bias.numpy()
     sb = None if inp.sel_bias is None else inp.sel_bias.numpy()
-    idx, gate = oracle.route_cfg(sub, logits, lb, sb)
-    oracle.permute(idx, gate, cfg.E)
-    if cfg.w_dtype in (2, 3):
-        oracle.layer_tokens(xs, idx, gate, q13[0], q2[0], np.arange(len(toks)), s13[0], s2[0],
-                            fp8=True if cfg.w_dtype == 2 else "mx", w13_scales=q13[1],
-                            w2_scales=q2[1], ws13_scales=s13[1], ws2_scales=s2[1])
-    else:
-        oracle.layer_tokens(xs, idx, gate, inp.w13, inp.w2, np.arange(len(toks)), inp.ws13,
-                            inp.ws2)
-    dt = time.perf_counter() - t0
-    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return {"value": len(toks) / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+
+    def run(tk):
+        sub = cfg.replace(T=len(tk))
+        xs = inp.x[tk]
+        t0 = time.perf_counter()
+        logits = oracle.router_logits(xs, inp.w_router)
+        idx, gate = oracle.route_cfg(sub, logits, lb, sb)
+        oracle.permute(idx, gate, cfg.E)
+        if cfg.w_dtype in (2, 3):
+            oracle.layer_tokens(xs, idx, gate, q13[0], q2[0], np.arange(len(tk)), s13[0],
+                                s2[0], fp8=True if cfg.w_dtype == 2 else "mx",
+                                w13_scales=q13[1], w2_scales=q2[1], ws13_scales=s13[1],
+                                ws2_scales=s2[1])
+        else:
+            oracle.layer_tokens(xs, idx, gate, inp.w13, inp.w2, np.arange(len(tk)), inp.ws13,
+                                inp.ws2)
+        return time.perf_counter() - t0
+
+    cores = oracle.max_threads()
+    dt = run(toks)
+    one = None
+    if sample_1t > 0:
+        oracle.set_threads(1)
+        try:
+            tk1 = toks[:min(sample_1t, len(toks))]
+            dt1 = run(tk1)
+        finally:
+            oracle.set_threads(cores)
+        one = {"value": round(len(tk1) / dt1, 3), "unit": "tokens/s", "cores": 1,
+               "sample": f"the first {len(tk1)} of those tokens in {dt1:.1f} s"}
+    return {"value": round(len(toks) / dt, 3), "unit": "tokens/s", "cores": cores,
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"{len(toks)} seeded tokens of the same workload, end to end (router "
                       f"logits, routing, permutation of the sub-batch, expert MLPs, shared "
-                      f"expert) in {dt:.1f} s; tokens are independent, so tokens/s scales"}
+                      f"expert) in {dt:.1f} s on {cores} OpenMP threads; tokens are "
+                      f"independent, so tokens/s scales",
+            "single_thread": one}
+
+
+def pct(vals, q):
+    """q-th percentile (0-100) of a list, linear interpolation between order statistics."""
+    v = sorted(vals)
+    if len(v) == 1:
+        return v[0]
+    pos = (len(v) - 1) * q / 100.0
+    lo = int(pos)
+    hi = min(lo + 1, len(v) - 1)
+    return v[lo] + (v[hi] - v[lo]) * (pos - lo)
+
+
+def time_permute_copy(moe, mi, cfg, x, idx, gate, flush, reps):
+    """The stand-alone moe_permute (routing metadata + the row copy x -> x_perm) with
+    row-major and with K-blocked x_perm (bf16 rows; the fp8 modes also quantise), each timed
+    with HIP events after a cache flush; algorithmic bytes T*H*b (x read) + A*H*b (x_perm
+    written) + 16*A (idx, gate read; pos, src, gate_perm written)."""
+    import torch
+    out = {}
+    A = cfg.T * cfg.k
+    b = 4 if cfg.act_dtype == mi.F32 else 2
+    layouts = [("row-major", 0)] + ([("K-blocked", 1)] if cfg.act_dtype != mi.F32 else [])
+    for what, lay in layouts:
+        pc = cfg.replace(w_dtype=mi.BF16 if cfg.act_dtype != mi.F32 else mi.F32, a_layout=lay)
+        ws = moe.workspace(pc, moe.OP_PERMUTE, x.device)
+        res = moe.permute(pc, x, idx, gate, ws=ws)         # warm-up, and the output buffers
+        ts = []
+        for _ in range(reps):
+            flush()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            moe.permute(pc, x, idx, gate, ws=ws, out=res)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        byt = cfg.T * cfg.H * b + A * cfg.H * b + 16 * A
+        med = pct(ts, 50)
+        out[what] = {"ms_median": round(med, 4), "ms_p10": round(pct(ts, 10), 4),
+                     "ms_p90": round(pct(ts, 90), 4),
+                     "GB/s": round(byt / (med * 1e-3) / 1e9, 1),
+                     "frac_hbm_peak": round(byt / (med * 1e-3) / PEAK_HBM, 4)}
+        del res, ws
+    return out
 
 
 def time_route_stats(moe, cfg, logits, lb, sb, reps=20):
@@ -332,12 +406,19 @@ def dense_ceiling(cfg, reps: int = 20):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="dsv3_bf16")
     ap.add_argument("--capacity-factor", type=float, default=0.0,
                     help="token-dropping routing with this expert capacity factor (0: dropless)")
     ap.add_argument("--cpu-sample", type=int, default=1024)
+    ap.add_argument("--cpu-sample-1t", type=int, default=64,
+                    help="tokens of the single-thread oracle figure (0: skip)")
+    ap.add_argument("--flush-mb", type=int, default=1024,
+                    help="MB of a scratch buffer written before every timed step, outside "
+                         "its events, to evict the memory-side cache and L2 (0: no flush)")
+    ap.add_argument("--no-permute-copy", action="store_true",
+                    help="skip timing the stand-alone permute copy")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-layer-bwd", action="store_true",
                     help="skip timing the whole-layer backward")
@@ -437,6 +518,15 @@ def main():
         moe.layer_forward(cfg, x, wr, w13, w2, lb, sb, None, ws13=ws13, ws2=ws2, y=y, ws=ws,
                           **sc)
 
+    # cache flush: a plain fill of a scratch buffer larger than the memory-side cache (256 MB)
+    # and the L2s, on the same stream, before every timed step and outside its events
+    flush_buf = (torch.empty(args.flush_mb << 20, dtype=torch.uint8, device=dev)
+                 if args.flush_mb > 0 else None)
+
+    def flush():
+        if flush_buf is not None:
+            flush_buf.fill_(1)
+
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
@@ -453,17 +543,24 @@ def main():
     w0 = time.perf_counter()
     e0.record()
     for evs in ev:
+        flush()
         moe.set_stage_events(evs)
         step()
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     moe.set_stage_events(None)
-    ms = e0.elapsed_time(e1) / args.steps
-    log(f"[bench] {ms:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f} ms/step)")
-    times = {name: sum(evs[i].elapsed_time(evs[i + 1]) for evs in ev) / args.steps
-             for i, name in enumerate(moe.STAGES)}
-    log("[bench] stages (ms, mean over the timed steps): " +
+    # one step = its first stage event to its last (the flush before it is outside)
+    step_ms = [evs[0].elapsed_time(evs[-1]) for evs in ev]
+    ms = pct(step_ms, 50)
+    loop_ms = e0.elapsed_time(e1)
+    log(f"[bench] step median {ms:.3f} ms (p10 {pct(step_ms, 10):.3f}, p90 "
+        f"{pct(step_ms, 90):.3f}); loop with flushes {loop_ms / args.steps:.3f} ms/step "
+        f"(wall {wall * 1e3 / args.steps:.3f} ms/step)")
+    stage_ms = {name: [evs[i].elapsed_time(evs[i + 1]) for evs in ev]
+                for i, name in enumerate(moe.STAGES)}
+    times = {name: pct(v, 50) for name, v in stage_ms.items()}
+    log("[bench] stages (ms, median over the timed steps): " +
         ", ".join(f"{k} {v:.3f}" for k, v in times.items()))
 
     _, ex = moe.layer_forward(cfg, x, wr, w13, w2, lb, sb, None, ws13=ws13, ws2=ws2, y=y,
@@ -472,6 +569,12 @@ def main():
     idx, gate = ex["topk_idx"], ex["topk_gate"]
     torch.cuda.synchronize()
     route_stats = time_route_stats(moe, cfg, ex["logits"], lb, sb)
+    permute_copy = None
+    if not args.no_permute_copy:
+        del ws
+        torch.cuda.empty_cache()
+        permute_copy = time_permute_copy(moe, mi, cfg, x, idx, gate, flush, 10)
+        ws = None
 
     backward = None
     if cfg.backward:
@@ -479,7 +582,7 @@ def main():
                                  args.bwd_reps)
     layer_backward = None
     if layer_bwd:
-        del ws
+        ws = None
         torch.cuda.empty_cache()
         layer_backward = time_layer_backward(moe, mi, cfg, dev, x, wr, ex["logits"], idx, gate,
                                              w13_bf, w2_bf, ws13_bf, ws2_bf, lb,
@@ -490,6 +593,8 @@ def main():
     for name, t in times.items():
         s = t * 1e-3
         per_stage[name] = {"ms": round(t, 4),
+                           "ms_p10": round(pct(stage_ms[name], 10), 4),
+                           "ms_p90": round(pct(stage_ms[name], 90), 4),
                            "GB/s": round(alg[name]["bytes"] / s / 1e9, 1),
                            "TFLOP/s": round(alg[name]["flops"] / s / 1e12, 1)}
     # dominant kernel: the grouped GEMM up (gate/up projection + SwiGLU)
@@ -514,6 +619,11 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "step_ms": {"median": round(ms, 4), "p10": round(pct(step_ms, 10), 4),
+                    "p90": round(pct(step_ms, 90), 4), "mean": round(sum(step_ms) / len(step_ms), 4),
+                    "timing": (f"HIP events around each step on its stream; {args.flush_mb} MB "
+                               "written before every step, outside its events"),
+                    "loop_ms_per_step_with_flushes": round(loop_ms / args.steps, 4)},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -533,6 +643,7 @@ def main():
         "grouped_gemm": {"TFLOP/s": round(gemm_flops / gemm_t / 1e12, 1),
                          "frac_mfma_peak": round(gemm_flops / gemm_t / PEAK_MFMA[dtype], 4)},
         "permute_GB/s": per_stage["permute"]["GB/s"],
+        "permute_copy": permute_copy,
         "permute_note": ("x rows copied to x_perm" if cfg.act_dtype == mi.F32 else
                          "routing metadata" +
                          (" + " + dtype + " quantisation of x" if fp8 else "") +
@@ -556,7 +667,7 @@ def main():
         result["layer_backward"] = layer_backward
     if not args.no_cpu:
         log(f"[bench] cpu baseline: oracle on {args.cpu_sample} tokens ...")
-        result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample)
+        result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample, args.cpu_sample_1t)
         log(f"[bench] cpu baseline {result['cpu_baseline']['value']:.2f} tokens/s")
     print(json.dumps(result), flush=True)
 

@@ -25,7 +25,11 @@
  *    MOE_ERR_WORKSPACE is returned. A failed launch returns MOE_ERR_HIP. Expert indices
  *    are not validated on the device: topk_idx must come from moe_route or lie in [0, E).
  *  - Every output is overwritten, never accumulated into. Results are deterministic:
- *    bit-identical across runs (no floating-point atomics, no split-K).
+ *    bit-identical across runs. No floating-point atomics are used; the one split-K (the
+ *    bf16 router GEMM inside moe_layer_forward, up to 8 K ranges) writes one partial sum
+ *    per range and adds them in a fixed range order.
+ *  - The library holds no state between calls except the instrumentation switch of
+ *    moe_set_stage_events (per host thread; it changes no result).
  *  - Layouts: every matrix keeps K (its last index) contiguous, so each expert GEMM is
  *    C = A B^T. A matrix [R, C] is either row-major (MOE_LAYOUT_ROWS) or K-blocked
  *    (MOE_LAYOUT_KBLOCK): stored as [C * eb / 64][R][64 bytes] (eb = element bytes), i.e.
@@ -106,7 +110,10 @@ typedef struct {
                              weight scales, fp32 accumulation) or MOE_MXFP8 (with act BF16
                              and row-major activations: 1x32 E8M0 scales along K for the
                              activations and the weights, fp32 accumulation; K-blocked
-                             weight codes take scales packed by moe_pack_mx_scales) */
+                             weight codes take scales packed by moe_pack_mx_scales).
+                             With the fp8 dtypes every one-byte activation matrix must stay
+                             below 4 GiB: (T*k + T) * max(H, F, shared_F) < 2^32, else
+                             MOE_ERR_UNSUPPORTED */
     int32_t shared_F;     /* width of the always-on shared expert, 0 = none */
     int32_t a_layout;     /* moe_layout of x_perm / act in the standalone calls (bf16, e4m3) */
     int32_t w_layout;     /* moe_layout of the expert weights (bf16, e4m3) */
@@ -125,13 +132,15 @@ const char* moe_status_string(int status);
 /* Workspace bytes needed by entry point `op` for `cfg`. Host only, no HIP call. */
 int moe_workspace_size(const moe_config* cfg, int op, size_t* bytes);
 
-/* Router scores ("scores = Router(x)" in the per-token loop): a linear router without bias,
+/* Router scores (the scoring step of the per-token loop in the study notes
+ * "Megatron-Core MoE -- 大规模稀疏专家并行实践", 实践案例 案例 1): a linear router without bias,
  *   logits[t, e] = sum_h x[t, h] * w_router[e, h],  fp32 accumulation and output.
  * x [T, H] and w_router [E, H] are in cfg->act_dtype; logits [T, E] fp32. */
 int moe_router_logits(const moe_config* cfg, const void* x, const void* w_router,
                       float* logits, hipStream_t stream);
 
-/* Top-k expert selection and gates ("experts = TopK(scores, k)"), one wavefront per token.
+/* Top-k expert selection and gates (the selection step of the same loop, 案例 1), one
+ * wavefront per token.
  *   l[e] = fp32(logits[t, e] + logit_bias[e])    (logit_bias [E] fp32, may be NULL)
  * then cfg->router (see moe_router). sel_bias [E] fp32 is used by the sigmoid router and
  * may be NULL there (zero bias). Slots are in rank order: key descending, ties to the
@@ -156,8 +165,11 @@ int moe_route_stats(const moe_config* cfg, const float* logits, const float* log
                     const float* sel_bias, int32_t* topk_idx, float* topk_gate,
                     float* prob_mean, void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* Permute (the routing metadata -- indices, counts, offsets -- and the grouped copy of x),
- * computed on the device without any host synchronisation. Dropless: exactly A = T*k rows.
+/* Permute: the routing metadata that says which token goes to which expert (indices,
+ * counts, offsets: the study notes, 实践案例 案例 1) and the copy of x grouped by expert, as
+ * the fused routing/permutation and sync-free kernels of the technical summary (section
+ * 2.4): computed on the device without any host synchronisation. Dropless: exactly
+ * A = T*k rows.
  *   counts[e]   = number of (t, j) with topk_idx[t, j] == e              [E]    int32
  *   offsets     = exclusive prefix sum of counts (offsets[E] = A)          [E+1]  int32
  *   pos[t*k+j]  = row of assignment (t, j); rows of one expert are in ascending token
@@ -238,7 +250,10 @@ int moe_grouped_gemm_down(const moe_config* cfg, const void* act, const void* ac
                           const void* ws2, const void* ws2_scales, void* y_perm,
                           void* shared_y, void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* Unpermute / combine: y[t, :] = sum_{j<k} y_perm[pos[t*k+j], :] (+ shared_y[t, :]), where a
+/* Unpermute / combine (the weighted sum over the selected experts that ends the per-token
+ * loop of the study notes, 实践案例 案例 1; the weights were folded in before the down
+ * projection, the memory-efficient permutation of the technical summary, section 2.2):
+ * y[t, :] = sum_{j<k} y_perm[pos[t*k+j], :] (+ shared_y[t, :]), where a
  * slot with pos < 0 (dropped by an expert capacity) contributes nothing,
  * summed in fp32 in slot order and rounded once to cfg->act_dtype. The gates were folded
  * in before the down projection, so no weight is applied here. A gather: no atomics.
@@ -246,14 +261,18 @@ int moe_grouped_gemm_down(const moe_config* cfg, const void* act, const void* ac
 int moe_unpermute_combine(const moe_config* cfg, const void* y_perm, const int32_t* pos,
                           const void* shared_y, void* y, hipStream_t stream);
 
-/* The whole layer: router GEMM (skipped when logits_in != NULL), route, permute, grouped
- * GEMM with the shared expert, combine. x [T, H] and w_router [E, H] in act_dtype; weights
+/* The whole layer, i.e. the per-token loop of the study notes (实践案例 案例 1) run for all T
+ * tokens at once with the fused routing/permutation, grouped GEMM and sync-free kernels of
+ * the technical summary (section 2.4): router GEMM (skipped when logits_in != NULL), route,
+ * permute, grouped GEMM with the shared expert, combine. x [T, H] and w_router [E, H] in
+ * act_dtype; weights
  * as in moe_grouped_gemm_swiglu (in cfg->w_layout); y [T, H] in act_dtype. The expert-grouped
  * activations live in the workspace, row-major whatever cfg->a_layout says (cfg->a_layout
  * applies to the stand-alone calls only). For bf16, the router's split-K partial sums use the
  * workspace's y_perm region before the down projection writes it.
- * Optional outputs (NULL = skip): logits_out [T, E], topk_idx_out [T, k],
- * topk_gate_out [T, k], counts_out [E] (the demand per expert, before any capacity).
+ * Optional outputs (NULL = skip): logits_out [T, E] (the router's logits, or a copy of
+ * logits_in when that is given), topk_idx_out [T, k], topk_gate_out [T, k], counts_out [E]
+ * (the demand per expert, before any capacity).
  * With cfg->capacity_factor > 0, dropped assignments (see moe_permute) add nothing to y. */
 int moe_layer_forward(const moe_config* cfg, const void* x, const void* w_router,
                       const float* logit_bias, const float* sel_bias, const float* logits_in,
@@ -264,7 +283,9 @@ int moe_layer_forward(const moe_config* cfg, const void* x, const void* w_router
                       void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Stage timing of moe_layer_forward (instrumentation; computes nothing). Not from the
- * pages: it lets a caller time each kernel of the layer on the stream it runs on.
+ * pages: it lets a caller time each kernel of the layer on the stream it runs on. This is
+ * the library's only state: a per-host-thread switch and the 7 event handles it was given
+ * (thread-local, so threads do not see each other's setting). It never changes a result.
  * events: MOE_N_STAGE_EVENTS hipEvent_t handles that the caller created (with timing) and
  * keeps alive. Until the next call on the same host thread, every moe_layer_forward on that
  * thread records events[i] on its stream when stage i starts and events[6] when the last one

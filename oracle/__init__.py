@@ -76,12 +76,26 @@ def lib():
                                                    P, P, I64, P, P, P, I64, P]
             L.orc_combine.argtypes = [P, P, I32, P, I32, I32, I32, P]
             L.orc_permute_capacity.argtypes = [P, P, I32, I32, I32, I32, P, P, P, P, P]
+            L.orc_set_threads.argtypes = [I32]
+            L.orc_set_threads.restype = None
+            L.orc_max_threads.argtypes = []
+            L.orc_max_threads.restype = I32
             for f in ("orc_quant_rows", "orc_quant_weight", "orc_router_logits", "orc_route",
                       "orc_permute", "orc_expert_rows", "orc_layer_tokens",
                       "orc_expert_bwd_rows", "orc_expert_wgrad_entries", "orc_combine"):
                 getattr(L, f).restype = None
             _lib = L
     return _lib
+
+
+def set_threads(n: int) -> None:
+    """Host threads of the oracle's parallel loops (for timing only; results are the same
+    for any count)."""
+    lib().orc_set_threads(int(n))
+
+
+def max_threads() -> int:
+    return int(lib().orc_max_threads())
 
 
 # ------------------------------------------------------------------------------------

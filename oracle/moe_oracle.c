@@ -19,6 +19,7 @@
  * Build: gcc -O2 -fopenmp -ffp-contract=off -shared -fPIC (no fast-math).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -226,7 +227,7 @@ static void fake_quant_row(const float* v, int n, double* out) {
 }
 
 /* ------------------------------------------------------------------------------------ */
-/* Router scores (step "scores = Router(x)" of the per-token loop)                        */
+/* Router scores: the scoring step of the per-token loop (study notes, 实践案例 案例 1)     */
 /* ------------------------------------------------------------------------------------ */
 
 /* logits[t, e] = fp32( sum_h x[t,h] * w_router[e,h] ), a linear router without bias
@@ -245,7 +246,7 @@ void orc_router_logits(const void* x, const void* wr, int dtype, int T, int H, i
 }
 
 /* ------------------------------------------------------------------------------------ */
-/* Top-k selection and gates (step "experts = TopK(scores, k)")                          */
+/* Top-k selection and gates: the selection step of that loop (案例 1)                  */
 /* ------------------------------------------------------------------------------------ */
 
 /* a ranks before b when its key is larger, or when the keys are equal and its index is
@@ -713,3 +714,8 @@ void orc_combine(const void* y_perm, const void* shared_y, int dtype, const int3
         }
     }
 }
+
+/* Host threads of the oracle's parallel loops (timing of the CPU baseline only; results do
+ * not depend on the thread count: every output is written by one thread, in a fixed order). */
+void orc_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+int orc_max_threads(void) { return omp_get_max_threads(); }

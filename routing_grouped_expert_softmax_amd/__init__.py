@@ -222,14 +222,16 @@ def route_stats(cfg, logits, logit_bias=None, sel_bias=None, ws=None, stream=Non
     return topk_idx, topk_gate, prob_mean
 
 
-def permute(cfg, x, topk_idx, topk_gate, want_x_q=False, ws=None, stream=None):
+def permute(cfg, x, topk_idx, topk_gate, want_x_q=False, ws=None, out=None, stream=None):
+    """moe_permute. `out` may pass the dict a previous call returned (same cfg), so that its
+    buffers are overwritten instead of new ones allocated."""
     dev = x.device
     T, H, E, k = cfg.T, cfg.H, cfg.E, cfg.k
     A = T * k
     fp8 = is_fp8(cfg)
     xsd, xss = act_scale_spec(cfg, A, H)
     qsd, qss = act_scale_spec(cfg, T, H)
-    out = dict(
+    out = out if out is not None else dict(
         counts=torch.empty(E, dtype=torch.int32, device=dev),
         offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
         pos=torch.empty(T, k, dtype=torch.int32, device=dev),

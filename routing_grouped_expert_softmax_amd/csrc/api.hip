@@ -69,6 +69,15 @@ int check_cfg(const moe_config* c) {
         if (c->w_dtype == MOE_MXFP8 && c->a_layout) return MOE_ERR_UNSUPPORTED;
         if (c->H % 256 || c->F % 128 || (c->shared_F && c->shared_F % 128))
             return MOE_ERR_UNSUPPORTED;
+        // the fp8 GEMMs address their one-byte activation rows with 32-bit offsets from the
+        // activation base: every fp8 activation matrix (x_perm / act with T*k rows, x_q /
+        // the shared act with T rows) must stay below 4 GiB
+        if (is_fp8(c->w_dtype)) {
+            const int64_t rows = (int64_t)c->T * c->k + c->T;
+            int64_t width = c->H > c->F ? c->H : c->F;
+            if (c->shared_F > width) width = c->shared_F;
+            if (rows * width >= ((int64_t)1 << 32)) return MOE_ERR_UNSUPPORTED;
+        }
     } else {
         return MOE_ERR_INVALID_ARG;
     }
@@ -563,6 +572,9 @@ int moe_layer_forward(const moe_config* cfg, const void* x, const void* w_router
     int32_t* counts = counts_out ? counts_out : L.counts;
     hipError_t e = stage_mark(0, stream);
     const float* lg = logits_in;
+    if (e == hipSuccess && lg && logits_out && logits_out != lg)
+        e = hipMemcpyAsync(logits_out, lg, (size_t)cfg->T * cfg->E * 4, hipMemcpyDeviceToDevice,
+                           stream);
     if (e == hipSuccess && !lg) {
         // bf16: split-K MFMA GEMM whose partial sums borrow the y_perm region (unused until
         // the down projection)

@@ -1,7 +1,7 @@
 // Router: logits = x W_r^T, and the per-token top-k selection with gates.
 //
-// Selection follows "experts = TopK(scores, k)" of the per-token loop in the study notes
-// "Megatron-Core MoE -- 大规模稀疏专家并行实践" (案例 1). It runs one wavefront per token:
+// Selection is the top-k step of the per-token loop in the study notes
+// "Megatron-Core MoE -- 大规模稀疏专家并行实践" (实践案例, 案例 1). It runs one wavefront per token:
 // lane l holds the keys of experts l, l+64, l+128, ... and k rounds of a 64-bit wavefront
 // max over (order-preserving key, inverted expert index) pick the next expert, so equal keys
 // go to the lower index without any arithmetic on the keys. The router logits stay fp32 (the

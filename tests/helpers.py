@@ -156,3 +156,42 @@ def mx_codes_close(q_gpu, s_gpu, act_ref_f64, err=1e-3):
     frac = float((np.asarray(q_gpu) != q_ref).mean())
     ds = np.asarray(s_gpu, np.int32) - np.asarray(s_ref, np.int32)
     return ratio, frac, int(np.max(np.abs(ds))), float((ds != 0).mean())
+
+
+def routing_margin(cfg, logits, logit_bias=None, sel_bias=None):
+    """Per token, how close the oracle's selection is to a tie, relative to max|key| of the
+    token: the smallest of (a) the key gap between the k-th selected expert and the best
+    unselected candidate and, for the group-limited router, (b) the score gap between the
+    last kept group and the best dropped group. Keys are the oracle's own: l + logit_bias
+    (softmax router), or fp32(s + sel_bias) with the oracle's s (sigmoid router). A token
+    whose expert set changes under a small perturbation of the logits must have a small
+    margin."""
+    import oracle
+    lg = np.asarray(logits, np.float32)
+    T, E = lg.shape
+    lb = None if logit_bias is None else np.asarray(logit_bias, np.float32)
+    l = lg if lb is None else (lg + lb[None, :]).astype(np.float32)
+    k = cfg.k
+    if cfg.router == oracle.SOFTMAX_TOPK:
+        key = l.astype(np.float64)
+        srt = -np.sort(-key, axis=1)
+        gap = srt[:, k - 1] - srt[:, k] if k < E else np.full(T, np.inf)
+    else:
+        _, _, s = oracle.route_cfg(cfg, lg, lb, sel_bias, return_scores=True)
+        sb = np.zeros(E, np.float32) if sel_bias is None else np.asarray(sel_bias, np.float32)
+        key32 = (s + sb[None, :]).astype(np.float32)
+        key = key32.astype(np.float64)
+        G, TG, per = cfg.n_groups, cfg.topk_groups, E // cfg.n_groups
+        grp = -np.sort(-key32.reshape(T, G, per), axis=2)
+        gs = (grp[:, :, 0] + grp[:, :, 1]).astype(np.float32).astype(np.float64)
+        gsrt = -np.sort(-gs, axis=1)
+        ggap = gsrt[:, TG - 1] - gsrt[:, TG] if TG < G else np.full(T, np.inf)
+        # expert gap inside the oracle's kept groups
+        gorder = np.argsort(-gs, axis=1, kind="stable")[:, :TG]
+        allowed = np.zeros((T, G), bool)
+        np.put_along_axis(allowed, gorder, True, axis=1)
+        masked = np.where(np.repeat(allowed, per, axis=1), key, -np.inf)
+        srt = -np.sort(-masked, axis=1)
+        egap = srt[:, k - 1] - srt[:, k] if k < TG * per else np.full(T, np.inf)
+        gap = np.minimum(ggap, egap)
+    return gap / np.maximum(np.max(np.abs(key), axis=1), 1e-30)

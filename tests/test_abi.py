@@ -221,3 +221,21 @@ def test_mxfp8_argument_checks(moe):
     assert L.moe_pack_mx_scales(p, 1, 16, 6, q, None) == 1          # cols not a multiple of 4
     assert L.moe_pack_mx_scales(p, 1, 16, 8, p, None) == 1          # in place
     assert L.moe_pack_mx_scales(p, 0, 16, 8, q, None) == 1          # no matrices
+
+
+def test_fp8_activation_size_limit(moe):
+    """The fp8 GEMMs address one-byte activation rows with 32-bit offsets, so every fp8
+    activation matrix must stay below 4 GiB: (T*k + T) * max(H, F, shared_F) < 2^32. At the
+    limit the configuration is rejected on the host (nothing launched); bf16 with the same
+    shape is accepted (its GEMMs keep 64-bit row addresses)."""
+    # (70000*8 + 70000) * 7168 = 4.5e9 >= 2^32
+    big = dict(T=70000, H=7168)
+    for dt in (mi.E4M3, mi.MXFP8):
+        assert ws_size(moe, cfgc(moe, w_dtype=dt, **big), moe.OP_LAYER_FORWARD)[0] == 2
+        assert ws_size(moe, cfgc(moe, w_dtype=dt, **big), moe.OP_GROUPED_GEMM)[0] == 2
+        # below the limit: 60000 * 9 * 7168 = 3.9e9 < 2^32
+        assert ws_size(moe, cfgc(moe, w_dtype=dt, T=60000, H=7168), moe.OP_PERMUTE)[0] == 0
+    assert ws_size(moe, cfgc(moe, **big), moe.OP_LAYER_FORWARD)[0] == 0
+    # the widest of H, F and shared_F counts
+    assert ws_size(moe, cfgc(moe, w_dtype=mi.E4M3, T=60000, H=1024, F=8192, shared_F=128),
+                   moe.OP_PERMUTE)[0] == 2

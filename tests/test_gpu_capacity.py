@@ -80,7 +80,8 @@ def test_combine_skips_dropped_slots(moe, name):
     ref = oracle.combine(y_perm, perm["pos"])
     e = rel_err(y, ref)
     print(f"   y {e:.3e}", flush=True)
-    assert e <= 2e-2
+    # the fp32 sum of the kept slots, rounded once to bf16: |error| <= 2^-9 |y| <= 2^-9 max|y|
+    assert e <= 2.0 ** -8
 
 
 def _weights(moe, cfg, inp):

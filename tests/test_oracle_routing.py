@@ -229,3 +229,85 @@ def test_combine_inverts_the_permutation():
         toks = perm["src"][rows]
         assert np.all(np.diff(toks) > 0)
         assert set(toks) == set(np.nonzero((idx == e).any(1))[0])
+
+
+def _exact_logits(x64, w64):
+    """Router scores from their definition with no rounding before the end: every product of
+    two fp32 (or bf16) values is exact in fp64, and math.fsum returns the correctly rounded
+    sum of the exact products; one rounding to fp32 follows."""
+    import math
+    T, E = x64.shape[0], w64.shape[0]
+    out = np.empty((T, E), np.float64)
+    for t in range(T):
+        prod = x64[t][None, :] * w64            # [E, H], exact
+        for e in range(E):
+            out[t, e] = math.fsum(prod[e])
+    return out
+
+
+@pytest.mark.parametrize("dtype,T,H,E", [("f32", 37, 129, 13), ("bf16", 29, 257, 7),
+                                          ("f32", 5, 1, 3), ("bf16", 16, 64, 24)])
+def test_router_logits_match_exact_matmul(dtype, T, H, E):
+    """Pin of the scoring step (study notes, 实践案例 案例 1; linear router without bias):
+    logits = fp32(x W_r^T) with W_r stored [E, H]. Checked against (a) the exactly rounded
+    definition (fsum of exact products) and (b) numpy's fp64 matmul, bit-equal after the
+    fp32 rounding. An odd H and an E that is not a multiple of 8 are included; a reading of
+    W_r as [H, E] or an fp32 accumulation would break the bit-equality."""
+    rng = np.random.default_rng(1000 + T * H + E)
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    w = (rng.standard_normal((E, H)) * 0.5).astype(np.float32)
+    if dtype == "bf16":
+        xt = torch.from_numpy(x).to(torch.bfloat16)
+        wt = torch.from_numpy(w).to(torch.bfloat16)
+        x64, w64 = xt.double().numpy(), wt.double().numpy()
+        got = oracle.router_logits(xt, wt)
+    else:
+        x64, w64 = x.astype(np.float64), w.astype(np.float64)
+        got = oracle.router_logits(x, w)
+    assert got.shape == (T, E) and got.dtype == np.float32
+    exact = _exact_logits(x64, w64).astype(np.float32)
+    np.testing.assert_array_equal(got.view(np.uint32), exact.view(np.uint32))
+    mm = (x64 @ w64.T).astype(np.float32)
+    np.testing.assert_array_equal(got.view(np.uint32), mm.view(np.uint32))
+    # the transposed reading or an fp32 accumulation would give other bits
+    if H > 1:
+        acc32 = np.zeros((T, E), np.float32)
+        for h in range(H):
+            acc32 = (acc32 + (x[:, h:h + 1] * w[:, h][None, :]).astype(np.float32)).astype(np.float32)
+        if dtype == "f32":
+            assert not np.array_equal(acc32.view(np.uint32), got.view(np.uint32))
+
+
+def test_router_logits_one_hot_weights_expose_x():
+    """W_r with one 1 per row selects a column of x: logits[t, e] = x[t, c_e] exactly."""
+    rng = np.random.default_rng(3)
+    T, H, E = 11, 40, 6
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    cols = np.array([39, 0, 7, 7, 21, 2])
+    w = np.zeros((E, H), np.float32)
+    w[np.arange(E), cols] = 1.0
+    np.testing.assert_array_equal(oracle.router_logits(x, w), x[:, cols])
+
+
+@pytest.mark.parametrize("name", ["qwen3_bf16", "dsv3_bf16"])
+def test_routing_margin_bounds_flips_under_perturbation(name):
+    """The tie margin the GPU-router tests use (helpers.routing_margin): perturbing the
+    oracle's logits by ~2e-5 relative changes the expert set of some tokens, and only of
+    tokens whose margin is tiny; every margin is >= 0 (the oracle's selection is a true
+    top-k)."""
+    import moe_inputs as mi
+    from helpers import routing_margin
+    cfg = mi.scaled(mi.CONFIGS[name], T=3000, H=256)
+    rng = np.random.default_rng(17)
+    lg = (rng.standard_normal((cfg.T, cfg.E)) * 1.3).astype(np.float32)
+    sb = (rng.standard_normal(cfg.E) * 0.01).astype(np.float32) if cfg.router else None
+    idx, _ = oracle.route_cfg(cfg, lg, None, sb)
+    m = routing_margin(cfg, lg, None, sb)
+    assert np.all(m >= 0)
+    pert = (lg * (1 + 2e-5 * rng.standard_normal(lg.shape))).astype(np.float32)
+    idx2, _ = oracle.route_cfg(cfg, pert, None, sb)
+    flipped = ~np.all(np.sort(idx, 1) == np.sort(idx2, 1), axis=1)
+    assert flipped.any()
+    assert np.all(m[flipped] <= 1e-4)
+    # margins spread far above the bound for most tokens
+    assert np.median(m) > 1e-3
