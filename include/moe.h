@@ -197,6 +197,20 @@ int moe_permute(const moe_config* cfg, const void* x, const int32_t* topk_idx,
                 void* x_q, void* x_q_scales, void* ws, size_t ws_bytes,
                 hipStream_t stream);
 
+/* moe_permute without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same arguments, outputs and results as moe_permute, bit for bit, but its scratch (the
+ * per-chunk expert histograms, ceil(T*k / 512) * E int32) lives in a 4 MiB device array
+ * inside the library that each GPU holds until the process ends. Sizes whose scratch exceeds
+ * 4 MiB (ceil(T*k / 512) * E > 1048576) return MOE_ERR_WORKSPACE and launch nothing. Every
+ * call overwrites the part it uses (nothing needs to start at zero). Calls that overlap on one
+ * GPU (several streams or host threads at once) share that array and race: serialise them.
+ * The stream must belong to the current device. Allocates nothing, ever. */
+int moe_permute_noalloc(const moe_config* cfg, const void* x, const int32_t* topk_idx,
+                        const float* topk_gate, int32_t* counts, int32_t* offsets,
+                        int32_t* pos, int32_t* src, float* gate_perm, void* x_perm,
+                        void* x_perm_scales, void* x_q, void* x_q_scales, hipStream_t stream);
+
 /* SwiGLU experts as one grouped GEMM over the expert-grouped rows (ragged per-expert M).
  * For expert e and its rows R_e = [offsets[e], offsets[e+1]):
  *   Z   = x_perm[R_e] W13_e^T                     [M_e, 2F]  (fp32 accumulation)

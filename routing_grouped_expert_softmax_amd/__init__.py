@@ -64,6 +64,7 @@ _SIGS = {
     "moe_route": [CFG, P, P, P, P, P, P],
     "moe_route_stats": [CFG, P, P, P, P, P, P, P, SZ, P],
     "moe_permute": [CFG, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
+    "moe_permute_noalloc": [CFG, P, P, P, P, P, P, P, P, P, P, P, P, P],
     "moe_grouped_gemm_swiglu": [CFG, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P,
                                 P, SZ, P],
     "moe_grouped_gemm_up": [CFG, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
@@ -252,6 +253,37 @@ def permute(cfg, x, topk_idx, topk_gate, want_x_q=False, ws=None, out=None, stre
         _ptr(out["counts"]), _ptr(out["offsets"]), _ptr(out["pos"]), _ptr(out["src"]),
         _ptr(out["gate_perm"]), _ptr(out["x_perm"]), _ptr(out["x_perm_scales"]),
         _ptr(out["x_q"]), _ptr(out["x_q_scales"]), _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def permute_noalloc(cfg, x, topk_idx, topk_gate, want_x_q=False, out=None, stream=None):
+    """moe_permute_noalloc: moe_permute with the library's own device scratch (no workspace).
+    Returns the same dict as permute(); `out` may pass a previous result to overwrite."""
+    dev = x.device
+    T, H, E, k = cfg.T, cfg.H, cfg.E, cfg.k
+    A = T * k
+    fp8 = is_fp8(cfg)
+    xsd, xss = act_scale_spec(cfg, A, H)
+    qsd, qss = act_scale_spec(cfg, T, H)
+    out = out if out is not None else dict(
+        counts=torch.empty(E, dtype=torch.int32, device=dev),
+        offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+        pos=torch.empty(T, k, dtype=torch.int32, device=dev),
+        src=torch.empty(A, dtype=torch.int32, device=dev),
+        gate_perm=torch.empty(A, dtype=torch.float32, device=dev),
+        x_perm=torch.empty(A, H, dtype=gemm_torch_dtype(cfg), device=dev),
+        x_perm_scales=torch.empty(xss, dtype=xsd, device=dev) if fp8 else None,
+        x_q=torch.empty(T, H, dtype=torch.uint8, device=dev) if (fp8 and want_x_q) else None,
+        x_q_scales=torch.empty(qss, dtype=qsd, device=dev) if (fp8 and want_x_q) else None,
+    )
+    c = make_config(cfg)
+    _check("moe_permute_noalloc", _lib.moe_permute_noalloc(
+        C.byref(c), _ptr(x, act_torch_dtype(cfg), (T, H), "x"),
+        _ptr(topk_idx, torch.int32, (T, k), "topk_idx"),
+        _ptr(topk_gate, torch.float32, (T, k), "topk_gate"),
+        _ptr(out["counts"]), _ptr(out["offsets"]), _ptr(out["pos"]), _ptr(out["src"]),
+        _ptr(out["gate_perm"]), _ptr(out["x_perm"]), _ptr(out["x_perm_scales"]),
+        _ptr(out["x_q"]), _ptr(out["x_q_scales"]), _stream(stream)))
     return out
 
 

@@ -5,6 +5,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/moe.h"
 #include "kernels.h"
 
@@ -339,6 +341,37 @@ int run_experts(const moe_config* c, int a_kb, const void* x_perm, const void* x
                     ws2_scales, y_perm, shared_y, sched, stream, mx_blocked);
 }
 
+// ---- the no-allocation permute's scratch -------------------------------------------------
+// The per-chunk expert histograms of the permute (its only scratch) in a file-scope device
+// array instead of the caller's workspace. Every GPU the library runs on holds its own copy
+// until the process ends. In host code `scratch` is a host-side stand-in: its device address
+// comes from hipGetSymbolAddress, looked up once per device with that device current, and
+// only that address is handed to kernels.
+constexpr size_t kNoAllocScratchBytes = (size_t)4 << 20;
+constexpr int kMaxDevices = 64;
+}  // namespace
+
+static __device__ __align__(256) int32_t scratch[kNoAllocScratchBytes / sizeof(int32_t)];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch (looked up on the first call on a device).
+int scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -434,6 +467,31 @@ int moe_permute(const moe_config* cfg, const void* x, const int32_t* topk_idx,
                                           cfg->H, cfg->E, cfg->k, counts, offsets, pos, src,
                                           gate_perm, x_perm, x_perm_scales, x_q, x_q_scales, ws,
                                           stream));
+}
+
+int moe_permute_noalloc(const moe_config* cfg, const void* x, const int32_t* topk_idx,
+                        const float* topk_gate, int32_t* counts, int32_t* offsets,
+                        int32_t* pos, int32_t* src, float* gate_perm, void* x_perm,
+                        void* x_perm_scales, void* x_q, void* x_q_scales, hipStream_t stream) {
+    int st = check_cfg(cfg);
+    if (st) return st;
+    if (!x || !topk_idx || !topk_gate || !counts || !offsets || !pos || !src || !gate_perm ||
+        !x_perm)
+        return MOE_ERR_INVALID_ARG;
+    const bool fp8 = is_fp8(cfg->w_dtype);
+    if (fp8 != (x_perm_scales != nullptr)) return MOE_ERR_INVALID_ARG;
+    if (!fp8 && (x_q || x_q_scales)) return MOE_ERR_INVALID_ARG;
+    if ((x_q == nullptr) != (x_q_scales == nullptr)) return MOE_ERR_INVALID_ARG;
+    if (moe::permute_ws_bytes(cfg->T, cfg->k, cfg->E) > kNoAllocScratchBytes)
+        return MOE_ERR_WORKSPACE;
+    void* sp = nullptr;
+    st = scratch_address(&sp);
+    if (st) return st;
+    const int mode = cfg->w_dtype == MOE_MXFP8 ? 3 : fp8 ? 2 : (cfg->act_dtype == MOE_F32 ? 0 : 1);
+    return hip_status(moe::launch_permute(mode, cfg->a_layout, capacity_of(cfg), x, topk_idx,
+                                          topk_gate, cfg->T, cfg->H, cfg->E, cfg->k, counts,
+                                          offsets, pos, src, gate_perm, x_perm, x_perm_scales,
+                                          x_q, x_q_scales, sp, stream));
 }
 
 int moe_grouped_gemm_swiglu(const moe_config* cfg, const void* x_perm,
