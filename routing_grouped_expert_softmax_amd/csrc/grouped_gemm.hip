@@ -680,9 +680,14 @@ MOE_DEVICE i32x8_t lds_frag32(const uint8_t* p0, const uint8_t* p1) {
     return i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
+// K loop of the e4m3 kernel. The MFMA takes the weight fragment as its first operand and the
+// activation fragment as its second, so a lane's 16 accumulator values of a 32 x 32 sub-tile
+// are one output row m (lane % 32) and 16 output columns n that lie in one 128-column weight
+// block: the promotion factor s_a[m][kb] * s_w[nb][kb] is one scalar per lane and sub-tile,
+// and promoting a partial tile costs 16 FMAs and one multiply per lane.
 template <class C, int NV, class Issue>
 MOE_DEVICE void e4m3_kloop(int nk, const uint8_t* lds, Issue& issue, const int (&a_off)[C::kTM],
-                           const int (&b_off)[C::kTN], const int (&co)[2][2], int srow0,
+                           const int (&b_off)[C::kTN], const int (&co)[2][2], int wm, int lane,
                            const float* __restrict__ wsc,
                            const int (&wsc_off)[C::kTN], f32x16_t (&acc)[C::kTM][C::kTN]) {
     constexpr int STAGES = C::kStages;
@@ -718,25 +723,21 @@ MOE_DEVICE void e4m3_kloop(int nk, const uint8_t* lds, Issue& issue, const int (
                     bv[s2][j] = lds_frag32(base + b_off[j] + co[s2][0], base + b_off[j] + co[s2][1]);
 #pragma unroll
             for (int i = 0; i < NVv; ++i) {
+                // this lane's output row of sub-tile i and its activation scale (wave w DMA'd
+                // the scales of tile rows kRpw w + [0, kRpw) to float kRpw-group * 64)
+                const int row = wm * (C::kTM * 32) + i * 32 + lane % 32;
+                const float sa = sa_l[(row / C::kRpw) * 64 + row % C::kRpw];
                 const i32x8_t a0 = lds_frag32(base + a_off[i] + co[0][0], base + a_off[i] + co[0][1]);
                 const i32x8_t a1 = lds_frag32(base + a_off[i] + co[1][0], base + a_off[i] + co[1][1]);
 #pragma unroll
                 for (int j = 0; j < C::kTN; ++j) {
                     f32x16_t pt = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        a0, bv[0][j], f32x16_t{}, 0, 0, 0, 0x7F7F7F7F, 0, 0x7F7F7F7F);
+                        bv[0][j], a0, f32x16_t{}, 0, 0, 0, 0x7F7F7F7F, 0, 0x7F7F7F7F);
                     pt = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        a1, bv[1][j], pt, 0, 0, 0, 0x7F7F7F7F, 0, 0x7F7F7F7F);
+                        bv[1][j], a1, pt, 0, 0, 0, 0x7F7F7F7F, 0, 0x7F7F7F7F);
+                    const float c = sa * sw[j];
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        // scales of rows q * 8 + (l / 32) * 4 + [0, 4) of sub-tile i
-                        const int row = srow0 + i * 32 + q * 8;   // this lane's 4 rows
-                        const f32x4_t v =
-                            *(const f32x4_t*)(sa_l + (row / C::kRpw) * 64 + row % C::kRpw);
-#pragma unroll
-                        for (int u = 0; u < 4; ++u)
-                            acc[i][j][4 * q + u] =
-                                fmaf(pt[4 * q + u], v[u] * sw[j], acc[i][j][4 * q + u]);
-                    }
+                    for (int r = 0; r < 16; ++r) acc[i][j][r] = fmaf(pt[r], c, acc[i][j][r]);
                 }
             }
         }
@@ -829,8 +830,6 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_e4m3_kernel(GemmArgs ga) {
 #pragma unroll
         for (int u = 0; u < 2; ++u)
             co[s][u] = ((4 * s + 2 * (lane / 32) + u) ^ chunk_swz<8>(lane % 32)) * 16;
-    // first of the rows (r/4)*8 + (l/32)*4 + [0,4) whose scales this lane applies
-    const int srow0 = wm * (BM / WM) + (lane / 32) * 4;
     // weight-scale offsets (per sub-tile j): [g][n_block][kb]
     const int nbn = N / 128;
     int wsc_off[C::kTN];
@@ -852,8 +851,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_e4m3_kernel(GemmArgs ga) {
     case V:                                                                                 \
         if (V <= C::kTM) {                                                                  \
             constexpr int NV = V <= C::kTM ? V : C::kTM;                                    \
-            e4m3_kloop<C, NV>(KB, lds, issue, a_off, b_off, co, srow0, (const float*)S.w_scales, wsc_off, \
-                              acc);                                                         \
+            e4m3_kloop<C, NV>(KB, lds, issue, a_off, b_off, co, wm, lane,                   \
+                              (const float*)S.w_scales, wsc_off, acc);                      \
         }                                                                                   \
         break;
     MOE_F8_CASE(0)
@@ -865,70 +864,75 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_e4m3_kernel(GemmArgs ga) {
     default: break;
     }
 
+    // Epilogue. Accumulator layout (weights as the first MFMA operand): element r of lane l of
+    // sub-tile (i, j) is tile row wm * (BM / WM) + 32 i + l % 32 and tile column
+    // wn * (BN / WN) + 32 j + 8 (r / 4) + 4 (l / 32) + r % 4, so every lane holds runs of four
+    // consecutive columns of one row and writes them with one store.
     if (KIND == 1) {
         uint16_t* out = (uint16_t*)S.out;
 #pragma unroll
         for (int i = 0; i < C::kTM; ++i) {
             if (i >= nvi) continue;
+            const int row = wm * (BM / WM) + i * 32 + lane % 32;
+            if (m0 + row >= Mg) continue;
+            const size_t grow = (size_t)rbase + m0 + row;
 #pragma unroll
-            for (int j = 0; j < C::kTN; ++j) {
-                const int col = nt * BN + wn * (BN / WN) + j * 32 + lane % 32;
+            for (int j = 0; j < C::kTN; ++j)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = wm * (BM / WM) + i * 32 + (r / 4) * 8 + (lane / 32) * 4 + r % 4;
-                    if (m0 + row >= Mg) continue;
-                    const size_t grow = (size_t)rbase + m0 + row;
-                    out[grow * N + col] = f32_to_bf16(acc[i][j][r]);
+                for (int q = 0; q < 4; ++q) {
+                    const int col = nt * BN + wn * (BN / WN) + j * 32 + 8 * q + 4 * (lane / 32);
+                    const uint2 v = make_uint2(pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                                               pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
+                    *(uint2*)(out + grow * N + col) = v;
                 }
-            }
         }
         return;
     }
-    // ---- GEMM1: act = gate * silu(Z_g) * Z_u, quantised per row over this tile's 128
-    // act columns (one 1 x 128 block): amax over lanes (shuffles), then over waves (LDS)
+    // ---- GEMM1: act = gate * silu(Z_g) * Z_u (sub-tile 0: gate columns, 1: the matching up
+    // columns), quantised per row over this tile's 128 act columns (one 1 x 128 block): amax
+    // over the lane's 16 values, its partner lane l ^ 32, then the WN waves (LDS)
     const int F = N / 2;
     float av[C::kTM][16];
     float* amax_l = (float*)lds;                       // [WN][BM]
-#pragma unroll
-    for (int i = 0; i < C::kTM; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int row = wm * (BM / WM) + i * 32 + (r / 4) * 8 + (lane / 32) * 4 + r % 4;
-            const int lr = m0 + row < Mg ? row : live - 1;
-            const float gt = S.gate ? S.gate[(size_t)rbase + m0 + lr] : 1.0f;
-            av[i][r] = gt * (silu_fast(acc[i][0][r]) * acc[i][1][r]);
-        }
     block_sync();                                      // every wave is done with the stages
 #pragma unroll
-    for (int i = 0; i < C::kTM; ++i)
+    for (int i = 0; i < C::kTM; ++i) {
+        const int row = wm * (BM / WM) + i * 32 + lane % 32;
+        const int lr = m0 + row < Mg ? row : live - 1;
+        const float gt = S.gate ? S.gate[(size_t)rbase + m0 + lr] : 1.0f;
+        float m = 0.0f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            float m = fabsf(av[i][r]);
-#pragma unroll
-            for (int off = 1; off < 32; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
-            const int row = wm * (BM / WM) + i * 32 + (r / 4) * 8 + (lane / 32) * 4 + r % 4;
-            if (lane % 32 == 0) amax_l[wn * BM + row] = m;
+            av[i][r] = gt * (silu_fast(acc[i][0][r]) * acc[i][1][r]);
+            m = fmaxf(m, fabsf(av[i][r]));
         }
+        m = fmaxf(m, __shfl_xor(m, 32));
+        if (lane < 32) amax_l[wn * BM + row] = m;
+    }
     __syncthreads();
     uint8_t* outq = (uint8_t*)S.out;
-    const int col = nt * (BN / 2) + wn * (BN / 2 / WN) + lane % 32;    // act column
 #pragma unroll
     for (int i = 0; i < C::kTM; ++i) {
         if (i >= nvi) continue;
+        const int row = wm * (BM / WM) + i * 32 + lane % 32;
+        if (m0 + row >= Mg) continue;
+        float m = 0.0f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int row = wm * (BM / WM) + i * 32 + (r / 4) * 8 + (lane / 32) * 4 + r % 4;
-            if (m0 + row >= Mg) continue;
-            float m = 0.0f;
+        for (int w = 0; w < WN; ++w) m = fmaxf(m, amax_l[w * BM + row]);
+        const float sc = e4m3_scale(m);
+        const size_t grow = (size_t)rbase + m0 + row;
 #pragma unroll
-            for (int w = 0; w < WN; ++w) m = fmaxf(m, amax_l[w * BM + row]);
-            const float sc = e4m3_scale(m);
-            const size_t grow = (size_t)rbase + m0 + row;
+        for (int q = 0; q < 4; ++q) {
+            const int col = nt * (BN / 2) + wn * (BN / 2 / WN) + 8 * q + 4 * (lane / 32);
+            const uint32_t codes = e4m3_rne_sat(av[i][4 * q] / sc) |
+                                   (e4m3_rne_sat(av[i][4 * q + 1] / sc) << 8) |
+                                   (e4m3_rne_sat(av[i][4 * q + 2] / sc) << 16) |
+                                   (e4m3_rne_sat(av[i][4 * q + 3] / sc) << 24);
             const size_t oi = S.out_kblock ? ((size_t)(col / 64) * S.rows_total + grow) * 64 + col % 64
                                            : grow * F + col;
-            outq[oi] = (uint8_t)e4m3_rne_sat(av[i][r] / sc);
-            if (wn == 0 && lane % 32 == 0) ((float*)S.out_scales)[grow * (F / 128) + nt] = sc;
+            *(uint32_t*)(outq + oi) = codes;
         }
+        if (wn == 0 && lane < 32) ((float*)S.out_scales)[grow * (F / 128) + nt] = sc;
     }
 }
 
