@@ -229,7 +229,7 @@ struct BfCfg {
 // rows in another). Operand fragments are double-buffered in registers: the LDS reads of
 // sub-step s + 1 are placed between the MFMAs of sub-step s (sched_group_barrier: MFMA /
 // DS-read interleave).
-template <class C, int NV>
+template <class C, int NV, bool TR>
 MOE_DEVICE void bf16_stage_mma(const uint8_t* base_a, const uint8_t* base_b,
                                const int (&a_off)[C::kTM], const int (&b_off)[C::kTN],
                                const int (&chunk_off)[C::kSub],
@@ -256,8 +256,10 @@ MOE_DEVICE void bf16_stage_mma(const uint8_t* base_a, const uint8_t* base_b,
         for (int i = 0; i < NV; ++i)
 #pragma unroll
             for (int j = 0; j < C::kTN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[cur][i], bv[cur][j],
-                                                                    acc[i][j], 0, 0, 0);
+                acc[i][j] = TR ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[cur][j], av[cur][i],
+                                                                         acc[i][j], 0, 0, 0)
+                               : __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[cur][i], bv[cur][j],
+                                                                         acc[i][j], 0, 0, 0);
     }
 #ifndef MOE_NO_SCHED_INTERLEAVE
     constexpr int kReads = C::kTN + NVv;
@@ -279,7 +281,7 @@ MOE_DEVICE void bf16_stage_mma(const uint8_t* base_a, const uint8_t* base_b,
 // weight stream -- which carries most of the HBM misses -- is prefetched further ahead.
 // vmcnt: loads complete in issue order, so step kt may proceed once at most the loads issued
 // after the later of A(kt), B(kt) remain.
-template <class C, int NV, class IssueA, class IssueB>
+template <class C, int NV, bool TR, class IssueA, class IssueB>
 MOE_DEVICE void bf16_kloop(int nk, const uint8_t* lds, IssueA& issue_a, IssueB& issue_b,
                            const int (&a_off)[C::kTM], const int (&b_off)[C::kTN],
                            const int (&chunk_off)[C::kSub],
@@ -320,8 +322,8 @@ MOE_DEVICE void bf16_kloop(int nk, const uint8_t* lds, IssueA& issue_a, IssueB& 
             if (kt + SA - 1 < nk) issue_a(kt + SA - 1, na);
             if (kt + SB - 1 < nk) issue_b(kt + SB - 1, nb);
         }
-        bf16_stage_mma<C, NV>(lds + sa * C::kASlot, lds + C::kBRing + sb * C::kBSlot, a_off,
-                              b_off, chunk_off, acc);
+        bf16_stage_mma<C, NV, TR>(lds + sa * C::kASlot, lds + C::kBRing + sb * C::kBSlot, a_off,
+                                  b_off, chunk_off, acc);
         if (++sa == SA) sa = 0;
         if (++sb == SB) sb = 0;
     }
@@ -383,7 +385,7 @@ MOE_DEVICE void bf16_kloop_pp(int nst, const uint8_t* lds, const uint8_t* const 
             for (int i = 0; i < NV; ++i)
 #pragma unroll
                 for (int j = 0; j < C::kTN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[u][i], bv[u][j],
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[u][j], av[u][i],
                                                                         acc[i][j], 0, 0, 0);
     };
     // this group's DMAs of step s + 1 have landed (later steps may still be in flight)
@@ -553,7 +555,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs ga) {
                 bf16_kloop_pp<C, NV>(nk, lds, src, pp_step, grp, gw, a_off, b_off,          \
                                      chunk_off, acc);                                       \
             else                                                                            \
-                bf16_kloop<C, NV>(nk, lds, issue_a, issue_b, a_off, b_off, chunk_off, acc); \
+                bf16_kloop<C, NV, true>(nk, lds, issue_a, issue_b, a_off, b_off, chunk_off,  \
+                                        acc);                                               \
         }                                                                                   \
         break;
     MOE_KLOOP_CASE(0)
@@ -569,13 +572,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs ga) {
     default: break;
     }
 
-    // epilogue. 32x32 accumulator layout: element r of lane l is
-    // row (r/4)*8 + (l/32)*4 + r%4, column l%32. The bf16 output tile (GEMM1: act) is staged
-    // in LDS as [BM][kEpCols + 8] and then written with 16-byte row chunks per lane, so every
-    // store is coalesced (a K-blocked act slice of the tile is one contiguous run).
-    constexpr int kEpCols = C::kEpCols, kEpStride = C::kEpStride;
-    block_sync();                                   // every wave is done with the stages
-    uint16_t* ep = (uint16_t*)lds;
+    // epilogue, straight from the registers. The weights are the first MFMA operand, so
+    // element r of lane l of sub-tile (i, j) is tile row sub_row(wm, i) + l % 32 and column
+    // 8 (r / 4) + 4 (l / 32) + r % 4 of the sub-tile's 32: every lane holds runs of four
+    // consecutive columns of one row and writes each run with one 8-byte store (a row's 64
+    // bytes of a sub-tile come from lanes l and l + 32 in four stores).
+    uint16_t* out = (uint16_t*)S.out;
     if (KIND == 0) {
         constexpr int half = C::kTN / 2;
         const int F = N / 2;
@@ -583,57 +585,64 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs ga) {
 #pragma unroll
         for (int i = 0; i < C::kTM; ++i) {
             if (i >= nvi) continue;
+            const int row = C::sub_row(wm, i) + lane % 32;
+            if (m0 + row >= Mg) continue;
+            const size_t grow = (size_t)rbase + m0 + row;
+            const float gt = gate_lds[row];
 #pragma unroll
-            for (int jj = 0; jj < half; ++jj) {
-                const int lcol = wn * (BN / 2 / WN) + jj * 32 + lane % 32;
-                const int col = nt * (BN / 2) + lcol;
+            for (int jj = 0; jj < half; ++jj)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = C::sub_row(wm, i) + (r / 4) * 8 + (lane / 32) * 4 + r % 4;
-                    const int lr = m0 + row < Mg ? row : live - 1;     // dead rows: any gate
-                    const size_t grow = (size_t)rbase + m0 + lr;
-                    const float zg = acc[i][jj][r], zu = acc[i][half + jj][r];
-                    const float gt = gate_lds[lr];
-                    ep[row * kEpStride + lcol] = f32_to_bf16(gt * (silu_fast(zg) * zu));
-                    if (zo && m0 + row < Mg) {
-                        zo[grow * N + col] = f32_to_bf16(zg);
-                        zo[grow * N + F + col] = f32_to_bf16(zu);
+                for (int q = 0; q < 4; ++q) {
+                    const int col = nt * (BN / 2) + wn * (BN / 2 / WN) + jj * 32 + 8 * q +
+                                    4 * (lane / 32);
+                    float a[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        a[u] = gt * (silu_fast(acc[i][jj][4 * q + u]) * acc[i][half + jj][4 * q + u]);
+                    const size_t oi = S.out_kblock
+                                          ? ((size_t)(col / 32) * S.rows_total + grow) * 32 + col % 32
+                                          : grow * F + col;
+                    *(uint2*)(out + oi) = make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
+                    if (zo) {
+                        const f32x16_t& g = acc[i][jj];
+                        const f32x16_t& u = acc[i][half + jj];
+                        *(uint2*)(zo + grow * N + col) =
+                            make_uint2(pack_bf16x2(g[4 * q], g[4 * q + 1]),
+                                       pack_bf16x2(g[4 * q + 2], g[4 * q + 3]));
+                        *(uint2*)(zo + grow * N + F + col) =
+                            make_uint2(pack_bf16x2(u[4 * q], u[4 * q + 1]),
+                                       pack_bf16x2(u[4 * q + 2], u[4 * q + 3]));
                     }
                 }
-            }
         }
     } else {
+        // GEMM2's bf16 tile (128 KB) goes through LDS: each lane's runs of four columns as
+        // 8-byte writes into [BM][kEpCols + 8], then 16-byte row chunks to global memory
+        // (measured faster here than 8-byte stores straight from the registers)
+        constexpr int kEpCols = C::kEpCols, kEpStride = C::kEpStride;
+        block_sync();                                   // every wave is done with the stages
+        uint16_t* ep = (uint16_t*)lds;
 #pragma unroll
         for (int i = 0; i < C::kTM; ++i) {
             if (i >= nvi) continue;
+            const int row = C::sub_row(wm, i) + lane % 32;
 #pragma unroll
-            for (int j = 0; j < C::kTN; ++j) {
-                const int lcol = wn * (BN / WN) + j * 32 + lane % 32;
+            for (int j = 0; j < C::kTN; ++j)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = C::sub_row(wm, i) + (r / 4) * 8 + (lane / 32) * 4 + r % 4;
-                    ep[row * kEpStride + lcol] = f32_to_bf16(acc[i][j][r]);
+                for (int q = 0; q < 4; ++q) {
+                    const int lcol = wn * (BN / WN) + j * 32 + 8 * q + 4 * (lane / 32);
+                    *(uint2*)(ep + row * kEpStride + lcol) =
+                        make_uint2(pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                                   pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
                 }
-            }
         }
-    }
-    __syncthreads();
-    {
-        constexpr int kChunks = kEpCols / 8;        // 16-byte chunks per tile row
-        const int Nout = KIND == 0 ? N / 2 : N;
-        const int c0 = nt * kEpCols;                // first output column of the tile
-        uint16_t* out = (uint16_t*)S.out;
+        __syncthreads();
+        constexpr int kChunks = kEpCols / 8;            // 16-byte chunks per tile row
+        const int c0 = nt * kEpCols;                    // first output column of the tile
         for (int c = tid; c < live * kChunks; c += C::kThreads) {
             const int row = c / kChunks, cc = c % kChunks;
             const uint4 v = *(const uint4*)(ep + row * kEpStride + cc * 8);
-            const size_t grow = (size_t)rbase + m0 + row;
-            const int col = c0 + cc * 8;
-            size_t oi;
-            if (KIND == 0 && S.out_kblock)
-                oi = ((size_t)(col / 32) * S.rows_total + grow) * 32 + col % 32;
-            else
-                oi = grow * Nout + col;
-            *(uint4*)(out + oi) = v;
+            *(uint4*)(out + ((size_t)rbase + m0 + row) * N + c0 + cc * 8) = v;
         }
     }
 }
@@ -1519,21 +1528,28 @@ __global__ __launch_bounds__(RouterCfg::kThreads) void router_gemm_kernel(Router
     for (int i = 0; i < C::kTM; ++i)
 #pragma unroll
         for (int j = 0; j < C::kTN; ++j) acc[i][j] = f32x16_t{};
-    bf16_kloop<C, C::kTM>(klen / 64, lds, issue_a, issue_b, a_off, b_off, chunk_off, acc);
+    bf16_kloop<C, C::kTM, true>(klen / 64, lds, issue_a, issue_b, a_off, b_off, chunk_off, acc);
 
-    // 32x32 accumulator: element r of lane l is row (r/4)*8 + (l/32)*4 + r%4, column l%32
+    // weights as the first MFMA operand: element r of lane l of sub-tile (i, j) is token
+    // m0 + sub_row(wm, i) + l % 32 and expert n0 + wn * 64 + 32 j + 8 (r / 4) + 4 (l / 32) + r % 4,
+    // so a lane writes four consecutive experts of one token with one 16-byte store (E is a
+    // multiple of 4 on this path, router_gemm_ksplit, so a run is all in range or all out)
     float* out = ra.part + (size_t)ks * ra.T * ra.E;
 #pragma unroll
-    for (int i = 0; i < C::kTM; ++i)
+    for (int i = 0; i < C::kTM; ++i) {
+        const int t = m0 + C::sub_row(wm, i) + lane % 32;
+        if (t >= ra.T) continue;
 #pragma unroll
-        for (int j = 0; j < C::kTN; ++j) {
-            const int e = n0 + wn * 64 + j * 32 + lane % 32;
+        for (int j = 0; j < C::kTN; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int t = m0 + C::sub_row(wm, i) + (r / 4) * 8 + (lane / 32) * 4 + r % 4;
-                if (t < ra.T && e < ra.E) out[(size_t)t * ra.E + e] = acc[i][j][r];
+            for (int q = 0; q < 4; ++q) {
+                const int e = n0 + wn * 64 + j * 32 + 8 * q + 4 * (lane / 32);
+                if (e < ra.E)
+                    *(f32x4_t*)(out + (size_t)t * ra.E + e) =
+                        f32x4_t{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                acc[i][j][4 * q + 3]};
             }
-        }
+    }
 }
 
 // logits = sum over the K ranges of the partial tiles, in range order.
