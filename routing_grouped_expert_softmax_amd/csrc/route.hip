@@ -43,21 +43,52 @@ MOE_DEVICE void stats_block_sum(const float (&p)[VPL], bool valid, int E, int la
 }
 
 // ---------------------------------------------------------------------------------------
-// top-k over the keys a wavefront holds; returns, in lane j < k, the j-th expert
+// top-k over the keys a wavefront holds; returns, in lane j < k, the j-th expert.
+//
+// Every expert's 64-bit rank key (order-preserving key, then inverted index) is distinct, so
+// the k selected experts are exactly those whose rank key is at least the k-th largest one.
+// That threshold is found bit by bit from the top, counting with ballots (no data crosses
+// lanes): a candidate bit stays set when at least k keys reach the prefix with it set. Then
+// the slot of each selected expert is the number of keys above its own (all of which are
+// selected), counted the same way, and the lane of that slot takes the expert. Keys of 0
+// mark absent experts; k never exceeds the number of present ones.
 // ---------------------------------------------------------------------------------------
 template <int VPL>
+MOE_DEVICE int count_ge(const uint64_t (&rk)[VPL], uint64_t v) {
+    int n = 0;
+#pragma unroll
+    for (int q = 0; q < VPL; ++q) n += __popcll(__ballot(rk[q] >= v));
+    return n;
+}
+
+template <int VPL>
 MOE_DEVICE int wave_topk(uint64_t (&rk)[VPL], int k, int lane) {
+    // the k-th largest key: the largest tau with count(rk >= tau) >= k. The top 32 bits (the
+    // order key) first; the index bits only matter when the k-th key ties with others.
+    uint64_t tau = 0;
+    for (int b = 63; b >= 32; --b) {
+        const uint64_t cand = tau | (1ull << b);
+        if (count_ge<VPL>(rk, cand) >= k) tau = cand;
+    }
+    if (count_ge<VPL>(rk, tau) != k) {
+        for (int b = 31; b >= 0; --b) {
+            const uint64_t cand = tau | (1ull << b);
+            if (count_ge<VPL>(rk, cand) >= k) tau = cand;
+        }
+    }
     int mine = -1;
-    for (int j = 0; j < k; ++j) {
-        uint64_t best = 0;
 #pragma unroll
-        for (int v = 0; v < VPL; ++v) best = rk[v] > best ? rk[v] : best;
-        best = wave_max_u64(best);
-        int e = rank_key_index(best);
-        if (lane == j) mine = e;
-#pragma unroll
-        for (int v = 0; v < VPL; ++v)
-            if (v * kWave + lane == e) rk[v] = 0;   // taken
+    for (int q = 0; q < VPL; ++q) {
+        uint64_t sel = __ballot(rk[q] >= tau && rk[q] != 0);
+        while (sel) {
+            const int l = __builtin_ctzll(sel);             // wave-uniform
+            sel &= sel - 1;
+            const uint64_t x =
+                ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(rk[q] >> 32), l) << 32) |
+                (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)rk[q], l);
+            const int slot = count_ge<VPL>(rk, x) - 1;       // keys above x
+            if (lane == slot) mine = q * kWave + l;
+        }
     }
     return mine;
 }
