@@ -145,6 +145,23 @@ MOE_DEVICE float silu_fast(float u) {
 }
 
 // ---------------------------------------------------------------------------------------
+// Output runs of the transposed 32 x 32 MFMA accumulators: lane l and lane l + 32 hold the
+// 4-column runs 8 q + 4 (l / 32) + [0, 4) of the same row. For two consecutive q (x: run q,
+// y: run q + 1, packed), v_permlane32_swap trades lane l's y for lane l + 32's x, so lane l
+// ends with columns 8 q .. 8 q + 7 and lane l + 32 with 8 q + 8 .. 8 q + 15: twice the bytes
+// per store. Every lane of the wave must execute it.
+// ---------------------------------------------------------------------------------------
+MOE_DEVICE uint4 pair_runs_x4(uint32_t x0, uint32_t x1, uint32_t y0, uint32_t y1) {
+    const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
+    const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
+    return make_uint4(s0[0], s1[0], s0[1], s1[1]);
+}
+MOE_DEVICE uint2 pair_runs_x2(uint32_t x, uint32_t y) {
+    const auto s = __builtin_amdgcn_permlane32_swap(x, y, false, false);
+    return make_uint2(s[0], s[1]);
+}
+
+// ---------------------------------------------------------------------------------------
 // LDS pipeline helpers of the MFMA kernels
 // ---------------------------------------------------------------------------------------
 #define MOE_LDS __attribute__((address_space(3)))

@@ -582,36 +582,45 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs ga) {
         constexpr int half = C::kTN / 2;
         const int F = N / 2;
         uint16_t* zo = (uint16_t*)S.z_out;
+        const int h = lane / 32;
 #pragma unroll
         for (int i = 0; i < C::kTM; ++i) {
             if (i >= nvi) continue;
             const int row = C::sub_row(wm, i) + lane % 32;
-            if (m0 + row >= Mg) continue;
-            const size_t grow = (size_t)rbase + m0 + row;
-            const float gt = gate_lds[row];
+            const bool live_row = m0 + row < Mg;       // lanes l and l + 32 share a row
+            const int lr = live_row ? row : live - 1;
+            const size_t grow = (size_t)rbase + m0 + lr;
+            const float gt = gate_lds[lr];
 #pragma unroll
             for (int jj = 0; jj < half; ++jj)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int col = nt * (BN / 2) + wn * (BN / 2 / WN) + jj * 32 + 8 * q +
-                                    4 * (lane / 32);
-                    float a[4];
+                for (int qp = 0; qp < 4; qp += 2) {
+                    // runs qp and qp + 1 of act, paired across lanes l, l + 32 (pair_runs_x4)
+                    const f32x16_t& g = acc[i][jj];
+                    const f32x16_t& u = acc[i][half + jj];
+                    float a[8];
 #pragma unroll
-                    for (int u = 0; u < 4; ++u)
-                        a[u] = gt * (silu_fast(acc[i][jj][4 * q + u]) * acc[i][half + jj][4 * q + u]);
+                    for (int e = 0; e < 8; ++e) a[e] = gt * (silu_fast(g[4 * qp + e]) * u[4 * qp + e]);
+                    const uint4 v = pair_runs_x4(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]),
+                                                 pack_bf16x2(a[4], a[5]), pack_bf16x2(a[6], a[7]));
+                    const int col = nt * (BN / 2) + wn * (BN / 2 / WN) + jj * 32 + 8 * (qp + h);
                     const size_t oi = S.out_kblock
                                           ? ((size_t)(col / 32) * S.rows_total + grow) * 32 + col % 32
                                           : grow * F + col;
-                    *(uint2*)(out + oi) = make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
+                    if (live_row) *(uint4*)(out + oi) = v;
                     if (zo) {
-                        const f32x16_t& g = acc[i][jj];
-                        const f32x16_t& u = acc[i][half + jj];
-                        *(uint2*)(zo + grow * N + col) =
-                            make_uint2(pack_bf16x2(g[4 * q], g[4 * q + 1]),
-                                       pack_bf16x2(g[4 * q + 2], g[4 * q + 3]));
-                        *(uint2*)(zo + grow * N + F + col) =
-                            make_uint2(pack_bf16x2(u[4 * q], u[4 * q + 1]),
-                                       pack_bf16x2(u[4 * q + 2], u[4 * q + 3]));
+                        const uint4 zg = pair_runs_x4(pack_bf16x2(g[4 * qp], g[4 * qp + 1]),
+                                                      pack_bf16x2(g[4 * qp + 2], g[4 * qp + 3]),
+                                                      pack_bf16x2(g[4 * qp + 4], g[4 * qp + 5]),
+                                                      pack_bf16x2(g[4 * qp + 6], g[4 * qp + 7]));
+                        const uint4 zu = pair_runs_x4(pack_bf16x2(u[4 * qp], u[4 * qp + 1]),
+                                                      pack_bf16x2(u[4 * qp + 2], u[4 * qp + 3]),
+                                                      pack_bf16x2(u[4 * qp + 4], u[4 * qp + 5]),
+                                                      pack_bf16x2(u[4 * qp + 6], u[4 * qp + 7]));
+                        if (live_row) {
+                            *(uint4*)(zo + grow * N + col) = zg;
+                            *(uint4*)(zo + grow * N + F + col) = zu;
+                        }
                     }
                 }
         }
@@ -883,16 +892,19 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_e4m3_kernel(GemmArgs ga) {
         for (int i = 0; i < C::kTM; ++i) {
             if (i >= nvi) continue;
             const int row = wm * (BM / WM) + i * 32 + lane % 32;
-            if (m0 + row >= Mg) continue;
-            const size_t grow = (size_t)rbase + m0 + row;
+            const bool live_row = m0 + row < Mg;       // lanes l and l + 32 share a row
+            const size_t grow = (size_t)rbase + m0 + (live_row ? row : 0);
 #pragma unroll
             for (int j = 0; j < C::kTN; ++j)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int col = nt * BN + wn * (BN / WN) + j * 32 + 8 * q + 4 * (lane / 32);
-                    const uint2 v = make_uint2(pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
-                                               pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
-                    *(uint2*)(out + grow * N + col) = v;
+                for (int qp = 0; qp < 4; qp += 2) {
+                    const f32x16_t& a = acc[i][j];
+                    const uint4 v = pair_runs_x4(pack_bf16x2(a[4 * qp], a[4 * qp + 1]),
+                                                 pack_bf16x2(a[4 * qp + 2], a[4 * qp + 3]),
+                                                 pack_bf16x2(a[4 * qp + 4], a[4 * qp + 5]),
+                                                 pack_bf16x2(a[4 * qp + 6], a[4 * qp + 7]));
+                    const int col = nt * BN + wn * (BN / WN) + j * 32 + 8 * (qp + lane / 32);
+                    if (live_row) *(uint4*)(out + grow * N + col) = v;
                 }
         }
         return;
@@ -924,24 +936,27 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_e4m3_kernel(GemmArgs ga) {
     for (int i = 0; i < C::kTM; ++i) {
         if (i >= nvi) continue;
         const int row = wm * (BM / WM) + i * 32 + lane % 32;
-        if (m0 + row >= Mg) continue;
+        const bool live_row = m0 + row < Mg;           // lanes l and l + 32 share a row
         float m = 0.0f;
 #pragma unroll
         for (int w = 0; w < WN; ++w) m = fmaxf(m, amax_l[w * BM + row]);
         const float sc = e4m3_scale(m);
-        const size_t grow = (size_t)rbase + m0 + row;
+        const size_t grow = (size_t)rbase + m0 + (live_row ? row : 0);
+        uint32_t codes[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int col = nt * (BN / 2) + wn * (BN / 2 / WN) + 8 * q + 4 * (lane / 32);
-            const uint32_t codes = e4m3_rne_sat(av[i][4 * q] / sc) |
-                                   (e4m3_rne_sat(av[i][4 * q + 1] / sc) << 8) |
-                                   (e4m3_rne_sat(av[i][4 * q + 2] / sc) << 16) |
-                                   (e4m3_rne_sat(av[i][4 * q + 3] / sc) << 24);
+        for (int q = 0; q < 4; ++q)
+            codes[q] = e4m3_rne_sat(av[i][4 * q] / sc) | (e4m3_rne_sat(av[i][4 * q + 1] / sc) << 8) |
+                       (e4m3_rne_sat(av[i][4 * q + 2] / sc) << 16) |
+                       (e4m3_rne_sat(av[i][4 * q + 3] / sc) << 24);
+#pragma unroll
+        for (int qp = 0; qp < 4; qp += 2) {
+            const uint2 v = pair_runs_x2(codes[qp], codes[qp + 1]);
+            const int col = nt * (BN / 2) + wn * (BN / 2 / WN) + 8 * (qp + lane / 32);
             const size_t oi = S.out_kblock ? ((size_t)(col / 64) * S.rows_total + grow) * 64 + col % 64
                                            : grow * F + col;
-            *(uint32_t*)(outq + oi) = codes;
+            if (live_row) *(uint2*)(outq + oi) = v;
         }
-        if (wn == 0 && lane < 32) ((float*)S.out_scales)[grow * (F / 128) + nt] = sc;
+        if (live_row && wn == 0 && lane < 32) ((float*)S.out_scales)[grow * (F / 128) + nt] = sc;
     }
 }
 
