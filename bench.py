@@ -276,6 +276,30 @@ def time_permute_copy(moe, mi, cfg, x, idx, gate, flush, reps):
     return out
 
 
+def hbm_copy_rate(dev, flush, reps=10):
+    """Context for the HBM-bound stages: torch's device copy of 1 GiB (the runtime's copy
+    kernel) after a cache flush, counting bytes read + written; median over reps."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev)
+    src.fill_(3)
+    dst = torch.empty(n, dtype=torch.uint8, device=dev)
+    ts = []
+    for _ in range(reps):
+        flush()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    med = pct(ts, 50)
+    del src, dst
+    return {"what": "device copy of 1 GiB (torch copy_), bytes read + written",
+            "ms": round(med, 4), "GB/s": round(2 * n / (med * 1e-3) / 1e9, 1),
+            "frac_hbm_peak": round(2 * n / (med * 1e-3) / PEAK_HBM, 4)}
+
+
 def time_route_stats(moe, cfg, logits, lb, sb, reps=20):
     """moe_route alone vs moe_route_stats (routing + fused load-balancing statistics) on the
     step's logits, HIP events on the current stream."""
@@ -574,6 +598,7 @@ def main():
         del ws
         torch.cuda.empty_cache()
         permute_copy = time_permute_copy(moe, mi, cfg, x, idx, gate, flush, 10)
+        permute_copy["hbm_copy_context"] = hbm_copy_rate(dev, flush)
         ws = None
 
     backward = None
