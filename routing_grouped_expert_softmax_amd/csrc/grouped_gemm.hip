@@ -1063,12 +1063,14 @@ MOE_DEVICE void mx_kloop(int nk, const uint8_t* lds, Issue& issue, const int (&a
                         lds_frag32(base + a_off[i] + co[s][0], base + a_off[i] + co[s][1]);
 #pragma unroll
                     for (int j = 0; j < C::kTN; ++j) {
+                        // weights as the first operand (transposed accumulators), each
+                        // operand with its own block scales
                         if (s == 0)
                             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                                av, bv[j], acc[i][j], 0, 0, 0, sa[i], 0, sb[j]);
+                                bv[j], av, acc[i][j], 0, 0, 0, sb[j], 0, sa[i]);
                         else
                             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                                av, bv[j], acc[i][j], 0, 0, 2, sa[i], 2, sb[j]);
+                                bv[j], av, acc[i][j], 0, 0, 2, sb[j], 2, sa[i]);
                     }
                 }
             }
@@ -1198,23 +1200,26 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmArgs ga) {
     default: break;
     }
 
-    // ---- epilogue (accumulator element r of lane l: row (r/4)*8 + (l/32)*4 + r%4, column
-    // l%32), staged in LDS so that every global store is a 16-byte (GEMM1 scales: 4-byte) run
-    block_sync();                                      // every wave is done with the stages
+    // ---- epilogue. Weights are the first MFMA operand: element r of lane l of sub-tile
+    // (i, j) is tile row wm * (BM / WM) + 32 i + l % 32 and column
+    // wn * (BN / WN) + 32 j + 8 (r / 4) + 4 (l / 32) + r % 4 (runs of four columns per lane).
     if (KIND == 1) {
+        // bf16 tile staged in LDS (8-byte writes), then 16-byte row chunks
+        block_sync();                                  // every wave is done with the stages
         uint16_t* ep = (uint16_t*)lds;
 #pragma unroll
         for (int i = 0; i < C::kTM; ++i) {
             if (i >= nvi) continue;
+            const int row = wm * (BM / WM) + i * 32 + lane % 32;
 #pragma unroll
-            for (int j = 0; j < C::kTN; ++j) {
-                const int lcol = wn * (BN / WN) + j * 32 + lane % 32;
+            for (int j = 0; j < C::kTN; ++j)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = wm * (BM / WM) + i * 32 + (r / 4) * 8 + half * 4 + r % 4;
-                    ep[row * C::kEpStride + lcol] = f32_to_bf16(acc[i][j][r]);
+                for (int q = 0; q < 4; ++q) {
+                    const int lcol = wn * (BN / WN) + j * 32 + 8 * q + 4 * half;
+                    *(uint2*)(ep + row * C::kEpStride + lcol) =
+                        make_uint2(pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                                   pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
                 }
-            }
         }
         __syncthreads();
         constexpr int kChunks = BN / 8;
@@ -1226,47 +1231,48 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmArgs ga) {
         }
         return;
     }
-    // GEMM1: act = gate * silu(Z_g) * Z_u, quantised per 1 x 32 block
+    // GEMM1: act = gate * silu(Z_g) * Z_u, quantised per 1 x 32 block. A block is the 32
+    // columns of gate sub-tile jj in one row: lane l holds 16 of them and lane l + 32 the
+    // other 16, so its amax takes the lane's own maximum and one exchange. Codes go out as
+    // 8-column runs (pair_runs_x2), the row's four block scales of this tile's 128 act columns
+    // (one per wave column) as bytes of its scale word.
     constexpr int hf = C::kTN / 2;
-    constexpr int kSc = BN / 64;                       // act blocks per tile row
-    uint8_t* ep = (uint8_t*)lds;
-    uint8_t* eps = ep + BM * C::kEpStride;             // [BM][kSc] scale codes
+    static_assert(hf == 1 && BN / 2 / WN == 32, "one 32-column block per wave and row");
+    const int F = N / 2;
+    uint8_t* outq = (uint8_t*)S.out;
+    uint8_t* outs = (uint8_t*)S.out_scales;
 #pragma unroll
     for (int i = 0; i < C::kTM; ++i) {
         if (i >= nvi) continue;
+        const int row = wm * (BM / WM) + i * 32 + lane % 32;
+        const bool live_row = m0 + row < Mg;           // lanes l and l + 32 share a row
+        const int lr = live_row ? row : live - 1;
+        const size_t grow = (size_t)rbase + m0 + lr;
+        const float gt = S.gate ? S.gate[grow] : 1.0f;
+        float v[16];
+        float m = 0.0f;
 #pragma unroll
-        for (int jj = 0; jj < hf; ++jj) {
-            const int lcol = wn * (BN / 2 / WN) + jj * 32 + lane % 32;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = wm * (BM / WM) + i * 32 + (r / 4) * 8 + half * 4 + r % 4;
-                const int lr = m0 + row < Mg ? row : live - 1;     // dead rows: any gate
-                const float gt = S.gate ? S.gate[(size_t)rbase + m0 + lr] : 1.0f;
-                const float v = gt * (silu_fast(acc[i][jj][r]) * acc[i][hf + jj][r]);
-                float m = fabsf(v);
-#pragma unroll
-                for (int off = 1; off < 32; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
-                const int X = mx_exponent(m);
-                ep[row * C::kEpStride + lcol] = (uint8_t)e4m3_rne_sat(v * exp2_neg(X));
-                if (lane % 32 == 0) eps[row * kSc + lcol / 32] = (uint8_t)(X + 127);
-            }
+        for (int r = 0; r < 16; ++r) {
+            v[r] = gt * (silu_fast(acc[i][0][r]) * acc[i][hf][r]);
+            m = fmaxf(m, fabsf(v[r]));
         }
-    }
-    __syncthreads();
-    {
-        const int F = N / 2;
-        constexpr int kChunks = BN / 2 / 16;           // 16-byte chunks of act per tile row
-        uint8_t* outq = (uint8_t*)S.out;
-        for (int c = tid; c < live * kChunks; c += C::kThreads) {
-            const int row = c / kChunks, cc = c % kChunks;
-            const uint4 v = *(const uint4*)(ep + row * C::kEpStride + cc * 16);
-            *(uint4*)(outq + ((size_t)rbase + m0 + row) * F + nt * (BN / 2) + cc * 16) = v;
+        m = fmaxf(m, __shfl_xor(m, 32));
+        const int X = mx_exponent(m);
+        const float inv = exp2_neg(X);
+        uint32_t codes[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            codes[q] = e4m3_rne_sat(v[4 * q] * inv) | (e4m3_rne_sat(v[4 * q + 1] * inv) << 8) |
+                       (e4m3_rne_sat(v[4 * q + 2] * inv) << 16) |
+                       (e4m3_rne_sat(v[4 * q + 3] * inv) << 24);
+#pragma unroll
+        for (int qp = 0; qp < 4; qp += 2) {
+            const uint2 w = pair_runs_x2(codes[qp], codes[qp + 1]);
+            const int col = nt * (BN / 2) + wn * 32 + 8 * (qp + half);
+            if (live_row) *(uint2*)(outq + grow * F + col) = w;
         }
-        uint8_t* outs = (uint8_t*)S.out_scales;
-        static_assert(kSc == 4, "one scale word (128 act columns) per tile row");
-        for (int row = tid; row < live; row += C::kThreads)
-            *(uint32_t*)(outs + ((size_t)rbase + m0 + row) * S.so_row + (size_t)nt * S.so_kb) =
-                *(const uint32_t*)(eps + row * kSc);
+        if (live_row && lane < 32)
+            outs[grow * S.so_row + (size_t)nt * S.so_kb + wn] = (uint8_t)(X + 127);
     }
 }
 
