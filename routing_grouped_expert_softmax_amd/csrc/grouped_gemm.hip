@@ -712,6 +712,11 @@ MOE_DEVICE void e4m3_kloop(int nk, const uint8_t* lds, Issue& issue, const int (
 #pragma unroll
     for (int s = 0; s < STAGES - 1; ++s)
         if (s < nk) issue(s, s);
+    // the weight-block scales of K block kt + 1 are loaded during block kt (a scalar load whose
+    // wait would otherwise sit in front of the block's first MFMAs)
+    float sw_next[C::kTN];
+#pragma unroll
+    for (int j = 0; j < C::kTN; ++j) sw_next[j] = NV > 0 ? wsc[wsc_off[j]] : 0.0f;
     int stage = 0;
     for (int kt = 0; kt < nk; ++kt) {
         const int later = nk - 1 - kt;
@@ -732,7 +737,10 @@ MOE_DEVICE void e4m3_kloop(int nk, const uint8_t* lds, Issue& issue, const int (
             const float* sa_l = (const float*)(base + C::kTileBytes);
             float sw[C::kTN];
 #pragma unroll
-            for (int j = 0; j < C::kTN; ++j) sw[j] = wsc[wsc_off[j] + kt];
+            for (int j = 0; j < C::kTN; ++j) {
+                sw[j] = sw_next[j];
+                if (kt + 1 < nk) sw_next[j] = wsc[wsc_off[j] + kt + 1];
+            }
             i32x8_t bv[2][C::kTN];
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2)
@@ -856,7 +864,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_e4m3_kernel(GemmArgs ga) {
         int nb;
         if (KIND == 0) nb = j < C::kTN / 2 ? nt : N / 256 + nt;   // gate block nt, up block F/128 + nt
         else nb = (nt * BN + wn * (BN / WN) + j * 32) / 128;
-        wsc_off[j] = (g * nbn + nb) * KB;
+        wsc_off[j] = __builtin_amdgcn_readfirstlane((g * nbn + nb) * KB);   // wave-uniform
     }
 
     f32x16_t acc[C::kTM][C::kTN];
