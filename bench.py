@@ -461,9 +461,9 @@ def main():
                          "of runs made with --calib-copy-gib, then exit")
     args = ap.parse_args()
     if args.write_traffic:
-        run = ("-- python -u bench.py --workload " + args.workload + " --steps 2 --warmup 1 "
-               f"--no-cpu --no-layer-bwd --calib-copy-gib {args.calib_copy_gib:g}")
-        rx = "--kernel-include-regex 'gemm_bf16|copyBuffer|elementwise'"
+        run = ("-- python3 -u bench.py --workload " + args.workload + " --steps 2 --warmup 1 "
+               f"--no-cpu --no-layer-bwd --no-permute-copy --calib-copy-gib {args.calib_copy_gib:g}")
+        rx = "--kernel-include-regex 'gemm_bf16|copyBuffer|elementwise'"  # one run per counter set
         cmd = (f"export TMPDIR=/tmp; rocprofv3 --pmc FETCH_SIZE {rx} -d <dir> -o f {run}; "
                f"rocprofv3 --pmc WRITE_SIZE TCC_HIT_sum TCC_MISS_sum {rx} -d <dir> -o w {run}; "
                f"python bench.py --write-traffic <dir>/f_results.db <dir>/w_results.db "
