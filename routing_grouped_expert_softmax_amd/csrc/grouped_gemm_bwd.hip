@@ -268,32 +268,36 @@ MOE_DEVICE void bwd_tile(const BwdArgs& ba, int L, uint8_t* lds) {
                 for (int i = 0; i < kTM; ++i)
 #pragma unroll
                     for (int j = 0; j < kTN; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j],
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[j], av[i],
                                                                             acc[i][j], 0, 0, 0);
             }
         }
         if (++stage == kStages) stage = 0;
     }
 
-    // ---- epilogue. 32x32 layout: element r of lane l is row (r/4)*8 + (l/32)*4 + r%4,
-    // column l % 32.
+    // ---- epilogue. The B operand goes first into the MFMA, so element r of lane l of
+    // sub-tile (i, j) is output row wm * BM / WM + 32 i + l % 32 and column
+    // wn * BN / WN + 32 j + 8 (r / 4) + 4 (l / 32) + r % 4: every lane holds runs of four
+    // consecutive columns of one row.
     if (EPI == 0) {
-        // stage the bf16 tile in LDS ([BM][BN + 8]), then write 16-byte row chunks
+        // stage the bf16 tile in LDS ([BM][BN + 8]) with one 8-byte write per run, then write
+        // 16-byte row chunks
         constexpr int kEpStride = kBN + 8;
         block_sync();                               // every wave is done with the stages
         uint16_t* ep = (uint16_t*)lds;
 #pragma unroll
         for (int i = 0; i < kTM; ++i) {
             if (i >= nvi) continue;
+            const int row = wm * (kBM / CF::WM) + i * 32 + lane % 32;
 #pragma unroll
-            for (int j = 0; j < kTN; ++j) {
-                const int lcol = wn * (kBN / CF::WN) + j * 32 + lane % 32;
+            for (int j = 0; j < kTN; ++j)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = wm * (kBM / CF::WM) + i * 32 + (r / 4) * 8 + (lane / 32) * 4 + r % 4;
-                    ep[row * kEpStride + lcol] = f32_to_bf16(acc[i][j][r]);
+                for (int q = 0; q < 4; ++q) {
+                    const int lcol = wn * (kBN / CF::WN) + j * 32 + 8 * q + 4 * (lane / 32);
+                    *(uint2*)(ep + row * kEpStride + lcol) =
+                        make_uint2(pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                                   pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
                 }
-            }
         }
         __syncthreads();
         uint16_t* out = ba.out + (RAGGED_K ? (size_t)g * ba.out_gstride : 0);
@@ -307,47 +311,55 @@ MOE_DEVICE void bwd_tile(const BwdArgs& ba, int L, uint8_t* lds) {
         }
         return;
     }
-    // SwiGLU backward on the dA tile (columns f of this N tile); dg partial per row
+    // SwiGLU backward on the dA tile (columns f of this N tile), four columns of one row per
+    // run: Z_g, Z_u read and dZ_g, dZ_u written 8 bytes at a time; dg partial per row
     const int F = ba.F;
-    float dgp[kTM][16];
+    float dgp[kTM];
 #pragma unroll
-    for (int i = 0; i < kTM; ++i)
+    for (int i = 0; i < kTM; ++i) {
+        dgp[i] = 0.0f;
+        const int row = wm * (kBM / CF::WM) + i * 32 + lane % 32;
+        if (i >= nvi || m0 + row >= Mg) continue;
+        const size_t grow = (size_t)rbase + m0 + row;
+        const float gt = ba.gate ? ba.gate[grow] : 1.0f;
+        const uint16_t* zr = ba.z + grow * 2 * F;
+        uint16_t* dzr = ba.dz + grow * 2 * F;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            dgp[i][r] = 0.0f;
-            const int row = wm * (kBM / CF::WM) + i * 32 + (r / 4) * 8 + (lane / 32) * 4 + r % 4;
-            if (i >= nvi || m0 + row >= Mg) continue;
-            const size_t grow = (size_t)rbase + m0 + row;
-            const float gt = ba.gate ? ba.gate[grow] : 1.0f;
+        for (int j = 0; j < kTN; ++j)
 #pragma unroll
-            for (int j = 0; j < kTN; ++j) {
-                const int f = nt * kBN + wn * (kBN / CF::WN) + j * 32 + lane % 32;
-                const float zg = bf16_to_f32(ba.z[grow * 2 * F + f]);
-                const float zu = bf16_to_f32(ba.z[grow * 2 * F + F + f]);
-                const float sg = 1.0f / (1.0f + expf(-zg));
-                const float si = zg * sg;
-                const float ds = sg * (1.0f + zg * (1.0f - sg));
-                const float da = acc[i][j][r];
-                const float dh = gt * da;
-                ba.dz[grow * 2 * F + f] = f32_to_bf16(dh * zu * ds);
-                ba.dz[grow * 2 * F + F + f] = f32_to_bf16(dh * si);
-                dgp[i][r] += da * (si * zu);
+            for (int q = 0; q < 4; ++q) {
+                const int f = nt * kBN + wn * (kBN / CF::WN) + j * 32 + 8 * q + 4 * (lane / 32);
+                const uint2 zgv = *(const uint2*)(zr + f);
+                const uint2 zuv = *(const uint2*)(zr + F + f);
+                const uint32_t zgw[2] = {zgv.x, zgv.y}, zuw[2] = {zuv.x, zuv.y};
+                float dzg[4], dzu[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float zg = bf16_to_f32((uint16_t)(zgw[e / 2] >> (16 * (e % 2))));
+                    const float zu = bf16_to_f32((uint16_t)(zuw[e / 2] >> (16 * (e % 2))));
+                    const float sg = 1.0f / (1.0f + expf(-zg));
+                    const float si = zg * sg;
+                    const float ds = sg * (1.0f + zg * (1.0f - sg));
+                    const float da = acc[i][j][4 * q + e];
+                    const float dh = gt * da;
+                    dzg[e] = dh * zu * ds;
+                    dzu[e] = dh * si;
+                    dgp[i] += da * (si * zu);
+                }
+                *(uint2*)(dzr + f) = make_uint2(pack_bf16x2(dzg[0], dzg[1]), pack_bf16x2(dzg[2], dzg[3]));
+                *(uint2*)(dzr + F + f) = make_uint2(pack_bf16x2(dzu[0], dzu[1]), pack_bf16x2(dzu[2], dzu[3]));
             }
-        }
-    // rows' partial sums: over the 32 lanes of each half (columns), then over the WN waves
-    // of a row band (LDS), in a fixed order
+    }
+    // rows' partial sums: the lane's own 4 kTN columns, its partner lane l ^ 32 (the row's other
+    // columns of the wave), then the WN waves of a row band (LDS), in a fixed order
     block_sync();
     float* red = (float*)lds;                          // [WN][kBM]
 #pragma unroll
-    for (int i = 0; i < kTM; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float v = dgp[i][r];
-#pragma unroll
-            for (int off = 1; off < 32; off <<= 1) v += __shfl_xor(v, off);
-            const int row = wm * (kBM / CF::WM) + i * 32 + (r / 4) * 8 + (lane / 32) * 4 + r % 4;
-            if (lane % 32 == 0) red[wn * kBM + row] = v;
-        }
+    for (int i = 0; i < kTM; ++i) {
+        const float v = dgp[i] + __shfl_xor(dgp[i], 32);
+        const int row = wm * (kBM / CF::WM) + i * 32 + lane % 32;
+        if (lane < 32) red[wn * kBM + row] = v;
+    }
     __syncthreads();
     if (threadIdx.x < kBM) {
         const int row = threadIdx.x;
