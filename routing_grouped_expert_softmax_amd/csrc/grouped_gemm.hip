@@ -117,6 +117,90 @@ __global__ __launch_bounds__(1024) void schedule_kernel(SchedArgs sa, int bm,
     }
 }
 
+// Mixed tile shapes for the bf16 kernel. A group of n rows takes n / 256 full 256-row M tiles
+// (256 x 256 output tiles) and, for a remainder r = n % 256: one more 256-row tile if r > 128,
+// else one 128-row tile on the 128 x 512 shape, whose 128 x 512 outputs cost about as much as
+// a 256 x 256 tile. (A 300-row expert then costs 1 + 1/2 tile rows instead of 2.) The unit
+// table lists every output tile in launch order: per group, bands of up to `mgroup` 256-row
+// M tiles; within a band, for each 512-column block c, the band's tiles at N tiles 2c and
+// 2c + 1, then the group's 128-row tile at block c (with the group's last band), so the tiles
+// that read the same weight rows get neighbouring ids. ntn0 = N / 256 (even).
+__global__ __launch_bounds__(1024) void schedule_mixed_kernel(SchedArgs sa, int ntn0, int mgroup,
+                                                              int4* __restrict__ units,
+                                                              int* __restrict__ unit_nt,
+                                                              int* __restrict__ total) {
+    __shared__ int wsum[16];
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int ntn1 = ntn0 / 2;
+    int nslot = 0;
+    for (int s = 0; s < sa.nseg; ++s) nslot += sa.groups[s];
+    int seg_of[2], grp_of[2], n_of[2], base_of[2], cnt_of[2];
+    int mine = 0;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int slot = 2 * tid + q;
+        seg_of[q] = -1;
+        cnt_of[q] = 0;
+        if (slot < nslot) {
+            int s = 0, g = slot;
+            if (g >= sa.groups[0]) { s = 1; g -= sa.groups[0]; }
+            int base, n;
+            if (sa.offsets[s]) {
+                base = sa.offsets[s][g];
+                n = sa.offsets[s][g + 1] - base;
+            } else {
+                base = 0;
+                n = sa.rows[s];
+            }
+            const int rem = n % 256;
+            const int n256 = n / 256 + (rem > 128 ? 1 : 0);
+            const int has128 = rem > 0 && rem <= 128 ? 1 : 0;
+            seg_of[q] = s; grp_of[q] = g; n_of[q] = n; base_of[q] = base;
+            cnt_of[q] = n256 * ntn0 + has128 * ntn1;
+        }
+        mine += cnt_of[q];
+    }
+    int v = mine;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int o = __shfl_up(v, off);
+        if (lane >= off) v += o;
+    }
+    if (lane == kWave - 1) wsum[wave] = v;
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += wsum[w];
+    int p = before + v - mine;
+    if (tid == blockDim.x - 1) *total = before + v;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        if (cnt_of[q] == 0) continue;
+        const int n = n_of[q], rem = n % 256;
+        const int n256 = n / 256 + (rem > 128 ? 1 : 0);
+        const int has128 = rem > 0 && rem <= 128;
+        const int x = (seg_of[q] << 20) | grp_of[q];
+        for (int b0 = 0; b0 < n256 || (b0 == 0 && has128); b0 += mgroup) {
+            const int b1 = b0 + mgroup < n256 ? b0 + mgroup : n256;
+            const bool last = b1 == n256;
+            for (int c = 0; c < ntn1; ++c) {
+                for (int h = 0; h < 2; ++h)
+                    for (int m = b0; m < b1; ++m) {
+                        const int m0 = m * 256, m1 = m0 + 256 < n ? m0 + 256 : n;
+                        units[p] = make_int4(x, m0, m1, base_of[q]);
+                        unit_nt[p] = 2 * c + h;
+                        ++p;
+                    }
+                if (last && has128) {
+                    units[p] = make_int4(x | (1 << 21), n / 256 * 256, n, base_of[q]);
+                    unit_nt[p] = c;
+                    ++p;
+                }
+            }
+            if (last) break;
+        }
+    }
+}
+
 struct GemmArgs {
     SegDev seg[2];
     const int4* tiles;
@@ -126,6 +210,9 @@ struct GemmArgs {
     int per_xcd_max;   // launched blocks / 8
     int bm;            // M tile rows
     int mgroup;        // M tiles of one group visited together per N tile
+    // mixed bf16 schedule (schedule_mixed_kernel): one entry per output tile, in launch order
+    const int4* units; // {seg << 20 | shape << 21 | group, first row, end row, global row base}
+    const int* unit_nt;// the tile's N tile (of its shape's N tiling)
 };
 
 // Map this workgroup to a live tile; false when there is none.
@@ -182,6 +269,10 @@ MOE_DEVICE bool pick_tile(const GemmArgs& ga, int& mt, int& nt) {
 #ifndef MOE_BF_PINGPONG
 #define MOE_BF_PINGPONG 1
 #endif
+// Interleaved K loop (bf16_kloop_il) for configurations the ping-pong loop does not take
+#ifndef MOE_BF_KLOOP_IL
+#define MOE_BF_KLOOP_IL 1
+#endif
 
 
 template <int KIND, int BM, int BN, int BK, int WM, int WN, int SA, int SB>
@@ -201,6 +292,7 @@ struct BfCfg {
     static constexpr int kSub = BK / 16;                    // MFMA K steps per stage
     static constexpr int kSlices = kRowBytes / 64;          // 64-byte K slices per stage
     static constexpr int kSA = SA, kSB = SB;
+    static constexpr int kBM = BM, kBN = BN, kBK = BK, kWM = WM, kWN = WN;
     // Row order of the waves' 32-row sub-tiles: interleaved (sub-tile i of wave row wm at
     // rows (i * WM + wm) * 32), so a ragged tile's live rows spread over all the waves, or
     // blocked (wm * BM / WM + i * 32).
@@ -214,8 +306,10 @@ struct BfCfg {
     static constexpr size_t kLdsEp = (size_t)BM * kEpStride * 2;
     // GEMM1: the tile's row gates, staged at tile start past the ring and the epilogue
     // staging (one 4-byte word per tile row)
+    // (when that would not fit, the epilogue reads them from global memory instead)
     static constexpr size_t kGateOff = ((kLdsLoop > kLdsEp ? kLdsLoop : kLdsEp) + 15) / 16 * 16;
-    static constexpr size_t kLds = kGateOff + (KIND == 0 ? (size_t)BM * 4 : 0);
+    static constexpr bool kGateLds = KIND == 0 && kGateOff + (size_t)BM * 4 <= 160 * 1024;
+    static constexpr size_t kLds = kGateLds ? kGateOff + (size_t)BM * 4 : kGateOff;
     static_assert(BK == 32 || BK == 64, "BK");
     static_assert(kDmaA * kRowsPerDma * kWaves == BM && kDmaB * kRowsPerDma * kWaves == BN,
                   "DMA split");
@@ -414,15 +508,89 @@ MOE_DEVICE void bf16_kloop_pp(int nst, const uint8_t* lds, const uint8_t* const 
     wait_vm_lgkm0<0>();
 }
 
+// Interleaved K loop, for tiles whose A and B slots differ in size (the 128 x 512 shape):
+// K step 32 (two MFMA sub-steps), S >= 3 ring slots, one barrier per K step placed between
+// the step's two sub-steps:
+//   phase A: LDS reads of sub-step 1 of step kt, interleaved with the MFMAs of sub-step 0;
+//   wait for this wave's DMAs of step kt + 1 and for its LDS reads, then the barrier (step
+//   kt + 1 is visible, and every wave is done reading slot kt % S);
+//   phase B: the DMAs of step kt + S into slot kt % S and the reads of sub-step 0 of step
+//   kt + 1, interleaved with the MFMAs of sub-step 1.
+// A DMA has S - 1 steps to land. Past the last step the DMAs re-load the last step into the
+// free slot, and the reads of the step after the last read a slot that holds a landed copy
+// (no branch in the loop, so the scheduler can interleave; those values are never used).
+template <class C, int NV, class IssueA, class IssueB>
+MOE_DEVICE void bf16_kloop_il(int nk, const uint8_t* lds, IssueA& issue_a, IssueB& issue_b,
+                              const int (&a_off)[C::kTM], const int (&b_off)[C::kTN],
+                              const int (&chunk_off)[C::kSub],
+                              f32x16_t (&acc)[C::kTM][C::kTN]) {
+    constexpr int S = C::kSA;
+    constexpr int Q = C::kDmaA + C::kDmaB;               // DMAs per wave per step
+    static_assert(C::kSA == C::kSB && S >= 3 && C::kSub == 2 && (S - 1) * Q < 64,
+                  "interleaved loop");
+    constexpr int NVv = NV > 0 ? NV : 1;
+    constexpr int kMfma = NVv * C::kTN, kReads = NVv + C::kTN;
+    bf16x8_t av[2][NVv], bv[2][C::kTN];
+    auto read = [&](int st, int u) {
+        if (NV == 0) return;
+        const uint8_t* ca = lds + (st % S) * C::kASlot;
+        const uint8_t* cb = lds + C::kBRing + (st % S) * C::kBSlot;
+#pragma unroll
+        for (int j = 0; j < C::kTN; ++j) bv[u][j] = *(const bf16x8_t*)(cb + b_off[j] + chunk_off[u]);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) av[u][i] = *(const bf16x8_t*)(ca + a_off[i] + chunk_off[u]);
+    };
+    auto mma = [&](int u) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+#pragma unroll
+            for (int j = 0; j < C::kTN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[u][j], av[u][i], acc[i][j],
+                                                                    0, 0, 0);
+    };
+    auto issue = [&](int st) {
+        const int t = st < nk ? st : nk - 1;
+        issue_a(t, st % S);
+        issue_b(t, st % S);
+    };
+#pragma unroll
+    for (int st = 0; st < S; ++st) issue(st);
+    wait_vm_lgkm0<(S - 1) * Q>();                        // step 0 landed
+    block_sync();
+    read(0, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+        read(kt, 1);                                     // phase A
+        mma(0);
+        if (NV > 0) {
+#pragma unroll
+            for (int x = 0; x < kMfma; ++x) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (x < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+        }
+        wait_vm_lgkm0<(S - 2) * Q>();                    // step kt + 1 landed, reads done
+        block_sync();
+        issue(kt + S);                                   // phase B
+        read(kt + 1, 0);
+        mma(1);
+        if (NV > 0) {
+#pragma unroll
+            for (int x = 0; x < kMfma; ++x) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (x < Q) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                if (x < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+        }
+    }
+    wait_vm_lgkm0<0>();
+}
+
+// One output tile of the bf16 kernel: rows [m0, Mg) of group g of segment seg (the group's
+// rows start at global row rbase), N tile nt.
 template <int KIND, int BM, int BN, int BK, int WM, int WN, int SA, int SB>
-__global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs ga) {
+MOE_DEVICE void bf16_tile(const GemmArgs& ga, int seg, int g, int m0, int Mg, int rbase, int nt,
+                          uint8_t* lds) {
     using C = BfCfg<KIND, BM, BN, BK, WM, WN, SA, SB>;
-    extern __shared__ __align__(16) uint8_t lds[];
-    int mt, nt;
-    if (!pick_tile(ga, mt, nt)) return;
-    const int4 ti = ga.tiles[mt];
-    const int seg = ti.x >> 20, g = ti.x & 0xFFFFF;
-    const int m0 = ti.y, Mg = tile_end(ti.y, ti.z, ga.bm), rbase = ti.w;   // Mg: tile end
     const SegDev S = seg == 0 ? ga.seg[0] : ga.seg[1];
     const int N = ga.N, K = ga.K;
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
@@ -511,7 +679,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs ga) {
     // GEMM1: the gates of the tile's live rows into LDS (read by the epilogue, after the
     // K loop's barriers), loaded while the first operand tiles are in flight
     float* gate_lds = (float*)(lds + C::kGateOff);
-    if (KIND == 0 && tid < live) gate_lds[tid] = S.gate ? S.gate[rbase + m0 + tid] : 1.0f;
+    if (C::kGateLds && tid < live) gate_lds[tid] = S.gate ? S.gate[rbase + m0 + tid] : 1.0f;
 
     // one branch-free K loop per count of live sub-tiles (every variant has the same
     // barriers, so waves of one block may take different variants)
@@ -519,6 +687,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs ga) {
     // ping-pong: one group of four waves fills the A slots, the other the B slots
     constexpr bool kPP = MOE_BF_PINGPONG && BM == 256 && BN == 256 && BK == 32 && SA == SB &&
                          SA >= 3 && WM * WN == 8;
+    constexpr bool kIL = !kPP && BK == 32 && SA == SB && SA >= 3 && MOE_BF_KLOOP_IL;
     // wave-uniform (scalar) so the group's extra barrier is a scalar branch: s_barrier does
     // not look at the exec mask
     const int grp = __builtin_amdgcn_readfirstlane(wave / 4);
@@ -554,6 +723,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs ga) {
             if constexpr (kPP)                                                              \
                 bf16_kloop_pp<C, NV>(nk, lds, src, pp_step, grp, gw, a_off, b_off,          \
                                      chunk_off, acc);                                       \
+            else if constexpr (kIL)                                                         \
+                bf16_kloop_il<C, NV>(nk, lds, issue_a, issue_b, a_off, b_off, chunk_off,    \
+                                     acc);                                                  \
             else                                                                            \
                 bf16_kloop<C, NV, true>(nk, lds, issue_a, issue_b, a_off, b_off, chunk_off,  \
                                         acc);                                               \
@@ -590,7 +762,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs ga) {
             const bool live_row = m0 + row < Mg;       // lanes l and l + 32 share a row
             const int lr = live_row ? row : live - 1;
             const size_t grow = (size_t)rbase + m0 + lr;
-            const float gt = gate_lds[lr];
+            const float gt = C::kGateLds ? gate_lds[lr] : S.gate ? S.gate[grow] : 1.0f;
 #pragma unroll
             for (int jj = 0; jj < half; ++jj)
 #pragma unroll
@@ -654,6 +826,42 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs ga) {
             *(uint4*)(out + ((size_t)rbase + m0 + row) * N + c0 + cc * 8) = v;
         }
     }
+}
+
+// One 256 x 256 (or other single-shape) tile per workgroup, from the M-tile schedule.
+template <int KIND, int BM, int BN, int BK, int WM, int WN, int SA, int SB>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs ga) {
+    extern __shared__ __align__(16) uint8_t lds[];
+    int mt, nt;
+    if (!pick_tile(ga, mt, nt)) return;
+    const int4 ti = ga.tiles[mt];
+    bf16_tile<KIND, BM, BN, BK, WM, WN, SA, SB>(ga, ti.x >> 20, ti.x & 0xFFFFF, ti.y,
+                                                tile_end(ti.y, ti.z, ga.bm), ti.w, nt, lds);
+}
+
+// Mixed shapes (schedule_mixed_kernel): workgroup b takes unit (b % 8) * per + b / 8, so
+// each XCD walks one contiguous run of the unit table; shape 0 runs the 256 x 256
+// configuration, shape 1 the 128 x 512 one.
+template <int KIND, class C0, class C1>
+__global__ __launch_bounds__(512) void gemm_bf16_mixed_kernel(GemmArgs ga) {
+    static_assert(C0::kThreads == 512 && C1::kThreads == 512, "8 waves");
+    extern __shared__ __align__(16) uint8_t lds[];
+    const int b = blockIdx.x;
+    const int xcd = b % 8, i = b / 8;
+    const int total = *ga.total;
+    const int per = (total + 7) / 8;
+    if (i >= per) return;
+    const int L = xcd * per + i;
+    if (L >= total) return;
+    const int4 u = ga.units[L];
+    const int nt = ga.unit_nt[L];
+    const int seg = (u.x >> 20) & 1, g = u.x & 0xFFFFF;
+    if ((u.x >> 21) == 0)
+        bf16_tile<KIND, C0::kBM, C0::kBN, C0::kBK, C0::kWM, C0::kWN, C0::kSA, C0::kSB>(
+            ga, seg, g, u.y, u.z, u.w, nt, lds);
+    else
+        bf16_tile<KIND, C1::kBM, C1::kBN, C1::kBK, C1::kWM, C1::kWN, C1::kSA, C1::kSB>(
+            ga, seg, g, u.y, u.z, u.w, nt, lds);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1403,6 +1611,32 @@ hipError_t run_bf16(const GemmArgs& ga, int nblocks, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Mixed shapes (schedule_mixed_kernel): the 256 x 256 configuration above plus this 128 x 512
+// one for a group's last <= 128 rows, when N is a multiple of 512
+#ifndef MOE_BF_MIXED
+#define MOE_BF_MIXED 1
+#endif
+#ifndef MOE_BF_UP_CFG128
+#define MOE_BF_UP_CFG128 128, 512, 32, 2, 4, 3, 3
+#endif
+#ifndef MOE_BF_DOWN_CFG128
+#define MOE_BF_DOWN_CFG128 128, 512, 32, 2, 4, 3, 3
+#endif
+
+template <int KIND, class C0, class C1>
+hipError_t run_bf16_mixed(const GemmArgs& ga, int nblocks, hipStream_t s) {
+    constexpr size_t kLds = C0::kLds > C1::kLds ? C0::kLds : C1::kLds;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_mixed_kernel<KIND, C0, C1>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    gemm_bf16_mixed_kernel<KIND, C0, C1><<<nblocks, 512, kLds, s>>>(ga);
+    return hipGetLastError();
+}
+
 template <int BM, int BN, int BK, int WM, int WN, int SA, int SB>
 constexpr int cfg_bm() { return BM; }
 template <int BM, int BN, int BK, int WM, int WN, int SA, int SB>
@@ -1655,12 +1889,27 @@ size_t schedule_ws_bytes(int max_rows, int groups, int bm) {
     return 256 + max_mtiles(max_rows, groups, bm) * sizeof(int4);
 }
 
+// The mixed bf16 schedule applies when both configurations fit N: 256 x 256 tiles as the
+// single-shape configuration, and N a multiple of 512.
+bool bf16_mixed(int kind, int dtype, int N) {
+    return MOE_BF_MIXED && dtype == 1 && bm_for(kind, dtype) == 256 &&
+           bn_for(kind, dtype) == 256 && N % 512 == 0;
+}
+
+// mixed schedule: at most max_mtiles 256-row M tiles of N / 256 units each (a 128-row tile
+// has half as many units); the unit table follows the 256-byte header, then the N tiles
+size_t mixed_units(int max_rows_total, int groups_total, int N) {
+    return max_mtiles(max_rows_total, groups_total, 256) * (size_t)(N / 256);
+}
+
 GemmPlan grouped_gemm_plan(int kind, int dtype, int max_rows_total, int groups_total, int N,
                            int K) {
-    (void)kind; (void)N; (void)K;
+    (void)K;
     GemmPlan p;
     p.bm = bm_for(kind, dtype);
     p.ws_bytes = 256 + max_mtiles(max_rows_total, groups_total, p.bm) * sizeof(int4);
+    if (bf16_mixed(kind, dtype, N))
+        p.ws_bytes = 256 + mixed_units(max_rows_total, groups_total, N) * (sizeof(int4) + sizeof(int));
     return p;
 }
 
@@ -1706,6 +1955,27 @@ hipError_t launch_grouped_gemm(int kind, int dtype, const Segment* segs, int nse
     sa.nseg = nseg;
     int* total = (int*)ws;
     int4* tiles = (int4*)((char*)ws + 256);
+    if (bf16_mixed(kind, dtype, N)) {
+        const size_t nunits = mixed_units(max_rows_total, groups_total, N);
+        int* unit_nt = (int*)((char*)ws + 256 + nunits * sizeof(int4));
+        schedule_mixed_kernel<<<1, 1024, 0, s>>>(sa, N / 256, MOE_TILE_MGROUP, tiles, unit_nt,
+                                                 total);
+        ga.units = tiles;
+        ga.unit_nt = unit_nt;
+        ga.total = total;
+        ga.N = N;
+        ga.K = K;
+        ga.ntn = N / bn;
+        ga.bm = bm;
+        ga.mgroup = MOE_TILE_MGROUP;
+        const int nblocks = (int)((nunits + 7) / 8 * 8);
+        ga.per_xcd_max = nblocks / 8;
+        if (kind == 0)
+            return run_bf16_mixed<0, BfCfg<0, MOE_BF_UP_CFG>, BfCfg<0, MOE_BF_UP_CFG128>>(
+                ga, nblocks, s);
+        return run_bf16_mixed<1, BfCfg<1, MOE_BF_DOWN_CFG>, BfCfg<1, MOE_BF_DOWN_CFG128>>(
+            ga, nblocks, s);
+    }
     schedule_kernel<<<1, 1024, 0, s>>>(sa, bm, tiles, total);
     ga.tiles = tiles;
     ga.total = total;

@@ -18,6 +18,8 @@ CASES = {
     "dsv3_small": mi.scaled(mi.CONFIGS["dsv3_bf16"], T=300, H=256, F=128, shared_F=128),
     # softmax top-8 of 16
     "qwen3_small": mi.scaled(mi.CONFIGS["qwen3_bf16"], T=257, H=256, F=128, E=16),
+    # N a multiple of 512 in both GEMMs: the bf16 kernels' mixed 256 / 128-row tile schedule
+    "qwen3_mixed_tiles": mi.scaled(mi.CONFIGS["qwen3_bf16"], T=700, H=512, F=256, E=16),
 }
 
 

@@ -1,9 +1,12 @@
-"""Ragged M tiles of the grouped GEMMs at the row counts where dealing an expert's rows evenly
-over its tiles moves the tile boundaries: one row past a tile (257, 513, 2049 rows), counts
-between tile multiples (300, 767), exact multiples (256, 512 - 1, 32), tiny and empty experts.
+"""Ragged M tiles of the grouped GEMMs at the row counts where the tile boundaries move: one
+row past a tile (257, 513, 2049 rows), counts between tile multiples (300, 767), exact
+multiples (256, 512 - 1, 32), tiny and empty experts, and remainders around 128 rows past a
+multiple of 256 (128, 129, 384, 385, 640, 100), where the bf16 kernels switch between a last
+256-row tile and a last 128-row tile on the 128 x 512 shape (the shape is used when N is a
+multiple of 512: the H512F256 case takes it in both GEMMs, F256 in the up GEMM only).
 The expert-grouped offsets are set directly (one slot per token, k = 1), every output row is
 compared with the oracle's expert math, and the backward's data gradients and gate gradients
-use the same offsets (its tiles come from the same schedule)."""
+use the same offsets."""
 import numpy as np
 import pytest
 import torch
@@ -14,8 +17,10 @@ from helpers import rel_err, tol
 
 pytestmark = pytest.mark.gpu
 
-COUNTS = np.array([257, 300, 0, 513, 33, 1, 2049, 32, 511, 767, 256, 255], np.int64)
-SHAPES = {"F128": dict(H=256, F=128), "F256": dict(H=256, F=256)}
+COUNTS = np.array([257, 300, 0, 513, 33, 1, 2049, 32, 511, 767, 256, 255, 128, 129, 384, 385,
+                   640, 100], np.int64)
+SHAPES = {"F128": dict(H=256, F=128), "F256": dict(H=256, F=256),
+          "H512F256": dict(H=512, F=256)}
 
 
 @pytest.fixture(scope="module")
