@@ -138,7 +138,8 @@ def write_traffic(fetch_db, write_db, copy_gib, workload, cmd):
         rows = c.execute("select kernel_name, dispatch_id, sum(value) from counters_collection "
                          "where counter_name = ? group by dispatch_id", (counter,)).fetchall()
         copy = max(v for kn, _, v in rows if "copyBuffer" in kn)
-        up = [v for kn, _, v in rows if "gemm_bf16_kernel<0," in kn]
+        up = [v for kn, _, v in rows
+              if "gemm_bf16_kernel<0," in kn or "gemm_bf16_mixed_kernel<0," in kn]
         return copy, sum(up) / len(up), len(up)
 
     nbytes = copy_gib * (1 << 30)
@@ -146,7 +147,7 @@ def write_traffic(fetch_db, write_db, copy_gib, workload, cmd):
     wc, wu, nw = per_dispatch(write_db, "WRITE_SIZE")
     ff, fw = nbytes / (fc * 1024), nbytes / (wc * 1024)
     lines = [
-        "# HBM traffic of one launch of the grouped GEMM up (gemm_bf16_kernel<0, ...>)",
+        "# HBM traffic of one launch of the grouped GEMM up (gemm_bf16_mixed_kernel<0, ...>)",
         "# counters: rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE (KiB per dispatch), each",
         "# scaled by the factor that maps the same counter onto a plain device copy of known",
         "# size issued in the same run (bytes copied / counter bytes)",

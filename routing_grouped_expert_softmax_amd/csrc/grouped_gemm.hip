@@ -124,22 +124,24 @@ __global__ __launch_bounds__(1024) void schedule_kernel(SchedArgs sa, int bm,
 // table lists every output tile in launch order: per group, bands of up to `mgroup` 256-row
 // M tiles; within a band, for each 512-column block c, the band's tiles at N tiles 2c and
 // 2c + 1, then the group's 128-row tile at block c (with the group's last band), so the tiles
-// that read the same weight rows get neighbouring ids. ntn0 = N / 256 (even).
+// that read the same weight rows get neighbouring ids. ntn0 = N / 256 (even). Every block
+// of the grid computes the per-group prefix and writes its share of the units.
 __global__ __launch_bounds__(1024) void schedule_mixed_kernel(SchedArgs sa, int ntn0, int mgroup,
                                                               int4* __restrict__ units,
                                                               int* __restrict__ unit_nt,
                                                               int* __restrict__ total) {
+    constexpr int kSlots = 2048;                       // two group slots per thread
     __shared__ int wsum[16];
+    __shared__ int s_start[kSlots + 1], s_n[kSlots], s_base[kSlots], s_x[kSlots];
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int ntn1 = ntn0 / 2;
     int nslot = 0;
     for (int s = 0; s < sa.nseg; ++s) nslot += sa.groups[s];
-    int seg_of[2], grp_of[2], n_of[2], base_of[2], cnt_of[2];
+    int cnt_of[2];
     int mine = 0;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
         const int slot = 2 * tid + q;
-        seg_of[q] = -1;
         cnt_of[q] = 0;
         if (slot < nslot) {
             int s = 0, g = slot;
@@ -155,8 +157,10 @@ __global__ __launch_bounds__(1024) void schedule_mixed_kernel(SchedArgs sa, int 
             const int rem = n % 256;
             const int n256 = n / 256 + (rem > 128 ? 1 : 0);
             const int has128 = rem > 0 && rem <= 128 ? 1 : 0;
-            seg_of[q] = s; grp_of[q] = g; n_of[q] = n; base_of[q] = base;
             cnt_of[q] = n256 * ntn0 + has128 * ntn1;
+            s_n[slot] = n;
+            s_base[slot] = base;
+            s_x[slot] = (s << 20) | g;
         }
         mine += cnt_of[q];
     }
@@ -170,33 +174,53 @@ __global__ __launch_bounds__(1024) void schedule_mixed_kernel(SchedArgs sa, int 
     __syncthreads();
     int before = 0;
     for (int w = 0; w < wave; ++w) before += wsum[w];
-    int p = before + v - mine;
-    if (tid == blockDim.x - 1) *total = before + v;
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        if (cnt_of[q] == 0) continue;
-        const int n = n_of[q], rem = n % 256;
+    const int p0 = before + v - mine;
+    if (2 * tid < nslot) s_start[2 * tid] = p0;
+    if (2 * tid + 1 < nslot) s_start[2 * tid + 1] = p0 + cnt_of[0];
+    int all = 0;
+    for (int w = 0; w < 16; ++w) all += wsum[w];
+    if (tid == 0) {
+        s_start[nslot] = all;
+        if (blockIdx.x == 0) *total = all;
+    }
+    __syncthreads();
+    // every unit in parallel over the grid's blocks (each block repeats the scan above): its
+    // slot (the last slot whose start <= u), then its position in the slot's launch order
+    const int uf = ntn1 * 2 * mgroup;                  // units of a full band
+    for (int u = blockIdx.x * blockDim.x + tid; u < all; u += gridDim.x * blockDim.x) {
+        int lo = 0, hi = nslot;                        // first slot with start > u, in (lo, hi]
+        while (lo < hi) {
+            const int mid = (lo + hi) / 2;
+            if (s_start[mid] <= u) lo = mid + 1;
+            else hi = mid;
+        }
+        const int slot = lo - 1;
+        const int n = s_n[slot], rem = n % 256;
         const int n256 = n / 256 + (rem > 128 ? 1 : 0);
-        const int has128 = rem > 0 && rem <= 128;
-        const int x = (seg_of[q] << 20) | grp_of[q];
-        for (int b0 = 0; b0 < n256 || (b0 == 0 && has128); b0 += mgroup) {
-            const int b1 = b0 + mgroup < n256 ? b0 + mgroup : n256;
-            const bool last = b1 == n256;
-            for (int c = 0; c < ntn1; ++c) {
-                for (int h = 0; h < 2; ++h)
-                    for (int m = b0; m < b1; ++m) {
-                        const int m0 = m * 256, m1 = m0 + 256 < n ? m0 + 256 : n;
-                        units[p] = make_int4(x, m0, m1, base_of[q]);
-                        unit_nt[p] = 2 * c + h;
-                        ++p;
-                    }
-                if (last && has128) {
-                    units[p] = make_int4(x | (1 << 21), n / 256 * 256, n, base_of[q]);
-                    unit_nt[p] = c;
-                    ++p;
-                }
-            }
-            if (last) break;
+        const int has128 = rem > 0 && rem <= 128 ? 1 : 0;
+        const int nbands = n256 > 0 ? (n256 + mgroup - 1) / mgroup : 1;
+        int li = u - s_start[slot], b, nb, extra;
+        if (li < (nbands - 1) * uf) {
+            b = li / uf;
+            li -= b * uf;
+            nb = mgroup;
+            extra = 0;
+        } else {
+            b = nbands - 1;
+            li -= b * uf;
+            nb = n256 - b * mgroup;
+            extra = has128;
+        }
+        const int stride = 2 * nb + extra;
+        const int c = li / stride, q = li % stride;
+        if (q < 2 * nb) {
+            const int m = b * mgroup + q % nb;
+            const int m0 = m * 256, m1 = m0 + 256 < n ? m0 + 256 : n;
+            units[u] = make_int4(s_x[slot], m0, m1, s_base[slot]);
+            unit_nt[u] = 2 * c + q / nb;
+        } else {
+            units[u] = make_int4(s_x[slot] | (1 << 21), n / 256 * 256, n, s_base[slot]);
+            unit_nt[u] = c;
         }
     }
 }
@@ -1958,8 +1982,8 @@ hipError_t launch_grouped_gemm(int kind, int dtype, const Segment* segs, int nse
     if (bf16_mixed(kind, dtype, N)) {
         const size_t nunits = mixed_units(max_rows_total, groups_total, N);
         int* unit_nt = (int*)((char*)ws + 256 + nunits * sizeof(int4));
-        schedule_mixed_kernel<<<1, 1024, 0, s>>>(sa, N / 256, MOE_TILE_MGROUP, tiles, unit_nt,
-                                                 total);
+        schedule_mixed_kernel<<<16, 1024, 0, s>>>(sa, N / 256, MOE_TILE_MGROUP, tiles, unit_nt,
+                                                  total);
         ga.units = tiles;
         ga.unit_nt = unit_nt;
         ga.total = total;
