@@ -119,14 +119,15 @@ __global__ __launch_bounds__(1024) void schedule_kernel(SchedArgs sa, int bm,
 
 // Mixed tile shapes for the bf16 kernel. A group of n rows takes n / 256 full 256-row M tiles
 // (256 x 256 output tiles) and, for a remainder r = n % 256: one more 256-row tile if r > 128,
-// else one 128-row tile on the 128 x 512 shape, whose 128 x 512 outputs cost about as much as
-// a 256 x 256 tile. (A 300-row expert then costs 1 + 1/2 tile rows instead of 2.) The unit
-// table lists every output tile in launch order: per group, bands of up to `mgroup` 256-row
-// M tiles; within a band, for each 512-column block c, the band's tiles at N tiles 2c and
-// 2c + 1, then the group's 128-row tile at block c (with the group's last band), so the tiles
-// that read the same weight rows get neighbouring ids. ntn0 = N / 256 (even). Every block
-// of the grid computes the per-group prefix and writes its share of the units.
-__global__ __launch_bounds__(1024) void schedule_mixed_kernel(SchedArgs sa, int ntn0, int mgroup,
+// else one 128-row tile on the 128 x (256 w1) shape (w1 = 1 or 2). The unit table lists every
+// output tile in launch order: per group, bands of up to `mgroup` 256-row M tiles; within a
+// band, for each column block c of 256 w1 columns, the band's tiles at the N tiles
+// w1 c .. w1 c + w1 - 1, then the group's 128-row tile at block c (with the group's last
+// band), so the tiles that read the same weight rows get neighbouring ids.
+// ntn0 = N / 256 (a multiple of w1). Every block of the grid computes the per-group prefix and
+// writes its share of the units.
+__global__ __launch_bounds__(1024) void schedule_mixed_kernel(SchedArgs sa, int ntn0, int w1,
+                                                              int mgroup,
                                                               int4* __restrict__ units,
                                                               int* __restrict__ unit_nt,
                                                               int* __restrict__ total) {
@@ -134,7 +135,7 @@ __global__ __launch_bounds__(1024) void schedule_mixed_kernel(SchedArgs sa, int 
     __shared__ int wsum[16];
     __shared__ int s_start[kSlots + 1], s_n[kSlots], s_base[kSlots], s_x[kSlots];
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-    const int ntn1 = ntn0 / 2;
+    const int ntn1 = ntn0 / w1;                        // 128-row tiles' N tiles
     int nslot = 0;
     for (int s = 0; s < sa.nseg; ++s) nslot += sa.groups[s];
     int cnt_of[2];
@@ -186,7 +187,7 @@ __global__ __launch_bounds__(1024) void schedule_mixed_kernel(SchedArgs sa, int 
     __syncthreads();
     // every unit in parallel over the grid's blocks (each block repeats the scan above): its
     // slot (the last slot whose start <= u), then its position in the slot's launch order
-    const int uf = ntn1 * 2 * mgroup;                  // units of a full band
+    const int uf = ntn0 * mgroup;                      // units of a full band
     for (int u = blockIdx.x * blockDim.x + tid; u < all; u += gridDim.x * blockDim.x) {
         int lo = 0, hi = nslot;                        // first slot with start > u, in (lo, hi]
         while (lo < hi) {
@@ -211,13 +212,13 @@ __global__ __launch_bounds__(1024) void schedule_mixed_kernel(SchedArgs sa, int 
             nb = n256 - b * mgroup;
             extra = has128;
         }
-        const int stride = 2 * nb + extra;
+        const int stride = w1 * nb + extra;
         const int c = li / stride, q = li % stride;
-        if (q < 2 * nb) {
+        if (q < w1 * nb) {
             const int m = b * mgroup + q % nb;
             const int m0 = m * 256, m1 = m0 + 256 < n ? m0 + 256 : n;
             units[u] = make_int4(s_x[slot], m0, m1, s_base[slot]);
-            unit_nt[u] = 2 * c + q / nb;
+            unit_nt[u] = w1 * c + q / nb;
         } else {
             units[u] = make_int4(s_x[slot] | (1 << 21), n / 256 * 256, n, s_base[slot]);
             unit_nt[u] = c;
@@ -1635,8 +1636,8 @@ hipError_t run_bf16(const GemmArgs& ga, int nblocks, hipStream_t s) {
     return hipGetLastError();
 }
 
-// Mixed shapes (schedule_mixed_kernel): the 256 x 256 configuration above plus this 128 x 512
-// one for a group's last <= 128 rows, when N is a multiple of 512
+// Mixed shapes (schedule_mixed_kernel): the 256 x 256 configuration above plus this 128-row one
+// (128 x 256 or 128 x 512) for a group's last <= 128 rows, when N is a multiple of its width
 #ifndef MOE_BF_MIXED
 #define MOE_BF_MIXED 1
 #endif
@@ -1915,9 +1916,13 @@ size_t schedule_ws_bytes(int max_rows, int groups, int bm) {
 
 // The mixed bf16 schedule applies when both configurations fit N: 256 x 256 tiles as the
 // single-shape configuration, and N a multiple of 512.
+template <int BM, int BN, int BK, int WM, int WN, int SA, int SB>
+constexpr int cfg_w1() { return BN / 256; }
+int bf16_w1(int kind) { return kind == 0 ? cfg_w1<MOE_BF_UP_CFG128>() : cfg_w1<MOE_BF_DOWN_CFG128>(); }
+
 bool bf16_mixed(int kind, int dtype, int N) {
     return MOE_BF_MIXED && dtype == 1 && bm_for(kind, dtype) == 256 &&
-           bn_for(kind, dtype) == 256 && N % 512 == 0;
+           bn_for(kind, dtype) == 256 && N % (256 * bf16_w1(kind)) == 0;
 }
 
 // mixed schedule: at most max_mtiles 256-row M tiles of N / 256 units each (a 128-row tile
@@ -1982,8 +1987,8 @@ hipError_t launch_grouped_gemm(int kind, int dtype, const Segment* segs, int nse
     if (bf16_mixed(kind, dtype, N)) {
         const size_t nunits = mixed_units(max_rows_total, groups_total, N);
         int* unit_nt = (int*)((char*)ws + 256 + nunits * sizeof(int4));
-        schedule_mixed_kernel<<<16, 1024, 0, s>>>(sa, N / 256, MOE_TILE_MGROUP, tiles, unit_nt,
-                                                  total);
+        schedule_mixed_kernel<<<16, 1024, 0, s>>>(sa, N / 256, bf16_w1(kind), MOE_TILE_MGROUP,
+                                                  tiles, unit_nt, total);
         ga.units = tiles;
         ga.unit_nt = unit_nt;
         ga.total = total;
