@@ -62,16 +62,15 @@ def algorithmic(cfg):
         d["permute"] = dict(bytes=T * H * b + T * H + T * (H // 32) + meta, flops=0)
     else:
         d["permute"] = dict(bytes=meta, flops=0)
-    # GEMM1 reads the tokens' rows (x, or its e4m3 codes) once: the routed rows are gathered
-    # from the same T rows the shared expert reads
-    up_b = (E * 2 * F * H * wb + T * H * wb + A * F * wb) * (1 + sx) + A * 4
-    if cfg.act_dtype == 0:
-        up_b += A * H * wb - T * H * wb                 # fp32 keeps the x_perm copy
+    # GEMM1 reads each routed row (A rows of x, or of its e4m3 codes, gathered or from the
+    # fp32 x_perm copy) and, for the shared expert, each token's row: every weight once, the
+    # rows it multiplies, the act rows it writes
+    up_b = (E * 2 * F * H * wb + A * H * wb + A * F * wb) * (1 + sx) + A * 4
     up_f = 2 * A * 2 * F * H
     dn_b = (E * H * F * wb + A * F * wb) * (1 + sx) + A * H * b
     dn_f = 2 * A * H * F
     if sF:
-        up_b += (2 * sF * H * wb + T * sF * wb) * (1 + sx)
+        up_b += (2 * sF * H * wb + T * H * wb + T * sF * wb) * (1 + sx)
         up_f += 2 * T * 2 * sF * H
         dn_b += (H * sF * wb + T * sF * wb) * (1 + sx) + T * H * b
         dn_f += 2 * T * H * sF
