@@ -1026,28 +1026,32 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_e4m3_kernel(GemmArgs ga) {
     // segment's activation base and the group's weight base
     const uint8_t* abase = (const uint8_t*)S.a;
     const uint8_t* wbase = (const uint8_t*)S.w + (size_t)g * S.w_mat;
-    uint32_t src[C::kDma];
-#pragma unroll
-    for (int q = 0; q < C::kDma; ++q) {
-        const int r = 8 * (wave + q * C::kWaves) + lane / 8;
-        const int c = (lane % 8) ^ chunk_swz<8>(r);
-        size_t rowp;
-        if (r < BM) {
-            const int rr = m0 + r < Mg ? m0 + r : Mg - 1;
-            rowp = (size_t)(S.a_rows ? S.a_rows[rbase + rr] : rbase + rr) * S.a_row;
-        } else {
-            const int rb = r - BM;
-            int wrow;
-            if (KIND == 0)
-                wrow = rb < BN / 2 ? nt * (BN / 2) + rb : N / 2 + nt * (BN / 2) + (rb - BN / 2);
-            else
-                wrow = nt * BN + rb;
-            rowp = (size_t)wrow * S.w_row;
-        }
-        const size_t step = r < BM ? S.a_kstep : S.w_kstep;
-        src[q] = (uint32_t)(rowp + (size_t)(c / 4) * step + (c % 4) * 16);
-    }
+    // instruction q fills tile rows 64 q + rl (rl = 8 wave + lane / 8): A rows (gathered) for
+    // q < kDmaA, else B rows 64 (q - kDmaA) + rl of the weight tile. Rows 64 apart share the
+    // chunk swizzle, so a B instruction's source is a wave-uniform row base plus one lane
+    // offset (lane_b) for all of them (fewer VGPRs than one offset per instruction).
+    constexpr int kDmaA = BM / 64, kDmaB = C::kDma - kDmaA;
+    static_assert(BM % 64 == 0 && (KIND == 1 || (BN / 2) % 64 == 0), "64-row DMA groups");
+    const int rl = 8 * wave + lane / 8;
+    const int cl = (lane % 8) ^ chunk_swz<8>(rl);
     const size_t a_step = S.a_kstep, w_step = S.w_kstep;
+    uint32_t src[kDmaA];
+#pragma unroll
+    for (int q = 0; q < kDmaA; ++q) {
+        const int r = 64 * q + rl;
+        const int rr = m0 + r < Mg ? m0 + r : Mg - 1;
+        const size_t rowp = (size_t)(S.a_rows ? S.a_rows[rbase + rr] : rbase + rr) * S.a_row;
+        src[q] = (uint32_t)(rowp + (size_t)(cl / 4) * a_step + (cl % 4) * 16);
+    }
+    const uint32_t lane_b =
+        (uint32_t)((size_t)rl * S.w_row + (size_t)(cl / 4) * w_step + (cl % 4) * 16);
+    auto wrow0 = [&](int qb) -> size_t {            // first weight row of B instruction qb
+        const int rb = 64 * qb;
+        if (KIND == 0)
+            return rb < BN / 2 ? (size_t)nt * (BN / 2) + rb
+                               : (size_t)N / 2 + (size_t)nt * (BN / 2) + (rb - BN / 2);
+        return (size_t)nt * BN + rb;
+    };
     // A-row scales: wave w loads rows kRpw w + lane % kRpw of this tile
     const float* ssrc;
     {
@@ -1058,11 +1062,15 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_e4m3_kernel(GemmArgs ga) {
     auto issue = [&](int kstep, int stage) {
         MOE_LDS uint8_t* base = (MOE_LDS uint8_t*)lds + stage * C::kStageBytes;
 #pragma unroll
-        for (int q = 0; q < C::kDma; ++q)
+        for (int q = 0; q < kDmaA; ++q)
             __builtin_amdgcn_global_load_lds(
-                (const void*)((q * 8 * C::kWaves < BM ? abase : wbase) + src[q] +
-                              (size_t)kstep * 2 * (q * 8 * C::kWaves < BM ? a_step : w_step)),
+                (const void*)(abase + src[q] + (size_t)kstep * 2 * a_step),
                 (MOE_LDS void*)(base + (wave + q * C::kWaves) * 1024), 16, 0, 0);
+#pragma unroll
+        for (int qb = 0; qb < kDmaB; ++qb)
+            __builtin_amdgcn_global_load_lds(
+                (const void*)(wbase + wrow0(qb) * S.w_row + lane_b + (size_t)kstep * 2 * w_step),
+                (MOE_LDS void*)(base + (wave + (kDmaA + qb) * C::kWaves) * 1024), 16, 0, 0);
         __builtin_amdgcn_global_load_lds((const void*)(ssrc + kstep),
                                          (MOE_LDS void*)(base + C::kTileBytes + wave * 256), 4, 0, 0);
     };
