@@ -330,8 +330,8 @@ struct BfCfg {
     static constexpr size_t kLdsLoop = (size_t)SA * kASlot + (size_t)SB * kBSlot;
     static constexpr size_t kLdsEp = (size_t)BM * kEpStride * 2;
     // GEMM1: the tile's row gates, staged at tile start past the ring and the epilogue
-    // staging (one 4-byte word per tile row)
-    // (when that would not fit, the epilogue reads them from global memory instead)
+    // staging (one 4-byte word per tile row), or read from global memory by the epilogue
+    // when they would not fit
     static constexpr size_t kGateOff = ((kLdsLoop > kLdsEp ? kLdsLoop : kLdsEp) + 15) / 16 * 16;
     static constexpr bool kGateLds = KIND == 0 && kGateOff + (size_t)BM * 4 <= 160 * 1024;
     static constexpr size_t kLds = kGateLds ? kGateOff + (size_t)BM * 4 : kGateOff;
