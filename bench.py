@@ -362,10 +362,14 @@ def time_backward(moe, mi, cfg, dev, x, inp, idx, gate, w13_bf, w2_bf, reps):
 
 
 def time_layer_backward(moe, mi, cfg, dev, x, wr, logits, idx, gate, w13, w2, ws13, ws2, lb,
-                        reps):
+                        reps, train=None, flush=None):
     """The whole-layer backward (moe_layer_backward) for the forward's routing, dY ~ N(0,1)
     seeded, bf16 row-major weights; timed on its own. Its FLOPs count the backward GEMMs only
-    (experts, shared expert, router), not the GEMM1 recompute it also runs."""
+    (experts, shared expert, router), not the GEMM1 recompute it also runs.
+    train (bf16 layers): dict(cfg, w13, w2, ws13, ws2, sb) of the timed forward; then the
+    training pair is timed too: moe_layer_forward_train (median over reps, a cache flush
+    before each, outside its events, as the forward steps) and moe_layer_backward_saved, which
+    takes Z and act from that forward instead of recomputing GEMM1."""
     import torch
     bcfg = cfg.replace(w_dtype=mi.BF16, a_layout=0, w_layout=0)
     gen = torch.Generator().manual_seed(20261202)
@@ -387,10 +391,57 @@ def time_layer_backward(moe, mi, cfg, dev, x, wr, logits, idx, gate, w13, w2, ws
         t += a.elapsed_time(b) / max(1, reps)
     A = cfg.T * cfg.k
     flops = 12 * (A * cfg.H * cfg.F + cfg.T * cfg.H * cfg.shared_F) + 4 * cfg.T * cfg.E * cfg.H
-    return {"what": "whole-layer backward (experts, shared expert, gates, router; recomputes "
-                    "GEMM1), bf16", "ms": round(t, 4),
-            "TFLOP/s": round(flops / (t * 1e-3) / 1e12, 1),
-            "tokens/s": round(cfg.T / (t * 1e-3), 1)}
+    out = {"what": "whole-layer backward (experts, shared expert, gates, router; recomputes "
+                   "GEMM1), bf16", "ms": round(t, 4),
+           "TFLOP/s": round(flops / (t * 1e-3) / 1e12, 1),
+           "tokens/s": round(cfg.T / (t * 1e-3), 1)}
+    if train is None:
+        return out
+    tcfg = train["cfg"].replace(a_layout=0)
+    saved = moe.workspace(tcfg, moe.OP_LAYER_SAVED, dev)
+    fws = moe.workspace(tcfg, moe.OP_LAYER_FORWARD, dev)
+    y = torch.empty(cfg.T, cfg.H, dtype=torch.bfloat16, device=dev)
+
+    def fwd(want=()):
+        return moe.layer_forward_train(tcfg, x, wr, train["w13"], train["w2"], lb, train["sb"],
+                                       ws13=train["ws13"], ws2=train["ws2"], y=y, want=want,
+                                       saved=saved, ws=fws)
+    _, ext, _ = fwd(("logits", "topk_idx", "topk_gate"))
+    torch.cuda.synchronize()
+    f_ms = []
+    for _ in range(max(3, reps)):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        if flush is not None:
+            flush()
+        a.record()
+        fwd()
+        b.record()
+        torch.cuda.synchronize()
+        f_ms.append(a.elapsed_time(b))
+
+    def run_saved():
+        return moe.layer_backward_saved(bcfg, x, wr, ext["logits"], ext["topk_idx"],
+                                        ext["topk_gate"], w13, w2, dy, saved, logit_bias=lb,
+                                        ws13=ws13, ws2=ws2, ws=lws)
+    run_saved()
+    torch.cuda.synchronize()
+    ts = 0.0
+    for _ in range(max(1, reps)):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        run_saved()
+        b.record()
+        torch.cuda.synchronize()
+        ts += a.elapsed_time(b) / max(1, reps)
+    fm = pct(f_ms, 50)
+    out["saved_activations"] = {
+        "what": "training pair: moe_layer_forward_train keeps GEMM1's Z and act "
+                f"({saved.numel() / 1e9:.2f} GB); moe_layer_backward_saved uses them instead "
+                "of recomputing GEMM1 (gradients bit-identical to the recomputing backward)",
+        "forward_train_ms": round(fm, 4), "backward_ms": round(ts, 4),
+        "backward_TFLOP/s": round(flops / (ts * 1e-3) / 1e12, 1),
+        "step_ms": round(fm + ts, 4), "step_tokens/s": round(cfg.T / ((fm + ts) * 1e-3), 1)}
+    return out
 
 
 def dense_ceiling(cfg, reps: int = 20):
@@ -609,9 +660,11 @@ def main():
     if layer_bwd:
         ws = None
         torch.cuda.empty_cache()
+        train = (dict(cfg=cfg, w13=w13, w2=w2, ws13=ws13, ws2=ws2, sb=sb)
+                 if cfg.w_dtype == mi.BF16 else None)
         layer_backward = time_layer_backward(moe, mi, cfg, dev, x, wr, ex["logits"], idx, gate,
                                              w13_bf, w2_bf, ws13_bf, ws2_bf, lb,
-                                             args.bwd_reps)
+                                             args.bwd_reps, train, flush)
     alg = algorithmic(cfg)
     dtype = {0: "fp32", 1: "bf16", 2: "e4m3", 3: "mxfp8"}[cfg.w_dtype]
     per_stage = {}

@@ -90,7 +90,10 @@ typedef enum {
     MOE_OP_LAYER_FORWARD = 2,
     MOE_OP_GROUPED_GEMM_BWD = 3,
     MOE_OP_LAYER_BACKWARD = 4,
-    MOE_OP_ROUTE_STATS = 5
+    MOE_OP_ROUTE_STATS = 5,
+    /* not a workspace: the size of the `saved` buffer of moe_layer_forward_train and
+     * moe_layer_backward_saved */
+    MOE_OP_LAYER_SAVED = 6
 } moe_op;
 
 /* Layer shape and numerics. Host memory, read only during a call. */
@@ -359,6 +362,41 @@ int moe_layer_backward(const moe_config* cfg, const void* x, const void* w_route
                        const void* ws13, const void* ws2, const void* dy, void* dx,
                        void* dw_router, void* dw13, void* dw2, void* dws13, void* dws2,
                        float* dlogits_out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* The training pair: a forward that keeps GEMM1's outputs, and the backward that uses them
+ * instead of recomputing GEMM1. The technical summary on large-scale MoE training with
+ * Megatron Core (section 2.2, fine-grained recomputation) weighs activation memory against
+ * recomputation; moe_layer_backward recomputes the whole GEMM1, this pair keeps it:
+ * Z [T*k, 2F] and act [T*k, F] of the routed rows in expert order, and the shared expert's
+ * Z [T, 2 shared_F] and act [T, shared_F], bf16 row-major, in one caller-owned buffer of
+ * moe_workspace_size(cfg, MOE_OP_LAYER_SAVED) bytes (about 0.9 GB for T = 8192, k = 8,
+ * F = shared_F = 2048). Its layout is private to the pair; contents live until the caller
+ * overwrites them.
+ * moe_layer_forward_train: moe_layer_forward for act_dtype = w_dtype = MOE_BF16, a_layout 0,
+ * no capacity (else MOE_ERR_UNSUPPORTED), any w_layout; same arguments without the fp8 scale
+ * pointers, plus saved (NULL or too small: MOE_ERR_INVALID_ARG / MOE_ERR_WORKSPACE). y and
+ * the optional outputs are bit-identical to moe_layer_forward's. Workspace:
+ * moe_workspace_size(cfg, MOE_OP_LAYER_FORWARD).
+ * moe_layer_backward_saved: moe_layer_backward with the buffer written by
+ * moe_layer_forward_train for the same x, routing (topk_idx, topk_gate) and weights (the
+ * backward's cfg may differ only in w_layout, which must be 0 here); every output is
+ * bit-identical to moe_layer_backward's, and no GEMM1 is run. Workspace:
+ * moe_workspace_size(cfg, MOE_OP_LAYER_BACKWARD). */
+int moe_layer_forward_train(const moe_config* cfg, const void* x, const void* w_router,
+                            const float* logit_bias, const float* sel_bias,
+                            const float* logits_in, const void* w13, const void* w2,
+                            const void* ws13, const void* ws2, void* y, float* logits_out,
+                            int32_t* topk_idx_out, float* topk_gate_out, int32_t* counts_out,
+                            void* saved, size_t saved_bytes, void* ws, size_t ws_bytes,
+                            hipStream_t stream);
+int moe_layer_backward_saved(const moe_config* cfg, const void* x, const void* w_router,
+                             const float* logits, const float* logit_bias,
+                             const int32_t* topk_idx, const float* topk_gate, const void* w13,
+                             const void* w2, const void* ws13, const void* ws2,
+                             const void* saved, size_t saved_bytes, const void* dy, void* dx,
+                             void* dw_router, void* dw13, void* dw2, void* dws13, void* dws2,
+                             float* dlogits_out, void* ws, size_t ws_bytes,
+                             hipStream_t stream);
 
 /* Re-layout of n_mat row-major matrices [rows, cols] of elem_bytes-byte elements into the
  * K-blocked layout [n_mat][cols * elem_bytes / 64][rows][64 bytes] (see Layouts). A pure

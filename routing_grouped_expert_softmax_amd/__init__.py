@@ -28,6 +28,7 @@ LAYOUT_ROWS, LAYOUT_KBLOCK = 0, 1
 OP_PERMUTE, OP_GROUPED_GEMM, OP_LAYER_FORWARD, OP_GROUPED_GEMM_BWD, OP_LAYER_BACKWARD = \
     0, 1, 2, 3, 4
 OP_ROUTE_STATS = 5
+OP_LAYER_SAVED = 6
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -78,6 +79,8 @@ _SIGS = {
     "moe_pack_kblock": [P, I64, I32, I32, I32, P, P],
     "moe_set_stage_events": [P, I32],
     "moe_layer_backward": [CFG, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
+    "moe_layer_forward_train": [CFG] + [P] * 15 + [SZ, P, SZ, P],
+    "moe_layer_backward_saved": [CFG] + [P] * 11 + [SZ] + [P] * 8 + [P, SZ, P],
 }
 for _name, _args in _SIGS.items():
     getattr(_lib, _name).argtypes = _args
@@ -440,6 +443,36 @@ def layer_forward(cfg, x, w_router, w13, w2, logit_bias=None, sel_bias=None, log
     return y, extras
 
 
+def layer_forward_train(cfg, x, w_router, w13, w2, logit_bias=None, sel_bias=None,
+                        logits_in=None, ws13=None, ws2=None, y=None, want=(), saved=None,
+                        ws=None, stream=None):
+    """The bf16 layer forward that also keeps GEMM1's Z and act for layer_backward_saved
+    (moe_layer_forward_train). Returns (y, extras dict as layer_forward, saved buffer)."""
+    dev = x.device
+    T, H, E, k, F, sF = cfg.T, cfg.H, cfg.E, cfg.k, cfg.F, cfg.shared_F
+    bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
+    if y is None:
+        y = torch.empty(T, H, dtype=bf, device=dev)
+    shapes = dict(logits=((T, E), f32), topk_idx=((T, k), i32), topk_gate=((T, k), f32),
+                  counts=((E,), i32))
+    extras = {n: torch.empty(shapes[n][0], dtype=shapes[n][1], device=dev) for n in want}
+    if saved is None:
+        saved = workspace(cfg, OP_LAYER_SAVED, dev)
+    if ws is None:
+        ws = workspace(cfg, OP_LAYER_FORWARD, dev)
+    c = make_config(cfg)
+    _check("moe_layer_forward_train", _lib.moe_layer_forward_train(
+        C.byref(c), _ptr(x, bf, (T, H), "x"), _ptr(w_router, bf, (E, H), "w_router"),
+        _ptr(logit_bias, f32, (E,), "logit_bias"), _ptr(sel_bias, f32, (E,), "sel_bias"),
+        _ptr(logits_in, f32, (T, E), "logits_in"), _ptr(w13, bf, (E, 2 * F, H), "w13"),
+        _ptr(w2, bf, (E, H, F), "w2"), _ptr(ws13, bf, (2 * sF, H), "ws13"),
+        _ptr(ws2, bf, (H, sF), "ws2"), _ptr(y, bf, (T, H), "y"), _ptr(extras.get("logits")),
+        _ptr(extras.get("topk_idx")), _ptr(extras.get("topk_gate")),
+        _ptr(extras.get("counts")), _ptr(saved, torch.uint8, name="saved"), saved.numel(), _ptr(ws),
+        ws.numel(), _stream(stream)))
+    return y, extras, saved
+
+
 def grouped_gemm_swiglu_bwd(cfg, dy_perm, x_perm, z, act, gate_perm, offsets, w13, w2,
                             want_dgate=True, ws=None, stream=None):
     """Backward of the grouped expert MLP (moe_grouped_gemm_swiglu_bwd). gate_perm may be
@@ -493,6 +526,37 @@ def layer_backward(cfg, x, w_router, logits, topk_idx, topk_gate, w13, w2, dy,
         _ptr(ws2, bf, (H, sF), "ws2"), _ptr(dy, bf, (T, H), "dy"), _ptr(out["dx"]),
         _ptr(out["dw_router"]), _ptr(out["dw13"]), _ptr(out["dw2"]), _ptr(out["dws13"]),
         _ptr(out["dws2"]), _ptr(out["dlogits"]), _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def layer_backward_saved(cfg, x, w_router, logits, topk_idx, topk_gate, w13, w2, dy, saved,
+                         logit_bias=None, ws13=None, ws2=None, want_dlogits=False, ws=None,
+                         stream=None):
+    """layer_backward with Z and act from layer_forward_train's saved buffer instead of a
+    recomputed GEMM1 (moe_layer_backward_saved). Returns the same dict as layer_backward."""
+    dev = x.device
+    T, H, E, k, F, sF = cfg.T, cfg.H, cfg.E, cfg.k, cfg.F, cfg.shared_F
+    bf, f32 = torch.bfloat16, torch.float32
+    out = dict(dx=torch.empty(T, H, dtype=bf, device=dev),
+               dw_router=torch.empty(E, H, dtype=bf, device=dev),
+               dw13=torch.empty(E, 2 * F, H, dtype=bf, device=dev),
+               dw2=torch.empty(E, H, F, dtype=bf, device=dev),
+               dws13=torch.empty(2 * sF, H, dtype=bf, device=dev) if sF else None,
+               dws2=torch.empty(H, sF, dtype=bf, device=dev) if sF else None,
+               dlogits=torch.empty(T, E, dtype=f32, device=dev) if want_dlogits else None)
+    if ws is None:
+        ws = workspace(cfg, OP_LAYER_BACKWARD, dev)
+    c = make_config(cfg)
+    _check("moe_layer_backward_saved", _lib.moe_layer_backward_saved(
+        C.byref(c), _ptr(x, bf, (T, H), "x"), _ptr(w_router, bf, (E, H), "w_router"),
+        _ptr(logits, f32, (T, E), "logits"), _ptr(logit_bias, f32, (E,), "logit_bias"),
+        _ptr(topk_idx, torch.int32, (T, k), "topk_idx"),
+        _ptr(topk_gate, f32, (T, k), "topk_gate"), _ptr(w13, bf, (E, 2 * F, H), "w13"),
+        _ptr(w2, bf, (E, H, F), "w2"), _ptr(ws13, bf, (2 * sF, H), "ws13"),
+        _ptr(ws2, bf, (H, sF), "ws2"), _ptr(saved, torch.uint8, name="saved"), saved.numel(),
+        _ptr(dy, bf, (T, H), "dy"), _ptr(out["dx"]), _ptr(out["dw_router"]),
+        _ptr(out["dw13"]), _ptr(out["dw2"]), _ptr(out["dws13"]), _ptr(out["dws2"]),
+        _ptr(out["dlogits"]), _ptr(ws), ws.numel(), _stream(stream)))
     return out
 
 

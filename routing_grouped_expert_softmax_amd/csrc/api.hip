@@ -236,6 +236,34 @@ int check_layer_bwd(const moe_config* c) {
     return MOE_OK;
 }
 
+// The GEMM1 outputs a training forward keeps for the backward: Z and act of the routed rows
+// (expert order) and of the shared expert, bf16 row-major.
+struct SavedActs {
+    void *z, *act, *zs, *acts;
+    size_t total;
+};
+
+SavedActs carve_saved(const moe_config* c, void* p) {
+    SavedActs S = {};
+    Carve cv(p);
+    const size_t T = c->T, F = c->F, sF = c->shared_F, A = T * c->k;
+    S.z = cv.take(A * 2 * F * 2);
+    S.act = cv.take(A * F * 2);
+    S.zs = sF ? cv.take(T * 2 * sF * 2) : nullptr;
+    S.acts = sF ? cv.take(T * sF * 2) : nullptr;
+    S.total = cv.off;
+    return S;
+}
+
+// A forward that saves its activations runs the bf16 layer without dropping (the backward's
+// conditions, any weight layout).
+int check_saved(const moe_config* c) {
+    if (c->act_dtype != MOE_BF16 || c->w_dtype != MOE_BF16 || c->a_layout)
+        return MOE_ERR_UNSUPPORTED;
+    if (c->capacity_factor != 0.0f) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
 size_t sched_ws_bytes(const moe_config* c) {
     const int dt = c->w_dtype;
     const int seg_groups = c->E + (c->shared_F ? 1 : 0);
@@ -253,13 +281,14 @@ int run_up(const moe_config* c, int a_kb, const void* x_perm, const void* x_perm
            const void* w13_scales, const void* x_shared, const void* x_shared_scales,
            const void* ws13, const void* ws13_scales, void* act, void* act_scales,
            void* shared_act, void* shared_act_scales, void* z_out, void* sched,
-           hipStream_t stream, const int32_t* a_rows = nullptr, bool mx_blocked = false) {
+           hipStream_t stream, const int32_t* a_rows = nullptr, bool mx_blocked = false,
+           void* shared_z_out = nullptr) {
     const int dt = c->w_dtype;
     const int A = c->T * c->k;
     Segment r1 = {x_perm, x_perm_scales, offsets, c->E, 0, gate_perm, w13, w13_scales,
                   act, act_scales, z_out, A, a_kb, c->w_layout, a_kb, a_rows};
     Segment s1 = {x_shared, x_shared_scales, nullptr, 1, c->T, nullptr, ws13, ws13_scales,
-                  shared_act, shared_act_scales, nullptr, c->T, 0, c->w_layout, a_kb};
+                  shared_act, shared_act_scales, shared_z_out, c->T, 0, c->w_layout, a_kb};
     if (dt == MOE_MXFP8) {
         // K-blocked weights carry blocked scales; the layer keeps its activation scales
         // blocked too, the routed ones already in expert order
@@ -322,7 +351,8 @@ int run_experts(const moe_config* c, int a_kb, const void* x_perm, const void* x
                 const void* ws13_scales, const void* ws2, const void* ws2_scales, void* act,
                 void* act_scales, void* y_perm, void* shared_y, void* z_out, void* ws,
                 hipStream_t stream, int mid_mark = -1, const int32_t* a_rows = nullptr,
-                bool mx_blocked = false) {
+                bool mx_blocked = false, void* shared_act_out = nullptr,
+                void* shared_z_out = nullptr) {
     Carve cv(ws);
     void* sched = cv.take(sched_ws_bytes(c));
     void* sh_act = nullptr;
@@ -331,10 +361,11 @@ int run_experts(const moe_config* c, int a_kb, const void* x_perm, const void* x
         const bool fp8 = is_fp8(c->w_dtype);
         sh_act = cv.take((size_t)c->T * c->shared_F * (fp8 ? 1 : elem_bytes(c->act_dtype)));
         if (fp8) sh_act_scales = cv.take(act_scale_bytes(c->w_dtype, c->T, c->shared_F));
+        if (shared_act_out) sh_act = shared_act_out;
     }
     int st = run_up(c, a_kb, x_perm, x_perm_scales, offsets, gate_perm, w13, w13_scales, x_shared,
                     x_shared_scales, ws13, ws13_scales, act, act_scales, sh_act, sh_act_scales,
-                    z_out, sched, stream, a_rows, mx_blocked);
+                    z_out, sched, stream, a_rows, mx_blocked, shared_z_out);
     if (st) return st;
     if (mid_mark >= 0 && stage_mark(mid_mark, stream) != hipSuccess) return MOE_ERR_HIP;
     return run_down(c, a_kb, act, act_scales, offsets, w2, w2_scales, sh_act, sh_act_scales, ws2,
@@ -405,6 +436,11 @@ int moe_workspace_size(const moe_config* cfg, int op, size_t* bytes) {
         st = check_layer_bwd(cfg);
         if (st) return st;
         *bytes = carve_layer_bwd(cfg, nullptr).total;
+        break;
+    case MOE_OP_LAYER_SAVED:
+        st = check_saved(cfg);
+        if (st) return st;
+        *bytes = carve_saved(cfg, nullptr).total;
         break;
     default: return MOE_ERR_INVALID_ARG;
     }
@@ -605,13 +641,16 @@ int moe_unpermute_combine(const moe_config* cfg, const void* y_perm, const int32
                                           cfg->H, cfg->k, y, stream));
 }
 
-int moe_layer_forward(const moe_config* cfg, const void* x, const void* w_router,
-                      const float* logit_bias, const float* sel_bias, const float* logits_in,
-                      const void* w13, const void* w13_scales, const void* w2,
-                      const void* w2_scales, const void* ws13, const void* ws13_scales,
-                      const void* ws2, const void* ws2_scales, void* y, float* logits_out,
-                      int32_t* topk_idx_out, float* topk_gate_out, int32_t* counts_out,
-                      void* ws, size_t ws_bytes, hipStream_t stream) {
+// The layer forward; sv != NULL: GEMM1 writes act and Z (routed and shared) into the saved
+// buffer instead of act alone into the workspace (moe_layer_forward_train).
+static int layer_forward_impl(const moe_config* cfg, const void* x, const void* w_router,
+                              const float* logit_bias, const float* sel_bias,
+                              const float* logits_in, const void* w13, const void* w13_scales,
+                              const void* w2, const void* w2_scales, const void* ws13,
+                              const void* ws13_scales, const void* ws2, const void* ws2_scales,
+                              void* y, float* logits_out, int32_t* topk_idx_out,
+                              float* topk_gate_out, int32_t* counts_out, void* ws,
+                              size_t ws_bytes, hipStream_t stream, const SavedActs* sv) {
     int st = check_cfg(cfg);
     if (st) return st;
     if (!x || !w13 || !w2 || !y || !ws) return MOE_ERR_INVALID_ARG;
@@ -674,8 +713,10 @@ int moe_layer_forward(const moe_config* cfg, const void* x, const void* w_router
     const void* a1_scales = gather && !mx ? (fp8 ? L.x_q_scales : nullptr) : L.x_perm_scales;
     st = run_experts(cfg, a_kb, a1, a1_scales, L.offsets, L.gate_perm, w13, w13_scales,
                      w2, w2_scales, cfg->shared_F ? xs : nullptr, fp8 ? L.x_q_scales : nullptr,
-                     ws13, ws13_scales, ws2, ws2_scales, L.act, L.act_scales, L.y_perm,
-                     L.shared_y, nullptr, L.scratch, stream, 4, gather ? L.src : nullptr, mx);
+                     ws13, ws13_scales, ws2, ws2_scales, sv ? sv->act : L.act, L.act_scales,
+                     L.y_perm, L.shared_y, sv ? sv->z : nullptr, L.scratch, stream, 4,
+                     gather ? L.src : nullptr, mx, sv ? sv->acts : nullptr,
+                     sv ? sv->zs : nullptr);
     if (st) return st;
     e = stage_mark(5, stream);
     if (e == hipSuccess)
@@ -683,6 +724,40 @@ int moe_layer_forward(const moe_config* cfg, const void* x, const void* w_router
                                 cfg->k, y, stream);
     if (e == hipSuccess) e = stage_mark(6, stream);
     return hip_status(e);
+}
+
+int moe_layer_forward(const moe_config* cfg, const void* x, const void* w_router,
+                      const float* logit_bias, const float* sel_bias, const float* logits_in,
+                      const void* w13, const void* w13_scales, const void* w2,
+                      const void* w2_scales, const void* ws13, const void* ws13_scales,
+                      const void* ws2, const void* ws2_scales, void* y, float* logits_out,
+                      int32_t* topk_idx_out, float* topk_gate_out, int32_t* counts_out,
+                      void* ws, size_t ws_bytes, hipStream_t stream) {
+    return layer_forward_impl(cfg, x, w_router, logit_bias, sel_bias, logits_in, w13,
+                              w13_scales, w2, w2_scales, ws13, ws13_scales, ws2, ws2_scales, y,
+                              logits_out, topk_idx_out, topk_gate_out, counts_out, ws, ws_bytes,
+                              stream, nullptr);
+}
+
+int moe_layer_forward_train(const moe_config* cfg, const void* x, const void* w_router,
+                            const float* logit_bias, const float* sel_bias,
+                            const float* logits_in, const void* w13, const void* w2,
+                            const void* ws13, const void* ws2, void* y, float* logits_out,
+                            int32_t* topk_idx_out, float* topk_gate_out, int32_t* counts_out,
+                            void* saved, size_t saved_bytes, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
+    int st = check_cfg(cfg);
+    if (st) return st;
+    st = check_saved(cfg);
+    if (st) return st;
+    if (!saved) return MOE_ERR_INVALID_ARG;
+    SavedActs sv = carve_saved(cfg, nullptr);
+    if (saved_bytes < sv.total) return MOE_ERR_WORKSPACE;
+    sv = carve_saved(cfg, saved);
+    return layer_forward_impl(cfg, x, w_router, logit_bias, sel_bias, logits_in, w13, nullptr,
+                              w2, nullptr, ws13, nullptr, ws2, nullptr, y, logits_out,
+                              topk_idx_out, topk_gate_out, counts_out, ws, ws_bytes, stream,
+                              &sv);
 }
 
 int moe_set_stage_events(void* const* events, int32_t n_events) {
@@ -718,12 +793,15 @@ int moe_grouped_gemm_swiglu_bwd(const moe_config* cfg, const void* dy_perm, cons
                                                    stream));
 }
 
-int moe_layer_backward(const moe_config* cfg, const void* x, const void* w_router,
-                       const float* logits, const float* logit_bias, const int32_t* topk_idx,
-                       const float* topk_gate, const void* w13, const void* w2,
-                       const void* ws13, const void* ws2, const void* dy, void* dx,
-                       void* dw_router, void* dw13, void* dw2, void* dws13, void* dws2,
-                       float* dlogits_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+// The layer backward; sv != NULL: Z and act come from the saved buffer of a training forward
+// instead of a recomputed GEMM1 (moe_layer_backward_saved).
+static int layer_backward_impl(const moe_config* cfg, const void* x, const void* w_router,
+                               const float* logits, const float* logit_bias,
+                               const int32_t* topk_idx, const float* topk_gate, const void* w13,
+                               const void* w2, const void* ws13, const void* ws2, const void* dy,
+                               void* dx, void* dw_router, void* dw13, void* dw2, void* dws13,
+                               void* dws2, float* dlogits_out, void* ws, size_t ws_bytes,
+                               hipStream_t stream, const SavedActs* sv) {
     int st = check_cfg(cfg);
     if (st) return st;
     st = check_layer_bwd(cfg);
@@ -749,27 +827,30 @@ int moe_layer_backward(const moe_config* cfg, const void* x, const void* w_route
         e = moe::launch_permute(1, 0, INT_MAX, dy, topk_idx, topk_gate, T, H, E, k, L.counts2,
                                 L.offsets2, L.pos2, L.src2, L.gate_perm2, L.dy_perm, nullptr,
                                 nullptr, nullptr, L.perm_scratch, stream);
-    // recompute Z and act of GEMM1 (routed, then the shared expert)
-    if (e == hipSuccess) {
+    // Z and act of GEMM1 (routed, then the shared expert): saved by the forward, or recomputed
+    void* z = sv ? sv->z : L.z;
+    void* act = sv ? sv->act : L.act;
+    void* zs = sv ? sv->zs : L.zs;
+    void* acts = sv ? sv->acts : L.acts;
+    if (e == hipSuccess && !sv) {
         Segment r1 = {L.x_perm, nullptr, L.offsets, E, 0, L.gate_perm, w13, nullptr, L.act,
                       nullptr, L.z, A, 0, 0, 0, nullptr};
         e = moe::launch_grouped_gemm(0, MOE_BF16, &r1, 1, A, 2 * F, H, L.sched, stream);
     }
     if (e == hipSuccess) e = moe::launch_offsets2(L.offs_one, T, stream);
-    if (e == hipSuccess && sF) {
+    if (e == hipSuccess && sF && !sv) {
         Segment s1 = {x, nullptr, nullptr, 1, T, nullptr, ws13, nullptr, L.acts, nullptr, L.zs,
                       T, 0, 0, 0, nullptr};
         e = moe::launch_grouped_gemm(0, MOE_BF16, &s1, 1, T, 2 * sF, H, L.sched, stream);
     }
     // expert gradients (routed: dgate through the fold; shared: gate 1)
     if (e == hipSuccess)
-        e = moe::launch_grouped_gemm_bwd(L.dy_perm, L.x_perm, L.z, L.act, L.gate_perm,
-                                         L.offsets, w13, w2, A, E, H, F, L.dx_perm, dw13, dw2,
+        e = moe::launch_grouped_gemm_bwd(L.dy_perm, L.x_perm, z, act, L.gate_perm, L.offsets,
+                                         w13, w2, A, E, H, F, L.dx_perm, dw13, dw2,
                                          L.dgate_perm, L.bws, stream);
     if (e == hipSuccess && sF)
-        e = moe::launch_grouped_gemm_bwd(dy, x, L.zs, L.acts, nullptr, L.offs_one, ws13, ws2,
-                                         T, 1, H, sF, L.dxs, dws13, dws2, nullptr, L.bws_s,
-                                         stream);
+        e = moe::launch_grouped_gemm_bwd(dy, x, zs, acts, nullptr, L.offs_one, ws13, ws2, T, 1,
+                                         H, sF, L.dxs, dws13, dws2, nullptr, L.bws_s, stream);
     // gates -> logits -> router weight and x
     if (e == hipSuccess)
         e = moe::launch_route_backward(cfg->router, logits, logit_bias, topk_idx, topk_gate,
@@ -783,6 +864,38 @@ int moe_layer_backward(const moe_config* cfg, const void* x, const void* w_route
                                 stream);
     if (e == hipSuccess) e = moe::launch_add_bf16(dx, L.dxr, (int64_t)T * H, stream);
     return hip_status(e);
+}
+
+int moe_layer_backward(const moe_config* cfg, const void* x, const void* w_router,
+                       const float* logits, const float* logit_bias, const int32_t* topk_idx,
+                       const float* topk_gate, const void* w13, const void* w2,
+                       const void* ws13, const void* ws2, const void* dy, void* dx,
+                       void* dw_router, void* dw13, void* dw2, void* dws13, void* dws2,
+                       float* dlogits_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+    return layer_backward_impl(cfg, x, w_router, logits, logit_bias, topk_idx, topk_gate, w13,
+                               w2, ws13, ws2, dy, dx, dw_router, dw13, dw2, dws13, dws2,
+                               dlogits_out, ws, ws_bytes, stream, nullptr);
+}
+
+int moe_layer_backward_saved(const moe_config* cfg, const void* x, const void* w_router,
+                             const float* logits, const float* logit_bias,
+                             const int32_t* topk_idx, const float* topk_gate, const void* w13,
+                             const void* w2, const void* ws13, const void* ws2,
+                             const void* saved, size_t saved_bytes, const void* dy, void* dx,
+                             void* dw_router, void* dw13, void* dw2, void* dws13, void* dws2,
+                             float* dlogits_out, void* ws, size_t ws_bytes,
+                             hipStream_t stream) {
+    int st = check_cfg(cfg);
+    if (st) return st;
+    st = check_layer_bwd(cfg);
+    if (st) return st;
+    if (!saved) return MOE_ERR_INVALID_ARG;
+    SavedActs sv = carve_saved(cfg, nullptr);
+    if (saved_bytes < sv.total) return MOE_ERR_WORKSPACE;
+    sv = carve_saved(cfg, const_cast<void*>(saved));
+    return layer_backward_impl(cfg, x, w_router, logits, logit_bias, topk_idx, topk_gate, w13,
+                               w2, ws13, ws2, dy, dx, dw_router, dw13, dw2, dws13, dws2,
+                               dlogits_out, ws, ws_bytes, stream, &sv);
 }
 
 int moe_pack_kblock(const void* in, int64_t n_mat, int32_t rows, int32_t cols,

@@ -186,6 +186,40 @@ def test_layer_backward_argument_checks(moe):
     assert L.moe_layer_backward(C.byref(c), *args, C.c_size_t(n - 1), None) == 3
 
 
+def test_training_pair_argument_checks(moe):
+    """moe_layer_forward_train / moe_layer_backward_saved: the saved buffer's size (Z and act
+    of the routed rows and of the shared expert, bf16, each region 256-byte aligned) and the
+    host-side rejections (no GPU call)."""
+    cfg = mi.CONFIGS["dsv3_bf16"]
+    c = moe.make_config(cfg)
+    st, n = ws_size(moe, c, moe.OP_LAYER_SAVED)
+    A, F, sF, T = cfg.T * cfg.k, cfg.F, cfg.shared_F, cfg.T
+    al = lambda b: (b + 255) // 256 * 256
+    assert st == 0 and n == al(A * 2 * F * 2) + al(A * F * 2) + al(T * 2 * sF * 2) + al(T * sF * 2)
+    assert ws_size(moe, cfgc(moe, base="dsv3_fp8_skew"), moe.OP_LAYER_SAVED)[0] == 2   # e4m3
+    assert ws_size(moe, cfgc(moe, base="tiny_fp32"), moe.OP_LAYER_SAVED)[0] == 2       # fp32
+    assert ws_size(moe, cfgc(moe, capacity_factor=1.25), moe.OP_LAYER_SAVED)[0] == 2
+    # K-blocked weights are fine for the forward (the backward needs row-major ones)
+    assert ws_size(moe, cfgc(moe, w_layout=1), moe.OP_LAYER_SAVED) == (0, n)
+    L = moe.lib()
+    p = C.c_void_p(0x1000)
+    big = C.c_size_t(1 << 40)
+    # forward: x .. counts_out (14 pointers), saved, saved_bytes, ws, ws_bytes, stream
+    fwd = [p] * 14
+    assert L.moe_layer_forward_train(C.byref(c), *fwd, None, C.c_size_t(n), p, big, None) == 1
+    assert L.moe_layer_forward_train(C.byref(c), *fwd, p, C.c_size_t(n - 1), p, big, None) == 3
+    cf8 = cfgc(moe, base="dsv3_fp8_skew")
+    assert L.moe_layer_forward_train(C.byref(cf8), *fwd, p, big, p, big, None) == 2
+    # backward: x .. ws2 (10 pointers), saved, saved_bytes, dy .. dlogits_out (8), ws, ...
+    head, tail = [p] * 10, [p] * 8
+    assert L.moe_layer_backward_saved(C.byref(c), *head, None, C.c_size_t(n), *tail, p, big,
+                                      None) == 1
+    assert L.moe_layer_backward_saved(C.byref(c), *head, p, C.c_size_t(n - 1), *tail, p, big,
+                                      None) == 3
+    ck = cfgc(moe, w_layout=1)
+    assert L.moe_layer_backward_saved(C.byref(ck), *head, p, big, *tail, p, big, None) == 2
+
+
 def test_capacity_and_stats_argument_checks(moe):
     """capacity_factor must be finite and >= 0; the backward calls need it 0; moe_route_stats
     sizes and checks its workspace (host-side checks only)."""

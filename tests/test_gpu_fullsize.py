@@ -391,3 +391,39 @@ def test_full_layer_backward_dsv3(moe):
     e2 = rel_err(g["dws2"].float().cpu(), dws2)
     log(f"dsv3_bf16 backward: shared expert dWs13 {e13:.3e} dWs2 {e2:.3e} (all {T} tokens)")
     assert e13 <= 2e-2 and e2 <= 2e-2
+
+
+def test_full_training_pair_dsv3(moe):
+    """The training pair at the DeepSeek-V3 bf16 size in the benchmarked launch configuration
+    (K-blocked weights for the forward, row-major ones for the backward):
+    moe_layer_forward_train's y and routing equal moe_layer_forward's, and
+    moe_layer_backward_saved's gradients equal moe_layer_backward's, bit for bit."""
+    c = full_case(moe, "dsv3_bf16")
+    cfg, inp, dev = c["cfg"].replace(a_layout=0), c["inp"], c["dev"]
+    log("dsv3_bf16: training pair")
+    x, wr = inp.x.cuda(), inp.w_router.cuda()
+    lb = None if c["lb"] is None else torch.from_numpy(c["lb"]).cuda()
+    sb = None if c["sb"] is None else torch.from_numpy(c["sb"]).cuda()
+    want = ("logits", "topk_idx", "topk_gate", "counts")
+    y, ex = moe.layer_forward(cfg, x, wr, dev["w13"], dev["w2"], lb, sb, ws13=dev["ws13"],
+                              ws2=dev["ws2"], want=want)
+    yt, ext, saved = moe.layer_forward_train(cfg, x, wr, dev["w13"], dev["w2"], lb, sb,
+                                             ws13=dev["ws13"], ws2=dev["ws2"], want=want)
+    torch.cuda.synchronize()
+    assert torch.equal(y, yt)
+    for n in want:
+        assert torch.equal(ex[n], ext[n]), n
+    del y, yt, ext
+    bcfg = cfg.replace(w_layout=0)
+    rm = {n: getattr(inp, n).cuda() for n in ("w13", "w2", "ws13", "ws2")}
+    rng = np.random.default_rng(8)
+    dy = torch.from_numpy(rng.standard_normal((cfg.T, cfg.H)).astype(np.float32)).to(
+        torch.bfloat16).cuda()
+    args = (bcfg, x, wr, ex["logits"], ex["topk_idx"], ex["topk_gate"], rm["w13"], rm["w2"], dy)
+    kw = dict(logit_bias=lb, ws13=rm["ws13"], ws2=rm["ws2"], want_dlogits=True)
+    g = moe.layer_backward(*args, **kw)
+    gs = moe.layer_backward_saved(*args, saved, **kw)
+    torch.cuda.synchronize()
+    for n, t in g.items():
+        assert torch.equal(t, gs[n]), n
+    log("dsv3_bf16: training pair bit-identical")

@@ -81,3 +81,48 @@ def test_layer_backward_deterministic(moe):
     torch.cuda.synchronize()
     for n in ("dx", "dw_router", "dw13", "dw2", "dws13", "dws2"):
         assert torch.equal(outs[0][n], outs[1][n]), n
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_training_pair_bit_identical(moe, name):
+    """moe_layer_forward_train keeps GEMM1's Z and act; moe_layer_backward_saved uses them
+    instead of recomputing GEMM1. Both must give exactly what moe_layer_forward and
+    moe_layer_backward give (the same kernels compute the same values). The dsv3 case runs the
+    training forward on K-blocked weights, as the benchmark does, and the backward on the
+    row-major ones."""
+    cfg = CASES[name]
+    print(f"[train pair] {name}: T={cfg.T} H={cfg.H} E={cfg.E} k={cfg.k} F={cfg.F} "
+          f"shared={cfg.shared_F}", flush=True)
+    inp = mi.make_inputs(cfg)
+    rng = np.random.default_rng(41)
+    dy = torch.from_numpy(rng.standard_normal((cfg.T, cfg.H)).astype(np.float32)).to(
+        torch.bfloat16).cuda()
+    x, wr, w13, w2 = inp.x.cuda(), inp.w_router.cuda(), inp.w13.cuda(), inp.w2.cuda()
+    ws13, ws2 = to_dev(inp.ws13), to_dev(inp.ws2)
+    lb, sb = to_dev(inp.logit_bias), to_dev(inp.sel_bias)
+    want = ("logits", "topk_idx", "topk_gate", "counts")
+    y, ex = moe.layer_forward(cfg, x, wr, w13, w2, lb, sb, ws13=ws13, ws2=ws2, want=want)
+    fcfg, fw = cfg, dict(w13=w13, w2=w2, ws13=ws13, ws2=ws2)
+    if name == "dsv3":
+        fcfg = cfg.replace(w_layout=1)
+        fw = {n: (moe.pack_kblock(t) if t is not None else None) for n, t in fw.items()}
+    yt, ext, saved = moe.layer_forward_train(fcfg, x, wr, fw["w13"], fw["w2"], lb, sb,
+                                             ws13=fw["ws13"], ws2=fw["ws2"], want=want)
+    torch.cuda.synchronize()
+    assert torch.equal(y, yt)
+    for n in want:
+        assert torch.equal(ex[n], ext[n]), n
+    args = (cfg, x, wr, ex["logits"], ex["topk_idx"], ex["topk_gate"], w13, w2, dy)
+    kw = dict(logit_bias=lb, ws13=ws13, ws2=ws2, want_dlogits=True)
+    g = moe.layer_backward(*args, **kw)
+    gs = moe.layer_backward_saved(*args, saved, **kw)
+    # a second saved backward after the buffer was used once: it is only read
+    gs2 = moe.layer_backward_saved(*args, saved, **kw)
+    torch.cuda.synchronize()
+    for n, t in g.items():
+        if t is None:
+            assert gs[n] is None, n
+            continue
+        assert torch.equal(t, gs[n]), n
+        assert torch.equal(t, gs2[n]), n
+
