@@ -89,9 +89,13 @@ struct BwdArgs {
     const uint8_t* zero;
 };
 
-// swizzle of the 16-byte chunks of a [k][128] operand row: the four rows one transposing read
-// touches land in four different 32-byte bank groups
-MOE_DEVICE int swz_t(int k) { return 2 * (k & 3); }
+// swizzle of the 16-byte chunks of a [k][cols] operand row (a row is a whole number of
+// 256-byte bank lines, so a chunk's banks depend on its index mod 16 alone). A transposing
+// read is served 32 lanes at a time: 64 bytes (4 chunks) of each of four consecutive k rows.
+// XOR-ing the chunk index with 4 (k & 3) puts those four rows on four different 64-byte
+// bank groups (with 2 (k & 3), rows k and k ^ 1 shared one and the reads were 2-way
+// conflicted).
+MOE_DEVICE int swz_t(int k) { return 4 * (k & 3); }
 
 MOE_DEVICE bf16x8_t tr_frag(const uint8_t* lo, const uint8_t* hi) {
     typedef short s4 __attribute__((ext_vector_type(4)));
