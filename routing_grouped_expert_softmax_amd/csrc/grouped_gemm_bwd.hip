@@ -126,8 +126,20 @@ MOE_DEVICE void bwd_tile(const BwdArgs& ba, int L, uint8_t* lds) {
             Mg = ba.offsets[g + 1] - rbase;
             m0 = mt * kBM;
         } else {
-            const int4 ti = ba.tiles[L / ba.ntn];
-            nt = L % ba.ntn;
+            // a group's M tiles go in bands of kBand, M fastest within a band, so the tiles
+            // that read one weight tile run side by side on one XCD and the later ones find
+            // it in L2 (N fastest: every M tile of an expert streamed its weights again)
+            constexpr int kBand = 4;
+            const int ntn = ba.ntn;
+            const int4 t0 = ba.tiles[L / ntn];                       // some tile of L's group
+            const int mt0 = L / ntn - t0.y / tile_span(t0.z, kBM);   // the group's first tile
+            const int me = (t0.z + kBM - 1) / kBM;                   // the group's M tiles
+            const int local = L - mt0 * ntn;
+            const int band = local / (kBand * ntn) * kBand;
+            const int mb = me - band < kBand ? me - band : kBand;
+            const int r = local - band * ntn;
+            const int4 ti = ba.tiles[mt0 + band + r % mb];
+            nt = r / mb;
             g = ti.x & 0xFFFFF;
             m0 = ti.y;
             Mg = tile_end(ti.y, ti.z, kBM);   // the tile's end row within the group
