@@ -323,7 +323,13 @@ MOE_DEVICE void bwd_tile(const BwdArgs& ba, int L, uint8_t* lds) {
             const int row = c / kChunks, cc = c % kChunks;
             const uint4 v = *(const uint4*)(ep + row * kEpStride + cc * 8);
             const size_t orow = RAGGED_K ? (size_t)mt * kBM + row : (size_t)rbase + m0 + row;
-            *(uint4*)(out + orow * ba.out_ld + (size_t)nt * kBN + cc * 8) = v;
+            uint16_t* dst = out + orow * ba.out_ld + (size_t)nt * kBN + cc * 8;
+            // weight gradients (read by no later kernel here) bypass the caches on the way out
+            if (RAGGED_K)
+                __builtin_nontemporal_store(i32x4_t{(int)v.x, (int)v.y, (int)v.z, (int)v.w},
+                                            (i32x4_t*)dst);
+            else
+                *(uint4*)dst = v;
         }
         return;
     }
