@@ -18,6 +18,8 @@
 // The weight gradients run K (an expert's rows) to a ragged end: rows past it are loaded
 // from a zeroed page of the workspace. dg is reduced per tile and then over tiles in a fixed
 // order, so the whole backward is deterministic (no atomics).
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -473,13 +475,47 @@ BwdWs carve_bwd(void* ws, int A, int E, int F) {
     return w;
 }
 
+// The weight gradients run beside the data gradients (the W/D split: dW needs only the
+// activations and dZ, so it need not wait for dx): on a side stream of the library's, joined
+// to the caller's stream by events. The data-gradient kernels stream weights from HBM, the
+// weight-gradient kernels mostly write dW, so the two overlap. One side stream and three
+// events per device, created on first use (default priority); the mutex keeps two host
+// threads from interleaving their records of the shared events.
+constexpr int kMaxDevices = 64;
+struct SideRes {
+    hipStream_t side = nullptr;
+    hipEvent_t ev[3] = {};
+};
+std::mutex g_side_mu;
+SideRes g_side[kMaxDevices];
+
+hipError_t side_res(SideRes** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    SideRes& r = g_side[dev];
+    if (!r.side) {
+        e = hipStreamCreateWithFlags(&r.side, hipStreamNonBlocking);
+        for (int i = 0; i < 3 && e == hipSuccess; ++i)
+            e = hipEventCreateWithFlags(&r.ev[i], hipEventDisableTiming);
+        if (e != hipSuccess) return e;
+    }
+    *out = &r;
+    return hipSuccess;
+}
+
 template <class CF>
 hipError_t bwd_all(const BwdWs& w, const void* dy_perm, const void* x_perm, const void* z,
                    const void* act, const float* gate_perm, const int32_t* offsets,
                    const void* w13, const void* w2, int A, int E, int H, int F, void* dx_perm,
                    void* dw13, void* dw2, float* dgate_perm, hipStream_t s) {
     constexpr int kBM = CF::BM, kBN = CF::BN;
-    hipError_t e = launch_schedule(offsets, E, kBM, w.sched, s);
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    SideRes* sr = nullptr;
+    hipError_t e = side_res(&sr);
+    if (e != hipSuccess) return e;
+    e = launch_schedule(offsets, E, kBM, w.sched, s);
     if (e != hipSuccess) return e;
     const int4* tiles = (const int4*)((char*)w.sched + 256);
     const int* total = (const int*)w.sched;
@@ -489,48 +525,62 @@ hipError_t bwd_all(const BwdWs& w, const void* dy_perm, const void* x_perm, cons
     const uint16_t* W13 = (const uint16_t*)w13;
     const uint16_t* W2 = (const uint16_t*)w2;
     auto round8 = [](size_t n) { return (int)((n + 7) / 8 * 8); };
+    // fork: the side stream starts after everything the caller queued (inputs, zero page)
+    e = hipEventRecord(sr->ev[0], s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(sr->side, sr->ev[0], 0);
+    if (e != hipSuccess) return e;
 
-    // dgrad 1: dA [A, F] = dy_perm W2_e (W2_e stored [H][F]: K rows) -> dZ, dg partials
-    BwdArgs d1 = {};
-    d1.a = {DY, (size_t)H, 0};
-    d1.b = {W2, (size_t)F, (size_t)H * F};
-    d1.offsets = offsets; d1.tiles = tiles; d1.total = total;
-    d1.N = F; d1.K = H; d1.ntn = F / kBN; d1.groups = E;
-    d1.z = (const uint16_t*)z; d1.gate = gate_perm; d1.dz = w.dz; d1.dg_part = w.dg_part;
-    d1.F = F; d1.zero = w.zero;
-    e = run_bwd<CF, OPK, OPT, 0, 1>(d1, round8(max_tiles * d1.ntn), s);
-    if (e != hipSuccess) return e;
-    if (dgate_perm) {
-        dg_reduce_kernel<<<(A + 255) / 256, 256, 0, s>>>(w.dg_part, A, F / kBN, dgate_perm);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    // dgrad 2: dx_perm [A, H] = dZ W13_e (W13_e stored [2F][H]: K rows)
-    BwdArgs d2 = {};
-    d2.a = {w.dz, (size_t)2 * F, 0};
-    d2.b = {W13, (size_t)H, (size_t)2 * F * H};
-    d2.offsets = offsets; d2.tiles = tiles; d2.total = total;
-    d2.N = H; d2.K = 2 * F; d2.ntn = H / kBN; d2.groups = E;
-    d2.out = (uint16_t*)dx_perm; d2.out_ld = H; d2.zero = w.zero;
-    e = run_bwd<CF, OPK, OPT, 0, 0>(d2, round8(max_tiles * d2.ntn), s);
-    if (e != hipSuccess) return e;
-    // wgrad 2: dW2_e [H, F] = dy_perm[R_e]^T act[R_e]
+    // wgrad 2 (side): dW2_e [H, F] = dy_perm[R_e]^T act[R_e]
     BwdArgs w2a = {};
     w2a.a = {DY, (size_t)H, 0};
     w2a.b = {(const uint16_t*)act, (size_t)F, 0};
     w2a.offsets = offsets; w2a.M = H; w2a.N = F; w2a.ntm = H / CF::BM; w2a.ntn = F / CF::BN;
     w2a.groups = E; w2a.out = (uint16_t*)dw2; w2a.out_ld = F; w2a.out_gstride = (size_t)H * F;
     w2a.zero = w.zero;
-    e = run_bwd<CF, OPT, OPT, 1, 0>(w2a, round8((size_t)E * w2a.ntm * w2a.ntn), s);
-    if (e != hipSuccess) return e;
-    // wgrad 1: dW13_e [2F, H] = dZ[R_e]^T x_perm[R_e]
-    BwdArgs w1 = {};
-    w1.a = {w.dz, (size_t)2 * F, 0};
-    w1.b = {X, (size_t)H, 0};
-    w1.offsets = offsets; w1.M = 2 * F; w1.N = H; w1.ntm = 2 * F / CF::BM; w1.ntn = H / CF::BN;
-    w1.groups = E; w1.out = (uint16_t*)dw13; w1.out_ld = H; w1.out_gstride = (size_t)2 * F * H;
-    w1.zero = w.zero;
-    return run_bwd<CF, OPT, OPT, 1, 0>(w1, round8((size_t)E * w1.ntm * w1.ntn), s);
+    e = run_bwd<CF, OPT, OPT, 1, 0>(w2a, round8((size_t)E * w2a.ntm * w2a.ntn), sr->side);
+    // dgrad 1: dA [A, F] = dy_perm W2_e (W2_e stored [H][F]: K rows) -> dZ, dg partials
+    if (e == hipSuccess) {
+        BwdArgs d1 = {};
+        d1.a = {DY, (size_t)H, 0};
+        d1.b = {W2, (size_t)F, (size_t)H * F};
+        d1.offsets = offsets; d1.tiles = tiles; d1.total = total;
+        d1.N = F; d1.K = H; d1.ntn = F / kBN; d1.groups = E;
+        d1.z = (const uint16_t*)z; d1.gate = gate_perm; d1.dz = w.dz; d1.dg_part = w.dg_part;
+        d1.F = F; d1.zero = w.zero;
+        e = run_bwd<CF, OPK, OPT, 0, 1>(d1, round8(max_tiles * d1.ntn), s);
+    }
+    if (e == hipSuccess && dgate_perm) {
+        dg_reduce_kernel<<<(A + 255) / 256, 256, 0, s>>>(w.dg_part, A, F / kBN, dgate_perm);
+        e = hipGetLastError();
+    }
+    // dZ is ready: wgrad 1 (side) and dgrad 2 (caller's stream)
+    if (e == hipSuccess) e = hipEventRecord(sr->ev[1], s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(sr->side, sr->ev[1], 0);
+    if (e == hipSuccess) {
+        // wgrad 1: dW13_e [2F, H] = dZ[R_e]^T x_perm[R_e]
+        BwdArgs w1 = {};
+        w1.a = {w.dz, (size_t)2 * F, 0};
+        w1.b = {X, (size_t)H, 0};
+        w1.offsets = offsets; w1.M = 2 * F; w1.N = H; w1.ntm = 2 * F / CF::BM;
+        w1.ntn = H / CF::BN; w1.groups = E; w1.out = (uint16_t*)dw13; w1.out_ld = H;
+        w1.out_gstride = (size_t)2 * F * H; w1.zero = w.zero;
+        e = run_bwd<CF, OPT, OPT, 1, 0>(w1, round8((size_t)E * w1.ntm * w1.ntn), sr->side);
+    }
+    if (e == hipSuccess) {
+        // dgrad 2: dx_perm [A, H] = dZ W13_e (W13_e stored [2F][H]: K rows)
+        BwdArgs d2 = {};
+        d2.a = {w.dz, (size_t)2 * F, 0};
+        d2.b = {W13, (size_t)H, (size_t)2 * F * H};
+        d2.offsets = offsets; d2.tiles = tiles; d2.total = total;
+        d2.N = H; d2.K = 2 * F; d2.ntn = H / kBN; d2.groups = E;
+        d2.out = (uint16_t*)dx_perm; d2.out_ld = H; d2.zero = w.zero;
+        e = run_bwd<CF, OPK, OPT, 0, 0>(d2, round8(max_tiles * d2.ntn), s);
+    }
+    // join, also after a failed launch, so that nothing queued on the side stream outlives
+    // the caller's view of this call
+    hipError_t j = hipEventRecord(sr->ev[2], sr->side);
+    if (j == hipSuccess) j = hipStreamWaitEvent(s, sr->ev[2], 0);
+    return e != hipSuccess ? e : j;
 }
 
 // Router weight and data gradients as one-group GEMMs of the same kernel:

@@ -27,6 +27,8 @@ CASES = {
                            w_dtype=BF, backward=True),
     # softmax router, no shared expert, F not a multiple of 256 (128 x 128 tiles)
     "qwen3": mi.scaled(mi.CONFIGS["qwen3_bf16"], T=200, H=256, F=384),
+    # a shared expert narrower than the routed ones (its GEMMs run as launches of their own)
+    "dsv3_narrow_shared": mi.scaled(mi.CONFIGS["dsv3_bf16"], T=160, H=256, F=256, shared_F=128),
 }
 
 
