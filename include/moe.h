@@ -20,10 +20,10 @@
  *  - Work is enqueued on `stream` and the call returns at once. The library never
  *    synchronises a stream or the device and never copies device -> host: expert counts
  *    and offsets stay on the device. The backward calls (moe_grouped_gemm_swiglu_bwd,
- *    moe_layer_backward, moe_layer_backward_saved) run their expert weight gradients on a
- *    side stream of the library's, forked from `stream` and joined back to it with events
- *    (the weight gradients overlap the data gradients), so all of a call's work is still
- *    ordered on `stream`.
+ *    moe_layer_backward, moe_layer_backward_saved) run their expert weight gradients on
+ *    two side streams of the library's, forked from `stream` and joined back to it with
+ *    events (the weight gradients overlap the data gradients), so all of a call's work is
+ *    still ordered on `stream`.
  *  - Arguments are validated on the host before anything is enqueued; on an invalid
  *    argument nothing is launched and MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED or
  *    MOE_ERR_WORKSPACE is returned. A failed launch returns MOE_ERR_HIP. Expert indices
@@ -34,8 +34,8 @@
  *    per range and adds them in a fixed range order.
  *  - The library holds no state between calls except the instrumentation switch of
  *    moe_set_stage_events (per host thread; it changes no result) and, per device, the
- *    backward's side stream and three events (created on the first backward call on that
- *    device, default priority, kept until the process ends; they carry no data).
+ *    backward's two side streams and four events (created on the first backward call on
+ *    that device, default priority, kept until the process ends; they carry no data).
  *  - Layouts: every matrix keeps K (its last index) contiguous, so each expert GEMM is
  *    C = A B^T. A matrix [R, C] is either row-major (MOE_LAYOUT_ROWS) or K-blocked
  *    (MOE_LAYOUT_KBLOCK): stored as [C * eb / 64][R][64 bytes] (eb = element bytes), i.e.

@@ -476,15 +476,17 @@ BwdWs carve_bwd(void* ws, int A, int E, int F) {
 }
 
 // The weight gradients run beside the data gradients (the W/D split: dW needs only the
-// activations and dZ, so it need not wait for dx): on a side stream of the library's, joined
-// to the caller's stream by events. The data-gradient kernels stream weights from HBM, the
-// weight-gradient kernels mostly write dW, so the two overlap. One side stream and three
-// events per device, created on first use (default priority); the mutex keeps two host
-// threads from interleaving their records of the shared events.
+// activations and dZ, so it need not wait for dx): dW2 on one side stream from the start,
+// dW13 on another once dZ exists, both joined back to the caller's stream by events. The
+// data-gradient kernels stream weights from HBM, the weight-gradient kernels mostly write
+// dW, so they overlap (dW13 on the first side stream too would wait for dW2, which the
+// data gradients slow down). Two side streams and four events per device, created on first
+// use (default priority); the mutex keeps two host threads from interleaving their records
+// of the shared events.
 constexpr int kMaxDevices = 64;
 struct SideRes {
-    hipStream_t side = nullptr;
-    hipEvent_t ev[3] = {};
+    hipStream_t side = nullptr, side2 = nullptr;
+    hipEvent_t ev[4] = {};
 };
 std::mutex g_side_mu;
 SideRes g_side[kMaxDevices];
@@ -497,7 +499,8 @@ hipError_t side_res(SideRes** out) {
     SideRes& r = g_side[dev];
     if (!r.side) {
         e = hipStreamCreateWithFlags(&r.side, hipStreamNonBlocking);
-        for (int i = 0; i < 3 && e == hipSuccess; ++i)
+        if (e == hipSuccess) e = hipStreamCreateWithFlags(&r.side2, hipStreamNonBlocking);
+        for (int i = 0; i < 4 && e == hipSuccess; ++i)
             e = hipEventCreateWithFlags(&r.ev[i], hipEventDisableTiming);
         if (e != hipSuccess) return e;
     }
@@ -553,9 +556,9 @@ hipError_t bwd_all(const BwdWs& w, const void* dy_perm, const void* x_perm, cons
         dg_reduce_kernel<<<(A + 255) / 256, 256, 0, s>>>(w.dg_part, A, F / kBN, dgate_perm);
         e = hipGetLastError();
     }
-    // dZ is ready: wgrad 1 (side) and dgrad 2 (caller's stream)
+    // dZ is ready: wgrad 1 (second side stream) and dgrad 2 (caller's stream)
     if (e == hipSuccess) e = hipEventRecord(sr->ev[1], s);
-    if (e == hipSuccess) e = hipStreamWaitEvent(sr->side, sr->ev[1], 0);
+    if (e == hipSuccess) e = hipStreamWaitEvent(sr->side2, sr->ev[1], 0);
     if (e == hipSuccess) {
         // wgrad 1: dW13_e [2F, H] = dZ[R_e]^T x_perm[R_e]
         BwdArgs w1 = {};
@@ -564,7 +567,7 @@ hipError_t bwd_all(const BwdWs& w, const void* dy_perm, const void* x_perm, cons
         w1.offsets = offsets; w1.M = 2 * F; w1.N = H; w1.ntm = 2 * F / CF::BM;
         w1.ntn = H / CF::BN; w1.groups = E; w1.out = (uint16_t*)dw13; w1.out_ld = H;
         w1.out_gstride = (size_t)2 * F * H; w1.zero = w.zero;
-        e = run_bwd<CF, OPT, OPT, 1, 0>(w1, round8((size_t)E * w1.ntm * w1.ntn), sr->side);
+        e = run_bwd<CF, OPT, OPT, 1, 0>(w1, round8((size_t)E * w1.ntm * w1.ntn), sr->side2);
     }
     if (e == hipSuccess) {
         // dgrad 2: dx_perm [A, H] = dZ W13_e (W13_e stored [2F][H]: K rows)
@@ -580,6 +583,8 @@ hipError_t bwd_all(const BwdWs& w, const void* dy_perm, const void* x_perm, cons
     // the caller's view of this call
     hipError_t j = hipEventRecord(sr->ev[2], sr->side);
     if (j == hipSuccess) j = hipStreamWaitEvent(s, sr->ev[2], 0);
+    if (j == hipSuccess) j = hipEventRecord(sr->ev[3], sr->side2);
+    if (j == hipSuccess) j = hipStreamWaitEvent(s, sr->ev[3], 0);
     return e != hipSuccess ? e : j;
 }
 
