@@ -843,14 +843,22 @@ static int layer_backward_impl(const moe_config* cfg, const void* x, const void*
                       T, 0, 0, 0, nullptr};
         e = moe::launch_grouped_gemm(0, MOE_BF16, &s1, 1, T, 2 * sF, H, L.sched, stream);
     }
-    // expert gradients (routed: dgate through the fold; shared: gate 1)
+    // expert gradients (routed: dgate through the fold; shared: gate 1). Their weight
+    // gradients run on the library's side streams, joined once at the end: nothing after
+    // them reads dW or writes what they read, so the shared expert, the router backward and
+    // the combine need not wait for them.
+    struct SideLock {
+        SideLock() { moe::bwd_side_lock(); }
+        ~SideLock() { moe::bwd_side_unlock(); }
+    } side_lock;
     if (e == hipSuccess)
         e = moe::launch_grouped_gemm_bwd(L.dy_perm, L.x_perm, z, act, L.gate_perm, L.offsets,
                                          w13, w2, A, E, H, F, L.dx_perm, dw13, dw2,
-                                         L.dgate_perm, L.bws, stream);
+                                         L.dgate_perm, L.bws, stream, false);
     if (e == hipSuccess && sF)
         e = moe::launch_grouped_gemm_bwd(dy, x, zs, acts, nullptr, L.offs_one, ws13, ws2, T, 1,
-                                         H, sF, L.dxs, dws13, dws2, nullptr, L.bws_s, stream);
+                                         H, sF, L.dxs, dws13, dws2, nullptr, L.bws_s, stream,
+                                         false);
     // gates -> logits -> router weight and x
     if (e == hipSuccess)
         e = moe::launch_route_backward(cfg->router, logits, logit_bias, topk_idx, topk_gate,
@@ -863,6 +871,9 @@ static int layer_backward_impl(const moe_config* cfg, const void* x, const void*
         e = moe::launch_combine(MOE_BF16, L.dx_perm, L.pos, sF ? L.dxs : nullptr, T, H, k, dx,
                                 stream);
     if (e == hipSuccess) e = moe::launch_add_bf16(dx, L.dxr, (int64_t)T * H, stream);
+    // join the weight gradients (also after a failure, so no side work outlives the call)
+    const hipError_t j = moe::bwd_side_join(stream);
+    if (e == hipSuccess) e = j;
     return hip_status(e);
 }
 

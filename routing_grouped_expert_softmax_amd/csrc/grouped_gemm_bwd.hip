@@ -482,13 +482,15 @@ BwdWs carve_bwd(void* ws, int A, int E, int F) {
 // dW, so they overlap (dW13 on the first side stream too would wait for dW2, which the
 // data gradients slow down). Two side streams and four events per device, created on first
 // use (default priority); the mutex keeps two host threads from interleaving their records
-// of the shared events.
+// of the shared events. A caller that queues several backward launches may defer the join
+// (join = false) and join once at its end, holding the lock across them (bwd_side_lock), so
+// that its next kernels need not wait for the weight gradients.
 constexpr int kMaxDevices = 64;
 struct SideRes {
     hipStream_t side = nullptr, side2 = nullptr;
     hipEvent_t ev[4] = {};
 };
-std::mutex g_side_mu;
+std::recursive_mutex g_side_mu;
 SideRes g_side[kMaxDevices];
 
 hipError_t side_res(SideRes** out) {
@@ -512,9 +514,9 @@ template <class CF>
 hipError_t bwd_all(const BwdWs& w, const void* dy_perm, const void* x_perm, const void* z,
                    const void* act, const float* gate_perm, const int32_t* offsets,
                    const void* w13, const void* w2, int A, int E, int H, int F, void* dx_perm,
-                   void* dw13, void* dw2, float* dgate_perm, hipStream_t s) {
+                   void* dw13, void* dw2, float* dgate_perm, hipStream_t s, bool join) {
     constexpr int kBM = CF::BM, kBN = CF::BN;
-    std::lock_guard<std::mutex> lock(g_side_mu);
+    std::lock_guard<std::recursive_mutex> lock(g_side_mu);
     SideRes* sr = nullptr;
     hipError_t e = side_res(&sr);
     if (e != hipSuccess) return e;
@@ -579,8 +581,9 @@ hipError_t bwd_all(const BwdWs& w, const void* dy_perm, const void* x_perm, cons
         d2.out = (uint16_t*)dx_perm; d2.out_ld = H; d2.zero = w.zero;
         e = run_bwd<CF, OPK, OPT, 0, 0>(d2, round8(max_tiles * d2.ntn), s);
     }
-    // join, also after a failed launch, so that nothing queued on the side stream outlives
-    // the caller's view of this call
+    // join (deferred when asked, unless a launch failed), so that nothing queued on the side
+    // streams outlives the caller's view of this call
+    if (!join && e == hipSuccess) return e;
     hipError_t j = hipEventRecord(sr->ev[2], sr->side);
     if (j == hipSuccess) j = hipStreamWaitEvent(s, sr->ev[2], 0);
     if (j == hipSuccess) j = hipEventRecord(sr->ev[3], sr->side2);
@@ -626,19 +629,34 @@ size_t bwd_ws_bytes(int T, int k, int E, int H, int F) {
     return carve_bwd(nullptr, T * k, E, F).total;
 }
 
+void bwd_side_lock() { g_side_mu.lock(); }
+void bwd_side_unlock() { g_side_mu.unlock(); }
+
+hipError_t bwd_side_join(hipStream_t s) {
+    std::lock_guard<std::recursive_mutex> lock(g_side_mu);
+    SideRes* sr = nullptr;
+    hipError_t e = side_res(&sr);
+    if (e == hipSuccess) e = hipEventRecord(sr->ev[2], sr->side);
+    if (e == hipSuccess) e = hipStreamWaitEvent(s, sr->ev[2], 0);
+    if (e == hipSuccess) e = hipEventRecord(sr->ev[3], sr->side2);
+    if (e == hipSuccess) e = hipStreamWaitEvent(s, sr->ev[3], 0);
+    return e;
+}
+
 hipError_t launch_grouped_gemm_bwd(const void* dy_perm, const void* x_perm, const void* z,
                                    const void* act, const float* gate_perm,
                                    const int32_t* offsets, const void* w13, const void* w2,
                                    int A, int E, int H, int F, void* dx_perm, void* dw13,
-                                   void* dw2, float* dgate_perm, void* ws, hipStream_t s) {
+                                   void* dw2, float* dgate_perm, void* ws, hipStream_t s,
+                                   bool join) {
     BwdWs w = carve_bwd(ws, A, E, F);
     zero_fill_kernel<<<1, 256, 0, s>>>((uint32_t*)w.zero, kZeroBytes / 4);
     // 256 x 256 tiles when every GEMM dimension divides by 256 (F, 2F and H), else 128 x 128
     if (F % BwdLarge::BN == 0 && H % BwdLarge::BN == 0 && MOE_BWD_LARGE)
         return bwd_all<BwdLarge>(w, dy_perm, x_perm, z, act, gate_perm, offsets, w13, w2, A, E,
-                                 H, F, dx_perm, dw13, dw2, dgate_perm, s);
+                                 H, F, dx_perm, dw13, dw2, dgate_perm, s, join);
     return bwd_all<BwdSmall>(w, dy_perm, x_perm, z, act, gate_perm, offsets, w13, w2, A, E, H,
-                             F, dx_perm, dw13, dw2, dgate_perm, s);
+                             F, dx_perm, dw13, dw2, dgate_perm, s, join);
 }
 
 size_t router_bwd_ws_bytes(int T) {
