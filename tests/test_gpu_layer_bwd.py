@@ -128,3 +128,49 @@ def test_training_pair_bit_identical(moe, name):
         assert torch.equal(t, gs[n]), n
         assert torch.equal(t, gs2[n]), n
 
+
+
+def test_concurrent_backwards_on_two_streams(moe):
+    """The backward's weight gradients run on side streams shared by every caller on a
+    device. Two host threads, each queuing layer backwards (one recomputing, one from saved
+    activations) on a stream of its own, must get exactly what the same calls give when run
+    one after the other."""
+    import threading
+    cfg = CASES["dsv3"]
+    inp = mi.make_inputs(cfg)
+    x, wr, w13, w2 = inp.x.cuda(), inp.w_router.cuda(), inp.w13.cuda(), inp.w2.cuda()
+    ws13, ws2, sb = to_dev(inp.ws13), to_dev(inp.ws2), to_dev(inp.sel_bias)
+    want = ("logits", "topk_idx", "topk_gate")
+    _, ex, saved = moe.layer_forward_train(cfg, x, wr, w13, w2, None, sb, ws13=ws13, ws2=ws2,
+                                           want=want)
+    rng = np.random.default_rng(13)
+    dys = [torch.from_numpy(rng.standard_normal((cfg.T, cfg.H)).astype(np.float32)).to(
+        torch.bfloat16).cuda() for _ in range(2)]
+    args = lambda dy: (cfg, x, wr, ex["logits"], ex["topk_idx"], ex["topk_gate"], w13, w2, dy)
+    kw = dict(ws13=ws13, ws2=ws2)
+    runs = [lambda ws=None, stream=None: moe.layer_backward(*args(dys[0]), ws=ws, stream=stream,
+                                                            **kw),
+            lambda ws=None, stream=None: moe.layer_backward_saved(*args(dys[1]), saved, ws=ws,
+                                                                  stream=stream, **kw)]
+    ref = [r() for r in runs]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in runs]
+    wss = [moe.workspace(cfg, moe.OP_LAYER_BACKWARD) for _ in runs]
+    torch.cuda.synchronize()
+    out = [[None] * 3 for _ in runs]
+
+    def worker(i):
+        with torch.cuda.stream(streams[i]):
+            for rep in range(3):
+                out[i][rep] = runs[i](ws=wss[i], stream=streams[i])
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(runs))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    for i in range(len(runs)):
+        for rep in range(3):
+            for n, t in ref[i].items():
+                if t is not None:
+                    assert torch.equal(t, out[i][rep][n]), (i, rep, n)
