@@ -557,7 +557,7 @@ def main():
     w13_bf, w2_bf, ws13_bf, ws2_bf = w13, w2, ws13, ws2     # row-major bf16 (backward)
     # the whole-layer backward (bf16) is timed with the bf16 and e4m3 workloads
     layer_bwd = (not args.no_layer_bwd and cfg.act_dtype == mi.BF16 and cfg.E % 128 == 0
-                 and cfg.w_dtype != mi.MXFP8)
+                 and cfg.w_dtype != mi.MXFP8 and cfg.capacity_factor == 0)   # dropless only
     if cfg.w_dtype == mi.MXFP8:   # E8M0 scales per 1 x 32 along K, quantised once
         w13, sc["w13_scales"] = moe.quantize_mx(w13)
         w2, sc["w2_scales"] = moe.quantize_mx(w2)
