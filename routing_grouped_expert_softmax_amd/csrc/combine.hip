@@ -185,12 +185,9 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict_
     for (int off = 1; off < 16; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
     float sc = e4m3_scale(amax);
     if (!ok) return;
-    uint32_t c[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) c[i] = e4m3_rne_sat(f[i] / sc);
     uint2 packed;
-    packed.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-    packed.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+    packed.x = e4m3x4(f[0] / sc, f[1] / sc, f[2] / sc, f[3] / sc);
+    packed.y = e4m3x4(f[4] / sc, f[5] / sc, f[6] / sc, f[7] / sc);
     *(uint2*)(q + base) = packed;
     if (sub == 0) scales[gblk] = sc;
 }
@@ -218,12 +215,9 @@ __global__ __launch_bounds__(256) void quant_mx_kernel(const void* __restrict__ 
     if (!ok) return;
     const int X = mx_exponent(amax);
     const float inv = exp2_neg(X);
-    uint32_t c[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) c[i] = e4m3_rne_sat(f[i] * inv);
     uint2 packed;
-    packed.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-    packed.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+    packed.x = e4m3x4(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv);
+    packed.y = e4m3x4(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv);
     *(uint2*)(q + base) = packed;
     if (sub == 0) {
         size_t si = (size_t)blk;
@@ -287,9 +281,8 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(const void* __restric
         uint32_t w[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-            w[u] = e4m3_rne_sat(f[i + 4 * u] / sc) | (e4m3_rne_sat(f[i + 4 * u + 1] / sc) << 8) |
-                   (e4m3_rne_sat(f[i + 4 * u + 2] / sc) << 16) |
-                   (e4m3_rne_sat(f[i + 4 * u + 3] / sc) << 24);
+            w[u] = e4m3x4(f[i + 4 * u] / sc, f[i + 4 * u + 1] / sc, f[i + 4 * u + 2] / sc,
+                          f[i + 4 * u + 3] / sc);
         *(uint4*)(q + base + i) = make_uint4(w[0], w[1], w[2], w[3]);
     }
     if (threadIdx.x == 0) scales[blk] = sc;

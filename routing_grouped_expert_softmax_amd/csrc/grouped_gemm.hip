@@ -1194,9 +1194,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_e4m3_kernel(GemmArgs ga) {
         uint32_t codes[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-            codes[q] = e4m3_rne_sat(av[i][4 * q] / sc) | (e4m3_rne_sat(av[i][4 * q + 1] / sc) << 8) |
-                       (e4m3_rne_sat(av[i][4 * q + 2] / sc) << 16) |
-                       (e4m3_rne_sat(av[i][4 * q + 3] / sc) << 24);
+            codes[q] = e4m3x4(av[i][4 * q] / sc, av[i][4 * q + 1] / sc, av[i][4 * q + 2] / sc,
+                              av[i][4 * q + 3] / sc);
 #pragma unroll
         for (int qp = 0; qp < 4; qp += 2) {
             const uint2 v = pair_runs_x2(codes[qp], codes[qp + 1]);
@@ -1511,9 +1510,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mx_kernel(GemmArgs ga) {
         uint32_t codes[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-            codes[q] = e4m3_rne_sat(v[4 * q] * inv) | (e4m3_rne_sat(v[4 * q + 1] * inv) << 8) |
-                       (e4m3_rne_sat(v[4 * q + 2] * inv) << 16) |
-                       (e4m3_rne_sat(v[4 * q + 3] * inv) << 24);
+            codes[q] = e4m3x4(v[4 * q] * inv, v[4 * q + 1] * inv, v[4 * q + 2] * inv,
+                              v[4 * q + 3] * inv);
 #pragma unroll
         for (int qp = 0; qp < 4; qp += 2) {
             const uint2 w = pair_runs_x2(codes[qp], codes[qp + 1]);

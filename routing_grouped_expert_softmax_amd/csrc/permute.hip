@@ -212,23 +212,20 @@ __global__ __launch_bounds__(256) void perm_quant_copy_kernel(
         for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
 #pragma unroll
         for (int off = 1; off < kLanesPerBlk; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-        uint32_t q[8];
+        uint2 packed;
         Sc sc;
         if (MX) {
             const int X = mx_exponent(amax);
             const float inv = exp2_neg(X);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) q[i] = e4m3_rne_sat(f[i] * inv);
+            packed.x = e4m3x4(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv);
+            packed.y = e4m3x4(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv);
             sc = (Sc)(X + 127);
         } else {
             const float s = e4m3_scale(amax);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) q[i] = e4m3_rne_sat(f[i] / s);
+            packed.x = e4m3x4(f[0] / s, f[1] / s, f[2] / s, f[3] / s);
+            packed.y = e4m3x4(f[4] / s, f[5] / s, f[6] / s, f[7] / s);
             sc = (Sc)s;
         }
-        uint2 packed;
-        packed.x = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
-        packed.y = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
         const int blk = c / kLanesPerBlk;
         const bool leader = (c % kLanesPerBlk) == 0;
         if (x_q && ok) {
