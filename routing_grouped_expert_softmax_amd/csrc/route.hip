@@ -201,43 +201,47 @@ __global__ __launch_bounds__(256) void route_sigmoid_group_kernel(
         stats_block_sum<VPL>(p, valid, E, lane, wave, prob_part);
         if (!valid) return;
     }
-    int kept = 0;
+    uint64_t kept_mask;           // bit g: group g is kept (the same in every lane)
     if (per == 32 && E == VPL * kWave) {
-        // groups are the 32-lane halves of the key registers (group 2 v + lane / 32 in v):
-        // the two largest keys of every group come from butterflies inside each half, all
-        // groups at once; then every lane ranks the group scores itself
+        // groups are the 32-lane halves of the key registers (group 2 v + lane / 32 in v).
+        // A group's score needs only the values of its two largest keys: the largest order
+        // key m1 (a butterfly of 32-bit maxima inside each half), and m1 again when it occurs
+        // twice in the group, else the largest of the others (a second butterfly).
         uint64_t gk[VPL];
 #pragma unroll
         for (int v = 0; v < VPL; ++v) {
-            const uint64_t rk = rank_key(key[v], v * kWave + lane);
-            uint64_t b1 = rk;
+            const uint32_t ok = float_order_key(key[v]);
+            uint32_t m1 = ok;
 #pragma unroll
-            for (int off = 1; off < 32; off <<= 1) {
-                const uint64_t o = __shfl_xor(b1, off);
-                b1 = o > b1 ? o : b1;
-            }
-            uint64_t b2 = rk == b1 ? 0 : rk;
+            for (int off = 1; off < 32; off <<= 1) m1 = max(m1, (uint32_t)__shfl_xor((int)m1, off));
+            const uint64_t eq = __ballot(ok == m1);
+            const int twice = __popc(lane < 32 ? (uint32_t)eq : (uint32_t)(eq >> 32)) >= 2;
+            uint32_t m2 = ok == m1 ? 0u : ok;
 #pragma unroll
-            for (int off = 1; off < 32; off <<= 1) {
-                const uint64_t o = __shfl_xor(b2, off);
-                b2 = o > b2 ? o : b2;
-            }
-            gk[v] = rank_key(rank_key_value(b1) + rank_key_value(b2), 2 * v + lane / 32);
+            for (int off = 1; off < 32; off <<= 1) m2 = max(m2, (uint32_t)__shfl_xor((int)m2, off));
+            if (twice) m2 = m1;
+            gk[v] = rank_key(float_from_order_key(m1) + float_from_order_key(m2),
+                             2 * v + lane / 32);
         }
-        // group g's key sits in register g / 2 of lane 32 (g % 2); kept: fewer than
-        // topk_groups groups rank above it (score desc, then group asc)
+        // group g's key sits in register g / 2 of lane 32 (g % 2). Lane l ranks group l % 8:
+        // it is kept when fewer than topk_groups groups rank above it (score desc, then
+        // group asc)
         uint64_t gkey[2 * VPL];
 #pragma unroll
-        for (int g = 0; g < 2 * VPL; ++g) gkey[g] = __shfl(gk[g / 2], (g % 2) * 32);
-        uint32_t kept_mask = 0;
-#pragma unroll
         for (int g = 0; g < 2 * VPL; ++g) {
-            int above = 0;
-#pragma unroll
-            for (int h = 0; h < 2 * VPL; ++h) above += gkey[h] > gkey[g];
-            kept_mask |= (above < topk_groups ? 1u : 0u) << g;
+            const uint64_t x = gk[g / 2];
+            const int src = (g % 2) * 32;
+            gkey[g] = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(x >> 32), src) << 32) |
+                      (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, src);
         }
-        kept = (lane < n_groups) ? (int)((kept_mask >> lane) & 1u) : 0;
+        const int myg = lane % (2 * VPL);
+        uint64_t mine = gkey[0];
+#pragma unroll
+        for (int g = 1; g < 2 * VPL; ++g) mine = myg == g ? gkey[g] : mine;
+        int above = 0;
+#pragma unroll
+        for (int h = 0; h < 2 * VPL; ++h) above += gkey[h] > mine;
+        kept_mask = __ballot(lane < 2 * VPL && above < topk_groups);
     } else {
     // group score = sum of the two largest keys of the group; lane g keeps group g's score
     uint64_t my_group_rk = 0;
@@ -263,6 +267,7 @@ __global__ __launch_bounds__(256) void route_sigmoid_group_kernel(
         if (lane == g) my_group_rk = rank_key(score, g);
     }
     // keep the topk_groups best groups; lane g learns whether group g is kept
+    int kept = 0;
     for (int i = 0; i < topk_groups; ++i) {
         uint64_t best = wave_max_u64(my_group_rk);
         if (lane == rank_key_index(best)) {
@@ -270,13 +275,14 @@ __global__ __launch_bounds__(256) void route_sigmoid_group_kernel(
             my_group_rk = 0;
         }
     }
+    kept_mask = __ballot(kept);
     }
     uint64_t rk[VPL];
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
         int e = v * kWave + lane;
         int g = (e < E ? e : 0) / per;
-        int keep = __shfl(kept, g);
+        const bool keep = (kept_mask >> g) & 1u;
         rk[v] = (e < E && keep) ? rank_key(key[v], e) : 0;
     }
     int e = wave_topk<VPL>(rk, k, lane);
