@@ -1,11 +1,14 @@
-"""moe_layer_forward captured into a HIP graph (torch.cuda.CUDAGraph) and replayed.
+"""moe_layer_forward and moe_layer_backward captured into a HIP graph (torch.cuda.CUDAGraph)
+and replayed.
 
-The whole path enqueues kernels on the caller's stream only: no host synchronisation, no
-device allocation, no memset, expert counts and offsets stay on the device. So it can be
-captured once and replayed with new input values. Each replay is checked bit for bit against
-an eager call on the same input (the path is deterministic), with eager work and stream
-synchronisations between the replays; the routing changes from one input to the next, so
-the replays also exercise the device-side tile schedule."""
+Neither path synchronises the host, allocates device memory or issues a memset; expert
+counts and offsets stay on the device. The forward enqueues on the caller's stream only; the
+backward also forks its weight gradients onto the library's side streams and joins them
+back, which a capture records as a fork and a join. So both can be captured once and
+replayed with new input values. Each replay is checked bit for bit against an eager call on
+the same input (the paths are deterministic), with eager work and stream synchronisations
+between the replays; in the forward the routing changes from one input to the next, so the
+replays also exercise the device-side tile schedule."""
 import pytest
 import torch
 
@@ -82,3 +85,53 @@ def test_layer_forward_graph_replays(moe, name):
         assert torch.equal(_bits(y_buf), _bits(y_ref)), rep
         print(f"   replay {rep}: identical to eager (max count {int(ex_ref['counts'].max())})",
               flush=True)
+
+
+def test_layer_backward_graph_replays(moe):
+    """moe_layer_backward captured into a graph: its weight gradients fork onto the library's
+    side streams and join back, which a capture records as a fork and a join of the graph.
+    Each replay with a new dY equals an eager backward on it, bit for bit."""
+    cfg = CASES["dsv3_small"]
+    inp = mi.make_inputs(cfg)
+    d = dict(w_router=inp.w_router.cuda(), w13=inp.w13.cuda(), w2=inp.w2.cuda(),
+             logit_bias=_dev(inp.logit_bias), sel_bias=_dev(inp.sel_bias),
+             ws13=_dev(inp.ws13), ws2=_dev(inp.ws2))
+    x = inp.x.cuda()
+    _, ex = moe.layer_forward(cfg, x, d["w_router"], d["w13"], d["w2"],
+                              logit_bias=d["logit_bias"], sel_bias=d["sel_bias"],
+                              ws13=d["ws13"], ws2=d["ws2"],
+                              want=("logits", "topk_idx", "topk_gate"))
+    dy_buf = torch.zeros(cfg.T, cfg.H, dtype=torch.bfloat16, device="cuda")
+    ws = moe.workspace(cfg, moe.OP_LAYER_BACKWARD, "cuda")
+
+    def backward(dy, ws=None):
+        return moe.layer_backward(cfg, x, d["w_router"], ex["logits"], ex["topk_idx"],
+                                  ex["topk_gate"], d["w13"], d["w2"], dy,
+                                  logit_bias=d["logit_bias"], ws13=d["ws13"], ws2=d["ws2"],
+                                  ws=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):                  # warm-up outside the capture
+        for _ in range(2):
+            backward(dy_buf, ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        g_out = backward(dy_buf, ws)
+    torch.cuda.synchronize()
+
+    gen = torch.Generator().manual_seed(20261204)
+    for rep in range(3):
+        dy_new = torch.randn(cfg.T, cfg.H, generator=gen).to(torch.bfloat16).cuda()
+        dy_buf.copy_(dy_new)
+        ref = backward(dy_new.clone())             # eager, own buffers and workspace
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for n, t in ref.items():
+            if t is not None:
+                assert torch.equal(_bits(g_out[n]), _bits(t)), (rep, n)
+        print(f"   backward replay {rep}: identical to eager", flush=True)
