@@ -14,7 +14,8 @@
  *
  * Conventions (every entry point):
  *  - Pointers are DEVICE pointers owned by the caller, except `cfg` and `bytes`, which are
- *    host pointers read (written) during the call only. The library never allocates or
+ *    host pointers read (written) during the call only. Device pointers must be 16-byte
+ *    aligned (the kernels load and store 16-byte vectors; the library does not check). The library never allocates or
  *    frees device memory; scratch comes from the caller's workspace `ws` of `ws_bytes`
  *    bytes, sized by moe_workspace_size().
  *  - Work is enqueued on `stream` and the call returns at once. The library never

@@ -123,6 +123,8 @@ def _ptr(t, dtype=None, shape=None, name="tensor"):
         raise ValueError(f"{name}: must be a GPU tensor")
     if not t.is_contiguous():
         raise ValueError(f"{name}: must be contiguous")
+    if t.data_ptr() % 16:
+        raise ValueError(f"{name}: must be 16-byte aligned (the kernels move 16-byte vectors)")
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
     if shape is not None and tuple(t.shape) != tuple(shape):

@@ -273,3 +273,4 @@ def test_fp8_activation_size_limit(moe):
     # the widest of H, F and shared_F counts
     assert ws_size(moe, cfgc(moe, w_dtype=mi.E4M3, T=60000, H=1024, F=8192, shared_F=128),
                    moe.OP_PERMUTE)[0] == 2
+

@@ -61,3 +61,15 @@ def test_layer_edge_case(moe, name):
     err = rel_err(y.cpu(), ref)
     print(f"[edge] {name}: rel err {err:.3e}", flush=True)
     assert err <= tol(cfg)
+
+
+def test_binding_rejects_misaligned_tensor(moe):
+    """A contiguous tensor whose data starts 2 bytes into an allocation is refused by the
+    binding before anything is launched (the kernels move 16-byte vectors)."""
+    cfg = mi.scaled(mi.CONFIGS["qwen3_bf16"], T=4, H=256, F=128, E=16)
+    raw = torch.empty(cfg.T * cfg.H * 2 + 16, dtype=torch.uint8, device="cuda")
+    x_bad = raw[2:2 + cfg.T * cfg.H * 2].view(torch.bfloat16).view(cfg.T, cfg.H)
+    assert x_bad.is_contiguous() and x_bad.data_ptr() % 16 == 2
+    w_r = torch.zeros(cfg.E, cfg.H, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError, match="16-byte aligned"):
+        moe.router_logits(cfg, x_bad, w_r)
