@@ -433,6 +433,27 @@ def time_layer_backward(moe, mi, cfg, dev, x, wr, logits, idx, gate, w13, w2, ws
         b.record()
         torch.cuda.synchronize()
         ts += a.elapsed_time(b) / max(1, reps)
+    # the same saved backward on the forward's own weight copy (K-blocked when the forward's
+    # are): one copy of the weights serves both passes
+    tk = None
+    if tcfg.w_layout:
+        kcfg = bcfg.replace(w_layout=tcfg.w_layout)
+
+        def run_saved_k():
+            return moe.layer_backward_saved(kcfg, x, wr, ext["logits"], ext["topk_idx"],
+                                            ext["topk_gate"], train["w13"], train["w2"], dy,
+                                            saved, logit_bias=lb, ws13=train["ws13"],
+                                            ws2=train["ws2"], ws=lws)
+        run_saved_k()
+        torch.cuda.synchronize()
+        tk = 0.0
+        for _ in range(max(1, reps)):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            run_saved_k()
+            b.record()
+            torch.cuda.synchronize()
+            tk += a.elapsed_time(b) / max(1, reps)
     fm = pct(f_ms, 50)
     out["saved_activations"] = {
         "what": "training pair: moe_layer_forward_train keeps GEMM1's Z and act "
@@ -441,6 +462,11 @@ def time_layer_backward(moe, mi, cfg, dev, x, wr, logits, idx, gate, w13, w2, ws
         "forward_train_ms": round(fm, 4), "backward_ms": round(ts, 4),
         "backward_TFLOP/s": round(flops / (ts * 1e-3) / 1e12, 1),
         "step_ms": round(fm + ts, 4), "step_tokens/s": round(cfg.T / ((fm + ts) * 1e-3), 1)}
+    if tk is not None:
+        out["saved_activations"]["backward_on_forward_weights_ms"] = round(tk, 4)
+        out["saved_activations"]["backward_on_forward_weights_note"] = (
+            "the saved backward reading the forward's K-blocked weight copy instead of a "
+            "row-major one (same gradients, bit for bit)")
     return out
 
 

@@ -329,10 +329,12 @@ int moe_set_stage_events(void* const* events, int32_t n_events);
  *   dx_perm = dZ W13_e                        [M_e, H]
  *   dW2_e   = dy_perm[R_e]^T act[R_e]         [H, F]
  *   dW13_e  = dZ[R_e]^T x_perm[R_e]           [2F, H]
- * All tensors bf16 and row-major (cfg->act_dtype == MOE_BF16, a_layout = w_layout = 0;
- * cfg->w_dtype is not used: the backward runs on the bf16 weights): dy_perm [A, H],
- * x_perm [A, H], z [A, 2F] and act [A, F] (the forward's saved Z and g * h), w13 [E, 2F, H],
- * w2 [E, H, F]. Outputs dx_perm [A, H], dw13 [E, 2F, H], dw2 [E, H, F] bf16 and
+ * All tensors bf16 (cfg->act_dtype == MOE_BF16, a_layout = 0; cfg->w_dtype is not used:
+ * the backward runs on the bf16 weights), row-major except the weights, which follow
+ * cfg->w_layout (row-major, or K-blocked as the forward takes them, so one copy serves
+ * both): dy_perm [A, H], x_perm [A, H], z [A, 2F] and act [A, F] (the forward's saved Z and
+ * g * h), w13 [E, 2F, H], w2 [E, H, F]. The results do not depend on the weight layout.
+ * Outputs (row-major) dx_perm [A, H], dw13 [E, 2F, H], dw2 [E, H, F] bf16 and
  * dgate_perm [A] fp32 (may be NULL). gate_perm may be NULL (gate 1 for every row: a shared
  * expert is one group whose offsets are {0, T}). Experts with no rows get zero weight
  * gradients. Deterministic: dg is summed per tile, then over tiles in a fixed order.
@@ -360,8 +362,10 @@ int moe_grouped_gemm_swiglu_bwd(const moe_config* cfg, const void* dy_perm,
  * the shared expert and dl W_r. Outputs (all overwritten): dx [T, H], dw_router [E, H],
  * dw13, dw2 (zero for experts without rows), dws13, dws2 (NULL without a shared expert) in
  * bf16, and dlogits_out [T, E] fp32 (optional, NULL = skip). dl passes through bf16 on its
- * way to the router GEMMs. Requires act_dtype = w_dtype = MOE_BF16, row-major layouts and
- * E % 128 == 0 (else MOE_ERR_UNSUPPORTED). Deterministic.
+ * way to the router GEMMs. Requires act_dtype = w_dtype = MOE_BF16, a_layout = 0 and
+ * E % 128 == 0 (else MOE_ERR_UNSUPPORTED); the expert weights (w13, w2, ws13, ws2) follow
+ * cfg->w_layout, the gradients are row-major, and the results do not depend on the weight
+ * layout. Deterministic.
  * Workspace: moe_workspace_size(cfg, MOE_OP_LAYER_BACKWARD). */
 int moe_layer_backward(const moe_config* cfg, const void* x, const void* w_router,
                        const float* logits, const float* logit_bias, const int32_t* topk_idx,
@@ -386,8 +390,8 @@ int moe_layer_backward(const moe_config* cfg, const void* x, const void* w_route
  * moe_workspace_size(cfg, MOE_OP_LAYER_FORWARD).
  * moe_layer_backward_saved: moe_layer_backward with the buffer written by
  * moe_layer_forward_train for the same x, routing (topk_idx, topk_gate) and weights (the
- * backward's cfg may differ only in w_layout, which must be 0 here); every output is
- * bit-identical to moe_layer_backward's, and no GEMM1 is run. Workspace:
+ * backward's cfg may differ only in w_layout); every output is bit-identical to
+ * moe_layer_backward's, and no GEMM1 is run. Workspace:
  * moe_workspace_size(cfg, MOE_OP_LAYER_BACKWARD). */
 int moe_layer_forward_train(const moe_config* cfg, const void* x, const void* w_router,
                             const float* logit_bias, const float* sel_bias,

@@ -229,7 +229,7 @@ LayerBwdWs carve_layer_bwd(const moe_config* c, void* ws) {
 }
 
 int check_layer_bwd(const moe_config* c) {
-    if (c->act_dtype != MOE_BF16 || c->w_dtype != MOE_BF16 || c->a_layout || c->w_layout)
+    if (c->act_dtype != MOE_BF16 || c->w_dtype != MOE_BF16 || c->a_layout)
         return MOE_ERR_UNSUPPORTED;
     if (c->capacity_factor != 0.0f) return MOE_ERR_UNSUPPORTED;     // dropless only
     if (c->E % 128) return MOE_ERR_UNSUPPORTED;          // router GEMM tiles
@@ -427,7 +427,7 @@ int moe_workspace_size(const moe_config* cfg, int op, size_t* bytes) {
     case MOE_OP_GROUPED_GEMM: *bytes = gemm_ws_bytes(cfg); break;
     case MOE_OP_LAYER_FORWARD: *bytes = carve_layer(cfg, nullptr).total; break;
     case MOE_OP_GROUPED_GEMM_BWD:
-        if (cfg->act_dtype != MOE_BF16 || cfg->a_layout || cfg->w_layout) return MOE_ERR_UNSUPPORTED;
+        if (cfg->act_dtype != MOE_BF16 || cfg->a_layout) return MOE_ERR_UNSUPPORTED;
         if (cfg->capacity_factor != 0.0f) return MOE_ERR_UNSUPPORTED;
         *bytes = moe::bwd_ws_bytes(cfg->T, cfg->k, cfg->E, cfg->H, cfg->F);
         break;
@@ -780,7 +780,7 @@ int moe_grouped_gemm_swiglu_bwd(const moe_config* cfg, const void* dy_perm, cons
                                 void* ws, size_t ws_bytes, hipStream_t stream) {
     int st = check_cfg(cfg);
     if (st) return st;
-    if (cfg->act_dtype != MOE_BF16 || cfg->a_layout || cfg->w_layout) return MOE_ERR_UNSUPPORTED;
+    if (cfg->act_dtype != MOE_BF16 || cfg->a_layout) return MOE_ERR_UNSUPPORTED;
     if (cfg->capacity_factor != 0.0f) return MOE_ERR_UNSUPPORTED;      // dropless only
     if (!dy_perm || !x_perm || !z || !act || !offsets || !w13 || !w2 || !dx_perm || !dw13 ||
         !dw2 || !ws)
@@ -790,7 +790,7 @@ int moe_grouped_gemm_swiglu_bwd(const moe_config* cfg, const void* dy_perm, cons
     return hip_status(moe::launch_grouped_gemm_bwd(dy_perm, x_perm, z, act, gate_perm, offsets,
                                                    w13, w2, cfg->T * cfg->k, cfg->E, cfg->H,
                                                    cfg->F, dx_perm, dw13, dw2, dgate_perm, ws,
-                                                   stream));
+                                                   stream, true, cfg->w_layout != 0));
 }
 
 // The layer backward; sv != NULL: Z and act come from the saved buffer of a training forward
@@ -834,13 +834,13 @@ static int layer_backward_impl(const moe_config* cfg, const void* x, const void*
     void* acts = sv ? sv->acts : L.acts;
     if (e == hipSuccess && !sv) {
         Segment r1 = {L.x_perm, nullptr, L.offsets, E, 0, L.gate_perm, w13, nullptr, L.act,
-                      nullptr, L.z, A, 0, 0, 0, nullptr};
+                      nullptr, L.z, A, 0, cfg->w_layout, 0, nullptr};
         e = moe::launch_grouped_gemm(0, MOE_BF16, &r1, 1, A, 2 * F, H, L.sched, stream);
     }
     if (e == hipSuccess) e = moe::launch_offsets2(L.offs_one, T, stream);
     if (e == hipSuccess && sF && !sv) {
         Segment s1 = {x, nullptr, nullptr, 1, T, nullptr, ws13, nullptr, L.acts, nullptr, L.zs,
-                      T, 0, 0, 0, nullptr};
+                      T, 0, cfg->w_layout, 0, nullptr};
         e = moe::launch_grouped_gemm(0, MOE_BF16, &s1, 1, T, 2 * sF, H, L.sched, stream);
     }
     // expert gradients (routed: dgate through the fold; shared: gate 1). Their weight
@@ -854,11 +854,11 @@ static int layer_backward_impl(const moe_config* cfg, const void* x, const void*
     if (e == hipSuccess)
         e = moe::launch_grouped_gemm_bwd(L.dy_perm, L.x_perm, z, act, L.gate_perm, L.offsets,
                                          w13, w2, A, E, H, F, L.dx_perm, dw13, dw2,
-                                         L.dgate_perm, L.bws, stream, false);
+                                         L.dgate_perm, L.bws, stream, false, cfg->w_layout != 0);
     if (e == hipSuccess && sF)
         e = moe::launch_grouped_gemm_bwd(dy, x, zs, acts, nullptr, L.offs_one, ws13, ws2, T, 1,
                                          H, sF, L.dxs, dws13, dws2, nullptr, L.bws_s, stream,
-                                         false);
+                                         false, cfg->w_layout != 0);
     // gates -> logits -> router weight and x
     if (e == hipSuccess)
         e = moe::launch_route_backward(cfg->router, logits, logit_bias, topk_idx, topk_gate,

@@ -70,6 +70,8 @@ struct Operand {
     const uint16_t* p;
     size_t ld;                    // elements between rows of the stored matrix
     size_t gstride;               // elements between groups (weights); 0 = rows are global
+    int kb_rows;                  // 0: row-major; R: each group's [R, ld] matrix K-blocked
+                                  // ([ld / 32][R][32 elements], the forward's weight layout)
 };
 
 struct BwdArgs {
@@ -180,10 +182,13 @@ MOE_DEVICE void bwd_tile(const BwdArgs& ba, int L, uint8_t* lds) {
             const int kr = (64 / cpr) * q + lane / cpr;
             const int c = (lane % cpr) ^ swz_t(kr);
             const size_t col = (size_t)(is_a ? mt * kBM : nt * kBN) + c * 8;
+            // byte offset of (row 0, col): K-blocked, the 8-element chunk at col sits in 64-byte
+            // slice col / 32 of every row, and the rows of a slice are 64 bytes apart
+            const size_t cb = op.kb_rows ? ((col / 32) * op.kb_rows * 32 + col % 32) * 2 : col * 2;
             if (RAGGED_K)
-                src = (const uint8_t*)(op.p + (size_t)rbase * op.ld + col);   // + k * ld
+                src = (const uint8_t*)(op.p + (size_t)rbase * op.ld) + cb;     // + k * kstride
             else
-                src = (const uint8_t*)(op.p + (size_t)g * op.gstride + col);  // + k * ld
+                src = (const uint8_t*)(op.p + (size_t)g * op.gstride) + cb;    // + k * kstride
             krow = kr;
         }
     };
@@ -201,8 +206,9 @@ MOE_DEVICE void bwd_tile(const BwdArgs& ba, int L, uint8_t* lds) {
                 sa = srcA[u] + (size_t)kstep * kBK * 2;
             } else {
                 const int kk = kstep * kBK + ka[u];
+                const size_t ks = ba.a.kb_rows ? 64 : ba.a.ld * 2;     // bytes between k rows
                 sa = (RAGGED_K && kk >= Mg) ? ba.zero + (lane % (kBM / 8)) * 16
-                                            : srcA[u] + (size_t)kk * ba.a.ld * 2;
+                                            : srcA[u] + (size_t)kk * ks;
             }
             __builtin_amdgcn_global_load_lds((const void*)sa, (MOE_LDS void*)(base + q * 1024),
                                              16, 0, 0);
@@ -215,8 +221,9 @@ MOE_DEVICE void bwd_tile(const BwdArgs& ba, int L, uint8_t* lds) {
                 sb = srcB[u] + (size_t)kstep * kBK * 2;
             } else {
                 const int kk = kstep * kBK + kb[u];
+                const size_t ks = ba.b.kb_rows ? 64 : ba.b.ld * 2;     // bytes between k rows
                 sb = (RAGGED_K && kk >= Mg) ? ba.zero + (lane % (kBN / 8)) * 16
-                                            : srcB[u] + (size_t)kk * ba.b.ld * 2;
+                                            : srcB[u] + (size_t)kk * ks;
             }
             __builtin_amdgcn_global_load_lds((const void*)sb,
                                              (MOE_LDS void*)(base + kOpBytes + q * 1024), 16, 0, 0);
@@ -514,7 +521,8 @@ template <class CF>
 hipError_t bwd_all(const BwdWs& w, const void* dy_perm, const void* x_perm, const void* z,
                    const void* act, const float* gate_perm, const int32_t* offsets,
                    const void* w13, const void* w2, int A, int E, int H, int F, void* dx_perm,
-                   void* dw13, void* dw2, float* dgate_perm, hipStream_t s, bool join) {
+                   void* dw13, void* dw2, float* dgate_perm, hipStream_t s, bool join,
+                   bool w_kblock) {
     constexpr int kBM = CF::BM, kBN = CF::BN;
     std::lock_guard<std::recursive_mutex> lock(g_side_mu);
     SideRes* sr = nullptr;
@@ -537,8 +545,8 @@ hipError_t bwd_all(const BwdWs& w, const void* dy_perm, const void* x_perm, cons
 
     // wgrad 2 (side): dW2_e [H, F] = dy_perm[R_e]^T act[R_e]
     BwdArgs w2a = {};
-    w2a.a = {DY, (size_t)H, 0};
-    w2a.b = {(const uint16_t*)act, (size_t)F, 0};
+    w2a.a = {DY, (size_t)H, 0, 0};
+    w2a.b = {(const uint16_t*)act, (size_t)F, 0, 0};
     w2a.offsets = offsets; w2a.M = H; w2a.N = F; w2a.ntm = H / CF::BM; w2a.ntn = F / CF::BN;
     w2a.groups = E; w2a.out = (uint16_t*)dw2; w2a.out_ld = F; w2a.out_gstride = (size_t)H * F;
     w2a.zero = w.zero;
@@ -546,8 +554,8 @@ hipError_t bwd_all(const BwdWs& w, const void* dy_perm, const void* x_perm, cons
     // dgrad 1: dA [A, F] = dy_perm W2_e (W2_e stored [H][F]: K rows) -> dZ, dg partials
     if (e == hipSuccess) {
         BwdArgs d1 = {};
-        d1.a = {DY, (size_t)H, 0};
-        d1.b = {W2, (size_t)F, (size_t)H * F};
+        d1.a = {DY, (size_t)H, 0, 0};
+        d1.b = {W2, (size_t)F, (size_t)H * F, w_kblock ? H : 0};
         d1.offsets = offsets; d1.tiles = tiles; d1.total = total;
         d1.N = F; d1.K = H; d1.ntn = F / kBN; d1.groups = E;
         d1.z = (const uint16_t*)z; d1.gate = gate_perm; d1.dz = w.dz; d1.dg_part = w.dg_part;
@@ -564,8 +572,8 @@ hipError_t bwd_all(const BwdWs& w, const void* dy_perm, const void* x_perm, cons
     if (e == hipSuccess) {
         // wgrad 1: dW13_e [2F, H] = dZ[R_e]^T x_perm[R_e]
         BwdArgs w1 = {};
-        w1.a = {w.dz, (size_t)2 * F, 0};
-        w1.b = {X, (size_t)H, 0};
+        w1.a = {w.dz, (size_t)2 * F, 0, 0};
+        w1.b = {X, (size_t)H, 0, 0};
         w1.offsets = offsets; w1.M = 2 * F; w1.N = H; w1.ntm = 2 * F / CF::BM;
         w1.ntn = H / CF::BN; w1.groups = E; w1.out = (uint16_t*)dw13; w1.out_ld = H;
         w1.out_gstride = (size_t)2 * F * H; w1.zero = w.zero;
@@ -574,8 +582,8 @@ hipError_t bwd_all(const BwdWs& w, const void* dy_perm, const void* x_perm, cons
     if (e == hipSuccess) {
         // dgrad 2: dx_perm [A, H] = dZ W13_e (W13_e stored [2F][H]: K rows)
         BwdArgs d2 = {};
-        d2.a = {w.dz, (size_t)2 * F, 0};
-        d2.b = {W13, (size_t)H, (size_t)2 * F * H};
+        d2.a = {w.dz, (size_t)2 * F, 0, 0};
+        d2.b = {W13, (size_t)H, (size_t)2 * F * H, w_kblock ? 2 * F : 0};
         d2.offsets = offsets; d2.tiles = tiles; d2.total = total;
         d2.N = H; d2.K = 2 * F; d2.ntn = H / kBN; d2.groups = E;
         d2.out = (uint16_t*)dx_perm; d2.out_ld = H; d2.zero = w.zero;
@@ -601,8 +609,8 @@ hipError_t router_bwd_all(const void* dl, const void* x, const void* w_router, i
     const uint16_t* DL = (const uint16_t*)dl;
     auto round8 = [](size_t n) { return (int)((n + 7) / 8 * 8); };
     BwdArgs wa = {};
-    wa.a = {DL, (size_t)E, 0};
-    wa.b = {(const uint16_t*)x, (size_t)H, 0};
+    wa.a = {DL, (size_t)E, 0, 0};
+    wa.b = {(const uint16_t*)x, (size_t)H, 0, 0};
     wa.offsets = offs2; wa.M = E; wa.N = H; wa.ntm = E / CF::BM; wa.ntn = H / CF::BN;
     wa.groups = 1; wa.out = (uint16_t*)dw_router; wa.out_ld = H; wa.out_gstride = 0;
     wa.zero = zero;
@@ -611,8 +619,8 @@ hipError_t router_bwd_all(const void* dl, const void* x, const void* w_router, i
     e = launch_schedule(offs2, 1, CF::BM, sched, s);
     if (e != hipSuccess) return e;
     BwdArgs da = {};
-    da.a = {DL, (size_t)E, 0};
-    da.b = {(const uint16_t*)w_router, (size_t)H, 0};
+    da.a = {DL, (size_t)E, 0, 0};
+    da.b = {(const uint16_t*)w_router, (size_t)H, 0, 0};
     da.offsets = offs2;
     da.tiles = (const int4*)((char*)sched + 256);
     da.total = (const int*)sched;
@@ -648,15 +656,15 @@ hipError_t launch_grouped_gemm_bwd(const void* dy_perm, const void* x_perm, cons
                                    const int32_t* offsets, const void* w13, const void* w2,
                                    int A, int E, int H, int F, void* dx_perm, void* dw13,
                                    void* dw2, float* dgate_perm, void* ws, hipStream_t s,
-                                   bool join) {
+                                   bool join, bool w_kblock) {
     BwdWs w = carve_bwd(ws, A, E, F);
     zero_fill_kernel<<<1, 256, 0, s>>>((uint32_t*)w.zero, kZeroBytes / 4);
     // 256 x 256 tiles when every GEMM dimension divides by 256 (F, 2F and H), else 128 x 128
     if (F % BwdLarge::BN == 0 && H % BwdLarge::BN == 0 && MOE_BWD_LARGE)
         return bwd_all<BwdLarge>(w, dy_perm, x_perm, z, act, gate_perm, offsets, w13, w2, A, E,
-                                 H, F, dx_perm, dw13, dw2, dgate_perm, s, join);
+                                 H, F, dx_perm, dw13, dw2, dgate_perm, s, join, w_kblock);
     return bwd_all<BwdSmall>(w, dy_perm, x_perm, z, act, gate_perm, offsets, w13, w2, A, E, H,
-                             F, dx_perm, dw13, dw2, dgate_perm, s, join);
+                             F, dx_perm, dw13, dw2, dgate_perm, s, join, w_kblock);
 }
 
 size_t router_bwd_ws_bytes(int T) {

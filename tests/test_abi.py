@@ -175,6 +175,12 @@ def test_layer_backward_argument_checks(moe):
     assert st == 0 and n > 0
     assert ws_size(moe, cfgc(moe, base="mixtral_bf16"), moe.OP_LAYER_BACKWARD)[0] == 2  # E = 8
     assert ws_size(moe, cfgc(moe, base="tiny_fp32"), moe.OP_LAYER_BACKWARD)[0] == 2    # fp32
+    # weights in either layout; activations row-major only
+    assert ws_size(moe, cfgc(moe, base="dsv3_bf16", w_layout=1), moe.OP_LAYER_BACKWARD) == (0, n)
+    assert ws_size(moe, cfgc(moe, base="dsv3_bf16", a_layout=1, w_layout=1),
+                   moe.OP_LAYER_BACKWARD)[0] == 2
+    assert ws_size(moe, cfgc(moe, base="dsv3_bf16", w_layout=1),
+                   moe.OP_GROUPED_GEMM_BWD)[0] == 0
     L = moe.lib()
     p = C.c_void_p(0x1000)
     args = [p] * 19
@@ -199,8 +205,9 @@ def test_training_pair_argument_checks(moe):
     assert ws_size(moe, cfgc(moe, base="dsv3_fp8_skew"), moe.OP_LAYER_SAVED)[0] == 2   # e4m3
     assert ws_size(moe, cfgc(moe, base="tiny_fp32"), moe.OP_LAYER_SAVED)[0] == 2       # fp32
     assert ws_size(moe, cfgc(moe, capacity_factor=1.25), moe.OP_LAYER_SAVED)[0] == 2
-    # K-blocked weights are fine for the forward (the backward needs row-major ones)
+    # K-blocked weights are fine on both sides; K-blocked activations are not
     assert ws_size(moe, cfgc(moe, w_layout=1), moe.OP_LAYER_SAVED) == (0, n)
+    assert ws_size(moe, cfgc(moe, a_layout=1, w_layout=1), moe.OP_LAYER_SAVED)[0] == 2
     L = moe.lib()
     p = C.c_void_p(0x1000)
     big = C.c_size_t(1 << 40)
@@ -216,7 +223,7 @@ def test_training_pair_argument_checks(moe):
                                       None) == 1
     assert L.moe_layer_backward_saved(C.byref(c), *head, p, C.c_size_t(n - 1), *tail, p, big,
                                       None) == 3
-    ck = cfgc(moe, w_layout=1)
+    ck = cfgc(moe, a_layout=1, w_layout=1)
     assert L.moe_layer_backward_saved(C.byref(ck), *head, p, big, *tail, p, big, None) == 2
 
 

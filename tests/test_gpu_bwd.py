@@ -125,3 +125,23 @@ def test_bwd_shared_expert_as_one_group(moe, name):
     e2 = rel_err(out["dw2"][0].cpu()[r2, c2], ref2)
     print(f"   dx {e_dx:.3e}  dW13 {e13:.3e}  dW2 {e2:.3e}", flush=True)
     assert e_dx <= TOL and e13 <= TOL and e2 <= TOL
+
+
+@pytest.mark.parametrize("name", ["dsv3_bwd_small", "dsv3_bwd_small2"])
+def test_bwd_kblocked_weights_bit_identical(moe, name):
+    """The backward reads the weights in either layout: with w_layout = 1 and the weights
+    K-blocked (the forward's layout, so one copy serves both passes) every output equals the
+    row-major run bit for bit. small covers the 256 x 256 tiles, small2 the 128 x 128 ones."""
+    c = case(name)
+    cfg, inp, perm = c["cfg"], c["inp"], c["perm"]
+    print(f"[bwd kblock] {name}", flush=True)
+    T8 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    w13, w2 = inp.w13.cuda(), inp.w2.cuda()
+    common = (c["dyp"].cuda(), c["xp"].cuda(), c["z"].cuda(), c["act"].cuda(),
+              T8(perm["gate_perm"]), T8(perm["offsets"]))
+    ref = moe.grouped_gemm_swiglu_bwd(cfg, *common, w13, w2)
+    got = moe.grouped_gemm_swiglu_bwd(cfg.replace(w_layout=1), *common, moe.pack_kblock(w13),
+                                      moe.pack_kblock(w2))
+    torch.cuda.synchronize()
+    for n in ("dx_perm", "dw13", "dw2", "dgate_perm"):
+        assert torch.equal(ref[n], got[n]), n

@@ -90,8 +90,8 @@ def test_training_pair_bit_identical(moe, name):
     """moe_layer_forward_train keeps GEMM1's Z and act; moe_layer_backward_saved uses them
     instead of recomputing GEMM1. Both must give exactly what moe_layer_forward and
     moe_layer_backward give (the same kernels compute the same values). The dsv3 case runs the
-    training forward on K-blocked weights, as the benchmark does, and the backward on the
-    row-major ones."""
+    training forward on K-blocked weights, as the benchmark does; every case then runs both
+    backwards on K-blocked weights too."""
     cfg = CASES[name]
     print(f"[train pair] {name}: T={cfg.T} H={cfg.H} E={cfg.E} k={cfg.k} F={cfg.F} "
           f"shared={cfg.shared_F}", flush=True)
@@ -127,6 +127,20 @@ def test_training_pair_bit_identical(moe, name):
             continue
         assert torch.equal(t, gs[n]), n
         assert torch.equal(t, gs2[n]), n
+    # both backwards on K-blocked weights (the forward's copy): the same gradients, bit for bit
+    kcfg = cfg.replace(w_layout=1)
+    kw_ = {n: (moe.pack_kblock(t) if t is not None else None)
+           for n, t in dict(w13=w13, w2=w2, ws13=ws13, ws2=ws2).items()}
+    kargs = (kcfg, x, wr, ex["logits"], ex["topk_idx"], ex["topk_gate"], kw_["w13"], kw_["w2"],
+             dy)
+    kkw = dict(logit_bias=lb, ws13=kw_["ws13"], ws2=kw_["ws2"], want_dlogits=True)
+    gk = moe.layer_backward(*kargs, **kkw)
+    gks = moe.layer_backward_saved(*kargs, saved, **kkw)
+    torch.cuda.synchronize()
+    for n, t in g.items():
+        if t is not None:
+            assert torch.equal(t, gk[n]), n
+            assert torch.equal(t, gks[n]), n
 
 
 
