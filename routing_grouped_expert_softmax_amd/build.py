@@ -50,6 +50,59 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def resource_usage() -> str:
+    """Recompile every source with the compiler's kernel-resource-usage remarks (nothing is
+    linked or replaced) and return one line per kernel: VGPRs, AGPRs, SGPRs, spilled VGPRs
+    and SGPRs, scratch bytes per lane, LDS bytes per block (static; the GEMMs add dynamic
+    LDS at launch) and waves per SIMD the registers allow."""
+    import re
+    import tempfile
+    rows = []
+    keys = {"VGPRs": "vgpr", "AGPRs": "agpr", "TotalSGPRs": "sgpr", "VGPRs Spill": "vspill",
+            "SGPRs Spill": "sspill", "ScratchSize [bytes/lane]": "scratch",
+            "LDS Size [bytes/block]": "lds", "Occupancy [waves/SIMD]": "occ"}
+    pat = re.compile(r"remark:\s+(Function Name|[A-Za-z ]+(?:\[[^\]]*\])?):\s*(\S+)")
+    with tempfile.TemporaryDirectory() as tmp:
+        for src in SOURCES:
+            cmd = [HIPCC] + FLAGS + ["-Rpass-analysis=kernel-resource-usage", "-c",
+                                     os.path.join(CSRC, src), "-o", os.path.join(tmp, "k.o")]
+            r = subprocess.run(cmd, capture_output=True, text=True)
+            if r.returncode != 0:
+                raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+            cur = None
+            for line in r.stderr.splitlines():
+                m = pat.search(line)
+                if not m:
+                    continue
+                k, v = m.group(1).strip(), m.group(2)
+                if k == "Function Name":
+                    cur = {"src": src, "name": v}
+                    rows.append(cur)
+                elif cur is not None and k in keys:
+                    cur[keys[k]] = v
+    try:                                    # demangled names where c++filt is present
+        names = subprocess.run(["c++filt"], input="\n".join(r["name"] for r in rows),
+                               text=True, capture_output=True).stdout.splitlines()
+        if len(names) == len(rows):
+            for r, n in zip(rows, names):
+                r["name"] = n
+    except OSError:
+        pass
+    for r in rows:                          # short names: no namespace, return type, arguments
+        n = r["name"].replace("moe::(anonymous namespace)::", "").replace("moe::", "")
+        n = n[5:] if n.startswith("void ") else n
+        r["name"] = n.split("(")[0]
+    cols = ["vgpr", "agpr", "sgpr", "vspill", "sspill", "scratch", "lds", "occ"]
+    out = ["source | " + " | ".join(cols) + " | kernel"]
+    for r in rows:
+        out.append(f"{r['src']} | " + " | ".join(str(r.get(c, "?")) for c in cols) +
+                   f" | {r['name']}")
+    return "\n".join(out)
+
+
 if __name__ == "__main__":
-    build(verbose=True)
+    if "--resource-usage" in sys.argv:
+        print(resource_usage())
+    else:
+        build(verbose=True)
     sys.exit(0)
