@@ -18,6 +18,7 @@
 // The weight gradients run K (an expert's rows) to a ragged end: rows past it are loaded
 // from a zeroed page of the workspace. dg is reduced per tile and then over tiles in a fixed
 // order, so the whole backward is deterministic (no atomics).
+#include <climits>
 #include <mutex>
 
 #include "common.h"
@@ -26,6 +27,11 @@
 namespace moe {
 namespace {
 
+// weight gradients dealt over the XCDs by a group plan (wgrad_plan_kernel), else in
+// contiguous runs
+#ifndef MOE_BWD_PLAN
+#define MOE_BWD_PLAN 1
+#endif
 #ifndef MOE_BWD_LARGE
 #define MOE_BWD_LARGE 1
 #endif
@@ -91,6 +97,9 @@ struct BwdArgs {
     float* dg_part;
     int F;
     const uint8_t* zero;
+    // ragged-K: the groups dealt over the XCDs (xorder[x * groups / 8 + j] = the j-th group
+    // XCD x walks), or nullptr for contiguous runs of tiles
+    const int32_t* xorder;
 };
 
 // swizzle of the 16-byte chunks of a [k][cols] operand row (a row is a whole number of
@@ -406,16 +415,74 @@ MOE_DEVICE void bwd_tile(const BwdArgs& ba, int L, uint8_t* lds) {
 
 // One tile per workgroup. The hardware deals workgroups round-robin over the 8 XCDs, so
 // workgroup b (on XCD b % 8) takes tile (b % 8) * per + b / 8: each XCD walks one contiguous
-// run of tiles.
+// run of tiles. With a group plan (ragged K), XCD x walks the tiles of its own list of
+// groups instead, group after group (every group has ntm * ntn tiles).
 template <class CF, int AO, int BO, int RAGGED_K, int EPI>
 __global__ __launch_bounds__(CF::kThreads) void bwd_gemm_kernel(BwdArgs ba) {
     extern __shared__ __align__(16) uint8_t lds[];
     const int xcd = blockIdx.x % 8, i = blockIdx.x / 8;
+    if (RAGGED_K && ba.xorder) {
+        const int tg = ba.ntm * ba.ntn, cap = ba.groups / 8;
+        const int j = i / tg;
+        if (j >= cap) return;
+        bwd_tile<CF, AO, BO, RAGGED_K, EPI>(ba, ba.xorder[xcd * cap + j] * tg + i % tg, lds);
+        return;
+    }
     const int total = RAGGED_K ? ba.groups * ba.ntm * ba.ntn : *ba.total * ba.ntn;
     const int per = (total + 7) / 8;
     const int L = xcd * per + i;
     if (i >= per || L >= total) return;
     bwd_tile<CF, AO, BO, RAGGED_K, EPI>(ba, L, lds);
+}
+
+// The weight-gradient GEMMs' group plan. A group's tiles take time in proportion to its rows
+// (their K) plus a fixed part (prologue and the output tile's stores, about kPlanTileRows
+// rows' worth), and the tiles of one group stay on one XCD, which reads the group's rows
+// once into its L2. Dealt in contiguous runs, a skewed load leaves one XCD with a third more
+// work than the mean. Here each XCD gets groups / 8 groups, chosen largest first, each to
+// the XCD with the least work so far among those with room (longest processing time first
+// under a cardinality cap), so each XCD's list also runs from its largest group down.
+// One workgroup: the groups are ranked by counting (ties by index), then one wave places
+// them, lanes 0..7 holding the XCDs' loads.
+constexpr int kPlanMaxGroups = 2048;
+constexpr int kPlanTileRows = 192;
+
+__global__ __launch_bounds__(256) void wgrad_plan_kernel(const int32_t* __restrict__ offsets,
+                                                         int E, int32_t* __restrict__ xorder) {
+    __shared__ int cost[kPlanMaxGroups];
+    __shared__ int ranked[kPlanMaxGroups];
+    const int tid = threadIdx.x, lane = tid % 64;
+    for (int e = tid; e < E; e += 256) cost[e] = offsets[e + 1] - offsets[e] + kPlanTileRows;
+    __syncthreads();
+    for (int e = tid; e < E; e += 256) {
+        const int ce = cost[e];
+        int r = 0;
+        for (int j = 0; j < E; ++j) {
+            const int cj = cost[j];
+            r += (cj > ce || (cj == ce && j < e)) ? 1 : 0;
+        }
+        ranked[r] = e;
+    }
+    __syncthreads();
+    if (tid >= 64) return;
+    const int cap = E / 8;
+    long long load = 0;          // lanes 0..7: XCD lane's work so far
+    int n = 0;                   // and its groups so far
+    for (int r = 0; r < E; ++r) {
+        const int e = ranked[r];
+        // (load, lane) of the XCDs with room, least first; lanes past 7 never win
+        long long key = (lane < 8 && n < cap) ? (load << 3) | lane : LLONG_MAX;
+#pragma unroll
+        for (int m = 1; m < 8; m <<= 1) {
+            const long long o = __shfl_xor(key, m);
+            key = o < key ? o : key;
+        }
+        if (lane == (int)(key & 7)) {
+            xorder[lane * cap + n] = e;
+            load += cost[e];
+            ++n;
+        }
+    }
 }
 
 __global__ __launch_bounds__(256) void dg_reduce_kernel(const float* __restrict__ part, int A,
@@ -457,6 +524,7 @@ hipError_t run_bwd(const BwdArgs& ba, int nblocks, hipStream_t s) {
 
 struct BwdWs {
     void* sched;
+    int32_t* xorder;              // weight-gradient group plan (E entries)
     uint8_t* zero;
     uint16_t* dz;
     float* dg_part;
@@ -472,6 +540,8 @@ BwdWs carve_bwd(void* ws, int A, int E, int F) {
     size_t off = 0;
     w.sched = p ? p + off : nullptr;
     off += al(schedule_ws_bytes(A, E, BwdSmall::BM));
+    w.xorder = p ? (int32_t*)(p + off) : nullptr;
+    off += al((size_t)E * 4);
     w.zero = p ? (uint8_t*)(p + off) : nullptr;
     off += al(kZeroBytes);
     w.dz = p ? (uint16_t*)(p + off) : nullptr;
@@ -530,6 +600,14 @@ hipError_t bwd_all(const BwdWs& w, const void* dy_perm, const void* x_perm, cons
     if (e != hipSuccess) return e;
     e = launch_schedule(offsets, E, kBM, w.sched, s);
     if (e != hipSuccess) return e;
+    // the weight gradients' XCD plan, for group counts it splits evenly
+    const int32_t* xorder = nullptr;
+    if (E % 8 == 0 && E >= 64 && E <= kPlanMaxGroups && MOE_BWD_PLAN) {
+        wgrad_plan_kernel<<<1, 256, 0, s>>>(offsets, E, w.xorder);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        xorder = w.xorder;
+    }
     const int4* tiles = (const int4*)((char*)w.sched + 256);
     const int* total = (const int*)w.sched;
     const size_t max_tiles = (size_t)(A + kBM - 1) / kBM + (size_t)E;
@@ -549,7 +627,7 @@ hipError_t bwd_all(const BwdWs& w, const void* dy_perm, const void* x_perm, cons
     w2a.b = {(const uint16_t*)act, (size_t)F, 0, 0};
     w2a.offsets = offsets; w2a.M = H; w2a.N = F; w2a.ntm = H / CF::BM; w2a.ntn = F / CF::BN;
     w2a.groups = E; w2a.out = (uint16_t*)dw2; w2a.out_ld = F; w2a.out_gstride = (size_t)H * F;
-    w2a.zero = w.zero;
+    w2a.zero = w.zero; w2a.xorder = xorder;
     e = run_bwd<CF, OPT, OPT, 1, 0>(w2a, round8((size_t)E * w2a.ntm * w2a.ntn), sr->side);
     // dgrad 1: dA [A, F] = dy_perm W2_e (W2_e stored [H][F]: K rows) -> dZ, dg partials
     if (e == hipSuccess) {
@@ -576,7 +654,7 @@ hipError_t bwd_all(const BwdWs& w, const void* dy_perm, const void* x_perm, cons
         w1.b = {X, (size_t)H, 0, 0};
         w1.offsets = offsets; w1.M = 2 * F; w1.N = H; w1.ntm = 2 * F / CF::BM;
         w1.ntn = H / CF::BN; w1.groups = E; w1.out = (uint16_t*)dw13; w1.out_ld = H;
-        w1.out_gstride = (size_t)2 * F * H; w1.zero = w.zero;
+        w1.out_gstride = (size_t)2 * F * H; w1.zero = w.zero; w1.xorder = xorder;
         e = run_bwd<CF, OPT, OPT, 1, 0>(w1, round8((size_t)E * w1.ntm * w1.ntn), sr->side2);
     }
     if (e == hipSuccess) {
