@@ -858,7 +858,7 @@ static int layer_backward_impl(const moe_config* cfg, const void* x, const void*
     if (e == hipSuccess && sF)
         e = moe::launch_grouped_gemm_bwd(dy, x, zs, acts, nullptr, L.offs_one, ws13, ws2, T, 1,
                                          H, sF, L.dxs, dws13, dws2, nullptr, L.bws_s, stream,
-                                         false, cfg->w_layout != 0);
+                                         false, cfg->w_layout != 0, false);
     // gates -> logits -> router weight and x
     if (e == hipSuccess)
         e = moe::launch_route_backward(cfg->router, logits, logit_bias, topk_idx, topk_gate,

@@ -592,7 +592,7 @@ hipError_t bwd_all(const BwdWs& w, const void* dy_perm, const void* x_perm, cons
                    const void* act, const float* gate_perm, const int32_t* offsets,
                    const void* w13, const void* w2, int A, int E, int H, int F, void* dx_perm,
                    void* dw13, void* dw2, float* dgate_perm, hipStream_t s, bool join,
-                   bool w_kblock) {
+                   bool w_kblock, bool use_side) {
     constexpr int kBM = CF::BM, kBN = CF::BN;
     std::lock_guard<std::recursive_mutex> lock(g_side_mu);
     SideRes* sr = nullptr;
@@ -617,9 +617,13 @@ hipError_t bwd_all(const BwdWs& w, const void* dy_perm, const void* x_perm, cons
     const uint16_t* W2 = (const uint16_t*)w2;
     auto round8 = [](size_t n) { return (int)((n + 7) / 8 * 8); };
     // fork: the side stream starts after everything the caller queued (inputs, zero page)
-    e = hipEventRecord(sr->ev[0], s);
-    if (e == hipSuccess) e = hipStreamWaitEvent(sr->side, sr->ev[0], 0);
-    if (e != hipSuccess) return e;
+    // (use_side = false: every launch on the caller's stream, in the same order)
+    hipStream_t s_w2 = use_side ? sr->side : s, s_w13 = use_side ? sr->side2 : s;
+    if (use_side) {
+        e = hipEventRecord(sr->ev[0], s);
+        if (e == hipSuccess) e = hipStreamWaitEvent(sr->side, sr->ev[0], 0);
+        if (e != hipSuccess) return e;
+    }
 
     // wgrad 2 (side): dW2_e [H, F] = dy_perm[R_e]^T act[R_e]
     BwdArgs w2a = {};
@@ -628,7 +632,7 @@ hipError_t bwd_all(const BwdWs& w, const void* dy_perm, const void* x_perm, cons
     w2a.offsets = offsets; w2a.M = H; w2a.N = F; w2a.ntm = H / CF::BM; w2a.ntn = F / CF::BN;
     w2a.groups = E; w2a.out = (uint16_t*)dw2; w2a.out_ld = F; w2a.out_gstride = (size_t)H * F;
     w2a.zero = w.zero; w2a.xorder = xorder;
-    e = run_bwd<CF, OPT, OPT, 1, 0>(w2a, round8((size_t)E * w2a.ntm * w2a.ntn), sr->side);
+    e = run_bwd<CF, OPT, OPT, 1, 0>(w2a, round8((size_t)E * w2a.ntm * w2a.ntn), s_w2);
     // dgrad 1: dA [A, F] = dy_perm W2_e (W2_e stored [H][F]: K rows) -> dZ, dg partials
     if (e == hipSuccess) {
         BwdArgs d1 = {};
@@ -645,8 +649,8 @@ hipError_t bwd_all(const BwdWs& w, const void* dy_perm, const void* x_perm, cons
         e = hipGetLastError();
     }
     // dZ is ready: wgrad 1 (second side stream) and dgrad 2 (caller's stream)
-    if (e == hipSuccess) e = hipEventRecord(sr->ev[1], s);
-    if (e == hipSuccess) e = hipStreamWaitEvent(sr->side2, sr->ev[1], 0);
+    if (e == hipSuccess && use_side) e = hipEventRecord(sr->ev[1], s);
+    if (e == hipSuccess && use_side) e = hipStreamWaitEvent(sr->side2, sr->ev[1], 0);
     if (e == hipSuccess) {
         // wgrad 1: dW13_e [2F, H] = dZ[R_e]^T x_perm[R_e]
         BwdArgs w1 = {};
@@ -655,7 +659,7 @@ hipError_t bwd_all(const BwdWs& w, const void* dy_perm, const void* x_perm, cons
         w1.offsets = offsets; w1.M = 2 * F; w1.N = H; w1.ntm = 2 * F / CF::BM;
         w1.ntn = H / CF::BN; w1.groups = E; w1.out = (uint16_t*)dw13; w1.out_ld = H;
         w1.out_gstride = (size_t)2 * F * H; w1.zero = w.zero; w1.xorder = xorder;
-        e = run_bwd<CF, OPT, OPT, 1, 0>(w1, round8((size_t)E * w1.ntm * w1.ntn), sr->side2);
+        e = run_bwd<CF, OPT, OPT, 1, 0>(w1, round8((size_t)E * w1.ntm * w1.ntn), s_w13);
     }
     if (e == hipSuccess) {
         // dgrad 2: dx_perm [A, H] = dZ W13_e (W13_e stored [2F][H]: K rows)
@@ -669,7 +673,7 @@ hipError_t bwd_all(const BwdWs& w, const void* dy_perm, const void* x_perm, cons
     }
     // join (deferred when asked, unless a launch failed), so that nothing queued on the side
     // streams outlives the caller's view of this call
-    if (!join && e == hipSuccess) return e;
+    if (!use_side || (!join && e == hipSuccess)) return e;
     hipError_t j = hipEventRecord(sr->ev[2], sr->side);
     if (j == hipSuccess) j = hipStreamWaitEvent(s, sr->ev[2], 0);
     if (j == hipSuccess) j = hipEventRecord(sr->ev[3], sr->side2);
@@ -734,15 +738,15 @@ hipError_t launch_grouped_gemm_bwd(const void* dy_perm, const void* x_perm, cons
                                    const int32_t* offsets, const void* w13, const void* w2,
                                    int A, int E, int H, int F, void* dx_perm, void* dw13,
                                    void* dw2, float* dgate_perm, void* ws, hipStream_t s,
-                                   bool join, bool w_kblock) {
+                                   bool join, bool w_kblock, bool use_side) {
     BwdWs w = carve_bwd(ws, A, E, F);
     zero_fill_kernel<<<1, 256, 0, s>>>((uint32_t*)w.zero, kZeroBytes / 4);
     // 256 x 256 tiles when every GEMM dimension divides by 256 (F, 2F and H), else 128 x 128
     if (F % BwdLarge::BN == 0 && H % BwdLarge::BN == 0 && MOE_BWD_LARGE)
         return bwd_all<BwdLarge>(w, dy_perm, x_perm, z, act, gate_perm, offsets, w13, w2, A, E,
-                                 H, F, dx_perm, dw13, dw2, dgate_perm, s, join, w_kblock);
+                                 H, F, dx_perm, dw13, dw2, dgate_perm, s, join, w_kblock, use_side);
     return bwd_all<BwdSmall>(w, dy_perm, x_perm, z, act, gate_perm, offsets, w13, w2, A, E, H,
-                             F, dx_perm, dw13, dw2, dgate_perm, s, join, w_kblock);
+                             F, dx_perm, dw13, dw2, dgate_perm, s, join, w_kblock, use_side);
 }
 
 size_t router_bwd_ws_bytes(int T) {

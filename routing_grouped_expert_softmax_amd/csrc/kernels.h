@@ -137,13 +137,15 @@ size_t bwd_ws_bytes(int T, int k, int E, int H, int F);
 // The weight gradients run on the library's side streams; join = false leaves them unjoined
 // for a caller that joins once after several launches (bwd_side_join), holding
 // bwd_side_lock() .. bwd_side_unlock() around the whole sequence. w_kblock: w13 and w2 are
-// K-blocked per expert (the forward's weight layout), else row-major.
+// K-blocked per expert (the forward's weight layout), else row-major. use_side = false runs
+// every launch on s (no side streams, nothing to join).
 hipError_t launch_grouped_gemm_bwd(const void* dy_perm, const void* x_perm, const void* z,
                                    const void* act, const float* gate_perm,
                                    const int32_t* offsets, const void* w13, const void* w2,
                                    int A, int E, int H, int F, void* dx_perm, void* dw13,
                                    void* dw2, float* dgate_perm, void* ws, hipStream_t s,
-                                   bool join = true, bool w_kblock = false);
+                                   bool join = true, bool w_kblock = false,
+                                   bool use_side = true);
 hipError_t bwd_side_join(hipStream_t s);
 void bwd_side_lock();
 void bwd_side_unlock();
