@@ -35,7 +35,7 @@
  *    per range and adds them in a fixed range order.
  *  - The library holds no state between calls except the instrumentation switch of
  *    moe_set_stage_events (per host thread; it changes no result) and, per device, the
- *    backward's two side streams and four events (created on the first backward call on
+ *    backward's two side streams and five events (created on the first backward call on
  *    that device, default priority, kept until the process ends; they carry no data).
  *  - Layouts: every matrix keeps K (its last index) contiguous, so each expert GEMM is
  *    C = A B^T. A matrix [R, C] is either row-major (MOE_LAYOUT_ROWS) or K-blocked

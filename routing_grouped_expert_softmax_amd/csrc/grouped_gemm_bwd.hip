@@ -425,7 +425,9 @@ __global__ __launch_bounds__(CF::kThreads) void bwd_gemm_kernel(BwdArgs ba) {
         const int tg = ba.ntm * ba.ntn, cap = ba.groups / 8;
         const int j = i / tg;
         if (j >= cap) return;
-        bwd_tile<CF, AO, BO, RAGGED_K, EPI>(ba, ba.xorder[xcd * cap + j] * tg + i % tg, lds);
+        int g = ba.xorder[xcd * cap + j];
+        g = g < 0 ? 0 : (g >= ba.groups ? ba.groups - 1 : g);
+        bwd_tile<CF, AO, BO, RAGGED_K, EPI>(ba, g * tg + i % tg, lds);
         return;
     }
     const int total = RAGGED_K ? ba.groups * ba.ntm * ba.ntn : *ba.total * ba.ntn;
@@ -447,12 +449,25 @@ __global__ __launch_bounds__(CF::kThreads) void bwd_gemm_kernel(BwdArgs ba) {
 constexpr int kPlanMaxGroups = 2048;
 constexpr int kPlanTileRows = 192;
 
+// minimum over each run of 8 lanes, in all 8: lanes ^ 1 and ^ 2 within a quad, then the
+// mirror lane within the 8 (lane i and 7 - i hold the two quads' minima)
+MOE_DEVICE unsigned min_of_8_lanes(unsigned v) {
+    v = min(v, (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));  // [1,0,3,2]
+    v = min(v, (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));  // [2,3,0,1]
+    v = min(v, (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false)); // half mirror
+    return v;
+}
+
 __global__ __launch_bounds__(256) void wgrad_plan_kernel(const int32_t* __restrict__ offsets,
                                                          int E, int32_t* __restrict__ xorder) {
     __shared__ int cost[kPlanMaxGroups];
-    __shared__ int ranked[kPlanMaxGroups];
+    __shared__ int ranked[kPlanMaxGroups];     // groups by cost, largest first
+    __shared__ int rcost[kPlanMaxGroups];      // and their costs
     const int tid = threadIdx.x, lane = tid % 64;
-    for (int e = tid; e < E; e += 256) cost[e] = offsets[e + 1] - offsets[e] + kPlanTileRows;
+    for (int e = tid; e < E; e += 256) {
+        cost[e] = offsets[e + 1] - offsets[e] + kPlanTileRows;
+        xorder[e] = e;          // every slot holds a valid group before the placement below
+    }
     __syncthreads();
     for (int e = tid; e < E; e += 256) {
         const int ce = cost[e];
@@ -462,24 +477,31 @@ __global__ __launch_bounds__(256) void wgrad_plan_kernel(const int32_t* __restri
             r += (cj > ce || (cj == ce && j < e)) ? 1 : 0;
         }
         ranked[r] = e;
+        rcost[r] = ce;
     }
     __syncthreads();
     if (tid >= 64) return;
+    // 32-bit keys (load >> sh) * 8 + lane: sh drops the low bits of loads past 2^27
+    const long long total = (long long)(offsets[E] - offsets[0]) + (long long)E * kPlanTileRows;
+    int sh = 0;
+    while ((total >> sh) >= (1ll << 27)) ++sh;
     const int cap = E / 8;
     long long load = 0;          // lanes 0..7: XCD lane's work so far
     int n = 0;                   // and its groups so far
+    int e_nx = ranked[0], c_nx = rcost[0];
     for (int r = 0; r < E; ++r) {
-        const int e = ranked[r];
-        // (load, lane) of the XCDs with room, least first; lanes past 7 never win
-        long long key = (lane < 8 && n < cap) ? (load << 3) | lane : LLONG_MAX;
-#pragma unroll
-        for (int m = 1; m < 8; m <<= 1) {
-            const long long o = __shfl_xor(key, m);
-            key = o < key ? o : key;
+        const int e = e_nx, c = c_nx;
+        if (r + 1 < E) {
+            e_nx = ranked[r + 1];
+            c_nx = rcost[r + 1];
         }
-        if (lane == (int)(key & 7)) {
+        // the least-loaded XCD with room (some XCD has room: r < E = 8 cap groups so far)
+        const unsigned key = min_of_8_lanes(
+            (lane < 8 && n < cap) ? ((unsigned)(load >> sh) << 3) | (unsigned)lane
+                                  : 0xFFFFFFFFu);
+        if (lane == (int)(key & 7) && n < cap) {
             xorder[lane * cap + n] = e;
-            load += cost[e];
+            load += c;
             ++n;
         }
     }
@@ -557,7 +579,7 @@ BwdWs carve_bwd(void* ws, int A, int E, int F) {
 // dW13 on another once dZ exists, both joined back to the caller's stream by events. The
 // data-gradient kernels stream weights from HBM, the weight-gradient kernels mostly write
 // dW, so they overlap (dW13 on the first side stream too would wait for dW2, which the
-// data gradients slow down). Two side streams and four events per device, created on first
+// data gradients slow down). Two side streams and five events per device, created on first
 // use (default priority); the mutex keeps two host threads from interleaving their records
 // of the shared events. A caller that queues several backward launches may defer the join
 // (join = false) and join once at its end, holding the lock across them (bwd_side_lock), so
@@ -565,7 +587,7 @@ BwdWs carve_bwd(void* ws, int A, int E, int F) {
 constexpr int kMaxDevices = 64;
 struct SideRes {
     hipStream_t side = nullptr, side2 = nullptr;
-    hipEvent_t ev[4] = {};
+    hipEvent_t ev[5] = {};
 };
 std::recursive_mutex g_side_mu;
 SideRes g_side[kMaxDevices];
@@ -579,7 +601,7 @@ hipError_t side_res(SideRes** out) {
     if (!r.side) {
         e = hipStreamCreateWithFlags(&r.side, hipStreamNonBlocking);
         if (e == hipSuccess) e = hipStreamCreateWithFlags(&r.side2, hipStreamNonBlocking);
-        for (int i = 0; i < 4 && e == hipSuccess; ++i)
+        for (int i = 0; i < 5 && e == hipSuccess; ++i)
             e = hipEventCreateWithFlags(&r.ev[i], hipEventDisableTiming);
         if (e != hipSuccess) return e;
     }
@@ -600,14 +622,6 @@ hipError_t bwd_all(const BwdWs& w, const void* dy_perm, const void* x_perm, cons
     if (e != hipSuccess) return e;
     e = launch_schedule(offsets, E, kBM, w.sched, s);
     if (e != hipSuccess) return e;
-    // the weight gradients' XCD plan, for group counts it splits evenly
-    const int32_t* xorder = nullptr;
-    if (E % 8 == 0 && E >= 64 && E <= kPlanMaxGroups && MOE_BWD_PLAN) {
-        wgrad_plan_kernel<<<1, 256, 0, s>>>(offsets, E, w.xorder);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        xorder = w.xorder;
-    }
     const int4* tiles = (const int4*)((char*)w.sched + 256);
     const int* total = (const int*)w.sched;
     const size_t max_tiles = (size_t)(A + kBM - 1) / kBM + (size_t)E;
@@ -623,6 +637,17 @@ hipError_t bwd_all(const BwdWs& w, const void* dy_perm, const void* x_perm, cons
         e = hipEventRecord(sr->ev[0], s);
         if (e == hipSuccess) e = hipStreamWaitEvent(sr->side, sr->ev[0], 0);
         if (e != hipSuccess) return e;
+    }
+    // the weight gradients' XCD plan, for group counts it splits evenly: first on the stream
+    // of dW2, which needs it, and off the caller's (dW13's stream waits for it below)
+    const int32_t* xorder = nullptr;
+    const bool plan = E % 8 == 0 && E >= 64 && E <= kPlanMaxGroups && MOE_BWD_PLAN;
+    if (plan) {
+        wgrad_plan_kernel<<<1, 256, 0, s_w2>>>(offsets, E, w.xorder);
+        e = hipGetLastError();
+        if (e == hipSuccess && use_side) e = hipEventRecord(sr->ev[4], s_w2);
+        if (e != hipSuccess) return e;
+        xorder = w.xorder;
     }
 
     // wgrad 2 (side): dW2_e [H, F] = dy_perm[R_e]^T act[R_e]
@@ -651,6 +676,7 @@ hipError_t bwd_all(const BwdWs& w, const void* dy_perm, const void* x_perm, cons
     // dZ is ready: wgrad 1 (second side stream) and dgrad 2 (caller's stream)
     if (e == hipSuccess && use_side) e = hipEventRecord(sr->ev[1], s);
     if (e == hipSuccess && use_side) e = hipStreamWaitEvent(sr->side2, sr->ev[1], 0);
+    if (e == hipSuccess && use_side && plan) e = hipStreamWaitEvent(sr->side2, sr->ev[4], 0);
     if (e == hipSuccess) {
         // wgrad 1: dW13_e [2F, H] = dZ[R_e]^T x_perm[R_e]
         BwdArgs w1 = {};
