@@ -397,7 +397,8 @@ def test_full_training_pair_dsv3(moe):
     """The training pair at the DeepSeek-V3 bf16 size in the benchmarked launch configuration
     (K-blocked weights for the forward, row-major ones for the backward):
     moe_layer_forward_train's y and routing equal moe_layer_forward's, and
-    moe_layer_backward_saved's gradients equal moe_layer_backward's, bit for bit."""
+    moe_layer_backward_saved's gradients equal moe_layer_backward's, bit for bit; so do the
+    saved backward's gradients on the forward's K-blocked weight copy."""
     c = full_case(moe, "dsv3_bf16")
     cfg, inp, dev = c["cfg"].replace(a_layout=0), c["inp"], c["dev"]
     log("dsv3_bf16: training pair")
@@ -427,3 +428,13 @@ def test_full_training_pair_dsv3(moe):
     for n, t in g.items():
         assert torch.equal(t, gs[n]), n
     log("dsv3_bf16: training pair bit-identical")
+    del g
+    # the saved backward on the forward's own K-blocked weight copy: the same gradients
+    kargs = (cfg, x, wr, ex["logits"], ex["topk_idx"], ex["topk_gate"], dev["w13"], dev["w2"],
+             dy)
+    gk = moe.layer_backward_saved(*kargs, saved, logit_bias=lb, ws13=dev["ws13"],
+                                  ws2=dev["ws2"], want_dlogits=True)
+    torch.cuda.synchronize()
+    for n, t in gs.items():
+        assert torch.equal(t, gk[n]), n
+    log("dsv3_bf16: backward on the K-blocked weights bit-identical")
