@@ -181,12 +181,12 @@ LayerWs carve_layer(const moe_config* c, void* ws) {
     return L;
 }
 
-// Workspace of the whole-layer backward: the routing metadata (twice: for x and for dY),
-// the expert-grouped x and dY, the recomputed Z and act (routed and shared), the data
-// gradients before they are combined, dl, and the scratch of every launch.
+// Workspace of the whole-layer backward: the routing metadata, the expert-grouped x and dY,
+// the recomputed Z and act (routed and shared), the data gradients before they are
+// combined, dl, and the scratch of every launch.
 struct LayerBwdWs {
-    int32_t *counts, *offsets, *pos, *src, *counts2, *offsets2, *pos2, *src2, *offs_one;
-    float *gate_perm, *gate_perm2, *dgate_perm;
+    int32_t *counts, *offsets, *pos, *src, *offs_one;
+    float *gate_perm, *dgate_perm;
     void *x_perm, *dy_perm, *z, *act, *zs, *acts, *dx_perm, *dxs, *dxr, *dl;
     void *perm_scratch, *sched, *bws, *bws_s, *rws;
     size_t total;
@@ -198,15 +198,11 @@ LayerBwdWs carve_layer_bwd(const moe_config* c, void* ws) {
     LayerBwdWs L = {};
     Carve cv(ws);
     const size_t T = c->T, H = c->H, E = c->E, k = c->k, F = c->F, sF = c->shared_F, A = T * k;
-    for (int rep = 0; rep < 2; ++rep) {
-        int32_t* counts = (int32_t*)cv.take(E * 4);
-        int32_t* offsets = (int32_t*)cv.take((E + 1) * 4);
-        int32_t* pos = (int32_t*)cv.take(A * 4);
-        int32_t* src = (int32_t*)cv.take(A * 4);
-        float* gp = (float*)cv.take(A * 4);
-        if (rep == 0) { L.counts = counts; L.offsets = offsets; L.pos = pos; L.src = src; L.gate_perm = gp; }
-        else { L.counts2 = counts; L.offsets2 = offsets; L.pos2 = pos; L.src2 = src; L.gate_perm2 = gp; }
-    }
+    L.counts = (int32_t*)cv.take(E * 4);
+    L.offsets = (int32_t*)cv.take((E + 1) * 4);
+    L.pos = (int32_t*)cv.take(A * 4);
+    L.src = (int32_t*)cv.take(A * 4);
+    L.gate_perm = (float*)cv.take(A * 4);
     L.offs_one = (int32_t*)cv.take(2 * 4);
     L.dgate_perm = (float*)cv.take(A * 4);
     L.x_perm = cv.take(A * H * 2);
@@ -819,14 +815,16 @@ static int layer_backward_impl(const moe_config* cfg, const void* x, const void*
     L = carve_layer_bwd(cfg, ws);
     const int T = cfg->T, H = cfg->H, E = cfg->E, k = cfg->k, F = cfg->F, sF = cfg->shared_F;
     const int A = T * k;
-    // expert-grouped x and dY (the permute of dY is the backward of the combine)
-    hipError_t e = moe::launch_permute(1, 0, INT_MAX, x, topk_idx, topk_gate, T, H, E, k, L.counts,
-                                       L.offsets, L.pos, L.src, L.gate_perm, L.x_perm, nullptr,
-                                       nullptr, nullptr, L.perm_scratch, stream);
-    if (e == hipSuccess)
-        e = moe::launch_permute(1, 0, INT_MAX, dy, topk_idx, topk_gate, T, H, E, k, L.counts2,
-                                L.offsets2, L.pos2, L.src2, L.gate_perm2, L.dy_perm, nullptr,
-                                nullptr, nullptr, L.perm_scratch, stream);
+    // the routing metadata once, then expert-grouped dY (the permute of dY is the backward of
+    // the combine) and x. x_perm feeds GEMM1's recompute, else only dW13: then the grouped
+    // backward gathers it itself, on dW13's stream beside dA.
+    hipError_t e = moe::launch_permute(1, -1, INT_MAX, x, topk_idx, topk_gate, T, H, E, k,
+                                       L.counts, L.offsets, L.pos, L.src, L.gate_perm, nullptr,
+                                       nullptr, nullptr, nullptr, L.perm_scratch, stream);
+    if (e == hipSuccess) e = moe::launch_gather_rows(dy, L.pos, T, k, H * 2, L.dy_perm, stream);
+    if (e == hipSuccess && !sv)
+        e = moe::launch_gather_rows(x, L.pos, T, k, H * 2, L.x_perm, stream);
+    const moe::BwdGatherX gx = {x, L.pos, T, k};
     // Z and act of GEMM1 (routed, then the shared expert): saved by the forward, or recomputed
     void* z = sv ? sv->z : L.z;
     void* act = sv ? sv->act : L.act;
@@ -854,7 +852,8 @@ static int layer_backward_impl(const moe_config* cfg, const void* x, const void*
     if (e == hipSuccess)
         e = moe::launch_grouped_gemm_bwd(L.dy_perm, L.x_perm, z, act, L.gate_perm, L.offsets,
                                          w13, w2, A, E, H, F, L.dx_perm, dw13, dw2,
-                                         L.dgate_perm, L.bws, stream, false, cfg->w_layout != 0);
+                                         L.dgate_perm, L.bws, stream, false, cfg->w_layout != 0,
+                                         true, sv ? &gx : nullptr);
     if (e == hipSuccess && sF)
         e = moe::launch_grouped_gemm_bwd(dy, x, zs, acts, nullptr, L.offs_one, ws13, ws2, T, 1,
                                          H, sF, L.dxs, dws13, dws2, nullptr, L.bws_s, stream,

@@ -614,7 +614,7 @@ hipError_t bwd_all(const BwdWs& w, const void* dy_perm, const void* x_perm, cons
                    const void* act, const float* gate_perm, const int32_t* offsets,
                    const void* w13, const void* w2, int A, int E, int H, int F, void* dx_perm,
                    void* dw13, void* dw2, float* dgate_perm, hipStream_t s, bool join,
-                   bool w_kblock, bool use_side) {
+                   bool w_kblock, bool use_side, const BwdGatherX* gx) {
     constexpr int kBM = CF::BM, kBN = CF::BN;
     std::lock_guard<std::recursive_mutex> lock(g_side_mu);
     SideRes* sr = nullptr;
@@ -636,6 +636,13 @@ hipError_t bwd_all(const BwdWs& w, const void* dy_perm, const void* x_perm, cons
     if (use_side) {
         e = hipEventRecord(sr->ev[0], s);
         if (e == hipSuccess) e = hipStreamWaitEvent(sr->side, sr->ev[0], 0);
+        if (e != hipSuccess) return e;
+    }
+    // x_perm, when asked, on dW13's stream beside dA (dW13 is its only reader here)
+    if (gx) {
+        if (use_side) e = hipStreamWaitEvent(sr->side2, sr->ev[0], 0);
+        if (e == hipSuccess) e = launch_gather_rows(gx->x, gx->pos, gx->T, gx->k, H * 2,
+                                                    (void*)x_perm, s_w13);
         if (e != hipSuccess) return e;
     }
     // the weight gradients' XCD plan, for group counts it splits evenly: first on the stream
@@ -764,15 +771,16 @@ hipError_t launch_grouped_gemm_bwd(const void* dy_perm, const void* x_perm, cons
                                    const int32_t* offsets, const void* w13, const void* w2,
                                    int A, int E, int H, int F, void* dx_perm, void* dw13,
                                    void* dw2, float* dgate_perm, void* ws, hipStream_t s,
-                                   bool join, bool w_kblock, bool use_side) {
+                                   bool join, bool w_kblock, bool use_side,
+                                   const BwdGatherX* gx) {
     BwdWs w = carve_bwd(ws, A, E, F);
     zero_fill_kernel<<<1, 256, 0, s>>>((uint32_t*)w.zero, kZeroBytes / 4);
     // 256 x 256 tiles when every GEMM dimension divides by 256 (F, 2F and H), else 128 x 128
     if (F % BwdLarge::BN == 0 && H % BwdLarge::BN == 0 && MOE_BWD_LARGE)
         return bwd_all<BwdLarge>(w, dy_perm, x_perm, z, act, gate_perm, offsets, w13, w2, A, E,
-                                 H, F, dx_perm, dw13, dw2, dgate_perm, s, join, w_kblock, use_side);
+                                 H, F, dx_perm, dw13, dw2, dgate_perm, s, join, w_kblock, use_side, gx);
     return bwd_all<BwdSmall>(w, dy_perm, x_perm, z, act, gate_perm, offsets, w13, w2, A, E, H,
-                             F, dx_perm, dw13, dw2, dgate_perm, s, join, w_kblock, use_side);
+                             F, dx_perm, dw13, dw2, dgate_perm, s, join, w_kblock, use_side, gx);
 }
 
 size_t router_bwd_ws_bytes(int T) {

@@ -139,13 +139,24 @@ size_t bwd_ws_bytes(int T, int k, int E, int H, int F);
 // bwd_side_lock() .. bwd_side_unlock() around the whole sequence. w_kblock: w13 and w2 are
 // K-blocked per expert (the forward's weight layout), else row-major. use_side = false runs
 // every launch on s (no side streams, nothing to join).
+// Rows of x [T, row_bytes] to their expert-order positions (pos [T * k], from
+// launch_permute; row-major out, row_bytes a multiple of 16): the permute's row copy alone.
+hipError_t launch_gather_rows(const void* x, const int32_t* pos, int T, int k, int row_bytes,
+                              void* out, hipStream_t s);
+// x_perm to be gathered by the backward itself, on the stream of dW13 (its only reader there)
+// while dA runs: the token-order x and the permute's pos.
+struct BwdGatherX {
+    const void* x;
+    const int32_t* pos;
+    int T, k;
+};
 hipError_t launch_grouped_gemm_bwd(const void* dy_perm, const void* x_perm, const void* z,
                                    const void* act, const float* gate_perm,
                                    const int32_t* offsets, const void* w13, const void* w2,
                                    int A, int E, int H, int F, void* dx_perm, void* dw13,
                                    void* dw2, float* dgate_perm, void* ws, hipStream_t s,
                                    bool join = true, bool w_kblock = false,
-                                   bool use_side = true);
+                                   bool use_side = true, const BwdGatherX* gx = nullptr);
 hipError_t bwd_side_join(hipStream_t s);
 void bwd_side_lock();
 void bwd_side_unlock();

@@ -378,4 +378,11 @@ hipError_t launch_permute(int mode, int kblock, int cap, const void* x, const in
     return hipGetLastError();
 }
 
+hipError_t launch_gather_rows(const void* x, const int32_t* pos, int T, int k, int row_bytes,
+                              void* out, hipStream_t s) {
+    perm_copy_kernel<<<(T + 3) / 4, 256, 0, s>>>((const uint4*)x, pos, T, row_bytes / 16, k, 0,
+                                               (uint4*)out);
+    return hipGetLastError();
+}
+
 }  // namespace moe
