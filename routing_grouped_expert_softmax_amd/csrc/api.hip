@@ -815,16 +815,19 @@ static int layer_backward_impl(const moe_config* cfg, const void* x, const void*
     L = carve_layer_bwd(cfg, ws);
     const int T = cfg->T, H = cfg->H, E = cfg->E, k = cfg->k, F = cfg->F, sF = cfg->shared_F;
     const int A = T * k;
-    // the routing metadata once, then expert-grouped dY (the permute of dY is the backward of
-    // the combine) and x. x_perm feeds GEMM1's recompute, else only dW13: then the grouped
-    // backward gathers it itself, on dW13's stream beside dA.
+    // the routing metadata once, then the expert-grouped x and dY (the permute of dY is the
+    // backward of the combine). Recomputing, x_perm comes first (GEMM1 reads it) and dY is
+    // left to the grouped backward (gathered on dW2's side stream; dA reads dY's rows through
+    // src); with saved activations dy_perm comes first and x_perm is left to the grouped
+    // backward (gathered on dW13's side stream beside dA). Measured, each is the faster form
+    // for its path.
     hipError_t e = moe::launch_permute(1, -1, INT_MAX, x, topk_idx, topk_gate, T, H, E, k,
                                        L.counts, L.offsets, L.pos, L.src, L.gate_perm, nullptr,
                                        nullptr, nullptr, nullptr, L.perm_scratch, stream);
-    if (e == hipSuccess) e = moe::launch_gather_rows(dy, L.pos, T, k, H * 2, L.dy_perm, stream);
-    if (e == hipSuccess && !sv)
-        e = moe::launch_gather_rows(x, L.pos, T, k, H * 2, L.x_perm, stream);
-    const moe::BwdGatherX gx = {x, L.pos, T, k};
+    if (e == hipSuccess)
+        e = sv ? moe::launch_gather_rows(dy, L.pos, T, k, H * 2, L.dy_perm, stream)
+               : moe::launch_gather_rows(x, L.pos, T, k, H * 2, L.x_perm, stream);
+    const moe::BwdGather gx = {sv ? x : nullptr, sv ? nullptr : dy, L.pos, L.src, T, k};
     // Z and act of GEMM1 (routed, then the shared expert): saved by the forward, or recomputed
     void* z = sv ? sv->z : L.z;
     void* act = sv ? sv->act : L.act;
@@ -853,7 +856,7 @@ static int layer_backward_impl(const moe_config* cfg, const void* x, const void*
         e = moe::launch_grouped_gemm_bwd(L.dy_perm, L.x_perm, z, act, L.gate_perm, L.offsets,
                                          w13, w2, A, E, H, F, L.dx_perm, dw13, dw2,
                                          L.dgate_perm, L.bws, stream, false, cfg->w_layout != 0,
-                                         true, sv ? &gx : nullptr);
+                                         true, &gx);
     if (e == hipSuccess && sF)
         e = moe::launch_grouped_gemm_bwd(dy, x, zs, acts, nullptr, L.offs_one, ws13, ws2, T, 1,
                                          H, sF, L.dxs, dws13, dws2, nullptr, L.bws_s, stream,

@@ -78,6 +78,8 @@ struct Operand {
     size_t gstride;               // elements between groups (weights); 0 = rows are global
     int kb_rows;                  // 0: row-major; R: each group's [R, ld] matrix K-blocked
                                   // ([ld / 32][R][32 elements], the forward's weight layout)
+    const int32_t* rows;          // ragged-M A only: row i of the operand is row rows[i] of p
+                                  // (a gather), or nullptr
 };
 
 struct BwdArgs {
@@ -180,7 +182,7 @@ MOE_DEVICE void bwd_tile(const BwdArgs& ba, int L, uint8_t* lds) {
             size_t row;
             if (is_a) {                       // ragged-M activations: global rows, clamped
                 const int rr = m0 + r < Mg ? m0 + r : Mg - 1;
-                row = (size_t)rbase + rr;
+                row = op.rows ? (size_t)op.rows[rbase + rr] : (size_t)rbase + rr;
             } else {
                 row = (size_t)nt * kBN + r;
             }
@@ -614,7 +616,7 @@ hipError_t bwd_all(const BwdWs& w, const void* dy_perm, const void* x_perm, cons
                    const void* act, const float* gate_perm, const int32_t* offsets,
                    const void* w13, const void* w2, int A, int E, int H, int F, void* dx_perm,
                    void* dw13, void* dw2, float* dgate_perm, hipStream_t s, bool join,
-                   bool w_kblock, bool use_side, const BwdGatherX* gx) {
+                   bool w_kblock, bool use_side, const BwdGather* gx) {
     constexpr int kBM = CF::BM, kBN = CF::BN;
     std::lock_guard<std::recursive_mutex> lock(g_side_mu);
     SideRes* sr = nullptr;
@@ -638,11 +640,16 @@ hipError_t bwd_all(const BwdWs& w, const void* dy_perm, const void* x_perm, cons
         if (e == hipSuccess) e = hipStreamWaitEvent(sr->side, sr->ev[0], 0);
         if (e != hipSuccess) return e;
     }
-    // x_perm, when asked, on dW13's stream beside dA (dW13 is its only reader here)
-    if (gx) {
+    // the expert-order copies the caller left to this call: x_perm on dW13's stream beside
+    // dA (dW13 is its only reader), dy_perm on dW2's stream (dA reads dY's rows through src)
+    if (gx && gx->x) {
         if (use_side) e = hipStreamWaitEvent(sr->side2, sr->ev[0], 0);
         if (e == hipSuccess) e = launch_gather_rows(gx->x, gx->pos, gx->T, gx->k, H * 2,
                                                     (void*)x_perm, s_w13);
+        if (e != hipSuccess) return e;
+    }
+    if (gx && gx->dy) {
+        e = launch_gather_rows(gx->dy, gx->pos, gx->T, gx->k, H * 2, (void*)dy_perm, s_w2);
         if (e != hipSuccess) return e;
     }
     // the weight gradients' XCD plan, for group counts it splits evenly: first on the stream
@@ -668,7 +675,8 @@ hipError_t bwd_all(const BwdWs& w, const void* dy_perm, const void* x_perm, cons
     // dgrad 1: dA [A, F] = dy_perm W2_e (W2_e stored [H][F]: K rows) -> dZ, dg partials
     if (e == hipSuccess) {
         BwdArgs d1 = {};
-        d1.a = {DY, (size_t)H, 0, 0};
+        d1.a = {DY, (size_t)H, 0, 0, nullptr};
+        if (gx && gx->dy) d1.a = {(const uint16_t*)gx->dy, (size_t)H, 0, 0, gx->src};
         d1.b = {W2, (size_t)F, (size_t)H * F, w_kblock ? H : 0};
         d1.offsets = offsets; d1.tiles = tiles; d1.total = total;
         d1.N = F; d1.K = H; d1.ntn = F / kBN; d1.groups = E;
@@ -772,7 +780,7 @@ hipError_t launch_grouped_gemm_bwd(const void* dy_perm, const void* x_perm, cons
                                    int A, int E, int H, int F, void* dx_perm, void* dw13,
                                    void* dw2, float* dgate_perm, void* ws, hipStream_t s,
                                    bool join, bool w_kblock, bool use_side,
-                                   const BwdGatherX* gx) {
+                                   const BwdGather* gx) {
     BwdWs w = carve_bwd(ws, A, E, F);
     zero_fill_kernel<<<1, 256, 0, s>>>((uint32_t*)w.zero, kZeroBytes / 4);
     // 256 x 256 tiles when every GEMM dimension divides by 256 (F, 2F and H), else 128 x 128

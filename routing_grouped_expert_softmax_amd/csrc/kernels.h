@@ -143,11 +143,14 @@ size_t bwd_ws_bytes(int T, int k, int E, int H, int F);
 // launch_permute; row-major out, row_bytes a multiple of 16): the permute's row copy alone.
 hipError_t launch_gather_rows(const void* x, const int32_t* pos, int T, int k, int row_bytes,
                               void* out, hipStream_t s);
-// x_perm to be gathered by the backward itself, on the stream of dW13 (its only reader there)
-// while dA runs: the token-order x and the permute's pos.
-struct BwdGatherX {
+// Expert-order copies left to the backward (the permute's pos and src; nullptr = the caller
+// filled that buffer): x (-> x_perm, gathered on dW13's stream while dA runs) and dY
+// (-> dy_perm, gathered on dW2's stream; dA then reads dY's rows through src).
+struct BwdGather {
     const void* x;
+    const void* dy;
     const int32_t* pos;
+    const int32_t* src;
     int T, k;
 };
 hipError_t launch_grouped_gemm_bwd(const void* dy_perm, const void* x_perm, const void* z,
@@ -156,7 +159,7 @@ hipError_t launch_grouped_gemm_bwd(const void* dy_perm, const void* x_perm, cons
                                    int A, int E, int H, int F, void* dx_perm, void* dw13,
                                    void* dw2, float* dgate_perm, void* ws, hipStream_t s,
                                    bool join = true, bool w_kblock = false,
-                                   bool use_side = true, const BwdGatherX* gx = nullptr);
+                                   bool use_side = true, const BwdGather* gx = nullptr);
 hipError_t bwd_side_join(hipStream_t s);
 void bwd_side_lock();
 void bwd_side_unlock();
